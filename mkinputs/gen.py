@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for one decode step: weights, KV cache, batch state.
+
+This module only draws random numbers and lays them out; it holds none of the
+decode step's arithmetic. Both the oracle (through numpy views) and the HIP
+path (through device pointers) consume what it returns.
+
+Recipe (random weights, as in the megakernel post's uniform-routing runs,
+section "Decode throughput" of the Chinese version):
+  * every matrix and the embedding: N(0, 0.02), rounded to bf16 (RNE);
+  * RMSNorm gains: 1 + N(0, 0.02) in bf16, so a missing or mis-indexed gain shows;
+  * synthetic context K and V: N(0, 1) in bf16;
+  * tokens uniform over the vocabulary; ragged lengths uniform in a range;
+  * page tables from a shuffled free-page pool.
+Each tensor gets its own torch.Generator seeded from (base seed, tensor name),
+so tensors are independent and each is reproducible on its own. Values depend
+on the device they are drawn on (torch's CPU and GPU generators differ); a run
+draws every input once and hands the same tensors to both sides.
+
+Canonical layouts (row-major, [in x out]):
+  emb [V, H]; gamma.{l} [H]; gamma_f [H]
+  wqkv.{l} [H, QH*D + 2*KVH*D]   columns: q heads, then k heads, then v heads
+  wo.{l} [QH*D, H]; wr.{l} [H, E]
+  wg.{l}, wu.{l} [E, H, F]; wd.{l} [E, F, H]; wlm [H, V]
+KV pool (one page = page_size tokens, shared page ids across layers):
+  pool [L, n_pages, 2, KVH, page_size*D] bf16, where plane 0 holds K with
+  element (slot, d) at slot*D + d, and plane 1 holds V transposed, element
+  (slot, d) at d*page_size + slot.
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from .configs import ModelConfig, Workload
+
+
+def tensor_seed(base: int, name: str) -> int:
+    h = hashlib.sha256(f"{base}:{name}".encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def _normal_bf16(shape, seed: int, std: float, mean: float, device) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    x.mul_(std)
+    if mean != 0.0:
+        x.add_(mean)
+    return x.to(torch.bfloat16)
+
+
+def weight_shapes(m: ModelConfig) -> Dict[str, tuple]:
+    H, E, F = m.hidden, m.n_experts, m.expert_ffn
+    s = {"emb": (m.vocab, H), "gamma_f": (H,), "wlm": (H, m.vocab)}
+    for l in range(m.n_layers):
+        s[f"gamma.{l}"] = (H,)
+        s[f"wqkv.{l}"] = (H, m.qkv_dim)
+        s[f"wo.{l}"] = (m.q_dim, H)
+        s[f"wr.{l}"] = (H, E)
+        s[f"wg.{l}"] = (E, H, F)
+        s[f"wu.{l}"] = (E, H, F)
+        s[f"wd.{l}"] = (E, F, H)
+    return s
+
+
+def make_weights(m: ModelConfig, seed: int = 1, device="cpu", std: float = 0.02) -> Dict[str, torch.Tensor]:
+    """All weights of model m as canonical bf16 tensors on `device`.
+
+    Expert tensors are drawn one expert at a time (seed per expert slice) to
+    bound the fp32 temporaries of the 48-layer model.
+    """
+    out: Dict[str, torch.Tensor] = {}
+    for name, shape in weight_shapes(m).items():
+        if name.startswith("gamma"):
+            out[name] = _normal_bf16(shape, tensor_seed(seed, name), std, 1.0, device)
+        elif name.split(".")[0] in ("wg", "wu", "wd"):
+            t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+            for e in range(shape[0]):
+                t[e] = _normal_bf16(shape[1:], tensor_seed(seed, f"{name}.e{e}"), std, 0.0, device)
+            out[name] = t
+        else:
+            out[name] = _normal_bf16(shape, tensor_seed(seed, name), std, 0.0, device)
+    return out
+
+
+@dataclass
+class BatchState:
+    tokens: torch.Tensor          # int32 [B]
+    seq_lens: torch.Tensor        # int32 [B], counts the token being decoded
+    block_tables: torch.Tensor    # int32 [B, max_pages_per_seq], -1 past the end
+    n_pages: int                  # pages in the pool
+    max_pages_per_seq: int
+
+
+def make_batch(w: Workload, extra_steps: int = 0, device="cpu", spare_pages: int = 0,
+               max_pages_per_seq: Optional[int] = None) -> BatchState:
+    """Tokens, lengths and scattered page tables for workload w.
+
+    Each sequence gets pages for seq_len + extra_steps positions, taken in
+    order from a seeded permutation of the pool (the shuffled free list).
+    """
+    m = w.model
+    P = m.page_size
+    rng = np.random.Generator(np.random.Philox(tensor_seed(w.seed_batch, w.name)))
+    B = w.batch
+    lo, hi = w.seq_len
+    if w.ragged:
+        lens = rng.integers(lo, hi + 1, size=B)
+    else:
+        lens = np.full(B, lo)
+    tokens = rng.integers(0, m.vocab, size=B)
+    need = [-(-(int(n) + extra_steps) // P) for n in lens]
+    mpps = max(need) if max_pages_per_seq is None else max_pages_per_seq
+    assert mpps >= max(need)
+    n_pages = sum(need) + spare_pages
+    perm = rng.permutation(n_pages)
+    bt = np.full((B, mpps), -1, dtype=np.int64)
+    off = 0
+    for b in range(B):
+        bt[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    return BatchState(
+        tokens=torch.tensor(tokens, dtype=torch.int32, device=device),
+        seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
+        block_tables=torch.tensor(bt, dtype=torch.int32, device=device),
+        n_pages=n_pages,
+        max_pages_per_seq=mpps,
+    )
+
+
+def kv_pool_shape(m: ModelConfig, n_pages: int) -> tuple:
+    return (m.n_layers, n_pages, 2, m.n_kv_heads, m.page_size * m.head_dim)
+
+
+def make_kv_pool(m: ModelConfig, n_pages: int, seed: int = 2, device="cpu", fill: bool = True) -> torch.Tensor:
+    """A KV pool filled with N(0, 1) bf16 (every slot of every page, per layer)."""
+    shape = kv_pool_shape(m, n_pages)
+    if not fill:
+        return torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    pool = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    for l in range(m.n_layers):
+        pool[l] = _normal_bf16(shape[1:], tensor_seed(seed, f"kv.{l}"), 1.0, 0.0, device)
+    return pool
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """A bf16 tensor's raw bits as a numpy uint16 array (host copy)."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class NumpyWeights:
+    """Lazy host view of canonical weights as bf16 bit arrays.
+
+    w(name) -> whole tensor; w(name, layer) -> per-layer tensor;
+    w(name, layer, expert) -> one expert's slice. Fetches (and for device
+    tensors, copies to the host) on first use.
+    """
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], cache: bool = True):
+        self.t = tensors
+        self.cache = cache
+        self._c: Dict[tuple, np.ndarray] = {}
+
+    def __call__(self, name: str, layer: Optional[int] = None, expert: Optional[int] = None) -> np.ndarray:
+        key = (name, layer, expert)
+        if key in self._c:
+            return self._c[key]
+        full = name if layer is None else f"{name}.{layer}"
+        t = self.t[full]
+        if expert is not None:
+            t = t[expert]
+        a = bf16_bits(t)
+        if self.cache:
+            self._c[key] = a
+        return a
+
+    def set(self, name: str, value_bits: np.ndarray, layer: Optional[int] = None):
+        """Replace a whole tensor's bits (used when test inputs are adjusted)."""
+        full = name if layer is None else f"{name}.{layer}"
+        dev = self.t[full].device
+        self.t[full] = torch.from_numpy(value_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        self._c = {k: v for k, v in self._c.items() if not (k[0] == name and k[1] == layer)}
