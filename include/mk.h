@@ -1,0 +1,195 @@
+/*
+ * mk.h - C ABI of the MI355X (gfx950) persistent decode megakernel.
+ *
+ * One call of mk_decode_step runs one decode step of a parallel-transformer
+ * mixture-of-experts decoder for a batch of sequences: embedding, then per
+ * layer RMSNorm -> {QKV + RoPE + paged KV append -> split-KV attention ->
+ * combine -> O projection} and {router -> top-k -> route finalize -> expert
+ * up/gate + SiLU -> expert down -> weighted combine}, rejoined by a fused
+ * residual add + RMSNorm; then the final norm, the LM head and the greedy
+ * token. Source: Cohere's post on the North Mini Code decode megakernel,
+ * sections "What is a Megakernel?" (one persistent workgroup per compute unit
+ * walking a host-built task list, global-memory counters for dependencies),
+ * "Tasks" (the opcode list), "The task descriptor" and the Chinese version's
+ * barrier listing (counters spun on and incremented) and engine section
+ * (update page tables, clear barriers, select schedule, launch, sample).
+ *
+ * Conventions for every entry point:
+ *   - Status codes, never exceptions; mk_last_error() gives a message.
+ *   - "device" pointers are HIP device memory of the device the handle was
+ *     created on; "host" pointers are ordinary host memory.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16).
+ *   - Streams are hipStream_t passed as void* (NULL = the default stream).
+ *   - Argument errors are detected on the host before anything is launched.
+ *     Errors found on the device (bad page/token index, a dependency wait
+ *     that exceeds its time limit) set a device error word; the kernel then
+ *     drains without touching memory further and mk_sync_status() reports it.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = 1,    /* bad pointer, size or shape */
+  MK_ERR_UNSUPPORTED = 2,    /* a shape or mode this build does not handle */
+  MK_ERR_OOM = 3,            /* device allocation failed */
+  MK_ERR_HIP = 4,            /* a HIP runtime call failed */
+  MK_ERR_DEVICE_TIMEOUT = 5, /* a dependency wait on the device timed out */
+  MK_ERR_DEVICE_FAULT = 6,   /* the device rejected an index (page, token, position) */
+  MK_ERR_STATE = 7           /* e.g. decode before all weights were loaded */
+} mk_status;
+
+typedef enum { MK_MODE_MEGAKERNEL = 0, MK_MODE_KERNEL_PER_OP = 1 } mk_mode;
+
+/* Model shape and limits.
+ * Layer l uses full attention iff window == 0 or l % full_every == full_every-1;
+ * other layers attend to the `window` most recent positions including the
+ * current one. Query head h reads key/value group h / (n_q_heads / n_kv_heads).
+ * RoPE rotates interleaved pairs (2i, 2i+1) by position * theta^(-2i/head_dim).
+ * RMSNorm is h / sqrt(mean(h^2) + rms_eps) * gamma. */
+typedef struct {
+  int32_t hidden;          /* H, a multiple of 256, <= 2048 */
+  int32_t n_q_heads;       /* QH */
+  int32_t n_kv_heads;      /* KVH, divides QH; QH / KVH <= 16, (QH / KVH) * D <= 1024 */
+  int32_t head_dim;        /* D: 64 or 128 */
+  int32_t n_experts;       /* E, a multiple of 8, <= 128 */
+  int32_t top_k;           /* k <= 8 */
+  int32_t expert_ffn;      /* F, a multiple of 128, <= 768 */
+  int32_t vocab;           /* V, a multiple of 16 */
+  int32_t n_layers;        /* L */
+  float rope_theta;
+  float rms_eps;
+  int32_t page_size;       /* tokens per KV page: 16 */
+  int32_t window;          /* 0 = all layers full attention */
+  int32_t full_every;      /* >= 1 */
+  int32_t max_batch;       /* largest batch mk_decode_step will be called with, <= 32 */
+  int32_t max_seq_len;     /* largest seq_len (positions + 1) any step may see */
+  int32_t max_pages_per_seq; /* row stride of block_tables */
+  int32_t n_pages;         /* pages in the KV pool */
+  int32_t mode;            /* mk_mode */
+} mk_config;
+
+typedef struct mk_handle mk_handle;
+
+/* Create a decoder for `cfg` on HIP device `device`.
+ * kv_pool: device, caller-owned, stays valid until mk_destroy. Layout, bf16:
+ *   [n_layers][n_pages][2][n_kv_heads][page_size * head_dim]
+ *   plane 0 = K, element (slot s, dim d) at s*head_dim + d;
+ *   plane 1 = V, stored transposed: element (slot s, dim d) at d*page_size + s.
+ * Page p of a sequence holds its positions [p*page_size, (p+1)*page_size)
+ * (tiny-vllm decode walkthrough, section on scattering K/V into blocks).
+ * kv_pool_bytes must equal the size of that layout.
+ * Allocates the library's weight copy (uninitialised), scratch, counters. */
+mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes,
+                    int device, mk_handle** out);
+
+/* Load one layer's weights from caller-owned device bf16 tensors in the
+ * canonical row-major [in x out] layout; the library repacks them into its own
+ * copy (so the caller may free them once `stream` has passed this call).
+ *   gamma [H]; wqkv [H][QH*D + 2*KVH*D] (q heads, then k heads, then v heads);
+ *   wo [QH*D][H]; wr [H][E]; wg, wu [E][H][F]; wd [E][F][H]. */
+mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* wqkv,
+                        const void* wo, const void* wr, const void* wg, const void* wu,
+                        const void* wd, void* stream);
+
+/* Load the embedding [V][H], final norm gain [H] and LM head [H][V] (bf16). */
+mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f,
+                          const void* wlm, void* stream);
+
+/* All weights at once: arrays of n_layers device pointers per tensor kind. */
+typedef struct {
+  const void* emb;
+  const void* gamma_f;
+  const void* wlm;
+  const void* const* gamma;
+  const void* const* wqkv;
+  const void* const* wo;
+  const void* const* wr;
+  const void* const* wg;
+  const void* const* wu;
+  const void* const* wd;
+} mk_weights;
+mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream);
+
+/* Flags of mk_decode_step. */
+#define MK_STEP_ADVANCE 1u /* after the step: tokens[b] = next token, seq_lens[b] += 1 */
+
+/* One decode step for `batch` sequences, enqueued on `stream` (no host sync).
+ *   tokens       device int32 [batch]: token being decoded per sequence
+ *   block_tables device int32 [batch][max_pages_per_seq]: physical page ids;
+ *                entries for pages holding positions < seq_len must be valid
+ *   seq_lens     device int32 [batch]: length INCLUDING this token; the token
+ *                sits at position seq_len - 1, and its K/V are appended there
+ *                before attention reads the cache
+ *   max_seq_len_hint host: an upper bound of seq_lens in this step (selects
+ *                the cached schedule; the device clamps nothing to it, it
+ *                rejects lengths beyond it with MK_ERR_DEVICE_FAULT)
+ *   logits       device float32 [batch][vocab], written
+ *   next_tokens  device int32 [batch] or NULL: greedy token (argmax, lowest
+ *                index on ties)
+ * The caller owns every argument buffer and keeps it unchanged until the
+ * stream has passed the step. Consecutive steps on one handle must be on the
+ * same stream or otherwise ordered (they share scratch and counters). */
+mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
+                         int32_t* seq_lens, int max_seq_len_hint, float* logits,
+                         int32_t* next_tokens, uint32_t flags, void* stream);
+
+/* Record every layer's routing of later steps into `trace` (device int32
+ * [n_layers][batch][top_k], expert ids in descending router-logit order, ties
+ * to the lower id); NULL stops recording. For checking routing decisions. */
+mk_status mk_set_routing_trace(mk_handle* h, int32_t* trace);
+
+/* Synchronise `stream` and report any device-side error of earlier steps
+ * (MK_ERR_DEVICE_TIMEOUT / MK_ERR_DEVICE_FAULT); clears the error word. */
+mk_status mk_sync_status(mk_handle* h, void* stream);
+
+/* Last error message of this handle (or of the last failed mk_create when h is NULL). */
+const char* mk_last_error(const mk_handle* h);
+
+void mk_destroy(mk_handle* h);
+
+/* ---- schedule introspection (host only, no device work) ---------------- */
+
+/* Task counts of the schedule for (batch, max_seq_len_hint): total tasks and
+ * the longest per-CU list, and the number of dependency counters. */
+typedef struct {
+  int32_t n_tasks;
+  int32_t max_tasks_per_cu;
+  int32_t n_counters;
+  int32_t n_cus;
+  int64_t weight_bytes_per_step; /* weights streamed at batch 1 routing (k experts) */
+} mk_schedule_info;
+mk_status mk_schedule_info_get(mk_handle* h, int batch, int max_seq_len_hint, mk_schedule_info* out);
+
+/* Copy the schedule's descriptors (n_tasks * 32 int32, CU-major, each CU's
+ * list in execution order) and per-CU offsets (n_cus + 1 int32) to host
+ * buffers sized from mk_schedule_info_get. */
+mk_status mk_schedule_export(mk_handle* h, int batch, int max_seq_len_hint, int32_t* tasks,
+                             int32_t* cu_offsets);
+
+/* Run the schedule on a host model of the device: each CU executes its list
+ * in order, a task runs once its counter waits are met, claimers drain their
+ * queues; n_active_experts[l] gives the routing outcome per layer (number of
+ * distinct experts). Reports deadlock (a state where no CU can progress) and
+ * checks every counter's final value against the arrivals it expects.
+ * `interleave_seed` picks the order in which ready CUs advance.
+ * Returns MK_OK if the run completes and every check holds. */
+mk_status mk_schedule_simulate(mk_handle* h, int batch, int max_seq_len_hint,
+                               const int32_t* n_active_experts, uint64_t interleave_seed,
+                               int32_t corrupt_task, char* report, size_t report_len);
+
+/* Create a handle without any device (schedule introspection and simulation
+ * only; mk_load_*, mk_decode_step return MK_ERR_STATE). */
+mk_status mk_create_host_only(const mk_config* cfg, int n_cus, mk_handle** out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

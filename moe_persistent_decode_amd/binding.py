@@ -1,0 +1,187 @@
+"""ctypes binding of libmk.so: the C ABI in include/mk.h, argument marshalling only.
+
+Every step of the decode runs in the library's HIP kernels; this module turns
+torch tensors into device pointers and status codes into exceptions. It never
+computes anything of the decode step itself and has no fallback: if the
+library is missing, importing the package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK = 0
+STATUS = {0: "MK_OK", 1: "MK_ERR_INVALID_ARG", 2: "MK_ERR_UNSUPPORTED", 3: "MK_ERR_OOM", 4: "MK_ERR_HIP",
+          5: "MK_ERR_DEVICE_TIMEOUT", 6: "MK_ERR_DEVICE_FAULT", 7: "MK_ERR_STATE"}
+MODE_MEGAKERNEL = 0
+MODE_KERNEL_PER_OP = 1
+STEP_ADVANCE = 1
+
+# every function include/mk.h declares
+EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
+           "mk_decode_step", "mk_set_routing_trace", "mk_sync_status", "mk_last_error", "mk_destroy",
+           "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate")
+
+
+class MkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class MkConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("hidden", "n_q_heads", "n_kv_heads", "head_dim", "n_experts",
+                                              "top_k", "expert_ffn", "vocab", "n_layers")] + [
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("page_size", "window", "full_every", "max_batch", "max_seq_len",
+                                      "max_pages_per_seq", "n_pages", "mode")]
+
+
+class MkScheduleInfo(ctypes.Structure):
+    _fields_ = [("n_tasks", ctypes.c_int32), ("max_tasks_per_cu", ctypes.c_int32),
+                ("n_counters", ctypes.c_int32), ("n_cus", ctypes.c_int32),
+                ("weight_bytes_per_step", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run moe_persistent_decode_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S, U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64
+    H = ctypes.c_void_p
+    lib.mk_create.argtypes = [ctypes.POINTER(MkConfig), P, S, I, ctypes.POINTER(H)]
+    lib.mk_create_host_only.argtypes = [ctypes.POINTER(MkConfig), I, ctypes.POINTER(H)]
+    lib.mk_load_layer.argtypes = [H, I, P, P, P, P, P, P, P, P]
+    lib.mk_load_globals.argtypes = [H, P, P, P, P]
+    lib.mk_load_weights.argtypes = [H, P, P]
+    lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
+    lib.mk_set_routing_trace.argtypes = [H, P]
+    lib.mk_sync_status.argtypes = [H, P]
+    lib.mk_last_error.argtypes = [H]
+    lib.mk_last_error.restype = ctypes.c_char_p
+    lib.mk_destroy.argtypes = [H]
+    lib.mk_destroy.restype = None
+    lib.mk_schedule_info_get.argtypes = [H, I, I, ctypes.POINTER(MkScheduleInfo)]
+    lib.mk_schedule_export.argtypes = [H, I, I, P, P]
+    lib.mk_schedule_simulate.argtypes = [H, I, I, P, U64, ctypes.c_int32, ctypes.c_char_p, S]
+    for name in EXPORTS:
+        if name not in ("mk_last_error", "mk_destroy"):
+            getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages_per_seq: int,
+                mode: int = MODE_MEGAKERNEL) -> MkConfig:
+    """MkConfig from a model-shape object (fields as in mkinputs.configs.ModelConfig)."""
+    return MkConfig(hidden=model.hidden, n_q_heads=model.n_q_heads, n_kv_heads=model.n_kv_heads,
+                    head_dim=model.head_dim, n_experts=model.n_experts, top_k=model.top_k,
+                    expert_ffn=model.expert_ffn, vocab=model.vocab, n_layers=model.n_layers,
+                    rope_theta=model.rope_theta, rms_eps=model.eps, page_size=model.page_size,
+                    window=model.window, full_every=model.full_every, max_batch=max_batch,
+                    max_seq_len=max_seq_len, max_pages_per_seq=max_pages_per_seq, n_pages=n_pages,
+                    mode=mode)
+
+
+class Decoder:
+    """One mk_handle. `kv_pool` is a caller-owned device bf16 tensor in the
+    pool layout of include/mk.h; it must outlive the decoder."""
+
+    def __init__(self, cfg: MkConfig, kv_pool=None, device: int = 0, host_only_cus: int = 0):
+        self._h = ctypes.c_void_p()
+        self.cfg = cfg
+        self.kv_pool = kv_pool
+        if host_only_cus:
+            st = lib.mk_create_host_only(ctypes.byref(cfg), host_only_cus, ctypes.byref(self._h))
+        else:
+            nbytes = kv_pool.numel() * kv_pool.element_size()
+            st = lib.mk_create(ctypes.byref(cfg), _ptr(kv_pool), nbytes, device, ctypes.byref(self._h))
+        if st != MK_OK:
+            raise MkError(st, lib.mk_last_error(None).decode())
+
+    def _check(self, st: int):
+        if st != MK_OK:
+            raise MkError(st, lib.mk_last_error(self._h).decode())
+
+    def close(self):
+        if self._h:
+            lib.mk_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- weights
+    def load_layer(self, layer: int, gamma, wqkv, wo, wr, wg, wu, wd, stream=None):
+        self._check(lib.mk_load_layer(self._h, layer, _ptr(gamma), _ptr(wqkv), _ptr(wo), _ptr(wr),
+                                      _ptr(wg), _ptr(wu), _ptr(wd), _stream_ptr(stream)))
+
+    def load_globals(self, emb, gamma_f, wlm, stream=None):
+        self._check(lib.mk_load_globals(self._h, _ptr(emb), _ptr(gamma_f), _ptr(wlm), _stream_ptr(stream)))
+
+    def load_weights(self, w: Dict[str, "object"], stream=None):
+        """Load canonical tensors named emb, gamma_f, wlm, gamma.{l}, wqkv.{l}, ..."""
+        self.load_globals(w["emb"], w["gamma_f"], w["wlm"], stream)
+        for l in range(self.cfg.n_layers):
+            self.load_layer(l, w[f"gamma.{l}"], w[f"wqkv.{l}"], w[f"wo.{l}"], w[f"wr.{l}"], w[f"wg.{l}"],
+                            w[f"wu.{l}"], w[f"wd.{l}"], stream)
+
+    # ---- decode
+    def step(self, tokens, block_tables, seq_lens, max_seq_len_hint: int, logits, next_tokens=None,
+             advance: bool = False, stream=None):
+        self._check(lib.mk_decode_step(self._h, tokens.shape[0], _ptr(tokens), _ptr(block_tables),
+                                       _ptr(seq_lens), int(max_seq_len_hint), _ptr(logits), _ptr(next_tokens),
+                                       STEP_ADVANCE if advance else 0, _stream_ptr(stream)))
+
+    def set_routing_trace(self, trace):
+        self._check(lib.mk_set_routing_trace(self._h, _ptr(trace)))
+
+    def sync(self, stream=None):
+        self._check(lib.mk_sync_status(self._h, _stream_ptr(stream)))
+
+    # ---- schedule (host only)
+    def schedule_info(self, batch: int, hint: int) -> MkScheduleInfo:
+        info = MkScheduleInfo()
+        self._check(lib.mk_schedule_info_get(self._h, batch, hint, ctypes.byref(info)))
+        return info
+
+    def schedule_export(self, batch: int, hint: int):
+        import numpy as np
+        info = self.schedule_info(batch, hint)
+        tasks = np.zeros((info.n_tasks, 32), dtype=np.int32)
+        off = np.zeros(info.n_cus + 1, dtype=np.int32)
+        self._check(lib.mk_schedule_export(self._h, batch, hint, tasks.ctypes.data, off.ctypes.data))
+        return tasks, off
+
+    def simulate(self, batch: int, hint: int, n_active, seed: int = 0, corrupt_task: int = -1):
+        import numpy as np
+        na = np.ascontiguousarray(np.asarray(n_active, dtype=np.int32))
+        buf = ctypes.create_string_buffer(256)
+        st = lib.mk_schedule_simulate(self._h, batch, hint, na.ctypes.data, seed, corrupt_task, buf, 256)
+        return st, buf.value.decode()

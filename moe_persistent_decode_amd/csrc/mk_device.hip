@@ -1,0 +1,874 @@
+// mk_device.hip - the persistent decode interpreter and its op bodies (gfx950).
+//
+// One workgroup of 512 threads (8 wave64s) stays resident per compute unit and
+// walks its host-built task list (Cohere North Mini Code megakernel post,
+// section "What is a Megakernel?"). Each task:
+//   1. issues the loads of its weight tiles (weights do not depend on this
+//      step's activations, so they stream before the dependency clears:
+//      section "Weight prefetch");
+//   2. spins until its input counters reach their targets (the barrier
+//      listing of the Chinese version: spin on a global counter, then fence);
+//   3. computes and stores its output tile;
+//   4. makes its stores visible at device scope and increments its output
+//      counter (release, then atomic add).
+// The same kernel, launched once per wave of same-type tasks with waits
+// switched off, is the kernel-per-op variant.
+//
+// Memory ordering on CDNA4: each XCD has its own L2, so a producer on one XCD
+// and a consumer on another need an agent-scope release (L2 write-back) before
+// the counter increment and an agent-scope acquire (L2 invalidate) after the
+// counter wait. Weights and the older part of the KV cache are never written
+// during a step and need neither.
+#include <hip/hip_runtime.h>
+
+#include "mk_internal.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace {
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// float -> bf16 bits, round to nearest even
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr float kNegInf = -__builtin_inff();
+
+struct SmemAttn {
+  float m[MK_WAVES][16];
+  float l[MK_WAVES][16];
+  float o[MK_WAVES][128][17];
+};
+
+// 96 KB of LDS: more than half of gfx950's 160 KB, so exactly one workgroup
+// fits per compute unit.
+union SmemU {
+  float red[MK_WAVES][64];
+  SmemAttn at;
+  float pad[24 * 1024];
+};
+
+struct Smem {
+  SmemU u;
+  float out[64];
+  float vred[MK_WAVES];
+  int ired[MK_WAVES];
+  int flag;
+  int claim;
+  int cnt[128];
+};
+
+__device__ void raise_error(const mk_params& P, uint32_t code, uint32_t detail, uint32_t value) {
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(&P.err[0], &expected, code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(&P.err[1], detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.err[2], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.err[3], (uint32_t)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Spin (thread 0) until ctr[c] >= tgt for each wait, or until another
+// workgroup raised an error, or until the time limit. Block-uniform result.
+__device__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm) {
+  if (threadIdx.x == 0) {
+    int ok = ld_relaxed(&P.err[0]) == 0;
+    if (ok && P.waits_enabled) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (int i = 0; i < n && ok; ++i) {
+        if (cs[i] < 0) continue;
+        const uint32_t* c = P.ctr + cs[i];
+        const uint32_t tgt = (uint32_t)ts[i];
+        uint32_t spins = 0;
+        while (ld_relaxed(c) < tgt) {
+          __builtin_amdgcn_s_sleep(2);
+          if ((++spins & 63u) == 0) {
+            if (ld_relaxed(&P.err[0]) != 0) { ok = 0; break; }
+            if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > P.timeout_ticks) {
+              raise_error(P, MK_DEVERR_TIMEOUT, (uint32_t)cs[i], ld_relaxed(c));
+              ok = 0;
+              break;
+            }
+          }
+        }
+      }
+      fence_acquire();
+    }
+    sm.flag = ok;
+  }
+  __syncthreads();
+  const bool ok = sm.flag != 0;
+  __syncthreads();
+  return ok;
+}
+
+__device__ __forceinline__ bool wait_task(const mk_params& P, const mk_task& t, Smem& sm) {
+  return wait_counters(P, t.wait_ctr, t.wait_tgt, 3, sm);
+}
+
+__device__ __forceinline__ bool wait_one(const mk_params& P, int32_t c, int32_t tgt, Smem& sm) {
+  return wait_counters(P, &c, &tgt, 1, sm);
+}
+
+// Publish this workgroup's stores at device scope, then count one arrival.
+__device__ void signal_counter(const mk_params& P, int32_t c) {
+  fence_release();
+  __syncthreads();
+  if (threadIdx.x == 0 && c >= 0)
+    __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int layer_window(const mk_params& P, int l) {
+  if (P.window == 0) return 0;
+  return (l % P.full_every) == P.full_every - 1 ? 0 : P.window;
+}
+
+// ----------------------------------------------------- batch-1 GEMV panels
+//
+// Weight matrices [K x N] are stored panel-tiled: 16-column panels, each a run
+// of K/32 chunks of 1 KB; in a chunk, lane l holds the 8 bf16 of rows
+// 32c + 8(l/16) + i (i = 0..7) of column 16j + l%16. Chunk c of a panel goes
+// to wave c % 8, so each wave keeps its slice of the activation vector in
+// registers and every load is one contiguous 1 KB line per wave.
+
+template <int NP, int NCH>
+struct WTile {
+  u32x4_t v[NP][NCH];
+};
+
+template <int NP, int NCH>
+__device__ __forceinline__ void wtile_load(WTile<NP, NCH>& w, const uint16_t* base, size_t pstride,
+                                           int np, int c0, int c1) {
+  const int wv = wave_id(), ln = lane_id();
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = c0 + wv + MK_WAVES * i;
+      if (pp < np && c < c1)
+        w.v[pp][i] = __builtin_nontemporal_load((const u32x4_t*)(base + pp * pstride + (size_t)c * 512) + ln);
+    }
+}
+
+__device__ __forceinline__ float dot8(float4 x0, float4 x1, u32x4_t q, float s) {
+  s = fmaf(x0.x, bf_lo(q.x), s);
+  s = fmaf(x0.y, bf_hi(q.x), s);
+  s = fmaf(x0.z, bf_lo(q.y), s);
+  s = fmaf(x0.w, bf_hi(q.y), s);
+  s = fmaf(x1.x, bf_lo(q.z), s);
+  s = fmaf(x1.y, bf_hi(q.z), s);
+  s = fmaf(x1.z, bf_lo(q.w), s);
+  s = fmaf(x1.w, bf_hi(q.w), s);
+  return s;
+}
+
+// y[16*pp + col] = sum_k x[k - 32*c0] * W[k][col] over chunks [c0, c1), into sm.out.
+// x: float32 activations starting at row 32*c0.
+template <int NP, int NCH>
+__device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0, int c1, Smem& sm) {
+  const int wv = wave_id(), ln = lane_id();
+  float acc[NP];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) acc[pp] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = c0 + wv + MK_WAVES * i;
+    if (c < c1) {
+      const float4* xp = (const float4*)(x + (size_t)(c - c0) * 32 + 8 * (ln >> 4));
+      const float4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp)
+        if (pp < np) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    acc[pp] += __shfl_xor(acc[pp], 16);
+    acc[pp] += __shfl_xor(acc[pp], 32);
+  }
+  if (ln < 16) {
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+      if (pp < np) sm.u.red[wv][pp * 16 + ln] = acc[pp];
+  }
+  __syncthreads();
+  if (threadIdx.x < np * 16) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k][threadIdx.x];
+    sm.out[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------- NORM
+// Residual add of the attention (4 group partials) and MoE (k expert outputs
+// weighted by the router, in rank order) branches, then RMSNorm with the next
+// layer's gain (megakernel post, section "Reduce wave quantization": the
+// parallel layer's branches rejoin in one fused residual add + RMSNorm).
+// Layer 0: the residual is the token's embedding row.
+__device__ void op_norm(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int b = t.a[0], l = t.layer, H = P.H;
+  float* h = P.h + (size_t)b * H;
+  int tok = 0;
+  if (l == 0) {
+    tok = P.tokens[b];
+    if (tok < 0 || tok >= P.V) {
+      if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 1000 + b, (uint32_t)tok);
+      tok = 0;
+    }
+  }
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += MK_WG_THREADS) {
+    float v;
+    if (l == 0) {
+      v = bf2f(P.emb[(size_t)tok * H + i]);
+    } else {
+      float a = 0.f;
+      for (int g = 0; g < P.KVH; ++g) a += P.ao[((size_t)g * P.B + b) * H + i];
+      float y = 0.f;
+      for (int j = 0; j < P.K; ++j)
+        y = fmaf(P.tk_w[b * P.K + j], P.dn[(size_t)(b * P.K + j) * H + i], y);
+      v = (h[i] + a) + y;
+    }
+    h[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if (lane_id() == 0) sm.vred[wave_id()] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
+  const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
+  const uint16_t* gam = P.gamma + (size_t)l * H;
+  for (int i = threadIdx.x; i < H; i += MK_WG_THREADS)
+    P.xn[(size_t)b * H + i] = h[i] * inv * bf2f(gam[i]);
+}
+
+// -------------------------------------------------------------------- QKV
+// QKV panels with RoPE in the epilogue and the K/V append into the paged
+// cache (megakernel post, section "Tasks": QKV_PROJ applies RoPE in-register
+// in its epilogue; tiny-vllm walkthrough: the new token's K/V are written to
+// page block_table[pos / 16], slot pos % 16, before attention).
+template <int NCH>
+__device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int l = t.layer, p0 = t.a[0], np = t.a[1];
+  const int kc = P.H / 32;
+  const size_t pstride = (size_t)kc * 512;
+  WTile<2, NCH> w;
+  wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
+  if (!wait_task(P, t, sm)) return;
+  const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
+  for (int b = 0; b < P.B; ++b) {
+    gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
+    if (wave_id() == 0) {
+      const int tid = threadIdx.x;
+      const float y = tid < np * 16 ? sm.out[tid] : 0.f;
+      const float yp = __shfl_xor(y, 1);
+      const int seq = P.seq_lens[b];
+      if (tid < np * 16) {
+        if (seq < 1 || seq > P.max_seq) {
+          if (tid == 0) raise_error(P, MK_DEVERR_FAULT, 2000 + b, (uint32_t)seq);
+        } else {
+          const int pos = seq - 1;
+          const int n = p0 * 16 + tid;
+          const bool odd = n & 1;
+          if (n < qd + kvd) {
+            const int d = (n < qd ? n : n - qd) % D;
+            const float c = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0];
+            const float s = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1];
+            // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
+            const float x0 = odd ? yp : y, x1 = odd ? y : yp;
+            const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
+            if (n < qd) {
+              P.q[(size_t)b * qd + n] = r;
+            } else {
+              const int g = (n - qd) / D;
+              const int page = P.bt[b * P.mpps + pos / PS];
+              if (page < 0 || page >= P.n_pages) {
+                raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
+              } else {
+                uint16_t* kp = P.kv + l * P.s_kv_l + ((size_t)(page * 2 + 0) * P.KVH + g) * PS * D;
+                kp[(pos % PS) * D + d] = (uint16_t)f2bf(r);
+              }
+            }
+          } else {
+            const int nn = n - qd - kvd;
+            const int g = nn / D, d = nn % D;
+            const int page = P.bt[b * P.mpps + pos / PS];
+            if (page < 0 || page >= P.n_pages) {
+              raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
+            } else {
+              uint16_t* vp = P.kv + l * P.s_kv_l + ((size_t)(page * 2 + 1) * P.KVH + g) * PS * D;
+              vp[d * PS + (pos % PS)] = (uint16_t)f2bf(y);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// -------------------------------------------------------------- attention
+// Split-KV partial attention of the G query heads of one kv group over a
+// range of pages (megakernel post, section "Tasks": ATTN_DECODE over partial
+// KV slices). MFMA with the keys as rows: S^T = K Q^T (16 keys x 16 heads per
+// page, heads >= G padded), online softmax per head, O^T += V^T P^T (V is
+// stored transposed within a page so each lane's operand is 8 contiguous
+// bytes). The 8 waves take alternate pages and merge at the end.
+template <int D>
+__device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
+  constexpr int NC = D / 32;
+  constexpr int NT = D / 16;
+  const int l = t.layer, b = t.a[0], g = t.a[1], s = t.a[2], pps = t.a[4];
+  const int wv = wave_id(), ln = lane_id();
+  const int PS = P.PS, G = P.G;
+  if (!wait_task(P, t, sm)) return;
+  const int seq = P.seq_lens[b];
+  if (seq < 1 || seq > P.max_seq) {
+    if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
+    return;
+  }
+  const int p = seq - 1;
+  const int win = layer_window(P, l);
+  const int lo = win ? max(0, p - win + 1) : 0;
+  const int lp_first = lo / PS, lp_last = p / PS;
+  const int my0 = lp_first + s * pps;
+  const int my1 = min(my0 + pps, lp_last + 1);
+  const uint16_t* kvl = P.kv + l * P.s_kv_l;
+  const size_t plane = (size_t)PS * D;
+  const float scale = P.attn_scale;
+
+  // Q^T operand: lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
+  bf16x8_t qb[NC];
+  {
+    const int hh = ln & 15;
+    const float* qp = P.q + (size_t)b * P.QH * D + (size_t)(g * G + min(hh, G - 1)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4_t pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = hh < G ? f2bf(qp[32 * c + 8 * (ln >> 4) + 2 * i]) : 0u;
+        const uint32_t hi = hh < G ? f2bf(qp[32 * c + 8 * (ln >> 4) + 2 * i + 1]) : 0u;
+        pk[i] = lo | (hi << 16);
+      }
+      qb[c] = __builtin_bit_cast(bf16x8_t, pk);
+    }
+  }
+
+  f32x4_t oacc[NT];
+#pragma unroll
+  for (int d = 0; d < NT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, lsum = 0.f;
+
+  u32x4_t kr[NC];
+  u32x2_t vr[NT];
+  bool bad = false;
+  auto load_page = [&](int lp, u32x4_t* kk, u32x2_t* vv) {
+    const int phys = P.bt[b * P.mpps + lp];
+    if (phys < 0 || phys >= P.n_pages) {
+      bad = true;
+      return;
+    }
+    const uint16_t* kp = kvl + ((size_t)(phys * 2 + 0) * P.KVH + g) * plane;
+    const uint16_t* vp = kvl + ((size_t)(phys * 2 + 1) * P.KVH + g) * plane;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kk[c] = *(const u32x4_t*)(kp + (ln & 15) * D + 32 * c + 8 * (ln >> 4));
+#pragma unroll
+    for (int d = 0; d < NT; ++d) vv[d] = *(const u32x2_t*)(vp + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4));
+  };
+
+  int lp = my0 + wv;
+  if (lp < my1) load_page(lp, kr, vr);
+  while (lp < my1 && !bad) {
+    u32x4_t kn[NC];
+    u32x2_t vn[NT];
+    const int nlp = lp + MK_WAVES;
+    if (nlp < my1) load_page(nlp, kn, vn);
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), qb[c], sacc, 0, 0, 0);
+    float sv[4];
+    float mloc = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = lp * PS + 4 * (ln >> 4) + i;
+      sv[i] = (pos >= lo && pos <= p) ? sacc[i] * scale : kNegInf;
+      mloc = fmaxf(mloc, sv[i]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float mnew = fmaxf(m, mloc);
+    if (mnew != kNegInf) {
+      const float alpha = (m == kNegInf) ? 0.f : __expf(m - mnew);
+      uint32_t pb[4];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = sv[i] == kNegInf ? 0.f : __expf(sv[i] - mnew);
+        pb[i] = f2bf(pv);
+        ps += bf2f((uint16_t)pb[i]);
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      lsum = lsum * alpha + ps;
+      m = mnew;
+      const s16x4_t pB = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+#pragma unroll
+      for (int d = 0; d < NT; ++d) {
+        oacc[d] *= alpha;
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vr[d]), pB, oacc[d], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = kn[c];
+#pragma unroll
+    for (int d = 0; d < NT; ++d) vr[d] = vn[d];
+    lp = nlp;
+  }
+  if (bad) raise_error(P, MK_DEVERR_FAULT, 5000 + b, (uint32_t)lp);
+
+  // merge the 8 waves' (m, l, O) per head
+  SmemAttn& A = sm.u.at;
+  if (ln < 16) {
+    A.m[wv][ln] = m;
+    A.l[wv][ln] = lsum;
+  }
+#pragma unroll
+  for (int d = 0; d < NT; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A.o[wv][16 * d + 4 * (ln >> 4) + i][ln & 15] = oacc[d][i];
+  __syncthreads();
+  const int stride = G * D + 2 * G;
+  float* dst = P.part + ((size_t)(b * P.KVH + g) * P.max_splits + s) * stride;
+  for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
+    const int hh = idx / D, dd = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < MK_WAVES; ++k) M = fmaxf(M, A.m[k][hh]);
+    float O = 0.f, L = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int k = 0; k < MK_WAVES; ++k) {
+        const float f = A.m[k][hh] == kNegInf ? 0.f : __expf(A.m[k][hh] - M);
+        O = fmaf(f, A.o[k][dd][hh], O);
+        L = fmaf(f, A.l[k][hh], L);
+      }
+    }
+    dst[hh * D + dd] = O;
+    if (dd == 0) {
+      dst[G * D + hh] = M;
+      dst[G * D + G + hh] = L;
+    }
+  }
+}
+
+// Log-sum-exp merge of one (sequence, kv group)'s split partials into the
+// attention output (megakernel post, section "Tasks": ATTN_COMBINE).
+__device__ void op_attn_combine(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int b = t.a[0], g = t.a[1], ns = t.a[2];
+  const int G = P.G, D = P.D;
+  const int stride = G * D + 2 * G;
+  const float* src = P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride;
+  for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
+    const int hh = idx / D, dd = idx % D;
+    float M = kNegInf;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, src[s * stride + G * D + hh]);
+    float O = 0.f, L = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = src[s * stride + G * D + hh];
+      const float f = ms == kNegInf ? 0.f : __expf(ms - M);
+      O = fmaf(f, src[s * stride + hh * D + dd], O);
+      L = fmaf(f, src[s * stride + G * D + G + hh], L);
+    }
+    P.o[(size_t)b * P.QH * D + (size_t)(g * G + hh) * D + dd] = O / L;
+  }
+}
+
+// ------------------------------------------------------------------ O proj
+// O projection split-K by kv group: group g's 8 heads contribute their slice
+// of the K dimension as soon as that group's attention lands (megakernel post,
+// section "Drop false dependencies").
+template <int NCH>
+__device__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int l = t.layer, g = t.a[0], p0 = t.a[1], np = t.a[2];
+  const int kc = P.QH * P.D / 32;
+  const int c0 = g * P.G * P.D / 32, c1 = c0 + P.G * P.D / 32;
+  const size_t pstride = (size_t)kc * 512;
+  WTile<2, NCH> w;
+  wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, np, c0, c1);
+  if (!wait_task(P, t, sm)) return;
+  for (int b = 0; b < P.B; ++b) {
+    gemv_b1(w, P.o + (size_t)b * P.QH * P.D + (size_t)g * P.G * P.D, np, c0, c1, sm);
+    if (threadIdx.x < np * 16)
+      P.ao[((size_t)g * P.B + b) * P.H + p0 * 16 + threadIdx.x] = sm.out[threadIdx.x];
+  }
+}
+
+// ------------------------------------------------------------------ router
+template <int NCH>
+__device__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int l = t.layer, p0 = t.a[0], np = t.a[1];
+  const int kc = P.H / 32;
+  const size_t pstride = (size_t)kc * 512;
+  WTile<2, NCH> w;
+  wtile_load(w, P.wr + l * P.s_wr + (size_t)p0 * pstride, pstride, np, 0, kc);
+  if (!wait_task(P, t, sm)) return;
+  for (int b = 0; b < P.B; ++b) {
+    gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
+    const int n = p0 * 16 + threadIdx.x;
+    if (threadIdx.x < np * 16 && n < P.E) P.r[(size_t)b * P.E + n] = sm.out[threadIdx.x];
+  }
+}
+
+// Top-k of each token's router logits (ties to the lower expert index), the
+// softmax over the kept logits, then the expert work queue: active experts in
+// ascending id, the token slots routed to each (megakernel post, section
+// "Tasks": ROUTER_TOPK and ROUTE_FINALIZE).
+__device__ void op_topk(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int E = P.E, K = P.K, B = P.B;
+  const int ln = lane_id();
+  for (int b = wave_id(); b < B; b += MK_WAVES) {
+    const float* r = P.r + (size_t)b * E;
+    const float v0 = ln < E ? r[ln] : kNegInf;
+    const float v1 = ln + 64 < E ? r[ln + 64] : kNegInf;
+    bool tk0 = ln >= E, tk1 = ln + 64 >= E;
+    float sel[MK_MAX_TOPK];
+    int idx[MK_MAX_TOPK];
+    for (int j = 0; j < K; ++j) {
+      float bv = kNegInf;
+      int bi = 0x7fffffff;
+      if (!tk0) { bv = v0; bi = ln; }
+      if (!tk1 && (v1 > bv || bi == 0x7fffffff)) { bv = v1; bi = ln + 64; }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      sel[j] = bv;
+      idx[j] = bi;
+      if (bi == ln) tk0 = true;
+      if (bi == ln + 64) tk1 = true;
+    }
+    const float mx = sel[0];
+    float e[MK_MAX_TOPK], sum = 0.f;
+    for (int j = 0; j < K; ++j) {
+      e[j] = __expf(sel[j] - mx);
+      sum += e[j];
+    }
+    if (ln == 0)
+      for (int j = 0; j < K; ++j) {
+        P.tk_idx[b * K + j] = idx[j];
+        P.tk_w[b * K + j] = e[j] / sum;
+        if (P.tk_trace) P.tk_trace[((size_t)t.layer * B + b) * K + j] = idx[j];
+      }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += MK_WG_THREADS) {
+    int c = 0;
+    for (int i = 0; i < B * K; ++i) c += P.tk_idx[i] == e;
+    sm.cnt[e] = c;
+  }
+  __syncthreads();
+  int32_t* R = P.route;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int e = 0; e < E; ++e)
+      if (sm.cnt[e] > 0) {
+        R[4 + n] = e;
+        R[4 + E + n] = sm.cnt[e];
+        sm.cnt[e] = -(n + 1);  // active slot of expert e
+        ++n;
+      }
+    R[0] = n;
+    R[1] = n * P.up_items_per_expert;
+    R[2] = n * P.down_items_per_expert;
+  }
+  __syncthreads();
+  if (threadIdx.x < B * K) {
+    const int i = threadIdx.x;
+    const int e = P.tk_idx[i];
+    const int a = -sm.cnt[e] - 1;
+    // rank of this slot among the slots routed to e (ascending slot index)
+    int rank = 0;
+    for (int k = 0; k < i; ++k) rank += P.tk_idx[k] == e;
+    R[4 + 2 * E + a * B + rank] = i;
+  }
+}
+
+__device__ __forceinline__ int claim(const mk_params& P, int32_t c, Smem& sm) {
+  if (threadIdx.x == 0)
+    sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int id = sm.claim;
+  __syncthreads();
+  return id;
+}
+
+// Expert up/gate + SiLU-and-multiply, claiming (expert, panel pair) items
+// from the queue ROUTER_TOPK built (megakernel post, section "Tasks":
+// MOE_UPGATE_ACT_DRAIN, and the scheduler section of the Chinese version:
+// claimers atomically take the next queue entry until it is empty).
+template <int NCH>
+__device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
+  const int E = P.E, F = P.F;
+  const int kc = P.H / 32;
+  const size_t pstride = (size_t)kc * 512;
+  const int* R = P.route;
+  const int n_items = R[1];
+  for (;;) {
+    if (ld_relaxed(&P.err[0]) != 0) return;
+    const int id = claim(P, claim_ctr, sm);
+    if (id >= n_items) break;
+    const int a = id / P.up_items_per_expert, tt = id % P.up_items_per_expert;
+    const int e = R[4 + a];
+    WTile<2, NCH> w;
+    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride, 2, 0, kc);
+    const int cnt = R[4 + E + a];
+    for (int r = 0; r < cnt; ++r) {
+      const int slot = R[4 + 2 * E + a * P.B + r];
+      const int b = slot / P.K;
+      gemv_b1(w, P.xn + (size_t)b * P.H, 2, 0, kc, sm);
+      if (threadIdx.x < 16) {
+        const float gt = sm.out[threadIdx.x], up = sm.out[16 + threadIdx.x];
+        P.u[(size_t)slot * F + tt * 16 + threadIdx.x] = gt / (1.0f + __expf(-gt)) * up;
+      }
+    }
+    signal_counter(P, done_base + a);
+  }
+}
+
+// Expert down, claiming (expert, panel group) items. The weights are loaded
+// before waiting for that expert's up/gate items (megakernel post, section
+// "What we have done differently": MoE down streams its weights while
+// up/gate still computes the hidden state it consumes).
+template <int NCH>
+__device__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
+  const int E = P.E, F = P.F, H = P.H;
+  const int kc = F / 32;
+  const size_t pstride = (size_t)kc * 512;
+  const int DP = P.down_panels_per_item;
+  const int* R = P.route;
+  const int n_items = R[2];
+  for (;;) {
+    if (ld_relaxed(&P.err[0]) != 0) return;
+    const int id = claim(P, claim_ctr, sm);
+    if (id >= n_items) break;
+    const int a = id / P.down_items_per_expert, tt = id % P.down_items_per_expert;
+    const int e = R[4 + a];
+    WTile<4, NCH> w;
+    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(tt * DP) * pstride, pstride, DP, 0, kc);
+    if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
+    const int cnt = R[4 + E + a];
+    for (int r = 0; r < cnt; ++r) {
+      const int slot = R[4 + 2 * E + a * P.B + r];
+      gemv_b1(w, P.u + (size_t)slot * F, DP, 0, kc, sm);
+      if (threadIdx.x < DP * 16) P.dn[(size_t)slot * H + tt * DP * 16 + threadIdx.x] = sm.out[threadIdx.x];
+    }
+  }
+}
+
+// ----------------------------------------------------------------- LM head
+template <int NCH>
+__device__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int p0 = t.a[0], np = t.a[1], ord = t.a[2];
+  const int kc = P.H / 32;
+  const size_t pstride = (size_t)kc * 512;
+  WTile<2, NCH> w;
+  wtile_load(w, P.wlm + (size_t)p0 * pstride, pstride, np, 0, kc);
+  if (!wait_task(P, t, sm)) return;
+  for (int b = 0; b < P.B; ++b) {
+    gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
+    if (wave_id() == 0) {
+      const int tid = threadIdx.x;
+      float v = kNegInf;
+      int ix = 0x7fffffff;
+      if (tid < np * 16) {
+        v = sm.out[tid];
+        ix = p0 * 16 + tid;
+        P.logits[(size_t)b * P.V + ix] = v;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(v, o);
+        const int oi = __shfl_xor(ix, o);
+        if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
+      }
+      if (tid == 0) {
+        P.lm_val[b * P.n_lm_tasks + ord] = v;
+        P.lm_arg[b * P.n_lm_tasks + ord] = ix;
+      }
+    }
+  }
+}
+
+// Greedy token: the largest logit, the lowest index on ties (tiny-vllm
+// walkthrough, section "The remaining layers and logits").
+__device__ void op_argmax(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int b = t.a[0], n = P.n_lm_tasks;
+  float v = kNegInf;
+  int ix = 0x7fffffff;
+  for (int i = threadIdx.x; i < n; i += MK_WG_THREADS) {
+    const float cv = P.lm_val[b * n + i];
+    const int ci = P.lm_arg[b * n + i];
+    if (cv > v || (cv == v && ci < ix)) { v = cv; ix = ci; }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(v, o);
+    const int oi = __shfl_xor(ix, o);
+    if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
+  }
+  if (lane_id() == 0) {
+    sm.vred[wave_id()] = v;
+    sm.ired[wave_id()] = ix;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 0; k < MK_WAVES; ++k)
+      if (sm.vred[k] > v || (sm.vred[k] == v && sm.ired[k] < ix)) { v = sm.vred[k]; ix = sm.ired[k]; }
+    if (P.next_tokens) P.next_tokens[b] = ix;
+    if (P.flags & 1u) {
+      P.tokens[b] = ix;
+      P.seq_lens[b] = P.seq_lens[b] + 1;
+    }
+  }
+}
+
+// --------------------------------------------------------------- dispatch
+
+template <int D>
+__device__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
+  switch (t.op) {
+    case MK_OP_NORM: op_norm(P, t, sm); break;
+    case MK_OP_QKV: op_qkv<8>(P, t, sm); break;
+    case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
+    case MK_OP_ATTN_COMBINE: op_attn_combine(P, t, sm); break;
+    case MK_OP_OPROJ: op_oproj<4>(P, t, sm); break;
+    case MK_OP_ROUTER: op_router<8>(P, t, sm); break;
+    case MK_OP_TOPK: op_topk(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe_up<8>(P, t, sm); break;
+    case MK_OP_MOE_DOWN: op_moe_down<3>(P, t, sm); break;
+    case MK_OP_LMHEAD: op_lmhead<8>(P, t, sm); break;
+    case MK_OP_ARGMAX: op_argmax(P, t, sm); break;
+    default: wait_task(P, t, sm); break;
+  }
+}
+
+}  // namespace
+
+// The interpreter: workgroup i runs tasks [task_off[i], task_off[i+1]).
+template <int D>
+__global__ __launch_bounds__(MK_WG_THREADS) void mk_interp(mk_params P) {
+  __shared__ Smem sm;
+  if (P.ctr_clear) {
+    for (int i = blockIdx.x * MK_WG_THREADS + threadIdx.x; i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
+      P.ctr_clear[i] = 0u;
+  }
+  const int beg = P.task_off[blockIdx.x], end = P.task_off[blockIdx.x + 1];
+  for (int i = beg; i < end; ++i) {
+    const mk_task& t = P.tasks[i];
+    run_task<D>(P, t, sm);
+    if (t.sig_ctr[0] >= 0) signal_counter(P, t.sig_ctr[0]);
+    if (t.sig_ctr[1] >= 0) signal_counter(P, t.sig_ctr[1]);
+    __syncthreads();
+  }
+}
+
+template __global__ void mk_interp<64>(mk_params);
+template __global__ void mk_interp<128>(mk_params);
+
+// ------------------------------------------------------------- repacking
+// Canonical row-major [K x N] (leading dimension ld) -> panel-tiled layout,
+// source panel j written to destination panel dst0 + j*dstep. One workgroup
+// per (32-row chunk, 512-column block, batch index z); z strides both sides.
+extern "C" __global__ __launch_bounds__(256) void mk_repack_panels(const uint16_t* src, uint16_t* dst,
+                                                                   int K, int N, int ld, int dst0, int dstep,
+                                                                   size_t src_zstride, size_t dst_zstride) {
+  __shared__ uint16_t tile[32][512 + 8];
+  const int c = blockIdx.x;           // chunk row
+  const int n0 = blockIdx.y * 512;    // first column
+  const int z = blockIdx.z;
+  const int width = min(512, N - n0);
+  const uint16_t* s = src + z * src_zstride;
+  uint16_t* d = dst + z * dst_zstride;
+  const int kc = K / 32;
+  for (int idx = threadIdx.x; idx < 32 * (width / 8); idx += 256) {
+    const int row = idx / (width / 8), c8 = idx % (width / 8);
+    const uint4 v = *(const uint4*)(s + (size_t)(32 * c + row) * ld + n0 + c8 * 8);
+    *(uint4*)&tile[row][c8 * 8] = v;
+  }
+  __syncthreads();
+  const int npan = width / 16;
+  for (int idx = threadIdx.x; idx < npan * 64; idx += 256) {
+    const int j = idx / 64, l = idx % 64;
+    uint16_t tmp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tmp[i] = tile[8 * (l >> 4) + i][16 * j + (l & 15)];
+    const int pj = dst0 + (n0 / 16 + j) * dstep;
+    *(uint4*)(d + ((size_t)pj * kc + c) * 512 + l * 8) = *(uint4*)tmp;
+  }
+}
+
+// ------------------------------------------------------------ host launch
+#include "mk_launch.h"
+
+hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool cooperative, hipStream_t stream) {
+  const void* fn = head_dim == 64 ? (const void*)mk_interp<64> : (const void*)mk_interp<128>;
+  void* args[] = {(void*)&P};
+  if (cooperative)
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(MK_WG_THREADS), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(MK_WG_THREADS), args, 0, stream);
+}
+
+hipError_t mk_launch_repack(const uint16_t* src, uint16_t* dst, int K, int N, int ld, int dst0, int dstep,
+                            int nz, size_t src_zstride, size_t dst_zstride, hipStream_t stream) {
+  dim3 grid(K / 32, (N + 511) / 512, nz);
+  hipLaunchKernelGGL(mk_repack_panels, grid, dim3(256), 0, stream, src, dst, K, N, ld, dst0, dstep, src_zstride,
+                     dst_zstride);
+  return hipGetLastError();
+}
+
+hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu) {
+  const void* fn = head_dim == 64 ? (const void*)mk_interp<64> : (const void*)mk_interp<128>;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, MK_WG_THREADS, 0);
+}

@@ -1,0 +1,1023 @@
+// mk_host.cpp - the C ABI: handle, weight repacking, schedule building and
+// caching, the decode-step launch, and a host model of the schedule.
+//
+// Scheduling follows Cohere's North Mini Code megakernel post (Chinese
+// version, task-scheduler section): the host builds named waves per layer,
+// orders them (qkv -> router -> top-k -> attention -> MoE up/down -> O-proj ->
+// RMSNorm), flattens them into one list and places task k on compute unit
+// k mod n_cu; attention and MoE work whose size is only known at run time is
+// taken by a fixed number of claimer tasks from shared queues. Schedules are
+// prebuilt per (batch, context bucket) and picked at each step (engine
+// section: select_schedule(max_live_context()) before every launch).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+#include "mk_launch.h"
+
+namespace {
+
+thread_local std::string g_create_error;
+
+// ------------------------------------------------------------------ schedule
+
+struct Schedule {
+  int B = 0, bucket = 0;
+  int n_splits_full = 0, n_splits_win = 0, pps = 16;
+  int n_qkv_tasks_per_group = 0;
+  int n_router = 0, n_oproj = 0, n_up_claimers = 0, n_down_claimers = 0, n_lm = 0;
+  int n_ctr = 0;
+  // counter layout
+  int c_norm0 = 0, c_lm = 0, c_layer0 = 0, c_per_layer = 0;
+  // flattened list, its waves (for kernel-per-op) and per-CU lists
+  std::vector<mk_task> flat;
+  std::vector<int> flat_wave;
+  std::vector<mk_task> cu_tasks;
+  std::vector<int32_t> cu_off;
+  std::vector<std::pair<int, int>> waves;  // [begin, end) into flat
+  // device copies
+  mk_task* d_cu_tasks = nullptr;
+  int32_t* d_cu_off = nullptr;
+  mk_task* d_flat = nullptr;
+};
+
+struct CtrIdx {
+  int qkv, attn, comb, oproj, router, route, up_claim, down_claim, down_exit, up_done;
+};
+
+mk_task make_task(int op, int layer) {
+  mk_task t;
+  std::memset(&t, 0, sizeof(t));
+  t.op = op;
+  t.layer = layer;
+  for (int i = 0; i < 3; ++i) {
+    t.wait_ctr[i] = -1;
+    t.wait_tgt[i] = 0;
+  }
+  t.sig_ctr[0] = t.sig_ctr[1] = -1;
+  return t;
+}
+
+void add_wait(mk_task& t, int c, int tgt) {
+  for (int i = 0; i < 3; ++i)
+    if (t.wait_ctr[i] < 0) {
+      t.wait_ctr[i] = c;
+      t.wait_tgt[i] = tgt;
+      return;
+    }
+  std::abort();
+}
+
+}  // namespace
+
+struct mk_handle {
+  mk_config cfg{};
+  int device = 0;
+  bool host_only = false;
+  int n_cu = 0;
+  std::string err;
+  // derived
+  int G = 0, qkv_dim = 0, q_dim = 0, kv_dim = 0, e_pad = 0;
+  int max_splits = 0, pps = 16, down_panels = 4, n_lm_tasks = 0, lm_np = 2;
+  // device memory
+  uint16_t* w_all = nullptr;
+  size_t s_wqkv = 0, s_wo = 0, s_wr = 0, s_wgu_l = 0, s_wgu_e = 0, s_wd_l = 0, s_wd_e = 0;
+  uint16_t *emb = nullptr, *gamma = nullptr, *wqkv = nullptr, *wo = nullptr, *wr = nullptr, *wgu = nullptr,
+           *wd = nullptr, *wlm = nullptr;
+  float* rope = nullptr;
+  uint16_t* kv = nullptr;
+  void* scratch = nullptr;
+  float *h = nullptr, *xn = nullptr, *q = nullptr, *part = nullptr, *o = nullptr, *ao = nullptr, *r = nullptr,
+        *tk_w = nullptr, *u = nullptr, *dn = nullptr, *lm_val = nullptr;
+  int32_t *tk_idx = nullptr, *route = nullptr, *lm_arg = nullptr;
+  uint32_t* ctr[2] = {nullptr, nullptr};
+  int n_ctr_cap = 0;
+  uint32_t* err_word = nullptr;
+  int32_t* wg_off_identity = nullptr;  // 0..max_tasks for kernel-per-op launches
+  int identity_len = 0;
+  std::vector<bool> layer_loaded;
+  bool globals_loaded = false;
+  uint64_t steps = 0;
+  int64_t timeout_ticks = 200000000;  // 2 s at 100 MHz
+  int32_t* tk_trace = nullptr;
+  std::map<std::pair<int, int>, std::unique_ptr<Schedule>> scheds;
+};
+
+namespace {
+
+mk_status fail(mk_handle* h, mk_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (h)
+    h->err = buf;
+  else
+    g_create_error = buf;
+  return st;
+}
+
+#define HIPCHECK(h, call)                                                                    \
+  do {                                                                                       \
+    hipError_t e_ = (call);                                                                  \
+    if (e_ != hipSuccess) return fail((h), MK_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+mk_status validate_config(const mk_config* c) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null config");
+  if (c->hidden <= 0 || c->hidden % 256 || c->hidden > 2048)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "hidden must be a multiple of 256 and <= 2048");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(nullptr, MK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G > 16 || G * c->head_dim > 1024)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "group size must be <= 16 and group width <= 1024");
+  if (c->n_experts <= 0 || c->n_experts % 8 || c->n_experts > 128)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "n_experts must be a multiple of 8, <= 128");
+  if (c->top_k <= 0 || c->top_k > MK_MAX_TOPK || c->top_k > c->n_experts)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "top_k must be in [1, 8]");
+  if (c->expert_ffn <= 0 || c->expert_ffn % 128 || c->expert_ffn > 768)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "expert_ffn must be a multiple of 128, <= 768");
+  if (c->vocab <= 0 || c->vocab % 16) return fail(nullptr, MK_ERR_UNSUPPORTED, "vocab must be a multiple of 16");
+  if (c->n_layers <= 0) return fail(nullptr, MK_ERR_INVALID_ARG, "n_layers must be positive");
+  if (c->page_size != 16) return fail(nullptr, MK_ERR_UNSUPPORTED, "page_size must be 16");
+  if (c->window < 0 || c->full_every < 1) return fail(nullptr, MK_ERR_INVALID_ARG, "bad window pattern");
+  if (c->max_batch < 1 || c->max_batch > 32) return fail(nullptr, MK_ERR_UNSUPPORTED, "max_batch must be in [1, 32]");
+  if (c->max_seq_len < 1) return fail(nullptr, MK_ERR_INVALID_ARG, "max_seq_len must be positive");
+  if (c->max_pages_per_seq < ceil_div(c->max_seq_len, c->page_size))
+    return fail(nullptr, MK_ERR_INVALID_ARG, "max_pages_per_seq too small for max_seq_len");
+  if (c->n_pages < 1) return fail(nullptr, MK_ERR_INVALID_ARG, "n_pages must be positive");
+  if (c->mode != MK_MODE_MEGAKERNEL && c->mode != MK_MODE_KERNEL_PER_OP)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "unknown mode");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(nullptr, MK_ERR_INVALID_ARG, "bad eps/theta");
+  return MK_OK;
+}
+
+void derive(mk_handle* h) {
+  const mk_config& c = h->cfg;
+  h->G = c.n_q_heads / c.n_kv_heads;
+  h->q_dim = c.n_q_heads * c.head_dim;
+  h->kv_dim = c.n_kv_heads * c.head_dim;
+  h->qkv_dim = h->q_dim + 2 * h->kv_dim;
+  h->e_pad = ceil_div(c.n_experts, 16) * 16;  // router columns padded to whole panels
+  h->pps = 16;
+  const int pages = ceil_div(c.max_seq_len, c.page_size) + 1;
+  h->max_splits = ceil_div(pages, h->pps);
+  h->down_panels = 4;
+  h->lm_np = 2;
+  h->n_lm_tasks = ceil_div(c.vocab / 16, h->lm_np);
+}
+
+int window_of(const mk_config& c, int l) {
+  if (c.window == 0) return 0;
+  return (l % c.full_every) == c.full_every - 1 ? 0 : c.window;
+}
+
+// Number of attention splits for a layer when sequences are at most `len` long.
+int splits_for(const mk_handle* h, int l, int len) {
+  const int win = window_of(h->cfg, l);
+  const int keys = win ? std::min(win, len) : len;
+  const int pages = ceil_div(keys, h->cfg.page_size) + 1;  // a window may straddle one extra page
+  return std::min(ceil_div(pages, h->pps), h->max_splits);
+}
+
+int bucket_of(int hint) { return ceil_div(hint, 256) * 256; }
+
+std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
+  const mk_config& c = h->cfg;
+  auto S = std::make_unique<Schedule>();
+  S->B = B;
+  S->bucket = std::min(bucket_of(hint), c.max_seq_len);
+  S->pps = h->pps;
+  const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts, H = c.hidden;
+  const int n_cu = h->n_cu;
+  const int router_panels = h->e_pad / 16;
+
+  // counter layout
+  int idx = 0;
+  S->c_norm0 = idx;
+  idx += L + 1;
+  S->c_lm = idx++;
+  S->c_layer0 = idx;
+  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + 1 + 1 + E;
+  idx += L * S->c_per_layer;
+  S->n_ctr = idx;
+  auto ci = [&](int l) {
+    CtrIdx x;
+    int b0 = S->c_layer0 + l * S->c_per_layer;
+    x.qkv = b0;
+    b0 += KVH;
+    x.attn = b0;
+    b0 += B * KVH;
+    x.comb = b0;
+    b0 += KVH;
+    x.oproj = b0++;
+    x.router = b0++;
+    x.route = b0++;
+    x.up_claim = b0++;
+    x.down_claim = b0++;
+    x.down_exit = b0++;
+    x.up_done = b0;
+    return x;
+  };
+
+  auto begin_wave = [&]() { S->waves.push_back({(int)S->flat.size(), (int)S->flat.size()}); };
+  auto push = [&](const mk_task& t) {
+    S->flat.push_back(t);
+    S->flat_wave.push_back((int)S->waves.size() - 1);
+    S->waves.back().second = (int)S->flat.size();
+  };
+
+  S->n_up_claimers = n_cu;
+  S->n_down_claimers = n_cu;
+  const int qkv_np = 1, oproj_np = 2, router_np = 1;
+
+  // layer-0 input: embedding + RMSNorm
+  begin_wave();
+  for (int b = 0; b < B; ++b) {
+    mk_task t = make_task(MK_OP_NORM, 0);
+    t.a[0] = b;
+    t.sig_ctr[0] = S->c_norm0 + 0;
+    push(t);
+  }
+  for (int l = 0; l < L; ++l) {
+    const CtrIdx x = ci(l);
+    const int norm_c = S->c_norm0 + l;
+    // qkv, per kv group: its q heads, its k head, its v head
+    begin_wave();
+    std::vector<int> n_qkv(KVH, 0);
+    for (int g = 0; g < KVH; ++g) {
+      const int ranges[3][2] = {{g * h->G * c.head_dim / 16, (g + 1) * h->G * c.head_dim / 16},
+                                {(h->q_dim + g * c.head_dim) / 16, (h->q_dim + (g + 1) * c.head_dim) / 16},
+                                {(h->q_dim + h->kv_dim + g * c.head_dim) / 16,
+                                 (h->q_dim + h->kv_dim + (g + 1) * c.head_dim) / 16}};
+      for (auto& rg : ranges)
+        for (int p = rg[0]; p < rg[1]; p += qkv_np) ++n_qkv[g];
+    }
+    for (int g = 0; g < KVH; ++g) {
+      const int ranges[3][2] = {{g * h->G * c.head_dim / 16, (g + 1) * h->G * c.head_dim / 16},
+                                {(h->q_dim + g * c.head_dim) / 16, (h->q_dim + (g + 1) * c.head_dim) / 16},
+                                {(h->q_dim + h->kv_dim + g * c.head_dim) / 16,
+                                 (h->q_dim + h->kv_dim + (g + 1) * c.head_dim) / 16}};
+      for (auto& rg : ranges)
+        for (int p = rg[0]; p < rg[1]; p += qkv_np) {
+          mk_task t = make_task(MK_OP_QKV, l);
+          t.a[0] = p;
+          t.a[1] = std::min(qkv_np, rg[1] - p);
+          t.a[2] = g;
+          add_wait(t, norm_c, B);
+          t.sig_ctr[0] = x.qkv + g;
+          push(t);
+        }
+    }
+    S->n_qkv_tasks_per_group = n_qkv[0];
+    // router
+    begin_wave();
+    int n_router = 0;
+    for (int p = 0; p < router_panels; p += router_np) {
+      mk_task t = make_task(MK_OP_ROUTER, l);
+      t.a[0] = p;
+      t.a[1] = std::min(router_np, router_panels - p);
+      add_wait(t, norm_c, B);
+      t.sig_ctr[0] = x.router;
+      push(t);
+      ++n_router;
+    }
+    S->n_router = n_router;
+    // top-k + route finalize
+    begin_wave();
+    {
+      mk_task t = make_task(MK_OP_TOPK, l);
+      add_wait(t, x.router, n_router);
+      t.sig_ctr[0] = x.route;
+      push(t);
+    }
+    // attention splits
+    begin_wave();
+    const int ns = splits_for(h, l, S->bucket);
+    if (window_of(c, l))
+      S->n_splits_win = ns;
+    else
+      S->n_splits_full = ns;
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < KVH; ++g)
+        for (int s = 0; s < ns; ++s) {
+          mk_task t = make_task(MK_OP_ATTN, l);
+          t.a[0] = b;
+          t.a[1] = g;
+          t.a[2] = s;
+          t.a[3] = ns;
+          t.a[4] = h->pps;
+          add_wait(t, x.qkv + g, n_qkv[g]);
+          t.sig_ctr[0] = x.attn + b * KVH + g;
+          push(t);
+        }
+    // MoE up/gate claimers
+    begin_wave();
+    for (int i = 0; i < S->n_up_claimers; ++i) {
+      mk_task t = make_task(MK_OP_MOE_UP, l);
+      t.a[0] = x.up_claim;
+      t.a[1] = x.up_done;
+      add_wait(t, x.route, 1);
+      push(t);
+    }
+    // MoE down claimers
+    begin_wave();
+    for (int i = 0; i < S->n_down_claimers; ++i) {
+      mk_task t = make_task(MK_OP_MOE_DOWN, l);
+      t.a[0] = x.down_claim;
+      t.a[1] = x.up_done;
+      add_wait(t, x.route, 1);
+      t.sig_ctr[0] = x.down_exit;
+      push(t);
+    }
+    // attention combine
+    begin_wave();
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < KVH; ++g) {
+        mk_task t = make_task(MK_OP_ATTN_COMBINE, l);
+        t.a[0] = b;
+        t.a[1] = g;
+        t.a[2] = ns;
+        add_wait(t, x.attn + b * KVH + g, ns);
+        t.sig_ctr[0] = x.comb + g;
+        push(t);
+      }
+    // O projection, split-K per kv group
+    begin_wave();
+    int n_oproj = 0;
+    for (int g = 0; g < KVH; ++g)
+      for (int p = 0; p < H / 16; p += oproj_np) {
+        mk_task t = make_task(MK_OP_OPROJ, l);
+        t.a[0] = g;
+        t.a[1] = p;
+        t.a[2] = std::min(oproj_np, H / 16 - p);
+        add_wait(t, x.comb + g, B);
+        t.sig_ctr[0] = x.oproj;
+        push(t);
+        ++n_oproj;
+      }
+    S->n_oproj = n_oproj;
+    // residual + RMSNorm -> next layer's input (or the final norm)
+    begin_wave();
+    for (int b = 0; b < B; ++b) {
+      mk_task t = make_task(MK_OP_NORM, l + 1);
+      t.a[0] = b;
+      add_wait(t, x.oproj, n_oproj);
+      add_wait(t, x.down_exit, S->n_down_claimers);
+      t.sig_ctr[0] = S->c_norm0 + l + 1;
+      push(t);
+    }
+  }
+  // LM head + greedy token
+  begin_wave();
+  S->n_lm = 0;
+  for (int p = 0, ord = 0; p < c.vocab / 16; p += h->lm_np, ++ord) {
+    mk_task t = make_task(MK_OP_LMHEAD, L);
+    t.a[0] = p;
+    t.a[1] = std::min(h->lm_np, c.vocab / 16 - p);
+    t.a[2] = ord;
+    add_wait(t, S->c_norm0 + L, B);
+    t.sig_ctr[0] = S->c_lm;
+    push(t);
+    ++S->n_lm;
+  }
+  begin_wave();
+  for (int b = 0; b < B; ++b) {
+    mk_task t = make_task(MK_OP_ARGMAX, L);
+    t.a[0] = b;
+    add_wait(t, S->c_lm, S->n_lm);
+    push(t);
+  }
+
+  // round-robin placement of the flattened list
+  std::vector<std::vector<mk_task>> per(n_cu);
+  for (size_t k = 0; k < S->flat.size(); ++k) per[k % n_cu].push_back(S->flat[k]);
+  S->cu_off.assign(n_cu + 1, 0);
+  for (int i = 0; i < n_cu; ++i) {
+    S->cu_off[i + 1] = S->cu_off[i] + (int)per[i].size();
+    S->cu_tasks.insert(S->cu_tasks.end(), per[i].begin(), per[i].end());
+  }
+  return S;
+}
+
+// Host model of the device: per-CU in-order lists, counters, claim queues.
+struct SimCU {
+  int pos = 0;
+  // claimer state
+  bool in_claimer = false;
+  int pending_item = -1;  // claimed down item waiting for its expert's up items
+};
+
+mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uint64_t seed, int corrupt,
+                   std::string& rep) {
+  const mk_config& c = h->cfg;
+  const int n_cu = h->n_cu, L = c.n_layers, E = c.n_experts, KVH = c.n_kv_heads;
+  const int F = c.expert_ffn, H = c.hidden;
+  const int up_per_e = F / 16, down_per_e = H / 16 / h->down_panels;
+  std::vector<mk_task> tasks = S.cu_tasks;
+  if (corrupt >= 0 && corrupt < (int)tasks.size()) {
+    // make the first wait of that task unsatisfiable by one arrival
+    for (int i = 0; i < 3; ++i)
+      if (tasks[corrupt].wait_ctr[i] >= 0) {
+        tasks[corrupt].wait_tgt[i] += 1;
+        break;
+      }
+  }
+  std::vector<int64_t> ctr(S.n_ctr, 0);
+  std::vector<SimCU> cu(n_cu);
+  std::mt19937_64 rng(seed);
+  auto layer_of_claim = [&](int counter) { return (counter - S.c_layer0) / S.c_per_layer; };
+  auto waits_met = [&](const mk_task& t) {
+    for (int i = 0; i < 3; ++i)
+      if (t.wait_ctr[i] >= 0 && ctr[t.wait_ctr[i]] < t.wait_tgt[i]) return false;
+    return true;
+  };
+  int64_t remaining = (int64_t)tasks.size();
+  std::vector<int> order(n_cu);
+  for (int i = 0; i < n_cu; ++i) order[i] = i;
+  while (remaining > 0) {
+    bool progress = false;
+    std::shuffle(order.begin(), order.end(), rng);
+    for (int k : order) {
+      SimCU& u = cu[k];
+      const int beg = S.cu_off[k], end = S.cu_off[k + 1];
+      if (beg + u.pos >= end) continue;
+      const mk_task& t = tasks[beg + u.pos];
+      if (!u.in_claimer) {
+        if (!waits_met(t)) continue;
+        if (t.op == MK_OP_MOE_UP || t.op == MK_OP_MOE_DOWN) {
+          u.in_claimer = true;
+          progress = true;
+          continue;
+        }
+        for (int i = 0; i < 2; ++i)
+          if (t.sig_ctr[i] >= 0) ctr[t.sig_ctr[i]]++;
+        u.pos++;
+        remaining--;
+        progress = true;
+        continue;
+      }
+      // claimer step
+      const int l = layer_of_claim(t.a[0]);
+      const int na = n_active[l];
+      if (t.op == MK_OP_MOE_UP) {
+        const int id = (int)ctr[t.a[0]]++;
+        if (id >= na * up_per_e) {
+          u.in_claimer = false;
+          for (int i = 0; i < 2; ++i)
+            if (t.sig_ctr[i] >= 0) ctr[t.sig_ctr[i]]++;
+          u.pos++;
+          remaining--;
+        } else {
+          ctr[t.a[1] + id / up_per_e]++;
+        }
+        progress = true;
+      } else {
+        if (u.pending_item < 0) {
+          const int id = (int)ctr[t.a[0]]++;
+          progress = true;
+          if (id >= na * down_per_e) {
+            u.in_claimer = false;
+            for (int i = 0; i < 2; ++i)
+              if (t.sig_ctr[i] >= 0) ctr[t.sig_ctr[i]]++;
+            u.pos++;
+            remaining--;
+          } else {
+            u.pending_item = id;
+          }
+        } else {
+          const int a = u.pending_item / down_per_e;
+          if (ctr[t.a[1] + a] >= up_per_e) {
+            u.pending_item = -1;
+            progress = true;
+          }
+        }
+      }
+    }
+    if (!progress) {
+      char buf[256];
+      snprintf(buf, sizeof(buf), "deadlock: %lld tasks left", (long long)remaining);
+      rep = buf;
+      return MK_ERR_DEVICE_TIMEOUT;
+    }
+  }
+  // final counter values against their expected arrivals
+  const int B = S.B;
+  std::vector<int64_t> want(S.n_ctr, 0);
+  for (int l = 0; l <= L; ++l) want[S.c_norm0 + l] = B;
+  want[S.c_lm] = S.n_lm;
+  for (int l = 0; l < L; ++l) {
+    const int b0 = S.c_layer0 + l * S.c_per_layer;
+    const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
+    int k = b0;
+    for (int g = 0; g < KVH; ++g) want[k++] = (h->qkv_dim / 16) / KVH;
+    for (int i = 0; i < B * KVH; ++i) want[k++] = ns;
+    for (int g = 0; g < KVH; ++g) want[k++] = B;
+    want[k++] = (int64_t)KVH * (H / 16 / 2);  // oproj tiles, 2 panels each
+    want[k++] = h->e_pad / 16;              // router tiles
+    want[k++] = 1;                          // route finalize
+    want[k++] = (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
+    want[k++] = (int64_t)n_active[l] * down_per_e + S.n_down_claimers;
+    want[k++] = S.n_down_claimers;
+    for (int a = 0; a < E; ++a) want[k++] = a < n_active[l] ? up_per_e : 0;
+  }
+  for (int i = 0; i < S.n_ctr; ++i)
+    if (ctr[i] != want[i]) {
+      char buf[256];
+      snprintf(buf, sizeof(buf), "counter %d ended at %lld, expected %lld", i, (long long)ctr[i], (long long)want[i]);
+      rep = buf;
+      return MK_ERR_STATE;
+    }
+  rep = "ok";
+  return MK_OK;
+}
+
+mk_status get_schedule(mk_handle* h, int B, int hint, Schedule** out) {
+  const int bucket = std::min(bucket_of(hint), h->cfg.max_seq_len);
+  auto key = std::make_pair(B, bucket);
+  auto it = h->scheds.find(key);
+  if (it == h->scheds.end()) {
+    auto S = build_schedule(h, B, hint);
+    if (S->n_ctr > h->n_ctr_cap && !h->host_only)
+      return fail(h, MK_ERR_UNSUPPORTED, "schedule needs %d counters, capacity %d", S->n_ctr, h->n_ctr_cap);
+    if (!h->host_only) {
+      HIPCHECK(h, hipSetDevice(h->device));
+      HIPCHECK(h, hipMalloc(&S->d_cu_tasks, S->cu_tasks.size() * sizeof(mk_task)));
+      HIPCHECK(h, hipMemcpy(S->d_cu_tasks, S->cu_tasks.data(), S->cu_tasks.size() * sizeof(mk_task),
+                            hipMemcpyHostToDevice));
+      HIPCHECK(h, hipMalloc(&S->d_cu_off, S->cu_off.size() * sizeof(int32_t)));
+      HIPCHECK(h, hipMemcpy(S->d_cu_off, S->cu_off.data(), S->cu_off.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+      HIPCHECK(h, hipMalloc(&S->d_flat, S->flat.size() * sizeof(mk_task)));
+      HIPCHECK(h, hipMemcpy(S->d_flat, S->flat.data(), S->flat.size() * sizeof(mk_task), hipMemcpyHostToDevice));
+      int longest = 0;
+      for (auto& w : S->waves) longest = std::max(longest, w.second - w.first);
+      if (longest + 1 > h->identity_len) {
+        if (h->wg_off_identity) hipFree(h->wg_off_identity);
+        std::vector<int32_t> id(longest + 1);
+        for (int i = 0; i <= longest; ++i) id[i] = i;
+        HIPCHECK(h, hipMalloc(&h->wg_off_identity, id.size() * sizeof(int32_t)));
+        HIPCHECK(h, hipMemcpy(h->wg_off_identity, id.data(), id.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+        h->identity_len = (int)id.size();
+      }
+    }
+    it = h->scheds.emplace(key, std::move(S)).first;
+  }
+  *out = it->second.get();
+  return MK_OK;
+}
+
+void free_schedule(Schedule* S) {
+  if (S->d_cu_tasks) hipFree(S->d_cu_tasks);
+  if (S->d_cu_off) hipFree(S->d_cu_off);
+  if (S->d_flat) hipFree(S->d_flat);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+const char* mk_last_error(const mk_handle* h) { return h ? h->err.c_str() : g_create_error.c_str(); }
+
+static mk_status create_common(const mk_config* cfg, mk_handle** out) {
+  if (!out) return fail(nullptr, MK_ERR_INVALID_ARG, "null out");
+  *out = nullptr;
+  mk_status st = validate_config(cfg);
+  if (st != MK_OK) return st;
+  return MK_OK;
+}
+
+mk_status mk_create_host_only(const mk_config* cfg, int n_cus, mk_handle** out) {
+  mk_status st = create_common(cfg, out);
+  if (st != MK_OK) return st;
+  if (n_cus < 1 || n_cus > MK_MAX_CUS) return fail(nullptr, MK_ERR_INVALID_ARG, "n_cus out of range");
+  auto* h = new mk_handle();
+  h->cfg = *cfg;
+  h->host_only = true;
+  h->n_cu = n_cus;
+  derive(h);
+  *out = h;
+  return MK_OK;
+}
+
+mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, int device, mk_handle** out) {
+  mk_status st = create_common(cfg, out);
+  if (st != MK_OK) return st;
+  const mk_config& c = *cfg;
+  const size_t kv_want = (size_t)c.n_layers * c.n_pages * 2 * c.n_kv_heads * c.page_size * c.head_dim * 2;
+  if (!kv_pool || kv_pool_bytes != kv_want)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "kv_pool must be %zu bytes (got %zu)", kv_want, kv_pool_bytes);
+  if ((uintptr_t)kv_pool % 16) return fail(nullptr, MK_ERR_INVALID_ARG, "kv_pool must be 16-byte aligned");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "no HIP device %d", device);
+  auto h = std::make_unique<mk_handle>();
+  h->cfg = c;
+  h->device = device;
+  derive(h.get());
+  if (hipSetDevice(device) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "hipSetDevice failed");
+  int n_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n_cu < 1)
+    return fail(nullptr, MK_ERR_HIP, "cannot query compute units");
+  int occ = 0;
+  if (mk_interp_occupancy(c.head_dim, &occ) != hipSuccess || occ < 1)
+    return fail(nullptr, MK_ERR_HIP, "interpreter kernel cannot be resident");
+  h->n_cu = std::min(n_cu, MK_MAX_CUS);
+  if (const char* e = std::getenv("MK_TIMEOUT_MS")) h->timeout_ticks = (int64_t)std::atoll(e) * 100000;
+
+  const int L = c.n_layers, H = c.hidden, E = c.n_experts, F = c.expert_ffn, V = c.vocab;
+  // weights
+  h->s_wqkv = (size_t)H * h->qkv_dim;
+  h->s_wo = (size_t)h->q_dim * H;
+  h->s_wr = (size_t)H * h->e_pad;
+  h->s_wgu_e = (size_t)H * 2 * F;
+  h->s_wgu_l = h->s_wgu_e * E;
+  h->s_wd_e = (size_t)F * H;
+  h->s_wd_l = h->s_wd_e * E;
+  size_t off = 0;
+  auto take = [&](size_t elems) {
+    size_t o = off;
+    off += align_up(elems, 256);
+    return o;
+  };
+  const size_t o_emb = take((size_t)V * H), o_gamma = take((size_t)(L + 1) * H), o_wlm = take((size_t)H * V);
+  const size_t o_wqkv = take(h->s_wqkv * L), o_wo = take(h->s_wo * L), o_wr = take(h->s_wr * L);
+  const size_t o_wgu = take(h->s_wgu_l * L), o_wd = take(h->s_wd_l * L);
+  if (hipMalloc(&h->w_all, off * 2) != hipSuccess)
+    return fail(nullptr, MK_ERR_OOM, "cannot allocate %.1f GB of weights", off * 2 / 1e9);
+  h->emb = h->w_all + o_emb;
+  h->gamma = h->w_all + o_gamma;
+  h->wlm = h->w_all + o_wlm;
+  h->wqkv = h->w_all + o_wqkv;
+  h->wo = h->w_all + o_wo;
+  h->wr = h->w_all + o_wr;
+  h->wgu = h->w_all + o_wgu;
+  h->wd = h->w_all + o_wd;
+  h->kv = (uint16_t*)kv_pool;
+  h->layer_loaded.assign(L, false);
+
+  // RoPE table: angle = pos * theta^(-2i/D) in double, cos/sin rounded to float
+  {
+    const int D = c.head_dim;
+    std::vector<float> tab((size_t)c.max_seq_len * D);
+    for (int pos = 0; pos < c.max_seq_len; ++pos)
+      for (int i = 0; i < D / 2; ++i) {
+        const double f = std::pow((double)c.rope_theta, -2.0 * i / D);
+        const double ang = (double)pos * f;
+        tab[((size_t)pos * (D / 2) + i) * 2 + 0] = (float)std::cos(ang);
+        tab[((size_t)pos * (D / 2) + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    if (hipMalloc(&h->rope, tab.size() * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "rope table");
+    if (hipMemcpy(h->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return fail(nullptr, MK_ERR_HIP, "rope upload");
+  }
+
+  // scratch
+  const int Bm = c.max_batch, K = c.top_k, G = h->G, D = c.head_dim, KVH = c.n_kv_heads;
+  size_t so = 0;
+  auto stake = [&](size_t bytes) {
+    size_t o = so;
+    so += align_up(bytes, 256);
+    return o;
+  };
+  const size_t s_h = stake((size_t)Bm * H * 4), s_xn = stake((size_t)Bm * H * 4);
+  const size_t s_q = stake((size_t)Bm * h->q_dim * 4), s_o = stake((size_t)Bm * h->q_dim * 4);
+  const size_t s_part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
+  const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_r = stake((size_t)Bm * E * 4);
+  const size_t s_tki = stake((size_t)Bm * K * 4), s_tkw = stake((size_t)Bm * K * 4);
+  const size_t s_route = stake((size_t)MK_ROUTE_INTS(E, Bm) * 4);
+  const size_t s_u = stake((size_t)Bm * K * F * 4), s_dn = stake((size_t)Bm * K * H * 4);
+  const size_t s_lmv = stake((size_t)Bm * h->n_lm_tasks * 4), s_lma = stake((size_t)Bm * h->n_lm_tasks * 4);
+  const size_t s_err = stake(16);
+  if (hipMalloc(&h->scratch, so) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "scratch");
+  hipMemset(h->scratch, 0, so);
+  char* sb = (char*)h->scratch;
+  h->h = (float*)(sb + s_h);
+  h->xn = (float*)(sb + s_xn);
+  h->q = (float*)(sb + s_q);
+  h->o = (float*)(sb + s_o);
+  h->part = (float*)(sb + s_part);
+  h->ao = (float*)(sb + s_ao);
+  h->r = (float*)(sb + s_r);
+  h->tk_idx = (int32_t*)(sb + s_tki);
+  h->tk_w = (float*)(sb + s_tkw);
+  h->route = (int32_t*)(sb + s_route);
+  h->u = (float*)(sb + s_u);
+  h->dn = (float*)(sb + s_dn);
+  h->lm_val = (float*)(sb + s_lmv);
+  h->lm_arg = (int32_t*)(sb + s_lma);
+  h->err_word = (uint32_t*)(sb + s_err);
+  // counters: capacity for the largest batch
+  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 6 + E);
+  for (int i = 0; i < 2; ++i) {
+    if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
+    hipMemset(h->ctr[i], 0, (size_t)h->n_ctr_cap * 4);
+  }
+  if (hipDeviceSynchronize() != hipSuccess) return fail(nullptr, MK_ERR_HIP, "create sync");
+  *out = h.release();
+  return MK_OK;
+}
+
+void mk_destroy(mk_handle* h) {
+  if (!h) return;
+  if (!h->host_only) {
+    hipSetDevice(h->device);
+    hipDeviceSynchronize();
+    for (auto& kv : h->scheds) free_schedule(kv.second.get());
+    if (h->wg_off_identity) hipFree(h->wg_off_identity);
+    if (h->w_all) hipFree(h->w_all);
+    if (h->rope) hipFree(h->rope);
+    if (h->scratch) hipFree(h->scratch);
+    for (auto* c : h->ctr)
+      if (c) hipFree(c);
+  }
+  delete h;
+}
+
+mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* wqkv, const void* wo, const void* wr,
+                        const void* wg, const void* wu, const void* wd, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  const mk_config& c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!gamma || !wqkv || !wo || !wr || !wg || !wu || !wd) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  for (const void* p : {gamma, wqkv, wo, wr, wg, wu, wd})
+    if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(h, hipSetDevice(h->device));
+  const int H = c.hidden, E = c.n_experts, F = c.expert_ffn;
+  HIPCHECK(h, hipMemcpyAsync(h->gamma + (size_t)layer * H, gamma, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wqkv, h->wqkv + layer * h->s_wqkv, H, h->qkv_dim, h->qkv_dim, 0, 1,
+                               1, 0, 0, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wo, h->wo + layer * h->s_wo, h->q_dim, H, H, 0, 1, 1, 0, 0, s));
+  if (h->e_pad == E) {
+    HIPCHECK(h, mk_launch_repack((const uint16_t*)wr, h->wr + layer * h->s_wr, H, E, E, 0, 1, 1, 0, 0, s));
+  } else {
+    // zero columns pad the router to whole 16-column panels; their logits are never read
+    uint16_t* tmp = nullptr;
+    HIPCHECK(h, hipMallocAsync((void**)&tmp, (size_t)H * h->e_pad * 2, s));
+    HIPCHECK(h, hipMemsetAsync(tmp, 0, (size_t)H * h->e_pad * 2, s));
+    HIPCHECK(h, hipMemcpy2DAsync(tmp, (size_t)h->e_pad * 2, wr, (size_t)E * 2, (size_t)E * 2, H,
+                                 hipMemcpyDeviceToDevice, s));
+    HIPCHECK(h, mk_launch_repack(tmp, h->wr + layer * h->s_wr, H, h->e_pad, h->e_pad, 0, 1, 1, 0, 0, s));
+    HIPCHECK(h, hipFreeAsync(tmp, s));
+  }
+  // gate and up panels interleaved: gate panel j -> 2j, up panel j -> 2j+1
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wg, h->wgu + layer * h->s_wgu_l, H, F, F, 0, 2, E, (size_t)H * F,
+                               h->s_wgu_e, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wu, h->wgu + layer * h->s_wgu_l, H, F, F, 1, 2, E, (size_t)H * F,
+                               h->s_wgu_e, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wd, h->wd + layer * h->s_wd_l, F, H, H, 0, 1, E, (size_t)F * H,
+                               h->s_wd_e, s));
+  h->layer_loaded[layer] = true;
+  return MK_OK;
+}
+
+mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f, const void* wlm, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  if (!emb || !gamma_f || !wlm) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  for (const void* p : {emb, gamma_f, wlm})
+    if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  const mk_config& c = h->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(h, hipSetDevice(h->device));
+  HIPCHECK(h, hipMemcpyAsync(h->emb, emb, (size_t)c.vocab * c.hidden * 2, hipMemcpyDeviceToDevice, s));
+  HIPCHECK(h, hipMemcpyAsync(h->gamma + (size_t)c.n_layers * c.hidden, gamma_f, (size_t)c.hidden * 2,
+                             hipMemcpyDeviceToDevice, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wlm, h->wlm, c.hidden, c.vocab, c.vocab, 0, 1, 1, 0, 0, s));
+  h->globals_loaded = true;
+  return MK_OK;
+}
+
+mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
+  if (!h || !w) return MK_ERR_INVALID_ARG;
+  if (!w->gamma || !w->wqkv || !w->wo || !w->wr || !w->wg || !w->wu || !w->wd)
+    return fail(h, MK_ERR_INVALID_ARG, "null per-layer pointer array");
+  mk_status st = mk_load_globals(h, w->emb, w->gamma_f, w->wlm, stream);
+  if (st != MK_OK) return st;
+  for (int l = 0; l < h->cfg.n_layers; ++l) {
+    st = mk_load_layer(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->wr[l], w->wg[l], w->wu[l], w->wd[l], stream);
+    if (st != MK_OK) return st;
+  }
+  return MK_OK;
+}
+
+static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const int32_t* bt, int32_t* seq_lens,
+                        float* logits, int32_t* next_tokens, uint32_t flags, mk_params& P) {
+  const mk_config& c = h->cfg;
+  std::memset(&P, 0, sizeof(P));
+  P.H = c.hidden;
+  P.QH = c.n_q_heads;
+  P.KVH = c.n_kv_heads;
+  P.D = c.head_dim;
+  P.G = h->G;
+  P.E = c.n_experts;
+  P.K = c.top_k;
+  P.F = c.expert_ffn;
+  P.V = c.vocab;
+  P.L = c.n_layers;
+  P.PS = c.page_size;
+  P.window = c.window;
+  P.full_every = c.full_every;
+  P.eps = c.rms_eps;
+  P.attn_scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  P.B = B;
+  P.mpps = c.max_pages_per_seq;
+  P.n_pages = c.n_pages;
+  P.max_seq = std::min(S->bucket, c.max_seq_len);
+  P.up_items_per_expert = c.expert_ffn / 16;
+  P.down_panels_per_item = h->down_panels;
+  P.down_items_per_expert = c.hidden / 16 / h->down_panels;
+  P.max_splits = h->max_splits;
+  P.n_lm_tasks = S->n_lm;
+  P.e_pad = h->e_pad;
+  P.emb = h->emb;
+  P.gamma = h->gamma;
+  P.wqkv = h->wqkv;
+  P.s_wqkv = h->s_wqkv;
+  P.wo = h->wo;
+  P.s_wo = h->s_wo;
+  P.wr = h->wr;
+  P.s_wr = h->s_wr;
+  P.wgu = h->wgu;
+  P.s_wgu_l = h->s_wgu_l;
+  P.s_wgu_e = h->s_wgu_e;
+  P.wd = h->wd;
+  P.s_wd_l = h->s_wd_l;
+  P.s_wd_e = h->s_wd_e;
+  P.wlm = h->wlm;
+  P.rope = h->rope;
+  P.kv = h->kv;
+  P.s_kv_l = (size_t)c.n_pages * 2 * c.n_kv_heads * c.page_size * c.head_dim;
+  P.tokens = tokens;
+  P.bt = bt;
+  P.seq_lens = seq_lens;
+  P.logits = logits;
+  P.next_tokens = next_tokens;
+  P.flags = flags;
+  P.h = h->h;
+  P.xn = h->xn;
+  P.q = h->q;
+  P.part = h->part;
+  P.o = h->o;
+  P.ao = h->ao;
+  P.r = h->r;
+  P.tk_idx = h->tk_idx;
+  P.tk_w = h->tk_w;
+  P.tk_trace = h->tk_trace;
+  P.route = h->route;
+  P.u = h->u;
+  P.dn = h->dn;
+  P.lm_val = h->lm_val;
+  P.lm_arg = h->lm_arg;
+  P.n_ctr = h->n_ctr_cap;  // clear the whole capacity: schedules differ in size
+  P.err = h->err_word;
+  P.timeout_ticks = h->timeout_ticks;
+}
+
+mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables, int32_t* seq_lens,
+                         int max_seq_len_hint, float* logits, int32_t* next_tokens, uint32_t flags, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  const mk_config& c = h->cfg;
+  if (batch < 1 || batch > c.max_batch) return fail(h, MK_ERR_INVALID_ARG, "batch %d not in [1, %d]", batch, c.max_batch);
+  if (batch != 1) return fail(h, MK_ERR_UNSUPPORTED, "this build decodes batch 1 only");
+  if (!tokens || !block_tables || !seq_lens || !logits)
+    return fail(h, MK_ERR_INVALID_ARG, "null tokens/block_tables/seq_lens/logits");
+  if (max_seq_len_hint < 1 || max_seq_len_hint > c.max_seq_len)
+    return fail(h, MK_ERR_INVALID_ARG, "max_seq_len_hint %d not in [1, %d]", max_seq_len_hint, c.max_seq_len);
+  if (flags & ~MK_STEP_ADVANCE) return fail(h, MK_ERR_INVALID_ARG, "unknown flags");
+  if ((flags & MK_STEP_ADVANCE) && max_seq_len_hint >= c.max_seq_len)
+    return fail(h, MK_ERR_INVALID_ARG, "advancing past max_seq_len");
+  if (!h->globals_loaded) return fail(h, MK_ERR_STATE, "embedding/LM head not loaded");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!h->layer_loaded[l]) return fail(h, MK_ERR_STATE, "layer %d not loaded", l);
+  Schedule* S = nullptr;
+  mk_status st = get_schedule(h, batch, max_seq_len_hint, &S);
+  if (st != MK_OK) return st;
+  HIPCHECK(h, hipSetDevice(h->device));
+  hipStream_t s = (hipStream_t)stream;
+  mk_params P;
+  fill_params(h, S, batch, tokens, block_tables, seq_lens, logits, next_tokens, flags, P);
+  // the lengths limit on the device is the hint (the schedule's splits cover it)
+  P.max_seq = max_seq_len_hint;
+  const int cur = (int)(h->steps & 1), nxt = cur ^ 1;
+  P.ctr = h->ctr[cur];
+  P.ctr_clear = h->ctr[nxt];
+  if (c.mode == MK_MODE_MEGAKERNEL) {
+    P.tasks = S->d_cu_tasks;
+    P.task_off = S->d_cu_off;
+    P.waits_enabled = 1;
+    HIPCHECK(h, mk_launch_interp(P, c.head_dim, h->n_cu, true, s));
+  } else {
+    P.waits_enabled = 0;
+    P.task_off = h->wg_off_identity;
+    for (size_t w = 0; w < S->waves.size(); ++w) {
+      const int b0 = S->waves[w].first, n = S->waves[w].second - S->waves[w].first;
+      if (n == 0) continue;
+      P.tasks = S->d_flat + b0;
+      P.ctr_clear = (w == 0) ? h->ctr[nxt] : nullptr;
+      HIPCHECK(h, mk_launch_interp(P, c.head_dim, n, false, s));
+    }
+  }
+  h->steps++;
+  return MK_OK;
+}
+
+mk_status mk_set_routing_trace(mk_handle* h, int32_t* trace) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  h->tk_trace = trace;
+  return MK_OK;
+}
+
+mk_status mk_sync_status(mk_handle* h, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return MK_OK;
+  HIPCHECK(h, hipSetDevice(h->device));
+  HIPCHECK(h, hipStreamSynchronize((hipStream_t)stream));
+  uint32_t e[4];
+  HIPCHECK(h, hipMemcpy(e, h->err_word, sizeof(e), hipMemcpyDeviceToHost));
+  if (e[0] == 0) return MK_OK;
+  HIPCHECK(h, hipMemset(h->err_word, 0, sizeof(e)));
+  // a failed step leaves counters mid-way: clear both sets
+  for (auto* c : h->ctr) HIPCHECK(h, hipMemset(c, 0, (size_t)h->n_ctr_cap * 4));
+  HIPCHECK(h, hipDeviceSynchronize());
+  if (e[0] == MK_DEVERR_TIMEOUT)
+    return fail(h, MK_ERR_DEVICE_TIMEOUT, "device wait timed out on counter %u (value %u, workgroup %u)", e[1], e[2],
+                e[3]);
+  return fail(h, MK_ERR_DEVICE_FAULT, "device rejected an index (site %u, value %u, workgroup %u)", e[1], e[2], e[3]);
+}
+
+mk_status mk_schedule_info_get(mk_handle* h, int batch, int hint, mk_schedule_info* out) {
+  if (!h || !out) return MK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > h->cfg.max_batch || hint < 1 || hint > h->cfg.max_seq_len)
+    return fail(h, MK_ERR_INVALID_ARG, "bad batch/hint");
+  Schedule* S = nullptr;
+  mk_status st = get_schedule(h, batch, hint, &S);
+  if (st != MK_OK) return st;
+  out->n_tasks = (int32_t)S->cu_tasks.size();
+  int mx = 0;
+  for (int i = 0; i < h->n_cu; ++i) mx = std::max(mx, S->cu_off[i + 1] - S->cu_off[i]);
+  out->max_tasks_per_cu = mx;
+  out->n_counters = S->n_ctr;
+  out->n_cus = h->n_cu;
+  const mk_config& c = h->cfg;
+  const int64_t per_layer = (int64_t)c.hidden * h->qkv_dim + (int64_t)h->q_dim * c.hidden +
+                            (int64_t)c.hidden * h->e_pad + c.hidden +
+                            (int64_t)c.top_k * 3 * c.hidden * c.expert_ffn;
+  out->weight_bytes_per_step = 2 * (per_layer * c.n_layers + (int64_t)c.hidden * c.vocab + c.hidden);
+  return MK_OK;
+}
+
+mk_status mk_schedule_export(mk_handle* h, int batch, int hint, int32_t* tasks, int32_t* cu_offsets) {
+  if (!h || !tasks || !cu_offsets) return MK_ERR_INVALID_ARG;
+  Schedule* S = nullptr;
+  mk_status st = get_schedule(h, batch, hint, &S);
+  if (st != MK_OK) return st;
+  std::memcpy(tasks, S->cu_tasks.data(), S->cu_tasks.size() * sizeof(mk_task));
+  std::memcpy(cu_offsets, S->cu_off.data(), S->cu_off.size() * sizeof(int32_t));
+  return MK_OK;
+}
+
+mk_status mk_schedule_simulate(mk_handle* h, int batch, int hint, const int32_t* n_active, uint64_t seed,
+                               int32_t corrupt_task, char* report, size_t report_len) {
+  if (!h || !n_active) return MK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > h->cfg.max_batch || hint < 1 || hint > h->cfg.max_seq_len)
+    return fail(h, MK_ERR_INVALID_ARG, "bad batch/hint");
+  for (int l = 0; l < h->cfg.n_layers; ++l)
+    if (n_active[l] < 1 || n_active[l] > std::min(h->cfg.n_experts, batch * h->cfg.top_k))
+      return fail(h, MK_ERR_INVALID_ARG, "n_active[%d] out of range", l);
+  Schedule* S = nullptr;
+  mk_status st = get_schedule(h, batch, hint, &S);
+  if (st != MK_OK) return st;
+  std::string rep;
+  st = simulate(h, *S, n_active, seed, corrupt_task, rep);
+  if (report && report_len) {
+    std::strncpy(report, rep.c_str(), report_len - 1);
+    report[report_len - 1] = 0;
+  }
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// mk_internal.h - task descriptor, opcodes and kernel parameters shared by the
+// host scheduler (mk_host.cpp) and the device interpreter (mk_device.hip).
+//
+// A task is one tile of one operation, described by 32 int32 fields (Cohere's
+// North Mini Code megakernel post, section "The task descriptor": field 0 the
+// opcode, then op-specific fields, the counters to wait on with their target
+// counts, and the counter to signal). The fields are read with scalar loads
+// because every lane of a workgroup runs the same task.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#define MK_WG_THREADS 512
+#define MK_WAVES (MK_WG_THREADS / 64)
+#define MK_MAX_CUS 1024
+#define MK_MAX_TOPK 8
+#define MK_TASK_INTS 32
+
+// Opcodes. The post names sixteen opcodes for its model family; this model
+// (no dense FFN) uses the ones below. MOE_GATHER is folded into the expert
+// up/gate task (it reads the routed token rows directly), MOE_COMBINE into
+// the residual + RMSNorm task (it sums each token's k expert outputs in rank
+// order while forming the residual), ROUTE_FINALIZE into ROUTER_TOPK.
+enum mk_opcode : int32_t {
+  MK_OP_NOP = 0,
+  MK_OP_NORM = 1,         // residual add (+ MoE combine) + RMSNorm; layer 0: embedding gather
+  MK_OP_QKV = 2,          // QKV panels + RoPE + paged KV append
+  MK_OP_ATTN = 3,         // split-KV partial attention over a page range
+  MK_OP_ATTN_COMBINE = 4, // log-sum-exp merge of the splits of one (sequence, kv group)
+  MK_OP_OPROJ = 5,        // O projection, split-K by kv group
+  MK_OP_ROUTER = 6,       // router logits
+  MK_OP_TOPK = 7,         // top-k + softmax weights + route finalize (expert work queue)
+  MK_OP_MOE_UP = 8,       // claimer over (expert, gate/up panel pair) items
+  MK_OP_MOE_DOWN = 9,     // claimer over (expert, down panel group) items
+  MK_OP_LMHEAD = 10,      // LM head panels + per-task argmax candidate
+  MK_OP_ARGMAX = 11,      // greedy token from the LM head candidates
+  MK_OP_COUNT = 12
+};
+
+struct mk_task {
+  int32_t op;
+  int32_t layer;
+  int32_t a[6];           // op arguments (see the op bodies)
+  int32_t wait_ctr[3];    // counter index or -1
+  int32_t wait_tgt[3];    // wait until counter >= target
+  int32_t sig_ctr[2];     // counters incremented once when the task is done, or -1
+  int32_t pad[16];
+};
+static_assert(sizeof(mk_task) == MK_TASK_INTS * 4, "descriptor is 32 int32");
+
+// Route scratch (int32), rebuilt per layer by MK_OP_TOPK:
+//   [0] n_active experts, [1] n_up_items, [2] n_down_items, [3] unused
+//   [4 .. 4+E)           active expert ids, ascending
+//   [4+E .. 4+2E)        tokens routed to each active expert
+//   [4+2E .. 4+2E+E*B)   per active expert: slots b*k + j routed to it, ascending b
+#define MK_ROUTE_INTS(E, B) (4 + 2 * (E) + (E) * (B))
+
+// Device error word: [0] code (0 none, 5 timeout, 6 fault), [1] detail, [2] value, [3] cu
+#define MK_DEVERR_TIMEOUT 5
+#define MK_DEVERR_FAULT 6
+
+struct mk_params {
+  // shape
+  int32_t H, QH, KVH, D, G, E, K, F, V, L, PS, window, full_every;
+  float eps;
+  float attn_scale;
+  int32_t B, mpps, n_pages, max_seq;
+  int32_t up_items_per_expert;   // F / 16 (gate/up panel pairs)
+  int32_t down_panels_per_item;  // panels per MoE down item
+  int32_t down_items_per_expert; // H / 16 / down_panels_per_item
+  int32_t max_splits;            // attention partial slots per (sequence, group)
+  int32_t n_lm_tasks;
+  int32_t e_pad;                 // router columns, padded to a multiple of 16
+  // packed weights (bf16 bit patterns)
+  const uint16_t* emb;           // [V][H] row-major
+  const uint16_t* gamma;         // [L+1][H]
+  const uint16_t* wqkv; size_t s_wqkv;      // per layer: panel-tiled [H x QKV]
+  const uint16_t* wo; size_t s_wo;          // per layer: panel-tiled [QH*D x H]
+  const uint16_t* wr; size_t s_wr;          // per layer: panel-tiled [H x e_pad]
+  const uint16_t* wgu; size_t s_wgu_l, s_wgu_e; // per layer, expert: [H x 2F], gate/up panels interleaved
+  const uint16_t* wd; size_t s_wd_l, s_wd_e;    // per layer, expert: panel-tiled [F x H]
+  const uint16_t* wlm;           // panel-tiled [H x V]
+  const float* rope;             // [max_seq][D/2][2] (cos, sin)
+  uint16_t* kv; size_t s_kv_l;   // KV pool, layer stride in elements
+  // batch (caller-owned)
+  int32_t* tokens;
+  const int32_t* bt;
+  int32_t* seq_lens;
+  float* logits;
+  int32_t* next_tokens;
+  uint32_t flags;
+  // scratch
+  float* h;      // [B][H] residual stream
+  float* xn;     // [B][H] normalised input of the current layer
+  float* q;      // [B][QH*D] rotated queries
+  float* part;   // [B][KVH][max_splits][G*D + 2G] attention partials (o, m, l)
+  float* o;      // [B][QH*D] attention output
+  float* ao;     // [KVH][B][H] O projection partials per kv group
+  float* r;      // [B][E] router logits
+  int32_t* tk_idx; float* tk_w;  // [B][K]
+  int32_t* tk_trace;             // optional [L][B][K] record of every layer's routing
+  int32_t* route;
+  float* u;      // [B*K][F] expert hidden (after SiLU-and-multiply)
+  float* dn;     // [B*K][H] expert outputs
+  float* lm_val; int32_t* lm_arg; // [B][n_lm_tasks] LM head argmax candidates
+  // synchronisation
+  uint32_t* ctr;        // counters of this step
+  uint32_t* ctr_clear;  // counters of the next step (cleared by this step), or null
+  int32_t n_ctr;
+  uint32_t* err;        // device error word
+  const mk_task* tasks;
+  const int32_t* task_off;   // per workgroup [off[wg], off[wg+1])
+  int32_t waits_enabled;     // 0 in kernel-per-op mode (stream order is the dependency)
+  int64_t timeout_ticks;     // wait time limit in s_memrealtime ticks (100 MHz)
+};

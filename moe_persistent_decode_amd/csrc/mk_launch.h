@@ -1,0 +1,10 @@
+// mk_launch.h - host entry points into the device code (defined in mk_device.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "mk_internal.h"
+
+hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool cooperative, hipStream_t stream);
+hipError_t mk_launch_repack(const uint16_t* src, uint16_t* dst, int K, int N, int ld, int dst0, int dstep,
+                            int nz, size_t src_zstride, size_t dst_zstride, hipStream_t stream);
+hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu);
