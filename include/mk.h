@@ -141,6 +141,12 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
                          int32_t* seq_lens, int max_seq_len_hint, float* logits,
                          int32_t* next_tokens, uint32_t flags, void* stream);
 
+/* Switch between the persistent megakernel and the kernel-per-op variant
+ * (the same op bodies launched once per wave of same-type tasks, with the
+ * stream order in place of the counter waits). Takes effect at the next step;
+ * steps must not be in flight on another stream. */
+mk_status mk_set_mode(mk_handle* h, int mode);
+
 /* Record every layer's routing of later steps into `trace` (device int32
  * [n_layers][batch][top_k], expert ids in descending router-logit order, ties
  * to the lower id); NULL stops recording. For checking routing decisions. */
@@ -154,6 +160,17 @@ mk_status mk_sync_status(mk_handle* h, void* stream);
 const char* mk_last_error(const mk_handle* h);
 
 void mk_destroy(mk_handle* h);
+
+/* Copy `bytes` of one of the library's per-step scratch buffers to host
+ * memory after synchronising the device (for op-level checks of the last
+ * step's last layer). Names and float32/int32 layouts:
+ *   "h" [max_batch][H] residual stream   "xn" [max_batch][H] normalised input
+ *   "q" [max_batch][QH*D] rotated query   "o" [max_batch][QH*D] attention out
+ *   "ao" [KVH][max_batch][H] O-proj partial per kv group
+ *   "r" [max_batch][E] router logits      "tk_idx"/"tk_w" [max_batch][k]
+ *   "route" expert work queue             "u" [max_batch*k][F] expert hidden
+ *   "dn" [max_batch*k][H] expert outputs (slot b*k + j). */
+mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes);
 
 /* ---- schedule introspection (host only, no device work) ---------------- */
 

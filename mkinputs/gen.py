@@ -67,24 +67,58 @@ def weight_shapes(m: ModelConfig) -> Dict[str, tuple]:
     return s
 
 
+def weight_tensor(m: ModelConfig, name: str, seed: int = 1, device="cpu", std: float = 0.02,
+                  expert: Optional[int] = None) -> torch.Tensor:
+    """One canonical weight (or one expert's slice of an expert tensor), drawn
+    exactly as make_weights draws it, so any piece can be regenerated alone."""
+    shape = weight_shapes(m)[name]
+    kind = name.split(".")[0]
+    if kind.startswith("gamma"):
+        return _normal_bf16(shape, tensor_seed(seed, name), std, 1.0, device)
+    if kind in ("wg", "wu", "wd"):
+        if expert is not None:
+            return _normal_bf16(shape[1:], tensor_seed(seed, f"{name}.e{expert}"), std, 0.0, device)
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for e in range(shape[0]):
+            t[e] = _normal_bf16(shape[1:], tensor_seed(seed, f"{name}.e{e}"), std, 0.0, device)
+        return t
+    return _normal_bf16(shape, tensor_seed(seed, name), std, 0.0, device)
+
+
+LAYER_KINDS = ("gamma", "wqkv", "wo", "wr", "wg", "wu", "wd")
+GLOBAL_NAMES = ("emb", "gamma_f", "wlm")
+
+
+def make_layer_weights(m: ModelConfig, layer: int, seed: int = 1, device="cpu") -> Dict[str, torch.Tensor]:
+    return {f"{k}.{layer}": weight_tensor(m, f"{k}.{layer}", seed, device) for k in LAYER_KINDS}
+
+
 def make_weights(m: ModelConfig, seed: int = 1, device="cpu", std: float = 0.02) -> Dict[str, torch.Tensor]:
     """All weights of model m as canonical bf16 tensors on `device`.
 
     Expert tensors are drawn one expert at a time (seed per expert slice) to
     bound the fp32 temporaries of the 48-layer model.
     """
-    out: Dict[str, torch.Tensor] = {}
-    for name, shape in weight_shapes(m).items():
-        if name.startswith("gamma"):
-            out[name] = _normal_bf16(shape, tensor_seed(seed, name), std, 1.0, device)
-        elif name.split(".")[0] in ("wg", "wu", "wd"):
-            t = torch.empty(shape, dtype=torch.bfloat16, device=device)
-            for e in range(shape[0]):
-                t[e] = _normal_bf16(shape[1:], tensor_seed(seed, f"{name}.e{e}"), std, 0.0, device)
-            out[name] = t
-        else:
-            out[name] = _normal_bf16(shape, tensor_seed(seed, name), std, 0.0, device)
-    return out
+    return {name: weight_tensor(m, name, seed, device, std) for name in weight_shapes(m)}
+
+
+class LazyWeights:
+    """Host bf16 bits of model weights, each drawn on `device` on first use
+    (identical to make_weights on that device) and kept in host memory."""
+
+    def __init__(self, m: ModelConfig, seed: int = 1, device="cuda"):
+        self.m, self.seed, self.device = m, seed, device
+        self._c: Dict[tuple, np.ndarray] = {}
+        self.overrides: Dict[tuple, np.ndarray] = {}
+
+    def __call__(self, name: str, layer: Optional[int] = None, expert: Optional[int] = None) -> np.ndarray:
+        key = (name, layer, expert)
+        if key in self.overrides:
+            return self.overrides[key]
+        if key not in self._c:
+            full = name if layer is None else f"{name}.{layer}"
+            self._c[key] = bf16_bits(weight_tensor(self.m, full, self.seed, self.device, expert=expert))
+        return self._c[key]
 
 
 @dataclass

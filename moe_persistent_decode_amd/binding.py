@@ -23,8 +23,8 @@ STEP_ADVANCE = 1
 
 # every function include/mk.h declares
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
-           "mk_decode_step", "mk_set_routing_trace", "mk_sync_status", "mk_last_error", "mk_destroy",
-           "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate")
+           "mk_decode_step", "mk_set_mode", "mk_set_routing_trace", "mk_sync_status", "mk_last_error", "mk_destroy",
+           "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
 
 class MkError(RuntimeError):
@@ -60,6 +60,8 @@ def _load():
     lib.mk_load_weights.argtypes = [H, P, P]
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
+    lib.mk_set_mode.argtypes = [H, I]
+    lib.mk_debug_read.argtypes = [H, ctypes.c_char_p, P, S]
     lib.mk_sync_status.argtypes = [H, P]
     lib.mk_last_error.argtypes = [H]
     lib.mk_last_error.restype = ctypes.c_char_p
@@ -159,8 +161,17 @@ class Decoder:
                                        _ptr(seq_lens), int(max_seq_len_hint), _ptr(logits), _ptr(next_tokens),
                                        STEP_ADVANCE if advance else 0, _stream_ptr(stream)))
 
+    def set_mode(self, mode: int):
+        self._check(lib.mk_set_mode(self._h, mode))
+
     def set_routing_trace(self, trace):
         self._check(lib.mk_set_routing_trace(self._h, _ptr(trace)))
+
+    def debug_read(self, name: str, shape, dtype="float32"):
+        import numpy as np
+        a = np.zeros(shape, dtype=dtype)
+        self._check(lib.mk_debug_read(self._h, name.encode(), a.ctypes.data, a.nbytes))
+        return a
 
     def sync(self, stream=None):
         self._check(lib.mk_sync_status(self._h, _stream_ptr(stream)))

@@ -14,11 +14,17 @@
 // The same kernel, launched once per wave of same-type tasks with waits
 // switched off, is the kernel-per-op variant.
 //
-// Memory ordering on CDNA4: each XCD has its own L2, so a producer on one XCD
-// and a consumer on another need an agent-scope release (L2 write-back) before
-// the counter increment and an agent-scope acquire (L2 invalidate) after the
-// counter wait. Weights and the older part of the KV cache are never written
-// during a step and need neither.
+// Memory ordering on CDNA4. Each XCD has its own L2, which is not coherent with
+// the other XCDs' L2s. A C++ release/acquire at agent scope is implemented by
+// writing back / invalidating the whole L2 (buffer_wbl2 / buffer_inv), which
+// costs microseconds per task, so the interpreter does not use them. Instead
+// every activation that crosses compute units within a step is stored and
+// loaded with device-scope (sc1) buffer instructions, which bypass the
+// non-coherent cache levels; a producer waits for its own stores to complete
+// (s_waitcnt) before its counter increment, and a consumer issues its loads
+// only after it has observed the counter. Weights and the KV cache written in
+// earlier steps are read with ordinary (non-temporal) loads: nothing writes
+// them during a step, and kernel boundaries make earlier steps' writes visible.
 #include <hip/hip_runtime.h>
 
 #include "mk_internal.h"
@@ -49,8 +55,58 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+// Raw buffer resource over a uniform base address (4 GB range). Loads past
+// the range return 0 instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
+}
+constexpr int kSC1 = 16;  // cache-policy bit: device (agent) scope coherence
+
+// Device-coherent access to a buffer of 32-bit words shared across compute units.
+struct Pub {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ explicit Pub(const void* base) : r(rsrc_of(base)) {}
+  __device__ __forceinline__ float ldf(int i) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, kSC1));
+  }
+  __device__ __forceinline__ int ldi(int i) const {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, kSC1);
+  }
+  __device__ __forceinline__ float4 ldf4(int i) const {  // 16-byte aligned element index
+    // (element values through __uint_as_float: a bit-cast of an ext-vector
+    // element would read the vector's first element)
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, i * 4, 0, kSC1);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+  }
+  __device__ __forceinline__ void stf(int i, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, i * 4, 0, kSC1);
+  }
+  __device__ __forceinline__ void sti(int i, int v) const {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, r, i * 4, 0, kSC1);
+  }
+  __device__ __forceinline__ void st16(int i, uint16_t v) const {  // i: 16-bit element index
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, i * 2, 0, kSC1);
+  }
+  __device__ __forceinline__ u32x4_t ld16x8(int i) const {  // 8 bf16 at 16-bit index i
+    return __builtin_amdgcn_raw_buffer_load_b128(r, i * 2, 0, kSC1);
+  }
+  __device__ __forceinline__ u32x2_t ld16x4(int i) const {  // 4 bf16 at 16-bit index i
+    return __builtin_amdgcn_raw_buffer_load_b64(r, i * 2, 0, kSC1);
+  }
+};
+
+// Wait until this wave's memory operations have completed.
+__device__ __forceinline__ void drain_memory() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after which device-coherent stores of every wave are complete.
+__device__ __forceinline__ void sync_published() {
+  drain_memory();
+  __syncthreads();
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -118,7 +174,6 @@ __device__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32
           }
         }
       }
-      fence_acquire();
     }
     sm.flag = ok;
   }
@@ -136,10 +191,9 @@ __device__ __forceinline__ bool wait_one(const mk_params& P, int32_t c, int32_t 
   return wait_counters(P, &c, &tgt, 1, sm);
 }
 
-// Publish this workgroup's stores at device scope, then count one arrival.
+// Count one arrival once every wave's device-coherent stores have completed.
 __device__ void signal_counter(const mk_params& P, int32_t c) {
-  fence_release();
-  __syncthreads();
+  sync_published();
   if (threadIdx.x == 0 && c >= 0)
     __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -189,9 +243,10 @@ __device__ __forceinline__ float dot8(float4 x0, float4 x1, u32x4_t q, float s) 
 }
 
 // y[16*pp + col] = sum_k x[k - 32*c0] * W[k][col] over chunks [c0, c1), into sm.out.
-// x: float32 activations starting at row 32*c0.
+// x: float32 activations (another compute unit's output) starting at row 32*c0.
 template <int NP, int NCH>
 __device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0, int c1, Smem& sm) {
+  const Pub X(x);
   const int wv = wave_id(), ln = lane_id();
   float acc[NP];
 #pragma unroll
@@ -200,8 +255,8 @@ __device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0,
   for (int i = 0; i < NCH; ++i) {
     const int c = c0 + wv + MK_WAVES * i;
     if (c < c1) {
-      const float4* xp = (const float4*)(x + (size_t)(c - c0) * 32 + 8 * (ln >> 4));
-      const float4 x0 = xp[0], x1 = xp[1];
+      const int xi = (c - c0) * 32 + 8 * (ln >> 4);
+      const float4 x0 = X.ldf4(xi), x1 = X.ldf4(xi + 4);
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp)
         if (pp < np) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
@@ -236,7 +291,7 @@ __device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0,
 __device__ void op_norm(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int b = t.a[0], l = t.layer, H = P.H;
-  float* h = P.h + (size_t)b * H;
+  const Pub h(P.h + (size_t)b * H), ao(P.ao), dn(P.dn), tkw(P.tk_w), xn(P.xn + (size_t)b * H);
   int tok = 0;
   if (l == 0) {
     tok = P.tokens[b];
@@ -252,13 +307,12 @@ __device__ void op_norm(const mk_params& P, const mk_task& t, Smem& sm) {
       v = bf2f(P.emb[(size_t)tok * H + i]);
     } else {
       float a = 0.f;
-      for (int g = 0; g < P.KVH; ++g) a += P.ao[((size_t)g * P.B + b) * H + i];
+      for (int g = 0; g < P.KVH; ++g) a += ao.ldf((g * P.B + b) * H + i);
       float y = 0.f;
-      for (int j = 0; j < P.K; ++j)
-        y = fmaf(P.tk_w[b * P.K + j], P.dn[(size_t)(b * P.K + j) * H + i], y);
-      v = (h[i] + a) + y;
+      for (int j = 0; j < P.K; ++j) y = fmaf(tkw.ldf(b * P.K + j), dn.ldf((b * P.K + j) * H + i), y);
+      v = (h.ldf(i) + a) + y;
     }
-    h[i] = v;
+    h.stf(i, v);
     ss = fmaf(v, v, ss);
   }
   ss = wave_sum(ss);
@@ -269,8 +323,8 @@ __device__ void op_norm(const mk_params& P, const mk_task& t, Smem& sm) {
   for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
   const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
   const uint16_t* gam = P.gamma + (size_t)l * H;
-  for (int i = threadIdx.x; i < H; i += MK_WG_THREADS)
-    P.xn[(size_t)b * H + i] = h[i] * inv * bf2f(gam[i]);
+  drain_memory();  // this thread's h stores complete before it reads them back
+  for (int i = threadIdx.x; i < H; i += MK_WG_THREADS) xn.stf(i, h.ldf(i) * inv * bf2f(gam[i]));
 }
 
 // -------------------------------------------------------------------- QKV
@@ -309,15 +363,15 @@ __device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
             const float x0 = odd ? yp : y, x1 = odd ? y : yp;
             const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
             if (n < qd) {
-              P.q[(size_t)b * qd + n] = r;
+              Pub(P.q + (size_t)b * qd).stf(n, r);
             } else {
               const int g = (n - qd) / D;
               const int page = P.bt[b * P.mpps + pos / PS];
               if (page < 0 || page >= P.n_pages) {
                 raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
               } else {
-                uint16_t* kp = P.kv + l * P.s_kv_l + ((size_t)(page * 2 + 0) * P.KVH + g) * PS * D;
-                kp[(pos % PS) * D + d] = (uint16_t)f2bf(r);
+                const int off = ((page * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d;
+                Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(r));
               }
             }
           } else {
@@ -327,8 +381,8 @@ __device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
             if (page < 0 || page >= P.n_pages) {
               raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
             } else {
-              uint16_t* vp = P.kv + l * P.s_kv_l + ((size_t)(page * 2 + 1) * P.KVH + g) * PS * D;
-              vp[d * PS + (pos % PS)] = (uint16_t)f2bf(y);
+              const int off = ((page * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS);
+              Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(y));
             }
           }
         }
@@ -372,16 +426,16 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   bf16x8_t qb[NC];
   {
     const int hh = ln & 15;
-    const float* qp = P.q + (size_t)b * P.QH * D + (size_t)(g * G + min(hh, G - 1)) * D;
+    const Pub Q(P.q + (size_t)b * P.QH * D + (size_t)g * G * D);
+    const int qo = min(hh, G - 1) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      const float4 a0 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4)), a1 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4) + 4);
+      const float qv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       u32x4_t pk;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = hh < G ? f2bf(qp[32 * c + 8 * (ln >> 4) + 2 * i]) : 0u;
-        const uint32_t hi = hh < G ? f2bf(qp[32 * c + 8 * (ln >> 4) + 2 * i + 1]) : 0u;
-        pk[i] = lo | (hi << 16);
-      }
+      for (int i = 0; i < 4; ++i)
+        pk[i] = hh < G ? (f2bf(qv[2 * i]) | (f2bf(qv[2 * i + 1]) << 16)) : 0u;
       qb[c] = __builtin_bit_cast(bf16x8_t, pk);
     }
   }
@@ -394,18 +448,31 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   u32x4_t kr[NC];
   u32x2_t vr[NT];
   bool bad = false;
+  // The page holding the current position gets this step's K/V from the QKV
+  // tasks of other compute units: read it device-coherently.
+  const Pub KV(kvl);
   auto load_page = [&](int lp, u32x4_t* kk, u32x2_t* vv) {
     const int phys = P.bt[b * P.mpps + lp];
     if (phys < 0 || phys >= P.n_pages) {
       bad = true;
       return;
     }
-    const uint16_t* kp = kvl + ((size_t)(phys * 2 + 0) * P.KVH + g) * plane;
-    const uint16_t* vp = kvl + ((size_t)(phys * 2 + 1) * P.KVH + g) * plane;
+    const int ko = ((phys * 2 + 0) * P.KVH + g) * (int)plane, vo = ((phys * 2 + 1) * P.KVH + g) * (int)plane;
+    if (lp == lp_last) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kk[c] = *(const u32x4_t*)(kp + (ln & 15) * D + 32 * c + 8 * (ln >> 4));
+      for (int c = 0; c < NC; ++c) kk[c] = KV.ld16x8(ko + (ln & 15) * D + 32 * c + 8 * (ln >> 4));
 #pragma unroll
-    for (int d = 0; d < NT; ++d) vv[d] = *(const u32x2_t*)(vp + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4));
+      for (int d = 0; d < NT; ++d) vv[d] = KV.ld16x4(vo + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4));
+    } else {
+      const uint16_t* kp = kvl + ko;
+      const uint16_t* vp = kvl + vo;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kk[c] = __builtin_nontemporal_load((const u32x4_t*)(kp + (ln & 15) * D + 32 * c + 8 * (ln >> 4)));
+#pragma unroll
+      for (int d = 0; d < NT; ++d)
+        vv[d] = __builtin_nontemporal_load((const u32x2_t*)(vp + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4)));
+    }
   };
 
   int lp = my0 + wv;
@@ -471,7 +538,7 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
     for (int i = 0; i < 4; ++i) A.o[wv][16 * d + 4 * (ln >> 4) + i][ln & 15] = oacc[d][i];
   __syncthreads();
   const int stride = G * D + 2 * G;
-  float* dst = P.part + ((size_t)(b * P.KVH + g) * P.max_splits + s) * stride;
+  const Pub dst(P.part + ((size_t)(b * P.KVH + g) * P.max_splits + s) * stride);
   for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
     const int hh = idx / D, dd = idx % D;
     float M = kNegInf;
@@ -486,10 +553,10 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
         L = fmaf(f, A.l[k][hh], L);
       }
     }
-    dst[hh * D + dd] = O;
+    dst.stf(hh * D + dd, O);
     if (dd == 0) {
-      dst[G * D + hh] = M;
-      dst[G * D + G + hh] = L;
+      dst.stf(G * D + hh, M);
+      dst.stf(G * D + G + hh, L);
     }
   }
 }
@@ -501,19 +568,20 @@ __device__ void op_attn_combine(const mk_params& P, const mk_task& t, Smem& sm) 
   const int b = t.a[0], g = t.a[1], ns = t.a[2];
   const int G = P.G, D = P.D;
   const int stride = G * D + 2 * G;
-  const float* src = P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride;
+  const Pub src(P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride);
+  const Pub dst(P.o + (size_t)b * P.QH * D + (size_t)g * G * D);
   for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
     const int hh = idx / D, dd = idx % D;
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, src[s * stride + G * D + hh]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, src.ldf(s * stride + G * D + hh));
     float O = 0.f, L = 0.f;
     for (int s = 0; s < ns; ++s) {
-      const float ms = src[s * stride + G * D + hh];
+      const float ms = src.ldf(s * stride + G * D + hh);
       const float f = ms == kNegInf ? 0.f : __expf(ms - M);
-      O = fmaf(f, src[s * stride + hh * D + dd], O);
-      L = fmaf(f, src[s * stride + G * D + G + hh], L);
+      O = fmaf(f, src.ldf(s * stride + hh * D + dd), O);
+      L = fmaf(f, src.ldf(s * stride + G * D + G + hh), L);
     }
-    P.o[(size_t)b * P.QH * D + (size_t)(g * G + hh) * D + dd] = O / L;
+    dst.stf(hh * D + dd, O / L);
   }
 }
 
@@ -532,8 +600,7 @@ __device__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   for (int b = 0; b < P.B; ++b) {
     gemv_b1(w, P.o + (size_t)b * P.QH * P.D + (size_t)g * P.G * P.D, np, c0, c1, sm);
-    if (threadIdx.x < np * 16)
-      P.ao[((size_t)g * P.B + b) * P.H + p0 * 16 + threadIdx.x] = sm.out[threadIdx.x];
+    if (threadIdx.x < np * 16) Pub(P.ao + ((size_t)g * P.B + b) * P.H).stf(p0 * 16 + threadIdx.x, sm.out[threadIdx.x]);
   }
 }
 
@@ -549,7 +616,7 @@ __device__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
   for (int b = 0; b < P.B; ++b) {
     gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
     const int n = p0 * 16 + threadIdx.x;
-    if (threadIdx.x < np * 16 && n < P.E) P.r[(size_t)b * P.E + n] = sm.out[threadIdx.x];
+    if (threadIdx.x < np * 16 && n < P.E) Pub(P.r + (size_t)b * P.E).stf(n, sm.out[threadIdx.x]);
   }
 }
 
@@ -561,10 +628,10 @@ __device__ void op_topk(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int E = P.E, K = P.K, B = P.B;
   const int ln = lane_id();
+  const Pub R(P.r), TI(P.tk_idx), TW(P.tk_w), RT(P.route);
   for (int b = wave_id(); b < B; b += MK_WAVES) {
-    const float* r = P.r + (size_t)b * E;
-    const float v0 = ln < E ? r[ln] : kNegInf;
-    const float v1 = ln + 64 < E ? r[ln + 64] : kNegInf;
+    const float v0 = ln < E ? R.ldf(b * E + ln) : kNegInf;
+    const float v1 = ln + 64 < E ? R.ldf(b * E + ln + 64) : kNegInf;
     bool tk0 = ln >= E, tk1 = ln + 64 >= E;
     float sel[MK_MAX_TOPK];
     int idx[MK_MAX_TOPK];
@@ -592,41 +659,40 @@ __device__ void op_topk(const mk_params& P, const mk_task& t, Smem& sm) {
     }
     if (ln == 0)
       for (int j = 0; j < K; ++j) {
-        P.tk_idx[b * K + j] = idx[j];
-        P.tk_w[b * K + j] = e[j] / sum;
+        TI.sti(b * K + j, idx[j]);
+        TW.stf(b * K + j, e[j] / sum);
         if (P.tk_trace) P.tk_trace[((size_t)t.layer * B + b) * K + j] = idx[j];
       }
   }
-  __syncthreads();
+  sync_published();
   for (int e = threadIdx.x; e < E; e += MK_WG_THREADS) {
     int c = 0;
-    for (int i = 0; i < B * K; ++i) c += P.tk_idx[i] == e;
+    for (int i = 0; i < B * K; ++i) c += TI.ldi(i) == e;
     sm.cnt[e] = c;
   }
   __syncthreads();
-  int32_t* R = P.route;
   if (threadIdx.x == 0) {
     int n = 0;
     for (int e = 0; e < E; ++e)
       if (sm.cnt[e] > 0) {
-        R[4 + n] = e;
-        R[4 + E + n] = sm.cnt[e];
+        RT.sti(4 + n, e);
+        RT.sti(4 + E + n, sm.cnt[e]);
         sm.cnt[e] = -(n + 1);  // active slot of expert e
         ++n;
       }
-    R[0] = n;
-    R[1] = n * P.up_items_per_expert;
-    R[2] = n * P.down_items_per_expert;
+    RT.sti(0, n);
+    RT.sti(1, n * P.up_items_per_expert);
+    RT.sti(2, n * P.down_items_per_expert);
   }
   __syncthreads();
   if (threadIdx.x < B * K) {
     const int i = threadIdx.x;
-    const int e = P.tk_idx[i];
+    const int e = TI.ldi(i);
     const int a = -sm.cnt[e] - 1;
     // rank of this slot among the slots routed to e (ascending slot index)
     int rank = 0;
-    for (int k = 0; k < i; ++k) rank += P.tk_idx[k] == e;
-    R[4 + 2 * E + a * B + rank] = i;
+    for (int k = 0; k < i; ++k) rank += TI.ldi(k) == e;
+    RT.sti(4 + 2 * E + a * B + rank, i);
   }
 }
 
@@ -650,24 +716,24 @@ __device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
   const int E = P.E, F = P.F;
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
-  const int* R = P.route;
-  const int n_items = R[1];
+  const Pub R(P.route), U(P.u);
+  const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(1));
   for (;;) {
     if (ld_relaxed(&P.err[0]) != 0) return;
     const int id = claim(P, claim_ctr, sm);
     if (id >= n_items) break;
     const int a = id / P.up_items_per_expert, tt = id % P.up_items_per_expert;
-    const int e = R[4 + a];
+    const int e = __builtin_amdgcn_readfirstlane(R.ldi(4 + a));
     WTile<2, NCH> w;
     wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride, 2, 0, kc);
-    const int cnt = R[4 + E + a];
+    const int cnt = __builtin_amdgcn_readfirstlane(R.ldi(4 + E + a));
     for (int r = 0; r < cnt; ++r) {
-      const int slot = R[4 + 2 * E + a * P.B + r];
+      const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B + r));
       const int b = slot / P.K;
       gemv_b1(w, P.xn + (size_t)b * P.H, 2, 0, kc, sm);
       if (threadIdx.x < 16) {
         const float gt = sm.out[threadIdx.x], up = sm.out[16 + threadIdx.x];
-        P.u[(size_t)slot * F + tt * 16 + threadIdx.x] = gt / (1.0f + __expf(-gt)) * up;
+        U.stf(slot * F + tt * 16 + threadIdx.x, gt / (1.0f + __expf(-gt)) * up);
       }
     }
     signal_counter(P, done_base + a);
@@ -686,22 +752,22 @@ __device__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
   const int kc = F / 32;
   const size_t pstride = (size_t)kc * 512;
   const int DP = P.down_panels_per_item;
-  const int* R = P.route;
-  const int n_items = R[2];
+  const Pub R(P.route), DN(P.dn);
+  const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(2));
   for (;;) {
     if (ld_relaxed(&P.err[0]) != 0) return;
     const int id = claim(P, claim_ctr, sm);
     if (id >= n_items) break;
     const int a = id / P.down_items_per_expert, tt = id % P.down_items_per_expert;
-    const int e = R[4 + a];
+    const int e = __builtin_amdgcn_readfirstlane(R.ldi(4 + a));
     WTile<4, NCH> w;
     wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(tt * DP) * pstride, pstride, DP, 0, kc);
     if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
-    const int cnt = R[4 + E + a];
+    const int cnt = __builtin_amdgcn_readfirstlane(R.ldi(4 + E + a));
     for (int r = 0; r < cnt; ++r) {
-      const int slot = R[4 + 2 * E + a * P.B + r];
+      const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B + r));
       gemv_b1(w, P.u + (size_t)slot * F, DP, 0, kc, sm);
-      if (threadIdx.x < DP * 16) P.dn[(size_t)slot * H + tt * DP * 16 + threadIdx.x] = sm.out[threadIdx.x];
+      if (threadIdx.x < DP * 16) DN.stf(slot * H + tt * DP * 16 + threadIdx.x, sm.out[threadIdx.x]);
     }
   }
 }
@@ -733,8 +799,8 @@ __device__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
         if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
       }
       if (tid == 0) {
-        P.lm_val[b * P.n_lm_tasks + ord] = v;
-        P.lm_arg[b * P.n_lm_tasks + ord] = ix;
+        Pub(P.lm_val).stf(b * P.n_lm_tasks + ord, v);
+        Pub(P.lm_arg).sti(b * P.n_lm_tasks + ord, ix);
       }
     }
   }
@@ -747,9 +813,10 @@ __device__ void op_argmax(const mk_params& P, const mk_task& t, Smem& sm) {
   const int b = t.a[0], n = P.n_lm_tasks;
   float v = kNegInf;
   int ix = 0x7fffffff;
+  const Pub LV(P.lm_val), LA(P.lm_arg);
   for (int i = threadIdx.x; i < n; i += MK_WG_THREADS) {
-    const float cv = P.lm_val[b * n + i];
-    const int ci = P.lm_arg[b * n + i];
+    const float cv = LV.ldf(b * n + i);
+    const int ci = LA.ldi(b * n + i);
     if (cv > v || (cv == v && ci < ix)) { v = cv; ix = ci; }
   }
 #pragma unroll

@@ -163,6 +163,9 @@ mk_status validate_config(const mk_config* c) {
   if (c->max_pages_per_seq < ceil_div(c->max_seq_len, c->page_size))
     return fail(nullptr, MK_ERR_INVALID_ARG, "max_pages_per_seq too small for max_seq_len");
   if (c->n_pages < 1) return fail(nullptr, MK_ERR_INVALID_ARG, "n_pages must be positive");
+  // device code addresses one layer of the pool with 32-bit byte offsets
+  if ((int64_t)c->n_pages * 2 * c->n_kv_heads * c->page_size * c->head_dim * 2 > INT32_MAX)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "one layer of the KV pool must stay below 2 GB");
   if (c->mode != MK_MODE_MEGAKERNEL && c->mode != MK_MODE_KERNEL_PER_OP)
     return fail(nullptr, MK_ERR_INVALID_ARG, "unknown mode");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(nullptr, MK_ERR_INVALID_ARG, "bad eps/theta");
@@ -945,6 +948,13 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
   return MK_OK;
 }
 
+mk_status mk_set_mode(mk_handle* h, int mode) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (mode != MK_MODE_MEGAKERNEL && mode != MK_MODE_KERNEL_PER_OP) return fail(h, MK_ERR_INVALID_ARG, "unknown mode");
+  h->cfg.mode = mode;
+  return MK_OK;
+}
+
 mk_status mk_set_routing_trace(mk_handle* h, int32_t* trace) {
   if (!h) return MK_ERR_INVALID_ARG;
   h->tk_trace = trace;
@@ -967,6 +977,36 @@ mk_status mk_sync_status(mk_handle* h, void* stream) {
     return fail(h, MK_ERR_DEVICE_TIMEOUT, "device wait timed out on counter %u (value %u, workgroup %u)", e[1], e[2],
                 e[3]);
   return fail(h, MK_ERR_DEVICE_FAULT, "device rejected an index (site %u, value %u, workgroup %u)", e[1], e[2], e[3]);
+}
+
+mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes) {
+  if (!h || !name || !host) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  const mk_config& c = h->cfg;
+  const size_t Bm = c.max_batch, H = c.hidden, E = c.n_experts, K = c.top_k;
+  struct Item { const char* n; const void* p; size_t sz; };
+  const Item items[] = {
+      {"h", h->h, Bm * H * 4},
+      {"xn", h->xn, Bm * H * 4},
+      {"q", h->q, Bm * h->q_dim * 4},
+      {"o", h->o, Bm * h->q_dim * 4},
+      {"ao", h->ao, (size_t)c.n_kv_heads * Bm * H * 4},
+      {"r", h->r, Bm * E * 4},
+      {"tk_idx", h->tk_idx, Bm * K * 4},
+      {"tk_w", h->tk_w, Bm * K * 4},
+      {"route", h->route, (size_t)MK_ROUTE_INTS(E, Bm) * 4},
+      {"u", h->u, Bm * K * c.expert_ffn * 4},
+      {"dn", h->dn, Bm * K * H * 4},
+  };
+  for (const Item& it : items)
+    if (std::strcmp(it.n, name) == 0) {
+      if (bytes > it.sz) return fail(h, MK_ERR_INVALID_ARG, "%s holds %zu bytes", name, it.sz);
+      HIPCHECK(h, hipSetDevice(h->device));
+      HIPCHECK(h, hipDeviceSynchronize());
+      HIPCHECK(h, hipMemcpy(host, it.p, bytes, hipMemcpyDeviceToHost));
+      return MK_OK;
+    }
+  return fail(h, MK_ERR_INVALID_ARG, "unknown scratch buffer '%s'", name);
 }
 
 mk_status mk_schedule_info_get(mk_handle* h, int batch, int hint, mk_schedule_info* out) {

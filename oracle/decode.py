@@ -196,6 +196,11 @@ class StepTrace:
     topk_w: List[np.ndarray] = field(default_factory=list)          # [B, k]
     x_norm: List[np.ndarray] = field(default_factory=list)          # [B, H] (record=True)
     h_out: List[np.ndarray] = field(default_factory=list)           # [B, H] (record=True)
+    q_rot: List[np.ndarray] = field(default_factory=list)           # [B, QH, D] (record=True)
+    attn_out: List[np.ndarray] = field(default_factory=list)        # [B, QH*D] (record=True)
+    attn_proj: List[np.ndarray] = field(default_factory=list)       # [B, H] (record=True)
+    expert_out: List[np.ndarray] = field(default_factory=list)      # [B, k, H] (record=True)
+    moe_out: List[np.ndarray] = field(default_factory=list)         # [B, H] (record=True)
     x_final: Optional[np.ndarray] = None                             # [B, H]
 
 
@@ -229,10 +234,12 @@ def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.nda
         k = qkv[:, QH * D:QH * D + KVH * D].reshape(B, KVH, D)
         v = qkv[:, QH * D + KVH * D:].reshape(B, KVH, D)
         o = np.zeros((B, QH, D), dtype=dtype)
+        qr = np.zeros((B, QH, D), dtype=dtype)
         win = cfg.layer_window(l)
         for b in range(B):
             p = int(seq_lens[b]) - 1
             qb = rope(q[b], p, cfg.rope_theta)
+            qr[b] = qb
             kb = rope(k[b], p, cfg.rope_theta)
             page, slot = page_slot(block_tables[b], p, P)
             for g in range(KVH):
@@ -271,6 +278,11 @@ def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.nda
         if record:
             tr.x_norm.append(x)
             tr.h_out.append(h.copy())
+            tr.q_rot.append(qr)
+            tr.attn_out.append(o.reshape(B, QH * D))
+            tr.attn_proj.append(a)
+            tr.expert_out.append(outs)
+            tr.moe_out.append(y)
     xf = rmsnorm(h, f(W("gamma_f")), cfg.eps)
     tr.x_final = xf
     logits = xf @ f(W("wlm"))
