@@ -147,6 +147,15 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
  * steps must not be in flight on another stream. */
 mk_status mk_set_mode(mk_handle* h, int mode);
 
+/* Record, for every task of later steps, four uint32 into `trace` (device,
+ * n_records * 4 words): {opcode | layer << 8 | workgroup << 16, start,
+ * dependencies satisfied, end}, times on the 100 MHz device clock (low 32
+ * bits). Megakernel records are indexed like the exported schedule (CU-major),
+ * kernel-per-op records in the flattened task order. NULL stops recording;
+ * a step whose schedule has more tasks than n_records fails with
+ * MK_ERR_INVALID_ARG. */
+mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records);
+
 /* Record every layer's routing of later steps into `trace` (device int32
  * [n_layers][batch][top_k], expert ids in descending router-logit order, ties
  * to the lower id); NULL stops recording. For checking routing decisions. */
@@ -164,11 +173,13 @@ void mk_destroy(mk_handle* h);
 /* Copy `bytes` of one of the library's per-step scratch buffers to host
  * memory after synchronising the device (for op-level checks of the last
  * step's last layer). Names and float32/int32 layouts:
- *   "h" [max_batch][H] residual stream   "xn" [max_batch][H] normalised input
+ *   "h" [max_batch][H] residual stream (after the step: the final layer's)
+ *   "ssq" [max_batch][H/CB] its per column block sums of squares
  *   "q" [max_batch][QH*D] rotated query   "o" [max_batch][QH*D] attention out
  *   "ao" [KVH][max_batch][H] O-proj partial per kv group
- *   "r" [max_batch][E] router logits      "tk_idx"/"tk_w" [max_batch][k]
- *   "route" expert work queue             "u" [max_batch*k][F] expert hidden
+ *   "rp" [K splits][max_batch][E] router logit partial sums
+ *   "tk_idx"/"tk_w" [max_batch][k]        "route" expert work queue
+ *   "gu" [max_batch*k][2][2][F] expert gate/up sums per K half
  *   "dn" [max_batch*k][H] expert outputs (slot b*k + j). */
 mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes);
 

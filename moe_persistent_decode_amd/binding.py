@@ -23,7 +23,7 @@ STEP_ADVANCE = 1
 
 # every function include/mk.h declares
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
-           "mk_decode_step", "mk_set_mode", "mk_set_routing_trace", "mk_sync_status", "mk_last_error", "mk_destroy",
+           "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_sync_status", "mk_last_error", "mk_destroy",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
 
@@ -61,6 +61,7 @@ def _load():
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
     lib.mk_set_mode.argtypes = [H, I]
+    lib.mk_set_task_trace.argtypes = [H, P, S]
     lib.mk_debug_read.argtypes = [H, ctypes.c_char_p, P, S]
     lib.mk_sync_status.argtypes = [H, P]
     lib.mk_last_error.argtypes = [H]
@@ -163,6 +164,9 @@ class Decoder:
 
     def set_mode(self, mode: int):
         self._check(lib.mk_set_mode(self._h, mode))
+
+    def set_task_trace(self, trace, n_records: int = 0):
+        self._check(lib.mk_set_task_trace(self._h, _ptr(trace), n_records))
 
     def set_routing_trace(self, trace):
         self._check(lib.mk_set_routing_trace(self._h, _ptr(trace)))

@@ -122,11 +122,20 @@ struct SmemAttn {
   float o[MK_WAVES][128][17];
 };
 
+// Attention combine scratch: per split and head, the rescale factor.
+#define MK_MAX_SPLITS 256
+struct SmemComb {
+  float f[MK_MAX_SPLITS][16];
+  float M[16];
+  float L[16];
+};
+
 // 96 KB of LDS: more than half of gfx950's 160 KB, so exactly one workgroup
 // fits per compute unit.
 union SmemU {
   float red[MK_WAVES][64];
   SmemAttn at;
+  SmemComb cb;
   float pad[24 * 1024];
 };
 
@@ -137,7 +146,12 @@ struct Smem {
   int ired[MK_WAVES];
   int flag;
   int claim;
-  int cnt[128];
+  int old;                // value an arrival counter held before this workgroup's increment
+  uint32_t t_waited;
+  int xc_layer;           // layer whose normalised input xc holds (-1: none)
+  float ssq[128];
+  float xc[2048];         // normalised input of one layer for batch 1 (per compute unit)
+  float us[768];          // expert hidden of one routed slot (down projection input)
 };
 
 __device__ void raise_error(const mk_params& P, uint32_t code, uint32_t detail, uint32_t value) {
@@ -176,6 +190,7 @@ __device__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32
       }
     }
     sm.flag = ok;
+    sm.t_waited = (uint32_t)__builtin_amdgcn_s_memrealtime();
   }
   __syncthreads();
   const bool ok = sm.flag != 0;
@@ -189,13 +204,6 @@ __device__ __forceinline__ bool wait_task(const mk_params& P, const mk_task& t, 
 
 __device__ __forceinline__ bool wait_one(const mk_params& P, int32_t c, int32_t tgt, Smem& sm) {
   return wait_counters(P, &c, &tgt, 1, sm);
-}
-
-// Count one arrival once every wave's device-coherent stores have completed.
-__device__ void signal_counter(const mk_params& P, int32_t c) {
-  sync_published();
-  if (threadIdx.x == 0 && c >= 0)
-    __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int layer_window(const mk_params& P, int l) {
@@ -282,56 +290,127 @@ __device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0,
   __syncthreads();
 }
 
-// ------------------------------------------------------------------- NORM
-// Residual add of the attention (4 group partials) and MoE (k expert outputs
-// weighted by the router, in rank order) branches, then RMSNorm with the next
-// layer's gain (megakernel post, section "Reduce wave quantization": the
-// parallel layer's branches rejoin in one fused residual add + RMSNorm).
-// Layer 0: the residual is the token's embedding row.
-__device__ void op_norm(const mk_params& P, const mk_task& t, Smem& sm) {
-  if (!wait_task(P, t, sm)) return;
-  const int b = t.a[0], l = t.layer, H = P.H;
-  const Pub h(P.h + (size_t)b * H), ao(P.ao), dn(P.dn), tkw(P.tk_w), xn(P.xn + (size_t)b * H);
-  int tok = 0;
+// ---------------------------------------------------------- arrivals
+// Count one arrival on counter c once every wave's device-coherent stores
+// have completed.
+__device__ void arrive_nr(const mk_params& P, int32_t c) {
+  sync_published();
+  if (threadIdx.x == 0 && c >= 0)
+    __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The same, returning (block-uniform) the value the counter held before this
+// arrival, so the last of a known number of arrivals can act on the result.
+__device__ int arrive(const mk_params& P, int32_t c, Smem& sm) {
+  sync_published();
+  if (threadIdx.x == 0)
+    sm.old = (int)__hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int old = sm.old;
+  __syncthreads();
+  return old;
+}
+
+// ----------------------------------------------------- layer input x-hat
+// The normalised input of layer l (megakernel post, section "Reduce wave
+// quantization": attention and the MoE both read the same RMS-normalised
+// input). Layer 0's residual is the token's embedding row; later layers'
+// residual stream h is complete once every column block's residual add has
+// arrived, each block leaving its sum of squares in ssq. Every compute unit
+// forms x = h / sqrt(mean(h^2) + eps) * gamma_l once per layer into LDS
+// (batch 1), so the fused residual + RMSNorm needs no task of its own.
+__device__ bool load_xhat(const mk_params& P, int l, Smem& sm) {
+  if (sm.xc_layer == l) return true;
+  const int H = P.H;
+  const uint16_t* gam = P.gamma + (size_t)l * H;
+  float v[4];  // H <= 2048 = 4 x 512 threads
+  float ss = 0.f;
   if (l == 0) {
-    tok = P.tokens[b];
+    int tok = P.tokens[0];
     if (tok < 0 || tok >= P.V) {
-      if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 1000 + b, (uint32_t)tok);
+      if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 1000, (uint32_t)tok);
       tok = 0;
     }
-  }
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += MK_WG_THREADS) {
-    float v;
-    if (l == 0) {
-      v = bf2f(P.emb[(size_t)tok * H + i]);
-    } else {
-      float a = 0.f;
-      for (int g = 0; g < P.KVH; ++g) a += ao.ldf((g * P.B + b) * H + i);
-      float y = 0.f;
-      for (int j = 0; j < P.K; ++j) y = fmaf(tkw.ldf(b * P.K + j), dn.ldf((b * P.K + j) * H + i), y);
-      v = (h.ldf(i) + a) + y;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * MK_WG_THREADS;
+      v[k] = i < H ? bf2f(P.emb[(size_t)tok * H + i]) : 0.f;
+      ss = fmaf(v[k], v[k], ss);
     }
-    h.stf(i, v);
-    ss = fmaf(v, v, ss);
+    ss = wave_sum(ss);
+    if (lane_id() == 0) sm.vred[wave_id()] = ss;
+  } else {
+    const Pub h(P.h), q(P.ssq);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * MK_WG_THREADS;
+      v[k] = i < H ? h.ldf(i) : 0.f;
+    }
+    if (threadIdx.x < P.NB) sm.ssq[threadIdx.x] = q.ldf(threadIdx.x);
   }
-  ss = wave_sum(ss);
-  if (lane_id() == 0) sm.vred[wave_id()] = ss;
   __syncthreads();
   float tot = 0.f;
+  if (l == 0) {
 #pragma unroll
-  for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
+    for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
+  } else {
+    for (int k = 0; k < P.NB; ++k) tot += sm.ssq[k];
+  }
   const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
-  const uint16_t* gam = P.gamma + (size_t)l * H;
-  drain_memory();  // this thread's h stores complete before it reads them back
-  for (int i = threadIdx.x; i < H; i += MK_WG_THREADS) xn.stf(i, h.ldf(i) * inv * bf2f(gam[i]));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = threadIdx.x + k * MK_WG_THREADS;
+    if (i < H) sm.xc[i] = v[k] * inv * bf2f(gam[i]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) sm.xc_layer = l;
+  __syncthreads();
+  return true;
+}
+
+// gemv with x from the LDS copy of x-hat (rows 32*c0 .. of the layer input)
+template <int NP, int NCH>
+__device__ void gemv_lds(const WTile<NP, NCH>& w, const float* xl, int np, int c0, int c1, Smem& sm) {
+  const int wv = wave_id(), ln = lane_id();
+  float acc[NP];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) acc[pp] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = c0 + wv + MK_WAVES * i;
+    if (c < c1) {
+      const float4* xp = (const float4*)(xl + c * 32 + 8 * (ln >> 4));
+      const float4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp)
+        if (pp < np) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    acc[pp] += __shfl_xor(acc[pp], 16);
+    acc[pp] += __shfl_xor(acc[pp], 32);
+  }
+  if (ln < 16) {
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+      if (pp < np) sm.u.red[wv][pp * 16 + ln] = acc[pp];
+  }
+  __syncthreads();
+  if (threadIdx.x < np * 16) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k][threadIdx.x];
+    sm.out[threadIdx.x] = s;
+  }
+  __syncthreads();
 }
 
 // -------------------------------------------------------------------- QKV
 // QKV panels with RoPE in the epilogue and the K/V append into the paged
 // cache (megakernel post, section "Tasks": QKV_PROJ applies RoPE in-register
 // in its epilogue; tiny-vllm walkthrough: the new token's K/V are written to
-// page block_table[pos / 16], slot pos % 16, before attention).
+// page block_table[pos / 16], slot pos % 16, before attention reads them).
 template <int NCH>
 __device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, p0 = t.a[0], np = t.a[1];
@@ -340,56 +419,48 @@ __device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
   WTile<2, NCH> w;
   wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
   if (!wait_task(P, t, sm)) return;
+  load_xhat(P, l, sm);
   const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
-  for (int b = 0; b < P.B; ++b) {
-    gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
-    if (wave_id() == 0) {
-      const int tid = threadIdx.x;
-      const float y = tid < np * 16 ? sm.out[tid] : 0.f;
-      const float yp = __shfl_xor(y, 1);
-      const int seq = P.seq_lens[b];
-      if (tid < np * 16) {
-        if (seq < 1 || seq > P.max_seq) {
-          if (tid == 0) raise_error(P, MK_DEVERR_FAULT, 2000 + b, (uint32_t)seq);
-        } else {
-          const int pos = seq - 1;
-          const int n = p0 * 16 + tid;
-          const bool odd = n & 1;
-          if (n < qd + kvd) {
-            const int d = (n < qd ? n : n - qd) % D;
-            const float c = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0];
-            const float s = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1];
-            // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
-            const float x0 = odd ? yp : y, x1 = odd ? y : yp;
-            const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
-            if (n < qd) {
-              Pub(P.q + (size_t)b * qd).stf(n, r);
-            } else {
-              const int g = (n - qd) / D;
-              const int page = P.bt[b * P.mpps + pos / PS];
-              if (page < 0 || page >= P.n_pages) {
-                raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
-              } else {
-                const int off = ((page * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d;
-                Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(r));
-              }
-            }
-          } else {
-            const int nn = n - qd - kvd;
-            const int g = nn / D, d = nn % D;
-            const int page = P.bt[b * P.mpps + pos / PS];
-            if (page < 0 || page >= P.n_pages) {
-              raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
-            } else {
-              const int off = ((page * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS);
-              Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(y));
-            }
+  gemv_lds(w, sm.xc, np, 0, kc, sm);
+  if (wave_id() == 0) {
+    const int tid = threadIdx.x;
+    const float y = tid < np * 16 ? sm.out[tid] : 0.f;
+    const float yp = __shfl_xor(y, 1);
+    const int seq = P.seq_lens[0];
+    if (tid < np * 16) {
+      if (seq < 1 || seq > P.max_seq) {
+        if (tid == 0) raise_error(P, MK_DEVERR_FAULT, 2000, (uint32_t)seq);
+      } else {
+        const int pos = seq - 1;
+        const int n = p0 * 16 + tid;
+        const bool odd = n & 1;
+        const int page = P.bt[pos / PS];
+        const bool page_ok = page >= 0 && page < P.n_pages;
+        if (n < qd + kvd) {
+          const int d = (n < qd ? n : n - qd) % D;
+          const float c = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0];
+          const float s = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1];
+          // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
+          const float x0 = odd ? yp : y, x1 = odd ? y : yp;
+          const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
+          if (n < qd) {
+            Pub(P.q).stf(n, r);
+          } else if (page_ok) {
+            const int g = (n - qd) / D;
+            const int off = ((page * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d;
+            Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(r));
           }
+        } else if (page_ok) {
+          const int nn = n - qd - kvd;
+          const int g = nn / D, d = nn % D;
+          const int off = ((page * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS);
+          Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(y));
         }
+        if (!page_ok && tid == 0) raise_error(P, MK_DEVERR_FAULT, 3000, (uint32_t)page);
       }
     }
-    __syncthreads();
   }
+  arrive_nr(P, t.sig_ctr[0]);
 }
 
 // -------------------------------------------------------------- attention
@@ -398,58 +469,37 @@ __device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
 // KV slices). MFMA with the keys as rows: S^T = K Q^T (16 keys x 16 heads per
 // page, heads >= G padded), online softmax per head, O^T += V^T P^T (V is
 // stored transposed within a page so each lane's operand is 8 contiguous
-// bytes). The 8 waves take alternate pages and merge at the end.
+// bytes). The 8 waves take alternate pages and merge at the end; each wave's
+// first page streams before the dependency wait (the older KV is immutable
+// this step). The split that completes a (sequence, group) merges all splits
+// (ATTN_COMBINE) without a task of its own.
+template <int D>
+__device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm);
+
 template <int D>
 __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
-  const int l = t.layer, b = t.a[0], g = t.a[1], s = t.a[2], pps = t.a[4];
+  const int l = t.layer, b = t.a[0], g = t.a[1], s = t.a[2], ns = t.a[3], pps = t.a[4];
   const int wv = wave_id(), ln = lane_id();
   const int PS = P.PS, G = P.G;
-  if (!wait_task(P, t, sm)) return;
   const int seq = P.seq_lens[b];
-  if (seq < 1 || seq > P.max_seq) {
-    if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
-    return;
-  }
-  const int p = seq - 1;
+  const bool seq_ok = seq >= 1 && seq <= P.max_seq;
+  const int p = seq_ok ? seq - 1 : 0;
   const int win = layer_window(P, l);
   const int lo = win ? max(0, p - win + 1) : 0;
   const int lp_first = lo / PS, lp_last = p / PS;
   const int my0 = lp_first + s * pps;
-  const int my1 = min(my0 + pps, lp_last + 1);
+  const int my1 = seq_ok ? min(my0 + pps, lp_last + 1) : my0;
   const uint16_t* kvl = P.kv + l * P.s_kv_l;
   const size_t plane = (size_t)PS * D;
   const float scale = P.attn_scale;
-
-  // Q^T operand: lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
-  bf16x8_t qb[NC];
-  {
-    const int hh = ln & 15;
-    const Pub Q(P.q + (size_t)b * P.QH * D + (size_t)g * G * D);
-    const int qo = min(hh, G - 1) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float4 a0 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4)), a1 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4) + 4);
-      const float qv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      u32x4_t pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pk[i] = hh < G ? (f2bf(qv[2 * i]) | (f2bf(qv[2 * i + 1]) << 16)) : 0u;
-      qb[c] = __builtin_bit_cast(bf16x8_t, pk);
-    }
-  }
-
-  f32x4_t oacc[NT];
-#pragma unroll
-  for (int d = 0; d < NT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lsum = 0.f;
 
   u32x4_t kr[NC];
   u32x2_t vr[NT];
   bool bad = false;
   // The page holding the current position gets this step's K/V from the QKV
-  // tasks of other compute units: read it device-coherently.
+  // tasks of other compute units: read it device-coherently, after the wait.
   const Pub KV(kvl);
   auto load_page = [&](int lp, u32x4_t* kk, u32x2_t* vv) {
     const int phys = P.bt[b * P.mpps + lp];
@@ -476,7 +526,37 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   };
 
   int lp = my0 + wv;
-  if (lp < my1) load_page(lp, kr, vr);
+  const bool early = lp < my1 && lp != lp_last;
+  if (early) load_page(lp, kr, vr);
+  if (!wait_task(P, t, sm)) return;
+  if (!seq_ok) {
+    if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
+    return;
+  }
+  if (lp < my1 && !early) load_page(lp, kr, vr);
+
+  // Q^T operand: lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
+  bf16x8_t qb[NC];
+  {
+    const int hh = ln & 15;
+    const Pub Q(P.q + (size_t)b * P.QH * D + (size_t)g * G * D);
+    const int qo = min(hh, G - 1) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float4 a0 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4)), a1 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4) + 4);
+      const float qv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      u32x4_t pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = hh < G ? (f2bf(qv[2 * i]) | (f2bf(qv[2 * i + 1]) << 16)) : 0u;
+      qb[c] = __builtin_bit_cast(bf16x8_t, pk);
+    }
+  }
+
+  f32x4_t oacc[NT];
+#pragma unroll
+  for (int d = 0; d < NT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, lsum = 0.f;
+
   while (lp < my1 && !bad) {
     u32x4_t kn[NC];
     u32x2_t vn[NT];
@@ -526,7 +606,7 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   }
   if (bad) raise_error(P, MK_DEVERR_FAULT, 5000 + b, (uint32_t)lp);
 
-  // merge the 8 waves' (m, l, O) per head
+  // merge the 8 waves' (m, l, O) per head into this split's partial
   SmemAttn& A = sm.u.at;
   if (ln < 16) {
     A.m[wv][ln] = m;
@@ -559,79 +639,171 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
       dst.stf(G * D + G + hh, L);
     }
   }
+  const int old = arrive(P, t.a[5], sm);
+  if (old == ns - 1) {
+    attn_combine<D>(P, b, g, ns, sm);
+    arrive_nr(P, t.sig_ctr[0]);
+  }
 }
 
 // Log-sum-exp merge of one (sequence, kv group)'s split partials into the
-// attention output (megakernel post, section "Tasks": ATTN_COMBINE).
-__device__ void op_attn_combine(const mk_params& P, const mk_task& t, Smem& sm) {
-  if (!wait_task(P, t, sm)) return;
-  const int b = t.a[0], g = t.a[1], ns = t.a[2];
-  const int G = P.G, D = P.D;
+// attention output (megakernel post, section "Tasks": ATTN_COMBINE):
+// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, splits in fixed order.
+template <int D>
+__device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm) {
+  const int G = P.G;
   const int stride = G * D + 2 * G;
   const Pub src(P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride);
+  SmemComb& C = sm.u.cb;
+  // split maxima, then per-head M and L
+  for (int i = threadIdx.x; i < ns * G; i += MK_WG_THREADS) {
+    const int s = i / G, hh = i % G;
+    C.f[s][hh] = src.ldf(s * stride + G * D + hh);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x;
+    float M = kNegInf;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, C.f[s][hh]);
+    C.M[hh] = M;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < ns * G; i += MK_WG_THREADS) {
+    const int s = i / G, hh = i % G;
+    const float ms = C.f[s][hh];
+    C.f[s][hh] = ms == kNegInf ? 0.f : __expf(ms - C.M[hh]);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x;
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) L = fmaf(C.f[s][hh], src.ldf(s * stride + G * D + G + hh), L);
+    C.L[hh] = L;
+  }
+  __syncthreads();
   const Pub dst(P.o + (size_t)b * P.QH * D + (size_t)g * G * D);
   for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
     const int hh = idx / D, dd = idx % D;
-    float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, src.ldf(s * stride + G * D + hh));
-    float O = 0.f, L = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = src.ldf(s * stride + G * D + hh);
-      const float f = ms == kNegInf ? 0.f : __expf(ms - M);
-      O = fmaf(f, src.ldf(s * stride + hh * D + dd), O);
-      L = fmaf(f, src.ldf(s * stride + G * D + G + hh), L);
+    float O = 0.f;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = src.ldf((s + k) * stride + hh * D + dd);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) O = fmaf(C.f[s + k][hh], v[k], O);
     }
-    dst.stf(hh * D + dd, O / L);
+    for (; s < ns; ++s) O = fmaf(C.f[s][hh], src.ldf(s * stride + hh * D + dd), O);
+    dst.stf(hh * D + dd, O / C.L[hh]);
+  }
+}
+
+// ------------------------------------------------------------- residual
+// Residual add of one column block, done by whichever contribution to the
+// block arrives last (the KVH O-projection partials and the block's tile of
+// every routed expert's down projection): h += sum_g a_g + sum_j w_j y_j,
+// the experts summed in rank order (MOE_COMBINE), then the block's sum of
+// squares for the next layer's RMSNorm. Layer 0 adds to the embedding row.
+__device__ void residual_block(const mk_params& P, int l, int cb, Smem& sm) {
+  const int H = P.H, K = P.K, CB = P.CB;
+  const Pub h(P.h), ao(P.ao), dn(P.dn), tkw(P.tk_w);
+  float ss = 0.f;
+  const int i = threadIdx.x;
+  if (i < CB) {
+    const int c = cb * CB + i;
+    float a = 0.f;
+    for (int g = 0; g < P.KVH; ++g) a += ao.ldf(g * H + c);
+    float y = 0.f;
+    for (int j = 0; j < K; ++j) y = fmaf(tkw.ldf(j), dn.ldf(j * H + c), y);
+    float h0;
+    if (l == 0) {
+      const int tok = P.tokens[0];
+      h0 = (tok >= 0 && tok < P.V) ? bf2f(P.emb[(size_t)tok * H + c]) : 0.f;
+    } else {
+      h0 = h.ldf(c);
+    }
+    const float v = (h0 + a) + y;
+    h.stf(c, v);
+    ss = v * v;
+  }
+  ss = wave_sum(ss);
+  if (lane_id() == 0) sm.vred[wave_id()] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
+    Pub(P.ssq).stf(cb, tot);
+  }
+}
+
+// After a contribution to column block cb: the last of the block's
+// KVH + n_active contributions does the residual and signals the next layer.
+__device__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base, int cb, Smem& sm) {
+  const int n_active = __builtin_amdgcn_readfirstlane(Pub(P.route).ldi(0));
+  const int old = arrive(P, ctr_base + cb, sm);
+  if (old == P.KVH + n_active - 1) {
+    residual_block(P, t.layer, cb, sm);
+    arrive_nr(P, t.sig_ctr[0]);
   }
 }
 
 // ------------------------------------------------------------------ O proj
-// O projection split-K by kv group: group g's 8 heads contribute their slice
-// of the K dimension as soon as that group's attention lands (megakernel post,
-// section "Drop false dependencies").
+// O projection split-K by kv group: group g's heads contribute their slice
+// of the K dimension as soon as that group's attention lands (megakernel
+// post, section "Drop false dependencies"); one task per (group, column block).
 template <int NCH>
 __device__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int l = t.layer, g = t.a[0], p0 = t.a[1], np = t.a[2];
+  const int l = t.layer, g = t.a[0], cb = t.a[1];
+  const int DP = P.CB / 16, p0 = cb * DP;
   const int kc = P.QH * P.D / 32;
   const int c0 = g * P.G * P.D / 32, c1 = c0 + P.G * P.D / 32;
   const size_t pstride = (size_t)kc * 512;
-  WTile<2, NCH> w;
-  wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, np, c0, c1);
+  WTile<4, NCH> w;
+  wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, DP, c0, c1);
   if (!wait_task(P, t, sm)) return;
-  for (int b = 0; b < P.B; ++b) {
-    gemv_b1(w, P.o + (size_t)b * P.QH * P.D + (size_t)g * P.G * P.D, np, c0, c1, sm);
-    if (threadIdx.x < np * 16) Pub(P.ao + ((size_t)g * P.B + b) * P.H).stf(p0 * 16 + threadIdx.x, sm.out[threadIdx.x]);
-  }
+  gemv_b1(w, P.o + (size_t)g * P.G * P.D, DP, c0, c1, sm);
+  if (threadIdx.x < DP * 16) Pub(P.ao + (size_t)g * P.H).stf(p0 * 16 + threadIdx.x, sm.out[threadIdx.x]);
+  block_arrive(P, t, t.a[2], cb, sm);
 }
 
 // ------------------------------------------------------------------ router
+// Router logits over a K range of a panel range (partial sums); the task that
+// completes the router does ROUTER_TOPK + ROUTE_FINALIZE (megakernel post,
+// section "Tasks"): sum the partials in fixed order, top-k (ties to the lower
+// expert index), softmax over the kept logits, the expert work queue.
+__device__ void topk_finalize(const mk_params& P, int l, Smem& sm);
+
 template <int NCH>
 __device__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int l = t.layer, p0 = t.a[0], np = t.a[1];
+  const int l = t.layer, p0 = t.a[0], np = t.a[1], c0 = t.a[2], c1 = t.a[3], ks = t.a[4];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
   WTile<2, NCH> w;
-  wtile_load(w, P.wr + l * P.s_wr + (size_t)p0 * pstride, pstride, np, 0, kc);
+  wtile_load(w, P.wr + l * P.s_wr + (size_t)p0 * pstride, pstride, np, c0, c1);
   if (!wait_task(P, t, sm)) return;
-  for (int b = 0; b < P.B; ++b) {
-    gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
-    const int n = p0 * 16 + threadIdx.x;
-    if (threadIdx.x < np * 16 && n < P.E) Pub(P.r + (size_t)b * P.E).stf(n, sm.out[threadIdx.x]);
+  load_xhat(P, l, sm);
+  gemv_lds(w, sm.xc, np, c0, c1, sm);
+  const int n = p0 * 16 + threadIdx.x;
+  if (threadIdx.x < np * 16 && n < P.E) Pub(P.rp + (size_t)ks * P.E).stf(n, sm.out[threadIdx.x]);
+  const int old = arrive(P, t.a[5], sm);
+  if (old == P.n_router_tasks - 1) {
+    topk_finalize(P, l, sm);
+    arrive_nr(P, t.sig_ctr[0]);
   }
 }
 
-// Top-k of each token's router logits (ties to the lower expert index), the
-// softmax over the kept logits, then the expert work queue: active experts in
-// ascending id, the token slots routed to each (megakernel post, section
-// "Tasks": ROUTER_TOPK and ROUTE_FINALIZE).
-__device__ void op_topk(const mk_params& P, const mk_task& t, Smem& sm) {
-  if (!wait_task(P, t, sm)) return;
-  const int E = P.E, K = P.K, B = P.B;
+__device__ void topk_finalize(const mk_params& P, int l, Smem& sm) {
+  const int E = P.E, K = P.K;
   const int ln = lane_id();
-  const Pub R(P.r), TI(P.tk_idx), TW(P.tk_w), RT(P.route);
-  for (int b = wave_id(); b < B; b += MK_WAVES) {
-    const float v0 = ln < E ? R.ldf(b * E + ln) : kNegInf;
-    const float v1 = ln + 64 < E ? R.ldf(b * E + ln + 64) : kNegInf;
+  const Pub R(P.rp), TI(P.tk_idx), TW(P.tk_w), RT(P.route);
+  if (wave_id() == 0) {
+    float v0 = 0.f, v1 = 0.f;
+    for (int k = 0; k < P.router_ks; ++k) {
+      if (ln < E) v0 += R.ldf(k * E + ln);
+      if (ln + 64 < E) v1 += R.ldf(k * E + ln + 64);
+    }
+    if (ln >= E) v0 = kNegInf;
+    if (ln + 64 >= E) v1 = kNegInf;
     bool tk0 = ln >= E, tk1 = ln + 64 >= E;
     float sel[MK_MAX_TOPK];
     int idx[MK_MAX_TOPK];
@@ -657,42 +829,30 @@ __device__ void op_topk(const mk_params& P, const mk_task& t, Smem& sm) {
       e[j] = __expf(sel[j] - mx);
       sum += e[j];
     }
-    if (ln == 0)
-      for (int j = 0; j < K; ++j) {
-        TI.sti(b * K + j, idx[j]);
-        TW.stf(b * K + j, e[j] / sum);
-        if (P.tk_trace) P.tk_trace[((size_t)t.layer * B + b) * K + j] = idx[j];
+    // batch 1: the k distinct experts are the active ones; queue them in
+    // ascending expert order, slot j of the token routed to each
+    if (ln < K) {
+      const int j = ln;
+      int my = 0, rank = 0;
+      for (int k = 0; k < K; ++k) {
+        if (k == j) my = idx[k];
       }
-  }
-  sync_published();
-  for (int e = threadIdx.x; e < E; e += MK_WG_THREADS) {
-    int c = 0;
-    for (int i = 0; i < B * K; ++i) c += TI.ldi(i) == e;
-    sm.cnt[e] = c;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int e = 0; e < E; ++e)
-      if (sm.cnt[e] > 0) {
-        RT.sti(4 + n, e);
-        RT.sti(4 + E + n, sm.cnt[e]);
-        sm.cnt[e] = -(n + 1);  // active slot of expert e
-        ++n;
-      }
-    RT.sti(0, n);
-    RT.sti(1, n * P.up_items_per_expert);
-    RT.sti(2, n * P.down_items_per_expert);
-  }
-  __syncthreads();
-  if (threadIdx.x < B * K) {
-    const int i = threadIdx.x;
-    const int e = TI.ldi(i);
-    const int a = -sm.cnt[e] - 1;
-    // rank of this slot among the slots routed to e (ascending slot index)
-    int rank = 0;
-    for (int k = 0; k < i; ++k) rank += TI.ldi(k) == e;
-    RT.sti(4 + 2 * E + a * B + rank, i);
+      for (int k = 0; k < K; ++k) rank += idx[k] < my;
+      TI.sti(j, my);
+      float wj = 0.f;
+      for (int k = 0; k < K; ++k)
+        if (k == j) wj = e[k] / sum;
+      TW.stf(j, wj);
+      RT.sti(4 + rank, my);
+      RT.sti(4 + E + rank, 1);
+      RT.sti(4 + 2 * E + rank * P.B, j);
+      if (P.tk_trace) P.tk_trace[(size_t)l * K + j] = my;
+    }
+    if (ln == 0) {
+      RT.sti(0, K);
+      RT.sti(1, K * P.up_items_per_expert);
+      RT.sti(2, K * P.down_items_per_expert);
+    }
   }
 }
 
@@ -705,74 +865,88 @@ __device__ __forceinline__ int claim(const mk_params& P, int32_t c, Smem& sm) {
   return id;
 }
 
-// Expert up/gate + SiLU-and-multiply, claiming (expert, panel pair) items
-// from the queue ROUTER_TOPK built (megakernel post, section "Tasks":
-// MOE_UPGATE_ACT_DRAIN, and the scheduler section of the Chinese version:
-// claimers atomically take the next queue entry until it is empty).
+// Expert up/gate over one K half of one gate/up panel pair, claimed from the
+// queue ROUTER_TOPK built (megakernel post, section "Tasks":
+// MOE_UPGATE_ACT_DRAIN; the scheduler section of the Chinese version:
+// claimers take the next entry atomically until the queue is empty). The two
+// K halves' gate and up sums are added, and the SiLU-and-multiply applied,
+// by the down projection that consumes them.
 template <int NCH>
 __device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
   const int E = P.E, F = P.F;
-  const int kc = P.H / 32;
+  const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
-  const Pub R(P.route), U(P.u);
+  const Pub R(P.route), GU(P.gu);
   const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(1));
+  load_xhat(P, l, sm);
   for (;;) {
     if (ld_relaxed(&P.err[0]) != 0) return;
     const int id = claim(P, claim_ctr, sm);
     if (id >= n_items) break;
-    const int a = id / P.up_items_per_expert, tt = id % P.up_items_per_expert;
+    const int a = id / P.up_items_per_expert, r = id % P.up_items_per_expert;
+    const int tt = r >> 1, kh = r & 1;
     const int e = __builtin_amdgcn_readfirstlane(R.ldi(4 + a));
+    const int c0 = kh * kh_chunks, c1 = c0 + kh_chunks;
     WTile<2, NCH> w;
-    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride, 2, 0, kc);
-    const int cnt = __builtin_amdgcn_readfirstlane(R.ldi(4 + E + a));
-    for (int r = 0; r < cnt; ++r) {
-      const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B + r));
-      const int b = slot / P.K;
-      gemv_b1(w, P.xn + (size_t)b * P.H, 2, 0, kc, sm);
-      if (threadIdx.x < 16) {
-        const float gt = sm.out[threadIdx.x], up = sm.out[16 + threadIdx.x];
-        U.stf(slot * F + tt * 16 + threadIdx.x, gt / (1.0f + __expf(-gt)) * up);
-      }
+    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride, 2, c0, c1);
+    const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B));
+    gemv_lds(w, sm.xc, 2, c0, c1, sm);
+    // gu[slot][kh][gate|up][F]
+    if (threadIdx.x < 32) {
+      const int which = threadIdx.x >> 4, col = tt * 16 + (threadIdx.x & 15);
+      GU.stf(((slot * 2 + kh) * 2 + which) * F + col, sm.out[threadIdx.x]);
     }
-    signal_counter(P, done_base + a);
+    arrive_nr(P, done_base + a);
   }
 }
 
-// Expert down, claiming (expert, panel group) items. The weights are loaded
-// before waiting for that expert's up/gate items (megakernel post, section
-// "What we have done differently": MoE down streams its weights while
-// up/gate still computes the hidden state it consumes).
+// Expert down over one column block, claiming (expert, block) items. Its
+// weights stream before waiting for that expert's up/gate items (megakernel
+// post, section "What we have done differently": MoE down streams weights
+// while up/gate still computes the hidden state it consumes).
 template <int NCH>
 __device__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
-  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
+  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], blk_base = t.a[2];
   const int E = P.E, F = P.F, H = P.H;
   const int kc = F / 32;
   const size_t pstride = (size_t)kc * 512;
-  const int DP = P.down_panels_per_item;
-  const Pub R(P.route), DN(P.dn);
+  const int DP = P.CB / 16;
+  const Pub R(P.route), DN(P.dn), GU(P.gu);
   const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(2));
   for (;;) {
     if (ld_relaxed(&P.err[0]) != 0) return;
     const int id = claim(P, claim_ctr, sm);
     if (id >= n_items) break;
-    const int a = id / P.down_items_per_expert, tt = id % P.down_items_per_expert;
+    const int a = id / P.down_items_per_expert, cb = id % P.down_items_per_expert;
     const int e = __builtin_amdgcn_readfirstlane(R.ldi(4 + a));
     WTile<4, NCH> w;
-    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(tt * DP) * pstride, pstride, DP, 0, kc);
+    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride, pstride, DP, 0, kc);
     if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
-    const int cnt = __builtin_amdgcn_readfirstlane(R.ldi(4 + E + a));
-    for (int r = 0; r < cnt; ++r) {
-      const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B + r));
-      gemv_b1(w, P.u + (size_t)slot * F, DP, 0, kc, sm);
-      if (threadIdx.x < DP * 16) DN.stf(slot * H + tt * DP * 16 + threadIdx.x, sm.out[threadIdx.x]);
+    const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B));
+    // u = silu(g0 + g1) * (u0 + u1) over F, staged in LDS
+    float* us = sm.us;
+    for (int k = threadIdx.x; k < F; k += MK_WG_THREADS) {
+      const float g0 = GU.ldf(((slot * 2 + 0) * 2 + 0) * F + k), g1 = GU.ldf(((slot * 2 + 1) * 2 + 0) * F + k);
+      const float u0 = GU.ldf(((slot * 2 + 0) * 2 + 1) * F + k), u1 = GU.ldf(((slot * 2 + 1) * 2 + 1) * F + k);
+      const float gt = g0 + g1;
+      us[k] = gt / (1.0f + __expf(-gt)) * (u0 + u1);
     }
+    __syncthreads();
+    gemv_lds(w, us, DP, 0, kc, sm);
+    if (threadIdx.x < DP * 16) DN.stf(slot * H + cb * DP * 16 + threadIdx.x, sm.out[threadIdx.x]);
+    block_arrive(P, t, blk_base, cb, sm);
   }
 }
 
 // ----------------------------------------------------------------- LM head
+// LM head panels with each task's argmax candidate; the task that completes
+// the head picks the greedy token: the largest logit, the lowest index on
+// ties (tiny-vllm walkthrough, section "The remaining layers and logits").
+__device__ void final_argmax(const mk_params& P, Smem& sm);
+
 template <int NCH>
 __device__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
   const int p0 = t.a[0], np = t.a[1], ord = t.a[2];
@@ -781,42 +955,40 @@ __device__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
   WTile<2, NCH> w;
   wtile_load(w, P.wlm + (size_t)p0 * pstride, pstride, np, 0, kc);
   if (!wait_task(P, t, sm)) return;
-  for (int b = 0; b < P.B; ++b) {
-    gemv_b1(w, P.xn + (size_t)b * P.H, np, 0, kc, sm);
-    if (wave_id() == 0) {
-      const int tid = threadIdx.x;
-      float v = kNegInf;
-      int ix = 0x7fffffff;
-      if (tid < np * 16) {
-        v = sm.out[tid];
-        ix = p0 * 16 + tid;
-        P.logits[(size_t)b * P.V + ix] = v;
-      }
+  load_xhat(P, P.L, sm);
+  gemv_lds(w, sm.xc, np, 0, kc, sm);
+  if (wave_id() == 0) {
+    const int tid = threadIdx.x;
+    float v = kNegInf;
+    int ix = 0x7fffffff;
+    if (tid < np * 16) {
+      v = sm.out[tid];
+      ix = p0 * 16 + tid;
+      P.logits[ix] = v;
+    }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(v, o);
-        const int oi = __shfl_xor(ix, o);
-        if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
-      }
-      if (tid == 0) {
-        Pub(P.lm_val).stf(b * P.n_lm_tasks + ord, v);
-        Pub(P.lm_arg).sti(b * P.n_lm_tasks + ord, ix);
-      }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(v, o);
+      const int oi = __shfl_xor(ix, o);
+      if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
+    }
+    if (tid == 0) {
+      Pub(P.lm_val).stf(ord, v);
+      Pub(P.lm_arg).sti(ord, ix);
     }
   }
+  const int old = arrive(P, t.a[3], sm);
+  if (old == P.n_lm_tasks - 1) final_argmax(P, sm);
 }
 
-// Greedy token: the largest logit, the lowest index on ties (tiny-vllm
-// walkthrough, section "The remaining layers and logits").
-__device__ void op_argmax(const mk_params& P, const mk_task& t, Smem& sm) {
-  if (!wait_task(P, t, sm)) return;
-  const int b = t.a[0], n = P.n_lm_tasks;
+__device__ void final_argmax(const mk_params& P, Smem& sm) {
+  const int n = P.n_lm_tasks;
+  const Pub LV(P.lm_val), LA(P.lm_arg);
   float v = kNegInf;
   int ix = 0x7fffffff;
-  const Pub LV(P.lm_val), LA(P.lm_arg);
   for (int i = threadIdx.x; i < n; i += MK_WG_THREADS) {
-    const float cv = LV.ldf(b * n + i);
-    const int ci = LA.ldi(b * n + i);
+    const float cv = LV.ldf(i);
+    const int ci = LA.ldi(i);
     if (cv > v || (cv == v && ci < ix)) { v = cv; ix = ci; }
   }
 #pragma unroll
@@ -833,10 +1005,10 @@ __device__ void op_argmax(const mk_params& P, const mk_task& t, Smem& sm) {
   if (threadIdx.x == 0) {
     for (int k = 0; k < MK_WAVES; ++k)
       if (sm.vred[k] > v || (sm.vred[k] == v && sm.ired[k] < ix)) { v = sm.vred[k]; ix = sm.ired[k]; }
-    if (P.next_tokens) P.next_tokens[b] = ix;
+    if (P.next_tokens) P.next_tokens[0] = ix;
     if (P.flags & 1u) {
-      P.tokens[b] = ix;
-      P.seq_lens[b] = P.seq_lens[b] + 1;
+      P.tokens[0] = ix;
+      P.seq_lens[0] = P.seq_lens[0] + 1;
     }
   }
 }
@@ -846,17 +1018,13 @@ __device__ void op_argmax(const mk_params& P, const mk_task& t, Smem& sm) {
 template <int D>
 __device__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
   switch (t.op) {
-    case MK_OP_NORM: op_norm(P, t, sm); break;
     case MK_OP_QKV: op_qkv<8>(P, t, sm); break;
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
-    case MK_OP_ATTN_COMBINE: op_attn_combine(P, t, sm); break;
     case MK_OP_OPROJ: op_oproj<4>(P, t, sm); break;
     case MK_OP_ROUTER: op_router<8>(P, t, sm); break;
-    case MK_OP_TOPK: op_topk(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe_up<8>(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe_up<4>(P, t, sm); break;
     case MK_OP_MOE_DOWN: op_moe_down<3>(P, t, sm); break;
     case MK_OP_LMHEAD: op_lmhead<8>(P, t, sm); break;
-    case MK_OP_ARGMAX: op_argmax(P, t, sm); break;
     default: wait_task(P, t, sm); break;
   }
 }
@@ -867,17 +1035,26 @@ __device__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
 template <int D>
 __global__ __launch_bounds__(MK_WG_THREADS) void mk_interp(mk_params P) {
   __shared__ Smem sm;
+  if (threadIdx.x == 0) sm.xc_layer = -1;
   if (P.ctr_clear) {
     for (int i = blockIdx.x * MK_WG_THREADS + threadIdx.x; i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
       P.ctr_clear[i] = 0u;
   }
+  __syncthreads();
   const int beg = P.task_off[blockIdx.x], end = P.task_off[blockIdx.x + 1];
   for (int i = beg; i < end; ++i) {
     const mk_task& t = P.tasks[i];
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
     run_task<D>(P, t, sm);
-    if (t.sig_ctr[0] >= 0) signal_counter(P, t.sig_ctr[0]);
-    if (t.sig_ctr[1] >= 0) signal_counter(P, t.sig_ctr[1]);
     __syncthreads();
+    if (P.trace && threadIdx.x == 0) {
+      // per-task timestamps (100 MHz device clock): start, waits satisfied, end
+      uint32_t* rec = P.trace + (size_t)(P.trace_base + i) * 4;
+      rec[0] = (uint32_t)t.op | ((uint32_t)t.layer << 8) | ((uint32_t)blockIdx.x << 16);
+      rec[1] = t0;
+      rec[2] = sm.t_waited;
+      rec[3] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+    }
   }
 }
 

@@ -36,11 +36,11 @@ thread_local std::string g_create_error;
 struct Schedule {
   int B = 0, bucket = 0;
   int n_splits_full = 0, n_splits_win = 0, pps = 16;
-  int n_qkv_tasks_per_group = 0;
   int n_router = 0, n_oproj = 0, n_up_claimers = 0, n_down_claimers = 0, n_lm = 0;
+  std::vector<int> n_qkv;  // QKV tasks per kv group
   int n_ctr = 0;
   // counter layout
-  int c_norm0 = 0, c_lm = 0, c_layer0 = 0, c_per_layer = 0;
+  int c_resid0 = 0, c_lm = 0, c_layer0 = 0, c_per_layer = 0;
   // flattened list, its waves (for kernel-per-op) and per-CU lists
   std::vector<mk_task> flat;
   std::vector<int> flat_wave;
@@ -53,8 +53,16 @@ struct Schedule {
   mk_task* d_flat = nullptr;
 };
 
+// Counters of one layer (indices into the counter array).
 struct CtrIdx {
-  int qkv, attn, comb, oproj, router, route, up_claim, down_claim, down_exit, up_done;
+  int qkv;       // [KVH] QKV tasks done per kv group
+  int attn;      // [B][KVH] attention splits done per (sequence, group)
+  int comb;      // [KVH] combined attention outputs per group
+  int router;    // router tasks done
+  int route;     // route finalized (1)
+  int up_claim, down_claim;  // claim counters of the two expert queues
+  int up_done;   // [E] up/gate items done per active expert slot
+  int colblk;    // [NB] contributions per residual column block
 };
 
 mk_task make_task(int op, int layer) {
@@ -90,7 +98,8 @@ struct mk_handle {
   std::string err;
   // derived
   int G = 0, qkv_dim = 0, q_dim = 0, kv_dim = 0, e_pad = 0;
-  int max_splits = 0, pps = 16, down_panels = 4, n_lm_tasks = 0, lm_np = 2;
+  int max_splits = 0, pps = 16, n_lm_tasks = 0, lm_np = 2;
+  int CB = 64, NB = 32, router_np = 2, router_ks = 4, n_router_tasks = 0;
   // device memory
   uint16_t* w_all = nullptr;
   size_t s_wqkv = 0, s_wo = 0, s_wr = 0, s_wgu_l = 0, s_wgu_e = 0, s_wd_l = 0, s_wd_e = 0;
@@ -99,8 +108,8 @@ struct mk_handle {
   float* rope = nullptr;
   uint16_t* kv = nullptr;
   void* scratch = nullptr;
-  float *h = nullptr, *xn = nullptr, *q = nullptr, *part = nullptr, *o = nullptr, *ao = nullptr, *r = nullptr,
-        *tk_w = nullptr, *u = nullptr, *dn = nullptr, *lm_val = nullptr;
+  float *h = nullptr, *q = nullptr, *part = nullptr, *o = nullptr, *ao = nullptr, *ssq = nullptr, *rp = nullptr,
+        *tk_w = nullptr, *gu = nullptr, *dn = nullptr, *lm_val = nullptr;
   int32_t *tk_idx = nullptr, *route = nullptr, *lm_arg = nullptr;
   uint32_t* ctr[2] = {nullptr, nullptr};
   int n_ctr_cap = 0;
@@ -112,6 +121,8 @@ struct mk_handle {
   uint64_t steps = 0;
   int64_t timeout_ticks = 200000000;  // 2 s at 100 MHz
   int32_t* tk_trace = nullptr;
+  uint32_t* task_trace = nullptr;
+  size_t task_trace_cap = 0;
   std::map<std::pair<int, int>, std::unique_ptr<Schedule>> scheds;
 };
 
@@ -179,12 +190,20 @@ void derive(mk_handle* h) {
   h->kv_dim = c.n_kv_heads * c.head_dim;
   h->qkv_dim = h->q_dim + 2 * h->kv_dim;
   h->e_pad = ceil_div(c.n_experts, 16) * 16;  // router columns padded to whole panels
-  h->pps = 16;
+  // attention: 16 pages per split, more when a context would need more
+  // than MK_MAX_SPLITS splits (the combine keeps one factor per split in LDS)
   const int pages = ceil_div(c.max_seq_len, c.page_size) + 1;
+  h->pps = std::max(16, ceil_div(pages, 256));
   h->max_splits = ceil_div(pages, h->pps);
-  h->down_panels = 4;
   h->lm_np = 2;
   h->n_lm_tasks = ceil_div(c.vocab / 16, h->lm_np);
+  // residual column blocks of 64 columns (4 panels) when the width allows
+  h->CB = c.hidden >= 1024 ? 64 : 32;
+  h->NB = c.hidden / h->CB;
+  // router: 2-panel tasks over K quarters (K halves for a small hidden size)
+  h->router_np = 2;
+  h->router_ks = c.hidden >= 1024 ? 4 : 2;
+  h->n_router_tasks = ceil_div(h->e_pad / 16, h->router_np) * h->router_ks;
 }
 
 int window_of(const mk_config& c, int l) {
@@ -208,19 +227,20 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   S->B = B;
   S->bucket = std::min(bucket_of(hint), c.max_seq_len);
   S->pps = h->pps;
-  const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts, H = c.hidden;
-  const int n_cu = h->n_cu;
-  const int router_panels = h->e_pad / 16;
+  const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
+  const int n_cu = h->n_cu, NB = h->NB;
+  const int kc = c.hidden / 32;
 
-  // counter layout
+  // counter layout: resid_done[l] for l = 1..L (index l - 1), lm, then per layer
   int idx = 0;
-  S->c_norm0 = idx;
-  idx += L + 1;
+  S->c_resid0 = idx;
+  idx += L;
   S->c_lm = idx++;
   S->c_layer0 = idx;
-  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + 1 + 1 + E;
+  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + E + NB;
   idx += L * S->c_per_layer;
   S->n_ctr = idx;
+  auto resid = [&](int l) { return S->c_resid0 + l - 1; };  // input of layer l ready (l >= 1)
   auto ci = [&](int l) {
     CtrIdx x;
     int b0 = S->c_layer0 + l * S->c_per_layer;
@@ -230,13 +250,13 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     b0 += B * KVH;
     x.comb = b0;
     b0 += KVH;
-    x.oproj = b0++;
     x.router = b0++;
     x.route = b0++;
     x.up_claim = b0++;
     x.down_claim = b0++;
-    x.down_exit = b0++;
     x.up_done = b0;
+    b0 += E;
+    x.colblk = b0;
     return x;
   };
 
@@ -249,69 +269,53 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
 
   S->n_up_claimers = n_cu;
   S->n_down_claimers = n_cu;
-  const int qkv_np = 1, oproj_np = 2, router_np = 1;
+  const int qkv_np = 1;
+  S->n_qkv.assign(KVH, 0);
 
-  // layer-0 input: embedding + RMSNorm
-  begin_wave();
-  for (int b = 0; b < B; ++b) {
-    mk_task t = make_task(MK_OP_NORM, 0);
-    t.a[0] = b;
-    t.sig_ctr[0] = S->c_norm0 + 0;
-    push(t);
-  }
   for (int l = 0; l < L; ++l) {
     const CtrIdx x = ci(l);
-    const int norm_c = S->c_norm0 + l;
+    auto wait_input = [&](mk_task& t) {
+      if (l > 0) add_wait(t, resid(l), NB);
+    };
     // qkv, per kv group: its q heads, its k head, its v head
     begin_wave();
-    std::vector<int> n_qkv(KVH, 0);
     for (int g = 0; g < KVH; ++g) {
       const int ranges[3][2] = {{g * h->G * c.head_dim / 16, (g + 1) * h->G * c.head_dim / 16},
                                 {(h->q_dim + g * c.head_dim) / 16, (h->q_dim + (g + 1) * c.head_dim) / 16},
                                 {(h->q_dim + h->kv_dim + g * c.head_dim) / 16,
                                  (h->q_dim + h->kv_dim + (g + 1) * c.head_dim) / 16}};
-      for (auto& rg : ranges)
-        for (int p = rg[0]; p < rg[1]; p += qkv_np) ++n_qkv[g];
-    }
-    for (int g = 0; g < KVH; ++g) {
-      const int ranges[3][2] = {{g * h->G * c.head_dim / 16, (g + 1) * h->G * c.head_dim / 16},
-                                {(h->q_dim + g * c.head_dim) / 16, (h->q_dim + (g + 1) * c.head_dim) / 16},
-                                {(h->q_dim + h->kv_dim + g * c.head_dim) / 16,
-                                 (h->q_dim + h->kv_dim + (g + 1) * c.head_dim) / 16}};
+      int n = 0;
       for (auto& rg : ranges)
         for (int p = rg[0]; p < rg[1]; p += qkv_np) {
           mk_task t = make_task(MK_OP_QKV, l);
           t.a[0] = p;
           t.a[1] = std::min(qkv_np, rg[1] - p);
           t.a[2] = g;
-          add_wait(t, norm_c, B);
+          wait_input(t);
           t.sig_ctr[0] = x.qkv + g;
           push(t);
+          ++n;
         }
+      S->n_qkv[g] = n;
     }
-    S->n_qkv_tasks_per_group = n_qkv[0];
-    // router
+    // router over K splits; the last one does top-k and route finalize
     begin_wave();
-    int n_router = 0;
-    for (int p = 0; p < router_panels; p += router_np) {
-      mk_task t = make_task(MK_OP_ROUTER, l);
-      t.a[0] = p;
-      t.a[1] = std::min(router_np, router_panels - p);
-      add_wait(t, norm_c, B);
-      t.sig_ctr[0] = x.router;
-      push(t);
-      ++n_router;
-    }
-    S->n_router = n_router;
-    // top-k + route finalize
-    begin_wave();
-    {
-      mk_task t = make_task(MK_OP_TOPK, l);
-      add_wait(t, x.router, n_router);
-      t.sig_ctr[0] = x.route;
-      push(t);
-    }
-    // attention splits
+    const int rpanels = h->e_pad / 16;
+    for (int ks = 0; ks < h->router_ks; ++ks)
+      for (int p = 0; p < rpanels; p += h->router_np) {
+        mk_task t = make_task(MK_OP_ROUTER, l);
+        t.a[0] = p;
+        t.a[1] = std::min(h->router_np, rpanels - p);
+        t.a[2] = ks * kc / h->router_ks;
+        t.a[3] = (ks + 1) * kc / h->router_ks;
+        t.a[4] = ks;
+        t.a[5] = x.router;
+        wait_input(t);
+        t.sig_ctr[0] = x.route;
+        push(t);
+      }
+    S->n_router = h->n_router_tasks;
+    // attention splits; the last split of a (sequence, group) combines
     begin_wave();
     const int ns = splits_for(h, l, S->bucket);
     if (window_of(c, l))
@@ -327,8 +331,9 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           t.a[2] = s;
           t.a[3] = ns;
           t.a[4] = h->pps;
-          add_wait(t, x.qkv + g, n_qkv[g]);
-          t.sig_ctr[0] = x.attn + b * KVH + g;
+          t.a[5] = x.attn + b * KVH + g;
+          add_wait(t, x.qkv + g, S->n_qkv[g]);
+          t.sig_ctr[0] = x.comb + g;
           push(t);
         }
     // MoE up/gate claimers
@@ -340,55 +345,35 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       add_wait(t, x.route, 1);
       push(t);
     }
-    // MoE down claimers
+    // MoE down claimers (their last block contribution does the residual)
     begin_wave();
     for (int i = 0; i < S->n_down_claimers; ++i) {
       mk_task t = make_task(MK_OP_MOE_DOWN, l);
       t.a[0] = x.down_claim;
       t.a[1] = x.up_done;
+      t.a[2] = x.colblk;
       add_wait(t, x.route, 1);
-      t.sig_ctr[0] = x.down_exit;
+      t.sig_ctr[0] = resid(l + 1);
       push(t);
     }
-    // attention combine
-    begin_wave();
-    for (int b = 0; b < B; ++b)
-      for (int g = 0; g < KVH; ++g) {
-        mk_task t = make_task(MK_OP_ATTN_COMBINE, l);
-        t.a[0] = b;
-        t.a[1] = g;
-        t.a[2] = ns;
-        add_wait(t, x.attn + b * KVH + g, ns);
-        t.sig_ctr[0] = x.comb + g;
-        push(t);
-      }
-    // O projection, split-K per kv group
+    // O projection per (group, column block)
     begin_wave();
     int n_oproj = 0;
     for (int g = 0; g < KVH; ++g)
-      for (int p = 0; p < H / 16; p += oproj_np) {
+      for (int cb = 0; cb < NB; ++cb) {
         mk_task t = make_task(MK_OP_OPROJ, l);
         t.a[0] = g;
-        t.a[1] = p;
-        t.a[2] = std::min(oproj_np, H / 16 - p);
+        t.a[1] = cb;
+        t.a[2] = x.colblk;
         add_wait(t, x.comb + g, B);
-        t.sig_ctr[0] = x.oproj;
+        add_wait(t, x.route, 1);
+        t.sig_ctr[0] = resid(l + 1);
         push(t);
         ++n_oproj;
       }
     S->n_oproj = n_oproj;
-    // residual + RMSNorm -> next layer's input (or the final norm)
-    begin_wave();
-    for (int b = 0; b < B; ++b) {
-      mk_task t = make_task(MK_OP_NORM, l + 1);
-      t.a[0] = b;
-      add_wait(t, x.oproj, n_oproj);
-      add_wait(t, x.down_exit, S->n_down_claimers);
-      t.sig_ctr[0] = S->c_norm0 + l + 1;
-      push(t);
-    }
   }
-  // LM head + greedy token
+  // LM head; the last task picks the greedy token
   begin_wave();
   S->n_lm = 0;
   for (int p = 0, ord = 0; p < c.vocab / 16; p += h->lm_np, ++ord) {
@@ -396,17 +381,10 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     t.a[0] = p;
     t.a[1] = std::min(h->lm_np, c.vocab / 16 - p);
     t.a[2] = ord;
-    add_wait(t, S->c_norm0 + L, B);
-    t.sig_ctr[0] = S->c_lm;
+    t.a[3] = S->c_lm;
+    add_wait(t, resid(L), NB);
     push(t);
     ++S->n_lm;
-  }
-  begin_wave();
-  for (int b = 0; b < B; ++b) {
-    mk_task t = make_task(MK_OP_ARGMAX, L);
-    t.a[0] = b;
-    add_wait(t, S->c_lm, S->n_lm);
-    push(t);
   }
 
   // round-robin placement of the flattened list
@@ -420,20 +398,20 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   return S;
 }
 
-// Host model of the device: per-CU in-order lists, counters, claim queues.
+// Host model of the device: per-CU in-order lists, counters, claim queues and
+// the last-arrival actions, with CUs advancing in a seeded random order.
 struct SimCU {
-  int pos = 0;
-  // claimer state
   bool in_claimer = false;
   int pending_item = -1;  // claimed down item waiting for its expert's up items
+  int pos = 0;
 };
 
 mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uint64_t seed, int corrupt,
                    std::string& rep) {
   const mk_config& c = h->cfg;
-  const int n_cu = h->n_cu, L = c.n_layers, E = c.n_experts, KVH = c.n_kv_heads;
-  const int F = c.expert_ffn, H = c.hidden;
-  const int up_per_e = F / 16, down_per_e = H / 16 / h->down_panels;
+  const int n_cu = h->n_cu, L = c.n_layers, E = c.n_experts, KVH = c.n_kv_heads, NB = h->NB;
+  const int F = c.expert_ffn;
+  const int up_per_e = 2 * F / 16, down_per_e = NB;
   std::vector<mk_task> tasks = S.cu_tasks;
   if (corrupt >= 0 && corrupt < (int)tasks.size()) {
     // make the first wait of that task unsatisfiable by one arrival
@@ -446,11 +424,15 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   std::vector<int64_t> ctr(S.n_ctr, 0);
   std::vector<SimCU> cu(n_cu);
   std::mt19937_64 rng(seed);
-  auto layer_of_claim = [&](int counter) { return (counter - S.c_layer0) / S.c_per_layer; };
+  auto layer_of = [&](int counter) { return (counter - S.c_layer0) / S.c_per_layer; };
   auto waits_met = [&](const mk_task& t) {
     for (int i = 0; i < 3; ++i)
       if (t.wait_ctr[i] >= 0 && ctr[t.wait_ctr[i]] < t.wait_tgt[i]) return false;
     return true;
+  };
+  // one contribution to a residual column block; the last one signals
+  auto block = [&](const mk_task& t, int base, int cb, int l) {
+    if (++ctr[base + cb] == KVH + n_active[l]) ctr[t.sig_ctr[0]]++;
   };
   int64_t remaining = (int64_t)tasks.size();
   std::vector<int> order(n_cu);
@@ -463,54 +445,71 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       const int beg = S.cu_off[k], end = S.cu_off[k + 1];
       if (beg + u.pos >= end) continue;
       const mk_task& t = tasks[beg + u.pos];
-      if (!u.in_claimer) {
-        if (!waits_met(t)) continue;
-        if (t.op == MK_OP_MOE_UP || t.op == MK_OP_MOE_DOWN) {
-          u.in_claimer = true;
-          progress = true;
-          continue;
-        }
-        for (int i = 0; i < 2; ++i)
-          if (t.sig_ctr[i] >= 0) ctr[t.sig_ctr[i]]++;
+      auto done = [&]() {
         u.pos++;
         remaining--;
         progress = true;
+      };
+      if (!u.in_claimer) {
+        if (!waits_met(t)) continue;
+        switch (t.op) {
+          case MK_OP_QKV:
+            ctr[t.sig_ctr[0]]++;
+            done();
+            break;
+          case MK_OP_ROUTER:
+            if (++ctr[t.a[5]] == h->n_router_tasks) ctr[t.sig_ctr[0]]++;
+            done();
+            break;
+          case MK_OP_ATTN:
+            if (++ctr[t.a[5]] == t.a[3]) ctr[t.sig_ctr[0]]++;
+            done();
+            break;
+          case MK_OP_OPROJ:
+            block(t, t.a[2], t.a[1], t.layer);
+            done();
+            break;
+          case MK_OP_LMHEAD:
+            ctr[t.a[3]]++;
+            done();
+            break;
+          case MK_OP_MOE_UP:
+          case MK_OP_MOE_DOWN:
+            u.in_claimer = true;
+            progress = true;
+            break;
+          default:
+            done();
+        }
         continue;
       }
       // claimer step
-      const int l = layer_of_claim(t.a[0]);
+      const int l = layer_of(t.a[0]);
       const int na = n_active[l];
       if (t.op == MK_OP_MOE_UP) {
         const int id = (int)ctr[t.a[0]]++;
         if (id >= na * up_per_e) {
           u.in_claimer = false;
-          for (int i = 0; i < 2; ++i)
-            if (t.sig_ctr[i] >= 0) ctr[t.sig_ctr[i]]++;
-          u.pos++;
-          remaining--;
+          done();
         } else {
           ctr[t.a[1] + id / up_per_e]++;
-        }
-        progress = true;
-      } else {
-        if (u.pending_item < 0) {
-          const int id = (int)ctr[t.a[0]]++;
           progress = true;
-          if (id >= na * down_per_e) {
-            u.in_claimer = false;
-            for (int i = 0; i < 2; ++i)
-              if (t.sig_ctr[i] >= 0) ctr[t.sig_ctr[i]]++;
-            u.pos++;
-            remaining--;
-          } else {
-            u.pending_item = id;
-          }
+        }
+      } else if (u.pending_item < 0) {
+        const int id = (int)ctr[t.a[0]]++;
+        progress = true;
+        if (id >= na * down_per_e) {
+          u.in_claimer = false;
+          done();
         } else {
-          const int a = u.pending_item / down_per_e;
-          if (ctr[t.a[1] + a] >= up_per_e) {
-            u.pending_item = -1;
-            progress = true;
-          }
+          u.pending_item = id;
+        }
+      } else {
+        const int a = u.pending_item / down_per_e, cb = u.pending_item % down_per_e;
+        if (ctr[t.a[1] + a] >= up_per_e) {
+          block(t, t.a[2], cb, l);
+          u.pending_item = -1;
+          progress = true;
         }
       }
     }
@@ -521,25 +520,23 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       return MK_ERR_DEVICE_TIMEOUT;
     }
   }
-  // final counter values against their expected arrivals
+  // every counter against the arrivals it must receive
   const int B = S.B;
   std::vector<int64_t> want(S.n_ctr, 0);
-  for (int l = 0; l <= L; ++l) want[S.c_norm0 + l] = B;
+  for (int l = 1; l <= L; ++l) want[S.c_resid0 + l - 1] = NB;
   want[S.c_lm] = S.n_lm;
   for (int l = 0; l < L; ++l) {
-    const int b0 = S.c_layer0 + l * S.c_per_layer;
     const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
-    int k = b0;
-    for (int g = 0; g < KVH; ++g) want[k++] = (h->qkv_dim / 16) / KVH;
+    int k = S.c_layer0 + l * S.c_per_layer;
+    for (int g = 0; g < KVH; ++g) want[k++] = (h->G * c.head_dim + 2 * c.head_dim) / 16;
     for (int i = 0; i < B * KVH; ++i) want[k++] = ns;
     for (int g = 0; g < KVH; ++g) want[k++] = B;
-    want[k++] = (int64_t)KVH * (H / 16 / 2);  // oproj tiles, 2 panels each
-    want[k++] = h->e_pad / 16;              // router tiles
-    want[k++] = 1;                          // route finalize
+    want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
+    want[k++] = 1;                                                   // route finalized
     want[k++] = (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
     want[k++] = (int64_t)n_active[l] * down_per_e + S.n_down_claimers;
-    want[k++] = S.n_down_claimers;
     for (int a = 0; a < E; ++a) want[k++] = a < n_active[l] ? up_per_e : 0;
+    for (int cb = 0; cb < NB; ++cb) want[k++] = KVH + n_active[l];
   }
   for (int i = 0; i < S.n_ctr; ++i)
     if (ctr[i] != want[i]) {
@@ -703,35 +700,35 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     so += align_up(bytes, 256);
     return o;
   };
-  const size_t s_h = stake((size_t)Bm * H * 4), s_xn = stake((size_t)Bm * H * 4);
+  const size_t s_h = stake((size_t)Bm * H * 4), s_ssq = stake((size_t)Bm * h->NB * 4);
   const size_t s_q = stake((size_t)Bm * h->q_dim * 4), s_o = stake((size_t)Bm * h->q_dim * 4);
   const size_t s_part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
-  const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_r = stake((size_t)Bm * E * 4);
+  const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_rp = stake((size_t)h->router_ks * Bm * E * 4);
   const size_t s_tki = stake((size_t)Bm * K * 4), s_tkw = stake((size_t)Bm * K * 4);
   const size_t s_route = stake((size_t)MK_ROUTE_INTS(E, Bm) * 4);
-  const size_t s_u = stake((size_t)Bm * K * F * 4), s_dn = stake((size_t)Bm * K * H * 4);
+  const size_t s_gu = stake((size_t)Bm * K * 4 * F * 4), s_dn = stake((size_t)Bm * K * H * 4);
   const size_t s_lmv = stake((size_t)Bm * h->n_lm_tasks * 4), s_lma = stake((size_t)Bm * h->n_lm_tasks * 4);
   const size_t s_err = stake(16);
   if (hipMalloc(&h->scratch, so) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "scratch");
   hipMemset(h->scratch, 0, so);
   char* sb = (char*)h->scratch;
   h->h = (float*)(sb + s_h);
-  h->xn = (float*)(sb + s_xn);
+  h->ssq = (float*)(sb + s_ssq);
   h->q = (float*)(sb + s_q);
   h->o = (float*)(sb + s_o);
   h->part = (float*)(sb + s_part);
   h->ao = (float*)(sb + s_ao);
-  h->r = (float*)(sb + s_r);
+  h->rp = (float*)(sb + s_rp);
   h->tk_idx = (int32_t*)(sb + s_tki);
   h->tk_w = (float*)(sb + s_tkw);
   h->route = (int32_t*)(sb + s_route);
-  h->u = (float*)(sb + s_u);
+  h->gu = (float*)(sb + s_gu);
   h->dn = (float*)(sb + s_dn);
   h->lm_val = (float*)(sb + s_lmv);
   h->lm_arg = (int32_t*)(sb + s_lma);
   h->err_word = (uint32_t*)(sb + s_err);
   // counters: capacity for the largest batch
-  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 6 + E);
+  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 4 + E + h->NB);
   for (int i = 0; i < 2; ++i) {
     if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
     hipMemset(h->ctr[i], 0, (size_t)h->n_ctr_cap * 4);
@@ -849,9 +846,12 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.mpps = c.max_pages_per_seq;
   P.n_pages = c.n_pages;
   P.max_seq = std::min(S->bucket, c.max_seq_len);
-  P.up_items_per_expert = c.expert_ffn / 16;
-  P.down_panels_per_item = h->down_panels;
-  P.down_items_per_expert = c.hidden / 16 / h->down_panels;
+  P.up_items_per_expert = 2 * c.expert_ffn / 16;
+  P.down_items_per_expert = h->NB;
+  P.CB = h->CB;
+  P.NB = h->NB;
+  P.n_router_tasks = h->n_router_tasks;
+  P.router_ks = h->router_ks;
   P.max_splits = h->max_splits;
   P.n_lm_tasks = S->n_lm;
   P.e_pad = h->e_pad;
@@ -880,17 +880,18 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.next_tokens = next_tokens;
   P.flags = flags;
   P.h = h->h;
-  P.xn = h->xn;
+  P.ssq = h->ssq;
   P.q = h->q;
   P.part = h->part;
   P.o = h->o;
   P.ao = h->ao;
-  P.r = h->r;
+  P.rp = h->rp;
   P.tk_idx = h->tk_idx;
   P.tk_w = h->tk_w;
   P.tk_trace = h->tk_trace;
+  P.trace = h->task_trace;
   P.route = h->route;
-  P.u = h->u;
+  P.gu = h->gu;
   P.dn = h->dn;
   P.lm_val = h->lm_val;
   P.lm_arg = h->lm_arg;
@@ -919,6 +920,9 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
   Schedule* S = nullptr;
   mk_status st = get_schedule(h, batch, max_seq_len_hint, &S);
   if (st != MK_OK) return st;
+  if (h->task_trace && S->cu_tasks.size() > h->task_trace_cap)
+    return fail(h, MK_ERR_INVALID_ARG, "task trace holds %zu records, the schedule has %zu tasks", h->task_trace_cap,
+                S->cu_tasks.size());
   HIPCHECK(h, hipSetDevice(h->device));
   hipStream_t s = (hipStream_t)stream;
   mk_params P;
@@ -940,11 +944,19 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
       const int b0 = S->waves[w].first, n = S->waves[w].second - S->waves[w].first;
       if (n == 0) continue;
       P.tasks = S->d_flat + b0;
+      P.trace_base = b0;
       P.ctr_clear = (w == 0) ? h->ctr[nxt] : nullptr;
       HIPCHECK(h, mk_launch_interp(P, c.head_dim, n, false, s));
     }
   }
   h->steps++;
+  return MK_OK;
+}
+
+mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  h->task_trace = trace;
+  h->task_trace_cap = trace ? n_records : 0;
   return MK_OK;
 }
 
@@ -987,15 +999,15 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
   struct Item { const char* n; const void* p; size_t sz; };
   const Item items[] = {
       {"h", h->h, Bm * H * 4},
-      {"xn", h->xn, Bm * H * 4},
+      {"ssq", h->ssq, Bm * h->NB * 4},
       {"q", h->q, Bm * h->q_dim * 4},
       {"o", h->o, Bm * h->q_dim * 4},
       {"ao", h->ao, (size_t)c.n_kv_heads * Bm * H * 4},
-      {"r", h->r, Bm * E * 4},
+      {"rp", h->rp, (size_t)h->router_ks * Bm * E * 4},
       {"tk_idx", h->tk_idx, Bm * K * 4},
       {"tk_w", h->tk_w, Bm * K * 4},
       {"route", h->route, (size_t)MK_ROUTE_INTS(E, Bm) * 4},
-      {"u", h->u, Bm * K * c.expert_ffn * 4},
+      {"gu", h->gu, Bm * K * 4 * c.expert_ffn * 4},
       {"dn", h->dn, Bm * K * H * 4},
   };
   for (const Item& it : items)

@@ -23,18 +23,14 @@
 // order while forming the residual), ROUTE_FINALIZE into ROUTER_TOPK.
 enum mk_opcode : int32_t {
   MK_OP_NOP = 0,
-  MK_OP_NORM = 1,         // residual add (+ MoE combine) + RMSNorm; layer 0: embedding gather
   MK_OP_QKV = 2,          // QKV panels + RoPE + paged KV append
-  MK_OP_ATTN = 3,         // split-KV partial attention over a page range
-  MK_OP_ATTN_COMBINE = 4, // log-sum-exp merge of the splits of one (sequence, kv group)
-  MK_OP_OPROJ = 5,        // O projection, split-K by kv group
-  MK_OP_ROUTER = 6,       // router logits
-  MK_OP_TOPK = 7,         // top-k + softmax weights + route finalize (expert work queue)
-  MK_OP_MOE_UP = 8,       // claimer over (expert, gate/up panel pair) items
-  MK_OP_MOE_DOWN = 9,     // claimer over (expert, down panel group) items
-  MK_OP_LMHEAD = 10,      // LM head panels + per-task argmax candidate
-  MK_OP_ARGMAX = 11,      // greedy token from the LM head candidates
-  MK_OP_COUNT = 12
+  MK_OP_ATTN = 3,         // split-KV partial attention (+ combine when last)
+  MK_OP_OPROJ = 5,        // O projection, split-K by kv group, one column block (+ residual when last)
+  MK_OP_ROUTER = 6,       // router logits over a K range (+ top-k / finalize when last)
+  MK_OP_MOE_UP = 8,       // claimer over (expert, gate/up panel pair, K half) items
+  MK_OP_MOE_DOWN = 9,     // claimer over (expert, column block) items (+ residual when last)
+  MK_OP_LMHEAD = 10,      // LM head panels + argmax candidate (+ greedy token when last)
+  MK_OP_COUNT = 11
 };
 
 struct mk_task {
@@ -65,9 +61,10 @@ struct mk_params {
   float eps;
   float attn_scale;
   int32_t B, mpps, n_pages, max_seq;
-  int32_t up_items_per_expert;   // F / 16 (gate/up panel pairs)
-  int32_t down_panels_per_item;  // panels per MoE down item
-  int32_t down_items_per_expert; // H / 16 / down_panels_per_item
+  int32_t up_items_per_expert;   // 2 * F / 16 (gate/up panel pairs x K halves)
+  int32_t down_items_per_expert; // NB (column blocks)
+  int32_t CB, NB;                // residual column block width (multiple of 16, <= 64) and count H / CB
+  int32_t n_router_tasks, router_ks; // router tasks, and the K splits among them
   int32_t max_splits;            // attention partial slots per (sequence, group)
   int32_t n_lm_tasks;
   int32_t e_pad;                 // router columns, padded to a multiple of 16
@@ -96,11 +93,12 @@ struct mk_params {
   float* part;   // [B][KVH][max_splits][G*D + 2G] attention partials (o, m, l)
   float* o;      // [B][QH*D] attention output
   float* ao;     // [KVH][B][H] O projection partials per kv group
-  float* r;      // [B][E] router logits
+  float* ssq;    // [B][NB] per column block sum of squares of the residual stream
+  float* rp;     // [router_ks][B][E] router logit partials
   int32_t* tk_idx; float* tk_w;  // [B][K]
   int32_t* tk_trace;             // optional [L][B][K] record of every layer's routing
   int32_t* route;
-  float* u;      // [B*K][F] expert hidden (after SiLU-and-multiply)
+  float* gu;     // [B*K][2 K halves][gate, up][F] expert up/gate partial sums
   float* dn;     // [B*K][H] expert outputs
   float* lm_val; int32_t* lm_arg; // [B][n_lm_tasks] LM head argmax candidates
   // synchronisation
@@ -111,5 +109,7 @@ struct mk_params {
   const mk_task* tasks;
   const int32_t* task_off;   // per workgroup [off[wg], off[wg+1])
   int32_t waits_enabled;     // 0 in kernel-per-op mode (stream order is the dependency)
+  uint32_t* trace;           // optional per-task record: {op | layer << 8, t_start, t_waited, t_end}
+  int32_t trace_base;        // index of this launch's first task in the trace
   int64_t timeout_ticks;     // wait time limit in s_memrealtime ticks (100 MHz)
 };
