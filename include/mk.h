@@ -147,10 +147,10 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
  * steps must not be in flight on another stream. */
 mk_status mk_set_mode(mk_handle* h, int mode);
 
-/* Record, for every task of later steps, four uint32 into `trace` (device,
- * n_records * 4 words): {opcode | layer << 8 | workgroup << 16, start,
- * dependencies satisfied, end}, times on the 100 MHz device clock (low 32
- * bits). Megakernel records are indexed like the exported schedule (CU-major),
+/* Record, for every task of later steps, eight uint32 into `trace` (device,
+ * n_records * 8 words): {opcode | layer << 8 | workgroup << 16, start,
+ * dependencies satisfied, inputs loaded, computed, end, 0, 0}, times on the
+ * 100 MHz device clock (low 32 bits; 0 where an op records no mark). Megakernel records are indexed like the exported schedule (CU-major),
  * kernel-per-op records in the flattened task order. NULL stops recording;
  * a step whose schedule has more tasks than n_records fails with
  * MK_ERR_INVALID_ARG. */
@@ -189,16 +189,16 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
  * the longest per-CU list, and the number of dependency counters. */
 typedef struct {
   int32_t n_tasks;
-  int32_t max_tasks_per_cu;
+  int32_t max_tasks_per_cu;   /* longest task list of one resident workgroup */
   int32_t n_counters;
-  int32_t n_cus;
+  int32_t n_cus;              /* resident workgroups (task lists): 2 per compute unit */
   int64_t weight_bytes_per_step; /* weights streamed at batch 1 routing (k experts) */
 } mk_schedule_info;
 mk_status mk_schedule_info_get(mk_handle* h, int batch, int max_seq_len_hint, mk_schedule_info* out);
 
-/* Copy the schedule's descriptors (n_tasks * 32 int32, CU-major, each CU's
- * list in execution order) and per-CU offsets (n_cus + 1 int32) to host
- * buffers sized from mk_schedule_info_get. */
+/* Copy the schedule's descriptors (n_tasks * 32 int32, list-major, each
+ * resident workgroup's list in execution order) and per-list offsets
+ * (n_cus + 1 int32) to host buffers sized from mk_schedule_info_get. */
 mk_status mk_schedule_export(mk_handle* h, int batch, int max_seq_len_hint, int32_t* tasks,
                              int32_t* cu_offsets);
 

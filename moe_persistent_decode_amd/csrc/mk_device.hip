@@ -1,7 +1,7 @@
 // mk_device.hip - the persistent decode interpreter and its op bodies (gfx950).
 //
-// One workgroup of 512 threads (8 wave64s) stays resident per compute unit and
-// walks its host-built task list (Cohere North Mini Code megakernel post,
+// One workgroup of 512 threads (8 wave64s) stays resident per compute unit
+// and walks its host-built task list (Cohere North Mini Code megakernel post,
 // section "What is a Megakernel?"). Each task:
 //   1. issues the loads of its weight tiles (weights do not depend on this
 //      step's activations, so they stream before the dependency clears:
@@ -130,13 +130,13 @@ struct SmemComb {
   float L[16];
 };
 
-// 96 KB of LDS: more than half of gfx950's 160 KB, so exactly one workgroup
-// fits per compute unit.
+// LDS per workgroup: with one workgroup per compute unit, more than half of
+// gfx950's 160 KB (so exactly one fits); with two, more than a third.
 union SmemU {
   float red[MK_WAVES][64];
   SmemAttn at;
   SmemComb cb;
-  float pad[24 * 1024];
+  float pad[MK_WGS_PER_CU == 1 ? 20480 : 11264];
 };
 
 struct Smem {
@@ -148,6 +148,7 @@ struct Smem {
   int claim;
   int old;                // value an arrival counter held before this workgroup's increment
   uint32_t t_waited;
+  uint32_t t_mark[2];     // op-defined intermediate timestamps (inputs ready, computed)
   int xc_layer;           // layer whose normalised input xc holds (-1: none)
   float ssq[128];
   float xc[2048];         // normalised input of one layer for batch 1 (per compute unit)
@@ -290,6 +291,10 @@ __device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0,
   __syncthreads();
 }
 
+__device__ __forceinline__ void mark(Smem& sm, int k) {
+  if (threadIdx.x == 0) sm.t_mark[k] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+}
+
 // ---------------------------------------------------------- arrivals
 // Count one arrival on counter c once every wave's device-coherent stores
 // have completed.
@@ -323,7 +328,8 @@ __device__ bool load_xhat(const mk_params& P, int l, Smem& sm) {
   if (sm.xc_layer == l) return true;
   const int H = P.H;
   const uint16_t* gam = P.gamma + (size_t)l * H;
-  float v[4];  // H <= 2048 = 4 x 512 threads
+  constexpr int NV = 2048 / MK_WG_THREADS;  // H <= 2048
+  float v[NV];
   float ss = 0.f;
   if (l == 0) {
     int tok = P.tokens[0];
@@ -332,7 +338,7 @@ __device__ bool load_xhat(const mk_params& P, int l, Smem& sm) {
       tok = 0;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int i = threadIdx.x + k * MK_WG_THREADS;
       v[k] = i < H ? bf2f(P.emb[(size_t)tok * H + i]) : 0.f;
       ss = fmaf(v[k], v[k], ss);
@@ -342,7 +348,7 @@ __device__ bool load_xhat(const mk_params& P, int l, Smem& sm) {
   } else {
     const Pub h(P.h), q(P.ssq);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int i = threadIdx.x + k * MK_WG_THREADS;
       v[k] = i < H ? h.ldf(i) : 0.f;
     }
@@ -358,7 +364,7 @@ __device__ bool load_xhat(const mk_params& P, int l, Smem& sm) {
   }
   const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < NV; ++k) {
     const int i = threadIdx.x + k * MK_WG_THREADS;
     if (i < H) sm.xc[i] = v[k] * inv * bf2f(gam[i]);
   }
@@ -412,16 +418,18 @@ __device__ void gemv_lds(const WTile<NP, NCH>& w, const float* xl, int np, int c
 // in its epilogue; tiny-vllm walkthrough: the new token's K/V are written to
 // page block_table[pos / 16], slot pos % 16, before attention reads them).
 template <int NCH>
-__device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, p0 = t.a[0], np = t.a[1];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
-  WTile<2, NCH> w;
+  WTile<1, NCH> w;  // one panel per task
   wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
   if (!wait_task(P, t, sm)) return;
   load_xhat(P, l, sm);
+  mark(sm, 0);
   const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
   gemv_lds(w, sm.xc, np, 0, kc, sm);
+  mark(sm, 1);
   if (wave_id() == 0) {
     const int tid = threadIdx.x;
     const float y = tid < np * 16 ? sm.out[tid] : 0.f;
@@ -476,8 +484,16 @@ __device__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
 template <int D>
 __device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm);
 
+// One wave's operands of one KV page of one kv group: K rows (keys) for the
+// score MFMA, V^T tiles for the output MFMA.
 template <int D>
-__device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
+struct KVPage {
+  u32x4_t k[D / 32];
+  u32x2_t v[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
   const int l = t.layer, b = t.a[0], g = t.a[1], s = t.a[2], ns = t.a[3], pps = t.a[4];
@@ -495,45 +511,46 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   const size_t plane = (size_t)PS * D;
   const float scale = P.attn_scale;
 
-  u32x4_t kr[NC];
-  u32x2_t vr[NT];
   bool bad = false;
   // The page holding the current position gets this step's K/V from the QKV
   // tasks of other compute units: read it device-coherently, after the wait.
   const Pub KV(kvl);
-  auto load_page = [&](int lp, u32x4_t* kk, u32x2_t* vv) {
+  auto load_page = [&](int lp) {
+    KVPage<D> pg;
     const int phys = P.bt[b * P.mpps + lp];
     if (phys < 0 || phys >= P.n_pages) {
       bad = true;
-      return;
+      return pg;
     }
     const int ko = ((phys * 2 + 0) * P.KVH + g) * (int)plane, vo = ((phys * 2 + 1) * P.KVH + g) * (int)plane;
     if (lp == lp_last) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kk[c] = KV.ld16x8(ko + (ln & 15) * D + 32 * c + 8 * (ln >> 4));
+      for (int c = 0; c < NC; ++c) pg.k[c] = KV.ld16x8(ko + (ln & 15) * D + 32 * c + 8 * (ln >> 4));
 #pragma unroll
-      for (int d = 0; d < NT; ++d) vv[d] = KV.ld16x4(vo + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4));
+      for (int d = 0; d < NT; ++d) pg.v[d] = KV.ld16x4(vo + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4));
     } else {
       const uint16_t* kp = kvl + ko;
       const uint16_t* vp = kvl + vo;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kk[c] = __builtin_nontemporal_load((const u32x4_t*)(kp + (ln & 15) * D + 32 * c + 8 * (ln >> 4)));
+        pg.k[c] = __builtin_nontemporal_load((const u32x4_t*)(kp + (ln & 15) * D + 32 * c + 8 * (ln >> 4)));
 #pragma unroll
       for (int d = 0; d < NT; ++d)
-        vv[d] = __builtin_nontemporal_load((const u32x2_t*)(vp + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4)));
+        pg.v[d] = __builtin_nontemporal_load((const u32x2_t*)(vp + (16 * d + (ln & 15)) * PS + 4 * (ln >> 4)));
     }
+    return pg;
   };
 
   int lp = my0 + wv;
   const bool early = lp < my1 && lp != lp_last;
-  if (early) load_page(lp, kr, vr);
+  KVPage<D> cur;
+  if (early) cur = load_page(lp);
   if (!wait_task(P, t, sm)) return;
   if (!seq_ok) {
     if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
     return;
   }
-  if (lp < my1 && !early) load_page(lp, kr, vr);
+  if (lp < my1 && !early) cur = load_page(lp);
 
   // Q^T operand: lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
   bf16x8_t qb[NC];
@@ -558,14 +575,13 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
   float m = kNegInf, lsum = 0.f;
 
   while (lp < my1 && !bad) {
-    u32x4_t kn[NC];
-    u32x2_t vn[NT];
+    KVPage<D> nxt;
     const int nlp = lp + MK_WAVES;
-    if (nlp < my1) load_page(nlp, kn, vn);
+    if (nlp < my1) nxt = load_page(nlp);
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), qb[c], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[c]), qb[c], sacc, 0, 0, 0);
     float sv[4];
     float mloc = kNegInf;
 #pragma unroll
@@ -595,13 +611,10 @@ __device__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
 #pragma unroll
       for (int d = 0; d < NT; ++d) {
         oacc[d] *= alpha;
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vr[d]), pB, oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, cur.v[d]), pB, oacc[d], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = kn[c];
-#pragma unroll
-    for (int d = 0; d < NT; ++d) vr[d] = vn[d];
+    cur = nxt;
     lp = nlp;
   }
   if (bad) raise_error(P, MK_DEVERR_FAULT, 5000 + b, (uint32_t)lp);
@@ -752,7 +765,7 @@ __device__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base,
 // of the K dimension as soon as that group's attention lands (megakernel
 // post, section "Drop false dependencies"); one task per (group, column block).
 template <int NCH>
-__device__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, g = t.a[0], cb = t.a[1];
   const int DP = P.CB / 16, p0 = cb * DP;
   const int kc = P.QH * P.D / 32;
@@ -761,7 +774,9 @@ __device__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
   WTile<4, NCH> w;
   wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, DP, c0, c1);
   if (!wait_task(P, t, sm)) return;
+  mark(sm, 0);
   gemv_b1(w, P.o + (size_t)g * P.G * P.D, DP, c0, c1, sm);
+  mark(sm, 1);
   if (threadIdx.x < DP * 16) Pub(P.ao + (size_t)g * P.H).stf(p0 * 16 + threadIdx.x, sm.out[threadIdx.x]);
   block_arrive(P, t, t.a[2], cb, sm);
 }
@@ -774,7 +789,7 @@ __device__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
 __device__ void topk_finalize(const mk_params& P, int l, Smem& sm);
 
 template <int NCH>
-__device__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, p0 = t.a[0], np = t.a[1], c0 = t.a[2], c1 = t.a[3], ks = t.a[4];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
@@ -782,7 +797,9 @@ __device__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
   wtile_load(w, P.wr + l * P.s_wr + (size_t)p0 * pstride, pstride, np, c0, c1);
   if (!wait_task(P, t, sm)) return;
   load_xhat(P, l, sm);
+  mark(sm, 0);
   gemv_lds(w, sm.xc, np, c0, c1, sm);
+  mark(sm, 1);
   const int n = p0 * 16 + threadIdx.x;
   if (threadIdx.x < np * 16 && n < P.E) Pub(P.rp + (size_t)ks * P.E).stf(n, sm.out[threadIdx.x]);
   const int old = arrive(P, t.a[5], sm);
@@ -805,48 +822,48 @@ __device__ void topk_finalize(const mk_params& P, int l, Smem& sm) {
     if (ln >= E) v0 = kNegInf;
     if (ln + 64 >= E) v1 = kNegInf;
     bool tk0 = ln >= E, tk1 = ln + 64 >= E;
-    float sel[MK_MAX_TOPK];
-    int idx[MK_MAX_TOPK];
-    for (int j = 0; j < K; ++j) {
-      float bv = kNegInf;
-      int bi = 0x7fffffff;
-      if (!tk0) { bv = v0; bi = ln; }
-      if (!tk1 && (v1 > bv || bi == 0x7fffffff)) { bv = v1; bi = ln + 64; }
+    // k rounds of a wave argmax (ties to the lower index); lane j keeps round j
+    float my_sel = kNegInf, top = kNegInf;
+    int my_idx = 0;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    for (int j = 0; j < MK_MAX_TOPK; ++j) {
+      if (j < K) {
+        float bv = kNegInf;
+        int bi = 0x7fffffff;
+        if (!tk0) { bv = v0; bi = ln; }
+        if (!tk1 && (v1 > bv || bi == 0x7fffffff)) { bv = v1; bi = ln + 64; }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
+          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        }
+        if (j == 0) top = bv;
+        if (ln == j) { my_sel = bv; my_idx = bi; }
+        if (bi == ln) tk0 = true;
+        if (bi == ln + 64) tk1 = true;
       }
-      sel[j] = bv;
-      idx[j] = bi;
-      if (bi == ln) tk0 = true;
-      if (bi == ln + 64) tk1 = true;
     }
-    const float mx = sel[0];
-    float e[MK_MAX_TOPK], sum = 0.f;
-    for (int j = 0; j < K; ++j) {
-      e[j] = __expf(sel[j] - mx);
-      sum += e[j];
-    }
+    // softmax over the kept logits (max-subtracted; the first kept is the max)
+    const float ej = ln < K ? __expf(my_sel - top) : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < MK_MAX_TOPK; ++j)
+      if (j < K) sum += __shfl(ej, j);
     // batch 1: the k distinct experts are the active ones; queue them in
-    // ascending expert order, slot j of the token routed to each
+    // ascending expert order, with the token's slot j routed to each
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < MK_MAX_TOPK; ++j)
+      if (j < K) rank += __shfl(my_idx, j) < my_idx;
     if (ln < K) {
       const int j = ln;
-      int my = 0, rank = 0;
-      for (int k = 0; k < K; ++k) {
-        if (k == j) my = idx[k];
-      }
-      for (int k = 0; k < K; ++k) rank += idx[k] < my;
-      TI.sti(j, my);
-      float wj = 0.f;
-      for (int k = 0; k < K; ++k)
-        if (k == j) wj = e[k] / sum;
-      TW.stf(j, wj);
-      RT.sti(4 + rank, my);
+      TI.sti(j, my_idx);
+      TW.stf(j, ej / sum);
+      RT.sti(4 + rank, my_idx);
       RT.sti(4 + E + rank, 1);
       RT.sti(4 + 2 * E + rank * P.B, j);
-      if (P.tk_trace) P.tk_trace[(size_t)l * K + j] = my;
+      if (P.tk_trace) P.tk_trace[(size_t)l * K + j] = my_idx;
     }
     if (ln == 0) {
       RT.sti(0, K);
@@ -872,7 +889,7 @@ __device__ __forceinline__ int claim(const mk_params& P, int32_t c, Smem& sm) {
 // K halves' gate and up sums are added, and the SiLU-and-multiply applied,
 // by the down projection that consumes them.
 template <int NCH>
-__device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
   const int E = P.E, F = P.F;
@@ -881,6 +898,7 @@ __device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
   const Pub R(P.route), GU(P.gu);
   const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(1));
   load_xhat(P, l, sm);
+  mark(sm, 0);
   for (;;) {
     if (ld_relaxed(&P.err[0]) != 0) return;
     const int id = claim(P, claim_ctr, sm);
@@ -899,6 +917,7 @@ __device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
       GU.stf(((slot * 2 + kh) * 2 + which) * F + col, sm.out[threadIdx.x]);
     }
     arrive_nr(P, done_base + a);
+    mark(sm, 1);
   }
 }
 
@@ -907,7 +926,7 @@ __device__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
 // post, section "What we have done differently": MoE down streams weights
 // while up/gate still computes the hidden state it consumes).
 template <int NCH>
-__device__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], blk_base = t.a[2];
   const int E = P.E, F = P.F, H = P.H;
@@ -948,7 +967,7 @@ __device__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
 __device__ void final_argmax(const mk_params& P, Smem& sm);
 
 template <int NCH>
-__device__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
   const int p0 = t.a[0], np = t.a[1], ord = t.a[2];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
@@ -1016,15 +1035,17 @@ __device__ void final_argmax(const mk_params& P, Smem& sm) {
 // --------------------------------------------------------------- dispatch
 
 template <int D>
-__device__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
   switch (t.op) {
-    case MK_OP_QKV: op_qkv<8>(P, t, sm); break;
+    // chunks per wave: K / 32 / MK_WAVES for the largest K of each op
+    // (hidden 2048, group width 1024, K half 1024, expert width 768)
+    case MK_OP_QKV: op_qkv<64 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
-    case MK_OP_OPROJ: op_oproj<4>(P, t, sm); break;
-    case MK_OP_ROUTER: op_router<8>(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe_up<4>(P, t, sm); break;
-    case MK_OP_MOE_DOWN: op_moe_down<3>(P, t, sm); break;
-    case MK_OP_LMHEAD: op_lmhead<8>(P, t, sm); break;
+    case MK_OP_OPROJ: op_oproj<32 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_ROUTER: op_router<32 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe_up<32 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_MOE_DOWN: op_moe_down<24 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_LMHEAD: op_lmhead<64 / MK_WAVES>(P, t, sm); break;
     default: wait_task(P, t, sm); break;
   }
 }
@@ -1033,9 +1054,13 @@ __device__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
 
 // The interpreter: workgroup i runs tasks [task_off[i], task_off[i+1]).
 template <int D>
-__global__ __launch_bounds__(MK_WG_THREADS) void mk_interp(mk_params P) {
+__global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_params Pk) {
   __shared__ Smem sm;
-  if (threadIdx.x == 0) sm.xc_layer = -1;
+  const mk_params& P = Pk;
+  if (threadIdx.x == 0) {
+    sm.xc_layer = -1;
+    sm.t_mark[0] = sm.t_mark[1] = 0;
+  }
   if (P.ctr_clear) {
     for (int i = blockIdx.x * MK_WG_THREADS + threadIdx.x; i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
       P.ctr_clear[i] = 0u;
@@ -1045,15 +1070,20 @@ __global__ __launch_bounds__(MK_WG_THREADS) void mk_interp(mk_params P) {
   for (int i = beg; i < end; ++i) {
     const mk_task& t = P.tasks[i];
     const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = 0;
     run_task<D>(P, t, sm);
     __syncthreads();
     if (P.trace && threadIdx.x == 0) {
-      // per-task timestamps (100 MHz device clock): start, waits satisfied, end
-      uint32_t* rec = P.trace + (size_t)(P.trace_base + i) * 4;
+      // per-task timestamps (100 MHz device clock): start, waits satisfied,
+      // inputs ready, computed, end
+      uint32_t* rec = P.trace + (size_t)(P.trace_base + i) * 8;
       rec[0] = (uint32_t)t.op | ((uint32_t)t.layer << 8) | ((uint32_t)blockIdx.x << 16);
       rec[1] = t0;
       rec[2] = sm.t_waited;
-      rec[3] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+      rec[3] = sm.t_mark[0];
+      rec[4] = sm.t_mark[1];
+      rec[5] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+      rec[6] = rec[7] = 0;
     }
   }
 }

@@ -94,7 +94,8 @@ struct mk_handle {
   mk_config cfg{};
   int device = 0;
   bool host_only = false;
-  int n_cu = 0;
+  int n_cu = 0;       // compute units
+  int n_workers = 0;  // resident workgroups: MK_WGS_PER_CU per compute unit
   std::string err;
   // derived
   int G = 0, qkv_dim = 0, q_dim = 0, kv_dim = 0, e_pad = 0;
@@ -228,7 +229,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   S->bucket = std::min(bucket_of(hint), c.max_seq_len);
   S->pps = h->pps;
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
-  const int n_cu = h->n_cu, NB = h->NB;
+  const int n_w = h->n_workers, NB = h->NB;
   const int kc = c.hidden / 32;
 
   // counter layout: resid_done[l] for l = 1..L (index l - 1), lm, then per layer
@@ -267,8 +268,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     S->waves.back().second = (int)S->flat.size();
   };
 
-  S->n_up_claimers = n_cu;
-  S->n_down_claimers = n_cu;
+  S->n_up_claimers = n_w;
+  S->n_down_claimers = n_w;
   const int qkv_np = 1;
   S->n_qkv.assign(KVH, 0);
 
@@ -387,11 +388,11 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     ++S->n_lm;
   }
 
-  // round-robin placement of the flattened list
-  std::vector<std::vector<mk_task>> per(n_cu);
-  for (size_t k = 0; k < S->flat.size(); ++k) per[k % n_cu].push_back(S->flat[k]);
-  S->cu_off.assign(n_cu + 1, 0);
-  for (int i = 0; i < n_cu; ++i) {
+  // round-robin placement of the flattened list over the resident workgroups
+  std::vector<std::vector<mk_task>> per(n_w);
+  for (size_t k = 0; k < S->flat.size(); ++k) per[k % n_w].push_back(S->flat[k]);
+  S->cu_off.assign(n_w + 1, 0);
+  for (int i = 0; i < n_w; ++i) {
     S->cu_off[i + 1] = S->cu_off[i] + (int)per[i].size();
     S->cu_tasks.insert(S->cu_tasks.end(), per[i].begin(), per[i].end());
   }
@@ -409,7 +410,7 @@ struct SimCU {
 mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uint64_t seed, int corrupt,
                    std::string& rep) {
   const mk_config& c = h->cfg;
-  const int n_cu = h->n_cu, L = c.n_layers, E = c.n_experts, KVH = c.n_kv_heads, NB = h->NB;
+  const int n_cu = h->n_workers, L = c.n_layers, E = c.n_experts, KVH = c.n_kv_heads, NB = h->NB;
   const int F = c.expert_ffn;
   const int up_per_e = 2 * F / 16, down_per_e = NB;
   std::vector<mk_task> tasks = S.cu_tasks;
@@ -615,6 +616,7 @@ mk_status mk_create_host_only(const mk_config* cfg, int n_cus, mk_handle** out) 
   h->cfg = *cfg;
   h->host_only = true;
   h->n_cu = n_cus;
+  h->n_workers = n_cus * MK_WGS_PER_CU;
   derive(h);
   *out = h;
   return MK_OK;
@@ -640,9 +642,11 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n_cu < 1)
     return fail(nullptr, MK_ERR_HIP, "cannot query compute units");
   int occ = 0;
-  if (mk_interp_occupancy(c.head_dim, &occ) != hipSuccess || occ < 1)
-    return fail(nullptr, MK_ERR_HIP, "interpreter kernel cannot be resident");
+  if (mk_interp_occupancy(c.head_dim, &occ) != hipSuccess || occ < MK_WGS_PER_CU)
+    return fail(nullptr, MK_ERR_HIP, "interpreter kernel: %d resident workgroups per CU, need %d", occ,
+                MK_WGS_PER_CU);
   h->n_cu = std::min(n_cu, MK_MAX_CUS);
+  h->n_workers = h->n_cu * MK_WGS_PER_CU;
   if (const char* e = std::getenv("MK_TIMEOUT_MS")) h->timeout_ticks = (int64_t)std::atoll(e) * 100000;
 
   const int L = c.n_layers, H = c.hidden, E = c.n_experts, F = c.expert_ffn, V = c.vocab;
@@ -936,7 +940,7 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
     P.tasks = S->d_cu_tasks;
     P.task_off = S->d_cu_off;
     P.waits_enabled = 1;
-    HIPCHECK(h, mk_launch_interp(P, c.head_dim, h->n_cu, true, s));
+    HIPCHECK(h, mk_launch_interp(P, c.head_dim, h->n_workers, true, s));
   } else {
     P.waits_enabled = 0;
     P.task_off = h->wg_off_identity;
@@ -953,7 +957,7 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
   return MK_OK;
 }
 
-mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records) {
+mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records) {  // records of 8 words
   if (!h) return MK_ERR_INVALID_ARG;
   h->task_trace = trace;
   h->task_trace_cap = trace ? n_records : 0;
@@ -1030,10 +1034,10 @@ mk_status mk_schedule_info_get(mk_handle* h, int batch, int hint, mk_schedule_in
   if (st != MK_OK) return st;
   out->n_tasks = (int32_t)S->cu_tasks.size();
   int mx = 0;
-  for (int i = 0; i < h->n_cu; ++i) mx = std::max(mx, S->cu_off[i + 1] - S->cu_off[i]);
+  for (int i = 0; i < h->n_workers; ++i) mx = std::max(mx, S->cu_off[i + 1] - S->cu_off[i]);
   out->max_tasks_per_cu = mx;
   out->n_counters = S->n_ctr;
-  out->n_cus = h->n_cu;
+  out->n_cus = h->n_workers;
   const mk_config& c = h->cfg;
   const int64_t per_layer = (int64_t)c.hidden * h->qkv_dim + (int64_t)h->q_dim * c.hidden +
                             (int64_t)c.hidden * h->e_pad + c.hidden +

@@ -10,8 +10,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// One workgroup of 8 wave64s stays resident per compute unit and walks its
+// task list (MK_WGS_PER_CU = 2 with 256 threads gives two independent lists
+// per compute unit instead; measured slower: the dependent chain of a layer
+// is latency-bound and a half-size workgroup takes twice as long per task).
 #define MK_WG_THREADS 512
 #define MK_WAVES (MK_WG_THREADS / 64)
+#define MK_WGS_PER_CU 1
 #define MK_MAX_CUS 1024
 #define MK_MAX_TOPK 8
 #define MK_TASK_INTS 32
