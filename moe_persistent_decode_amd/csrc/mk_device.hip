@@ -40,7 +40,9 @@ namespace {
 // ------------------------------------------------------------------ helpers
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index as a scalar (wave-uniform) value, so per-wave chunk choices
+// compile to scalar branches instead of exec-mask juggling.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -126,34 +128,50 @@ struct SmemAttn {
 #define MK_MAX_SPLITS 256
 struct SmemComb {
   float f[MK_MAX_SPLITS][16];
+  float l[MK_MAX_SPLITS][16];
   float M[16];
   float L[16];
 };
 
 // LDS per workgroup: with one workgroup per compute unit, more than half of
 // gfx950's 160 KB (so exactly one fits); with two, more than a third.
+struct SmemTopk {
+  alignas(16) float logit[128];
+  float sel_val[MK_MAX_TOPK];
+  int sel_idx[MK_MAX_TOPK];
+};
+
 union SmemU {
   float red[MK_WAVES][64];
+  SmemTopk tk;
   SmemAttn at;
   SmemComb cb;
   float pad[MK_WGS_PER_CU == 1 ? 20480 : 11264];
 };
 
+// Arrays read as float4 must be 16-byte aligned: a 16-byte LDS read from a
+// 4-byte aligned address runs about five times slower on gfx950 (a 64-chunk
+// GEMV over an LDS vector measured 3.7 us unaligned against 0.7 us aligned).
 struct Smem {
   SmemU u;
-  float out[64];
-  float vred[MK_WAVES];
+  alignas(16) float out[64];
+  alignas(16) float ssq[128];
+  alignas(16) float xc[2048];  // normalised input of one layer for batch 1 (per compute unit)
+  alignas(16) float us[768];   // expert hidden of one routed slot (down projection input)
+  alignas(16) float vred[MK_WAVES];
   int ired[MK_WAVES];
   int flag;
   int claim;
   int old;                // value an arrival counter held before this workgroup's increment
   uint32_t t_waited;
-  uint32_t t_mark[2];     // op-defined intermediate timestamps (inputs ready, computed)
+  uint32_t t_mark[4];     // op-defined intermediate timestamps (e.g. inputs ready, computed)
   int xc_layer;           // layer whose normalised input xc holds (-1: none)
-  float ssq[128];
-  float xc[2048];         // normalised input of one layer for batch 1 (per compute unit)
-  float us[768];          // expert hidden of one routed slot (down projection input)
+  int rt_hdr[4];          // route header: n_active, up items, down items
+  int rt_e[128];          // active experts, ascending
+  int rt_slot[128];       // batch 1: the routed slot of each active expert
 };
+static_assert(offsetof(Smem, xc) % 16 == 0 && offsetof(Smem, us) % 16 == 0 &&
+              offsetof(Smem, out) % 16 == 0 && offsetof(Smem, ssq) % 16 == 0, "LDS vectors 16-byte aligned");
 
 __device__ void raise_error(const mk_params& P, uint32_t code, uint32_t detail, uint32_t value) {
   uint32_t expected = 0;
@@ -225,6 +243,8 @@ struct WTile {
   u32x4_t v[NP][NCH];
 };
 
+// Chunks outside [c0, c1) and panels at or beyond np are zero, so the GEMVs
+// below run without per-chunk branches.
 template <int NP, int NCH>
 __device__ __forceinline__ void wtile_load(WTile<NP, NCH>& w, const uint16_t* base, size_t pstride,
                                            int np, int c0, int c1) {
@@ -236,6 +256,8 @@ __device__ __forceinline__ void wtile_load(WTile<NP, NCH>& w, const uint16_t* ba
       const int c = c0 + wv + MK_WAVES * i;
       if (pp < np && c < c1)
         w.v[pp][i] = __builtin_nontemporal_load((const u32x4_t*)(base + pp * pstride + (size_t)c * 512) + ln);
+      else
+        w.v[pp][i] = u32x4_t{0u, 0u, 0u, 0u};
     }
 }
 
@@ -262,14 +284,12 @@ __device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0,
   for (int pp = 0; pp < NP; ++pp) acc[pp] = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = c0 + wv + MK_WAVES * i;
-    if (c < c1) {
-      const int xi = (c - c0) * 32 + 8 * (ln >> 4);
-      const float4 x0 = X.ldf4(xi), x1 = X.ldf4(xi + 4);
+    // out-of-range chunks read a valid row and multiply zero weights
+    const int c = max(min(c0 + wv + MK_WAVES * i, c1 - 1), c0);
+    const int xi = (c - c0) * 32 + 8 * (ln >> 4);
+    const float4 x0 = X.ldf4(xi), x1 = X.ldf4(xi + 4);
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp)
-        if (pp < np) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
-    }
+    for (int pp = 0; pp < NP; ++pp) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
   }
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
@@ -383,14 +403,12 @@ __device__ void gemv_lds(const WTile<NP, NCH>& w, const float* xl, int np, int c
   for (int pp = 0; pp < NP; ++pp) acc[pp] = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = c0 + wv + MK_WAVES * i;
-    if (c < c1) {
-      const float4* xp = (const float4*)(xl + c * 32 + 8 * (ln >> 4));
-      const float4 x0 = xp[0], x1 = xp[1];
+    // out-of-range chunks read a valid row and multiply zero weights
+    const int c = max(min(c0 + wv + MK_WAVES * i, c1 - 1), c0);
+    const float4* xp = (const float4*)(xl + c * 32 + 8 * (ln >> 4));
+    const float4 x0 = xp[0], x1 = xp[1];
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp)
-        if (pp < np) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
-    }
+    for (int pp = 0; pp < NP; ++pp) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
   }
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
@@ -422,7 +440,7 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   const int l = t.layer, p0 = t.a[0], np = t.a[1];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
-  WTile<1, NCH> w;  // one panel per task
+  WTile<2, NCH> w;  // up to two panels per task
   wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
   if (!wait_task(P, t, sm)) return;
   load_xhat(P, l, sm);
@@ -541,16 +559,20 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
     return pg;
   };
 
+  // each wave's first two pages stream before the wait (two-deep pipeline)
   int lp = my0 + wv;
-  const bool early = lp < my1 && lp != lp_last;
-  KVPage<D> cur;
-  if (early) cur = load_page(lp);
+  const int lpn = lp + MK_WAVES;
+  const bool early0 = lp < my1 && lp != lp_last, early1 = lpn < my1 && lpn != lp_last;
+  KVPage<D> cur, nxt;
+  if (early0) cur = load_page(lp);
+  if (early1) nxt = load_page(lpn);
   if (!wait_task(P, t, sm)) return;
   if (!seq_ok) {
     if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
     return;
   }
-  if (lp < my1 && !early) cur = load_page(lp);
+  if (lp < my1 && !early0) cur = load_page(lp);
+  if (lpn < my1 && !early1) nxt = load_page(lpn);
 
   // Q^T operand: lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
   bf16x8_t qb[NC];
@@ -575,9 +597,9 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
   float m = kNegInf, lsum = 0.f;
 
   while (lp < my1 && !bad) {
-    KVPage<D> nxt;
-    const int nlp = lp + MK_WAVES;
-    if (nlp < my1) nxt = load_page(nlp);
+    KVPage<D> nxt2;
+    const int nlp2 = lp + 2 * MK_WAVES;
+    if (nlp2 < my1) nxt2 = load_page(nlp2);
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -615,7 +637,8 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
       }
     }
     cur = nxt;
-    lp = nlp;
+    nxt = nxt2;
+    lp += MK_WAVES;
   }
   if (bad) raise_error(P, MK_DEVERR_FAULT, 5000 + b, (uint32_t)lp);
 
@@ -652,9 +675,12 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
       dst.stf(G * D + G + hh, L);
     }
   }
+  mark(sm, 0);
   const int old = arrive(P, t.a[5], sm);
+  mark(sm, 1);
   if (old == ns - 1) {
     attn_combine<D>(P, b, g, ns, sm);
+    mark(sm, 3);
     arrive_nr(P, t.sig_ctr[0]);
   }
 }
@@ -668,10 +694,11 @@ __device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm)
   const int stride = G * D + 2 * G;
   const Pub src(P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride);
   SmemComb& C = sm.u.cb;
-  // split maxima, then per-head M and L
+  // split maxima and sums, all loads in flight together
   for (int i = threadIdx.x; i < ns * G; i += MK_WG_THREADS) {
     const int s = i / G, hh = i % G;
     C.f[s][hh] = src.ldf(s * stride + G * D + hh);
+    C.l[s][hh] = src.ldf(s * stride + G * D + G + hh);
   }
   __syncthreads();
   if (threadIdx.x < G) {
@@ -690,24 +717,41 @@ __device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm)
   if (threadIdx.x < G) {
     const int hh = threadIdx.x;
     float L = 0.f;
-    for (int s = 0; s < ns; ++s) L = fmaf(C.f[s][hh], src.ldf(s * stride + G * D + G + hh), L);
+    for (int s = 0; s < ns; ++s) L = fmaf(C.f[s][hh], C.l[s][hh], L);
     C.L[hh] = L;
   }
   __syncthreads();
+  mark(sm, 2);
   const Pub dst(P.o + (size_t)b * P.QH * D + (size_t)g * G * D);
-  for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
-    const int hh = idx / D, dd = idx % D;
-    float O = 0.f;
-    int s = 0;
-    for (; s + 8 <= ns; s += 8) {
-      float v[8];
+  // each thread's outputs (G * D <= 1024: at most two) over up to 32 splits
+  // at a time, every load in flight together
+  constexpr int NO = 1024 / MK_WG_THREADS, SB = 32;
+  float O[NO];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = src.ldf((s + k) * stride + hh * D + dd);
+  for (int u = 0; u < NO; ++u) O[u] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+    float v[NO][SB];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) O = fmaf(C.f[s + k][hh], v[k], O);
+    for (int u = 0; u < NO; ++u) {
+      const int idx = threadIdx.x + u * MK_WG_THREADS;
+      const int hh = idx / D, dd = idx % D;
+#pragma unroll
+      for (int k = 0; k < SB; ++k)
+        v[u][k] = (idx < G * D && s0 + k < ns) ? src.ldf((s0 + k) * stride + hh * D + dd) : 0.f;
     }
-    for (; s < ns; ++s) O = fmaf(C.f[s][hh], src.ldf(s * stride + hh * D + dd), O);
-    dst.stf(hh * D + dd, O / C.L[hh]);
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int idx = threadIdx.x + u * MK_WG_THREADS;
+      const int hh = min(idx / D, G - 1);
+#pragma unroll
+      for (int k = 0; k < SB; ++k)
+        if (s0 + k < ns) O[u] = fmaf(C.f[s0 + k][hh], v[u][k], O[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NO; ++u) {
+    const int idx = threadIdx.x + u * MK_WG_THREADS;
+    if (idx < G * D) dst.stf(idx, O[u] / C.L[idx / D]);
   }
 }
 
@@ -724,10 +768,15 @@ __device__ void residual_block(const mk_params& P, int l, int cb, Smem& sm) {
   const int i = threadIdx.x;
   if (i < CB) {
     const int c = cb * CB + i;
-    float a = 0.f;
-    for (int g = 0; g < P.KVH; ++g) a += ao.ldf(g * H + c);
-    float y = 0.f;
-    for (int j = 0; j < K; ++j) y = fmaf(tkw.ldf(j), dn.ldf(j * H + c), y);
+    // every load in flight before the sums (fixed order: groups, then ranks)
+    float av[MK_MAX_KVH], wv[MK_MAX_TOPK], yv[MK_MAX_TOPK];
+#pragma unroll
+    for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = g < P.KVH ? ao.ldf(g * H + c) : 0.f;
+#pragma unroll
+    for (int j = 0; j < MK_MAX_TOPK; ++j) {
+      wv[j] = j < K ? tkw.ldf(j) : 0.f;
+      yv[j] = j < K ? dn.ldf(j * H + c) : 0.f;
+    }
     float h0;
     if (l == 0) {
       const int tok = P.tokens[0];
@@ -735,6 +784,14 @@ __device__ void residual_block(const mk_params& P, int l, int cb, Smem& sm) {
     } else {
       h0 = h.ldf(c);
     }
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < MK_MAX_KVH; ++g)
+      if (g < P.KVH) a += av[g];
+    float y = 0.f;
+#pragma unroll
+    for (int j = 0; j < MK_MAX_TOPK; ++j)
+      if (j < K) y = fmaf(wv[j], yv[j], y);
     const float v = (h0 + a) + y;
     h.stf(c, v);
     ss = v * v;
@@ -804,68 +861,68 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   if (threadIdx.x < np * 16 && n < P.E) Pub(P.rp + (size_t)ks * P.E).stf(n, sm.out[threadIdx.x]);
   const int old = arrive(P, t.a[5], sm);
   if (old == P.n_router_tasks - 1) {
+    mark(sm, 2);
     topk_finalize(P, l, sm);
+    mark(sm, 3);
     arrive_nr(P, t.sig_ctr[0]);
   }
 }
 
+// Top-k by ranking: expert i's rank is the number of experts ahead of it
+// (a larger logit, or an equal logit and a lower index); the experts ranked
+// below k are kept, in rank order. Every comparison is independent, so this
+// runs in a few hundred cycles instead of k dependent rounds of a wave argmax.
 __device__ void topk_finalize(const mk_params& P, int l, Smem& sm) {
   const int E = P.E, K = P.K;
-  const int ln = lane_id();
+  const int i = threadIdx.x;
   const Pub R(P.rp), TI(P.tk_idx), TW(P.tk_w), RT(P.route);
-  if (wave_id() == 0) {
-    float v0 = 0.f, v1 = 0.f;
-    for (int k = 0; k < P.router_ks; ++k) {
-      if (ln < E) v0 += R.ldf(k * E + ln);
-      if (ln + 64 < E) v1 += R.ldf(k * E + ln + 64);
-    }
-    if (ln >= E) v0 = kNegInf;
-    if (ln + 64 >= E) v1 = kNegInf;
-    bool tk0 = ln >= E, tk1 = ln + 64 >= E;
-    // k rounds of a wave argmax (ties to the lower index); lane j keeps round j
-    float my_sel = kNegInf, top = kNegInf;
-    int my_idx = 0;
+  float* lg = sm.u.tk.logit;
+  if (i < E) {
+    float p[MK_MAX_RKS];
 #pragma unroll
-    for (int j = 0; j < MK_MAX_TOPK; ++j) {
-      if (j < K) {
-        float bv = kNegInf;
-        int bi = 0x7fffffff;
-        if (!tk0) { bv = v0; bi = ln; }
-        if (!tk1 && (v1 > bv || bi == 0x7fffffff)) { bv = v1; bi = ln + 64; }
+    for (int k = 0; k < MK_MAX_RKS; ++k) p[k] = k < P.router_ks ? R.ldf(k * E + i) : 0.f;
+    float v = 0.f;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oi = __shfl_xor(bi, o);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        if (j == 0) top = bv;
-        if (ln == j) { my_sel = bv; my_idx = bi; }
-        if (bi == ln) tk0 = true;
-        if (bi == ln + 64) tk1 = true;
-      }
+    for (int k = 0; k < MK_MAX_RKS; ++k)
+      if (k < P.router_ks) v += p[k];
+    lg[i] = v;
+  }
+  __syncthreads();
+  if (i < E) {
+    const float v = lg[i];
+    int rank = 0;
+    for (int j = 0; j < E; j += 4) {
+      const float4 q = *(const float4*)(lg + j);
+      rank += (q.x > v) | ((q.x == v) & (j + 0 < i));
+      rank += (q.y > v) | ((q.y == v) & (j + 1 < i));
+      rank += (q.z > v) | ((q.z == v) & (j + 2 < i));
+      rank += (q.w > v) | ((q.w == v) & (j + 3 < i));
     }
-    // softmax over the kept logits (max-subtracted; the first kept is the max)
-    const float ej = ln < K ? __expf(my_sel - top) : 0.f;
+    if (rank < K) {
+      sm.u.tk.sel_idx[rank] = i;
+      sm.u.tk.sel_val[rank] = v;
+    }
+  }
+  __syncthreads();
+  if (i < K) {
+    // softmax over the kept logits (max-subtracted; rank 0 is the max),
+    // summed in rank order
+    const float top = sm.u.tk.sel_val[0];
     float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < MK_MAX_TOPK; ++j)
-      if (j < K) sum += __shfl(ej, j);
+    for (int j = 0; j < K; ++j) sum += __expf(sm.u.tk.sel_val[j] - top);
+    const int my_idx = sm.u.tk.sel_idx[i];
+    const float ej = __expf(sm.u.tk.sel_val[i] - top);
     // batch 1: the k distinct experts are the active ones; queue them in
     // ascending expert order, with the token's slot j routed to each
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < MK_MAX_TOPK; ++j)
-      if (j < K) rank += __shfl(my_idx, j) < my_idx;
-    if (ln < K) {
-      const int j = ln;
-      TI.sti(j, my_idx);
-      TW.stf(j, ej / sum);
-      RT.sti(4 + rank, my_idx);
-      RT.sti(4 + E + rank, 1);
-      RT.sti(4 + 2 * E + rank * P.B, j);
-      if (P.tk_trace) P.tk_trace[(size_t)l * K + j] = my_idx;
-    }
-    if (ln == 0) {
+    int pos = 0;
+    for (int j = 0; j < K; ++j) pos += sm.u.tk.sel_idx[j] < my_idx;
+    TI.sti(i, my_idx);
+    TW.stf(i, ej / sum);
+    RT.sti(4 + pos, my_idx);
+    RT.sti(4 + E + pos, 1);
+    RT.sti(4 + 2 * E + pos * P.B, i);
+    if (P.tk_trace) P.tk_trace[(size_t)l * K + i] = my_idx;
+    if (i == 0) {
       RT.sti(0, K);
       RT.sti(1, K * P.up_items_per_expert);
       RT.sti(2, K * P.down_items_per_expert);
@@ -888,36 +945,88 @@ __device__ __forceinline__ int claim(const mk_params& P, int32_t c, Smem& sm) {
 // claimers take the next entry atomically until the queue is empty). The two
 // K halves' gate and up sums are added, and the SiLU-and-multiply applied,
 // by the down projection that consumes them.
+// Route entries of the layer's active experts into LDS (one round trip).
+__device__ __forceinline__ void load_route(const mk_params& P, Smem& sm) {
+  const Pub R(P.route);
+  const int E = P.E;
+  const int i = threadIdx.x;
+  if (i < 4) sm.rt_hdr[i] = R.ldi(i);
+  if (i < E) {
+    sm.rt_e[i] = R.ldi(4 + i);
+    sm.rt_slot[i] = R.ldi(4 + 2 * E + i * P.B);
+  }
+  __syncthreads();
+}
+
+// Claim n consecutive items of a work queue: returns (block-uniform) the first.
+__device__ __forceinline__ int claim_n(const mk_params& P, int32_t c, int n, Smem& sm) {
+  if (threadIdx.x == 0)
+    sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int id = sm.claim;
+  __syncthreads();
+  return id;
+}
+
+#define MK_UP_BATCH 4  // at most this many up/gate items claimed together, their weights in flight together
+
 template <int NCH>
 __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
-  const int E = P.E, F = P.F;
+  const int F = P.F, upe = P.up_items_per_expert;
   const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
-  const Pub R(P.route), GU(P.gu);
-  const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(1));
+  const Pub GU(P.gu);
+  load_route(P, sm);
+  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
+  // batch size: the queue spread over the claimers expected to be free
+  const int nb = min(MK_UP_BATCH, max(1, (n_items + t.a[2] - 1) / t.a[2]));
+  int id0 = claim_n(P, claim_ctr, nb, sm);
   load_xhat(P, l, sm);
   mark(sm, 0);
-  for (;;) {
+  bool first = true;
+  while (id0 < n_items) {
     if (ld_relaxed(&P.err[0]) != 0) return;
-    const int id = claim(P, claim_ctr, sm);
-    if (id >= n_items) break;
-    const int a = id / P.up_items_per_expert, r = id % P.up_items_per_expert;
-    const int tt = r >> 1, kh = r & 1;
-    const int e = __builtin_amdgcn_readfirstlane(R.ldi(4 + a));
-    const int c0 = kh * kh_chunks, c1 = c0 + kh_chunks;
-    WTile<2, NCH> w;
-    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride, 2, c0, c1);
-    const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B));
-    gemv_lds(w, sm.xc, 2, c0, c1, sm);
-    // gu[slot][kh][gate|up][F]
-    if (threadIdx.x < 32) {
-      const int which = threadIdx.x >> 4, col = tt * 16 + (threadIdx.x & 15);
-      GU.stf(((slot * 2 + kh) * 2 + which) * F + col, sm.out[threadIdx.x]);
+    WTile<2, NCH> w[MK_UP_BATCH];
+#pragma unroll
+    for (int k = 0; k < MK_UP_BATCH; ++k) {
+      const int id = id0 + k;
+      const int a = id / upe, r = id % upe;
+      const int tt = r >> 1, kh = r & 1;
+      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[min(a, P.E - 1)]);
+      const int c0 = kh * kh_chunks;
+      // an item past the queue's end loads nothing (np = 0: a zero tile)
+      wtile_load(w[k], P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
+                 (k < nb && id < n_items) ? 2 : 0, c0, c0 + kh_chunks);
     }
-    arrive_nr(P, done_base + a);
     mark(sm, 1);
+    // the next claim travels while the weights stream
+    const int next = claim_n(P, claim_ctr, nb, sm);
+#pragma unroll
+    for (int k = 0; k < MK_UP_BATCH; ++k) {
+      const int id = id0 + k;
+      if (k >= nb || id >= n_items) break;
+      const int a = id / upe, r = id % upe;
+      const int tt = r >> 1, kh = r & 1;
+      const int c0 = kh * kh_chunks;
+      const int slot = __builtin_amdgcn_readfirstlane(sm.rt_slot[a]);
+      gemv_lds(w[k], sm.xc, 2, c0, c0 + kh_chunks, sm);
+      if (k == 0 && first) mark(sm, 2);
+      // gu[slot][kh][gate|up][F]
+      if (threadIdx.x < 32) {
+        const int which = threadIdx.x >> 4, col = tt * 16 + (threadIdx.x & 15);
+        GU.stf(((slot * 2 + kh) * 2 + which) * F + col, sm.out[threadIdx.x]);
+      }
+    }
+    // one drain for the batch, then each item's arrival on its expert's counter
+    sync_published();
+    if ((int)threadIdx.x < nb && id0 + (int)threadIdx.x < n_items)
+      __hip_atomic_fetch_add(&P.ctr[done_base + (id0 + (int)threadIdx.x) / upe], 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    if (first) mark(sm, 3);
+    first = false;
+    id0 = next;
   }
 }
 
@@ -933,21 +1042,25 @@ __device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t
   const int kc = F / 32;
   const size_t pstride = (size_t)kc * 512;
   const int DP = P.CB / 16;
-  const Pub R(P.route), DN(P.dn), GU(P.gu);
-  const int n_items = __builtin_amdgcn_readfirstlane(R.ldi(2));
-  for (;;) {
+  const Pub DN(P.dn), GU(P.gu);
+  int id = claim(P, claim_ctr, sm);
+  load_route(P, sm);
+  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
+  while (id < n_items) {
     if (ld_relaxed(&P.err[0]) != 0) return;
-    const int id = claim(P, claim_ctr, sm);
-    if (id >= n_items) break;
     const int a = id / P.down_items_per_expert, cb = id % P.down_items_per_expert;
-    const int e = __builtin_amdgcn_readfirstlane(R.ldi(4 + a));
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
     WTile<4, NCH> w;
     wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride, pstride, DP, 0, kc);
+    // the next claim travels while the weights stream
+    const int next = claim(P, claim_ctr, sm);
     if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
-    const int slot = __builtin_amdgcn_readfirstlane(R.ldi(4 + 2 * E + a * P.B));
+    const int slot = __builtin_amdgcn_readfirstlane(sm.rt_slot[a]);
     // u = silu(g0 + g1) * (u0 + u1) over F, staged in LDS
     float* us = sm.us;
-    for (int k = threadIdx.x; k < F; k += MK_WG_THREADS) {
+#pragma unroll
+    for (int k = threadIdx.x; k < MK_MAX_F; k += MK_WG_THREADS) {
+      if (k >= F) break;
       const float g0 = GU.ldf(((slot * 2 + 0) * 2 + 0) * F + k), g1 = GU.ldf(((slot * 2 + 1) * 2 + 0) * F + k);
       const float u0 = GU.ldf(((slot * 2 + 0) * 2 + 1) * F + k), u1 = GU.ldf(((slot * 2 + 1) * 2 + 1) * F + k);
       const float gt = g0 + g1;
@@ -957,6 +1070,7 @@ __device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t
     gemv_lds(w, us, DP, 0, kc, sm);
     if (threadIdx.x < DP * 16) DN.stf(slot * H + cb * DP * 16 + threadIdx.x, sm.out[threadIdx.x]);
     block_arrive(P, t, blk_base, cb, sm);
+    id = next;
   }
 }
 
@@ -1005,10 +1119,19 @@ __device__ void final_argmax(const mk_params& P, Smem& sm) {
   const Pub LV(P.lm_val), LA(P.lm_arg);
   float v = kNegInf;
   int ix = 0x7fffffff;
-  for (int i = threadIdx.x; i < n; i += MK_WG_THREADS) {
-    const float cv = LV.ldf(i);
-    const int ci = LA.ldi(i);
-    if (cv > v || (cv == v && ci < ix)) { v = cv; ix = ci; }
+  constexpr int U = 8;  // candidates per thread in flight together
+  for (int base = 0; base < n; base += U * MK_WG_THREADS) {
+    float cv[U];
+    int ci[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * MK_WG_THREADS + threadIdx.x;
+      cv[u] = i < n ? LV.ldf(i) : kNegInf;
+      ci[u] = i < n ? LA.ldi(i) : 0x7fffffff;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (cv[u] > v || (cv[u] == v && ci[u] < ix)) { v = cv[u]; ix = ci[u]; }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -1059,7 +1182,7 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
   const mk_params& P = Pk;
   if (threadIdx.x == 0) {
     sm.xc_layer = -1;
-    sm.t_mark[0] = sm.t_mark[1] = 0;
+    sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
   }
   if (P.ctr_clear) {
     for (int i = blockIdx.x * MK_WG_THREADS + threadIdx.x; i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
@@ -1070,7 +1193,7 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
   for (int i = beg; i < end; ++i) {
     const mk_task& t = P.tasks[i];
     const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
-    if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = 0;
+    if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
     run_task<D>(P, t, sm);
     __syncthreads();
     if (P.trace && threadIdx.x == 0) {
@@ -1083,7 +1206,8 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
       rec[3] = sm.t_mark[0];
       rec[4] = sm.t_mark[1];
       rec[5] = (uint32_t)__builtin_amdgcn_s_memrealtime();
-      rec[6] = rec[7] = 0;
+      rec[6] = sm.t_mark[2];
+      rec[7] = sm.t_mark[3];
     }
   }
 }

@@ -157,6 +157,7 @@ mk_status validate_config(const mk_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return fail(nullptr, MK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads)
     return fail(nullptr, MK_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (c->n_kv_heads > MK_MAX_KVH) return fail(nullptr, MK_ERR_UNSUPPORTED, "n_kv_heads must be <= %d", MK_MAX_KVH);
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G > 16 || G * c->head_dim > 1024)
     return fail(nullptr, MK_ERR_UNSUPPORTED, "group size must be <= 16 and group width <= 1024");
@@ -270,7 +271,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
 
   S->n_up_claimers = n_w;
   S->n_down_claimers = n_w;
-  const int qkv_np = 1;
+  const int qkv_np = 2;
   S->n_qkv.assign(KVH, 0);
 
   for (int l = 0; l < L; ++l) {
@@ -278,6 +279,23 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     auto wait_input = [&](mk_task& t) {
       if (l > 0) add_wait(t, resid(l), NB);
     };
+    // router over K splits; the last one does top-k and route finalize
+    begin_wave();
+    const int rpanels = h->e_pad / 16;
+    for (int ks = 0; ks < h->router_ks; ++ks)
+      for (int p = 0; p < rpanels; p += h->router_np) {
+        mk_task t = make_task(MK_OP_ROUTER, l);
+        t.a[0] = p;
+        t.a[1] = std::min(h->router_np, rpanels - p);
+        t.a[2] = ks * kc / h->router_ks;
+        t.a[3] = (ks + 1) * kc / h->router_ks;
+        t.a[4] = ks;
+        t.a[5] = x.router;
+        wait_input(t);
+        t.sig_ctr[0] = x.route;
+        push(t);
+      }
+    S->n_router = h->n_router_tasks;
     // qkv, per kv group: its q heads, its k head, its v head
     begin_wave();
     for (int g = 0; g < KVH; ++g) {
@@ -299,23 +317,6 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         }
       S->n_qkv[g] = n;
     }
-    // router over K splits; the last one does top-k and route finalize
-    begin_wave();
-    const int rpanels = h->e_pad / 16;
-    for (int ks = 0; ks < h->router_ks; ++ks)
-      for (int p = 0; p < rpanels; p += h->router_np) {
-        mk_task t = make_task(MK_OP_ROUTER, l);
-        t.a[0] = p;
-        t.a[1] = std::min(h->router_np, rpanels - p);
-        t.a[2] = ks * kc / h->router_ks;
-        t.a[3] = (ks + 1) * kc / h->router_ks;
-        t.a[4] = ks;
-        t.a[5] = x.router;
-        wait_input(t);
-        t.sig_ctr[0] = x.route;
-        push(t);
-      }
-    S->n_router = h->n_router_tasks;
     // attention splits; the last split of a (sequence, group) combines
     begin_wave();
     const int ns = splits_for(h, l, S->bucket);
@@ -339,10 +340,13 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         }
     // MoE up/gate claimers
     begin_wave();
+    const int n_attn = B * KVH * ns;
     for (int i = 0; i < S->n_up_claimers; ++i) {
       mk_task t = make_task(MK_OP_MOE_UP, l);
       t.a[0] = x.up_claim;
       t.a[1] = x.up_done;
+      // claimers likely free when the queue opens (those not running attention)
+      t.a[2] = std::max(1, S->n_up_claimers - n_attn);
       add_wait(t, x.route, 1);
       push(t);
     }
@@ -529,7 +533,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   for (int l = 0; l < L; ++l) {
     const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
     int k = S.c_layer0 + l * S.c_per_layer;
-    for (int g = 0; g < KVH; ++g) want[k++] = (h->G * c.head_dim + 2 * c.head_dim) / 16;
+    for (int g = 0; g < KVH; ++g) want[k++] = S.n_qkv[g];
     for (int i = 0; i < B * KVH; ++i) want[k++] = ns;
     for (int g = 0; g < KVH; ++g) want[k++] = B;
     want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks

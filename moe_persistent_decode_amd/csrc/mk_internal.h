@@ -19,6 +19,9 @@
 #define MK_WGS_PER_CU 1
 #define MK_MAX_CUS 1024
 #define MK_MAX_TOPK 8
+#define MK_MAX_KVH 16   // kv heads (n_q_heads <= 256 with groups <= 16)
+#define MK_MAX_RKS 4    // router K splits
+#define MK_MAX_F 768    // expert width
 #define MK_TASK_INTS 32
 
 // Opcodes. The post names sixteen opcodes for its model family; this model

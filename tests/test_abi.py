@@ -1,0 +1,153 @@
+"""CPU tests of the C ABI: exports, host-side validation, the task schedule.
+
+No GPU is touched: the library is loaded, every function that include/mk.h
+declares must be exported, and host-only handles (mk_create_host_only) build
+and simulate the per-CU task lists of the persistent kernel.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mkinputs import configs
+from moe_persistent_decode_amd import sol
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(mk_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    import moe_persistent_decode_amd as mk
+    declared = _header_functions()
+    assert len(declared) >= 15, declared
+    lib = ctypes.CDLL(mk.LIB_PATH)
+    missing = [f for f in declared if not hasattr(lib, f)]
+    assert not missing, missing
+    assert sorted(mk.EXPORTS) == declared
+
+
+def _host(m, batch=1, max_seq=8192 + 64, n_cus=256, mode=0):
+    import moe_persistent_decode_amd as mk
+    from moe_persistent_decode_amd.binding import Decoder
+    P = m.page_size
+    mpps = -(-max_seq // P)
+    cfg = mk.make_config(m, batch, max_seq, mpps * batch, mpps, mode)
+    return Decoder(cfg, host_only_cus=n_cus)
+
+
+def _bad(m, **kw):
+    import moe_persistent_decode_amd as mk
+    from moe_persistent_decode_amd.binding import Decoder
+    cfg = mk.make_config(m, 1, 1024, 64, 64, 0)
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    with pytest.raises(mk.MkError) as e:
+        Decoder(cfg, host_only_cus=256)
+    return e.value
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 300), ("hidden", 4096), ("head_dim", 96), ("n_q_heads", 5), ("n_q_heads", 64), ("n_experts", 12),
+    ("top_k", 9), ("top_k", 0), ("expert_ffn", 100), ("vocab", 1000), ("page_size", 32),
+    ("n_layers", 0), ("max_batch", 0), ("max_batch", 33), ("n_pages", 0), ("rms_eps", -1.0),
+])
+def test_invalid_configs_are_rejected(field, value):
+    err = _bad(configs.TINY, **{field: value})
+    assert err.status in (1, 2), err
+
+
+def test_schedule_full_model_batch1():
+    m = configs.FULL48
+    d = _host(m)
+    info = d.schedule_info(1, 8192)
+    assert info.n_cus == 256
+    assert info.max_tasks_per_cu <= -(-info.n_tasks // 256) + 1
+    tasks, off = d.schedule_export(1, 8192)
+    assert off[0] == 0 and off[-1] == info.n_tasks and np.all(np.diff(off) >= 0)
+    ops = tasks[:, 0] & 0xFF
+    # every layer's QKV covers the projection's output panels exactly once
+    assert np.count_nonzero(ops == 10) >= 1  # LM head tasks
+    # weight bytes the schedule streams: all dense weights, the LM head and 8 experts per layer
+    exp = sum(sol.layer_weight_bytes(m) - 2 * m.hidden for _ in range(m.n_layers))
+    assert info.weight_bytes_per_step >= exp
+    st, msg = d.simulate(1, 8192, [m.top_k] * m.n_layers, seed=1)
+    assert st == 0, msg
+    d.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_schedule_simulation_random_routing_completes(seed):
+    m = configs.small_variant(configs.FULL48, n_layers=4)
+    d = _host(m)
+    rng = np.random.default_rng(seed)
+    st, msg = d.simulate(1, 8192, rng.integers(1, m.top_k + 1, size=m.n_layers), seed=seed)
+    assert st == 0, msg
+    d.close()
+
+
+def test_schedule_simulation_detects_a_lost_signal():
+    """Dropping one task's signal must leave a waiter unsatisfied (the
+    simulator reports the deadlock rather than completing)."""
+    m = configs.small_variant(configs.FULL48, n_layers=2)
+    d = _host(m)
+    info = d.schedule_info(1, 4096)
+    st_ok, _ = d.simulate(1, 4096, [8, 8], seed=0)
+    assert st_ok == 0
+    st, msg = d.simulate(1, 4096, [8, 8], seed=0, corrupt_task=info.n_tasks // 3)
+    assert st != 0 and msg
+    d.close()
+
+
+def test_schedule_tiny_model_on_few_cus():
+    d = _host(configs.TINY, max_seq=256, n_cus=4)
+    st, msg = d.simulate(1, 200, [2, 2], seed=3)
+    assert st == 0, msg
+    d.close()
+
+
+# ---- speed-of-light arithmetic against the megakernel post's numbers
+# (section "What is a Megakernel?" / introduction: a 30B model with 3.3B active
+# parameters streams 6.6 GB of bf16 weights plus about 0.5 GB of KV at 8K per
+# step; at 3.35 TB/s that is about 470 tok/s)
+
+def test_model_sizes_match_the_posts_description():
+    total, active = configs.FULL48.param_counts()
+    assert abs(total / 1e9 - 30.4) < 0.5
+    assert abs(active / 1e9 - 3.3) < 0.05
+    kv = sum(min(8192, configs.FULL48.layer_window(l)) or 8192 for l in range(48)) \
+        * sol.kv_bytes_per_token(configs.FULL48)
+    assert abs(kv / 1e9 - 0.5) < 0.01
+
+
+def test_sol_reproduces_the_posts_470_tok_s():
+    m = configs.FULL48
+    _, active = m.param_counts()
+    kv = sum(min(8192, m.layer_window(l)) or 8192 for l in range(48)) * sol.kv_bytes_per_token(m)
+    post_bytes = 2 * active + kv
+    assert abs(sol.sol_tokens_per_s(post_bytes, 1, 3.35e12) - 470) < 10
+    # step_bytes streams the same except the embedding table (one row is read)
+    # and adds the token's K/V append and the fp32 logits written
+    b = sol.step_bytes(m, [8192], [8] * 48)
+    emb = 2 * m.vocab * m.hidden
+    extra = 48 * sol.kv_bytes_per_token(m) + 2 * m.hidden + 4 * m.vocab
+    assert b == post_bytes - emb + extra
+
+
+def test_step_bytes_window_and_batch():
+    m = configs.FULL48
+    one = sol.step_bytes(m, [100], [8] * 48)
+    two = sol.step_bytes(m, [100, 100], [8] * 48)
+    per_seq = 48 * 101 * sol.kv_bytes_per_token(m) + 2 * m.hidden + 4 * m.vocab
+    assert two - one == per_seq
+    # beyond the window only full layers grow
+    a = sol.step_bytes(m, [5000], [8] * 48)
+    b = sol.step_bytes(m, [5001], [8] * 48)
+    assert b - a == 12 * sol.kv_bytes_per_token(m)
