@@ -15,16 +15,34 @@
 // switched off, is the kernel-per-op variant.
 //
 // Memory ordering on CDNA4. Each XCD has its own L2, which is not coherent with
-// the other XCDs' L2s. A C++ release/acquire at agent scope is implemented by
-// writing back / invalidating the whole L2 (buffer_wbl2 / buffer_inv), which
-// costs microseconds per task, so the interpreter does not use them. Instead
-// every activation that crosses compute units within a step is stored and
-// loaded with device-scope (sc1) buffer instructions, which bypass the
-// non-coherent cache levels; a producer waits for its own stores to complete
-// (s_waitcnt) before its counter increment, and a consumer issues its loads
-// only after it has observed the counter. Weights and the KV cache written in
-// earlier steps are read with ordinary (non-temporal) loads: nothing writes
-// them during a step, and kernel boundaries make earlier steps' writes visible.
+// the other XCDs' L2s (plain loads on one XCD were measured to return values
+// another XCD had overwritten, within a launch and across launches). A C++
+// release/acquire at agent scope is implemented by writing back / invalidating
+// the whole L2 (buffer_wbl2 / buffer_inv), which costs microseconds per task,
+// so the interpreter does not use them. Instead every activation that crosses
+// compute units within a step is stored and loaded with device-scope (sc1)
+// buffer instructions, which bypass the non-coherent cache levels; a producer
+// waits for its own stores to complete (s_waitcnt) before its counter
+// increment, and a consumer issues its loads only after it has observed the
+// counter. Weights and the KV cache written in earlier steps are read with
+// ordinary (non-temporal) loads: nothing writes them during a step, and kernel
+// boundaries make earlier steps' writes visible to ordinary loads of data no
+// XCD has cached (weights are never written after loading; a KV slot is
+// written once, by the step that appends it, and read by later steps).
+//
+// Matrix products. Every projection runs on the matrix cores with the tokens
+// as MFMA rows (16 per tile, batch <= 32 in two tiles) and 16 weight columns
+// per panel: v_mfma_f32_16x16x32_bf16 takes the activations as the A operand
+// (bf16) and one 1 KB chunk of a weight panel as the B operand, in exactly the
+// layout the panels are stored in. The K dimension is spread over the 8 waves
+// and their partial tiles are summed through LDS in a fixed order.
+//
+// Layer inputs. The residual add of a column block (the last contribution to
+// arrive performs it) also writes u = bf16(h * gamma_next) and the block's
+// per-token sum of squares. A consumer multiplies its projection of u by
+// 1/sqrt(mean(h^2) + eps) per token, which equals projecting the RMS-normalised
+// input (the norm's scale is a per-row factor), so no workgroup ever forms the
+// normalised vector itself.
 #include <hip/hip_runtime.h>
 
 #include "mk_internal.h"
@@ -44,8 +62,6 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // compile to scalar branches instead of exec-mask juggling.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // float -> bf16 bits, round to nearest even
 __device__ __forceinline__ uint32_t f2bf(float f) {
@@ -53,6 +69,7 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -64,7 +81,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
 }
 constexpr int kSC1 = 16;  // cache-policy bit: device (agent) scope coherence
 
-// Device-coherent access to a buffer of 32-bit words shared across compute units.
+// Device-coherent access to a buffer shared across compute units.
 struct Pub {
   __amdgpu_buffer_rsrc_t r;
   __device__ __forceinline__ explicit Pub(const void* base) : r(rsrc_of(base)) {}
@@ -110,13 +127,9 @@ __device__ __forceinline__ void sync_published() {
   __syncthreads();
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 constexpr float kNegInf = -__builtin_inff();
+
+// ------------------------------------------------------------------ LDS
 
 struct SmemAttn {
   float m[MK_WAVES][16];
@@ -124,7 +137,7 @@ struct SmemAttn {
   float o[MK_WAVES][128][17];
 };
 
-// Attention combine scratch: per split and head, the rescale factor.
+// Attention combine scratch: per split and head, the rescale factor and sum.
 #define MK_MAX_SPLITS 256
 struct SmemComb {
   float f[MK_MAX_SPLITS][16];
@@ -133,59 +146,62 @@ struct SmemComb {
   float L[16];
 };
 
-// LDS per workgroup: with one workgroup per compute unit, more than half of
-// gfx950's 160 KB (so exactly one fits); with two, more than a third.
 struct SmemTopk {
-  alignas(16) float logit[128];
-  float sel_val[MK_MAX_TOPK];
-  int sel_idx[MK_MAX_TOPK];
+  alignas(16) float logit[MK_MAX_BATCH][128];
+  float sel_val[MK_MAX_BATCH][MK_MAX_TOPK];
+  int sel_idx[MK_MAX_BATCH][MK_MAX_TOPK];
 };
 
+// Partial output tiles of the 8 waves: [wave][panel][row tile][16 x 16].
+#define MK_RED_TILES 8  // panels x row tiles of the largest product
 union SmemU {
-  float red[MK_WAVES][64];
-  SmemTopk tk;
+  float red[MK_WAVES * MK_RED_TILES * 256];
   SmemAttn at;
   SmemComb cb;
-  float pad[MK_WGS_PER_CU == 1 ? 20480 : 11264];
+  SmemTopk tk;
 };
 
-// Arrays read as float4 must be 16-byte aligned: a 16-byte LDS read from a
-// 4-byte aligned address runs about five times slower on gfx950 (a 64-chunk
-// GEMV over an LDS vector measured 3.7 us unaligned against 0.7 us aligned).
+// LDS per workgroup: one workgroup per compute unit (more than half of
+// gfx950's 160 KB).
 struct Smem {
   SmemU u;
-  alignas(16) float out[64];
-  alignas(16) float ssq[128];
-  alignas(16) float xc[2048];  // normalised input of one layer for batch 1 (per compute unit)
-  alignas(16) float us[768];   // expert hidden of one routed slot (down projection input)
-  alignas(16) float vred[MK_WAVES];
+  alignas(16) float out[MK_RED_TILES * 256];     // summed tiles [panel][row tile][16][16]
+  alignas(16) uint16_t act[MK_MAX_BATCH * MK_MAX_F];  // expert hidden rows (bf16), down projection input
+  alignas(16) float ssq[MK_MAX_BATCH * 64];      // per-token sums of squares per column block
+  float inv_rms[MK_MAX_BATCH];
+  float tkw[MK_MAX_BATCH * MK_MAX_TOPK];
+  int row_off[MK_UP_BATCH_MAX][MK_MAX_BATCH];    // activation row offsets of the current items
+  float vred[MK_WAVES];
   int ired[MK_WAVES];
   int flag;
   int claim;
   int old;                // value an arrival counter held before this workgroup's increment
   uint32_t t_waited;
   uint32_t t_mark[4];     // op-defined intermediate timestamps (e.g. inputs ready, computed)
-  int xc_layer;           // layer whose normalised input xc holds (-1: none)
   int rt_hdr[4];          // route header: n_active, up items, down items
   int rt_e[128];          // active experts, ascending
-  int rt_slot[128];       // batch 1: the routed slot of each active expert
+  int rt_cnt[128];        // tokens routed to each active expert
+  int rt_slot[128 * MK_MAX_BATCH];  // per active expert: its routed slots b * k + j, ascending b
 };
-static_assert(offsetof(Smem, xc) % 16 == 0 && offsetof(Smem, us) % 16 == 0 &&
-              offsetof(Smem, out) % 16 == 0 && offsetof(Smem, ssq) % 16 == 0, "LDS vectors 16-byte aligned");
+static_assert(offsetof(Smem, out) % 16 == 0 && offsetof(Smem, act) % 16 == 0 && offsetof(Smem, ssq) % 16 == 0,
+              "LDS vectors 16-byte aligned");
 
-__device__ void raise_error(const mk_params& P, uint32_t code, uint32_t detail, uint32_t value) {
+__device__ __noinline__ void raise_error_w(uint32_t* err, uint32_t code, uint32_t detail, uint32_t value) {
   uint32_t expected = 0;
-  if (__hip_atomic_compare_exchange_strong(&P.err[0], &expected, code, __ATOMIC_RELAXED,
+  if (__hip_atomic_compare_exchange_strong(&err[0], &expected, code, __ATOMIC_RELAXED,
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-    __hip_atomic_store(&P.err[1], detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&P.err[2], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&P.err[3], (uint32_t)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&err[1], detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&err[2], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&err[3], (uint32_t)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+// (the parameter block is not passed to an out-of-line call: that would make
+// the compiler copy it to scratch memory)
+#define raise_error(P, code, detail, value) raise_error_w((P).err, (code), (detail), (value))
 
 // Spin (thread 0) until ctr[c] >= tgt for each wait, or until another
 // workgroup raised an error, or until the time limit. Block-uniform result.
-__device__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm) {
+__device__ __forceinline__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm) {
   if (threadIdx.x == 0) {
     int ok = ld_relaxed(&P.err[0]) == 0;
     if (ok && P.waits_enabled) {
@@ -230,21 +246,84 @@ __device__ __forceinline__ int layer_window(const mk_params& P, int l) {
   return (l % P.full_every) == P.full_every - 1 ? 0 : P.window;
 }
 
-// ----------------------------------------------------- batch-1 GEMV panels
+__device__ __forceinline__ void mark(Smem& sm, int k) {
+  if (threadIdx.x == 0) sm.t_mark[k] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+}
+
+// ---------------------------------------------------------- arrivals
+// Count one arrival on counter c once every wave's device-coherent stores
+// have completed.
+__device__ __forceinline__ void arrive_nr(const mk_params& P, int32_t c) {
+  sync_published();
+  if (threadIdx.x == 0 && c >= 0)
+    __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The same, returning (block-uniform) the value the counter held before this
+// arrival, so the last of a known number of arrivals can act on the result.
+__device__ __forceinline__ int arrive(const mk_params& P, int32_t c, Smem& sm) {
+  sync_published();
+  if (threadIdx.x == 0)
+    sm.old = (int)__hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int old = sm.old;
+  __syncthreads();
+  return old;
+}
+
+// Claim n consecutive items of a work queue: returns (block-uniform) the first.
+__device__ __forceinline__ int claim_n(const mk_params& P, int32_t c, int n, Smem& sm) {
+  if (threadIdx.x == 0)
+    sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int id = sm.claim;
+  __syncthreads();
+  return id;
+}
+
+// ------------------------------------------------------- scratch addressing
+// Layer inputs alternate between two buffers by layer parity: u and the sums
+// of squares of layer l are read while layer l's residual adds write those of
+// layer l + 1.
+__device__ __forceinline__ const uint16_t* u_of(const mk_params& P, int l) {
+  return P.u + (size_t)(l & 1) * P.B * P.H;
+}
+__device__ __forceinline__ uint16_t* u_of_w(const mk_params& P, int l) {
+  return P.u + (size_t)(l & 1) * P.B * P.H;
+}
+__device__ __forceinline__ float* ssq_of(const mk_params& P, int l) {
+  return P.ssq + (size_t)(l & 1) * P.B * P.NB;
+}
+
+// 1/sqrt(mean(h^2) + eps) of every token of layer l's input, from the column
+// blocks' sums of squares (summed in block order), into sm.inv_rms.
+__device__ __forceinline__ void load_inv_rms(const mk_params& P, int l, Smem& sm) {
+  const Pub S(ssq_of(P, l));
+  const int n = P.B * P.NB;
+  for (int i = threadIdx.x; i < n; i += MK_WG_THREADS) sm.ssq[i] = S.ldf(i);
+  __syncthreads();
+  if ((int)threadIdx.x < P.B) {
+    const float* q = sm.ssq + threadIdx.x * P.NB;
+    float tot = 0.f;
+    for (int k = 0; k < P.NB; ++k) tot += q[k];
+    sm.inv_rms[threadIdx.x] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+  }
+  __syncthreads();
+}
+
+// --------------------------------------------------------- matrix tiles
 //
 // Weight matrices [K x N] are stored panel-tiled: 16-column panels, each a run
 // of K/32 chunks of 1 KB; in a chunk, lane l holds the 8 bf16 of rows
-// 32c + 8(l/16) + i (i = 0..7) of column 16j + l%16. Chunk c of a panel goes
-// to wave c % 8, so each wave keeps its slice of the activation vector in
-// registers and every load is one contiguous 1 KB line per wave.
-
+// 32c + 8(l/16) + i (i = 0..7) of column 16j + l%16 (the B operand of
+// v_mfma_f32_16x16x32_bf16). Chunk c of a panel goes to wave c % 8, so every
+// load is one contiguous 1 KB line per wave.
 template <int NP, int NCH>
 struct WTile {
   u32x4_t v[NP][NCH];
 };
 
-// Chunks outside [c0, c1) and panels at or beyond np are zero, so the GEMVs
-// below run without per-chunk branches.
+// Chunks outside [c0, c1) and panels at or beyond np are zero.
 template <int NP, int NCH>
 __device__ __forceinline__ void wtile_load(WTile<NP, NCH>& w, const uint16_t* base, size_t pstride,
                                            int np, int c0, int c1) {
@@ -261,232 +340,110 @@ __device__ __forceinline__ void wtile_load(WTile<NP, NCH>& w, const uint16_t* ba
     }
 }
 
-__device__ __forceinline__ float dot8(float4 x0, float4 x1, u32x4_t q, float s) {
-  s = fmaf(x0.x, bf_lo(q.x), s);
-  s = fmaf(x0.y, bf_hi(q.x), s);
-  s = fmaf(x0.z, bf_lo(q.y), s);
-  s = fmaf(x0.w, bf_hi(q.y), s);
-  s = fmaf(x1.x, bf_lo(q.z), s);
-  s = fmaf(x1.y, bf_hi(q.z), s);
-  s = fmaf(x1.z, bf_lo(q.w), s);
-  s = fmaf(x1.w, bf_hi(q.w), s);
-  return s;
-}
+// Activation operand: MT row tiles of 16 tokens; lane l holds the 8 bf16 of
+// row 16 mt + l%16 at K offsets 32c + 8(l/16) .. +7 of each of its chunks.
+template <int MT, int NCH>
+struct ATile {
+  u32x4_t a[MT][NCH];
+};
 
-// y[16*pp + col] = sum_k x[k - 32*c0] * W[k][col] over chunks [c0, c1), into sm.out.
-// x: float32 activations (another compute unit's output) starting at row 32*c0.
-template <int NP, int NCH>
-__device__ void gemv_b1(const WTile<NP, NCH>& w, const float* x, int np, int c0, int c1, Smem& sm) {
-  const Pub X(x);
+// A rows from a bf16 matrix shared across compute units; row r starts at
+// element offset off[r] (negative: a zero row). Chunks are absolute: row
+// element 32c + 8(l/16). Chunks outside [c0, c1) are zero.
+template <int MT, int NCH>
+__device__ __forceinline__ void atile_load_bf16(ATile<MT, NCH>& A, const Pub& src, const int* off, int c0, int c1) {
   const int wv = wave_id(), ln = lane_id();
-  float acc[NP];
 #pragma unroll
-  for (int pp = 0; pp < NP; ++pp) acc[pp] = 0.f;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int o = off[mt * 16 + (ln & 15)];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    // out-of-range chunks read a valid row and multiply zero weights
-    const int c = max(min(c0 + wv + MK_WAVES * i, c1 - 1), c0);
-    const int xi = (c - c0) * 32 + 8 * (ln >> 4);
-    const float4 x0 = X.ldf4(xi), x1 = X.ldf4(xi + 4);
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
-  }
-#pragma unroll
-  for (int pp = 0; pp < NP; ++pp) {
-    acc[pp] += __shfl_xor(acc[pp], 16);
-    acc[pp] += __shfl_xor(acc[pp], 32);
-  }
-  if (ln < 16) {
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
-      if (pp < np) sm.u.red[wv][pp * 16 + ln] = acc[pp];
-  }
-  __syncthreads();
-  if (threadIdx.x < np * 16) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k][threadIdx.x];
-    sm.out[threadIdx.x] = s;
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void mark(Smem& sm, int k) {
-  if (threadIdx.x == 0) sm.t_mark[k] = (uint32_t)__builtin_amdgcn_s_memrealtime();
-}
-
-// ---------------------------------------------------------- arrivals
-// Count one arrival on counter c once every wave's device-coherent stores
-// have completed.
-__device__ void arrive_nr(const mk_params& P, int32_t c) {
-  sync_published();
-  if (threadIdx.x == 0 && c >= 0)
-    __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The same, returning (block-uniform) the value the counter held before this
-// arrival, so the last of a known number of arrivals can act on the result.
-__device__ int arrive(const mk_params& P, int32_t c, Smem& sm) {
-  sync_published();
-  if (threadIdx.x == 0)
-    sm.old = (int)__hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int old = sm.old;
-  __syncthreads();
-  return old;
-}
-
-// ----------------------------------------------------- layer input x-hat
-// The normalised input of layer l (megakernel post, section "Reduce wave
-// quantization": attention and the MoE both read the same RMS-normalised
-// input). Layer 0's residual is the token's embedding row; later layers'
-// residual stream h is complete once every column block's residual add has
-// arrived, each block leaving its sum of squares in ssq. Every compute unit
-// forms x = h / sqrt(mean(h^2) + eps) * gamma_l once per layer into LDS
-// (batch 1), so the fused residual + RMSNorm needs no task of its own.
-__device__ bool load_xhat(const mk_params& P, int l, Smem& sm) {
-  if (sm.xc_layer == l) return true;
-  const int H = P.H;
-  const uint16_t* gam = P.gamma + (size_t)l * H;
-  constexpr int NV = 2048 / MK_WG_THREADS;  // H <= 2048
-  float v[NV];
-  float ss = 0.f;
-  if (l == 0) {
-    int tok = P.tokens[0];
-    if (tok < 0 || tok >= P.V) {
-      if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 1000, (uint32_t)tok);
-      tok = 0;
+    for (int i = 0; i < NCH; ++i) {
+      const int c = c0 + wv + MK_WAVES * i;
+      A.a[mt][i] = (c < c1 && o >= 0) ? src.ld16x8(o + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
     }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int i = threadIdx.x + k * MK_WG_THREADS;
-      v[k] = i < H ? bf2f(P.emb[(size_t)tok * H + i]) : 0.f;
-      ss = fmaf(v[k], v[k], ss);
-    }
-    ss = wave_sum(ss);
-    if (lane_id() == 0) sm.vred[wave_id()] = ss;
-  } else {
-    const Pub h(P.h), q(P.ssq);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int i = threadIdx.x + k * MK_WG_THREADS;
-      v[k] = i < H ? h.ldf(i) : 0.f;
-    }
-    if (threadIdx.x < P.NB) sm.ssq[threadIdx.x] = q.ldf(threadIdx.x);
   }
-  __syncthreads();
-  float tot = 0.f;
-  if (l == 0) {
-#pragma unroll
-    for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
-  } else {
-    for (int k = 0; k < P.NB; ++k) tot += sm.ssq[k];
-  }
-  const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int i = threadIdx.x + k * MK_WG_THREADS;
-    if (i < H) sm.xc[i] = v[k] * inv * bf2f(gam[i]);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) sm.xc_layer = l;
-  __syncthreads();
-  return true;
 }
 
-// gemv with x from the LDS copy of x-hat (rows 32*c0 .. of the layer input)
-template <int NP, int NCH>
-__device__ void gemv_lds(const WTile<NP, NCH>& w, const float* xl, int np, int c0, int c1, Smem& sm) {
+// A rows from a float32 matrix shared across compute units, rounded to bf16;
+// row r starts at off[r]; chunk c reads row elements 32 (c - c0) + 8(l/16).
+template <int MT, int NCH>
+__device__ __forceinline__ void atile_load_f32(ATile<MT, NCH>& A, const Pub& src, const int* off, int c0, int c1) {
   const int wv = wave_id(), ln = lane_id();
-  float acc[NP];
+  float4 x[MT][NCH][2];
 #pragma unroll
-  for (int pp = 0; pp < NP; ++pp) acc[pp] = 0.f;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int o = off[mt * 16 + (ln & 15)];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    // out-of-range chunks read a valid row and multiply zero weights
-    const int c = max(min(c0 + wv + MK_WAVES * i, c1 - 1), c0);
-    const float4* xp = (const float4*)(xl + c * 32 + 8 * (ln >> 4));
-    const float4 x0 = xp[0], x1 = xp[1];
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) acc[pp] = dot8(x0, x1, w.v[pp][i], acc[pp]);
-  }
-#pragma unroll
-  for (int pp = 0; pp < NP; ++pp) {
-    acc[pp] += __shfl_xor(acc[pp], 16);
-    acc[pp] += __shfl_xor(acc[pp], 32);
-  }
-  if (ln < 16) {
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
-      if (pp < np) sm.u.red[wv][pp * 16 + ln] = acc[pp];
-  }
-  __syncthreads();
-  if (threadIdx.x < np * 16) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k][threadIdx.x];
-    sm.out[threadIdx.x] = s;
-  }
-  __syncthreads();
-}
-
-// -------------------------------------------------------------------- QKV
-// QKV panels with RoPE in the epilogue and the K/V append into the paged
-// cache (megakernel post, section "Tasks": QKV_PROJ applies RoPE in-register
-// in its epilogue; tiny-vllm walkthrough: the new token's K/V are written to
-// page block_table[pos / 16], slot pos % 16, before attention reads them).
-template <int NCH>
-__device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int l = t.layer, p0 = t.a[0], np = t.a[1];
-  const int kc = P.H / 32;
-  const size_t pstride = (size_t)kc * 512;
-  WTile<2, NCH> w;  // up to two panels per task
-  wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
-  if (!wait_task(P, t, sm)) return;
-  load_xhat(P, l, sm);
-  mark(sm, 0);
-  const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
-  gemv_lds(w, sm.xc, np, 0, kc, sm);
-  mark(sm, 1);
-  if (wave_id() == 0) {
-    const int tid = threadIdx.x;
-    const float y = tid < np * 16 ? sm.out[tid] : 0.f;
-    const float yp = __shfl_xor(y, 1);
-    const int seq = P.seq_lens[0];
-    if (tid < np * 16) {
-      if (seq < 1 || seq > P.max_seq) {
-        if (tid == 0) raise_error(P, MK_DEVERR_FAULT, 2000, (uint32_t)seq);
+    for (int i = 0; i < NCH; ++i) {
+      const int c = c0 + wv + MK_WAVES * i;
+      if (c < c1 && o >= 0) {
+        const int e = o + 32 * (c - c0) + 8 * (ln >> 4);
+        x[mt][i][0] = src.ldf4(e);
+        x[mt][i][1] = src.ldf4(e + 4);
       } else {
-        const int pos = seq - 1;
-        const int n = p0 * 16 + tid;
-        const bool odd = n & 1;
-        const int page = P.bt[pos / PS];
-        const bool page_ok = page >= 0 && page < P.n_pages;
-        if (n < qd + kvd) {
-          const int d = (n < qd ? n : n - qd) % D;
-          const float c = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0];
-          const float s = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1];
-          // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
-          const float x0 = odd ? yp : y, x1 = odd ? y : yp;
-          const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
-          if (n < qd) {
-            Pub(P.q).stf(n, r);
-          } else if (page_ok) {
-            const int g = (n - qd) / D;
-            const int off = ((page * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d;
-            Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(r));
-          }
-        } else if (page_ok) {
-          const int nn = n - qd - kvd;
-          const int g = nn / D, d = nn % D;
-          const int off = ((page * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS);
-          Pub(P.kv + l * P.s_kv_l).st16(off, (uint16_t)f2bf(y));
-        }
-        if (!page_ok && tid == 0) raise_error(P, MK_DEVERR_FAULT, 3000, (uint32_t)page);
+        x[mt][i][0] = x[mt][i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   }
-  arrive_nr(P, t.sig_ctr[0]);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float4 p = x[mt][i][0], q = x[mt][i][1];
+      A.a[mt][i] = u32x4_t{pack_bf2(p.x, p.y), pack_bf2(p.z, p.w), pack_bf2(q.x, q.y), pack_bf2(q.z, q.w)};
+    }
+}
+
+template <int NP, int MT>
+struct Acc {
+  f32x4_t c[NP][MT];
+};
+
+template <int NP, int MT, int NCH>
+__device__ __forceinline__ void mfma_tiles(Acc<NP, MT>& acc, const WTile<NP, NCH>& w, const ATile<MT, NCH>& A) {
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc.c[pp][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A.a[mt][i]),
+                                                                __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                acc.c[pp][mt], 0, 0, 0);
+}
+
+// Sum the 8 waves' partial tiles (fixed order) into sm.out, indexed
+// [(pp * MT + mt) * 256 + row * 16 + col].
+template <int NP, int MT>
+__device__ __forceinline__ void reduce_tiles(const Acc<NP, MT>& acc, Smem& sm) {
+  static_assert(NP * MT <= MK_RED_TILES, "reduction buffer");
+  constexpr int N = NP * MT * 256;
+  const int wv = wave_id(), ln = lane_id();
+  float* red = sm.u.red + wv * N;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(pp * MT + mt) * 256 + (4 * (ln >> 4) + i) * 16 + (ln & 15)] = acc.c[pp][mt][i];
+  __syncthreads();
+#pragma unroll
+  for (int o = threadIdx.x; o < N; o += MK_WG_THREADS) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k * N + o];
+    sm.out[o] = s;
+  }
+  __syncthreads();
+}
+
+// Row offsets of the batch's tokens (row b at b * stride + base), -1 beyond.
+__device__ __forceinline__ void set_rows_batch(const mk_params& P, Smem& sm, int slot, int stride, int base) {
+  if (threadIdx.x < MK_MAX_BATCH) sm.row_off[slot][threadIdx.x] = (int)threadIdx.x < P.B ? (int)threadIdx.x * stride + base : -1;
 }
 
 // -------------------------------------------------------------- attention
@@ -500,7 +457,7 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
 // this step). The split that completes a (sequence, group) merges all splits
 // (ATTN_COMBINE) without a task of its own.
 template <int D>
-__device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm);
+__device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm);
 
 // One wave's operands of one KV page of one kv group: K rows (keys) for the
 // score MFMA, V^T tiles for the output MFMA.
@@ -689,7 +646,7 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
 // attention output (megakernel post, section "Tasks": ATTN_COMBINE):
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, splits in fixed order.
 template <int D>
-__device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm) {
+__device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm) {
   const int G = P.G;
   const int stride = G * D + 2 * G;
   const Pub src(P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride);
@@ -751,64 +708,175 @@ __device__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm)
 #pragma unroll
   for (int u = 0; u < NO; ++u) {
     const int idx = threadIdx.x + u * MK_WG_THREADS;
-    if (idx < G * D) dst.stf(idx, O[u] / C.L[idx / D]);
+    // bf16: the O projection's matrix-core operand
+    if (idx < G * D) dst.st16(idx, (uint16_t)f2bf(O[u] / C.L[idx / D]));
   }
+}
+
+// ---------------------------------------------------------------- embed
+// Layer 0's input for one column block: h = Emb[token] for every sequence,
+// u = bf16(h * gamma_0) and the block's per-token sum of squares.
+__device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv, int n,
+                                                  Smem& sm);
+
+__device__ __forceinline__ void op_embed(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int cb = t.a[0];
+  const int H = P.H, CB = P.CB, n = P.B * CB;
+  constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;  // elements per thread (CB <= 64)
+  float hv[NI];
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int idx = threadIdx.x + k * MK_WG_THREADS;
+    hv[k] = 0.f;
+    if (idx < n) {
+      const int b = idx / CB, c = cb * CB + idx % CB;
+      int tok = P.tokens[b];
+      if (tok < 0 || tok >= P.V) {
+        raise_error(P, MK_DEVERR_FAULT, 1000 + b, (uint32_t)tok);
+        tok = 0;
+      }
+      hv[k] = bf2f(P.emb[(size_t)tok * H + c]);
+    }
+  }
+  write_block_input(P, 0, cb, hv, n, sm);
+  arrive_nr(P, t.sig_ctr[0]);
+}
+
+// Store the residual stream of column block cb (hv[k] = element idx =
+// threadIdx.x + k * 512 of the block, row idx / CB), the next layer's input
+// u = bf16(h * gamma_{l_next}) and the block's per-token sum of squares.
+__device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv, int n,
+                                                  Smem& sm) {
+  const int H = P.H, CB = P.CB;
+  constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;
+  const Pub h(P.h), U(u_of_w(P, l_next));
+  const uint16_t* gam = P.gamma + (size_t)l_next * H;
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int idx = threadIdx.x + k * MK_WG_THREADS;
+    if (idx < n) {
+      const int b = idx / CB, c = cb * CB + idx % CB;
+      h.stf(b * H + c, hv[k]);
+      U.st16(b * H + c, (uint16_t)f2bf(hv[k] * bf2f(gam[c])));
+      sm.out[idx] = hv[k] * hv[k];
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < P.B) {
+    float s = 0.f;
+    for (int i = 0; i < CB; ++i) s += sm.out[threadIdx.x * CB + i];
+    Pub(ssq_of(P, l_next)).stf(threadIdx.x * P.NB + cb, s);
+  }
+}
+
+// -------------------------------------------------------------------- QKV
+// QKV panels with RoPE in the epilogue and the K/V append into the paged
+// cache (megakernel post, section "Tasks": QKV_PROJ applies RoPE in-register
+// in its epilogue; tiny-vllm walkthrough: the new token's K/V are written to
+// page block_table[pos / 16], slot pos % 16, before attention reads them).
+template <int MT, int NCH>
+__device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int l = t.layer, p0 = t.a[0], np = t.a[1];
+  const int kc = P.H / 32;
+  const size_t pstride = (size_t)kc * 512;
+  WTile<2, NCH> w;
+  wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
+  if (!wait_task(P, t, sm)) return;
+  set_rows_batch(P, sm, 0, P.H, 0);
+  __syncthreads();
+  ATile<MT, NCH> A;
+  atile_load_bf16(A, Pub(u_of(P, l)), sm.row_off[0], 0, kc);
+  load_inv_rms(P, l, sm);
+  mark(sm, 0);
+  Acc<2, MT> acc;
+  mfma_tiles(acc, w, A);
+  reduce_tiles(acc, sm);
+  mark(sm, 1);
+  const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
+  const Pub KV(P.kv + l * P.s_kv_l), Q(P.q);
+  for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int b = mt * 16 + m;
+    if (pp >= np || b >= P.B) continue;
+    const int seq = P.seq_lens[b];
+    if (seq < 1 || seq > P.max_seq) {
+      raise_error(P, MK_DEVERR_FAULT, 2000 + b, (uint32_t)seq);
+      continue;
+    }
+    const float inv = sm.inv_rms[b];
+    const float y = sm.out[o] * inv, yp = sm.out[o ^ 1] * inv;  // o ^ 1: the pair partner column
+    const int pos = seq - 1;
+    const int n = (p0 + pp) * 16 + nn;
+    const bool odd = n & 1;
+    const int page = P.bt[b * P.mpps + pos / PS];
+    const bool page_ok = page >= 0 && page < P.n_pages;
+    if (n < qd + kvd) {
+      const int d = (n < qd ? n : n - qd) % D;
+      const float c = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0];
+      const float s = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1];
+      // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
+      const float x0 = odd ? yp : y, x1 = odd ? y : yp;
+      const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
+      if (n < qd) {
+        Q.stf(b * qd + n, r);
+      } else if (page_ok) {
+        const int g = (n - qd) / D;
+        KV.st16(((page * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d, (uint16_t)f2bf(r));
+      }
+    } else if (page_ok) {
+      const int nn2 = n - qd - kvd;
+      const int g = nn2 / D, d = nn2 % D;
+      KV.st16(((page * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS), (uint16_t)f2bf(y));
+    }
+    if (!page_ok) raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
+  }
+  arrive_nr(P, t.sig_ctr[0]);
 }
 
 // ------------------------------------------------------------- residual
 // Residual add of one column block, done by whichever contribution to the
 // block arrives last (the KVH O-projection partials and the block's tile of
-// every routed expert's down projection): h += sum_g a_g + sum_j w_j y_j,
-// the experts summed in rank order (MOE_COMBINE), then the block's sum of
-// squares for the next layer's RMSNorm. Layer 0 adds to the embedding row.
-__device__ void residual_block(const mk_params& P, int l, int cb, Smem& sm) {
-  const int H = P.H, K = P.K, CB = P.CB;
+// every routed expert's down projection): h += sum_g a_g + sum_j w_j y_j per
+// token, the experts summed in rank order (MOE_COMBINE), then the next
+// layer's input u and the block's sums of squares (the fused residual add +
+// RMSNorm of the megakernel post, section "Reduce wave quantization").
+__device__ __forceinline__ void residual_block(const mk_params& P, int l, int cb, Smem& sm) {
+  const int H = P.H, K = P.K, CB = P.CB, B = P.B, n = B * CB;
+  constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;
   const Pub h(P.h), ao(P.ao), dn(P.dn), tkw(P.tk_w);
-  float ss = 0.f;
-  const int i = threadIdx.x;
-  if (i < CB) {
-    const int c = cb * CB + i;
-    // every load in flight before the sums (fixed order: groups, then ranks)
-    float av[MK_MAX_KVH], wv[MK_MAX_TOPK], yv[MK_MAX_TOPK];
-#pragma unroll
-    for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = g < P.KVH ? ao.ldf(g * H + c) : 0.f;
-#pragma unroll
-    for (int j = 0; j < MK_MAX_TOPK; ++j) {
-      wv[j] = j < K ? tkw.ldf(j) : 0.f;
-      yv[j] = j < K ? dn.ldf(j * H + c) : 0.f;
-    }
-    float h0;
-    if (l == 0) {
-      const int tok = P.tokens[0];
-      h0 = (tok >= 0 && tok < P.V) ? bf2f(P.emb[(size_t)tok * H + c]) : 0.f;
-    } else {
-      h0 = h.ldf(c);
-    }
-    float a = 0.f;
-#pragma unroll
-    for (int g = 0; g < MK_MAX_KVH; ++g)
-      if (g < P.KVH) a += av[g];
-    float y = 0.f;
-#pragma unroll
-    for (int j = 0; j < MK_MAX_TOPK; ++j)
-      if (j < K) y = fmaf(wv[j], yv[j], y);
-    const float v = (h0 + a) + y;
-    h.stf(c, v);
-    ss = v * v;
-  }
-  ss = wave_sum(ss);
-  if (lane_id() == 0) sm.vred[wave_id()] = ss;
+  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) sm.tkw[i] = tkw.ldf(i);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float tot = 0.f;
-    for (int k = 0; k < MK_WAVES; ++k) tot += sm.vred[k];
-    Pub(P.ssq).stf(cb, tot);
+  float hv[NI];
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int idx = threadIdx.x + k * MK_WG_THREADS;
+    hv[k] = 0.f;
+    if (idx < n) {
+      const int b = idx / CB, c = cb * CB + idx % CB;
+      // every load in flight before the sums (fixed order: groups, then ranks)
+      float av[MK_MAX_KVH], yv[MK_MAX_TOPK];
+#pragma unroll
+      for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = g < P.KVH ? ao.ldf((g * B + b) * H + c) : 0.f;
+#pragma unroll
+      for (int j = 0; j < MK_MAX_TOPK; ++j) yv[j] = j < K ? dn.ldf((b * K + j) * H + c) : 0.f;
+      const float h0 = h.ldf(b * H + c);
+      float a = 0.f;
+#pragma unroll
+      for (int g = 0; g < MK_MAX_KVH; ++g)
+        if (g < P.KVH) a += av[g];
+      float y = 0.f;
+#pragma unroll
+      for (int j = 0; j < MK_MAX_TOPK; ++j)
+        if (j < K) y = fmaf(sm.tkw[b * K + j], yv[j], y);
+      hv[k] = (h0 + a) + y;
+    }
   }
+  write_block_input(P, l + 1, cb, hv, n, sm);
 }
 
 // After a contribution to column block cb: the last of the block's
 // KVH + n_active contributions does the residual and signals the next layer.
-__device__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base, int cb, Smem& sm) {
+__device__ __forceinline__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base, int cb, Smem& sm) {
   const int n_active = __builtin_amdgcn_readfirstlane(Pub(P.route).ldi(0));
   const int old = arrive(P, ctr_base + cb, sm);
   if (old == P.KVH + n_active - 1) {
@@ -821,7 +889,7 @@ __device__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base,
 // O projection split-K by kv group: group g's heads contribute their slice
 // of the K dimension as soon as that group's attention lands (megakernel
 // post, section "Drop false dependencies"); one task per (group, column block).
-template <int NCH>
+template <int MT, int NCH>
 __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, g = t.a[0], cb = t.a[1];
   const int DP = P.CB / 16, p0 = cb * DP;
@@ -832,9 +900,20 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
   wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, DP, c0, c1);
   if (!wait_task(P, t, sm)) return;
   mark(sm, 0);
-  gemv_b1(w, P.o + (size_t)g * P.G * P.D, DP, c0, c1, sm);
+  set_rows_batch(P, sm, 0, P.QH * P.D, 0);
+  __syncthreads();
+  ATile<MT, NCH> A;
+  atile_load_bf16(A, Pub(P.o), sm.row_off[0], c0, c1);
+  Acc<4, MT> acc;
+  mfma_tiles(acc, w, A);
+  reduce_tiles(acc, sm);
   mark(sm, 1);
-  if (threadIdx.x < DP * 16) Pub(P.ao + (size_t)g * P.H).stf(p0 * 16 + threadIdx.x, sm.out[threadIdx.x]);
+  const Pub AO(P.ao);
+  for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int b = mt * 16 + m;
+    if (pp < DP && b < P.B) AO.stf((g * P.B + b) * P.H + (p0 + pp) * 16 + nn, sm.out[o]);
+  }
   block_arrive(P, t, t.a[2], cb, sm);
 }
 
@@ -843,9 +922,9 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
 // completes the router does ROUTER_TOPK + ROUTE_FINALIZE (megakernel post,
 // section "Tasks"): sum the partials in fixed order, top-k (ties to the lower
 // expert index), softmax over the kept logits, the expert work queue.
-__device__ void topk_finalize(const mk_params& P, int l, Smem& sm);
+__device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm);
 
-template <int NCH>
+template <int MT, int NCH>
 __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, p0 = t.a[0], np = t.a[1], c0 = t.a[2], c1 = t.a[3], ks = t.a[4];
   const int kc = P.H / 32;
@@ -853,12 +932,22 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   WTile<2, NCH> w;
   wtile_load(w, P.wr + l * P.s_wr + (size_t)p0 * pstride, pstride, np, c0, c1);
   if (!wait_task(P, t, sm)) return;
-  load_xhat(P, l, sm);
+  set_rows_batch(P, sm, 0, P.H, 0);
+  __syncthreads();
+  ATile<MT, NCH> A;
+  atile_load_bf16(A, Pub(u_of(P, l)), sm.row_off[0], c0, c1);
+  load_inv_rms(P, l, sm);
   mark(sm, 0);
-  gemv_lds(w, sm.xc, np, c0, c1, sm);
+  Acc<2, MT> acc;
+  mfma_tiles(acc, w, A);
+  reduce_tiles(acc, sm);
   mark(sm, 1);
-  const int n = p0 * 16 + threadIdx.x;
-  if (threadIdx.x < np * 16 && n < P.E) Pub(P.rp + (size_t)ks * P.E).stf(n, sm.out[threadIdx.x]);
+  const Pub RP(P.rp);
+  for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int b = mt * 16 + m, e = (p0 + pp) * 16 + nn;
+    if (pp < np && b < P.B && e < P.E) RP.stf((ks * P.B + b) * P.E + e, sm.out[o] * sm.inv_rms[b]);
+  }
   const int old = arrive(P, t.a[5], sm);
   if (old == P.n_router_tasks - 1) {
     mark(sm, 2);
@@ -868,155 +957,176 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   }
 }
 
-// Top-k by ranking: expert i's rank is the number of experts ahead of it
-// (a larger logit, or an equal logit and a lower index); the experts ranked
-// below k are kept, in rank order. Every comparison is independent, so this
-// runs in a few hundred cycles instead of k dependent rounds of a wave argmax.
-__device__ void topk_finalize(const mk_params& P, int l, Smem& sm) {
-  const int E = P.E, K = P.K;
-  const int i = threadIdx.x;
+// Top-k by ranking: expert e's rank for token b is the number of experts
+// ahead of it (a larger logit, or an equal logit and a lower index); the
+// experts ranked below k are kept, in rank order. Every comparison is
+// independent, so this takes a few hundred cycles per token instead of k
+// dependent rounds of an argmax. Then the route: the active experts in
+// ascending order, the tokens routed to each, and the work-item counts.
+__device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm) {
+  const int E = P.E, K = P.K, B = P.B;
   const Pub R(P.rp), TI(P.tk_idx), TW(P.tk_w), RT(P.route);
-  float* lg = sm.u.tk.logit;
-  if (i < E) {
+  SmemTopk& T = sm.u.tk;
+  for (int i = threadIdx.x; i < B * E; i += MK_WG_THREADS) {
     float p[MK_MAX_RKS];
 #pragma unroll
-    for (int k = 0; k < MK_MAX_RKS; ++k) p[k] = k < P.router_ks ? R.ldf(k * E + i) : 0.f;
+    for (int k = 0; k < MK_MAX_RKS; ++k) p[k] = k < P.router_ks ? R.ldf(k * B * E + i) : 0.f;
     float v = 0.f;
 #pragma unroll
     for (int k = 0; k < MK_MAX_RKS; ++k)
       if (k < P.router_ks) v += p[k];
-    lg[i] = v;
+    T.logit[i / E][i % E] = v;
   }
   __syncthreads();
-  if (i < E) {
-    const float v = lg[i];
+  for (int i = threadIdx.x; i < B * E; i += MK_WG_THREADS) {
+    const int b = i / E, e = i % E;
+    const float v = T.logit[b][e];
     int rank = 0;
     for (int j = 0; j < E; j += 4) {
-      const float4 q = *(const float4*)(lg + j);
-      rank += (q.x > v) | ((q.x == v) & (j + 0 < i));
-      rank += (q.y > v) | ((q.y == v) & (j + 1 < i));
-      rank += (q.z > v) | ((q.z == v) & (j + 2 < i));
-      rank += (q.w > v) | ((q.w == v) & (j + 3 < i));
+      const float4 q = *(const float4*)(&T.logit[b][j]);
+      rank += (q.x > v) | ((q.x == v) & (j + 0 < e));
+      rank += (q.y > v) | ((q.y == v) & (j + 1 < e));
+      rank += (q.z > v) | ((q.z == v) & (j + 2 < e));
+      rank += (q.w > v) | ((q.w == v) & (j + 3 < e));
     }
     if (rank < K) {
-      sm.u.tk.sel_idx[rank] = i;
-      sm.u.tk.sel_val[rank] = v;
+      T.sel_idx[b][rank] = e;
+      T.sel_val[b][rank] = v;
     }
   }
   __syncthreads();
-  if (i < K) {
+  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) {
     // softmax over the kept logits (max-subtracted; rank 0 is the max),
     // summed in rank order
-    const float top = sm.u.tk.sel_val[0];
+    const int b = i / K, j = i % K;
+    const float top = T.sel_val[b][0];
     float sum = 0.f;
-    for (int j = 0; j < K; ++j) sum += __expf(sm.u.tk.sel_val[j] - top);
-    const int my_idx = sm.u.tk.sel_idx[i];
-    const float ej = __expf(sm.u.tk.sel_val[i] - top);
-    // batch 1: the k distinct experts are the active ones; queue them in
-    // ascending expert order, with the token's slot j routed to each
-    int pos = 0;
-    for (int j = 0; j < K; ++j) pos += sm.u.tk.sel_idx[j] < my_idx;
-    TI.sti(i, my_idx);
-    TW.stf(i, ej / sum);
-    RT.sti(4 + pos, my_idx);
-    RT.sti(4 + E + pos, 1);
-    RT.sti(4 + 2 * E + pos * P.B, i);
-    if (P.tk_trace) P.tk_trace[(size_t)l * K + i] = my_idx;
-    if (i == 0) {
-      RT.sti(0, K);
-      RT.sti(1, K * P.up_items_per_expert);
-      RT.sti(2, K * P.down_items_per_expert);
+    for (int jj = 0; jj < K; ++jj) sum += __expf(T.sel_val[b][jj] - top);
+    TI.sti(i, T.sel_idx[b][j]);
+    TW.stf(i, __expf(T.sel_val[b][j] - top) / sum);
+    if (P.tk_trace) P.tk_trace[((size_t)l * B + b) * K + j] = T.sel_idx[b][j];
+  }
+  // route: expert e's position among the active experts, its token count and
+  // its slots (b * k + j, ascending b: a token keeps an expert at most once)
+  if ((int)threadIdx.x < E) {
+    const int e = threadIdx.x;
+    int cnt = 0;
+    for (int b = 0; b < B; ++b)
+      for (int j = 0; j < K; ++j) cnt += T.sel_idx[b][j] == e;
+    sm.rt_cnt[e] = cnt;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < E) {
+    const int e = threadIdx.x, cnt = sm.rt_cnt[e];
+    int a = 0, n_active = 0;
+    for (int x = 0; x < E; ++x) {
+      a += (x < e) & (sm.rt_cnt[x] > 0);
+      n_active += sm.rt_cnt[x] > 0;
+    }
+    if (cnt > 0) {
+      RT.sti(4 + a, e);
+      RT.sti(4 + E + a, cnt);
+      int r = 0;
+      for (int b = 0; b < B; ++b)
+        for (int j = 0; j < K; ++j)
+          if (T.sel_idx[b][j] == e) RT.sti(4 + 2 * E + a * B + r++, b * K + j);
+    }
+    if (e == 0) {
+      RT.sti(0, n_active);
+      RT.sti(1, n_active * P.up_items_per_expert);
+      RT.sti(2, n_active * P.down_items_per_expert);
     }
   }
 }
 
-__device__ __forceinline__ int claim(const mk_params& P, int32_t c, Smem& sm) {
-  if (threadIdx.x == 0)
-    sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int id = sm.claim;
-  __syncthreads();
-  return id;
-}
-
-// Expert up/gate over one K half of one gate/up panel pair, claimed from the
-// queue ROUTER_TOPK built (megakernel post, section "Tasks":
-// MOE_UPGATE_ACT_DRAIN; the scheduler section of the Chinese version:
-// claimers take the next entry atomically until the queue is empty). The two
-// K halves' gate and up sums are added, and the SiLU-and-multiply applied,
-// by the down projection that consumes them.
 // Route entries of the layer's active experts into LDS (one round trip).
 __device__ __forceinline__ void load_route(const mk_params& P, Smem& sm) {
   const Pub R(P.route);
-  const int E = P.E;
+  const int E = P.E, B = P.B;
   const int i = threadIdx.x;
   if (i < 4) sm.rt_hdr[i] = R.ldi(i);
   if (i < E) {
     sm.rt_e[i] = R.ldi(4 + i);
-    sm.rt_slot[i] = R.ldi(4 + 2 * E + i * P.B);
+    sm.rt_cnt[i] = R.ldi(4 + E + i);
   }
+  for (int k = i; k < E * B; k += MK_WG_THREADS) sm.rt_slot[k] = R.ldi(4 + 2 * E + k);
   __syncthreads();
 }
 
-// Claim n consecutive items of a work queue: returns (block-uniform) the first.
-__device__ __forceinline__ int claim_n(const mk_params& P, int32_t c, int n, Smem& sm) {
-  if (threadIdx.x == 0)
-    sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int id = sm.claim;
-  __syncthreads();
-  return id;
-}
-
-#define MK_UP_BATCH 4  // at most this many up/gate items claimed together, their weights in flight together
-
-template <int NCH>
+// ------------------------------------------------------------------ MoE
+// Expert up/gate over one K half of one gate/up panel pair for all tokens
+// routed to the expert, claimed from the queue ROUTER_TOPK built (megakernel
+// post, section "Tasks": MOE_UPGATE_ACT_DRAIN; the scheduler section of the
+// Chinese version: claimers take the next entry atomically until the queue is
+// empty). The two K halves' gate and up sums are added, and the
+// SiLU-and-multiply applied, by the down projection that consumes them.
+// Claims take several items at a time (their weights stream together); the
+// batch size spreads the queue over the claimers expected to be free.
+template <int MT, int NCH, int NBMAX>
 __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
-  const int F = P.F, upe = P.up_items_per_expert;
+  const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
   const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
-  const Pub GU(P.gu);
+  const Pub GU(P.gu), U(u_of(P, l));
   load_route(P, sm);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
-  // batch size: the queue spread over the claimers expected to be free
-  const int nb = min(MK_UP_BATCH, max(1, (n_items + t.a[2] - 1) / t.a[2]));
+  const int nb = min(NBMAX, max(1, (n_items + t.a[2] - 1) / t.a[2]));
   int id0 = claim_n(P, claim_ctr, nb, sm);
-  load_xhat(P, l, sm);
+  load_inv_rms(P, l, sm);
   mark(sm, 0);
   bool first = true;
   while (id0 < n_items) {
     if (ld_relaxed(&P.err[0]) != 0) return;
-    WTile<2, NCH> w[MK_UP_BATCH];
+    // row offsets of each item's tokens
+    for (int i = threadIdx.x; i < NBMAX * MK_MAX_BATCH; i += MK_WG_THREADS) {
+      const int k = i / MK_MAX_BATCH, r = i % MK_MAX_BATCH, id = id0 + k;
+      int off = -1;
+      if (k < nb && id < n_items) {
+        const int a = id / upe;
+        if (r < sm.rt_cnt[a]) off = (sm.rt_slot[a * B + r] / K) * P.H;
+      }
+      sm.row_off[k][r] = off;
+    }
+    __syncthreads();
+    WTile<2, NCH> w[NBMAX];
+    ATile<MT, NCH> A[NBMAX];
 #pragma unroll
-    for (int k = 0; k < MK_UP_BATCH; ++k) {
+    for (int k = 0; k < NBMAX; ++k) {
       const int id = id0 + k;
-      const int a = id / upe, r = id % upe;
+      const bool valid = k < nb && id < n_items;
+      const int a = valid ? id / upe : 0, r = id % upe;
       const int tt = r >> 1, kh = r & 1;
-      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[min(a, P.E - 1)]);
+      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[min(a, E - 1)]);
       const int c0 = kh * kh_chunks;
       // an item past the queue's end loads nothing (np = 0: a zero tile)
       wtile_load(w[k], P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
-                 (k < nb && id < n_items) ? 2 : 0, c0, c0 + kh_chunks);
+                 valid ? 2 : 0, c0, c0 + kh_chunks);
+      atile_load_bf16(A[k], U, sm.row_off[k], valid ? c0 : 0, valid ? c0 + kh_chunks : 0);
     }
     mark(sm, 1);
     // the next claim travels while the weights stream
     const int next = claim_n(P, claim_ctr, nb, sm);
 #pragma unroll
-    for (int k = 0; k < MK_UP_BATCH; ++k) {
+    for (int k = 0; k < NBMAX; ++k) {
       const int id = id0 + k;
       if (k >= nb || id >= n_items) break;
       const int a = id / upe, r = id % upe;
       const int tt = r >> 1, kh = r & 1;
-      const int c0 = kh * kh_chunks;
-      const int slot = __builtin_amdgcn_readfirstlane(sm.rt_slot[a]);
-      gemv_lds(w[k], sm.xc, 2, c0, c0 + kh_chunks, sm);
+      const int cnt = sm.rt_cnt[a];
+      Acc<2, MT> acc;
+      mfma_tiles(acc, w[k], A[k]);
+      reduce_tiles(acc, sm);
       if (k == 0 && first) mark(sm, 2);
       // gu[slot][kh][gate|up][F]
-      if (threadIdx.x < 32) {
-        const int which = threadIdx.x >> 4, col = tt * 16 + (threadIdx.x & 15);
-        GU.stf(((slot * 2 + kh) * 2 + which) * F + col, sm.out[threadIdx.x]);
+      for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
+        const int which = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+        const int row = mt * 16 + m;
+        if (row < cnt) {
+          const int slot = sm.rt_slot[a * B + row];
+          GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, sm.out[o] * sm.inv_rms[slot / K]);
+        }
       }
     }
     // one drain for the batch, then each item's arrival on its expert's counter
@@ -1030,74 +1140,168 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
   }
 }
 
-// Expert down over one column block, claiming (expert, block) items. Its
-// weights stream before waiting for that expert's up/gate items (megakernel
-// post, section "What we have done differently": MoE down streams weights
-// while up/gate still computes the hidden state it consumes).
-template <int NCH>
+// Expert down over one column block for all tokens routed to the expert,
+// claiming (expert, block) items. Its weights stream before waiting for that
+// expert's up/gate items (megakernel post, section "What we have done
+// differently": MoE down streams weights while up/gate still computes the
+// hidden state it consumes).
+template <int MT, int NCH>
 __device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], blk_base = t.a[2];
-  const int E = P.E, F = P.F, H = P.H;
+  const int F = P.F, H = P.H, B = P.B;
   const int kc = F / 32;
   const size_t pstride = (size_t)kc * 512;
   const int DP = P.CB / 16;
   const Pub DN(P.dn), GU(P.gu);
-  int id = claim(P, claim_ctr, sm);
+  int id = claim_n(P, claim_ctr, 1, sm);
   load_route(P, sm);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
   while (id < n_items) {
     if (ld_relaxed(&P.err[0]) != 0) return;
     const int a = id / P.down_items_per_expert, cb = id % P.down_items_per_expert;
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    const int cnt = sm.rt_cnt[a];
     WTile<4, NCH> w;
     wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride, pstride, DP, 0, kc);
     // the next claim travels while the weights stream
-    const int next = claim(P, claim_ctr, sm);
+    const int next = claim_n(P, claim_ctr, 1, sm);
     if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
-    const int slot = __builtin_amdgcn_readfirstlane(sm.rt_slot[a]);
-    // u = silu(g0 + g1) * (u0 + u1) over F, staged in LDS
-    float* us = sm.us;
+    // act = silu(g0 + g1) * (u0 + u1) per routed row, bf16 in LDS
+    const int n = MT * 16 * F;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
+      float g[4][4];
 #pragma unroll
-    for (int k = threadIdx.x; k < MK_MAX_F; k += MK_WG_THREADS) {
-      if (k >= F) break;
-      const float g0 = GU.ldf(((slot * 2 + 0) * 2 + 0) * F + k), g1 = GU.ldf(((slot * 2 + 1) * 2 + 0) * F + k);
-      const float u0 = GU.ldf(((slot * 2 + 0) * 2 + 1) * F + k), u1 = GU.ldf(((slot * 2 + 1) * 2 + 1) * F + k);
-      const float gt = g0 + g1;
-      us[k] = gt / (1.0f + __expf(-gt)) * (u0 + u1);
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * MK_WG_THREADS, row = i / F, f = i % F;
+        const bool live = i < n && row < cnt;
+        const int slot = live ? sm.rt_slot[a * B + row] : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * MK_WG_THREADS;
+        if (i < n) {
+          const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
+          sm.act[i] = (uint16_t)f2bf(gt / (1.0f + __expf(-gt)) * ut);
+        }
+      }
     }
     __syncthreads();
-    gemv_lds(w, us, DP, 0, kc, sm);
-    if (threadIdx.x < DP * 16) DN.stf(slot * H + cb * DP * 16 + threadIdx.x, sm.out[threadIdx.x]);
+    ATile<MT, NCH> A;
+    {
+      const int wv = wave_id(), ln = lane_id();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = wv + MK_WAVES * i;
+          A.a[mt][i] = c < kc ? *(const u32x4_t*)(sm.act + (mt * 16 + (ln & 15)) * F + 32 * c + 8 * (ln >> 4))
+                              : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    Acc<4, MT> acc;
+    mfma_tiles(acc, w, A);
+    reduce_tiles(acc, sm);
+    for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
+      const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+      const int row = mt * 16 + m;
+      if (pp < DP && row < cnt) DN.stf(sm.rt_slot[a * B + row] * H + (cb * DP + pp) * 16 + nn, sm.out[o]);
+    }
     block_arrive(P, t, blk_base, cb, sm);
     id = next;
   }
 }
 
 // ----------------------------------------------------------------- LM head
-// LM head panels with each task's argmax candidate; the task that completes
-// the head picks the greedy token: the largest logit, the lowest index on
-// ties (tiny-vllm walkthrough, section "The remaining layers and logits").
-__device__ void final_argmax(const mk_params& P, Smem& sm);
+// LM head over a range of panels, two at a time with the next pair's weights
+// streaming while the current pair computes; each task keeps every token's
+// best logit (the lowest index on ties) and the task that completes the head
+// picks the greedy tokens (tiny-vllm walkthrough, section "The remaining
+// layers and logits": replace the running best only on a strictly greater
+// value).
+__device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm);
 
-template <int NCH>
+template <int NP, int MT, int NCH>
+__device__ __forceinline__ void lm_pair(const mk_params& P, const WTile<NP, NCH>& w, const ATile<MT, NCH>& A, int p,
+                                        int np, float& bv, int& bi, Smem& sm) {
+  Acc<NP, MT> acc;
+  mfma_tiles(acc, w, A);
+  reduce_tiles(acc, sm);
+  for (int o = threadIdx.x; o < NP * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int b = mt * 16 + m;
+    if (pp < np && b < P.B) P.logits[(size_t)b * P.V + (p + pp) * 16 + nn] = sm.out[o] * sm.inv_rms[b];
+  }
+  if ((int)threadIdx.x < P.B) {
+    const int b = threadIdx.x, mt = b / 16, m = b % 16;
+    const float inv = sm.inv_rms[b];
+    for (int pp = 0; pp < np; ++pp)
+      for (int nn = 0; nn < 16; ++nn) {
+        const float v = sm.out[(pp * MT + mt) * 256 + m * 16 + nn] * inv;
+        if (v > bv) {
+          bv = v;
+          bi = (p + pp) * 16 + nn;
+        }
+      }
+  }
+  __syncthreads();
+}
+
+// NP panels per step (two steps' weights in registers at a time).
+template <int MT, int NCH, int NP>
 __device__ __forceinline__ void op_lmhead(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int p0 = t.a[0], np = t.a[1], ord = t.a[2];
+  const int p0 = t.a[0], p1 = t.a[1], ord = t.a[2];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
-  WTile<2, NCH> w;
-  wtile_load(w, P.wlm + (size_t)p0 * pstride, pstride, np, 0, kc);
+  const int L = P.L;
+  WTile<NP, NCH> w0, w1;
+  wtile_load(w0, P.wlm + (size_t)p0 * pstride, pstride, min(NP, p1 - p0), 0, kc);
   if (!wait_task(P, t, sm)) return;
-  load_xhat(P, P.L, sm);
-  gemv_lds(w, sm.xc, np, 0, kc, sm);
-  if (wave_id() == 0) {
-    const int tid = threadIdx.x;
+  set_rows_batch(P, sm, 0, P.H, 0);
+  __syncthreads();
+  ATile<MT, NCH> A;
+  atile_load_bf16(A, Pub(u_of(P, L)), sm.row_off[0], 0, kc);
+  load_inv_rms(P, L, sm);
+  float bv = kNegInf;
+  int bi = 0x7fffffff;
+  for (int p = p0; p < p1; p += 2 * NP) {
+    if (p + NP < p1) wtile_load(w1, P.wlm + (size_t)(p + NP) * pstride, pstride, min(NP, p1 - p - NP), 0, kc);
+    lm_pair(P, w0, A, p, min(NP, p1 - p), bv, bi, sm);
+    if (p + NP >= p1) break;
+    if (p + 2 * NP < p1) wtile_load(w0, P.wlm + (size_t)(p + 2 * NP) * pstride, pstride, min(NP, p1 - p - 2 * NP), 0, kc);
+    lm_pair(P, w1, A, p + NP, min(NP, p1 - p - NP), bv, bi, sm);
+  }
+  if ((int)threadIdx.x < P.B) {
+    Pub(P.lm_val).stf(threadIdx.x * P.n_lm_tasks + ord, bv);
+    Pub(P.lm_arg).sti(threadIdx.x * P.n_lm_tasks + ord, bi);
+  }
+  const int old = arrive(P, t.a[3], sm);
+  if (old == P.n_lm_tasks - 1) final_argmax(P, sm);
+}
+
+// Greedy token of every sequence from the LM-head tasks' candidates; with
+// MK_STEP_ADVANCE the token becomes the next step's input and the length grows.
+__device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm) {
+  const int n = P.n_lm_tasks;
+  const Pub LV(P.lm_val), LA(P.lm_arg);
+  const int wv = wave_id(), ln = lane_id();
+  for (int b = wv; b < P.B; b += MK_WAVES) {
     float v = kNegInf;
     int ix = 0x7fffffff;
-    if (tid < np * 16) {
-      v = sm.out[tid];
-      ix = p0 * 16 + tid;
-      P.logits[ix] = v;
+    for (int base = 0; base < n; base += 4 * 64) {
+      float cv[4];
+      int ci[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * 64 + ln;
+        cv[u] = i < n ? LV.ldf(b * n + i) : kNegInf;
+        ci[u] = i < n ? LA.ldi(b * n + i) : 0x7fffffff;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (cv[u] > v || (cv[u] == v && ci[u] < ix)) { v = cv[u]; ix = ci[u]; }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -1105,70 +1309,31 @@ __device__ __forceinline__ void op_lmhead(const mk_params& P, const mk_task& t, 
       const int oi = __shfl_xor(ix, o);
       if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
     }
-    if (tid == 0) {
-      Pub(P.lm_val).stf(ord, v);
-      Pub(P.lm_arg).sti(ord, ix);
-    }
-  }
-  const int old = arrive(P, t.a[3], sm);
-  if (old == P.n_lm_tasks - 1) final_argmax(P, sm);
-}
-
-__device__ void final_argmax(const mk_params& P, Smem& sm) {
-  const int n = P.n_lm_tasks;
-  const Pub LV(P.lm_val), LA(P.lm_arg);
-  float v = kNegInf;
-  int ix = 0x7fffffff;
-  constexpr int U = 8;  // candidates per thread in flight together
-  for (int base = 0; base < n; base += U * MK_WG_THREADS) {
-    float cv[U];
-    int ci[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * MK_WG_THREADS + threadIdx.x;
-      cv[u] = i < n ? LV.ldf(i) : kNegInf;
-      ci[u] = i < n ? LA.ldi(i) : 0x7fffffff;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (cv[u] > v || (cv[u] == v && ci[u] < ix)) { v = cv[u]; ix = ci[u]; }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(ix, o);
-    if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
-  }
-  if (lane_id() == 0) {
-    sm.vred[wave_id()] = v;
-    sm.ired[wave_id()] = ix;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 0; k < MK_WAVES; ++k)
-      if (sm.vred[k] > v || (sm.vred[k] == v && sm.ired[k] < ix)) { v = sm.vred[k]; ix = sm.ired[k]; }
-    if (P.next_tokens) P.next_tokens[0] = ix;
-    if (P.flags & 1u) {
-      P.tokens[0] = ix;
-      P.seq_lens[0] = P.seq_lens[0] + 1;
+    if (ln == 0) {
+      if (P.next_tokens) P.next_tokens[b] = ix;
+      if (P.flags & 1u) {
+        P.tokens[b] = ix;
+        P.seq_lens[b] = P.seq_lens[b] + 1;
+      }
     }
   }
 }
 
 // --------------------------------------------------------------- dispatch
 
-template <int D>
-__device__ __forceinline__ void run_task(const mk_params& P, const mk_task& t, Smem& sm) {
+template <int D, int MT>
+__device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t, Smem& sm) {
   switch (t.op) {
     // chunks per wave: K / 32 / MK_WAVES for the largest K of each op
     // (hidden 2048, group width 1024, K half 1024, expert width 768)
-    case MK_OP_QKV: op_qkv<64 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_EMBED: op_embed(P, t, sm); break;
+    case MK_OP_QKV: op_qkv<MT, 64 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
-    case MK_OP_OPROJ: op_oproj<32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_ROUTER: op_router<32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe_up<32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_MOE_DOWN: op_moe_down<24 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_LMHEAD: op_lmhead<64 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe_up<MT, 32 / MK_WAVES, MT == 1 ? 3 : 2>(P, t, sm); break;
+    case MK_OP_MOE_DOWN: op_moe_down<MT, 24 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, 1>(P, t, sm); break;
     default: wait_task(P, t, sm); break;
   }
 }
@@ -1176,14 +1341,12 @@ __device__ __forceinline__ void run_task(const mk_params& P, const mk_task& t, S
 }  // namespace
 
 // The interpreter: workgroup i runs tasks [task_off[i], task_off[i+1]).
-template <int D>
+// MT: row tiles of 16 tokens (1 for batch <= 16, 2 for batch <= 32).
+template <int D, int MT>
 __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_params Pk) {
   __shared__ Smem sm;
   const mk_params& P = Pk;
-  if (threadIdx.x == 0) {
-    sm.xc_layer = -1;
-    sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
-  }
+  if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
   if (P.ctr_clear) {
     for (int i = blockIdx.x * MK_WG_THREADS + threadIdx.x; i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
       P.ctr_clear[i] = 0u;
@@ -1194,11 +1357,22 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
     const mk_task& t = P.tasks[i];
     const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
     if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
-    run_task<D>(P, t, sm);
+    // The parameter block through an opaque copy of its (constant address
+    // space) pointer per task: parameter fields are then loaded inside each op
+    // with scalar loads instead of being hoisted out of the task loop and held
+    // in registers across every op.
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef const __attribute__((address_space(4))) mk_params* kparams_ptr;
+    kparams_ptr Pt = (kparams_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(Pt));
+    run_task_mt<D, MT>(*(const mk_params*)Pt, t, sm);
+#else
+    run_task_mt<D, MT>(P, t, sm);
+#endif
     __syncthreads();
     if (P.trace && threadIdx.x == 0) {
       // per-task timestamps (100 MHz device clock): start, waits satisfied,
-      // inputs ready, computed, end
+      // op-defined marks, end
       uint32_t* rec = P.trace + (size_t)(P.trace_base + i) * 8;
       rec[0] = (uint32_t)t.op | ((uint32_t)t.layer << 8) | ((uint32_t)blockIdx.x << 16);
       rec[1] = t0;
@@ -1212,8 +1386,10 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
   }
 }
 
-template __global__ void mk_interp<64>(mk_params);
-template __global__ void mk_interp<128>(mk_params);
+template __global__ void mk_interp<64, 1>(mk_params);
+template __global__ void mk_interp<64, 2>(mk_params);
+template __global__ void mk_interp<128, 1>(mk_params);
+template __global__ void mk_interp<128, 2>(mk_params);
 
 // ------------------------------------------------------------- repacking
 // Canonical row-major [K x N] (leading dimension ld) -> panel-tiled layout,
@@ -1250,8 +1426,13 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_panels(const uint16_
 // ------------------------------------------------------------ host launch
 #include "mk_launch.h"
 
+static const void* interp_fn(int head_dim, int mt) {
+  if (head_dim == 64) return mt == 1 ? (const void*)mk_interp<64, 1> : (const void*)mk_interp<64, 2>;
+  return mt == 1 ? (const void*)mk_interp<128, 1> : (const void*)mk_interp<128, 2>;
+}
+
 hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool cooperative, hipStream_t stream) {
-  const void* fn = head_dim == 64 ? (const void*)mk_interp<64> : (const void*)mk_interp<128>;
+  const void* fn = interp_fn(head_dim, P.B > 16 ? 2 : 1);
   void* args[] = {(void*)&P};
   if (cooperative)
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(MK_WG_THREADS), args, 0, stream);
@@ -1266,7 +1447,13 @@ hipError_t mk_launch_repack(const uint16_t* src, uint16_t* dst, int K, int N, in
   return hipGetLastError();
 }
 
+// Resident workgroups per compute unit of the interpreter (the smaller of the
+// two row-tile variants).
 hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu) {
-  const void* fn = head_dim == 64 ? (const void*)mk_interp<64> : (const void*)mk_interp<128>;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, MK_WG_THREADS, 0);
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, interp_fn(head_dim, 1), MK_WG_THREADS, 0);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, interp_fn(head_dim, 2), MK_WG_THREADS, 0);
+  *blocks_per_cu = a < b ? a : b;
+  return e;
 }

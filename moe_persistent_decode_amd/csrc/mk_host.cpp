@@ -109,7 +109,9 @@ struct mk_handle {
   float* rope = nullptr;
   uint16_t* kv = nullptr;
   void* scratch = nullptr;
-  float *h = nullptr, *q = nullptr, *part = nullptr, *o = nullptr, *ao = nullptr, *ssq = nullptr, *rp = nullptr,
+  uint16_t* u = nullptr;
+  uint16_t* o = nullptr;
+  float *h = nullptr, *q = nullptr, *part = nullptr, *ao = nullptr, *ssq = nullptr, *rp = nullptr,
         *tk_w = nullptr, *gu = nullptr, *dn = nullptr, *lm_val = nullptr;
   int32_t *tk_idx = nullptr, *route = nullptr, *lm_arg = nullptr;
   uint32_t* ctr[2] = {nullptr, nullptr};
@@ -192,13 +194,14 @@ void derive(mk_handle* h) {
   h->kv_dim = c.n_kv_heads * c.head_dim;
   h->qkv_dim = h->q_dim + 2 * h->kv_dim;
   h->e_pad = ceil_div(c.n_experts, 16) * 16;  // router columns padded to whole panels
-  // attention: 16 pages per split, more when a context would need more
-  // than MK_MAX_SPLITS splits (the combine keeps one factor per split in LDS)
+  // attention: at least 16 pages per split, more when a context would need
+  // more than MK_MAX_SPLITS splits (the combine keeps one factor per split in LDS)
   const int pages = ceil_div(c.max_seq_len, c.page_size) + 1;
   h->pps = std::max(16, ceil_div(pages, 256));
   h->max_splits = ceil_div(pages, h->pps);
   h->lm_np = 2;
-  h->n_lm_tasks = ceil_div(c.vocab / 16, h->lm_np);
+  // LM head: one task per workgroup (fewer for a small vocabulary)
+  h->n_lm_tasks = std::min(h->n_workers > 0 ? h->n_workers : 1, ceil_div(c.vocab / 16, 2));
   // residual column blocks of 64 columns (4 panels) when the width allows
   h->CB = c.hidden >= 1024 ? 64 : 32;
   h->NB = c.hidden / h->CB;
@@ -213,12 +216,21 @@ int window_of(const mk_config& c, int l) {
   return (l % c.full_every) == c.full_every - 1 ? 0 : c.window;
 }
 
+// Pages per attention split for a batch of B sequences up to `len` long:
+// about two tasks per workgroup over a layer's (sequence, group) pairs, at
+// least 16 pages each.
+int pps_for(const mk_handle* h, int B, int len) {
+  const int pages = ceil_div(len, h->cfg.page_size) + 1;
+  const int target = std::max(1, 2 * h->n_workers / (B * h->cfg.n_kv_heads));
+  return std::max(h->pps, ceil_div(pages, target));
+}
+
 // Number of attention splits for a layer when sequences are at most `len` long.
-int splits_for(const mk_handle* h, int l, int len) {
+int splits_for(const mk_handle* h, int l, int len, int pps) {
   const int win = window_of(h->cfg, l);
   const int keys = win ? std::min(win, len) : len;
   const int pages = ceil_div(keys, h->cfg.page_size) + 1;  // a window may straddle one extra page
-  return std::min(ceil_div(pages, h->pps), h->max_splits);
+  return std::min(ceil_div(pages, pps), h->max_splits);
 }
 
 int bucket_of(int hint) { return ceil_div(hint, 256) * 256; }
@@ -228,21 +240,22 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   auto S = std::make_unique<Schedule>();
   S->B = B;
   S->bucket = std::min(bucket_of(hint), c.max_seq_len);
-  S->pps = h->pps;
+  S->pps = pps_for(h, B, S->bucket);
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
   const int n_w = h->n_workers, NB = h->NB;
   const int kc = c.hidden / 32;
 
-  // counter layout: resid_done[l] for l = 1..L (index l - 1), lm, then per layer
+  // counter layout: resid_done[l] for l = 0..L (input of layer l complete;
+  // L: the LM head's input), lm, then per layer
   int idx = 0;
   S->c_resid0 = idx;
-  idx += L;
+  idx += L + 1;
   S->c_lm = idx++;
   S->c_layer0 = idx;
   S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + E + NB;
   idx += L * S->c_per_layer;
   S->n_ctr = idx;
-  auto resid = [&](int l) { return S->c_resid0 + l - 1; };  // input of layer l ready (l >= 1)
+  auto resid = [&](int l) { return S->c_resid0 + l; };  // input of layer l ready
   auto ci = [&](int l) {
     CtrIdx x;
     int b0 = S->c_layer0 + l * S->c_per_layer;
@@ -274,11 +287,18 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   const int qkv_np = 2;
   S->n_qkv.assign(KVH, 0);
 
+  // layer 0's input: embedding rows per column block
+  begin_wave();
+  for (int cb = 0; cb < NB; ++cb) {
+    mk_task t = make_task(MK_OP_EMBED, 0);
+    t.a[0] = cb;
+    t.sig_ctr[0] = resid(0);
+    push(t);
+  }
+
   for (int l = 0; l < L; ++l) {
     const CtrIdx x = ci(l);
-    auto wait_input = [&](mk_task& t) {
-      if (l > 0) add_wait(t, resid(l), NB);
-    };
+    auto wait_input = [&](mk_task& t) { add_wait(t, resid(l), NB); };
     // router over K splits; the last one does top-k and route finalize
     begin_wave();
     const int rpanels = h->e_pad / 16;
@@ -319,7 +339,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     }
     // attention splits; the last split of a (sequence, group) combines
     begin_wave();
-    const int ns = splits_for(h, l, S->bucket);
+    const int ns = splits_for(h, l, S->bucket, S->pps);
     if (window_of(c, l))
       S->n_splits_win = ns;
     else
@@ -332,7 +352,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           t.a[1] = g;
           t.a[2] = s;
           t.a[3] = ns;
-          t.a[4] = h->pps;
+          t.a[4] = S->pps;
           t.a[5] = x.attn + b * KVH + g;
           add_wait(t, x.qkv + g, S->n_qkv[g]);
           t.sig_ctr[0] = x.comb + g;
@@ -378,18 +398,20 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       }
     S->n_oproj = n_oproj;
   }
-  // LM head; the last task picks the greedy token
+  // LM head: contiguous panel ranges (whole pairs); the last task picks the
+  // greedy tokens
   begin_wave();
-  S->n_lm = 0;
-  for (int p = 0, ord = 0; p < c.vocab / 16; p += h->lm_np, ++ord) {
+  const int n_panels = c.vocab / 16, n_pairs = ceil_div(n_panels, 2);
+  S->n_lm = h->n_lm_tasks;
+  for (int i = 0; i < S->n_lm; ++i) {
+    const int pa = (int)((int64_t)i * n_pairs / S->n_lm), pb = (int)((int64_t)(i + 1) * n_pairs / S->n_lm);
     mk_task t = make_task(MK_OP_LMHEAD, L);
-    t.a[0] = p;
-    t.a[1] = std::min(h->lm_np, c.vocab / 16 - p);
-    t.a[2] = ord;
+    t.a[0] = 2 * pa;
+    t.a[1] = std::min(2 * pb, n_panels);
+    t.a[2] = i;
     t.a[3] = S->c_lm;
     add_wait(t, resid(L), NB);
     push(t);
-    ++S->n_lm;
   }
 
   // round-robin placement of the flattened list over the resident workgroups
@@ -458,6 +480,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       if (!u.in_claimer) {
         if (!waits_met(t)) continue;
         switch (t.op) {
+          case MK_OP_EMBED:
           case MK_OP_QKV:
             ctr[t.sig_ctr[0]]++;
             done();
@@ -528,7 +551,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   // every counter against the arrivals it must receive
   const int B = S.B;
   std::vector<int64_t> want(S.n_ctr, 0);
-  for (int l = 1; l <= L; ++l) want[S.c_resid0 + l - 1] = NB;
+  for (int l = 0; l <= L; ++l) want[S.c_resid0 + l] = NB;
   want[S.c_lm] = S.n_lm;
   for (int l = 0; l < L; ++l) {
     const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
@@ -640,7 +663,6 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   auto h = std::make_unique<mk_handle>();
   h->cfg = c;
   h->device = device;
-  derive(h.get());
   if (hipSetDevice(device) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "hipSetDevice failed");
   int n_cu = 0;
   if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n_cu < 1)
@@ -651,6 +673,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
                 MK_WGS_PER_CU);
   h->n_cu = std::min(n_cu, MK_MAX_CUS);
   h->n_workers = h->n_cu * MK_WGS_PER_CU;
+  derive(h.get());
   if (const char* e = std::getenv("MK_TIMEOUT_MS")) h->timeout_ticks = (int64_t)std::atoll(e) * 100000;
 
   const int L = c.n_layers, H = c.hidden, E = c.n_experts, F = c.expert_ffn, V = c.vocab;
@@ -708,7 +731,8 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     so += align_up(bytes, 256);
     return o;
   };
-  const size_t s_h = stake((size_t)Bm * H * 4), s_ssq = stake((size_t)Bm * h->NB * 4);
+  const size_t s_h = stake((size_t)Bm * H * 4), s_ssq = stake((size_t)2 * Bm * h->NB * 4);
+  const size_t s_u = stake((size_t)2 * Bm * H * 2);
   const size_t s_q = stake((size_t)Bm * h->q_dim * 4), s_o = stake((size_t)Bm * h->q_dim * 4);
   const size_t s_part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
   const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_rp = stake((size_t)h->router_ks * Bm * E * 4);
@@ -721,9 +745,10 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   hipMemset(h->scratch, 0, so);
   char* sb = (char*)h->scratch;
   h->h = (float*)(sb + s_h);
+  h->u = (uint16_t*)(sb + s_u);
   h->ssq = (float*)(sb + s_ssq);
   h->q = (float*)(sb + s_q);
-  h->o = (float*)(sb + s_o);
+  h->o = (uint16_t*)(sb + s_o);
   h->part = (float*)(sb + s_part);
   h->ao = (float*)(sb + s_ao);
   h->rp = (float*)(sb + s_rp);
@@ -888,6 +913,7 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.next_tokens = next_tokens;
   P.flags = flags;
   P.h = h->h;
+  P.u = h->u;
   P.ssq = h->ssq;
   P.q = h->q;
   P.part = h->part;
@@ -914,7 +940,6 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
   if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
   const mk_config& c = h->cfg;
   if (batch < 1 || batch > c.max_batch) return fail(h, MK_ERR_INVALID_ARG, "batch %d not in [1, %d]", batch, c.max_batch);
-  if (batch != 1) return fail(h, MK_ERR_UNSUPPORTED, "this build decodes batch 1 only");
   if (!tokens || !block_tables || !seq_lens || !logits)
     return fail(h, MK_ERR_INVALID_ARG, "null tokens/block_tables/seq_lens/logits");
   if (max_seq_len_hint < 1 || max_seq_len_hint > c.max_seq_len)
@@ -1007,9 +1032,10 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
   struct Item { const char* n; const void* p; size_t sz; };
   const Item items[] = {
       {"h", h->h, Bm * H * 4},
-      {"ssq", h->ssq, Bm * h->NB * 4},
+      {"ssq", h->ssq, 2 * Bm * h->NB * 4},
+      {"u", h->u, 2 * Bm * H * 2},
       {"q", h->q, Bm * h->q_dim * 4},
-      {"o", h->o, Bm * h->q_dim * 4},
+      {"o", h->o, Bm * h->q_dim * 2},
       {"ao", h->ao, (size_t)c.n_kv_heads * Bm * H * 4},
       {"rp", h->rp, (size_t)h->router_ks * Bm * E * 4},
       {"tk_idx", h->tk_idx, Bm * K * 4},

@@ -19,18 +19,23 @@
 #define MK_WGS_PER_CU 1
 #define MK_MAX_CUS 1024
 #define MK_MAX_TOPK 8
-#define MK_MAX_KVH 16   // kv heads (n_q_heads <= 256 with groups <= 16)
+#define MK_MAX_KVH 8    // kv heads
 #define MK_MAX_RKS 4    // router K splits
 #define MK_MAX_F 768    // expert width
+#define MK_MAX_BATCH 32 // sequences per step (two row tiles of 16)
+#define MK_UP_BATCH_MAX 4  // expert up/gate items claimed together
 #define MK_TASK_INTS 32
 
 // Opcodes. The post names sixteen opcodes for its model family; this model
 // (no dense FFN) uses the ones below. MOE_GATHER is folded into the expert
 // up/gate task (it reads the routed token rows directly), MOE_COMBINE into
-// the residual + RMSNorm task (it sums each token's k expert outputs in rank
-// order while forming the residual), ROUTE_FINALIZE into ROUTER_TOPK.
+// the residual + RMSNorm step (it sums each token's k expert outputs in rank
+// order while forming the residual), ROUTER_TOPK and ROUTE_FINALIZE into the
+// last router task, ATTN_COMBINE into the last attention split, and the
+// residual + RMSNorm itself into the last contribution to each column block.
 enum mk_opcode : int32_t {
   MK_OP_NOP = 0,
+  MK_OP_EMBED = 1,        // embedding rows of one column block: layer 0's input
   MK_OP_QKV = 2,          // QKV panels + RoPE + paged KV append
   MK_OP_ATTN = 3,         // split-KV partial attention (+ combine when last)
   MK_OP_OPROJ = 5,        // O projection, split-K by kv group, one column block (+ residual when last)
@@ -52,7 +57,7 @@ struct mk_task {
 };
 static_assert(sizeof(mk_task) == MK_TASK_INTS * 4, "descriptor is 32 int32");
 
-// Route scratch (int32), rebuilt per layer by MK_OP_TOPK:
+// Route scratch (int32), rebuilt per layer by the last router task:
 //   [0] n_active experts, [1] n_up_items, [2] n_down_items, [3] unused
 //   [4 .. 4+E)           active expert ids, ascending
 //   [4+E .. 4+2E)        tokens routed to each active expert
@@ -74,7 +79,7 @@ struct mk_params {
   int32_t CB, NB;                // residual column block width (multiple of 16, <= 64) and count H / CB
   int32_t n_router_tasks, router_ks; // router tasks, and the K splits among them
   int32_t max_splits;            // attention partial slots per (sequence, group)
-  int32_t n_lm_tasks;
+  int32_t n_lm_tasks;            // LM-head tasks (argmax candidates per sequence)
   int32_t e_pad;                 // router columns, padded to a multiple of 16
   // packed weights (bf16 bit patterns)
   const uint16_t* emb;           // [V][H] row-major
@@ -96,12 +101,12 @@ struct mk_params {
   uint32_t flags;
   // scratch
   float* h;      // [B][H] residual stream
-  float* xn;     // [B][H] normalised input of the current layer
+  uint16_t* u;   // [2][B][H] layer input bf16(h * gamma_l), buffer l % 2
   float* q;      // [B][QH*D] rotated queries
   float* part;   // [B][KVH][max_splits][G*D + 2G] attention partials (o, m, l)
-  float* o;      // [B][QH*D] attention output
+  uint16_t* o;   // [B][QH*D] attention output (bf16)
   float* ao;     // [KVH][B][H] O projection partials per kv group
-  float* ssq;    // [B][NB] per column block sum of squares of the residual stream
+  float* ssq;    // [2][B][NB] per column block sums of squares of layer l's input, buffer l % 2
   float* rp;     // [router_ks][B][E] router logit partials
   int32_t* tk_idx; float* tk_w;  // [B][K]
   int32_t* tk_trace;             // optional [L][B][K] record of every layer's routing
@@ -117,7 +122,8 @@ struct mk_params {
   const mk_task* tasks;
   const int32_t* task_off;   // per workgroup [off[wg], off[wg+1])
   int32_t waits_enabled;     // 0 in kernel-per-op mode (stream order is the dependency)
-  uint32_t* trace;           // optional per-task record: {op | layer << 8, t_start, t_waited, t_end}
+  uint32_t* trace;           // optional per-task record (8 words): op | layer << 8 | workgroup << 16,
+                             // start, waits satisfied, mark 0, mark 1, end, mark 2, mark 3
   int32_t trace_base;        // index of this launch's first task in the trace
   int64_t timeout_ticks;     // wait time limit in s_memrealtime ticks (100 MHz)
 };

@@ -17,7 +17,11 @@ from tests.harness import bits_to_torch, logits_close, make_decoder, say
 pytestmark = pytest.mark.gpu
 
 
-def _close(name, got, ref, rtol=2e-2, atol_frac=2e-3):
+# The projections run on the matrix cores with bf16 operands (the layer input,
+# the attention output and the expert hidden state are rounded to bf16, a
+# relative error of 2^-9 each), so a stage may differ from the float32
+# oracle by a few tenths of a percent of its scale.
+def _close(name, got, ref, rtol=2e-2, atol_frac=1e-2):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     scale = max(np.abs(ref).max(), 1e-30)
@@ -53,7 +57,8 @@ def test_one_layer_stages_tiny(mode):
     dec.sync()
     H, QD, KVH, K = model.hidden, model.q_dim, model.n_kv_heads, model.top_k
     _close("q", dec.debug_read("q", (1, QD)), tr.q_rot[0].reshape(1, QD))
-    _close("attn o", dec.debug_read("o", (1, QD)), tr.attn_out[0])
+    # the attention output is kept in bf16 (the O projection's operand)
+    _close("attn o", od.bf16_to_float(dec.debug_read("o", (1, QD), "uint16")), tr.attn_out[0])
     ao = dec.debug_read("ao", (KVH, 1, H))
     _close("o-proj", ao.sum(0), tr.attn_proj[0])
     # router partial sums over K halves (hidden < 1024) or quarters

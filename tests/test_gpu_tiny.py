@@ -4,7 +4,7 @@ Case: the recorded seed's weights, a 128-token context of uniform random
 tokens whose KV the oracle builds, then 16 greedy steps. Every step's logits
 must be within 3e-2 (max abs) and 1e-2 (relative L2) of the oracle's, every
 greedy token and every layer's top-k expert set identical, and the appended
-K/V within bf16 rounding of the oracle's.
+K/V within the bf16 operand rounding of the oracle's.
 """
 import numpy as np
 import pytest
@@ -34,22 +34,19 @@ def _gpu_weights(tc):
 
 
 def _check_kv(gpu_pool: np.ndarray, ref_pool: np.ndarray):
-    """Layer 0's cache holds bf16 roundings of fp32 values that differ only by
-    accumulation order (~1e-6 relative): equal or one bf16 step apart. Later
-    layers' K/V come from activations that already carry the attention's bf16
-    operand rounding (~2e-3 relative): within 1% of the layer's largest value."""
+    """The appended K/V are bf16 roundings of projections whose operands the
+    GPU rounds to bf16 (the layer input; from layer 1 on also the attention
+    output), about 2e-3 relative each: every layer's cache must be within 1%
+    of its largest value element-wise and 0.5% in relative L2 (a wrong slot,
+    page, head or rotation is off by the values' own size)."""
     a = od.bf16_to_float(gpu_pool, np.float64)
     b = od.bf16_to_float(ref_pool, np.float64)
     d = np.abs(a - b)
-    m = np.maximum(np.abs(a), np.abs(b))
-    ulp = np.where(m > 0, 2.0 ** (np.floor(np.log2(np.maximum(m, 1e-30))) - 7), 0.0)
-    bad = d[0] > ulp[0] * 1.0001
-    if bad.any():
-        i = np.argwhere(bad)[0]
-        raise AssertionError(f"layer-0 KV differs by more than one bf16 step at {tuple(i)}: "
-                             f"gpu={a[0][tuple(i)]} ref={b[0][tuple(i)]}")
-    for l in range(1, a.shape[0]):
-        assert d[l].max() <= 1e-2 * np.abs(b[l]).max() + ulp[l].max(), (l, float(d[l].max()))
+    for l in range(a.shape[0]):
+        scale = np.abs(b[l]).max()
+        ulp = 2.0 ** (np.floor(np.log2(max(scale, 1e-30))) - 7)
+        assert d[l].max() <= 1e-2 * scale + ulp, (l, float(d[l].max()), scale)
+        assert np.linalg.norm(d[l]) <= 5e-3 * np.linalg.norm(b[l]) + ulp, (l, float(np.linalg.norm(d[l])))
 
 
 @pytest.mark.parametrize("mode,name", MODES)
