@@ -147,9 +147,13 @@ struct SmemComb {
 };
 
 struct SmemTopk {
+  alignas(16) uint64_t key[MK_MAX_BATCH][128];  // ordered (logit, -index) keys; 0 beyond E
   alignas(16) float logit[MK_MAX_BATCH][128];
   float sel_val[MK_MAX_BATCH][MK_MAX_TOPK];
   int sel_idx[MK_MAX_BATCH][MK_MAX_TOPK];
+  uint32_t tokmask[128];  // tokens (bit b) routed to each expert
+  int apos[128];          // each expert's position among the active experts
+  uint64_t ballot[2];
 };
 
 // Partial output tiles of the 8 waves: [wave][panel][row tile][16 x 16].
@@ -467,11 +471,14 @@ struct KVPage {
   u32x2_t v[D / 16];
 };
 
+// One split (b, g, s): waits until the QKV tasks of group g are done
+// (qkv_ctr >= qkv_tgt), counts itself on attn_ctr, and the last of the ns
+// splits combines them and signals sig_ctr.
 template <int D>
-__device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
+__device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int g, int s, int ns, int pps,
+                                           int qkv_ctr, int qkv_tgt, int attn_ctr, int sig_ctr, Smem& sm) {
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
-  const int l = t.layer, b = t.a[0], g = t.a[1], s = t.a[2], ns = t.a[3], pps = t.a[4];
   const int wv = wave_id(), ln = lane_id();
   const int PS = P.PS, G = P.G;
   const int seq = P.seq_lens[b];
@@ -523,7 +530,7 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
   KVPage<D> cur, nxt;
   if (early0) cur = load_page(lp);
   if (early1) nxt = load_page(lpn);
-  if (!wait_task(P, t, sm)) return;
+  if (!wait_one(P, qkv_ctr, qkv_tgt, sm)) return;
   if (!seq_ok) {
     if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
     return;
@@ -633,12 +640,32 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
     }
   }
   mark(sm, 0);
-  const int old = arrive(P, t.a[5], sm);
+  const int old = arrive(P, attn_ctr, sm);
   mark(sm, 1);
   if (old == ns - 1) {
     attn_combine<D>(P, b, g, ns, sm);
     mark(sm, 3);
-    arrive_nr(P, t.sig_ctr[0]);
+    arrive_nr(P, sig_ctr);
+  }
+}
+
+// Attention claimer (megakernel post, Chinese version, scheduler section:
+// ATTN_DRAIN claimers steal the next split from the layer's shared queue
+// until it is empty): items (b, g, s) in that order, so a split never waits
+// behind a slow task on a particular compute unit.
+//   a[0] claim counter, a[1] QKV counter base (per group), a[2] QKV tasks per
+//   group, a[3] splits per (sequence, group), a[4] pages per split,
+//   a[5] attention counter base (per sequence and group); sig_ctr[0]: the
+//   combined-output counter base (per group).
+template <int D>
+__device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int ns = t.a[3], n_items = P.B * P.KVH * ns;
+  int id = claim_n(P, t.a[0], 1, sm);
+  while (id < n_items) {
+    const int bg = id / ns, s = id % ns, b = bg / P.KVH, g = bg % P.KVH;
+    attn_split<D>(P, t.layer, b, g, s, ns, t.a[4], t.a[1] + g, t.a[2], t.a[5] + bg, t.sig_ctr[0] + g, sm);
+    if (ld_relaxed(&P.err[0]) != 0) return;
+    id = claim_n(P, t.a[0], 1, sm);
   }
 }
 
@@ -975,23 +1002,35 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
 #pragma unroll
     for (int k = 0; k < MK_MAX_RKS; ++k)
       if (k < P.router_ks) v += p[k];
-    T.logit[i / E][i % E] = v;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < B * E; i += MK_WG_THREADS) {
     const int b = i / E, e = i % E;
-    const float v = T.logit[b][e];
+    T.logit[b][e] = v;
+    // a 64-bit key ordered like (logit, -index): the float's bits made
+    // monotone as an unsigned integer, then the complemented index
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    T.key[b][e] = ((uint64_t)ord << 32) | (uint32_t)(0xffffu - e);
+  }
+  // keys past the last expert of each row: zero, below every real key
+  for (int i = threadIdx.x; i < B * 128; i += MK_WG_THREADS)
+    if (i % 128 >= E) T.key[i / 128][i % 128] = 0ull;
+  __syncthreads();
+  // rank of (b, e): the keys above its own; four threads per pair, each over
+  // a quarter of the experts, summed across the four adjacent lanes
+  for (int i = threadIdx.x; i < B * E * 4; i += MK_WG_THREADS) {
+    const int q = i & 3, pe = i >> 2, b = pe / E, e = pe % E;
+    const uint64_t me = T.key[b][e];
+    const int j0 = q * 32;
     int rank = 0;
-    for (int j = 0; j < E; j += 4) {
-      const float4 q = *(const float4*)(&T.logit[b][j]);
-      rank += (q.x > v) | ((q.x == v) & (j + 0 < e));
-      rank += (q.y > v) | ((q.y == v) & (j + 1 < e));
-      rank += (q.z > v) | ((q.z == v) & (j + 2 < e));
-      rank += (q.w > v) | ((q.w == v) & (j + 3 < e));
+#pragma unroll 4
+    for (int j = 0; j < 32; j += 2) {
+      const uint64_t k0 = T.key[b][j0 + j], k1 = T.key[b][j0 + j + 1];
+      rank += (k0 > me) + (k1 > me);
     }
-    if (rank < K) {
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    if (q == 0 && rank < K) {
       T.sel_idx[b][rank] = e;
-      T.sel_val[b][rank] = v;
+      T.sel_val[b][rank] = T.logit[b][e];
     }
   }
   __syncthreads();
@@ -1006,50 +1045,73 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
     TW.stf(i, __expf(T.sel_val[b][j] - top) / sum);
     if (P.tk_trace) P.tk_trace[((size_t)l * B + b) * K + j] = T.sel_idx[b][j];
   }
-  // route: expert e's position among the active experts, its token count and
-  // its slots (b * k + j, ascending b: a token keeps an expert at most once)
-  if ((int)threadIdx.x < E) {
+  // route: each expert's set of tokens as a bit mask (a token keeps an expert
+  // at most once), the experts' positions among the active ones from two wave
+  // ballots, and each slot's rank within its expert (tokens in ascending order)
+  if ((int)threadIdx.x < E) T.tokmask[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS)
+    atomicOr(&T.tokmask[T.sel_idx[i / K][i % K]], 1u << (i / K));
+  __syncthreads();
+  if (threadIdx.x < 128) {
     const int e = threadIdx.x;
-    int cnt = 0;
-    for (int b = 0; b < B; ++b)
-      for (int j = 0; j < K; ++j) cnt += T.sel_idx[b][j] == e;
-    sm.rt_cnt[e] = cnt;
+    const bool act = e < E && T.tokmask[e] != 0u;
+    const uint64_t bal = __ballot(act);
+    if (lane_id() == 0) T.ballot[e >> 6] = bal;
   }
   __syncthreads();
+  const uint64_t b0 = T.ballot[0], b1 = E > 64 ? T.ballot[1] : 0ull;
+  const int n_active = __popcll(b0) + __popcll(b1);
   if ((int)threadIdx.x < E) {
-    const int e = threadIdx.x, cnt = sm.rt_cnt[e];
-    int a = 0, n_active = 0;
-    for (int x = 0; x < E; ++x) {
-      a += (x < e) & (sm.rt_cnt[x] > 0);
-      n_active += sm.rt_cnt[x] > 0;
-    }
-    if (cnt > 0) {
+    const int e = threadIdx.x;
+    const uint32_t mask = T.tokmask[e];
+    const int a = e < 64 ? __popcll(b0 & ((1ull << e) - 1ull)) : __popcll(b0) + __popcll(b1 & ((1ull << (e - 64)) - 1ull));
+    T.apos[e] = a;
+    if (mask) {
       RT.sti(4 + a, e);
-      RT.sti(4 + E + a, cnt);
-      int r = 0;
-      for (int b = 0; b < B; ++b)
-        for (int j = 0; j < K; ++j)
-          if (T.sel_idx[b][j] == e) RT.sti(4 + 2 * E + a * B + r++, b * K + j);
+      RT.sti(4 + E + a, __popc(mask));
     }
-    if (e == 0) {
-      RT.sti(0, n_active);
-      RT.sti(1, n_active * P.up_items_per_expert);
-      RT.sti(2, n_active * P.down_items_per_expert);
-    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) {
+    const int b = i / K, e = T.sel_idx[b][i % K];
+    const int r = __popc(T.tokmask[e] & ((1u << b) - 1u));
+    RT.sti(4 + 2 * E + T.apos[e] * B + r, i);
+  }
+  if (threadIdx.x == 0) {
+    RT.sti(0, n_active);
+    RT.sti(1, n_active * P.up_items_per_expert);
+    RT.sti(2, n_active * P.down_items_per_expert);
   }
 }
 
-// Route entries of the layer's active experts into LDS (one round trip).
-__device__ __forceinline__ void load_route(const mk_params& P, Smem& sm) {
+// A claimer's start in one round trip: the first claim of n items (thread 0;
+// the result in sm.claim), the route entries of the layer's active experts
+// and, with l >= 0, the sums of squares of layer l's input (then sm.inv_rms).
+__device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_ctr, int n, int l, Smem& sm) {
   const Pub R(P.route);
   const int E = P.E, B = P.B;
   const int i = threadIdx.x;
+  int c = 0;
+  if (i == 0) c = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i < 4) sm.rt_hdr[i] = R.ldi(i);
   if (i < E) {
     sm.rt_e[i] = R.ldi(4 + i);
     sm.rt_cnt[i] = R.ldi(4 + E + i);
   }
   for (int k = i; k < E * B; k += MK_WG_THREADS) sm.rt_slot[k] = R.ldi(4 + 2 * E + k);
+  if (l >= 0) {
+    const Pub S(ssq_of(P, l));
+    for (int k = i; k < B * P.NB; k += MK_WG_THREADS) sm.ssq[k] = S.ldf(k);
+  }
+  if (i == 0) sm.claim = c;
+  __syncthreads();
+  if (l >= 0 && i < B) {
+    const float* q = sm.ssq + i * P.NB;
+    float tot = 0.f;
+    for (int k = 0; k < P.NB; ++k) tot += q[k];
+    sm.inv_rms[i] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+  }
   __syncthreads();
 }
 
@@ -1070,15 +1132,16 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
   const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
   const Pub GU(P.gu), U(u_of(P, l));
-  load_route(P, sm);
+  // items per claim: the host's estimate of the queue over the claimers
+  // expected to be free (any value is correct: claims continue until the
+  // queue is empty)
+  const int nb = min(NBMAX, max(1, t.a[2]));
+  claimer_start(P, claim_ctr, nb, l, sm);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
-  const int nb = min(NBMAX, max(1, (n_items + t.a[2] - 1) / t.a[2]));
-  int id0 = claim_n(P, claim_ctr, nb, sm);
-  load_inv_rms(P, l, sm);
+  int id0 = sm.claim;
   mark(sm, 0);
   bool first = true;
   while (id0 < n_items) {
-    if (ld_relaxed(&P.err[0]) != 0) return;
     // row offsets of each item's tokens
     for (int i = threadIdx.x; i < NBMAX * MK_MAX_BATCH; i += MK_WG_THREADS) {
       const int k = i / MK_MAX_BATCH, r = i % MK_MAX_BATCH, id = id0 + k;
@@ -1154,11 +1217,10 @@ __device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t
   const size_t pstride = (size_t)kc * 512;
   const int DP = P.CB / 16;
   const Pub DN(P.dn), GU(P.gu);
-  int id = claim_n(P, claim_ctr, 1, sm);
-  load_route(P, sm);
+  claimer_start(P, claim_ctr, 1, -1, sm);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
+  int id = sm.claim;
   while (id < n_items) {
-    if (ld_relaxed(&P.err[0]) != 0) return;
     const int a = id / P.down_items_per_expert, cb = id % P.down_items_per_expert;
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
     const int cnt = sm.rt_cnt[a];

@@ -38,6 +38,7 @@ struct Schedule {
   int n_splits_full = 0, n_splits_win = 0, pps = 16;
   int n_router = 0, n_oproj = 0, n_up_claimers = 0, n_down_claimers = 0, n_lm = 0;
   std::vector<int> n_qkv;  // QKV tasks per kv group
+  std::vector<int> n_attn_claimers;  // per layer
   int n_ctr = 0;
   // counter layout
   int c_resid0 = 0, c_lm = 0, c_layer0 = 0, c_per_layer = 0;
@@ -60,6 +61,7 @@ struct CtrIdx {
   int comb;      // [KVH] combined attention outputs per group
   int router;    // router tasks done
   int route;     // route finalized (1)
+  int attn_claim;  // claim counter of the attention split queue
   int up_claim, down_claim;  // claim counters of the two expert queues
   int up_done;   // [E] up/gate items done per active expert slot
   int colblk;    // [NB] contributions per residual column block
@@ -252,7 +254,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   idx += L + 1;
   S->c_lm = idx++;
   S->c_layer0 = idx;
-  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + E + NB;
+  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + 1 + E + NB;
   idx += L * S->c_per_layer;
   S->n_ctr = idx;
   auto resid = [&](int l) { return S->c_resid0 + l; };  // input of layer l ready
@@ -267,6 +269,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     b0 += KVH;
     x.router = b0++;
     x.route = b0++;
+    x.attn_claim = b0++;
     x.up_claim = b0++;
     x.down_claim = b0++;
     x.up_done = b0;
@@ -337,6 +340,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         }
       S->n_qkv[g] = n;
     }
+    if (S->n_qkv[KVH - 1] != S->n_qkv[0]) std::abort();
     // attention splits; the last split of a (sequence, group) combines
     begin_wave();
     const int ns = splits_for(h, l, S->bucket, S->pps);
@@ -344,29 +348,33 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       S->n_splits_win = ns;
     else
       S->n_splits_full = ns;
-    for (int b = 0; b < B; ++b)
-      for (int g = 0; g < KVH; ++g)
-        for (int s = 0; s < ns; ++s) {
-          mk_task t = make_task(MK_OP_ATTN, l);
-          t.a[0] = b;
-          t.a[1] = g;
-          t.a[2] = s;
-          t.a[3] = ns;
-          t.a[4] = S->pps;
-          t.a[5] = x.attn + b * KVH + g;
-          add_wait(t, x.qkv + g, S->n_qkv[g]);
-          t.sig_ctr[0] = x.comb + g;
-          push(t);
-        }
+    // claimers over the (sequence, group, split) queue
+    const int n_attn_items = B * KVH * ns;
+    S->n_attn_claimers.push_back(std::min(n_w, n_attn_items));
+    for (int i = 0; i < S->n_attn_claimers.back(); ++i) {
+      mk_task t = make_task(MK_OP_ATTN, l);
+      t.a[0] = x.attn_claim;
+      t.a[1] = x.qkv;
+      t.a[2] = S->n_qkv[0];
+      t.a[3] = ns;
+      t.a[4] = S->pps;
+      t.a[5] = x.attn;
+      t.sig_ctr[0] = x.comb;
+      push(t);
+    }
     // MoE up/gate claimers
     begin_wave();
-    const int n_attn = B * KVH * ns;
+    const int n_attn = S->n_attn_claimers.back();
     for (int i = 0; i < S->n_up_claimers; ++i) {
       mk_task t = make_task(MK_OP_MOE_UP, l);
       t.a[0] = x.up_claim;
       t.a[1] = x.up_done;
-      // claimers likely free when the queue opens (those not running attention)
-      t.a[2] = std::max(1, S->n_up_claimers - n_attn);
+      // items per claim: the expected queue (distinct experts of B tokens'
+      // top-k under uniform routing) over the claimers likely free when it
+      // opens (those not running attention)
+      const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
+      const int n_free = std::max(1, S->n_up_claimers - n_attn);
+      t.a[2] = std::max(1, (int)std::ceil(e_act * 2 * c.expert_ffn / 16 / n_free));
       add_wait(t, x.route, 1);
       push(t);
     }
@@ -439,15 +447,15 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   const int n_cu = h->n_workers, L = c.n_layers, E = c.n_experts, KVH = c.n_kv_heads, NB = h->NB;
   const int F = c.expert_ffn;
   const int up_per_e = 2 * F / 16, down_per_e = NB;
+  const int B = S.B;
   std::vector<mk_task> tasks = S.cu_tasks;
-  if (corrupt >= 0 && corrupt < (int)tasks.size()) {
-    // make the first wait of that task unsatisfiable by one arrival
-    for (int i = 0; i < 3; ++i)
-      if (tasks[corrupt].wait_ctr[i] >= 0) {
-        tasks[corrupt].wait_tgt[i] += 1;
-        break;
-      }
-  }
+  // make the first wait of the first task at or after `corrupt` that waits
+  // on something unsatisfiable by one arrival
+  for (int k = std::max(corrupt, 0); corrupt >= 0 && k < (int)tasks.size(); ++k)
+    if (tasks[k].wait_ctr[0] >= 0) {
+      tasks[k].wait_tgt[0] += 1;
+      break;
+    }
   std::vector<int64_t> ctr(S.n_ctr, 0);
   std::vector<SimCU> cu(n_cu);
   std::mt19937_64 rng(seed);
@@ -489,10 +497,6 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
             if (++ctr[t.a[5]] == h->n_router_tasks) ctr[t.sig_ctr[0]]++;
             done();
             break;
-          case MK_OP_ATTN:
-            if (++ctr[t.a[5]] == t.a[3]) ctr[t.sig_ctr[0]]++;
-            done();
-            break;
           case MK_OP_OPROJ:
             block(t, t.a[2], t.a[1], t.layer);
             done();
@@ -501,6 +505,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
             ctr[t.a[3]]++;
             done();
             break;
+          case MK_OP_ATTN:
           case MK_OP_MOE_UP:
           case MK_OP_MOE_DOWN:
             u.in_claimer = true;
@@ -514,7 +519,26 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       // claimer step
       const int l = layer_of(t.a[0]);
       const int na = n_active[l];
-      if (t.op == MK_OP_MOE_UP) {
+      if (t.op == MK_OP_ATTN) {
+        const int ns = t.a[3], n_items = B * KVH * ns;
+        if (u.pending_item < 0) {
+          const int id = (int)ctr[t.a[0]]++;
+          progress = true;
+          if (id >= n_items) {
+            u.in_claimer = false;
+            done();
+          } else {
+            u.pending_item = id;
+          }
+        } else {
+          const int bg = u.pending_item / ns, g = bg % KVH;
+          if (ctr[t.a[1] + g] >= t.a[2]) {
+            if (++ctr[t.a[5] + bg] == ns) ctr[t.sig_ctr[0] + g]++;
+            u.pending_item = -1;
+            progress = true;
+          }
+        }
+      } else if (t.op == MK_OP_MOE_UP) {
         const int id = (int)ctr[t.a[0]]++;
         if (id >= na * up_per_e) {
           u.in_claimer = false;
@@ -549,7 +573,6 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     }
   }
   // every counter against the arrivals it must receive
-  const int B = S.B;
   std::vector<int64_t> want(S.n_ctr, 0);
   for (int l = 0; l <= L; ++l) want[S.c_resid0 + l] = NB;
   want[S.c_lm] = S.n_lm;
@@ -561,6 +584,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     for (int g = 0; g < KVH; ++g) want[k++] = B;
     want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
     want[k++] = 1;                                                   // route finalized
+    want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
     want[k++] = (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
     want[k++] = (int64_t)n_active[l] * down_per_e + S.n_down_claimers;
     for (int a = 0; a < E; ++a) want[k++] = a < n_active[l] ? up_per_e : 0;
@@ -761,7 +785,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->lm_arg = (int32_t*)(sb + s_lma);
   h->err_word = (uint32_t*)(sb + s_err);
   // counters: capacity for the largest batch
-  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 4 + E + h->NB);
+  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 5 + E + h->NB);
   for (int i = 0; i < 2; ++i) {
     if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
     hipMemset(h->ctr[i], 0, (size_t)h->n_ctr_cap * 4);
