@@ -37,6 +37,13 @@
 // layout the panels are stored in. The K dimension is spread over the 8 waves
 // and their partial tiles are summed through LDS in a fixed order.
 //
+// Precision. A bf16 operand carries 8 significant bits; rounding every
+// activation to it would add about 2^-9 relative error per projection and
+// layer, which over 48 layers exceeds the float32 reference's tolerance. So
+// every activation operand is a split pair: hi = bf16(x), lo = bf16(x - hi),
+// and each product is two MFMAs (W hi + W lo), leaving about 2^-17 relative
+// error; the weights and the KV cache are bf16 exactly as stored.
+//
 // Layer inputs. The residual add of a column block (the last contribution to
 // arrive performs it) also writes u = bf16(h * gamma_next) and the block's
 // per-token sum of squares. A consumer multiplies its projection of u by
@@ -70,6 +77,12 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+// The split pair of x: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  const uint32_t h = f2bf(x);
+  hi = (uint16_t)h;
+  lo = (uint16_t)f2bf(x - bf2f((uint16_t)h));
+}
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -289,11 +302,16 @@ __device__ __forceinline__ int claim_n(const mk_params& P, int32_t c, int n, Sme
 // Layer inputs alternate between two buffers by layer parity: u and the sums
 // of squares of layer l are read while layer l's residual adds write those of
 // layer l + 1.
-__device__ __forceinline__ const uint16_t* u_of(const mk_params& P, int l) {
-  return P.u + (size_t)(l & 1) * P.B * P.H;
+// u is stored as the split pair: part 0 = bf16(x), part 1 = bf16(x - part 0).
+__device__ __forceinline__ const uint16_t* u_of(const mk_params& P, int l, int part) {
+  return P.u + ((size_t)(l & 1) * 2 + part) * P.B * P.H;
 }
-__device__ __forceinline__ uint16_t* u_of_w(const mk_params& P, int l) {
-  return P.u + (size_t)(l & 1) * P.B * P.H;
+__device__ __forceinline__ uint16_t* u_of_w(const mk_params& P, int l, int part) {
+  return P.u + ((size_t)(l & 1) * 2 + part) * P.B * P.H;
+}
+// The attention output, split the same way: [hi|lo][B][QH*D].
+__device__ __forceinline__ uint16_t* o_of(const mk_params& P, int part) {
+  return P.o + (size_t)part * P.B * P.QH * P.D;
 }
 __device__ __forceinline__ float* ssq_of(const mk_params& P, int l) {
   return P.ssq + (size_t)(l & 1) * P.B * P.NB;
@@ -403,8 +421,10 @@ struct Acc {
   f32x4_t c[NP][MT];
 };
 
+// acc = (A hi + A lo) W over this wave's chunks.
 template <int NP, int MT, int NCH>
-__device__ __forceinline__ void mfma_tiles(Acc<NP, MT>& acc, const WTile<NP, NCH>& w, const ATile<MT, NCH>& A) {
+__device__ __forceinline__ void mfma_tiles(Acc<NP, MT>& acc, const WTile<NP, NCH>& w, const ATile<MT, NCH>& Ah,
+                                           const ATile<MT, NCH>& Al) {
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
@@ -414,10 +434,14 @@ __device__ __forceinline__ void mfma_tiles(Acc<NP, MT>& acc, const WTile<NP, NCH
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A.a[mt][i]),
+      for (int mt = 0; mt < MT; ++mt) {
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Al.a[mt][i]),
                                                                 __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
                                                                 acc.c[pp][mt], 0, 0, 0);
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Ah.a[mt][i]),
+                                                                __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                acc.c[pp][mt], 0, 0, 0);
+      }
 }
 
 // Sum the 8 waves' partial tiles (fixed order) into sm.out, indexed
@@ -538,8 +562,8 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   if (lp < my1 && !early0) cur = load_page(lp);
   if (lpn < my1 && !early1) nxt = load_page(lpn);
 
-  // Q^T operand: lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
-  bf16x8_t qb[NC];
+  // Q^T operand (split pair): lane holds q[head ln%16][dims 32c + 8(ln/16) + i]
+  bf16x8_t qb[NC], ql[NC];
   {
     const int hh = ln & 15;
     const Pub Q(P.q + (size_t)b * P.QH * D + (size_t)g * G * D);
@@ -548,10 +572,17 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
     for (int c = 0; c < NC; ++c) {
       const float4 a0 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4)), a1 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4) + 4);
       const float qv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      u32x4_t pk;
+      u32x4_t pk, pl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = hh < G ? (f2bf(qv[2 * i]) | (f2bf(qv[2 * i + 1]) << 16)) : 0u;
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(qv[2 * i], h0, l0);
+        split_bf16(qv[2 * i + 1], h1, l1);
+        pk[i] = hh < G ? ((uint32_t)h0 | ((uint32_t)h1 << 16)) : 0u;
+        pl[i] = hh < G ? ((uint32_t)l0 | ((uint32_t)l1 << 16)) : 0u;
+      }
       qb[c] = __builtin_bit_cast(bf16x8_t, pk);
+      ql[c] = __builtin_bit_cast(bf16x8_t, pl);
     }
   }
 
@@ -560,14 +591,14 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   for (int d = 0; d < NT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
 
-  while (lp < my1 && !bad) {
-    KVPage<D> nxt2;
-    const int nlp2 = lp + 2 * MK_WAVES;
-    if (nlp2 < my1) nxt2 = load_page(nlp2);
+  // online softmax over one page (keys as MFMA rows)
+  auto do_page = [&](const KVPage<D>& pg, int lp) {
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[c]), qb[c], sacc, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pg.k[c]), ql[c], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pg.k[c]), qb[c], sacc, 0, 0, 0);
+    }
     float sv[4];
     float mloc = kNegInf;
 #pragma unroll
@@ -597,11 +628,19 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
 #pragma unroll
       for (int d = 0; d < NT; ++d) {
         oacc[d] *= alpha;
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, cur.v[d]), pB, oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, pg.v[d]), pB, oacc[d], 0, 0, 0);
       }
     }
-    cur = nxt;
-    nxt = nxt2;
+  };
+  // two pages in registers: each wave computes one while the page two ahead
+  // of it streams into the other's registers
+  while (lp < my1 && !bad) {
+    do_page(cur, lp);
+    if (lp + 2 * MK_WAVES < my1) cur = load_page(lp + 2 * MK_WAVES);
+    lp += MK_WAVES;
+    if (lp >= my1 || bad) break;
+    do_page(nxt, lp);
+    if (lp + 2 * MK_WAVES < my1) nxt = load_page(lp + 2 * MK_WAVES);
     lp += MK_WAVES;
   }
   if (bad) raise_error(P, MK_DEVERR_FAULT, 5000 + b, (uint32_t)lp);
@@ -706,7 +745,8 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
   }
   __syncthreads();
   mark(sm, 2);
-  const Pub dst(P.o + (size_t)b * P.QH * D + (size_t)g * G * D);
+  const size_t dst_off = (size_t)b * P.QH * D + (size_t)g * G * D;
+  const Pub dst_h(o_of(P, 0) + dst_off), dst_l(o_of(P, 1) + dst_off);
   // each thread's outputs (G * D <= 1024: at most two) over up to 32 splits
   // at a time, every load in flight together
   constexpr int NO = 1024 / MK_WG_THREADS, SB = 32;
@@ -735,8 +775,13 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
 #pragma unroll
   for (int u = 0; u < NO; ++u) {
     const int idx = threadIdx.x + u * MK_WG_THREADS;
-    // bf16: the O projection's matrix-core operand
-    if (idx < G * D) dst.st16(idx, (uint16_t)f2bf(O[u] / C.L[idx / D]));
+    // the O projection's matrix-core operand, as a split pair
+    if (idx < G * D) {
+      uint16_t hi, lo;
+      split_bf16(O[u] / C.L[idx / D], hi, lo);
+      dst_h.st16(idx, hi);
+      dst_l.st16(idx, lo);
+    }
   }
 }
 
@@ -776,7 +821,7 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
                                                   Smem& sm) {
   const int H = P.H, CB = P.CB;
   constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;
-  const Pub h(P.h), U(u_of_w(P, l_next));
+  const Pub h(P.h), Uh(u_of_w(P, l_next, 0)), Ul(u_of_w(P, l_next, 1));
   const uint16_t* gam = P.gamma + (size_t)l_next * H;
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
@@ -784,7 +829,10 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
     if (idx < n) {
       const int b = idx / CB, c = cb * CB + idx % CB;
       h.stf(b * H + c, hv[k]);
-      U.st16(b * H + c, (uint16_t)f2bf(hv[k] * bf2f(gam[c])));
+      uint16_t hi, lo;
+      split_bf16(hv[k] * bf2f(gam[c]), hi, lo);
+      Uh.st16(b * H + c, hi);
+      Ul.st16(b * H + c, lo);
       sm.out[idx] = hv[k] * hv[k];
     }
   }
@@ -811,12 +859,13 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   if (!wait_task(P, t, sm)) return;
   set_rows_batch(P, sm, 0, P.H, 0);
   __syncthreads();
-  ATile<MT, NCH> A;
-  atile_load_bf16(A, Pub(u_of(P, l)), sm.row_off[0], 0, kc);
+  ATile<MT, NCH> Ah, Al;
+  atile_load_bf16(Ah, Pub(u_of(P, l, 0)), sm.row_off[0], 0, kc);
+  atile_load_bf16(Al, Pub(u_of(P, l, 1)), sm.row_off[0], 0, kc);
   load_inv_rms(P, l, sm);
   mark(sm, 0);
   Acc<2, MT> acc;
-  mfma_tiles(acc, w, A);
+  mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
   const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
@@ -929,10 +978,11 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
   mark(sm, 0);
   set_rows_batch(P, sm, 0, P.QH * P.D, 0);
   __syncthreads();
-  ATile<MT, NCH> A;
-  atile_load_bf16(A, Pub(P.o), sm.row_off[0], c0, c1);
+  ATile<MT, NCH> Ah, Al;
+  atile_load_bf16(Ah, Pub(o_of(P, 0)), sm.row_off[0], c0, c1);
+  atile_load_bf16(Al, Pub(o_of(P, 1)), sm.row_off[0], c0, c1);
   Acc<4, MT> acc;
-  mfma_tiles(acc, w, A);
+  mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
   const Pub AO(P.ao);
@@ -961,12 +1011,13 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   if (!wait_task(P, t, sm)) return;
   set_rows_batch(P, sm, 0, P.H, 0);
   __syncthreads();
-  ATile<MT, NCH> A;
-  atile_load_bf16(A, Pub(u_of(P, l)), sm.row_off[0], c0, c1);
+  ATile<MT, NCH> Ah, Al;
+  atile_load_bf16(Ah, Pub(u_of(P, l, 0)), sm.row_off[0], c0, c1);
+  atile_load_bf16(Al, Pub(u_of(P, l, 1)), sm.row_off[0], c0, c1);
   load_inv_rms(P, l, sm);
   mark(sm, 0);
   Acc<2, MT> acc;
-  mfma_tiles(acc, w, A);
+  mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
   const Pub RP(P.rp);
@@ -1131,7 +1182,7 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
   const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
   const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
-  const Pub GU(P.gu), U(u_of(P, l));
+  const Pub GU(P.gu), Uh(u_of(P, l, 0)), Ul(u_of(P, l, 1));
   // items per claim: the host's estimate of the queue over the claimers
   // expected to be free (any value is correct: claims continue until the
   // queue is empty)
@@ -1154,7 +1205,7 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
     }
     __syncthreads();
     WTile<2, NCH> w[NBMAX];
-    ATile<MT, NCH> A[NBMAX];
+    ATile<MT, NCH> Ah[NBMAX], Al[NBMAX];
 #pragma unroll
     for (int k = 0; k < NBMAX; ++k) {
       const int id = id0 + k;
@@ -1166,7 +1217,8 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
       // an item past the queue's end loads nothing (np = 0: a zero tile)
       wtile_load(w[k], P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
                  valid ? 2 : 0, c0, c0 + kh_chunks);
-      atile_load_bf16(A[k], U, sm.row_off[k], valid ? c0 : 0, valid ? c0 + kh_chunks : 0);
+      atile_load_bf16(Ah[k], Uh, sm.row_off[k], valid ? c0 : 0, valid ? c0 + kh_chunks : 0);
+      atile_load_bf16(Al[k], Ul, sm.row_off[k], valid ? c0 : 0, valid ? c0 + kh_chunks : 0);
     }
     mark(sm, 1);
     // the next claim travels while the weights stream
@@ -1179,7 +1231,7 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
       const int tt = r >> 1, kh = r & 1;
       const int cnt = sm.rt_cnt[a];
       Acc<2, MT> acc;
-      mfma_tiles(acc, w[k], A[k]);
+      mfma_tiles(acc, w[k], Ah[k], Al[k]);
       reduce_tiles(acc, sm);
       if (k == 0 && first) mark(sm, 2);
       // gu[slot][kh][gate|up][F]
@@ -1229,42 +1281,55 @@ __device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t
     // the next claim travels while the weights stream
     const int next = claim_n(P, claim_ctr, 1, sm);
     if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
-    // act = silu(g0 + g1) * (u0 + u1) per routed row, bf16 in LDS
-    const int n = MT * 16 * F;
-    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
-      float g[4][4];
+    // act = silu(g0 + g1) * (u0 + u1) per routed row, staged in LDS as the
+    // split pair (16 rows at a time: hi in act[0, 16F), lo in act[16F, 32F))
+    Acc<4, MT> acc;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * MK_WG_THREADS, row = i / F, f = i % F;
-        const bool live = i < n && row < cnt;
-        const int slot = live ? sm.rt_slot[a * B + row] : 0;
+    for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
-      }
+      for (int mt = 0; mt < MT; ++mt) acc.c[pp][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * MK_WG_THREADS;
-        if (i < n) {
-          const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
-          sm.act[i] = (uint16_t)f2bf(gt / (1.0f + __expf(-gt)) * ut);
+    for (int mt = 0; mt < MT; ++mt) {
+      const int n = 16 * F;
+      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
+        float g[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + k * MK_WG_THREADS, row = mt * 16 + i / F, f = i % F;
+          const bool live = i < n && row < cnt;
+          const int slot = live ? sm.rt_slot[a * B + row] : 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + k * MK_WG_THREADS;
+          if (i < n) {
+            const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
+            split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[n + i]);
+          }
         }
       }
-    }
-    __syncthreads();
-    ATile<MT, NCH> A;
-    {
+      __syncthreads();
       const int wv = wave_id(), ln = lane_id();
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int i = 0; i < NCH; ++i) {
+        const int c = wv + MK_WAVES * i;
+        const int off = (ln & 15) * F + 32 * c + 8 * (ln >> 4);
+        const u32x4_t ah = c < kc ? *(const u32x4_t*)(sm.act + off) : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t al = c < kc ? *(const u32x4_t*)(sm.act + n + off) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int c = wv + MK_WAVES * i;
-          A.a[mt][i] = c < kc ? *(const u32x4_t*)(sm.act + (mt * 16 + (ln & 15)) * F + 32 * c + 8 * (ln >> 4))
-                              : u32x4_t{0u, 0u, 0u, 0u};
+        for (int pp = 0; pp < 4; ++pp) {
+          acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                                  __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                  acc.c[pp][mt], 0, 0, 0);
+          acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                                  __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                  acc.c[pp][mt], 0, 0, 0);
         }
+      }
+      __syncthreads();
     }
-    Acc<4, MT> acc;
-    mfma_tiles(acc, w, A);
     reduce_tiles(acc, sm);
     for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
       const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
@@ -1285,11 +1350,18 @@ __device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t
 // value).
 __device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm);
 
+// Panels [p, p + np): the products, then (while the tiles reduce) the next
+// panels' weights into the same registers, then the logits and the running
+// best of every token.
 template <int NP, int MT, int NCH>
-__device__ __forceinline__ void lm_pair(const mk_params& P, const WTile<NP, NCH>& w, const ATile<MT, NCH>& A, int p,
-                                        int np, float& bv, int& bi, Smem& sm) {
+__device__ __forceinline__ void lm_pair(const mk_params& P, WTile<NP, NCH>& w, const ATile<MT, NCH>& Ah,
+                                        const ATile<MT, NCH>& Al, int p, int np, int p1, float& bv, int& bi,
+                                        Smem& sm) {
   Acc<NP, MT> acc;
-  mfma_tiles(acc, w, A);
+  mfma_tiles(acc, w, Ah, Al);
+  const int kc = P.H / 32;
+  const size_t pstride = (size_t)kc * 512;
+  if (p + NP < p1) wtile_load(w, P.wlm + (size_t)(p + NP) * pstride, pstride, min(NP, p1 - p - NP), 0, kc);
   reduce_tiles(acc, sm);
   for (int o = threadIdx.x; o < NP * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
@@ -1318,23 +1390,18 @@ __device__ __forceinline__ void op_lmhead(const mk_params& P, const mk_task& t, 
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
   const int L = P.L;
-  WTile<NP, NCH> w0, w1;
+  WTile<NP, NCH> w0;
   wtile_load(w0, P.wlm + (size_t)p0 * pstride, pstride, min(NP, p1 - p0), 0, kc);
   if (!wait_task(P, t, sm)) return;
   set_rows_batch(P, sm, 0, P.H, 0);
   __syncthreads();
-  ATile<MT, NCH> A;
-  atile_load_bf16(A, Pub(u_of(P, L)), sm.row_off[0], 0, kc);
+  ATile<MT, NCH> Ah, Al;
+  atile_load_bf16(Ah, Pub(u_of(P, L, 0)), sm.row_off[0], 0, kc);
+  atile_load_bf16(Al, Pub(u_of(P, L, 1)), sm.row_off[0], 0, kc);
   load_inv_rms(P, L, sm);
   float bv = kNegInf;
   int bi = 0x7fffffff;
-  for (int p = p0; p < p1; p += 2 * NP) {
-    if (p + NP < p1) wtile_load(w1, P.wlm + (size_t)(p + NP) * pstride, pstride, min(NP, p1 - p - NP), 0, kc);
-    lm_pair(P, w0, A, p, min(NP, p1 - p), bv, bi, sm);
-    if (p + NP >= p1) break;
-    if (p + 2 * NP < p1) wtile_load(w0, P.wlm + (size_t)(p + 2 * NP) * pstride, pstride, min(NP, p1 - p - 2 * NP), 0, kc);
-    lm_pair(P, w1, A, p + NP, min(NP, p1 - p - NP), bv, bi, sm);
-  }
+  for (int p = p0; p < p1; p += NP) lm_pair(P, w0, Ah, Al, p, min(NP, p1 - p), p1, bv, bi, sm);
   if ((int)threadIdx.x < P.B) {
     Pub(P.lm_val).stf(threadIdx.x * P.n_lm_tasks + ord, bv);
     Pub(P.lm_arg).sti(threadIdx.x * P.n_lm_tasks + ord, bi);
@@ -1393,9 +1460,9 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
     case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe_up<MT, 32 / MK_WAVES, MT == 1 ? 3 : 2>(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe_up<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
     case MK_OP_MOE_DOWN: op_moe_down<MT, 24 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, 1>(P, t, sm); break;
+    case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
     default: wait_task(P, t, sm); break;
   }
 }

@@ -756,7 +756,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     return o;
   };
   const size_t s_h = stake((size_t)Bm * H * 4), s_ssq = stake((size_t)2 * Bm * h->NB * 4);
-  const size_t s_u = stake((size_t)2 * Bm * H * 2);
+  const size_t s_u = stake((size_t)4 * Bm * H * 2);
   const size_t s_q = stake((size_t)Bm * h->q_dim * 4), s_o = stake((size_t)Bm * h->q_dim * 4);
   const size_t s_part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
   const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_rp = stake((size_t)h->router_ks * Bm * E * 4);
@@ -1057,9 +1057,9 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
   const Item items[] = {
       {"h", h->h, Bm * H * 4},
       {"ssq", h->ssq, 2 * Bm * h->NB * 4},
-      {"u", h->u, 2 * Bm * H * 2},
+      {"u", h->u, 4 * Bm * H * 2},
       {"q", h->q, Bm * h->q_dim * 4},
-      {"o", h->o, Bm * h->q_dim * 2},
+      {"o", h->o, 2 * Bm * h->q_dim * 2},
       {"ao", h->ao, (size_t)c.n_kv_heads * Bm * H * 4},
       {"rp", h->rp, (size_t)h->router_ks * Bm * E * 4},
       {"tk_idx", h->tk_idx, Bm * K * 4},

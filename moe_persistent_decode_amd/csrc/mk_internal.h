@@ -101,10 +101,10 @@ struct mk_params {
   uint32_t flags;
   // scratch
   float* h;      // [B][H] residual stream
-  uint16_t* u;   // [2][B][H] layer input bf16(h * gamma_l), buffer l % 2
+  uint16_t* u;   // [2][2][B][H] layer input x = h * gamma_l as the split pair (bf16(x), bf16(x - bf16(x))), buffer l % 2
   float* q;      // [B][QH*D] rotated queries
   float* part;   // [B][KVH][max_splits][G*D + 2G] attention partials (o, m, l)
-  uint16_t* o;   // [B][QH*D] attention output (bf16)
+  uint16_t* o;   // [2][B][QH*D] attention output as the split pair (hi, lo), bf16
   float* ao;     // [KVH][B][H] O projection partials per kv group
   float* ssq;    // [2][B][NB] per column block sums of squares of layer l's input, buffer l % 2
   float* rp;     // [router_ks][B][E] router logit partials
