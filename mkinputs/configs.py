@@ -116,6 +116,11 @@ WORKLOADS = {
     # batch 32, ragged contexts U{512..16384}
     "full48_b32_ragged": Workload("full48_b32_ragged", FULL48, batch=32, seq_len=(512, 16384),
                                   ragged=True, steps=16),
+    # the one-layer model at the long-context shapes (parity cases)
+    "layer1_b1_256k": Workload("layer1_b1_256k", LAYER1, batch=1, seq_len=(262144, 262144), steps=4),
+    "layer1_b4_64k": Workload("layer1_b4_64k", LAYER1, batch=4, seq_len=(65536, 65536), steps=4),
+    "layer1_b32_ragged": Workload("layer1_b32_ragged", LAYER1, batch=32, seq_len=(512, 16384),
+                                  ragged=True, steps=4),
     # long context
     "full48_b1_256k": Workload("full48_b1_256k", FULL48, batch=1, seq_len=(262144, 262144), steps=64),
     "full48_b4_64k": Workload("full48_b4_64k", FULL48, batch=4, seq_len=(65536, 65536), steps=64),

@@ -1182,7 +1182,7 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
   const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
   const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
-  const Pub GU(P.gu), Uh(u_of(P, l, 0)), Ul(u_of(P, l, 1));
+  const Pub GU(P.gu);
   // items per claim: the host's estimate of the queue over the claimers
   // expected to be free (any value is correct: claims continue until the
   // queue is empty)
@@ -1190,22 +1190,21 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
   claimer_start(P, claim_ctr, nb, l, sm);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
   int id0 = sm.claim;
+  // the layer input of every token over the whole K, once per claimer: each
+  // item multiplies its expert's weights with all token rows (one tile of 16
+  // rows costs the same for any count) and keeps the rows routed to it
+  set_rows_batch(P, sm, 0, P.H, 0);
+  __syncthreads();
+  // (per K half, in the chunk-to-wave order the half's weights use)
+  ATile<MT, NCH> Ah0, Al0, Ah1, Al1;
+  atile_load_bf16(Ah0, Pub(u_of(P, l, 0)), sm.row_off[0], 0, kh_chunks);
+  atile_load_bf16(Al0, Pub(u_of(P, l, 1)), sm.row_off[0], 0, kh_chunks);
+  atile_load_bf16(Ah1, Pub(u_of(P, l, 0)), sm.row_off[0], kh_chunks, kc);
+  atile_load_bf16(Al1, Pub(u_of(P, l, 1)), sm.row_off[0], kh_chunks, kc);
   mark(sm, 0);
   bool first = true;
   while (id0 < n_items) {
-    // row offsets of each item's tokens
-    for (int i = threadIdx.x; i < NBMAX * MK_MAX_BATCH; i += MK_WG_THREADS) {
-      const int k = i / MK_MAX_BATCH, r = i % MK_MAX_BATCH, id = id0 + k;
-      int off = -1;
-      if (k < nb && id < n_items) {
-        const int a = id / upe;
-        if (r < sm.rt_cnt[a]) off = (sm.rt_slot[a * B + r] / K) * P.H;
-      }
-      sm.row_off[k][r] = off;
-    }
-    __syncthreads();
     WTile<2, NCH> w[NBMAX];
-    ATile<MT, NCH> Ah[NBMAX], Al[NBMAX];
 #pragma unroll
     for (int k = 0; k < NBMAX; ++k) {
       const int id = id0 + k;
@@ -1217,8 +1216,6 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
       // an item past the queue's end loads nothing (np = 0: a zero tile)
       wtile_load(w[k], P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
                  valid ? 2 : 0, c0, c0 + kh_chunks);
-      atile_load_bf16(Ah[k], Uh, sm.row_off[k], valid ? c0 : 0, valid ? c0 + kh_chunks : 0);
-      atile_load_bf16(Al[k], Ul, sm.row_off[k], valid ? c0 : 0, valid ? c0 + kh_chunks : 0);
     }
     mark(sm, 1);
     // the next claim travels while the weights stream
@@ -1230,18 +1227,27 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
       const int a = id / upe, r = id % upe;
       const int tt = r >> 1, kh = r & 1;
       const int cnt = sm.rt_cnt[a];
+      // this K half's operand (a bitwise blend: a select between the two
+      // tiles would be turned into a dynamically indexed array in scratch)
+      ATile<MT, NCH> Hh, Hl;
+      const uint32_t hi_half = 0u - (uint32_t)kh;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          Hh.a[mt][i] = (Ah1.a[mt][i] & hi_half) | (Ah0.a[mt][i] & ~hi_half);
+          Hl.a[mt][i] = (Al1.a[mt][i] & hi_half) | (Al0.a[mt][i] & ~hi_half);
+        }
       Acc<2, MT> acc;
-      mfma_tiles(acc, w[k], Ah[k], Al[k]);
+      mfma_tiles(acc, w[k], Hh, Hl);
       reduce_tiles(acc, sm);
       if (k == 0 && first) mark(sm, 2);
-      // gu[slot][kh][gate|up][F]
-      for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
-        const int which = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
-        const int row = mt * 16 + m;
-        if (row < cnt) {
-          const int slot = sm.rt_slot[a * B + row];
-          GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, sm.out[o] * sm.inv_rms[slot / K]);
-        }
+      // gu[slot][kh][gate|up][F] for the tokens routed to the expert
+      for (int o = threadIdx.x; o < 2 * cnt * 16; o += MK_WG_THREADS) {
+        const int which = o / (cnt * 16), rr = (o / 16) % cnt, nn = o % 16;
+        const int slot = sm.rt_slot[a * B + rr], b = slot / K;
+        const float v = sm.out[(which * MT + b / 16) * 256 + (b % 16) * 16 + nn];
+        GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, v * sm.inv_rms[b]);
       }
     }
     // one drain for the batch, then each item's arrival on its expert's counter
@@ -1460,7 +1466,7 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
     case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe_up<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe_up<MT, 32 / MK_WAVES, MT == 1 ? 3 : 1>(P, t, sm); break;
     case MK_OP_MOE_DOWN: op_moe_down<MT, 24 / MK_WAVES>(P, t, sm); break;
     case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
     default: wait_task(P, t, sm); break;

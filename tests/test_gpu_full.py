@@ -8,7 +8,9 @@ N(0, 1) K/V:
 - the one-layer model: three teacher-forced steps in both modes, every
   stage of the first step (rotated query, attention output, O-projection
   partials, router logits, top-k, expert outputs, residual) and every step's
-  logits, greedy token, top-k set and appended K/V;
+  logits, greedy token, top-k set and appended K/V; the same model at a
+  262144-token context, at batch 4 with 64K contexts and at batch 32 with
+  ragged 512..16384 contexts;
 - the 48-layer model (12 full, 36 window-4096 layers): two steps of the
   megakernel, logits, greedy token and all 48 layers' top-k sets.
 
@@ -52,10 +54,11 @@ class FullCase:
         self.W = gen.LazyWeights(m, wl.seed_weights, device="cuda")
         self.uploaded = {}
         self.bt = self.bs.block_tables.cuda()
-        self.route = torch.full((m.n_layers, 1, m.top_k), -1, dtype=torch.int32, device=dev)
+        B = wl.batch
+        self.route = torch.full((m.n_layers, B, m.top_k), -1, dtype=torch.int32, device=dev)
         self.dec.set_routing_trace(self.route)
-        self.logits = torch.empty((1, m.vocab), dtype=torch.float32, device=dev)
-        self.nxt = torch.empty(1, dtype=torch.int32, device=dev)
+        self.logits = torch.empty((B, m.vocab), dtype=torch.float32, device=dev)
+        self.nxt = torch.empty(B, dtype=torch.int32, device=dev)
 
     def _load_layer(self, l):
         w = gen.make_layer_weights(self.m, l, self.wl.seed_weights, "cuda")
@@ -78,40 +81,43 @@ class FullCase:
         self.dec.step(torch.tensor(tokens, dtype=torch.int32, device="cuda"), self.bt,
                       torch.tensor(lens, dtype=torch.int32, device="cuda"), int(lens.max()), self.logits, self.nxt)
         self.dec.sync()
-        return self.logits.cpu().numpy(), int(self.nxt.item()), self.route.cpu().numpy()
+        return self.logits.cpu().numpy(), self.nxt.cpu().numpy(), self.route.cpu().numpy()
 
     def compare(self, s, lg_ref, tr_ref, lg, tok, route):
-        ok, mx, rl2 = logits_close(lg[0], lg_ref[0])
-        gap = float(tj.greedy_gap(lg_ref)[0])
-        say(f"  step {s}: logits max|d|={mx:.2e} relL2={rl2:.2e}; token gpu={tok} ref={int(od.greedy(lg_ref)[0])} "
-            f"(gap {gap:.3f}); repaired router layers {sorted(self.repaired)}")
-        assert ok, (s, mx, rl2)
-        if gap >= 1e-2:
-            assert tok == int(od.greedy(lg_ref)[0]), s
-        for l in range(self.m.n_layers):
-            assert sorted(route[l, 0].tolist()) == sorted(tr_ref.topk_idx[l][0].tolist()), (s, l)
+        ref_tok = od.greedy(lg_ref)
+        gaps = tj.greedy_gap(lg_ref)
+        for b in range(lg.shape[0]):
+            ok, mx, rl2 = logits_close(lg[b], lg_ref[b])
+            say(f"  step {s} row {b}: logits max|d|={mx:.2e} relL2={rl2:.2e}; token gpu={int(tok[b])} "
+                f"ref={int(ref_tok[b])} (gap {gaps[b]:.3f})")
+            assert ok, (s, b, mx, rl2)
+            if gaps[b] >= 1e-2:
+                assert int(tok[b]) == int(ref_tok[b]), (s, b)
+            for l in range(self.m.n_layers):
+                assert sorted(route[l, b].tolist()) == sorted(tr_ref.topk_idx[l][b].tolist()), (s, b, l)
+        say(f"  repaired router layers {sorted(self.repaired)}")
 
     def check_kv(self, lens_per_step):
         gpu = torch_to_bits(self.pool)
         m, P = self.m, self.m.page_size
         touched = np.zeros(gpu.shape, bool)
         for lens in lens_per_step:
-            pos = int(lens[0]) - 1
-            page = int(self.bs.block_tables[0, pos // P])
-            for plane in range(2):
-                a = od.bf16_to_float(gpu[:, page, plane], np.float64)
-                r = od.bf16_to_float(self.pool_host[:, page, plane], np.float64)
-                if plane == 0:
-                    a = a.reshape(m.n_layers, m.n_kv_heads, P, m.head_dim)[:, :, pos % P]
-                    r = r.reshape(m.n_layers, m.n_kv_heads, P, m.head_dim)[:, :, pos % P]
-                    touched[:, page, 0].reshape(m.n_layers, m.n_kv_heads, P, m.head_dim)[:, :, pos % P] = True
-                else:
-                    a = a.reshape(m.n_layers, m.n_kv_heads, m.head_dim, P)[..., pos % P]
-                    r = r.reshape(m.n_layers, m.n_kv_heads, m.head_dim, P)[..., pos % P]
-                    touched[:, page, 1].reshape(m.n_layers, m.n_kv_heads, m.head_dim, P)[..., pos % P] = True
-                for l in range(m.n_layers):
-                    d = np.abs(a[l] - r[l])
-                    assert d.max() <= 1e-2 * np.abs(r[l]).max() + 1e-3, (pos, l, plane, float(d.max()))
+            for b in range(len(lens)):
+                pos = int(lens[b]) - 1
+                page = int(self.bs.block_tables[b, pos // P])
+                for plane in range(2):
+                    a = od.bf16_to_float(gpu[:, page, plane], np.float64)
+                    r = od.bf16_to_float(self.pool_host[:, page, plane], np.float64)
+                    t = touched[:, page, plane]
+                    if plane == 0:
+                        shape, sel = (m.n_layers, m.n_kv_heads, P, m.head_dim), (slice(None), slice(None), pos % P)
+                    else:
+                        shape, sel = (m.n_layers, m.n_kv_heads, m.head_dim, P), (Ellipsis, pos % P)
+                    a, r = a.reshape(shape)[sel], r.reshape(shape)[sel]
+                    t.reshape(shape)[sel] = True
+                    for l in range(m.n_layers):
+                        d = np.abs(a[l] - r[l])
+                        assert d.max() <= 1e-2 * np.abs(r[l]).max() + 1e-3, (pos, l, plane, float(d.max()))
         assert np.array_equal(gpu[~touched], self.pool0[~touched]), "a slot no step appended to changed"
 
     def close(self):
@@ -168,6 +174,13 @@ def _run(wl, steps, mode, stages):
 @pytest.mark.parametrize("mode", [0, 1])
 def test_layer1_b1_8k(mode):
     _run(configs.WORKLOADS["layer1_b1_8k"], 3, mode, stages=True)
+
+
+@pytest.mark.parametrize("name", ["layer1_b1_256k", "layer1_b4_64k", "layer1_b32_ragged"])
+def test_layer1_long_and_batched(name):
+    """The split-KV attention over 256K positions (more than 250 splits
+    merged), four 64K sequences, and 32 ragged sequences (two row tiles)."""
+    _run(configs.WORKLOADS[name], 2, 0, stages=False)
 
 
 def test_full48_b1_8k_megakernel():
