@@ -44,9 +44,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="full48_b1_8k")
     ap.add_argument("--batch-workload", default="full48_b32_ragged",
-                    help="second measured workload ('none' to skip)")
+                    help="second measured workload, reported under second_workload ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ab", action="store_true", help="skip the kernel-per-op comparison")
+    ap.add_argument("--op-trace", default=None, metavar="PATH",
+                    help="after timing, trace one more megakernel step per task and write a per-opcode summary (markdown)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference for HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "megakernel_traffic.json"),
@@ -66,7 +68,7 @@ class Run:
         self.K, self.W = steps, warmup
         dev = torch.device("cuda:0")
         self.stream = torch.cuda.current_stream()
-        extra = runs * (warmup + steps) + 1
+        extra = runs * (warmup + steps) + 2
         self.bs = gen.make_batch(wl, extra_steps=extra)
         self.max_seq = int(self.bs.seq_lens.max()) + extra
         t0 = time.time()
@@ -141,7 +143,56 @@ class Run:
         torch.cuda.empty_cache()
 
 
-def measure(wl, steps, warmup, ab):
+OPNAMES = {1: "EMBED", 2: "QKV", 3: "ATTN (claimer)", 5: "O_PROJ", 6: "ROUTER (+TOPK)", 8: "MOE_UP (claimer)",
+           9: "MOE_DOWN (claimer)", 10: "LM_HEAD"}
+
+
+def op_trace(r, path):
+    """One traced megakernel step: per task its opcode, layer, workgroup and
+    device timestamps (start, dependencies satisfied, end); summarised per
+    opcode and, for two layers, as a phase timeline."""
+    import numpy as np
+    import torch
+
+    import moe_persistent_decode_amd as mk
+    r.dec.set_mode(mk.MODE_MEGAKERNEL)
+    info = r.dec.schedule_info(r.B, r.hint + r.done)
+    buf = torch.zeros((info.n_tasks, 8), dtype=torch.int32, device="cuda")
+    r.dec.set_task_trace(buf, info.n_tasks)
+    r.run(1)
+    r.dec.sync(r.stream)
+    r.dec.set_task_trace(None, 0)
+    tr = buf.cpu().numpy().astype(np.int64) & 0xffffffff
+    op, layer = tr[:, 0] & 0xff, (tr[:, 0] >> 8) & 0xff
+    t0 = tr[:, 1].min()
+    us = lambda k: (tr[:, k] - t0) / 100.0  # 100 MHz device clock
+    start, waited, end = us(1), us(2), us(5)
+    span = end.max()
+    lines = [f"# Per-opcode time of one decode step: {r.wl.name}", "",
+             f"One traced megakernel step (batch {r.B}); step span {span:.1f} us over {info.n_cus} workgroups.", "",
+             "| opcode | tasks | mean wait (us) | mean run after wait (us) | workgroup-time share |",
+             "|---|---:|---:|---:|---:|"]
+    busy = (end - start).sum()
+    for k in sorted(set(op.tolist())):
+        m = op == k
+        lines.append(f"| {OPNAMES.get(int(k), k)} | {int(m.sum())} | {(waited - start)[m].mean():.2f} | "
+                     f"{(end - waited)[m].mean():.2f} | {(end - start)[m].sum() / busy:.1%} |")
+    L = r.m.n_layers
+    for l in sorted({1, L // 4 + (3 - (L // 4) % 4) % 4, L - 1} & set(range(L))):
+        lines += ["", f"Layer {l} ({'full' if r.m.layer_window(l) == 0 else 'window'} attention): "
+                  "first dependency satisfied / median / last end (us from step start)", "",
+                  "| opcode | first waited | median waited | last end |", "|---|---:|---:|---:|"]
+        for k in (6, 2, 3, 8, 9, 5):
+            m = (layer == l) & (op == k)
+            if m.any():
+                lines.append(f"| {OPNAMES[k]} | {waited[m].min():.1f} | {np.median(waited[m]):.1f} | {end[m].max():.1f} |")
+    m = op == 10
+    lines += ["", f"LM head: first waited {waited[m].min():.1f} us, last end {end[m].max():.1f} us."]
+    open(path, "w").write("\n".join(lines) + "\n")
+    log(f"[bench] per-opcode trace written to {path}")
+
+
+def measure(wl, steps, warmup, ab, trace_path=None):
     import moe_persistent_decode_amd as mk
     r = Run(wl, steps, warmup, 2 if ab else 1)
     ms, first = r.timed(mk.MODE_MEGAKERNEL, record=True)
@@ -157,6 +208,8 @@ def measure(wl, steps, warmup, ab):
         res["kernel_per_op"] = {"ms_per_step": round(ms_op / r.K, 4), "tok_s": round(r.B * r.K / (ms_op / 1e3), 2),
                                 "megakernel_speedup": round(ms_op / ms, 3)}
         log(f"[bench] {wl.name} kernel-per-op: {ms_op / r.K:.3f} ms/step -> megakernel {ms_op / ms:.2f}x")
+    if trace_path:
+        op_trace(r, trace_path)
     bs = r.bs
     r.close()
     return res, bs
@@ -173,7 +226,7 @@ def main():
     from mkinputs import configs, gen
     torch.cuda.set_device(0)
     wl = configs.WORKLOADS[args.workload]
-    res, bs = measure(wl, args.steps, args.warmup, not args.no_ab)
+    res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace)
 
     # HBM bytes per launch from the committed counter profile, only while the
     # device code is the one that was profiled
@@ -215,7 +268,7 @@ def main():
         wb = configs.WORKLOADS[args.batch_workload]
         kb = max(8, args.steps // 4)
         rb, _ = measure(wb, kb, min(args.warmup, 4), False)
-        out["batch32"] = {"workload": wb.name, "batch": wb.batch, "lengths": rb["lens"], "steps": kb,
+        out["second_workload"] = {"workload": wb.name, "batch": wb.batch, "lengths": rb["lens"], "steps": kb,
                           "tok_s": round(rb["tok_s"], 2), "ms_per_step": round(rb["ms_per_step"], 4),
                           "achieved_gbs": round(rb["gbs"], 1), "frac": round(rb["gbs"] / PEAK_GBS, 4),
                           "algorithmic_bytes_per_launch": int(rb["bytes"]),

@@ -192,6 +192,7 @@ struct Smem {
   int ired[MK_WAVES];
   int flag;
   int claim;
+  int claim2;
   int old;                // value an arrival counter held before this workgroup's increment
   uint32_t t_waited;
   uint32_t t_mark[4];     // op-defined intermediate timestamps (e.g. inputs ready, computed)
@@ -218,10 +219,12 @@ __device__ __noinline__ void raise_error_w(uint32_t* err, uint32_t code, uint32_
 
 // Spin (thread 0) until ctr[c] >= tgt for each wait, or until another
 // workgroup raised an error, or until the time limit. Block-uniform result.
-__device__ __forceinline__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm) {
+// force: wait even in the kernel-per-op variant (for producers in the same launch).
+__device__ __forceinline__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm,
+                                              bool force = false) {
   if (threadIdx.x == 0) {
     int ok = ld_relaxed(&P.err[0]) == 0;
-    if (ok && P.waits_enabled) {
+    if (ok && (P.waits_enabled || force)) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       for (int i = 0; i < n && ok; ++i) {
         if (cs[i] < 0) continue;
@@ -254,8 +257,8 @@ __device__ __forceinline__ bool wait_task(const mk_params& P, const mk_task& t, 
   return wait_counters(P, t.wait_ctr, t.wait_tgt, 3, sm);
 }
 
-__device__ __forceinline__ bool wait_one(const mk_params& P, int32_t c, int32_t tgt, Smem& sm) {
-  return wait_counters(P, &c, &tgt, 1, sm);
+__device__ __forceinline__ bool wait_one(const mk_params& P, int32_t c, int32_t tgt, Smem& sm, bool force = false) {
+  return wait_counters(P, &c, &tgt, 1, sm, force);
 }
 
 __device__ __forceinline__ int layer_window(const mk_params& P, int l) {
@@ -1139,12 +1142,15 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
 // A claimer's start in one round trip: the first claim of n items (thread 0;
 // the result in sm.claim), the route entries of the layer's active experts
 // and, with l >= 0, the sums of squares of layer l's input (then sm.inv_rms).
-__device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_ctr, int n, int l, Smem& sm) {
+__device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_ctr, int n, int l, Smem& sm,
+                                              int32_t claim2_ctr = -1) {
   const Pub R(P.route);
   const int E = P.E, B = P.B;
   const int i = threadIdx.x;
   int c = 0;
   if (i == 0) c = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (i == 64 && claim2_ctr >= 0)
+    sm.claim2 = (int)__hip_atomic_fetch_add(&P.ctr[claim2_ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i < 4) sm.rt_hdr[i] = R.ldi(i);
   if (i < E) {
     sm.rt_e[i] = R.ldi(4 + i);
@@ -1175,8 +1181,18 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
 // SiLU-and-multiply applied, by the down projection that consumes them.
 // Claims take several items at a time (their weights stream together); the
 // batch size spreads the queue over the claimers expected to be free.
-template <int MT, int NCH, int NBMAX>
-__device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, Smem& sm) {
+template <int MT, int NCH>
+__device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb, const WTile<4, NCH>& w,
+                                          Smem& sm);
+
+// The MoE claimer: expert up/gate items first, then down items. The first
+// down item is claimed at the start and its weights stream alongside the
+// up/gate weights, so they are resident when its expert's up/gate completes.
+//   a[0] up/gate claim counter, a[1] per-expert up/gate done counters,
+//   a[2] items per up/gate claim, a[3] down claim counter, a[4] column-block
+//   counters; sig_ctr[0]: the next layer's input counter.
+template <int MT, int NCH, int NBMAX, int NCHD>
+__device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
   const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
@@ -1187,9 +1203,24 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
   // expected to be free (any value is correct: claims continue until the
   // queue is empty)
   const int nb = min(NBMAX, max(1, t.a[2]));
-  claimer_start(P, claim_ctr, nb, l, sm);
+  claimer_start(P, claim_ctr, nb, l, sm, t.a[3]);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
+  const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
   int id0 = sm.claim;
+  int idd = sm.claim2;
+  // the first down item's weights (with one row tile; two row tiles of
+  // operands leave no registers for them, and they load after the up/gate
+  // items)
+  const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
+  const size_t pstride_d = (size_t)kcd * 512;
+  WTile<4, NCHD> wd;
+  if (MT == 1) {
+    const bool v = idd < n_down;
+    const int a = v ? idd / dpe : 0, cb = idd % dpe;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
+               v ? DP : 0, 0, kcd);
+  }
   // the layer input of every token over the whole K, once per claimer: each
   // item multiplies its expert's weights with all token rows (one tile of 16
   // rows costs the same for any count) and keeps the rows routed to it
@@ -1259,92 +1290,98 @@ __device__ __forceinline__ void op_moe_up(const mk_params& P, const mk_task& t, 
     first = false;
     id0 = next;
   }
+  if (MT != 1 && idd < n_down) {
+    const int a = idd / dpe, cb = idd % dpe;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0, kcd);
+  }
+  // down items: the next claim travels while the current item computes
+  while (idd < n_down) {
+    const int next = claim_n(P, t.a[3], 1, sm);
+    down_item<MT, NCHD>(P, t, idd / dpe, idd % dpe, wd, sm);
+    if (ld_relaxed(&P.err[0]) != 0) return;
+    idd = next;
+    if (idd < n_down) {
+      const int a = idd / dpe, cb = idd % dpe;
+      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+      wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0,
+                 kcd);
+    }
+  }
 }
 
-// Expert down over one column block for all tokens routed to the expert,
-// claiming (expert, block) items. Its weights stream before waiting for that
-// expert's up/gate items (megakernel post, section "What we have done
-// differently": MoE down streams weights while up/gate still computes the
-// hidden state it consumes).
+// Expert down over one column block for all tokens routed to expert slot a
+// (megakernel post, section "Tasks": MOE_DOWN_DRAIN). Its weights (w) were
+// loaded before this waits for that expert's up/gate items (section "What we
+// have done differently": MoE down streams weights while up/gate still
+// computes the hidden state it consumes). The contribution counts on the
+// column block; the last one does the residual add.
 template <int MT, int NCH>
-__device__ __forceinline__ void op_moe_down(const mk_params& P, const mk_task& t, Smem& sm) {
-  if (!wait_task(P, t, sm)) return;
-  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], blk_base = t.a[2];
+__device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb, const WTile<4, NCH>& w,
+                                          Smem& sm) {
   const int F = P.F, H = P.H, B = P.B;
   const int kc = F / 32;
-  const size_t pstride = (size_t)kc * 512;
   const int DP = P.CB / 16;
+  const int cnt = sm.rt_cnt[a];
   const Pub DN(P.dn), GU(P.gu);
-  claimer_start(P, claim_ctr, 1, -1, sm);
-  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
-  int id = sm.claim;
-  while (id < n_items) {
-    const int a = id / P.down_items_per_expert, cb = id % P.down_items_per_expert;
-    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    const int cnt = sm.rt_cnt[a];
-    WTile<4, NCH> w;
-    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride, pstride, DP, 0, kc);
-    // the next claim travels while the weights stream
-    const int next = claim_n(P, claim_ctr, 1, sm);
-    if (!wait_one(P, done_base + a, P.up_items_per_expert, sm)) return;
-    // act = silu(g0 + g1) * (u0 + u1) per routed row, staged in LDS as the
-    // split pair (16 rows at a time: hi in act[0, 16F), lo in act[16F, 32F))
-    Acc<4, MT> acc;
+  // the up/gate items may run in this same launch (kernel-per-op variant too)
+  if (!wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
+  // act = silu(g0 + g1) * (u0 + u1) per routed row, staged in LDS as the
+  // split pair (16 rows at a time: hi in act[0, 16F), lo in act[16F, 32F))
+  Acc<4, MT> acc;
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
+  for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc.c[pp][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc.c[pp][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int n = 16 * F;
-      for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
-        float g[4][4];
+  for (int mt = 0; mt < MT; ++mt) {
+    const int n = 16 * F;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
+      float g[4][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int i = i0 + k * MK_WG_THREADS, row = mt * 16 + i / F, f = i % F;
-          const bool live = i < n && row < cnt;
-          const int slot = live ? sm.rt_slot[a * B + row] : 0;
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * MK_WG_THREADS, row = mt * 16 + i / F, f = i % F;
+        const bool live = i < n && row < cnt;
+        const int slot = live ? sm.rt_slot[a * B + row] : 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
-        }
+        for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int i = i0 + k * MK_WG_THREADS;
-          if (i < n) {
-            const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
-            split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[n + i]);
-          }
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * MK_WG_THREADS;
+        if (i < n) {
+          const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
+          split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[n + i]);
         }
       }
-      __syncthreads();
-      const int wv = wave_id(), ln = lane_id();
+    }
+    __syncthreads();
+    const int wv = wave_id(), ln = lane_id();
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int c = wv + MK_WAVES * i;
-        const int off = (ln & 15) * F + 32 * c + 8 * (ln >> 4);
-        const u32x4_t ah = c < kc ? *(const u32x4_t*)(sm.act + off) : u32x4_t{0u, 0u, 0u, 0u};
-        const u32x4_t al = c < kc ? *(const u32x4_t*)(sm.act + n + off) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NCH; ++i) {
+      const int c = wv + MK_WAVES * i;
+      const int off = (ln & 15) * F + 32 * c + 8 * (ln >> 4);
+      const u32x4_t ah = c < kc ? *(const u32x4_t*)(sm.act + off) : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t al = c < kc ? *(const u32x4_t*)(sm.act + n + off) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
-                                                                  __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
-                                                                  acc.c[pp][mt], 0, 0, 0);
-          acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
-                                                                  __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
-                                                                  acc.c[pp][mt], 0, 0, 0);
-        }
+      for (int pp = 0; pp < 4; ++pp) {
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                                __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                acc.c[pp][mt], 0, 0, 0);
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                                __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                acc.c[pp][mt], 0, 0, 0);
       }
-      __syncthreads();
     }
-    reduce_tiles(acc, sm);
-    for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
-      const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
-      const int row = mt * 16 + m;
-      if (pp < DP && row < cnt) DN.stf(sm.rt_slot[a * B + row] * H + (cb * DP + pp) * 16 + nn, sm.out[o]);
-    }
-    block_arrive(P, t, blk_base, cb, sm);
-    id = next;
+    __syncthreads();
   }
+  reduce_tiles(acc, sm);
+  for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int row = mt * 16 + m;
+    if (pp < DP && row < cnt) DN.stf(sm.rt_slot[a * B + row] * H + (cb * DP + pp) * 16 + nn, sm.out[o]);
+  }
+  block_arrive(P, t, t.a[4], cb, sm);
 }
 
 // ----------------------------------------------------------------- LM head
@@ -1466,8 +1503,7 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
     case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe_up<MT, 32 / MK_WAVES, MT == 1 ? 3 : 1>(P, t, sm); break;
-    case MK_OP_MOE_DOWN: op_moe_down<MT, 24 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_MOE_UP: op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm); break;
     case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
     default: wait_task(P, t, sm); break;
   }

@@ -375,18 +375,11 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
       const int n_free = std::max(1, S->n_up_claimers - n_attn);
       t.a[2] = std::max(1, (int)std::ceil(e_act * 2 * c.expert_ffn / 16 / n_free));
-      add_wait(t, x.route, 1);
-      push(t);
-    }
-    // MoE down claimers (their last block contribution does the residual)
-    begin_wave();
-    for (int i = 0; i < S->n_down_claimers; ++i) {
-      mk_task t = make_task(MK_OP_MOE_DOWN, l);
-      t.a[0] = x.down_claim;
-      t.a[1] = x.up_done;
-      t.a[2] = x.colblk;
-      add_wait(t, x.route, 1);
+      // then the down items (their last block contribution does the residual)
+      t.a[3] = x.down_claim;
+      t.a[4] = x.colblk;
       t.sig_ctr[0] = resid(l + 1);
+      add_wait(t, x.route, 1);
       push(t);
     }
     // O projection per (group, column block)
@@ -437,7 +430,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
 // the last-arrival actions, with CUs advancing in a seeded random order.
 struct SimCU {
   bool in_claimer = false;
-  int pending_item = -1;  // claimed down item waiting for its expert's up items
+  int pending_item = -1;  // claimed item waiting for its dependency
+  int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items
   int pos = 0;
 };
 
@@ -507,8 +501,8 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
             break;
           case MK_OP_ATTN:
           case MK_OP_MOE_UP:
-          case MK_OP_MOE_DOWN:
             u.in_claimer = true;
+            u.phase = 0;
             progress = true;
             break;
           default:
@@ -538,17 +532,17 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
             progress = true;
           }
         }
-      } else if (t.op == MK_OP_MOE_UP) {
+      } else if (u.phase == 0) {  // MoE claimer, up/gate items
         const int id = (int)ctr[t.a[0]]++;
+        progress = true;
         if (id >= na * up_per_e) {
-          u.in_claimer = false;
-          done();
+          u.phase = 1;
+          u.pending_item = -1;
         } else {
           ctr[t.a[1] + id / up_per_e]++;
-          progress = true;
         }
-      } else if (u.pending_item < 0) {
-        const int id = (int)ctr[t.a[0]]++;
+      } else if (u.pending_item < 0) {  // MoE claimer, down items
+        const int id = (int)ctr[t.a[3]]++;
         progress = true;
         if (id >= na * down_per_e) {
           u.in_claimer = false;
@@ -559,7 +553,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       } else {
         const int a = u.pending_item / down_per_e, cb = u.pending_item % down_per_e;
         if (ctr[t.a[1] + a] >= up_per_e) {
-          block(t, t.a[2], cb, l);
+          block(t, t.a[4], cb, l);
           u.pending_item = -1;
           progress = true;
         }
@@ -586,7 +580,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     want[k++] = 1;                                                   // route finalized
     want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
     want[k++] = (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
-    want[k++] = (int64_t)n_active[l] * down_per_e + S.n_down_claimers;
+    want[k++] = (int64_t)n_active[l] * down_per_e + S.n_up_claimers;
     for (int a = 0; a < E; ++a) want[k++] = a < n_active[l] ? up_per_e : 0;
     for (int cb = 0; cb < NB; ++cb) want[k++] = KVH + n_active[l];
   }

@@ -40,8 +40,8 @@ enum mk_opcode : int32_t {
   MK_OP_ATTN = 3,         // split-KV partial attention (+ combine when last)
   MK_OP_OPROJ = 5,        // O projection, split-K by kv group, one column block (+ residual when last)
   MK_OP_ROUTER = 6,       // router logits over a K range (+ top-k / finalize when last)
-  MK_OP_MOE_UP = 8,       // claimer over (expert, gate/up panel pair, K half) items
-  MK_OP_MOE_DOWN = 9,     // claimer over (expert, column block) items (+ residual when last)
+  MK_OP_MOE_UP = 8,       // MoE claimer: (expert, gate/up panel pair, K half) items, then
+                          // (expert, column block) down items (+ residual when last)
   MK_OP_LMHEAD = 10,      // LM head panels + argmax candidate (+ greedy token when last)
   MK_OP_COUNT = 11
 };
