@@ -57,7 +57,7 @@ typedef enum { MK_MODE_MEGAKERNEL = 0, MK_MODE_KERNEL_PER_OP = 1 } mk_mode;
 typedef struct {
   int32_t hidden;          /* H, a multiple of 256, <= 2048 */
   int32_t n_q_heads;       /* QH */
-  int32_t n_kv_heads;      /* KVH <= 16, divides QH; QH / KVH <= 16, (QH / KVH) * D <= 1024 */
+  int32_t n_kv_heads;      /* KVH <= 8, divides QH; QH / KVH <= 16, (QH / KVH) * D <= 1024 */
   int32_t head_dim;        /* D: 64 or 128 */
   int32_t n_experts;       /* E, a multiple of 8, <= 128 */
   int32_t top_k;           /* k <= 8 */

@@ -93,6 +93,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
 }
 constexpr int kSC1 = 16;  // cache-policy bit: device (agent) scope coherence
+constexpr int kNT = 2;    // cache-policy bit: non-temporal (streamed once)
 
 // Device-coherent access to a buffer shared across compute units.
 struct Pub {
@@ -118,6 +119,9 @@ struct Pub {
   }
   __device__ __forceinline__ void st16(int i, uint16_t v) const {  // i: 16-bit element index
     __builtin_amdgcn_raw_buffer_store_b16(v, r, i * 2, 0, kSC1);
+  }
+  __device__ __forceinline__ void st16x4(int i, u32x2_t v) const {  // 4 bf16 at 16-bit index i (8-byte aligned)
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, i * 2, 0, kSC1);
   }
   __device__ __forceinline__ u32x4_t ld16x8(int i) const {  // 8 bf16 at 16-bit index i
     return __builtin_amdgcn_raw_buffer_load_b128(r, i * 2, 0, kSC1);
@@ -157,6 +161,7 @@ struct SmemComb {
   float l[MK_MAX_SPLITS][16];
   float M[16];
   float L[16];
+  alignas(16) float4 part[MK_WG_THREADS];  // per thread partition: partial sums of 4 outputs
 };
 
 struct SmemTopk {
@@ -194,6 +199,7 @@ struct Smem {
   int claim;
   int claim2;
   int old;                // value an arrival counter held before this workgroup's increment
+  int t_old[2];
   uint32_t t_waited;
   uint32_t t_mark[4];     // op-defined intermediate timestamps (e.g. inputs ready, computed)
   int rt_hdr[4];          // route header: n_active, up items, down items
@@ -223,15 +229,21 @@ __device__ __noinline__ void raise_error_w(uint32_t* err, uint32_t code, uint32_
 __device__ __forceinline__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm,
                                               bool force = false) {
   if (threadIdx.x == 0) {
+    const bool active = P.waits_enabled || force;
+    // the first reading of every counter and the error word in one round trip
+    uint32_t v[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) v[i] = (i < n && active && cs[i] >= 0) ? ld_relaxed(P.ctr + cs[i]) : 0xffffffffu;
     int ok = ld_relaxed(&P.err[0]) == 0;
-    if (ok && (P.waits_enabled || force)) {
+    if (ok && active) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      for (int i = 0; i < n && ok; ++i) {
-        if (cs[i] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        if (i >= n || !ok || cs[i] < 0) continue;
         const uint32_t* c = P.ctr + cs[i];
         const uint32_t tgt = (uint32_t)ts[i];
         uint32_t spins = 0;
-        while (ld_relaxed(c) < tgt) {
+        for (uint32_t x = v[i]; x < tgt; x = ld_relaxed(c)) {
           __builtin_amdgcn_s_sleep(2);
           if ((++spins & 63u) == 0) {
             if (ld_relaxed(&P.err[0]) != 0) { ok = 0; break; }
@@ -348,20 +360,23 @@ struct WTile {
   u32x4_t v[NP][NCH];
 };
 
-// Chunks outside [c0, c1) and panels at or beyond np are zero.
+// Chunks outside [c0, c1) and panels at or beyond np are zero. The loads go
+// through one buffer resource over the np panels, a chunk outside the range
+// reading past its end (which returns zeros): no branches, so the compiler
+// counts the loads in flight exactly and waits only for the ones it uses.
 template <int NP, int NCH>
 __device__ __forceinline__ void wtile_load(WTile<NP, NCH>& w, const uint16_t* base, size_t pstride,
                                            int np, int c0, int c1) {
   const int wv = wave_id(), ln = lane_id();
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, np * (int)pstride * 2, 0x00020000);
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = c0 + wv + MK_WAVES * i;
-      if (pp < np && c < c1)
-        w.v[pp][i] = __builtin_nontemporal_load((const u32x4_t*)(base + pp * pstride + (size_t)c * 512) + ln);
-      else
-        w.v[pp][i] = u32x4_t{0u, 0u, 0u, 0u};
+      const int off = (pp < np && c < c1) ? (pp * (int)pstride + c * 512) * 2 + ln * 16 : 0x7ffffff0;
+      w.v[pp][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
     }
 }
 
@@ -750,59 +765,71 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
   mark(sm, 2);
   const size_t dst_off = (size_t)b * P.QH * D + (size_t)g * G * D;
   const Pub dst_h(o_of(P, 0) + dst_off), dst_l(o_of(P, 1) + dst_off);
-  // each thread's outputs (G * D <= 1024: at most two) over up to 32 splits
-  // at a time, every load in flight together
-  constexpr int NO = 1024 / MK_WG_THREADS, SB = 32;
-  float O[NO];
+  // 16-byte loads: a split's G * D outputs are GD4 groups of four; the
+  // workgroup forms NP partitions of GD4 threads, partition p taking splits
+  // p, p + NP, ..., up to SB of them in flight at a time
+  const int GD4 = G * D / 4, NP = MK_WG_THREADS / GD4;
+  const int part = threadIdx.x / GD4, j = threadIdx.x % GD4, hh = 4 * j / D;
+  constexpr int SB = MK_COMB_SB;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (part < NP) {
+    for (int s0 = part; s0 < ns; s0 += NP * SB) {
+      float4 v[SB];
 #pragma unroll
-  for (int u = 0; u < NO; ++u) O[u] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += SB) {
-    float v[NO][SB];
+      for (int k = 0; k < SB; ++k) {
+        const int s = s0 + k * NP;
+        v[k] = s < ns ? src.ldf4(s * stride + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
-    for (int u = 0; u < NO; ++u) {
-      const int idx = threadIdx.x + u * MK_WG_THREADS;
-      const int hh = idx / D, dd = idx % D;
-#pragma unroll
-      for (int k = 0; k < SB; ++k)
-        v[u][k] = (idx < G * D && s0 + k < ns) ? src.ldf((s0 + k) * stride + hh * D + dd) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < NO; ++u) {
-      const int idx = threadIdx.x + u * MK_WG_THREADS;
-      const int hh = min(idx / D, G - 1);
-#pragma unroll
-      for (int k = 0; k < SB; ++k)
-        if (s0 + k < ns) O[u] = fmaf(C.f[s0 + k][hh], v[u][k], O[u]);
+      for (int k = 0; k < SB; ++k) {
+        const int s = s0 + k * NP;
+        if (s < ns) {
+          const float f = C.f[s][hh];
+          O.x = fmaf(f, v[k].x, O.x);
+          O.y = fmaf(f, v[k].y, O.y);
+          O.z = fmaf(f, v[k].z, O.z);
+          O.w = fmaf(f, v[k].w, O.w);
+        }
+      }
     }
   }
-#pragma unroll
-  for (int u = 0; u < NO; ++u) {
-    const int idx = threadIdx.x + u * MK_WG_THREADS;
-    // the O projection's matrix-core operand, as a split pair
-    if (idx < G * D) {
-      uint16_t hi, lo;
-      split_bf16(O[u] / C.L[idx / D], hi, lo);
-      dst_h.st16(idx, hi);
-      dst_l.st16(idx, lo);
+  C.part[threadIdx.x] = O;
+  __syncthreads();
+  if (threadIdx.x < GD4) {
+    float4 t = C.part[threadIdx.x];
+    for (int q = 1; q < NP; ++q) {
+      const float4 u = C.part[q * GD4 + threadIdx.x];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
     }
+    // the O projection's matrix-core operand, as a split pair
+    const float inv = 1.f / C.L[hh];
+    const float r[4] = {t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+    uint16_t h[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16(r[i], h[i], lo[i]);
+    dst_h.st16x4(4 * j, u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)});
+    dst_l.st16x4(4 * j, u32x2_t{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)});
   }
 }
 
 // ---------------------------------------------------------------- embed
 // Layer 0's input for one column block: h = Emb[token] for every sequence,
 // u = bf16(h * gamma_0) and the block's per-token sum of squares.
-__device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv, int n,
-                                                  Smem& sm);
+__device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv,
+                                                  const float* gv, int n, Smem& sm);
 
 __device__ __forceinline__ void op_embed(const mk_params& P, const mk_task& t, Smem& sm) {
   const int cb = t.a[0];
   const int H = P.H, CB = P.CB, n = P.B * CB;
   constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;  // elements per thread (CB <= 64)
-  float hv[NI];
+  float hv[NI], gv[NI];
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
     const int idx = threadIdx.x + k * MK_WG_THREADS;
-    hv[k] = 0.f;
+    hv[k] = gv[k] = 0.f;
     if (idx < n) {
       const int b = idx / CB, c = cb * CB + idx % CB;
       int tok = P.tokens[b];
@@ -811,21 +838,22 @@ __device__ __forceinline__ void op_embed(const mk_params& P, const mk_task& t, S
         tok = 0;
       }
       hv[k] = bf2f(P.emb[(size_t)tok * H + c]);
+      gv[k] = bf2f(P.gamma[c]);
     }
   }
-  write_block_input(P, 0, cb, hv, n, sm);
+  write_block_input(P, 0, cb, hv, gv, n, sm);
   arrive_nr(P, t.sig_ctr[0]);
 }
 
 // Store the residual stream of column block cb (hv[k] = element idx =
 // threadIdx.x + k * 512 of the block, row idx / CB), the next layer's input
-// u = bf16(h * gamma_{l_next}) and the block's per-token sum of squares.
-__device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv, int n,
-                                                  Smem& sm) {
+// u = bf16(h * gamma_{l_next}) (gv[k]: the element's gamma) and the block's
+// per-token sum of squares.
+__device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv,
+                                                  const float* gv, int n, Smem& sm) {
   const int H = P.H, CB = P.CB;
   constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;
   const Pub h(P.h), Uh(u_of_w(P, l_next, 0)), Ul(u_of_w(P, l_next, 1));
-  const uint16_t* gam = P.gamma + (size_t)l_next * H;
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
     const int idx = threadIdx.x + k * MK_WG_THREADS;
@@ -833,7 +861,7 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
       const int b = idx / CB, c = cb * CB + idx % CB;
       h.stf(b * H + c, hv[k]);
       uint16_t hi, lo;
-      split_bf16(hv[k] * bf2f(gam[c]), hi, lo);
+      split_bf16(hv[k] * gv[k], hi, lo);
       Uh.st16(b * H + c, hi);
       Ul.st16(b * H + c, lo);
       sm.out[idx] = hv[k] * hv[k];
@@ -919,18 +947,19 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
 // token, the experts summed in rank order (MOE_COMBINE), then the next
 // layer's input u and the block's sums of squares (the fused residual add +
 // RMSNorm of the megakernel post, section "Reduce wave quantization").
+// The routing weights are in sm.tkw.
 __device__ __forceinline__ void residual_block(const mk_params& P, int l, int cb, Smem& sm) {
   const int H = P.H, K = P.K, CB = P.CB, B = P.B, n = B * CB;
   constexpr int NI = MK_MAX_BATCH * 64 / MK_WG_THREADS;
-  const Pub h(P.h), ao(P.ao), dn(P.dn), tkw(P.tk_w);
-  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) sm.tkw[i] = tkw.ldf(i);
-  __syncthreads();
-  float hv[NI];
+  const Pub h(P.h), ao(P.ao), dn(P.dn);
+  const uint16_t* gam = P.gamma + (size_t)(l + 1) * H;
+  float hv[NI], gv[NI];
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
     const int idx = threadIdx.x + k * MK_WG_THREADS;
-    hv[k] = 0.f;
+    hv[k] = gv[k] = 0.f;
     if (idx < n) {
+      gv[k] = bf2f(gam[cb * CB + idx % CB]);
       const int b = idx / CB, c = cb * CB + idx % CB;
       // every load in flight before the sums (fixed order: groups, then ranks)
       float av[MK_MAX_KVH], yv[MK_MAX_TOPK];
@@ -950,18 +979,28 @@ __device__ __forceinline__ void residual_block(const mk_params& P, int l, int cb
       hv[k] = (h0 + a) + y;
     }
   }
-  write_block_input(P, l + 1, cb, hv, n, sm);
+  write_block_input(P, l + 1, cb, hv, gv, n, sm);
 }
 
 // After a contribution to column block cb: the last of the block's
 // KVH + n_active contributions does the residual and signals the next layer.
+// The arrival, the active-expert count and the routing weights travel in one
+// round trip.
 __device__ __forceinline__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base, int cb, Smem& sm) {
-  const int n_active = __builtin_amdgcn_readfirstlane(Pub(P.route).ldi(0));
-  const int old = arrive(P, ctr_base + cb, sm);
+  sync_published();
+  const int i = threadIdx.x;
+  if (i == 0) sm.old = (int)__hip_atomic_fetch_add(&P.ctr[ctr_base + cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (i == 64) sm.t_old[0] = Pub(P.route).ldi(0);
+  const float w = i < P.B * P.K ? Pub(P.tk_w).ldf(i) : 0.f;  // B * K <= 512
+  __syncthreads();
+  const int old = sm.old, n_active = sm.t_old[0];
   if (old == P.KVH + n_active - 1) {
+    if (i < P.B * P.K) sm.tkw[i] = w;
+    __syncthreads();
     residual_block(P, t.layer, cb, sm);
     arrive_nr(P, t.sig_ctr[0]);
   }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ O proj
@@ -1140,7 +1179,7 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
 }
 
 // A claimer's start in one round trip: the first claim of n items (thread 0;
-// the result in sm.claim), the route entries of the layer's active experts
+// the result in sm.claim; none with claim_ctr < 0), the route entries of the layer's active experts
 // and, with l >= 0, the sums of squares of layer l's input (then sm.inv_rms).
 __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_ctr, int n, int l, Smem& sm,
                                               int32_t claim2_ctr = -1) {
@@ -1148,7 +1187,8 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
   const int E = P.E, B = P.B;
   const int i = threadIdx.x;
   int c = 0;
-  if (i == 0) c = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (i == 0 && claim_ctr >= 0)
+    c = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i == 64 && claim2_ctr >= 0)
     sm.claim2 = (int)__hip_atomic_fetch_add(&P.ctr[claim2_ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i < 4) sm.rt_hdr[i] = R.ldi(i);
@@ -1157,6 +1197,7 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
     sm.rt_cnt[i] = R.ldi(4 + E + i);
   }
   for (int k = i; k < E * B; k += MK_WG_THREADS) sm.rt_slot[k] = R.ldi(4 + 2 * E + k);
+  if (i < B * P.K) sm.tkw[i] = Pub(P.tk_w).ldf(i);
   if (l >= 0) {
     const Pub S(ssq_of(P, l));
     for (int k = i; k < B * P.NB; k += MK_WG_THREADS) sm.ssq[k] = S.ldf(k);
@@ -1308,6 +1349,207 @@ __device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Sme
                  kcd);
     }
   }
+}
+
+// Two adjacent column blocks (cb0, cb0 + 1) of one expert's down projection
+// for at most 16 routed tokens, each block's weights already in registers.
+// stage: build the expert's SiLU-and-multiply operand in LDS first (after its
+// up/gate items completed); otherwise the operand of the previous pair, the
+// same expert, is reused. Each block's arrival may complete its residual.
+template <int NCH>
+__device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, int a, int cb0,
+                                          const WTile<4, NCH>& w0, const WTile<4, NCH>& w1, bool stage, Smem& sm) {
+  const int F = P.F, H = P.H, B = P.B;
+  const int kc = F / 32;
+  const int DP = P.CB / 16;
+  const int cnt = sm.rt_cnt[a];
+  const Pub DN(P.dn), GU(P.gu);
+  if (stage) {
+    if (!wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
+    const int n = 16 * F;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
+      float g[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * MK_WG_THREADS, row = i / F, f = i % F;
+        const bool live = i < n && row < cnt;
+        const int slot = live ? sm.rt_slot[a * B + row] : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * MK_WG_THREADS;
+        if (i < n) {
+          const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
+          split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[n + i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  Acc<8, 1> acc;
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) acc.c[pp][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wv = wave_id(), ln = lane_id(), n = 16 * F;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = wv + MK_WAVES * i;
+    const int off = (ln & 15) * F + 32 * c + 8 * (ln >> 4);
+    const u32x4_t ah = c < kc ? *(const u32x4_t*)(sm.act + off) : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t al = c < kc ? *(const u32x4_t*)(sm.act + n + off) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const u32x4_t wv4 = pp < 4 ? w0.v[pp][i] : w1.v[pp - 4][i];
+      acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                             __builtin_bit_cast(bf16x8_t, wv4), acc.c[pp][0], 0, 0, 0);
+      acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                             __builtin_bit_cast(bf16x8_t, wv4), acc.c[pp][0], 0, 0, 0);
+    }
+  }
+  reduce_tiles(acc, sm);
+  for (int o = threadIdx.x; o < 8 * 256; o += MK_WG_THREADS) {
+    const int pp = o / 256, m = (o / 16) % 16, nn = o % 16;
+    const int cb = cb0 + pp / 4, p4 = pp % 4;
+    if (p4 < DP && m < cnt) DN.stf(sm.rt_slot[a * B + m] * H + (cb * DP + p4) * 16 + nn, sm.out[o]);
+  }
+  // both blocks' arrivals in one round trip
+  sync_published();
+  if (threadIdx.x < 2)
+    sm.t_old[threadIdx.x] = (int)__hip_atomic_fetch_add(&P.ctr[t.a[4] + cb0 + threadIdx.x], 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int last = P.KVH + __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) - 1;
+  const int o0 = sm.t_old[0], o1 = sm.t_old[1];
+  __syncthreads();
+  if (o0 == last) {
+    residual_block(P, t.layer, cb0, sm);
+    arrive_nr(P, t.sig_ctr[0]);
+  }
+  if (o1 == last) {
+    residual_block(P, t.layer, cb0 + 1, sm);
+    arrive_nr(P, t.sig_ctr[0]);
+  }
+}
+
+// The MoE claimer with fixed shares (at most 16 tokens): claimer k of n takes
+// up/gate items [k N / n, (k + 1) N / n) of the layer's N and down column-block
+// pairs likewise, so the shares are even and no claim round trips to a shared
+// counter sit on the path. The activation operand loads as soon as the layer
+// input is complete, while the route is still pending; up/gate weights stream
+// two items deep; the first down block's weights stream from the start.
+//   b[0], b[1]: this claimer's index among the claimers on compute units
+//   without attention work in this layer, and their count (b[0] < 0: none for
+//   this claimer); b[2], b[3]: its index among all claimers, and their count
+//   (used in the kernel-per-op variant, where attention ran before);
+//   wait_ctr[0]: the layer input, wait_ctr[1]: the route; the other
+//   arguments as for the claiming variant.
+template <int NCH, int NCHD>
+__device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int sk = P.waits_enabled ? t.b[0] : t.b[2], sn = P.waits_enabled ? t.b[1] : t.b[3];
+  if (sk < 0) return;
+  const int l = t.layer, done_base = t.a[1];
+  const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
+  const int kc = P.H / 32, kh_chunks = kc / 2;
+  const size_t pstride = (size_t)kc * 512;
+  const Pub GU(P.gu);
+  if (!wait_one(P, t.wait_ctr[0], t.wait_tgt[0], sm)) return;
+  set_rows_batch(P, sm, 0, P.H, 0);
+  __syncthreads();
+  ATile<1, NCH> Ah0, Al0, Ah1, Al1;
+  atile_load_bf16(Ah0, Pub(u_of(P, l, 0)), sm.row_off[0], 0, kh_chunks);
+  atile_load_bf16(Al0, Pub(u_of(P, l, 1)), sm.row_off[0], 0, kh_chunks);
+  atile_load_bf16(Ah1, Pub(u_of(P, l, 0)), sm.row_off[0], kh_chunks, kc);
+  atile_load_bf16(Al1, Pub(u_of(P, l, 1)), sm.row_off[0], kh_chunks, kc);
+  if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
+  claimer_start(P, -1, 0, l, sm);
+  mark(sm, 0);
+  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
+  const int n_pairs = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]) / 2;
+  const int lo = (int)((int64_t)sk * n_items / sn), hi = (int)((int64_t)(sk + 1) * n_items / sn);
+  const int plo = (int)((int64_t)sk * n_pairs / sn), phi = (int)((int64_t)(sk + 1) * n_pairs / sn);
+  const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
+  const size_t pstride_d = (size_t)kcd * 512;
+  auto down_load = [&](WTile<4, NCHD>& w, int item, bool valid) {
+    const int a = valid ? item / dpe : 0, cb = item % dpe;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
+               valid ? DP : 0, 0, kcd);
+  };
+  WTile<4, NCHD> wd0;
+  down_load(wd0, 2 * plo, plo < phi);
+  auto up_load = [&](WTile<2, NCH>& w, int id) {
+    const bool valid = id < hi;
+    const int a = valid ? id / upe : 0, r = id % upe;
+    const int tt = r >> 1, kh = r & 1;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    const int c0 = kh * kh_chunks;
+    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
+               valid ? 2 : 0, c0, c0 + kh_chunks);
+  };
+  auto up_do = [&](const WTile<2, NCH>& w, int id) {
+    const int a = id / upe, r = id % upe;
+    const int tt = r >> 1, kh = r & 1;
+    const int cnt = sm.rt_cnt[a];
+    // this K half's operand (a bitwise blend: a select between the two tiles
+    // would be turned into a dynamically indexed array in scratch)
+    ATile<1, NCH> Hh, Hl;
+    const uint32_t hi_half = 0u - (uint32_t)kh;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      Hh.a[0][i] = (Ah1.a[0][i] & hi_half) | (Ah0.a[0][i] & ~hi_half);
+      Hl.a[0][i] = (Al1.a[0][i] & hi_half) | (Al0.a[0][i] & ~hi_half);
+    }
+    Acc<2, 1> acc;
+    mfma_tiles(acc, w, Hh, Hl);
+    reduce_tiles(acc, sm);
+    // gu[slot][kh][gate|up][F] for the tokens routed to the expert: at most
+    // 2 x 16 x 16 values, one per thread
+    const int o = threadIdx.x;
+    if (o < 2 * cnt * 16) {
+      const int which = o / (cnt * 16), rr = (o / 16) % cnt, nn = o % 16;
+      const int slot = sm.rt_slot[a * B + rr], b = slot / K;
+      GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, sm.out[which * 256 + b * 16 + nn] * sm.inv_rms[b]);
+    }
+  };
+  {
+    WTile<2, NCH> w0, w1;
+    up_load(w0, lo);
+    up_load(w1, lo + 1);
+    for (int id = lo; id < hi; id += 2) {
+      up_do(w0, id);
+      if (id + 2 < hi) up_load(w0, id + 2);
+      if (id + 1 < hi) up_do(w1, id + 1);
+      if (id + 3 < hi) up_load(w1, id + 3);
+    }
+  }
+  mark(sm, 1);
+  // the second down block's weights, then this share's up/gate arrivals
+  // (one per item, on its expert's counter)
+  WTile<4, NCHD> wd1;
+  down_load(wd1, 2 * plo + 1, plo < phi);
+  sync_published();
+  if (lo < hi) {
+    const int a0 = lo / upe, a1 = (hi - 1) / upe;
+    const int a = a0 + (int)threadIdx.x;
+    if (a <= a1) {
+      const int n = min(hi, (a + 1) * upe) - max(lo, a * upe);
+      __hip_atomic_fetch_add(&P.ctr[done_base + a], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  mark(sm, 2);
+  int staged = -1;
+  for (int p = plo; p < phi; ++p) {
+    const int a = (2 * p) / dpe, cb0 = (2 * p) % dpe;
+    if (p > plo) {
+      down_load(wd0, 2 * p, true);
+      down_load(wd1, 2 * p + 1, true);
+    }
+    down_pair<NCHD>(P, t, a, cb0, wd0, wd1, a != staged, sm);
+    staged = a;
+    if (ld_relaxed(&P.err[0]) != 0) return;
+  }
+  mark(sm, 3);
 }
 
 // Expert down over one column block for all tokens routed to expert slot a
@@ -1503,7 +1745,12 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
     case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
-    case MK_OP_MOE_UP: op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_MOE_UP:
+      if (MT == 1 && t.b[1] > 0)
+        op_moe_static<32 / MK_WAVES, 24 / MK_WAVES>(P, t, sm);
+      else
+        op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm);
+      break;
     case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
     default: wait_task(P, t, sm); break;
   }
@@ -1525,9 +1772,20 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
   __syncthreads();
   const int beg = P.task_off[blockIdx.x], end = P.task_off[blockIdx.x + 1];
   for (int i = beg; i < end; ++i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the descriptor through a constant-address-space pointer: its fields are
+    // then read with scalar loads, batched, instead of one vector load per
+    // field on the way into each wait
+    typedef const __attribute__((address_space(4))) mk_task* ktask_ptr;
+    const mk_task& t = *(const mk_task*)((ktask_ptr)P.tasks + i);
+#else
     const mk_task& t = P.tasks[i];
+#endif
     const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
-    if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
+    if (threadIdx.x == 0) {
+      sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
+      sm.t_waited = t0;  // a task without waits
+    }
     // The parameter block through an opaque copy of its (constant address
     // space) pointer per task: parameter fields are then loaded inside each op
     // with scalar loads instead of being hoisted out of the task loop and held

@@ -39,6 +39,7 @@ struct Schedule {
   int n_router = 0, n_oproj = 0, n_up_claimers = 0, n_down_claimers = 0, n_lm = 0;
   std::vector<int> n_qkv;  // QKV tasks per kv group
   std::vector<int> n_attn_claimers;  // per layer
+  std::vector<int> moe_fixed;        // per layer: MoE claimers with fixed shares
   int n_ctr = 0;
   // counter layout
   int c_resid0 = 0, c_lm = 0, c_layer0 = 0, c_per_layer = 0;
@@ -224,7 +225,18 @@ int window_of(const mk_config& c, int l) {
 int pps_for(const mk_handle* h, int B, int len) {
   const int pages = ceil_div(len, h->cfg.page_size) + 1;
   const int target = std::max(1, 2 * h->n_workers / (B * h->cfg.n_kv_heads));
-  return std::max(h->pps, ceil_div(pages, target));
+  int pps = std::max(h->pps, ceil_div(pages, target));
+  // The combine merges up to `cap` splits per round trip to memory; when the
+  // split count just passes a multiple of it, splits up to 1/8 longer save
+  // that round trip.
+  const int gd4 = h->cfg.n_q_heads / h->cfg.n_kv_heads * h->cfg.head_dim / 4;
+  const int cap = std::max(1, MK_WG_THREADS / gd4) * MK_COMB_SB;
+  const int rounds = ceil_div(ceil_div(pages, pps), cap);
+  if (rounds > 1) {
+    const int p1 = ceil_div(pages, (rounds - 1) * cap);
+    if (8 * p1 <= 9 * pps) pps = p1;
+  }
+  return pps;
 }
 
 // Number of attention splits for a layer when sequences are at most `len` long.
@@ -350,6 +362,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       S->n_splits_full = ns;
     // claimers over the (sequence, group, split) queue
     const int n_attn_items = B * KVH * ns;
+    const int attn_flat0 = (int)S->flat.size();
     S->n_attn_claimers.push_back(std::min(n_w, n_attn_items));
     for (int i = 0; i < S->n_attn_claimers.back(); ++i) {
       mk_task t = make_task(MK_OP_ATTN, l);
@@ -365,6 +378,18 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     // MoE up/gate claimers
     begin_wave();
     const int n_attn = S->n_attn_claimers.back();
+    // Fixed shares (at most 16 tokens, an even number of column blocks): the
+    // claimers whose compute unit (round-robin placement: flat index modulo
+    // the workgroups) runs no attention claimer in this layer split the work
+    // evenly; the others have none.
+    std::vector<char> attn_cu(n_w, 0);
+    for (int i = 0; i < n_attn; ++i) attn_cu[(attn_flat0 + i) % n_w] = 1;
+    const int moe_flat0 = (int)S->flat.size();
+    int n_static = 0;
+    for (int i = 0; i < S->n_up_claimers; ++i) n_static += !attn_cu[(moe_flat0 + i) % n_w];
+    const bool fixed = B <= 16 && NB % 2 == 0 && n_static >= std::max(1, n_w / 8);
+    S->moe_fixed.push_back(fixed ? 1 : 0);
+    int k_static = 0;
     for (int i = 0; i < S->n_up_claimers; ++i) {
       mk_task t = make_task(MK_OP_MOE_UP, l);
       t.a[0] = x.up_claim;
@@ -379,6 +404,13 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       t.a[3] = x.down_claim;
       t.a[4] = x.colblk;
       t.sig_ctr[0] = resid(l + 1);
+      if (fixed) {
+        t.b[0] = attn_cu[(moe_flat0 + i) % n_w] ? -1 : k_static++;
+        t.b[1] = n_static;
+        t.b[2] = i;
+        t.b[3] = S->n_up_claimers;
+        add_wait(t, resid(l), NB);
+      }
       add_wait(t, x.route, 1);
       push(t);
     }
@@ -431,7 +463,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
 struct SimCU {
   bool in_claimer = false;
   int pending_item = -1;  // claimed item waiting for its dependency
-  int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items
+  int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items, 2 fixed-share down pairs
+  int pair_end = 0;       // fixed shares: end of this claimer's down pairs (pending_item: the next)
   int pos = 0;
 };
 
@@ -453,7 +486,6 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   std::vector<int64_t> ctr(S.n_ctr, 0);
   std::vector<SimCU> cu(n_cu);
   std::mt19937_64 rng(seed);
-  auto layer_of = [&](int counter) { return (counter - S.c_layer0) / S.c_per_layer; };
   auto waits_met = [&](const mk_task& t) {
     for (int i = 0; i < 3; ++i)
       if (t.wait_ctr[i] >= 0 && ctr[t.wait_ctr[i]] < t.wait_tgt[i]) return false;
@@ -511,8 +543,41 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
         continue;
       }
       // claimer step
-      const int l = layer_of(t.a[0]);
+      const int l = t.layer;
       const int na = n_active[l];
+      if (t.op == MK_OP_MOE_UP && S.moe_fixed[l] && u.phase == 0) {
+        // fixed shares: the up/gate items at once, then the down pairs
+        const int k = t.b[0], n = t.b[1];
+        progress = true;
+        if (k < 0) {
+          u.in_claimer = false;
+          done();
+          continue;
+        }
+        const int n_items = na * up_per_e, n_pairs = na * down_per_e / 2;
+        for (int id = (int)((int64_t)k * n_items / n); id < (int)((int64_t)(k + 1) * n_items / n); ++id)
+          ctr[t.a[1] + id / up_per_e]++;
+        u.phase = 2;
+        u.pending_item = (int)((int64_t)k * n_pairs / n);
+        u.pair_end = (int)((int64_t)(k + 1) * n_pairs / n);
+        continue;
+      }
+      if (t.op == MK_OP_MOE_UP && u.phase == 2) {
+        if (u.pending_item >= u.pair_end) {
+          u.in_claimer = false;
+          u.pending_item = -1;
+          done();
+          continue;
+        }
+        const int item = 2 * u.pending_item, a = item / down_per_e, cb = item % down_per_e;
+        if (ctr[t.a[1] + a] >= up_per_e) {
+          block(t, t.a[4], cb, l);
+          block(t, t.a[4], cb + 1, l);
+          u.pending_item++;
+          progress = true;
+        }
+        continue;
+      }
       if (t.op == MK_OP_ATTN) {
         const int ns = t.a[3], n_items = B * KVH * ns;
         if (u.pending_item < 0) {
@@ -579,8 +644,8 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
     want[k++] = 1;                                                   // route finalized
     want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
-    want[k++] = (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
-    want[k++] = (int64_t)n_active[l] * down_per_e + S.n_up_claimers;
+    want[k++] = S.moe_fixed[l] ? 0 : (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
+    want[k++] = S.moe_fixed[l] ? 0 : (int64_t)n_active[l] * down_per_e + S.n_up_claimers;
     for (int a = 0; a < E; ++a) want[k++] = a < n_active[l] ? up_per_e : 0;
     for (int cb = 0; cb < NB; ++cb) want[k++] = KVH + n_active[l];
   }

@@ -22,7 +22,9 @@
 #define MK_MAX_KVH 8    // kv heads
 #define MK_MAX_RKS 4    // router K splits
 #define MK_MAX_F 768    // expert width
-#define MK_MAX_BATCH 32 // sequences per step (two row tiles of 16)
+#define MK_MAX_BATCH 32
+// Attention combine: split partials in flight per thread (16-byte loads)
+#define MK_COMB_SB 16 // sequences per step (two row tiles of 16)
 #define MK_UP_BATCH_MAX 4  // expert up/gate items claimed together
 #define MK_TASK_INTS 32
 
@@ -53,7 +55,8 @@ struct mk_task {
   int32_t wait_ctr[3];    // counter index or -1
   int32_t wait_tgt[3];    // wait until counter >= target
   int32_t sig_ctr[2];     // counters incremented once when the task is done, or -1
-  int32_t pad[16];
+  int32_t b[4];           // more op arguments (see the op bodies)
+  int32_t pad[12];
 };
 static_assert(sizeof(mk_task) == MK_TASK_INTS * 4, "descriptor is 32 int32");
 
