@@ -1437,14 +1437,14 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
 // pairs likewise, so the shares are even and no claim round trips to a shared
 // counter sit on the path. The activation operand loads as soon as the layer
 // input is complete, while the route is still pending; up/gate weights stream
-// two items deep; the first down block's weights stream from the start.
+// UPD items deep.
 //   b[0], b[1]: this claimer's index among the claimers on compute units
 //   without attention work in this layer, and their count (b[0] < 0: none for
 //   this claimer); b[2], b[3]: its index among all claimers, and their count
 //   (used in the kernel-per-op variant, where attention ran before);
 //   wait_ctr[0]: the layer input, wait_ctr[1]: the route; the other
 //   arguments as for the claiming variant.
-template <int NCH, int NCHD>
+template <int NCH, int NCHD, int UPD>
 __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task& t, Smem& sm) {
   const int sk = P.waits_enabled ? t.b[0] : t.b[2], sn = P.waits_enabled ? t.b[1] : t.b[3];
   if (sk < 0) return;
@@ -1476,8 +1476,6 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
     wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
                valid ? DP : 0, 0, kcd);
   };
-  WTile<4, NCHD> wd0;
-  down_load(wd0, 2 * plo, plo < phi);
   auto up_load = [&](WTile<2, NCH>& w, int id) {
     const bool valid = id < hi;
     const int a = valid ? id / upe : 0, r = id % upe;
@@ -1513,21 +1511,23 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
     }
   };
   {
-    WTile<2, NCH> w0, w1;
-    up_load(w0, lo);
-    up_load(w1, lo + 1);
-    for (int id = lo; id < hi; id += 2) {
-      up_do(w0, id);
-      if (id + 2 < hi) up_load(w0, id + 2);
-      if (id + 1 < hi) up_do(w1, id + 1);
-      if (id + 3 < hi) up_load(w1, id + 3);
+    // UPD items in flight; a load past the share's end reads nothing (a zero
+    // tile), so every iteration issues the same loads and the compiler waits
+    // for exactly the item it computes next
+    WTile<2, NCH> w[UPD];
+#pragma unroll
+    for (int k = 0; k < UPD; ++k) up_load(w[k], lo + k);
+    for (int id = lo; id < hi; id += UPD) {
+#pragma unroll
+      for (int k = 0; k < UPD; ++k) {
+        if (id + k < hi) up_do(w[k], id + k);
+        up_load(w[k], id + k + UPD);
+      }
     }
   }
   mark(sm, 1);
-  // the second down block's weights, then this share's up/gate arrivals
-  // (one per item, on its expert's counter)
-  WTile<4, NCHD> wd1;
-  down_load(wd1, 2 * plo + 1, plo < phi);
+  // this share's up/gate arrivals (one per item, on its expert's counter),
+  // then the first down pair's weights
   sync_published();
   if (lo < hi) {
     const int a0 = lo / upe, a1 = (hi - 1) / upe;
@@ -1537,6 +1537,9 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
       __hip_atomic_fetch_add(&P.ctr[done_base + a], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  WTile<4, NCHD> wd0, wd1;
+  down_load(wd0, 2 * plo, plo < phi);
+  down_load(wd1, 2 * plo + 1, plo < phi);
   mark(sm, 2);
   int staged = -1;
   for (int p = plo; p < phi; ++p) {
@@ -1747,7 +1750,7 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_MOE_UP:
       if (MT == 1 && t.b[1] > 0)
-        op_moe_static<32 / MK_WAVES, 24 / MK_WAVES>(P, t, sm);
+        op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
       else
         op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm);
       break;
