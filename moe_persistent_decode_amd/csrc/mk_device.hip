@@ -1351,13 +1351,14 @@ __device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Sme
   }
 }
 
-// Two adjacent column blocks (cb0, cb0 + 1) of one expert's down projection
-// for at most 16 routed tokens, each block's weights already in registers.
+// One or two (nblk) adjacent column blocks (cb0, cb0 + 1) of one expert's down
+// projection for at most 16 routed tokens, each block's weights already in
+// registers (the second a zero tile when nblk is 1).
 // stage: build the expert's SiLU-and-multiply operand in LDS first (after its
 // up/gate items completed); otherwise the operand of the previous pair, the
 // same expert, is reused. Each block's arrival may complete its residual.
 template <int NCH>
-__device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, int a, int cb0,
+__device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, int a, int cb0, int nblk,
                                           const WTile<4, NCH>& w0, const WTile<4, NCH>& w1, bool stage, Smem& sm) {
   const int F = P.F, H = P.H, B = P.B;
   const int kc = F / 32;
@@ -1411,11 +1412,11 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
   for (int o = threadIdx.x; o < 8 * 256; o += MK_WG_THREADS) {
     const int pp = o / 256, m = (o / 16) % 16, nn = o % 16;
     const int cb = cb0 + pp / 4, p4 = pp % 4;
-    if (p4 < DP && m < cnt) DN.stf(sm.rt_slot[a * B + m] * H + (cb * DP + p4) * 16 + nn, sm.out[o]);
+    if (pp / 4 < nblk && p4 < DP && m < cnt) DN.stf(sm.rt_slot[a * B + m] * H + (cb * DP + p4) * 16 + nn, sm.out[o]);
   }
-  // both blocks' arrivals in one round trip
+  // the blocks' arrivals in one round trip
   sync_published();
-  if (threadIdx.x < 2)
+  if ((int)threadIdx.x < nblk)
     sm.t_old[threadIdx.x] = (int)__hip_atomic_fetch_add(&P.ctr[t.a[4] + cb0 + threadIdx.x], 1u, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -1426,28 +1427,29 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
     residual_block(P, t.layer, cb0, sm);
     arrive_nr(P, t.sig_ctr[0]);
   }
-  if (o1 == last) {
+  if (nblk == 2 && o1 == last) {
     residual_block(P, t.layer, cb0 + 1, sm);
     arrive_nr(P, t.sig_ctr[0]);
   }
 }
 
-// The MoE claimer with fixed shares (at most 16 tokens): claimer k of n takes
-// up/gate items [k N / n, (k + 1) N / n) of the layer's N and down column-block
-// pairs likewise, so the shares are even and no claim round trips to a shared
-// counter sit on the path. The activation operand loads as soon as the layer
-// input is complete, while the route is still pending; up/gate weights stream
-// UPD items deep.
-//   b[0], b[1]: this claimer's index among the claimers on compute units
-//   without attention work in this layer, and their count (b[0] < 0: none for
-//   this claimer); b[2], b[3]: its index among all claimers, and their count
-//   (used in the kernel-per-op variant, where attention ran before);
+// The MoE claimer with fixed shares (at most 16 tokens): claimer k takes a
+// weighted share of the layer's up/gate items and, among the claimers with
+// weight, an equal share of its down items, so no claim round trips to a
+// shared counter sit on the path. The
+// activation operand loads as soon as the layer input is complete, while the
+// route is still pending; up/gate weights stream UPD items deep.
+//   b[0] this claimer's index k, b[1] the count nf of claimers (indices first)
+//   on compute units without attention work in this layer, b[2] all
+//   claimers, b[3] the up/gate weight of the others (of 256);
 //   wait_ctr[0]: the layer input, wait_ctr[1]: the route; the other
 //   arguments as for the claiming variant.
 template <int NCH, int NCHD, int UPD>
 __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int sk = P.waits_enabled ? t.b[0] : t.b[2], sn = P.waits_enabled ? t.b[1] : t.b[3];
-  if (sk < 0) return;
+  // claimers [0, nf) weigh 256, the others wa (all 256 in the kernel-per-op
+  // variant, where attention ran in an earlier launch)
+  const int sk = t.b[0], nf = t.b[1], nt = t.b[2], wa = P.waits_enabled ? t.b[3] : 256;
+  auto pre = [&](int j) -> int64_t { return j <= nf ? (int64_t)j * 256 : (int64_t)nf * 256 + (int64_t)(j - nf) * wa; };
   const int l = t.layer, done_base = t.a[1];
   const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
   const int kc = P.H / 32, kh_chunks = kc / 2;
@@ -1465,9 +1467,12 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
   claimer_start(P, -1, 0, l, sm);
   mark(sm, 0);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
-  const int n_pairs = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]) / 2;
-  const int lo = (int)((int64_t)sk * n_items / sn), hi = (int)((int64_t)(sk + 1) * n_items / sn);
-  const int plo = (int)((int64_t)sk * n_pairs / sn), phi = (int)((int64_t)(sk + 1) * n_pairs / sn);
+  const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
+  const int64_t tot = pre(nt);
+  const int lo = (int)(n_items * pre(sk) / tot), hi = (int)(n_items * pre(sk + 1) / tot);
+  const int nd = wa == 0 ? nf : nt;  // down items: to the claimers with up/gate weight
+  const int dlo = sk < nd ? (int)((int64_t)n_down * sk / nd) : 0;
+  const int dhi = sk < nd ? (int)((int64_t)n_down * (sk + 1) / nd) : 0;
   const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
   const size_t pstride_d = (size_t)kcd * 512;
   auto down_load = [&](WTile<4, NCHD>& w, int item, bool valid) {
@@ -1537,19 +1542,22 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
       __hip_atomic_fetch_add(&P.ctr[done_base + a], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  // down items in groups of one or two blocks of one expert
+  auto group_n = [&](int i) { return (i + 1 < dhi && (i + 1) % dpe != 0) ? 2 : 1; };
   WTile<4, NCHD> wd0, wd1;
-  down_load(wd0, 2 * plo, plo < phi);
-  down_load(wd1, 2 * plo + 1, plo < phi);
+  down_load(wd0, dlo, dlo < dhi);
+  down_load(wd1, dlo + 1, dlo < dhi && group_n(dlo) == 2);
   mark(sm, 2);
   int staged = -1;
-  for (int p = plo; p < phi; ++p) {
-    const int a = (2 * p) / dpe, cb0 = (2 * p) % dpe;
-    if (p > plo) {
-      down_load(wd0, 2 * p, true);
-      down_load(wd1, 2 * p + 1, true);
+  for (int i = dlo; i < dhi;) {
+    const int a = i / dpe, cb0 = i % dpe, ng = group_n(i);
+    if (i > dlo) {
+      down_load(wd0, i, true);
+      down_load(wd1, i + 1, ng == 2);
     }
-    down_pair<NCHD>(P, t, a, cb0, wd0, wd1, a != staged, sm);
+    down_pair<NCHD>(P, t, a, cb0, ng, wd0, wd1, a != staged, sm);
     staged = a;
+    i += ng;
     if (ld_relaxed(&P.err[0]) != 0) return;
   }
   mark(sm, 3);

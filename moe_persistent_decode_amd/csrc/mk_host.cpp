@@ -378,18 +378,34 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     // MoE up/gate claimers
     begin_wave();
     const int n_attn = S->n_attn_claimers.back();
-    // Fixed shares (at most 16 tokens, an even number of column blocks): the
-    // claimers whose compute unit (round-robin placement: flat index modulo
-    // the workgroups) runs no attention claimer in this layer split the work
-    // evenly; the others have none.
+    // Fixed shares (at most 16 tokens): the up/gate items go to the claimers
+    // whose compute unit (round-robin placement: flat index modulo the
+    // workgroups) runs no attention claimer in this layer, when there are
+    // enough of them: the split that completes a (sequence, group) merges
+    // the splits afterwards, and an up/gate share behind that would hold up
+    // the expert's down items. Otherwise every claimer takes a share weighted
+    // so that each compute unit streams about the same bytes in this phase:
+    // the equal share less the key/value bytes of its attention work (weight
+    // wa of 256). Down items are shared equally among the claimers with
+    // up/gate work.
     std::vector<char> attn_cu(n_w, 0);
     for (int i = 0; i < n_attn; ++i) attn_cu[(attn_flat0 + i) % n_w] = 1;
     const int moe_flat0 = (int)S->flat.size();
-    int n_static = 0;
-    for (int i = 0; i < S->n_up_claimers; ++i) n_static += !attn_cu[(moe_flat0 + i) % n_w];
-    const bool fixed = B <= 16 && NB % 2 == 0 && n_static >= std::max(1, n_w / 8);
+    int n_free = 0;
+    for (int i = 0; i < S->n_up_claimers; ++i) n_free += !attn_cu[(moe_flat0 + i) % n_w];
+    const bool fixed = B <= 16;
+    int wa = 256;
+    {
+      const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
+      const double up_bytes = e_act * 2.0 * c.expert_ffn * c.hidden * 2.0;
+      const double kv_per = n_attn > 0 ? (double)n_attn_items * S->pps * c.page_size * c.head_dim * 4.0 / n_attn : 0.0;
+      const double f = (up_bytes + (S->n_up_claimers - n_free) * kv_per) / S->n_up_claimers;
+      wa = f > 0 ? (int)std::lround(256.0 * std::max(0.0, f - kv_per) / f) : 256;
+      if (n_free >= n_w / 4) wa = 0;
+      if (n_free == 0 && wa == 0) wa = 256;
+    }
     S->moe_fixed.push_back(fixed ? 1 : 0);
-    int k_static = 0;
+    int k_free = 0, k_attn = n_free;
     for (int i = 0; i < S->n_up_claimers; ++i) {
       mk_task t = make_task(MK_OP_MOE_UP, l);
       t.a[0] = x.up_claim;
@@ -405,10 +421,10 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       t.a[4] = x.colblk;
       t.sig_ctr[0] = resid(l + 1);
       if (fixed) {
-        t.b[0] = attn_cu[(moe_flat0 + i) % n_w] ? -1 : k_static++;
-        t.b[1] = n_static;
-        t.b[2] = i;
-        t.b[3] = S->n_up_claimers;
+        t.b[0] = attn_cu[(moe_flat0 + i) % n_w] ? k_attn++ : k_free++;
+        t.b[1] = n_free;
+        t.b[2] = S->n_up_claimers;
+        t.b[3] = wa;
         add_wait(t, resid(l), NB);
       }
       add_wait(t, x.route, 1);
@@ -458,13 +474,27 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   return S;
 }
 
+// The fixed shares of MoE claimer k (claimers [0, nf) weigh 256 each, the
+// rest wa each): up/gate items [lo, hi) of n_items, down items [dlo, dhi) of
+// n_down in equal shares over the claimers with up/gate weight. The device
+// computes the same.
+void fixed_shares(int k, int nf, int nt, int wa, int n_items, int n_down, int& lo, int& hi, int& dlo, int& dhi) {
+  auto pre = [&](int j) -> int64_t { return j <= nf ? (int64_t)j * 256 : (int64_t)nf * 256 + (int64_t)(j - nf) * wa; };
+  const int64_t tot = pre(nt);
+  lo = (int)(n_items * pre(k) / tot);
+  hi = (int)(n_items * pre(k + 1) / tot);
+  const int nd = wa == 0 ? nf : nt;  // down items: to the same claimers as the up/gate items
+  dlo = k < nd ? (int)((int64_t)n_down * k / nd) : 0;
+  dhi = k < nd ? (int)((int64_t)n_down * (k + 1) / nd) : 0;
+}
+
 // Host model of the device: per-CU in-order lists, counters, claim queues and
 // the last-arrival actions, with CUs advancing in a seeded random order.
 struct SimCU {
   bool in_claimer = false;
   int pending_item = -1;  // claimed item waiting for its dependency
   int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items, 2 fixed-share down pairs
-  int pair_end = 0;       // fixed shares: end of this claimer's down pairs (pending_item: the next)
+  int item_end = 0;       // fixed shares: end of this claimer's down items (pending_item: the next)
   int pos = 0;
 };
 
@@ -546,33 +576,27 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       const int l = t.layer;
       const int na = n_active[l];
       if (t.op == MK_OP_MOE_UP && S.moe_fixed[l] && u.phase == 0) {
-        // fixed shares: the up/gate items at once, then the down pairs
-        const int k = t.b[0], n = t.b[1];
-        progress = true;
-        if (k < 0) {
-          u.in_claimer = false;
-          done();
-          continue;
-        }
-        const int n_items = na * up_per_e, n_pairs = na * down_per_e / 2;
-        for (int id = (int)((int64_t)k * n_items / n); id < (int)((int64_t)(k + 1) * n_items / n); ++id)
-          ctr[t.a[1] + id / up_per_e]++;
+        // fixed shares: the up/gate items at once, then the down items
+        const int n_items = na * up_per_e, n_down = na * down_per_e;
+        int lo, hi, dlo, dhi;
+        fixed_shares(t.b[0], t.b[1], t.b[2], t.b[3], n_items, n_down, lo, hi, dlo, dhi);
+        for (int id = lo; id < hi; ++id) ctr[t.a[1] + id / up_per_e]++;
         u.phase = 2;
-        u.pending_item = (int)((int64_t)k * n_pairs / n);
-        u.pair_end = (int)((int64_t)(k + 1) * n_pairs / n);
+        u.pending_item = dlo;
+        u.item_end = dhi;
+        progress = true;
         continue;
       }
       if (t.op == MK_OP_MOE_UP && u.phase == 2) {
-        if (u.pending_item >= u.pair_end) {
+        if (u.pending_item >= u.item_end) {
           u.in_claimer = false;
           u.pending_item = -1;
           done();
           continue;
         }
-        const int item = 2 * u.pending_item, a = item / down_per_e, cb = item % down_per_e;
+        const int a = u.pending_item / down_per_e, cb = u.pending_item % down_per_e;
         if (ctr[t.a[1] + a] >= up_per_e) {
           block(t, t.a[4], cb, l);
-          block(t, t.a[4], cb + 1, l);
           u.pending_item++;
           progress = true;
         }
