@@ -328,6 +328,17 @@ __device__ __forceinline__ uint16_t* u_of_w(const mk_params& P, int l, int part)
 __device__ __forceinline__ uint16_t* o_of(const mk_params& P, int part) {
   return P.o + (size_t)part * P.B * P.QH * P.D;
 }
+// Routing scratch, one region per layer (a compute unit may still read a
+// layer's route after the next layer's router has run):
+// router partials [ks][B][E], top-k ids and weights [B][K], route.
+__device__ __forceinline__ float* rp_of(const mk_params& P, int l) {
+  return P.rp + (size_t)l * P.router_ks * P.B * P.E;
+}
+__device__ __forceinline__ int32_t* tki_of(const mk_params& P, int l) { return P.tk_idx + (size_t)l * P.B * P.K; }
+__device__ __forceinline__ float* tkw_of(const mk_params& P, int l) { return P.tk_w + (size_t)l * P.B * P.K; }
+__device__ __forceinline__ int32_t* route_of(const mk_params& P, int l) {
+  return P.route + (size_t)l * MK_ROUTE_INTS(P.E, P.B);
+}
 __device__ __forceinline__ float* ssq_of(const mk_params& P, int l) {
   return P.ssq + (size_t)(l & 1) * P.B * P.NB;
 }
@@ -990,8 +1001,8 @@ __device__ __forceinline__ void block_arrive(const mk_params& P, const mk_task& 
   sync_published();
   const int i = threadIdx.x;
   if (i == 0) sm.old = (int)__hip_atomic_fetch_add(&P.ctr[ctr_base + cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (i == 64) sm.t_old[0] = Pub(P.route).ldi(0);
-  const float w = i < P.B * P.K ? Pub(P.tk_w).ldf(i) : 0.f;  // B * K <= 512
+  if (i == 64) sm.t_old[0] = Pub(route_of(P, t.layer)).ldi(0);
+  const float w = i < P.B * P.K ? Pub(tkw_of(P, t.layer)).ldf(i) : 0.f;  // B * K <= 512
   __syncthreads();
   const int old = sm.old, n_active = sm.t_old[0];
   if (old == P.KVH + n_active - 1) {
@@ -1041,6 +1052,7 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
 // completes the router does ROUTER_TOPK + ROUTE_FINALIZE (megakernel post,
 // section "Tasks"): sum the partials in fixed order, top-k (ties to the lower
 // expert index), softmax over the kept logits, the expert work queue.
+__device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm, bool publish);
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm);
 
 template <int MT, int NCH>
@@ -1062,7 +1074,7 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
-  const Pub RP(P.rp);
+  const Pub RP(rp_of(P, l));
   for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m, e = (p0 + pp) * 16 + nn;
@@ -1082,11 +1094,23 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
 // experts ranked below k are kept, in rank order. Every comparison is
 // independent, so this takes a few hundred cycles per token instead of k
 // dependent rounds of an argmax. Then the route: the active experts in
-// ascending order, the tokens routed to each, and the work-item counts.
-__device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm) {
+// ascending order, the tokens routed to each, and the work-item counts, built
+// in LDS (sm.rt_*, the routing weights in sm.tkw) and, with publish, stored for
+// the other compute units. Without publish, layer l's sums of squares load
+// alongside the router logits (then sm.inv_rms).
+__device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm, bool publish) {
   const int E = P.E, K = P.K, B = P.B;
-  const Pub R(P.rp), TI(P.tk_idx), TW(P.tk_w), RT(P.route);
+  const Pub R(rp_of(P, l)), TI(tki_of(P, l)), TW(tkw_of(P, l)), RT(route_of(P, l));
   SmemTopk& T = sm.u.tk;
+  float sq[2];  // B * NB <= 1024
+  if (!publish) {
+    const Pub S(ssq_of(P, l));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = threadIdx.x + k * MK_WG_THREADS;
+      sq[k] = i < B * P.NB ? S.ldf(i) : 0.f;
+    }
+  }
   for (int i = threadIdx.x; i < B * E; i += MK_WG_THREADS) {
     float p[MK_MAX_RKS];
 #pragma unroll
@@ -1106,7 +1130,21 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
   // keys past the last expert of each row: zero, below every real key
   for (int i = threadIdx.x; i < B * 128; i += MK_WG_THREADS)
     if (i % 128 >= E) T.key[i / 128][i % 128] = 0ull;
+  if ((int)threadIdx.x < E) T.tokmask[threadIdx.x] = 0u;
+  if (!publish) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = threadIdx.x + k * MK_WG_THREADS;
+      if (i < B * P.NB) sm.ssq[i] = sq[k];
+    }
+  }
   __syncthreads();
+  if (!publish && (int)threadIdx.x < B) {
+    const float* q = sm.ssq + threadIdx.x * P.NB;
+    float tot = 0.f;
+    for (int k = 0; k < P.NB; ++k) tot += q[k];
+    sm.inv_rms[threadIdx.x] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+  }
   // rank of (b, e): the keys above its own; four threads per pair, each over
   // a quarter of the experts, summed across the four adjacent lanes
   for (int i = threadIdx.x; i < B * E * 4; i += MK_WG_THREADS) {
@@ -1124,6 +1162,9 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
     if (q == 0 && rank < K) {
       T.sel_idx[b][rank] = e;
       T.sel_val[b][rank] = T.logit[b][e];
+      // route: each expert's set of tokens as a bit mask (a token keeps an
+      // expert at most once)
+      atomicOr(&T.tokmask[e], 1u << b);
     }
   }
   __syncthreads();
@@ -1134,18 +1175,16 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
     const float top = T.sel_val[b][0];
     float sum = 0.f;
     for (int jj = 0; jj < K; ++jj) sum += __expf(T.sel_val[b][jj] - top);
-    TI.sti(i, T.sel_idx[b][j]);
-    TW.stf(i, __expf(T.sel_val[b][j] - top) / sum);
-    if (P.tk_trace) P.tk_trace[((size_t)l * B + b) * K + j] = T.sel_idx[b][j];
+    const float w = __expf(T.sel_val[b][j] - top) / sum;
+    sm.tkw[i] = w;
+    if (publish) {
+      TI.sti(i, T.sel_idx[b][j]);
+      TW.stf(i, w);
+      if (P.tk_trace) P.tk_trace[((size_t)l * B + b) * K + j] = T.sel_idx[b][j];
+    }
   }
-  // route: each expert's set of tokens as a bit mask (a token keeps an expert
-  // at most once), the experts' positions among the active ones from two wave
-  // ballots, and each slot's rank within its expert (tokens in ascending order)
-  if ((int)threadIdx.x < E) T.tokmask[threadIdx.x] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS)
-    atomicOr(&T.tokmask[T.sel_idx[i / K][i % K]], 1u << (i / K));
-  __syncthreads();
+  // the experts' positions among the active ones from two wave ballots, and
+  // each slot's rank within its expert (tokens in ascending order)
   if (threadIdx.x < 128) {
     const int e = threadIdx.x;
     const bool act = e < E && T.tokmask[e] != 0u;
@@ -1161,29 +1200,42 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
     const int a = e < 64 ? __popcll(b0 & ((1ull << e) - 1ull)) : __popcll(b0) + __popcll(b1 & ((1ull << (e - 64)) - 1ull));
     T.apos[e] = a;
     if (mask) {
-      RT.sti(4 + a, e);
-      RT.sti(4 + E + a, __popc(mask));
+      sm.rt_e[a] = e;
+      sm.rt_cnt[a] = __popc(mask);
+      if (publish) {
+        RT.sti(4 + a, e);
+        RT.sti(4 + E + a, __popc(mask));
+      }
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) {
     const int b = i / K, e = T.sel_idx[b][i % K];
     const int r = __popc(T.tokmask[e] & ((1u << b) - 1u));
-    RT.sti(4 + 2 * E + T.apos[e] * B + r, i);
+    sm.rt_slot[T.apos[e] * B + r] = i;
+    if (publish) RT.sti(4 + 2 * E + T.apos[e] * B + r, i);
   }
   if (threadIdx.x == 0) {
-    RT.sti(0, n_active);
-    RT.sti(1, n_active * P.up_items_per_expert);
-    RT.sti(2, n_active * P.down_items_per_expert);
+    sm.rt_hdr[0] = n_active;
+    sm.rt_hdr[1] = n_active * P.up_items_per_expert;
+    sm.rt_hdr[2] = n_active * P.down_items_per_expert;
+    if (publish) {
+      RT.sti(0, n_active);
+      RT.sti(1, n_active * P.up_items_per_expert);
+      RT.sti(2, n_active * P.down_items_per_expert);
+    }
   }
+  __syncthreads();
 }
+
+__device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm) { route_build(P, l, sm, true); }
 
 // A claimer's start in one round trip: the first claim of n items (thread 0;
 // the result in sm.claim; none with claim_ctr < 0), the route entries of the layer's active experts
 // and, with l >= 0, the sums of squares of layer l's input (then sm.inv_rms).
 __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_ctr, int n, int l, Smem& sm,
                                               int32_t claim2_ctr = -1) {
-  const Pub R(P.route);
+  const Pub R(route_of(P, l));
   const int E = P.E, B = P.B;
   const int i = threadIdx.x;
   int c = 0;
@@ -1197,7 +1249,7 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
     sm.rt_cnt[i] = R.ldi(4 + E + i);
   }
   for (int k = i; k < E * B; k += MK_WG_THREADS) sm.rt_slot[k] = R.ldi(4 + 2 * E + k);
-  if (i < B * P.K) sm.tkw[i] = Pub(P.tk_w).ldf(i);
+  if (i < B * P.K) sm.tkw[i] = Pub(tkw_of(P, l)).ldf(i);
   if (l >= 0) {
     const Pub S(ssq_of(P, l));
     for (int k = i; k < B * P.NB; k += MK_WG_THREADS) sm.ssq[k] = S.ldf(k);
@@ -1442,8 +1494,9 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
 //   b[0] this claimer's index k, b[1] the count nf of claimers (indices first)
 //   on compute units without attention work in this layer, b[2] all
 //   claimers, b[3] the up/gate weight of the others (of 256);
-//   wait_ctr[0]: the layer input, wait_ctr[1]: the route; the other
-//   arguments as for the claiming variant.
+//   wait_ctr[0]: the layer input, wait_ctr[1]: the router tasks (each
+//   claimer takes the top-k and builds the route itself, the same on every
+//   compute unit); the other arguments as for the claiming variant.
 template <int NCH, int NCHD, int UPD>
 __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task& t, Smem& sm) {
   // claimers [0, nf) weigh 256, the others wa (all 256 in the kernel-per-op
@@ -1463,8 +1516,9 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
   atile_load_bf16(Al0, Pub(u_of(P, l, 1)), sm.row_off[0], 0, kh_chunks);
   atile_load_bf16(Ah1, Pub(u_of(P, l, 0)), sm.row_off[0], kh_chunks, kc);
   atile_load_bf16(Al1, Pub(u_of(P, l, 1)), sm.row_off[0], kh_chunks, kc);
+  // the router's partial logits complete: this claimer's own top-k and route
   if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
-  claimer_start(P, -1, 0, l, sm);
+  route_build(P, l, sm, false);
   mark(sm, 0);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
   const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);

@@ -426,8 +426,10 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         t.b[2] = S->n_up_claimers;
         t.b[3] = wa;
         add_wait(t, resid(l), NB);
+        add_wait(t, x.router, h->n_router_tasks);
+      } else {
+        add_wait(t, x.route, 1);
       }
-      add_wait(t, x.route, 1);
       push(t);
     }
     // O projection per (group, column block)
@@ -842,9 +844,10 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   const size_t s_u = stake((size_t)4 * Bm * H * 2);
   const size_t s_q = stake((size_t)Bm * h->q_dim * 4), s_o = stake((size_t)Bm * h->q_dim * 4);
   const size_t s_part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
-  const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_rp = stake((size_t)h->router_ks * Bm * E * 4);
-  const size_t s_tki = stake((size_t)Bm * K * 4), s_tkw = stake((size_t)Bm * K * 4);
-  const size_t s_route = stake((size_t)MK_ROUTE_INTS(E, Bm) * 4);
+  // routing scratch: one region per layer
+  const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_rp = stake((size_t)L * h->router_ks * Bm * E * 4);
+  const size_t s_tki = stake((size_t)L * Bm * K * 4), s_tkw = stake((size_t)L * Bm * K * 4);
+  const size_t s_route = stake((size_t)L * MK_ROUTE_INTS(E, Bm) * 4);
   const size_t s_gu = stake((size_t)Bm * K * 4 * F * 4), s_dn = stake((size_t)Bm * K * H * 4);
   const size_t s_lmv = stake((size_t)Bm * h->n_lm_tasks * 4), s_lma = stake((size_t)Bm * h->n_lm_tasks * 4);
   const size_t s_err = stake(16);
