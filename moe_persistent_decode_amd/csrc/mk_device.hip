@@ -1811,7 +1811,7 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_MOE_UP:
-      if (MT == 1 && t.b[1] > 0)
+      if (MT == 1 && t.b[2] > 0)  // fixed shares (b[2]: the claimer count)
         op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
       else
         op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm);

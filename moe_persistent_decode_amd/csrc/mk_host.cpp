@@ -291,11 +291,15 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   };
 
   auto begin_wave = [&]() { S->waves.push_back({(int)S->flat.size(), (int)S->flat.size()}); };
-  auto push = [&](const mk_task& t) {
+  // placement: workgroup `cu`, or (cu < 0) round-robin by flat index
+  std::vector<int> flat_cu;
+  auto push_at = [&](const mk_task& t, int cu) {
     S->flat.push_back(t);
     S->flat_wave.push_back((int)S->waves.size() - 1);
     S->waves.back().second = (int)S->flat.size();
+    flat_cu.push_back(cu);
   };
+  auto push = [&](const mk_task& t) { push_at(t, -1); };
 
   S->n_up_claimers = n_w;
   S->n_down_claimers = n_w;
@@ -414,8 +418,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       // top-k under uniform routing) over the claimers likely free when it
       // opens (those not running attention)
       const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
-      const int n_free = std::max(1, S->n_up_claimers - n_attn);
-      t.a[2] = std::max(1, (int)std::ceil(e_act * 2 * c.expert_ffn / 16 / n_free));
+      const int n_early = std::max(1, S->n_up_claimers - n_attn);
+      t.a[2] = std::max(1, (int)std::ceil(e_act * 2 * c.expert_ffn / 16 / n_early));
       // then the down items (their last block contribution does the residual)
       t.a[3] = x.down_claim;
       t.a[4] = x.colblk;
@@ -432,7 +436,9 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       }
       push(t);
     }
-    // O projection per (group, column block)
+    // O projection per (group, column block), on the compute units that ran
+    // this layer's attention claimers (their MoE shares are empty or light,
+    // so the projection does not queue behind expert work)
     begin_wave();
     int n_oproj = 0;
     for (int g = 0; g < KVH; ++g)
@@ -444,7 +450,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         add_wait(t, x.comb + g, B);
         add_wait(t, x.route, 1);
         t.sig_ctr[0] = resid(l + 1);
-        push(t);
+        push_at(t, -1);
         ++n_oproj;
       }
     S->n_oproj = n_oproj;
@@ -465,9 +471,10 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     push(t);
   }
 
-  // round-robin placement of the flattened list over the resident workgroups
+  // per-workgroup lists in flat order (every wait is on an earlier task of
+  // the flat list, so the lists cannot deadlock), placed as chosen above
   std::vector<std::vector<mk_task>> per(n_w);
-  for (size_t k = 0; k < S->flat.size(); ++k) per[k % n_w].push_back(S->flat[k]);
+  for (size_t k = 0; k < S->flat.size(); ++k) per[flat_cu[k] >= 0 ? flat_cu[k] : k % n_w].push_back(S->flat[k]);
   S->cu_off.assign(n_w + 1, 0);
   for (int i = 0; i < n_w; ++i) {
     S->cu_off[i + 1] = S->cu_off[i] + (int)per[i].size();
