@@ -450,7 +450,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         add_wait(t, x.comb + g, B);
         add_wait(t, x.route, 1);
         t.sig_ctr[0] = resid(l + 1);
-        push_at(t, -1);
+        push_at(t, n_attn > 0 ? (attn_flat0 + n_oproj % n_attn) % n_w : -1);
         ++n_oproj;
       }
     S->n_oproj = n_oproj;
