@@ -1518,8 +1518,9 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
   atile_load_bf16(Al1, Pub(u_of(P, l, 1)), sm.row_off[0], kh_chunks, kc);
   // the router's partial logits complete: this claimer's own top-k and route
   if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
-  route_build(P, l, sm, false);
   mark(sm, 0);
+  route_build(P, l, sm, false);
+  mark(sm, 1);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
   const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
   const int64_t tot = pre(nt);
@@ -1584,7 +1585,6 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
       }
     }
   }
-  mark(sm, 1);
   // this share's up/gate arrivals (one per item, on its expert's counter),
   // then the first down pair's weights
   sync_published();
