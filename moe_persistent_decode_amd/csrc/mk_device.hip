@@ -64,10 +64,17 @@ namespace {
 
 // ------------------------------------------------------------------ helpers
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// The lane from mbcnt rather than from the work-item id: it depends on no
+// register, so the compiler recomputes lane-derived values where it needs
+// them instead of keeping the id live through the kernel and spilling it
+// (a spill reload is a vector memory load, and waiting for it waits for
+// every weight load issued before it).
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 // Wave index as a scalar (wave-uniform) value, so per-wave chunk choices
 // compile to scalar branches instead of exec-mask juggling.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// The thread's index in the workgroup, from the two above.
+__device__ __forceinline__ int tid() { return (wave_id() << 6) | lane_id(); }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // float -> bf16 bits, round to nearest even
@@ -228,7 +235,7 @@ __device__ __noinline__ void raise_error_w(uint32_t* err, uint32_t code, uint32_
 // force: wait even in the kernel-per-op variant (for producers in the same launch).
 __device__ __forceinline__ bool wait_counters(const mk_params& P, const int32_t* cs, const int32_t* ts, int n, Smem& sm,
                                               bool force = false) {
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     const bool active = P.waits_enabled || force;
     // the first reading of every counter and the error word in one round trip
     uint32_t v[3];
@@ -279,7 +286,7 @@ __device__ __forceinline__ int layer_window(const mk_params& P, int l) {
 }
 
 __device__ __forceinline__ void mark(Smem& sm, int k) {
-  if (threadIdx.x == 0) sm.t_mark[k] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+  if (tid() == 0) sm.t_mark[k] = (uint32_t)__builtin_amdgcn_s_memrealtime();
 }
 
 // ---------------------------------------------------------- arrivals
@@ -287,7 +294,7 @@ __device__ __forceinline__ void mark(Smem& sm, int k) {
 // have completed.
 __device__ __forceinline__ void arrive_nr(const mk_params& P, int32_t c) {
   sync_published();
-  if (threadIdx.x == 0 && c >= 0)
+  if (tid() == 0 && c >= 0)
     __hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -295,7 +302,7 @@ __device__ __forceinline__ void arrive_nr(const mk_params& P, int32_t c) {
 // arrival, so the last of a known number of arrivals can act on the result.
 __device__ __forceinline__ int arrive(const mk_params& P, int32_t c, Smem& sm) {
   sync_published();
-  if (threadIdx.x == 0)
+  if (tid() == 0)
     sm.old = (int)__hip_atomic_fetch_add(&P.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int old = sm.old;
@@ -305,7 +312,7 @@ __device__ __forceinline__ int arrive(const mk_params& P, int32_t c, Smem& sm) {
 
 // Claim n consecutive items of a work queue: returns (block-uniform) the first.
 __device__ __forceinline__ int claim_n(const mk_params& P, int32_t c, int n, Smem& sm) {
-  if (threadIdx.x == 0)
+  if (tid() == 0)
     sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int id = sm.claim;
@@ -348,13 +355,13 @@ __device__ __forceinline__ float* ssq_of(const mk_params& P, int l) {
 __device__ __forceinline__ void load_inv_rms(const mk_params& P, int l, Smem& sm) {
   const Pub S(ssq_of(P, l));
   const int n = P.B * P.NB;
-  for (int i = threadIdx.x; i < n; i += MK_WG_THREADS) sm.ssq[i] = S.ldf(i);
+  for (int i = tid(); i < n; i += MK_WG_THREADS) sm.ssq[i] = S.ldf(i);
   __syncthreads();
-  if ((int)threadIdx.x < P.B) {
-    const float* q = sm.ssq + threadIdx.x * P.NB;
+  if ((int)tid() < P.B) {
+    const float* q = sm.ssq + tid() * P.NB;
     float tot = 0.f;
     for (int k = 0; k < P.NB; ++k) tot += q[k];
-    sm.inv_rms[threadIdx.x] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+    sm.inv_rms[tid()] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
   }
   __syncthreads();
 }
@@ -489,7 +496,7 @@ __device__ __forceinline__ void reduce_tiles(const Acc<NP, MT>& acc, Smem& sm) {
       for (int i = 0; i < 4; ++i) red[(pp * MT + mt) * 256 + (4 * (ln >> 4) + i) * 16 + (ln & 15)] = acc.c[pp][mt][i];
   __syncthreads();
 #pragma unroll
-  for (int o = threadIdx.x; o < N; o += MK_WG_THREADS) {
+  for (int o = tid(); o < N; o += MK_WG_THREADS) {
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k * N + o];
@@ -500,7 +507,7 @@ __device__ __forceinline__ void reduce_tiles(const Acc<NP, MT>& acc, Smem& sm) {
 
 // Row offsets of the batch's tokens (row b at b * stride + base), -1 beyond.
 __device__ __forceinline__ void set_rows_batch(const mk_params& P, Smem& sm, int slot, int stride, int base) {
-  if (threadIdx.x < MK_MAX_BATCH) sm.row_off[slot][threadIdx.x] = (int)threadIdx.x < P.B ? (int)threadIdx.x * stride + base : -1;
+  if (tid() < MK_MAX_BATCH) sm.row_off[slot][tid()] = (int)tid() < P.B ? (int)tid() * stride + base : -1;
 }
 
 // -------------------------------------------------------------- attention
@@ -585,7 +592,7 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   if (early1) nxt = load_page(lpn);
   if (!wait_one(P, qkv_ctr, qkv_tgt, sm)) return;
   if (!seq_ok) {
-    if (threadIdx.x == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
+    if (tid() == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
     return;
   }
   if (lp < my1 && !early0) cur = load_page(lp);
@@ -687,7 +694,7 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   __syncthreads();
   const int stride = G * D + 2 * G;
   const Pub dst(P.part + ((size_t)(b * P.KVH + g) * P.max_splits + s) * stride);
-  for (int idx = threadIdx.x; idx < G * D; idx += MK_WG_THREADS) {
+  for (int idx = tid(); idx < G * D; idx += MK_WG_THREADS) {
     const int hh = idx / D, dd = idx % D;
     float M = kNegInf;
 #pragma unroll
@@ -747,27 +754,27 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
   const Pub src(P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride);
   SmemComb& C = sm.u.cb;
   // split maxima and sums, all loads in flight together
-  for (int i = threadIdx.x; i < ns * G; i += MK_WG_THREADS) {
+  for (int i = tid(); i < ns * G; i += MK_WG_THREADS) {
     const int s = i / G, hh = i % G;
     C.f[s][hh] = src.ldf(s * stride + G * D + hh);
     C.l[s][hh] = src.ldf(s * stride + G * D + G + hh);
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int hh = threadIdx.x;
+  if (tid() < G) {
+    const int hh = tid();
     float M = kNegInf;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, C.f[s][hh]);
     C.M[hh] = M;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < ns * G; i += MK_WG_THREADS) {
+  for (int i = tid(); i < ns * G; i += MK_WG_THREADS) {
     const int s = i / G, hh = i % G;
     const float ms = C.f[s][hh];
     C.f[s][hh] = ms == kNegInf ? 0.f : __expf(ms - C.M[hh]);
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int hh = threadIdx.x;
+  if (tid() < G) {
+    const int hh = tid();
     float L = 0.f;
     for (int s = 0; s < ns; ++s) L = fmaf(C.f[s][hh], C.l[s][hh], L);
     C.L[hh] = L;
@@ -780,7 +787,7 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
   // workgroup forms NP partitions of GD4 threads, partition p taking splits
   // p, p + NP, ..., up to SB of them in flight at a time
   const int GD4 = G * D / 4, NP = MK_WG_THREADS / GD4;
-  const int part = threadIdx.x / GD4, j = threadIdx.x % GD4, hh = 4 * j / D;
+  const int part = tid() / GD4, j = tid() % GD4, hh = 4 * j / D;
   constexpr int SB = MK_COMB_SB;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
   if (part < NP) {
@@ -804,12 +811,12 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
       }
     }
   }
-  C.part[threadIdx.x] = O;
+  C.part[tid()] = O;
   __syncthreads();
-  if (threadIdx.x < GD4) {
-    float4 t = C.part[threadIdx.x];
+  if (tid() < GD4) {
+    float4 t = C.part[tid()];
     for (int q = 1; q < NP; ++q) {
-      const float4 u = C.part[q * GD4 + threadIdx.x];
+      const float4 u = C.part[q * GD4 + tid()];
       t.x += u.x;
       t.y += u.y;
       t.z += u.z;
@@ -839,7 +846,7 @@ __device__ __forceinline__ void op_embed(const mk_params& P, const mk_task& t, S
   float hv[NI], gv[NI];
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    const int idx = threadIdx.x + k * MK_WG_THREADS;
+    const int idx = tid() + k * MK_WG_THREADS;
     hv[k] = gv[k] = 0.f;
     if (idx < n) {
       const int b = idx / CB, c = cb * CB + idx % CB;
@@ -857,7 +864,7 @@ __device__ __forceinline__ void op_embed(const mk_params& P, const mk_task& t, S
 }
 
 // Store the residual stream of column block cb (hv[k] = element idx =
-// threadIdx.x + k * 512 of the block, row idx / CB), the next layer's input
+// tid() + k * 512 of the block, row idx / CB), the next layer's input
 // u = bf16(h * gamma_{l_next}) (gv[k]: the element's gamma) and the block's
 // per-token sum of squares.
 __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next, int cb, const float* hv,
@@ -867,7 +874,7 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
   const Pub h(P.h), Uh(u_of_w(P, l_next, 0)), Ul(u_of_w(P, l_next, 1));
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    const int idx = threadIdx.x + k * MK_WG_THREADS;
+    const int idx = tid() + k * MK_WG_THREADS;
     if (idx < n) {
       const int b = idx / CB, c = cb * CB + idx % CB;
       h.stf(b * H + c, hv[k]);
@@ -879,10 +886,10 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < P.B) {
+  if ((int)tid() < P.B) {
     float s = 0.f;
-    for (int i = 0; i < CB; ++i) s += sm.out[threadIdx.x * CB + i];
-    Pub(ssq_of(P, l_next)).stf(threadIdx.x * P.NB + cb, s);
+    for (int i = 0; i < CB; ++i) s += sm.out[tid() * CB + i];
+    Pub(ssq_of(P, l_next)).stf(tid() * P.NB + cb, s);
   }
 }
 
@@ -912,7 +919,7 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   mark(sm, 1);
   const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
   const Pub KV(P.kv + l * P.s_kv_l), Q(P.q);
-  for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < 2 * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
     if (pp >= np || b >= P.B) continue;
@@ -967,7 +974,7 @@ __device__ __forceinline__ void residual_block(const mk_params& P, int l, int cb
   float hv[NI], gv[NI];
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    const int idx = threadIdx.x + k * MK_WG_THREADS;
+    const int idx = tid() + k * MK_WG_THREADS;
     hv[k] = gv[k] = 0.f;
     if (idx < n) {
       gv[k] = bf2f(gam[cb * CB + idx % CB]);
@@ -999,7 +1006,7 @@ __device__ __forceinline__ void residual_block(const mk_params& P, int l, int cb
 // round trip.
 __device__ __forceinline__ void block_arrive(const mk_params& P, const mk_task& t, int ctr_base, int cb, Smem& sm) {
   sync_published();
-  const int i = threadIdx.x;
+  const int i = tid();
   if (i == 0) sm.old = (int)__hip_atomic_fetch_add(&P.ctr[ctr_base + cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i == 64) sm.t_old[0] = Pub(route_of(P, t.layer)).ldi(0);
   const float w = i < P.B * P.K ? Pub(tkw_of(P, t.layer)).ldf(i) : 0.f;  // B * K <= 512
@@ -1039,7 +1046,7 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
   reduce_tiles(acc, sm);
   mark(sm, 1);
   const Pub AO(P.ao);
-  for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < 4 * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
     if (pp < DP && b < P.B) AO.stf((g * P.B + b) * P.H + (p0 + pp) * 16 + nn, sm.out[o]);
@@ -1075,7 +1082,7 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   reduce_tiles(acc, sm);
   mark(sm, 1);
   const Pub RP(rp_of(P, l));
-  for (int o = threadIdx.x; o < 2 * MT * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < 2 * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m, e = (p0 + pp) * 16 + nn;
     if (pp < np && b < P.B && e < P.E) RP.stf((ks * P.B + b) * P.E + e, sm.out[o] * sm.inv_rms[b]);
@@ -1107,11 +1114,11 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     const Pub S(ssq_of(P, l));
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int i = threadIdx.x + k * MK_WG_THREADS;
+      const int i = tid() + k * MK_WG_THREADS;
       sq[k] = i < B * P.NB ? S.ldf(i) : 0.f;
     }
   }
-  for (int i = threadIdx.x; i < B * E; i += MK_WG_THREADS) {
+  for (int i = tid(); i < B * E; i += MK_WG_THREADS) {
     float p[MK_MAX_RKS];
 #pragma unroll
     for (int k = 0; k < MK_MAX_RKS; ++k) p[k] = k < P.router_ks ? R.ldf(k * B * E + i) : 0.f;
@@ -1128,26 +1135,26 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     T.key[b][e] = ((uint64_t)ord << 32) | (uint32_t)(0xffffu - e);
   }
   // keys past the last expert of each row: zero, below every real key
-  for (int i = threadIdx.x; i < B * 128; i += MK_WG_THREADS)
+  for (int i = tid(); i < B * 128; i += MK_WG_THREADS)
     if (i % 128 >= E) T.key[i / 128][i % 128] = 0ull;
-  if ((int)threadIdx.x < E) T.tokmask[threadIdx.x] = 0u;
+  if ((int)tid() < E) T.tokmask[tid()] = 0u;
   if (!publish) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int i = threadIdx.x + k * MK_WG_THREADS;
+      const int i = tid() + k * MK_WG_THREADS;
       if (i < B * P.NB) sm.ssq[i] = sq[k];
     }
   }
   __syncthreads();
-  if (!publish && (int)threadIdx.x < B) {
-    const float* q = sm.ssq + threadIdx.x * P.NB;
+  if (!publish && (int)tid() < B) {
+    const float* q = sm.ssq + tid() * P.NB;
     float tot = 0.f;
     for (int k = 0; k < P.NB; ++k) tot += q[k];
-    sm.inv_rms[threadIdx.x] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+    sm.inv_rms[tid()] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
   }
   // rank of (b, e): the keys above its own; four threads per pair, each over
   // a quarter of the experts, summed across the four adjacent lanes
-  for (int i = threadIdx.x; i < B * E * 4; i += MK_WG_THREADS) {
+  for (int i = tid(); i < B * E * 4; i += MK_WG_THREADS) {
     const int q = i & 3, pe = i >> 2, b = pe / E, e = pe % E;
     const uint64_t me = T.key[b][e];
     const int j0 = q * 32;
@@ -1168,7 +1175,7 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) {
+  for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
     // softmax over the kept logits (max-subtracted; rank 0 is the max),
     // summed in rank order
     const int b = i / K, j = i % K;
@@ -1185,8 +1192,8 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
   }
   // the experts' positions among the active ones from two wave ballots, and
   // each slot's rank within its expert (tokens in ascending order)
-  if (threadIdx.x < 128) {
-    const int e = threadIdx.x;
+  if (tid() < 128) {
+    const int e = tid();
     const bool act = e < E && T.tokmask[e] != 0u;
     const uint64_t bal = __ballot(act);
     if (lane_id() == 0) T.ballot[e >> 6] = bal;
@@ -1194,8 +1201,8 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
   __syncthreads();
   const uint64_t b0 = T.ballot[0], b1 = E > 64 ? T.ballot[1] : 0ull;
   const int n_active = __popcll(b0) + __popcll(b1);
-  if ((int)threadIdx.x < E) {
-    const int e = threadIdx.x;
+  if ((int)tid() < E) {
+    const int e = tid();
     const uint32_t mask = T.tokmask[e];
     const int a = e < 64 ? __popcll(b0 & ((1ull << e) - 1ull)) : __popcll(b0) + __popcll(b1 & ((1ull << (e - 64)) - 1ull));
     T.apos[e] = a;
@@ -1209,13 +1216,13 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < B * K; i += MK_WG_THREADS) {
+  for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
     const int b = i / K, e = T.sel_idx[b][i % K];
     const int r = __popc(T.tokmask[e] & ((1u << b) - 1u));
     sm.rt_slot[T.apos[e] * B + r] = i;
     if (publish) RT.sti(4 + 2 * E + T.apos[e] * B + r, i);
   }
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     sm.rt_hdr[0] = n_active;
     sm.rt_hdr[1] = n_active * P.up_items_per_expert;
     sm.rt_hdr[2] = n_active * P.down_items_per_expert;
@@ -1237,7 +1244,7 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
                                               int32_t claim2_ctr = -1) {
   const Pub R(route_of(P, l));
   const int E = P.E, B = P.B;
-  const int i = threadIdx.x;
+  const int i = tid();
   int c = 0;
   if (i == 0 && claim_ctr >= 0)
     c = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1367,7 +1374,7 @@ __device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Sme
       reduce_tiles(acc, sm);
       if (k == 0 && first) mark(sm, 2);
       // gu[slot][kh][gate|up][F] for the tokens routed to the expert
-      for (int o = threadIdx.x; o < 2 * cnt * 16; o += MK_WG_THREADS) {
+      for (int o = tid(); o < 2 * cnt * 16; o += MK_WG_THREADS) {
         const int which = o / (cnt * 16), rr = (o / 16) % cnt, nn = o % 16;
         const int slot = sm.rt_slot[a * B + rr], b = slot / K;
         const float v = sm.out[(which * MT + b / 16) * 256 + (b % 16) * 16 + nn];
@@ -1376,8 +1383,8 @@ __device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Sme
     }
     // one drain for the batch, then each item's arrival on its expert's counter
     sync_published();
-    if ((int)threadIdx.x < nb && id0 + (int)threadIdx.x < n_items)
-      __hip_atomic_fetch_add(&P.ctr[done_base + (id0 + (int)threadIdx.x) / upe], 1u, __ATOMIC_RELAXED,
+    if ((int)tid() < nb && id0 + (int)tid() < n_items)
+      __hip_atomic_fetch_add(&P.ctr[done_base + (id0 + (int)tid()) / upe], 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     if (first) mark(sm, 3);
     first = false;
@@ -1420,7 +1427,7 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
   if (stage) {
     if (!wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
     const int n = 16 * F;
-    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
+    for (int i0 = tid(); i0 < n; i0 += 4 * MK_WG_THREADS) {
       float g[4][4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1461,15 +1468,15 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
     }
   }
   reduce_tiles(acc, sm);
-  for (int o = threadIdx.x; o < 8 * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < 8 * 256; o += MK_WG_THREADS) {
     const int pp = o / 256, m = (o / 16) % 16, nn = o % 16;
     const int cb = cb0 + pp / 4, p4 = pp % 4;
     if (pp / 4 < nblk && p4 < DP && m < cnt) DN.stf(sm.rt_slot[a * B + m] * H + (cb * DP + p4) * 16 + nn, sm.out[o]);
   }
   // the blocks' arrivals in one round trip
   sync_published();
-  if ((int)threadIdx.x < nblk)
-    sm.t_old[threadIdx.x] = (int)__hip_atomic_fetch_add(&P.ctr[t.a[4] + cb0 + threadIdx.x], 1u, __ATOMIC_RELAXED,
+  if ((int)tid() < nblk)
+    sm.t_old[tid()] = (int)__hip_atomic_fetch_add(&P.ctr[t.a[4] + cb0 + tid()], 1u, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int last = P.KVH + __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) - 1;
@@ -1563,7 +1570,7 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
     reduce_tiles(acc, sm);
     // gu[slot][kh][gate|up][F] for the tokens routed to the expert: at most
     // 2 x 16 x 16 values, one per thread
-    const int o = threadIdx.x;
+    const int o = tid();
     if (o < 2 * cnt * 16) {
       const int which = o / (cnt * 16), rr = (o / 16) % cnt, nn = o % 16;
       const int slot = sm.rt_slot[a * B + rr], b = slot / K;
@@ -1590,7 +1597,7 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
   sync_published();
   if (lo < hi) {
     const int a0 = lo / upe, a1 = (hi - 1) / upe;
-    const int a = a0 + (int)threadIdx.x;
+    const int a = a0 + (int)tid();
     if (a <= a1) {
       const int n = min(hi, (a + 1) * upe) - max(lo, a * upe);
       __hip_atomic_fetch_add(&P.ctr[done_base + a], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1643,7 +1650,7 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int n = 16 * F;
-    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * MK_WG_THREADS) {
+    for (int i0 = tid(); i0 < n; i0 += 4 * MK_WG_THREADS) {
       float g[4][4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1683,7 +1690,7 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
     __syncthreads();
   }
   reduce_tiles(acc, sm);
-  for (int o = threadIdx.x; o < 4 * MT * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < 4 * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int row = mt * 16 + m;
     if (pp < DP && row < cnt) DN.stf(sm.rt_slot[a * B + row] * H + (cb * DP + pp) * 16 + nn, sm.out[o]);
@@ -1713,13 +1720,13 @@ __device__ __forceinline__ void lm_pair(const mk_params& P, WTile<NP, NCH>& w, c
   const size_t pstride = (size_t)kc * 512;
   if (p + NP < p1) wtile_load(w, P.wlm + (size_t)(p + NP) * pstride, pstride, min(NP, p1 - p - NP), 0, kc);
   reduce_tiles(acc, sm);
-  for (int o = threadIdx.x; o < NP * MT * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < NP * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
     if (pp < np && b < P.B) P.logits[(size_t)b * P.V + (p + pp) * 16 + nn] = sm.out[o] * sm.inv_rms[b];
   }
-  if ((int)threadIdx.x < P.B) {
-    const int b = threadIdx.x, mt = b / 16, m = b % 16;
+  if ((int)tid() < P.B) {
+    const int b = tid(), mt = b / 16, m = b % 16;
     const float inv = sm.inv_rms[b];
     for (int pp = 0; pp < np; ++pp)
       for (int nn = 0; nn < 16; ++nn) {
@@ -1752,9 +1759,9 @@ __device__ __forceinline__ void op_lmhead(const mk_params& P, const mk_task& t, 
   float bv = kNegInf;
   int bi = 0x7fffffff;
   for (int p = p0; p < p1; p += NP) lm_pair(P, w0, Ah, Al, p, min(NP, p1 - p), p1, bv, bi, sm);
-  if ((int)threadIdx.x < P.B) {
-    Pub(P.lm_val).stf(threadIdx.x * P.n_lm_tasks + ord, bv);
-    Pub(P.lm_arg).sti(threadIdx.x * P.n_lm_tasks + ord, bi);
+  if ((int)tid() < P.B) {
+    Pub(P.lm_val).stf(tid() * P.n_lm_tasks + ord, bv);
+    Pub(P.lm_arg).sti(tid() * P.n_lm_tasks + ord, bi);
   }
   const int old = arrive(P, t.a[3], sm);
   if (old == P.n_lm_tasks - 1) final_argmax(P, sm);
@@ -1829,9 +1836,9 @@ template <int D, int MT>
 __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_params Pk) {
   __shared__ Smem sm;
   const mk_params& P = Pk;
-  if (threadIdx.x == 0) sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
+  if (tid() == 0) sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
   if (P.ctr_clear) {
-    for (int i = blockIdx.x * MK_WG_THREADS + threadIdx.x; i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
+    for (int i = blockIdx.x * MK_WG_THREADS + tid(); i < P.n_ctr; i += gridDim.x * MK_WG_THREADS)
       P.ctr_clear[i] = 0u;
   }
   __syncthreads();
@@ -1847,7 +1854,7 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
     const mk_task& t = P.tasks[i];
 #endif
     const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
-    if (threadIdx.x == 0) {
+    if (tid() == 0) {
       sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = sm.t_mark[3] = 0;
       sm.t_waited = t0;  // a task without waits
     }
@@ -1864,7 +1871,7 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
     run_task_mt<D, MT>(P, t, sm);
 #endif
     __syncthreads();
-    if (P.trace && threadIdx.x == 0) {
+    if (P.trace && tid() == 0) {
       // per-task timestamps (100 MHz device clock): start, waits satisfied,
       // op-defined marks, end
       uint32_t* rec = P.trace + (size_t)(P.trace_base + i) * 8;
@@ -1900,14 +1907,14 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_panels(const uint16_
   const uint16_t* s = src + z * src_zstride;
   uint16_t* d = dst + z * dst_zstride;
   const int kc = K / 32;
-  for (int idx = threadIdx.x; idx < 32 * (width / 8); idx += 256) {
+  for (int idx = tid(); idx < 32 * (width / 8); idx += 256) {
     const int row = idx / (width / 8), c8 = idx % (width / 8);
     const uint4 v = *(const uint4*)(s + (size_t)(32 * c + row) * ld + n0 + c8 * 8);
     *(uint4*)&tile[row][c8 * 8] = v;
   }
   __syncthreads();
   const int npan = width / 16;
-  for (int idx = threadIdx.x; idx < npan * 64; idx += 256) {
+  for (int idx = tid(); idx < npan * 64; idx += 256) {
     const int j = idx / 64, l = idx % 64;
     uint16_t tmp[8];
 #pragma unroll
