@@ -143,8 +143,8 @@ class Run:
         torch.cuda.empty_cache()
 
 
-OPNAMES = {1: "EMBED", 2: "QKV", 3: "ATTN (claimer)", 5: "O_PROJ", 6: "ROUTER (+TOPK)", 8: "MOE_UP (claimer)",
-           9: "MOE_DOWN (claimer)", 10: "LM_HEAD"}
+OPNAMES = {1: "EMBED", 2: "QKV", 3: "ATTN (claimer)", 4: "RESIDUAL", 5: "O_PROJ", 6: "ROUTER (+TOPK)",
+           8: "MOE_UP (claimer)", 9: "MOE_FUSED (claimer)", 10: "LM_HEAD"}
 
 
 def op_trace(r, path):
@@ -182,7 +182,7 @@ def op_trace(r, path):
         lines += ["", f"Layer {l} ({'full' if r.m.layer_window(l) == 0 else 'window'} attention): "
                   "first dependency satisfied / median / last end (us from step start)", "",
                   "| opcode | first waited | median waited | last end |", "|---|---:|---:|---:|"]
-        for k in (6, 2, 3, 8, 9, 5):
+        for k in (6, 2, 3, 8, 9, 5, 4):
             m = (layer == l) & (op == k)
             if m.any():
                 lines.append(f"| {OPNAMES[k]} | {waited[m].min():.1f} | {np.median(waited[m]):.1f} | {end[m].max():.1f} |")

@@ -213,7 +213,10 @@ struct Smem {
   int rt_e[128];          // active experts, ascending
   int rt_cnt[128];        // tokens routed to each active expert
   int rt_slot[128 * MK_MAX_BATCH];  // per active expert: its routed slots b * k + j, ascending b
+  int tb[MK_FUSED_B + 1];  // fused MoE residual: each token's range of (claimer, token) rows
 };
+static_assert(2 * MK_FUSED_B * MK_MAX_H + 2 * MK_FUSED_B * 16 <= MK_MAX_BATCH * MK_MAX_F,
+              "fused MoE operands fit the expert hidden-row buffer");
 static_assert(offsetof(Smem, out) % 16 == 0 && offsetof(Smem, act) % 16 == 0 && offsetof(Smem, ssq) % 16 == 0,
               "LDS vectors 16-byte aligned");
 
@@ -465,6 +468,25 @@ __device__ __forceinline__ void mfma_tiles(Acc<NP, MT>& acc, const WTile<NP, NCH
   for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc.c[pp][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Al.a[mt][i]),
+                                                                __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                acc.c[pp][mt], 0, 0, 0);
+        acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Ah.a[mt][i]),
+                                                                __builtin_bit_cast(bf16x8_t, w.v[pp][i]),
+                                                                acc.c[pp][mt], 0, 0, 0);
+      }
+}
+
+// acc += (A hi + A lo) W over this wave's chunks.
+template <int NP, int MT, int NCH>
+__device__ __forceinline__ void mfma_tiles_add(Acc<NP, MT>& acc, const WTile<NP, NCH>& w, const ATile<MT, NCH>& Ah,
+                                               const ATile<MT, NCH>& Al) {
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
 #pragma unroll
@@ -1051,7 +1073,10 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
     const int b = mt * 16 + m;
     if (pp < DP && b < P.B) AO.stf((g * P.B + b) * P.H + (p0 + pp) * 16 + nn, sm.out[o]);
   }
-  block_arrive(P, t, t.a[2], cb, sm);
+  if (t.b[0] == 1)
+    arrive_nr(P, t.a[2]);  // fused MoE: a residual task sums the block
+  else
+    block_arrive(P, t, t.a[2], cb, sm);
 }
 
 // ------------------------------------------------------------------ router
@@ -1698,6 +1723,334 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
   block_arrive(P, t, t.a[4], cb, sm);
 }
 
+
+// ------------------------------------------------------- fused MoE
+// Batches of at most MK_FUSED_B tokens. An item is one 16-row slice s of an
+// active expert's hidden layer: the slice's gate and up columns over the whole
+// K (two K halves on the matrix cores), SiLU(gate) * up scaled by the routing
+// weight of each token routed to the expert, then the slice's 16 rows of the
+// down projection, accumulated per token over the claimer's items (megakernel
+// post, section "Tasks": MOE_UPGATE_ACT and MOE_DOWN with the weighted sum of
+// MOE_COMBINE; the hidden slice never leaves the compute unit, so there is
+// no up/gate-to-down dependency between compute units). Each claimer stores
+// one row per token its items saw; the residual tasks sum the rows.
+
+// Claimer k's share [lo, hi) of n_items: claimers [0, nf) weigh 256, the
+// others wa (of 256). The host schedules the same shares.
+__device__ __forceinline__ void fused_share(int k, int nf, int nt, int wa, int n_items, int& lo, int& hi) {
+  auto pre = [&](int j) -> int64_t { return j <= nf ? (int64_t)j * 256 : (int64_t)nf * 256 + (int64_t)(j - nf) * wa; };
+  const int64_t tot = pre(nt);
+  lo = (int)(n_items * pre(k) / tot);
+  hi = (int)(n_items * pre(k + 1) / tot);
+}
+
+// Tokens (bit b) routed to the active experts of items [lo, hi) (S items per expert).
+__device__ __forceinline__ uint32_t fused_tokens(const mk_params& P, const Smem& sm, int lo, int hi, int S) {
+  uint32_t m = 0u;
+  if (lo < hi)
+    for (int a = lo / S; a <= (hi - 1) / S; ++a)
+      for (int r = 0; r < sm.rt_cnt[a]; ++r) m |= 1u << (sm.rt_slot[a * P.B + r] / P.K);
+  return m;
+}
+
+// Slice s (rows 16 s .. 16 s + 15) of a down projection [F x H] in the
+// panel-tiled layout: in each of the H / 16 panels, one 512-byte half of
+// chunk s / 2. Thread t takes piece t % 32 of that half (column t % 16, rows
+// 8 ((t / 16) % 2) .. + 7 of the slice) in panels t / 32 + 16 j. An invalid
+// slice reads nothing (zeros).
+template <int NJ>
+struct DTile {
+  u32x4_t v[NJ];
+};
+
+template <int NJ>
+__device__ __forceinline__ void dtile_load(DTile<NJ>& d, const uint16_t* base, size_t pstride, int npan, int s,
+                                           bool valid) {
+  const int t = tid();
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0, valid ? npan * (int)pstride * 2 : 0, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int p = (t >> 5) + 16 * j;
+    const int off = p < npan ? (p * (int)pstride + (s >> 1) * 512 + (s & 1) * 256) * 2 + (t & 31) * 16 : 0x7ffffff0;
+    d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
+  }
+}
+
+// Activation operand from the layer input staged in LDS (xs: [MK_FUSED_B][H]
+// bf16, one part of the split pair); rows at or beyond B are zero.
+template <int NCH>
+__device__ __forceinline__ void atile_lds(ATile<1, NCH>& A, const uint16_t* xs, int H, int B, int c0, int c1) {
+  const int wv = wave_id(), ln = lane_id(), row = ln & 15;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = c0 + wv + MK_WAVES * i;
+    A.a[0][i] = (c < c1 && row < B) ? *(const u32x4_t*)(xs + row * H + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int NJ, int NCH>
+__device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int sk = t.b[0], nf = t.b[1], nt = t.b[2], wa = P.waits_enabled ? t.b[3] : 256;
+  const int l = t.layer;
+  const int F = P.F, H = P.H, B = P.B;
+  const int S = F / 16;
+  const int kc = H / 32, kh_chunks = kc / 2;
+  const size_t pstride = (size_t)kc * 512, pstride_d = (size_t)(F / 32) * 512;
+  // LDS: the layer input's split pair [2][MK_FUSED_B][H] (bf16), then the
+  // current slice's weighted hidden values [MK_FUSED_B][16] (float)
+  uint16_t* xs = sm.act;
+  float* actf = reinterpret_cast<float*>(sm.act + 2 * MK_FUSED_B * MK_MAX_H);
+  if (!wait_one(P, t.wait_ctr[0], t.wait_tgt[0], sm)) return;
+  {
+    const Pub Uh(u_of(P, l, 0)), Ul(u_of(P, l, 1));
+    const int n8 = B * H / 8;  // 8 bf16 per thread and load
+    u32x4_t vh[MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS], vl[MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS];
+#pragma unroll
+    for (int k = 0; k < MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS; ++k) {
+      const int i = tid() + k * MK_WG_THREADS;
+      vh[k] = i < n8 ? Uh.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+      vl[k] = i < n8 ? Ul.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS; ++k) {
+      const int i = tid() + k * MK_WG_THREADS;
+      if (i < n8) {
+        *(u32x4_t*)(xs + 8 * i) = vh[k];
+        *(u32x4_t*)(xs + MK_FUSED_B * MK_MAX_H + 8 * i) = vl[k];
+      }
+    }
+  }
+  const uint16_t* xh = xs;
+  const uint16_t* xl = xs + MK_FUSED_B * MK_MAX_H;
+  // the router's partial logits complete: this claimer's own top-k and route
+  if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
+  mark(sm, 0);
+  route_build(P, l, sm, false);
+  mark(sm, 1);
+  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) * S;
+  int lo, hi;
+  fused_share(sk, nf, nt, wa, n_items, lo, hi);
+  auto up_load = [&](WTile<2, NCH>& w, int id, int kh) {
+    const bool valid = id < hi;
+    const int a = valid ? id / S : 0, s = id % S;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * s) * pstride, pstride, valid ? 2 : 0,
+               kh * kh_chunks, (kh + 1) * kh_chunks);
+  };
+  auto down_load = [&](DTile<NJ>& d, int id) {
+    const bool valid = id < hi;
+    const int a = valid ? id / S : 0, s = id % S;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    dtile_load(d, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e, pstride_d, H / 16, s, valid);
+  };
+  float acc[NJ][MK_FUSED_B];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int b = 0; b < MK_FUSED_B; ++b) acc[j][b] = 0.f;
+  {
+    // one item's three weight units in flight while the previous item's
+    // compute: each unit is reissued for the next item as soon as it is used
+    // (an item past the share reads nothing)
+    WTile<2, NCH> wu0, wu1;
+    DTile<NJ> wdn;
+    up_load(wu0, lo, 0);
+    up_load(wu1, lo, 1);
+    down_load(wdn, lo);
+    const int rh = (lane_id() >> 4) & 1;
+    for (int id = lo; id < hi; ++id) {
+      const int a = id / S;
+      Acc<2, 1> ac;
+      {
+        ATile<1, NCH> Ah, Al;
+        atile_lds(Ah, xh, H, B, 0, kh_chunks);
+        atile_lds(Al, xl, H, B, 0, kh_chunks);
+        mfma_tiles(ac, wu0, Ah, Al);
+      }
+      up_load(wu0, id + 1, 0);
+      {
+        ATile<1, NCH> Ah, Al;
+        atile_lds(Ah, xh, H, B, kh_chunks, kc);
+        atile_lds(Al, xl, H, B, kh_chunks, kc);
+        mfma_tiles_add(ac, wu1, Ah, Al);
+      }
+      up_load(wu1, id + 1, 1);
+      reduce_tiles(ac, sm);
+      // weighted SiLU(gate) * up of the slice for every token routed to the expert
+      {
+        const int o = tid();
+        if (o < MK_FUSED_B * 16) {
+          const int b = o >> 4, r = o & 15;
+          float v = 0.f;
+          if (b < B) {
+            int slot = -1;
+            for (int rr = 0; rr < sm.rt_cnt[a]; ++rr) {
+              const int s2 = sm.rt_slot[a * B + rr];
+              if (s2 / P.K == b) slot = s2;
+            }
+            if (slot >= 0) {
+              const float inv = sm.inv_rms[b];
+              const float g = sm.out[b * 16 + r] * inv, u = sm.out[256 + b * 16 + r] * inv;
+              v = sm.tkw[slot] * (g / (1.0f + __expf(-g)) * u);
+            }
+          }
+          actf[o] = v;
+        }
+      }
+      __syncthreads();
+      // the slice's down rows: 8 of them per thread, one token at a time
+#pragma unroll
+      for (int b = 0; b < MK_FUSED_B; ++b) {
+        if (b < B) {
+          const float4 p = *(const float4*)(actf + b * 16 + 8 * rh);
+          const float4 q = *(const float4*)(actf + b * 16 + 8 * rh + 4);
+          const float x[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t w2 = wdn.v[j][k];
+              acc[j][b] = fmaf(x[2 * k + 1], __uint_as_float(w2 & 0xffff0000u),
+                               fmaf(x[2 * k], __uint_as_float(w2 << 16), acc[j][b]));
+            }
+        }
+      }
+      down_load(wdn, id + 1);
+    }
+  }
+  mark(sm, 2);
+  // rows 0-7 and 8-15 of each column, then this claimer's row of each token it saw
+  const uint32_t seen = fused_tokens(P, sm, lo, hi, S);
+  const Pub MP(P.mp);
+  const int t0 = tid(), col = t0 & 15;
+  const bool wr = ((t0 >> 4) & 1) == 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int p = (t0 >> 5) + 16 * j;
+#pragma unroll
+    for (int b = 0; b < MK_FUSED_B; ++b) {
+      const float v = acc[j][b] + __shfl_xor(acc[j][b], 16);
+      if (wr && p < H / 16 && b < B && ((seen >> b) & 1u)) MP.stf((sk * MK_FUSED_B + b) * H + p * 16 + col, v);
+    }
+  }
+  arrive_nr(P, t.sig_ctr[0]);
+  mark(sm, 3);
+}
+
+// The published route of layer l into LDS (header, active experts, token counts, slots).
+__device__ __forceinline__ void route_load(const mk_params& P, int l, Smem& sm) {
+  const Pub R(route_of(P, l));
+  const int E = P.E, B = P.B, i = tid();
+  if (i < 4) sm.rt_hdr[i] = R.ldi(i);
+  if (i < E) {
+    sm.rt_e[i] = R.ldi(4 + i);
+    sm.rt_cnt[i] = R.ldi(4 + E + i);
+  }
+  for (int k = i; k < E * B; k += MK_WG_THREADS) sm.rt_slot[k] = R.ldi(4 + 2 * E + k);
+  __syncthreads();
+}
+
+// Residual add of column block cb once every fused MoE claimer and O
+// projection of the layer has arrived: h += sum_g ao_g + the claimers' rows of
+// each token (summed in claimer order), then the next layer's input and the
+// block's sums of squares. Which claimers hold a row of which token follows
+// from the route and the shares, worked out while the experts still run.
+//   a[0] cb; b[1..3] as for the claimers; wait_ctr[0] every contribution,
+//   wait_ctr[1] the route.
+__device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t, Smem& sm) {
+  const int l = t.layer, cb = t.a[0];
+  const int nf = t.b[1], nt = t.b[2], wa = P.waits_enabled ? t.b[3] : 256;
+  const int H = P.H, CB = P.CB, B = P.B, n = B * CB;
+  const int S = P.F / 16;
+  const int i = tid();
+  // the block's residual stream and gamma, written before this layer began
+  float h0 = 0.f, g0 = 0.f;
+  if (i < n) {
+    const int b = i / CB, c = cb * CB + i % CB;
+    h0 = Pub(P.h).ldf(b * H + c);
+    g0 = bf2f(P.gamma[(size_t)(l + 1) * H + c]);
+  }
+  if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
+  route_load(P, l, sm);
+  // (claimer, token) rows, token-major, claimers ascending: per wave ballots
+  int* list = sm.rt_slot + 128 * MK_FUSED_B;  // past the slots of at most MK_FUSED_B tokens
+  int* wcnt = sm.ired;                         // per wave, one token at a time
+  const int n_items = sm.rt_hdr[0] * S;
+  uint32_t mine = 0u;
+  if (i < nt) {
+    int lo, hi;
+    fused_share(i, nf, nt, wa, n_items, lo, hi);
+    mine = fused_tokens(P, sm, lo, hi, S);
+  }
+  int* tb = sm.tb;
+  if (i == 0) tb[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    const bool has = (mine >> b) & 1u;
+    const uint64_t bal = __ballot(has);
+    if (lane_id() == 0) wcnt[wave_id()] = __popcll(bal);
+    __syncthreads();
+    int before = tb[b];
+    for (int w = 0; w < wave_id(); ++w) before += wcnt[w];
+    if (has) list[before + __popcll(bal & ((1ull << lane_id()) - 1ull))] = i;
+    if (i == 0) {
+      int tot = tb[b];
+      for (int w = 0; w < MK_WAVES; ++w) tot += wcnt[w];
+      tb[b + 1] = tot;
+    }
+    __syncthreads();
+  }
+  // every contribution has arrived
+  if (!wait_one(P, t.wait_ctr[0], t.wait_tgt[0], sm)) return;
+  mark(sm, 0);
+  float av[MK_MAX_KVH];
+  {
+    const int b = i / CB, c = cb * CB + i % CB;
+    const Pub ao(P.ao);
+#pragma unroll
+    for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = (i < n && g < P.KVH) ? ao.ldf((g * B + b) * H + c) : 0.f;
+  }
+  // the rows: thread = (column quad cq, group gq); groups stride the list
+  const int NQ = CB / 4, NG = MK_WG_THREADS / NQ;
+  const int cq = i % NQ, gq = i / NQ;
+  const Pub MP(P.mp);
+  float4* red = reinterpret_cast<float4*>(sm.u.red);  // [MK_FUSED_B][NG][NQ]
+  for (int b = 0; b < B; ++b) {
+    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int p0 = tb[b], p1 = tb[b + 1];
+    for (int p = p0 + gq; p < p1; p += 8 * NG) {
+      float4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pu = p + u * NG;
+        x[u] = pu < p1 ? MP.ldf4((list[pu] * MK_FUSED_B + b) * H + cb * CB + 4 * cq) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s4.x += x[u].x; s4.y += x[u].y; s4.z += x[u].z; s4.w += x[u].w;
+      }
+    }
+    red[(b * NG + gq) * NQ + cq] = s4;
+  }
+  __syncthreads();
+  float hv[MK_MAX_BATCH * 64 / MK_WG_THREADS] = {}, gv[MK_MAX_BATCH * 64 / MK_WG_THREADS] = {};
+  if (i < n) {
+    const int b = i / CB, c4 = (i % CB) / 4, q = i % 4;
+    const float* rf = reinterpret_cast<const float*>(red);
+    float y = 0.f;
+    for (int g = 0; g < NG; ++g) y += rf[((b * NG + g) * NQ + c4) * 4 + q];
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < MK_MAX_KVH; ++g)
+      if (g < P.KVH) a += av[g];
+    hv[0] = (h0 + a) + y;
+    gv[0] = g0;
+  }
+  __syncthreads();
+  write_block_input(P, l + 1, cb, hv, gv, n, sm);
+  arrive_nr(P, t.sig_ctr[0]);
+}
+
 // ----------------------------------------------------------------- LM head
 // LM head over a range of panels, two at a time with the next pair's weights
 // streaming while the current pair computes; each task keeps every token's
@@ -1822,6 +2175,12 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
         op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
       else
         op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm);
+      break;
+    case MK_OP_MOE_FUSED:
+      if (MT == 1) op_moe_fused<2048 / 256, 32 / MK_WAVES>(P, t, sm);
+      break;
+    case MK_OP_RESIDUAL:
+      if (MT == 1) op_residual(P, t, sm);
       break;
     case MK_OP_LMHEAD: op_lmhead<MT, 64 / MK_WAVES, MT == 1 ? 2 : 1>(P, t, sm); break;
     default: wait_task(P, t, sm); break;

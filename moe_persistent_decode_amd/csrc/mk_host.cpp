@@ -40,6 +40,7 @@ struct Schedule {
   std::vector<int> n_qkv;  // QKV tasks per kv group
   std::vector<int> n_attn_claimers;  // per layer
   std::vector<int> moe_fixed;        // per layer: MoE claimers with fixed shares
+  std::vector<int> moe_fused;        // per layer: fused MoE claimers (their count), 0 otherwise
   int n_ctr = 0;
   // counter layout
   int c_resid0 = 0, c_lm = 0, c_layer0 = 0, c_per_layer = 0;
@@ -66,6 +67,7 @@ struct CtrIdx {
   int up_claim, down_claim;  // claim counters of the two expert queues
   int up_done;   // [E] up/gate items done per active expert slot
   int colblk;    // [NB] contributions per residual column block
+  int fin;       // fused MoE: claimers and O projections done
 };
 
 mk_task make_task(int op, int layer) {
@@ -115,7 +117,7 @@ struct mk_handle {
   uint16_t* u = nullptr;
   uint16_t* o = nullptr;
   float *h = nullptr, *q = nullptr, *part = nullptr, *ao = nullptr, *ssq = nullptr, *rp = nullptr,
-        *tk_w = nullptr, *gu = nullptr, *dn = nullptr, *lm_val = nullptr;
+        *tk_w = nullptr, *gu = nullptr, *dn = nullptr, *mp = nullptr, *lm_val = nullptr;
   int32_t *tk_idx = nullptr, *route = nullptr, *lm_arg = nullptr;
   uint32_t* ctr[2] = {nullptr, nullptr};
   int n_ctr_cap = 0;
@@ -266,7 +268,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   idx += L + 1;
   S->c_lm = idx++;
   S->c_layer0 = idx;
-  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + 1 + E + NB;
+  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + 1 + E + NB + 1;
   idx += L * S->c_per_layer;
   S->n_ctr = idx;
   auto resid = [&](int l) { return S->c_resid0 + l; };  // input of layer l ready
@@ -287,6 +289,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     x.up_done = b0;
     b0 += E;
     x.colblk = b0;
+    b0 += NB;
+    x.fin = b0;
     return x;
   };
 
@@ -408,6 +412,60 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       if (n_free >= n_w / 4) wa = 0;
       if (n_free == 0 && wa == 0) wa = 256;
     }
+    // Fused MoE (at most MK_FUSED_B tokens): the same shares over (expert,
+    // hidden slice) items; claimers whose share is empty by weight (wa = 0)
+    // are left out, and a residual task per column block sums the claimers'
+    // rows once all of them and the O projections have arrived.
+    const bool fused = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
+    if (fused) {
+      S->moe_fixed.push_back(0);
+      const int nt = wa == 0 ? n_free : S->n_up_claimers;
+      S->moe_fused.push_back(nt);
+      int k_free = 0, k_attn = n_free;
+      for (int i = 0; i < S->n_up_claimers; ++i) {
+        const int cu = (moe_flat0 + i) % n_w;
+        if (wa == 0 && attn_cu[cu]) continue;
+        mk_task t = make_task(MK_OP_MOE_FUSED, l);
+        t.b[0] = attn_cu[cu] ? k_attn++ : k_free++;
+        t.b[1] = n_free;
+        t.b[2] = nt;
+        t.b[3] = wa;
+        add_wait(t, resid(l), NB);
+        add_wait(t, x.router, h->n_router_tasks);
+        t.sig_ctr[0] = x.fin;
+        push_at(t, cu);
+      }
+      if (k_free + k_attn - n_free != nt) std::abort();
+      begin_wave();
+      int n_oproj = 0;
+      for (int g = 0; g < KVH; ++g)
+        for (int cb = 0; cb < NB; ++cb) {
+          mk_task t = make_task(MK_OP_OPROJ, l);
+          t.a[0] = g;
+          t.a[1] = cb;
+          t.a[2] = x.fin;
+          t.b[0] = 1;
+          add_wait(t, x.comb + g, B);
+          push_at(t, (attn_flat0 + n_oproj % n_attn) % n_w);
+          ++n_oproj;
+        }
+      S->n_oproj = n_oproj;
+      // residual tasks on the attention units, after their O projections
+      begin_wave();
+      for (int cb = 0; cb < NB; ++cb) {
+        mk_task t = make_task(MK_OP_RESIDUAL, l);
+        t.a[0] = cb;
+        t.b[1] = n_free;
+        t.b[2] = nt;
+        t.b[3] = wa;
+        add_wait(t, x.fin, nt + n_oproj);
+        add_wait(t, x.route, 1);
+        t.sig_ctr[0] = resid(l + 1);
+        push_at(t, (attn_flat0 + (n_oproj + cb) % n_attn) % n_w);
+      }
+      continue;
+    }
+    S->moe_fused.push_back(0);
     S->moe_fixed.push_back(fixed ? 1 : 0);
     int k_free = 0, k_attn = n_free;
     for (int i = 0; i < S->n_up_claimers; ++i) {
@@ -555,6 +613,8 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
         switch (t.op) {
           case MK_OP_EMBED:
           case MK_OP_QKV:
+          case MK_OP_MOE_FUSED:
+          case MK_OP_RESIDUAL:
             ctr[t.sig_ctr[0]]++;
             done();
             break;
@@ -563,7 +623,10 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
             done();
             break;
           case MK_OP_OPROJ:
-            block(t, t.a[2], t.a[1], t.layer);
+            if (t.b[0] == 1)
+              ctr[t.a[2]]++;
+            else
+              block(t, t.a[2], t.a[1], t.layer);
             done();
             break;
           case MK_OP_LMHEAD:
@@ -677,10 +740,12 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
     want[k++] = 1;                                                   // route finalized
     want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
-    want[k++] = S.moe_fixed[l] ? 0 : (int64_t)n_active[l] * up_per_e + S.n_up_claimers;
-    want[k++] = S.moe_fixed[l] ? 0 : (int64_t)n_active[l] * down_per_e + S.n_up_claimers;
-    for (int a = 0; a < E; ++a) want[k++] = a < n_active[l] ? up_per_e : 0;
-    for (int cb = 0; cb < NB; ++cb) want[k++] = KVH + n_active[l];
+    const bool fused = S.moe_fused[l] > 0, claiming = !S.moe_fixed[l] && !fused;
+    want[k++] = claiming ? (int64_t)n_active[l] * up_per_e + S.n_up_claimers : 0;
+    want[k++] = claiming ? (int64_t)n_active[l] * down_per_e + S.n_up_claimers : 0;
+    for (int a = 0; a < E; ++a) want[k++] = (!fused && a < n_active[l]) ? up_per_e : 0;
+    for (int cb = 0; cb < NB; ++cb) want[k++] = fused ? 0 : KVH + n_active[l];
+    want[k++] = fused ? S.moe_fused[l] + S.n_oproj : 0;  // fused MoE: claimers and O projections
   }
   for (int i = 0; i < S.n_ctr; ++i)
     if (ctr[i] != want[i]) {
@@ -856,6 +921,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   const size_t s_tki = stake((size_t)L * Bm * K * 4), s_tkw = stake((size_t)L * Bm * K * 4);
   const size_t s_route = stake((size_t)L * MK_ROUTE_INTS(E, Bm) * 4);
   const size_t s_gu = stake((size_t)Bm * K * 4 * F * 4), s_dn = stake((size_t)Bm * K * H * 4);
+  const size_t s_mp = stake((size_t)std::max(h->n_workers, 1) * MK_FUSED_B * H * 4);
   const size_t s_lmv = stake((size_t)Bm * h->n_lm_tasks * 4), s_lma = stake((size_t)Bm * h->n_lm_tasks * 4);
   const size_t s_err = stake(16);
   if (hipMalloc(&h->scratch, so) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "scratch");
@@ -874,11 +940,12 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->route = (int32_t*)(sb + s_route);
   h->gu = (float*)(sb + s_gu);
   h->dn = (float*)(sb + s_dn);
+  h->mp = (float*)(sb + s_mp);
   h->lm_val = (float*)(sb + s_lmv);
   h->lm_arg = (int32_t*)(sb + s_lma);
   h->err_word = (uint32_t*)(sb + s_err);
   // counters: capacity for the largest batch
-  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 5 + E + h->NB);
+  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 5 + E + h->NB + 1);
   for (int i = 0; i < 2; ++i) {
     if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
     hipMemset(h->ctr[i], 0, (size_t)h->n_ctr_cap * 4);
@@ -1044,6 +1111,7 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.route = h->route;
   P.gu = h->gu;
   P.dn = h->dn;
+  P.mp = h->mp;
   P.lm_val = h->lm_val;
   P.lm_arg = h->lm_arg;
   P.n_ctr = h->n_ctr_cap;  // clear the whole capacity: schedules differ in size
@@ -1160,6 +1228,7 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
       {"route", h->route, (size_t)MK_ROUTE_INTS(E, Bm) * 4},
       {"gu", h->gu, Bm * K * 4 * c.expert_ffn * 4},
       {"dn", h->dn, Bm * K * H * 4},
+      {"mp", h->mp, (size_t)std::max(h->n_workers, 1) * MK_FUSED_B * H * 4},
   };
   for (const Item& it : items)
     if (std::strcmp(it.n, name) == 0) {

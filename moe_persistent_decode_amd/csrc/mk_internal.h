@@ -22,10 +22,15 @@
 #define MK_MAX_KVH 8    // kv heads
 #define MK_MAX_RKS 4    // router K splits
 #define MK_MAX_F 768    // expert width
+#define MK_MAX_H 2048   // hidden size
 #define MK_MAX_BATCH 32
 // Attention combine: split partials in flight per thread (16-byte loads)
 #define MK_COMB_SB 16 // sequences per step (two row tiles of 16)
 #define MK_UP_BATCH_MAX 4  // expert up/gate items claimed together
+// Batches up to this size run the fused MoE: each claimer takes 16-row
+// slices of the active experts' hidden layer through up/gate, SiLU and down,
+// and stores one partial output row per token it saw; residual tasks sum them.
+#define MK_FUSED_B 4
 #define MK_TASK_INTS 32
 
 // Opcodes. The post names sixteen opcodes for its model family; this model
@@ -40,10 +45,13 @@ enum mk_opcode : int32_t {
   MK_OP_EMBED = 1,        // embedding rows of one column block: layer 0's input
   MK_OP_QKV = 2,          // QKV panels + RoPE + paged KV append
   MK_OP_ATTN = 3,         // split-KV partial attention (+ combine when last)
+  MK_OP_RESIDUAL = 4,     // residual + MoE combine of one column block, the next layer's input (fused MoE)
   MK_OP_OPROJ = 5,        // O projection, split-K by kv group, one column block (+ residual when last)
   MK_OP_ROUTER = 6,       // router logits over a K range (+ top-k / finalize when last)
   MK_OP_MOE_UP = 8,       // MoE claimer: (expert, gate/up panel pair, K half) items, then
                           // (expert, column block) down items (+ residual when last)
+  MK_OP_MOE_FUSED = 9,    // MoE claimer, small batches: (expert, 16-row hidden slice) items through
+                          // up/gate, SiLU and down, one partial output row per token
   MK_OP_LMHEAD = 10,      // LM head panels + argmax candidate (+ greedy token when last)
   MK_OP_COUNT = 11
 };
@@ -116,6 +124,7 @@ struct mk_params {
   int32_t* route;
   float* gu;     // [B*K][2 K halves][gate, up][F] expert up/gate partial sums
   float* dn;     // [B*K][H] expert outputs
+  float* mp;     // fused MoE: [claimer][MK_FUSED_B][H] partial outputs (routing weights applied)
   float* lm_val; int32_t* lm_arg; // [B][n_lm_tasks] LM head argmax candidates
   // synchronisation
   uint32_t* ctr;        // counters of this step

@@ -155,22 +155,52 @@ def test_step_bytes_window_and_batch():
     assert b - a == 12 * sol.kv_bytes_per_token(m)
 
 
-@pytest.mark.parametrize("batch,seq", [(1, 8192), (4, 65536)])
+@pytest.mark.parametrize("batch,seq", [(1, 8192), (4, 65536), (8, 16384)])
 def test_fixed_moe_shares_follow_the_placement(batch, seq):
-    """MoE claimers with fixed shares: per layer the indices are a permutation
-    of the claimers, those on compute units without an attention claimer in
-    that layer come first, and their count is the one the tasks carry."""
+    """MoE claimers with fixed shares (fused up to 4 tokens): per layer the
+    indices are a permutation of the claimers, those on compute units without
+    an attention claimer in that layer come first, and their count is the one
+    the tasks carry."""
     m = configs.FULL48 if batch == 1 else configs.small_variant(configs.FULL48, n_layers=2)
     d = _host(m, batch=batch, max_seq=seq + 64)
     tasks, off = d.schedule_export(batch, seq)
     ops, layer = tasks[:, 0] & 0xFF, tasks[:, 1]
     cu = np.searchsorted(off, np.arange(len(tasks)), side="right") - 1
+    want_op = 9 if batch <= 4 else 8
     for l in range(m.n_layers):
-        moe = np.nonzero((ops == 8) & (layer == l))[0]
+        moe = np.nonzero((ops == want_op) & (layer == l))[0]
+        assert len(moe) > 0
         attn_cus = set(cu[(ops == 3) & (layer == l)].tolist())
         k, nf, nt = tasks[moe, 16], tasks[moe, 17], tasks[moe, 18]
         assert np.all(nt == len(moe)) and sorted(k.tolist()) == list(range(len(moe)))
         free = np.array([c not in attn_cus for c in cu[moe]])
         assert np.all(nf == free.sum())
         assert np.all(k[free] < nf[0]) and np.all(k[~free] >= nf[0])
+    d.close()
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_fused_moe_residual_tasks(batch):
+    """Fused MoE layers: one residual task per column block, each waiting for
+    every claimer and O projection of its layer (plain arrivals on one
+    counter) and signalling the next layer's input; no task of the layer uses
+    the per-block arrival counters."""
+    m = configs.small_variant(configs.FULL48, n_layers=3)
+    d = _host(m, batch=batch, max_seq=8192 + 64)
+    tasks, off = d.schedule_export(batch, 8192)
+    ops, layer = tasks[:, 0] & 0xFF, tasks[:, 1]
+    wait_c, wait_t, sig = tasks[:, 8:11], tasks[:, 11:14], tasks[:, 14]
+    NB = m.hidden // 64
+    for l in range(m.n_layers):
+        res = np.nonzero((ops == 4) & (layer == l))[0]
+        assert sorted(tasks[res, 2].tolist()) == list(range(NB))
+        moe = np.nonzero((ops == 9) & (layer == l))[0]
+        op = np.nonzero((ops == 5) & (layer == l))[0]
+        fin = set(sig[moe].tolist()) | set(tasks[op, 4].tolist())
+        assert len(fin) == 1 and np.all(tasks[op, 16] == 1)
+        (fin,) = fin
+        for r in res:
+            j = list(wait_c[r]).index(fin)
+            assert wait_t[r, j] == len(moe) + len(op)
+        assert len(set(sig[res].tolist())) == 1
     d.close()

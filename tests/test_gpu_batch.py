@@ -120,6 +120,18 @@ def test_batch4_ragged(mode):
     _run(4, 20, 150, seed=22, mode=mode)
 
 
+def test_batch2_fused_moe():
+    """Two tokens through the fused MoE (slices of up/gate + down per claimer,
+    partial rows summed by the residual tasks)."""
+    _run(2, 30, 170, seed=45, mode=0)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_batch8_fixed_shares(mode):
+    """Eight tokens: up/gate items and down pairs in fixed shares."""
+    _run(8, 20, 150, seed=31, mode=mode)
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_batch32_ragged_two_row_tiles(mode):
     _run(32, 16, 200, seed=12, mode=mode)

@@ -144,10 +144,13 @@ def _stages_layer1(c, tr):
     close("router", rp.sum(0), tr.router_logits[0])
     idx = d.debug_read("tk_idx", (1, K), "int32")
     assert sorted(idx[0].tolist()) == sorted(tr.topk_idx[0][0].tolist())
-    dn = d.debug_read("dn", (K, H))
-    order = [list(idx[0]).index(e) for e in tr.topk_idx[0][0]]
-    close("experts", dn[order], tr.expert_out[0][0])
-    close("h", d.debug_read("h", (1, H)), tr.h_out[0])
+    # one token runs the fused MoE (no per-expert rows): the combined expert
+    # output, from the new residual less its input and the attention projection
+    h_out = d.debug_read("h", (1, H))
+    h_in = od.bf16_to_float(c.W("emb")[int(c.bs.tokens[0])], np.float64)
+    ao = d.debug_read("ao", (KVH, 1, H)).sum(0)
+    close("experts", h_out[0] - h_in - ao[0], tr.moe_out[0][0])
+    close("h", h_out, tr.h_out[0])
 
 
 def _run(wl, steps, mode, stages):
