@@ -2013,26 +2013,34 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
   // the rows: thread = (column quad cq, group gq); groups stride the list
   const int NQ = CB / 4, NG = MK_WG_THREADS / NQ;
   const int cq = i % NQ, gq = i / NQ;
-  const Pub MP(P.mp);
+  // the rows through a resource over exactly the claimers' rows: a row past
+  // the token's list reads past the end (zeros), so the loads carry no branch
+  const __amdgpu_buffer_rsrc_t mr =
+      __builtin_amdgcn_make_buffer_rsrc(P.mp, (short)0, nt * MK_FUSED_B * H * 4, 0x00020000);
   float4* red = reinterpret_cast<float4*>(sm.u.red);  // [MK_FUSED_B][NG][NQ]
   for (int b = 0; b < B; ++b) {
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     const int p0 = tb[b], p1 = tb[b + 1];
     for (int p = p0 + gq; p < p1; p += 8 * NG) {
-      float4 x[8];
+      u32x4_t x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int pu = p + u * NG;
-        x[u] = pu < p1 ? MP.ldf4((list[pu] * MK_FUSED_B + b) * H + cb * CB + 4 * cq) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int off = pu < p1 ? ((list[pu] * MK_FUSED_B + b) * H + cb * CB + 4 * cq) * 4 : 0x7ffffff0;
+        x[u] = __builtin_amdgcn_raw_buffer_load_b128(mr, off, 0, kSC1);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        s4.x += x[u].x; s4.y += x[u].y; s4.z += x[u].z; s4.w += x[u].w;
+        s4.x += __uint_as_float(x[u][0]);
+        s4.y += __uint_as_float(x[u][1]);
+        s4.z += __uint_as_float(x[u][2]);
+        s4.w += __uint_as_float(x[u][3]);
       }
     }
     red[(b * NG + gq) * NQ + cq] = s4;
   }
   __syncthreads();
+  mark(sm, 1);
   float hv[MK_MAX_BATCH * 64 / MK_WG_THREADS] = {}, gv[MK_MAX_BATCH * 64 / MK_WG_THREADS] = {};
   if (i < n) {
     const int b = i / CB, c4 = (i % CB) / 4, q = i % 4;
@@ -2048,7 +2056,9 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
   }
   __syncthreads();
   write_block_input(P, l + 1, cb, hv, gv, n, sm);
+  mark(sm, 2);
   arrive_nr(P, t.sig_ctr[0]);
+  mark(sm, 3);
 }
 
 // ----------------------------------------------------------------- LM head

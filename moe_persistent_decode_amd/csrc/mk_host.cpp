@@ -450,8 +450,13 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           ++n_oproj;
         }
       S->n_oproj = n_oproj;
-      // residual tasks on the attention units, after their O projections
+      // residual tasks on the units that get no router or QKV task of the
+      // next layer (round-robin from the flat index after these tasks), so
+      // those tasks' weights still stream before the layer input is ready
       begin_wave();
+      int n_qkv_tasks = 0;
+      for (int g = 0; g < KVH; ++g) n_qkv_tasks += S->n_qkv[g];
+      const int next0 = (int)S->flat.size() + NB + h->n_router_tasks + n_qkv_tasks;
       for (int cb = 0; cb < NB; ++cb) {
         mk_task t = make_task(MK_OP_RESIDUAL, l);
         t.a[0] = cb;
@@ -461,7 +466,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         add_wait(t, x.fin, nt + n_oproj);
         add_wait(t, x.route, 1);
         t.sig_ctr[0] = resid(l + 1);
-        push_at(t, (attn_flat0 + (n_oproj + cb) % n_attn) % n_w);
+        push_at(t, (next0 + cb) % n_w);
       }
       continue;
     }
