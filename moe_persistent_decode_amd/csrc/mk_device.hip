@@ -904,14 +904,12 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
       split_bf16(hv[k] * gv[k], hi, lo);
       Uh.st16(b * H + c, hi);
       Ul.st16(b * H + c, lo);
-      sm.out[idx] = hv[k] * hv[k];
     }
-  }
-  __syncthreads();
-  if ((int)tid() < P.B) {
-    float s = 0.f;
-    for (int i = 0; i < CB; ++i) s += sm.out[tid() * CB + i];
-    Pub(ssq_of(P, l_next)).stf(tid() * P.NB + cb, s);
+    // the row's sum of squares across its CB lanes (a row never straddles
+    // a wave: CB divides 64), butterfly order
+    float sq = idx < n ? hv[k] * hv[k] : 0.f;
+    for (int o = 1; o < CB; o <<= 1) sq += __shfl_xor(sq, o);
+    if (idx < n && idx % CB == 0) Pub(ssq_of(P, l_next)).stf((idx / CB) * P.NB + cb, sq);
   }
 }
 
@@ -2011,13 +2009,15 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
     for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = (i < n && g < P.KVH) ? ao.ldf((g * B + b) * H + c) : 0.f;
   }
   // the rows: thread = (column quad cq, group gq); groups stride the list
+  // (a row's NQ quads in adjacent lanes, so each load instruction reads whole
+  // rows; the groups of a wave summed with a butterfly, then the 8 waves')
   const int NQ = CB / 4, NG = MK_WG_THREADS / NQ;
   const int cq = i % NQ, gq = i / NQ;
   // the rows through a resource over exactly the claimers' rows: a row past
   // the token's list reads past the end (zeros), so the loads carry no branch
   const __amdgpu_buffer_rsrc_t mr =
       __builtin_amdgcn_make_buffer_rsrc(P.mp, (short)0, nt * MK_FUSED_B * H * 4, 0x00020000);
-  float4* red = reinterpret_cast<float4*>(sm.u.red);  // [MK_FUSED_B][NG][NQ]
+  float4* red = reinterpret_cast<float4*>(sm.u.red);  // [MK_FUSED_B][MK_WAVES][NQ]
   for (int b = 0; b < B; ++b) {
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     const int p0 = tb[b], p1 = tb[b + 1];
@@ -2037,16 +2037,23 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
         s4.w += __uint_as_float(x[u][3]);
       }
     }
-    red[(b * NG + gq) * NQ + cq] = s4;
+    for (int o = NQ; o < 64; o <<= 1) {
+      s4.x += __shfl_xor(s4.x, o);
+      s4.y += __shfl_xor(s4.y, o);
+      s4.z += __shfl_xor(s4.z, o);
+      s4.w += __shfl_xor(s4.w, o);
+    }
+    if (lane_id() < NQ) red[(b * MK_WAVES + wave_id()) * NQ + cq] = s4;
   }
   __syncthreads();
   mark(sm, 1);
   float hv[MK_MAX_BATCH * 64 / MK_WG_THREADS] = {}, gv[MK_MAX_BATCH * 64 / MK_WG_THREADS] = {};
   if (i < n) {
-    const int b = i / CB, c4 = (i % CB) / 4, q = i % 4;
+    const int b = i / CB;
     const float* rf = reinterpret_cast<const float*>(red);
     float y = 0.f;
-    for (int g = 0; g < NG; ++g) y += rf[((b * NG + g) * NQ + c4) * 4 + q];
+#pragma unroll
+    for (int w = 0; w < MK_WAVES; ++w) y += rf[(b * MK_WAVES + w) * CB + i % CB];
     float a = 0.f;
 #pragma unroll
     for (int g = 0; g < MK_MAX_KVH; ++g)
