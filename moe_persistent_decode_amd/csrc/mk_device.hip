@@ -76,6 +76,45 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // The thread's index in the workgroup, from the two above.
 __device__ __forceinline__ int tid() { return (wave_id() << 6) | lane_id(); }
 
+// The value of lane (this lane ^ M). Masks below 32 go through ds_swizzle,
+// whose pattern is an immediate: no per-lane address register, which the
+// compiler would otherwise hoist out of the task loop and keep live through
+// every op (as it does for ds_bpermute addresses). Mask 32 uses ds_bpermute.
+template <int M>
+__device__ __forceinline__ int xor_lane(int v) {
+  static_assert(M > 0 && M <= 32 && (M & (M - 1)) == 0, "power-of-two lane mask");
+  if constexpr (M < 32)
+    return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1f);
+  else
+    return __builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, v);
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  return __int_as_float(xor_lane<M>(__float_as_int(v)));
+}
+// Sum over aligned groups of n lanes (n a power of two, at most 64; every
+// lane of a group ends with its sum), butterfly order.
+__device__ __forceinline__ float group_sum(float v, int n) {
+  if (n > 1) v += xor_lane<1>(v);
+  if (n > 2) v += xor_lane<2>(v);
+  if (n > 4) v += xor_lane<4>(v);
+  if (n > 8) v += xor_lane<8>(v);
+  if (n > 16) v += xor_lane<16>(v);
+  if (n > 32) v += xor_lane<32>(v);
+  return v;
+}
+// Sum over the lanes of a wave that share the lane bits below m (m a power
+// of two, at most 32): lanes l, l ^ m, l ^ 2m, ...
+__device__ __forceinline__ float group_sum_above(float v, int m) {
+  if (m <= 1) v += xor_lane<1>(v);
+  if (m <= 2) v += xor_lane<2>(v);
+  if (m <= 4) v += xor_lane<4>(v);
+  if (m <= 8) v += xor_lane<8>(v);
+  if (m <= 16) v += xor_lane<16>(v);
+  if (m <= 32) v += xor_lane<32>(v);
+  return v;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // float -> bf16 bits, round to nearest even
 __device__ __forceinline__ uint32_t f2bf(float f) {
@@ -353,19 +392,29 @@ __device__ __forceinline__ float* ssq_of(const mk_params& P, int l) {
   return P.ssq + (size_t)(l & 1) * P.B * P.NB;
 }
 
-// 1/sqrt(mean(h^2) + eps) of every token of layer l's input, from the column
-// blocks' sums of squares (summed in block order), into sm.inv_rms.
+// 1/sqrt(mean(h^2) + eps) of every token from the column blocks' sums of
+// squares in sm.ssq ([B][NB], written before a barrier): 32 lanes per token,
+// each summing every 32nd block, then a butterfly; into sm.inv_rms.
+__device__ __forceinline__ void inv_rms_lds(const mk_params& P, Smem& sm) {
+  const int NB = P.NB;
+#pragma unroll
+  for (int k = 0; k < MK_MAX_BATCH * 32 / MK_WG_THREADS; ++k) {
+    const int i = tid() + k * MK_WG_THREADS, b = i >> 5, j = i & 31;
+    float v = 0.f;
+    if (b < P.B)
+      for (int q = j; q < NB; q += 32) v += sm.ssq[b * NB + q];
+    v = group_sum(v, 32);
+    if (b < P.B && j == 0) sm.inv_rms[b] = 1.0f / sqrtf(v / (float)P.H + P.eps);
+  }
+}
+
+// The same for layer l's input, loading the sums of squares.
 __device__ __forceinline__ void load_inv_rms(const mk_params& P, int l, Smem& sm) {
   const Pub S(ssq_of(P, l));
   const int n = P.B * P.NB;
   for (int i = tid(); i < n; i += MK_WG_THREADS) sm.ssq[i] = S.ldf(i);
   __syncthreads();
-  if ((int)tid() < P.B) {
-    const float* q = sm.ssq + tid() * P.NB;
-    float tot = 0.f;
-    for (int k = 0; k < P.NB; ++k) tot += q[k];
-    sm.inv_rms[tid()] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
-  }
+  inv_rms_lds(P, sm);
   __syncthreads();
 }
 
@@ -665,8 +714,8 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
       sv[i] = (pos >= lo && pos <= p) ? sacc[i] * scale : kNegInf;
       mloc = fmaxf(mloc, sv[i]);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = fmaxf(mloc, xor_lane<16>(mloc));
+    mloc = fmaxf(mloc, xor_lane<32>(mloc));
     const float mnew = fmaxf(m, mloc);
     if (mnew != kNegInf) {
       const float alpha = (m == kNegInf) ? 0.f : __expf(m - mnew);
@@ -678,8 +727,8 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
         pb[i] = f2bf(pv);
         ps += bf2f((uint16_t)pb[i]);
       }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps += xor_lane<16>(ps);
+      ps += xor_lane<32>(ps);
       lsum = lsum * alpha + ps;
       m = mnew;
       const s16x4_t pB = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
@@ -908,7 +957,7 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
     // the row's sum of squares across its CB lanes (a row never straddles
     // a wave: CB divides 64), butterfly order
     float sq = idx < n ? hv[k] * hv[k] : 0.f;
-    for (int o = 1; o < CB; o <<= 1) sq += __shfl_xor(sq, o);
+    sq = group_sum(sq, CB);
     if (idx < n && idx % CB == 0) Pub(ssq_of(P, l_next)).stf((idx / CB) * P.NB + cb, sq);
   }
 }
@@ -1169,12 +1218,7 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   __syncthreads();
-  if (!publish && (int)tid() < B) {
-    const float* q = sm.ssq + tid() * P.NB;
-    float tot = 0.f;
-    for (int k = 0; k < P.NB; ++k) tot += q[k];
-    sm.inv_rms[tid()] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
-  }
+  if (!publish) inv_rms_lds(P, sm);
   // rank of (b, e): the keys above its own; four threads per pair, each over
   // a quarter of the experts, summed across the four adjacent lanes
   for (int i = tid(); i < B * E * 4; i += MK_WG_THREADS) {
@@ -1187,8 +1231,8 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
       const uint64_t k0 = T.key[b][j0 + j], k1 = T.key[b][j0 + j + 1];
       rank += (k0 > me) + (k1 > me);
     }
-    rank += __shfl_xor(rank, 1);
-    rank += __shfl_xor(rank, 2);
+    rank += xor_lane<1>(rank);
+    rank += xor_lane<2>(rank);
     if (q == 0 && rank < K) {
       T.sel_idx[b][rank] = e;
       T.sel_val[b][rank] = T.logit[b][e];
@@ -1286,12 +1330,7 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
   }
   if (i == 0) sm.claim = c;
   __syncthreads();
-  if (l >= 0 && i < B) {
-    const float* q = sm.ssq + i * P.NB;
-    float tot = 0.f;
-    for (int k = 0; k < P.NB; ++k) tot += q[k];
-    sm.inv_rms[i] = 1.0f / sqrtf(tot / (float)P.H + P.eps);
-  }
+  if (l >= 0) inv_rms_lds(P, sm);
   __syncthreads();
 }
 
@@ -1928,7 +1967,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     const int p = (t0 >> 5) + 16 * j;
 #pragma unroll
     for (int b = 0; b < MK_FUSED_B; ++b) {
-      const float v = acc[j][b] + __shfl_xor(acc[j][b], 16);
+      const float v = acc[j][b] + xor_lane<16>(acc[j][b]);
       if (wr && p < H / 16 && b < B && ((seen >> b) & 1u)) MP.stf((sk * MK_FUSED_B + b) * H + p * 16 + col, v);
     }
   }
@@ -2037,12 +2076,11 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
         s4.w += __uint_as_float(x[u][3]);
       }
     }
-    for (int o = NQ; o < 64; o <<= 1) {
-      s4.x += __shfl_xor(s4.x, o);
-      s4.y += __shfl_xor(s4.y, o);
-      s4.z += __shfl_xor(s4.z, o);
-      s4.w += __shfl_xor(s4.w, o);
-    }
+    // (the wave's groups: lanes that differ in the bits above the quad index)
+    s4.x = group_sum_above(s4.x, NQ);
+    s4.y = group_sum_above(s4.y, NQ);
+    s4.z = group_sum_above(s4.z, NQ);
+    s4.w = group_sum_above(s4.w, NQ);
     if (lane_id() < NQ) red[(b * MK_WAVES + wave_id()) * NQ + cq] = s4;
   }
   __syncthreads();
@@ -2159,12 +2197,15 @@ __device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm) {
       for (int u = 0; u < 4; ++u)
         if (cv[u] > v || (cv[u] == v && ci[u] < ix)) { v = cv[u]; ix = ci[u]; }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(v, o);
-      const int oi = __shfl_xor(ix, o);
+    auto step = [&](float ov, int oi) {
       if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
-    }
+    };
+    step(xor_lane<32>(v), xor_lane<32>(ix));
+    step(xor_lane<16>(v), xor_lane<16>(ix));
+    step(xor_lane<8>(v), xor_lane<8>(ix));
+    step(xor_lane<4>(v), xor_lane<4>(ix));
+    step(xor_lane<2>(v), xor_lane<2>(ix));
+    step(xor_lane<1>(v), xor_lane<1>(ix));
     if (ln == 0) {
       if (P.next_tokens) P.next_tokens[b] = ix;
       if (P.flags & 1u) {
