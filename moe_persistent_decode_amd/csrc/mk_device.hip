@@ -1093,16 +1093,18 @@ __device__ __forceinline__ void block_arrive(const mk_params& P, const mk_task& 
 // ------------------------------------------------------------------ O proj
 // O projection split-K by kv group: group g's heads contribute their slice
 // of the K dimension as soon as that group's attention lands (megakernel
-// post, section "Drop false dependencies"); one task per (group, column block).
-template <int MT, int NCH>
+// post, section "Drop false dependencies"); one task per (group, column block),
+// or (NPO = 8, a[3] = 2) per (group, two adjacent column blocks), whose 256 KB
+// of weights all stream before the wait.
+template <int MT, int NCH, int NPO>
 __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int l = t.layer, g = t.a[0], cb = t.a[1];
-  const int DP = P.CB / 16, p0 = cb * DP;
+  const int l = t.layer, g = t.a[0], cb = t.a[1], nblk = NPO == 8 ? t.a[3] : 1;
+  const int DP = P.CB / 16, p0 = cb * DP, np = DP * nblk;
   const int kc = P.QH * P.D / 32;
   const int c0 = g * P.G * P.D / 32, c1 = c0 + P.G * P.D / 32;
   const size_t pstride = (size_t)kc * 512;
-  WTile<4, NCH> w;
-  wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, DP, c0, c1);
+  WTile<NPO, NCH> w;
+  wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, np, c0, c1);
   if (!wait_task(P, t, sm)) return;
   mark(sm, 0);
   set_rows_batch(P, sm, 0, P.QH * P.D, 0);
@@ -1110,15 +1112,15 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
   ATile<MT, NCH> Ah, Al;
   atile_load_bf16(Ah, Pub(o_of(P, 0)), sm.row_off[0], c0, c1);
   atile_load_bf16(Al, Pub(o_of(P, 1)), sm.row_off[0], c0, c1);
-  Acc<4, MT> acc;
+  Acc<NPO, MT> acc;
   mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
   const Pub AO(P.ao);
-  for (int o = tid(); o < 4 * MT * 256; o += MK_WG_THREADS) {
+  for (int o = tid(); o < NPO * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
-    if (pp < DP && b < P.B) AO.stf((g * P.B + b) * P.H + (p0 + pp) * 16 + nn, sm.out[o]);
+    if (pp < np && b < P.B) AO.stf((g * P.B + b) * P.H + (p0 + pp) * 16 + nn, sm.out[o]);
   }
   if (t.b[0] == 1)
     arrive_nr(P, t.a[2]);  // fused MoE: a residual task sums the block
@@ -2226,7 +2228,12 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_EMBED: op_embed(P, t, sm); break;
     case MK_OP_QKV: op_qkv<MT, 64 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
-    case MK_OP_OPROJ: op_oproj<MT, 32 / MK_WAVES>(P, t, sm); break;
+    case MK_OP_OPROJ:
+      if (MT == 1 && t.a[3] == 2)
+        op_oproj<1, 32 / MK_WAVES, 8>(P, t, sm);
+      else
+        op_oproj<MT, 32 / MK_WAVES, 4>(P, t, sm);
+      break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_MOE_UP:
       if (MT == 1 && t.b[2] > 0)  // fixed shares (b[2]: the claimer count)

@@ -36,6 +36,7 @@ thread_local std::string g_create_error;
 struct Schedule {
   int B = 0, bucket = 0;
   int n_splits_full = 0, n_splits_win = 0, pps = 16;
+  int pps_full = 16;  // pages per split of full-attention layers (pps unless the fused MoE runs)
   int n_router = 0, n_oproj = 0, n_up_claimers = 0, n_down_claimers = 0, n_lm = 0;
   std::vector<int> n_qkv;  // QKV tasks per kv group
   std::vector<int> n_attn_claimers;  // per layer
@@ -257,6 +258,21 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   S->B = B;
   S->bucket = std::min(bucket_of(hint), c.max_seq_len);
   S->pps = pps_for(h, B, S->bucket);
+  // Fused MoE with a window pattern: full-attention layers get as many splits
+  // as the window layers (longer ones), so the same number of compute units
+  // holds attention work and the rest share the experts (fewer attention
+  // claimers leave more units, and each fewer expert slices, on the chain
+  // that sets the layer's time).
+  S->pps_full = S->pps;
+  if (B <= MK_FUSED_B && h->n_workers <= MK_WG_THREADS && c.window > 0) {
+    int lw = 0;
+    while (lw < c.n_layers && !window_of(c, lw)) ++lw;
+    if (lw < c.n_layers) {
+      const int ns_win = splits_for(h, lw, S->bucket, S->pps);
+      const int pages = ceil_div(S->bucket, c.page_size) + 1;
+      S->pps_full = std::max(S->pps, ceil_div(pages, std::max(ns_win, 1)));
+    }
+  }
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
   const int n_w = h->n_workers, NB = h->NB;
   const int kc = c.hidden / 32;
@@ -363,7 +379,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     if (S->n_qkv[KVH - 1] != S->n_qkv[0]) std::abort();
     // attention splits; the last split of a (sequence, group) combines
     begin_wave();
-    const int ns = splits_for(h, l, S->bucket, S->pps);
+    const int pps_l = window_of(c, l) ? S->pps : S->pps_full;
+    const int ns = splits_for(h, l, S->bucket, pps_l);
     if (window_of(c, l))
       S->n_splits_win = ns;
     else
@@ -378,7 +395,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       t.a[1] = x.qkv;
       t.a[2] = S->n_qkv[0];
       t.a[3] = ns;
-      t.a[4] = S->pps;
+      t.a[4] = pps_l;
       t.a[5] = x.attn;
       t.sig_ctr[0] = x.comb;
       push(t);
@@ -406,7 +423,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     {
       const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
       const double up_bytes = e_act * 2.0 * c.expert_ffn * c.hidden * 2.0;
-      const double kv_per = n_attn > 0 ? (double)n_attn_items * S->pps * c.page_size * c.head_dim * 4.0 / n_attn : 0.0;
+      const double kv_per = n_attn > 0 ? (double)n_attn_items * pps_l * c.page_size * c.head_dim * 4.0 / n_attn : 0.0;
       const double f = (up_bytes + (S->n_up_claimers - n_free) * kv_per) / S->n_up_claimers;
       wa = f > 0 ? (int)std::lround(256.0 * std::max(0.0, f - kv_per) / f) : 256;
       if (n_free >= n_w / 4) wa = 0;
@@ -436,14 +453,19 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         push_at(t, cu);
       }
       if (k_free + k_attn - n_free != nt) std::abort();
+      // O projection per (group, two column blocks) when that gives at most
+      // one task per attention unit's worth of pairs, so each unit's weights
+      // stream before its wait
       begin_wave();
       int n_oproj = 0;
+      const int per = (NB % 2 == 0 && KVH * NB / 2 <= n_attn) ? 2 : 1;
       for (int g = 0; g < KVH; ++g)
-        for (int cb = 0; cb < NB; ++cb) {
+        for (int cb = 0; cb < NB; cb += per) {
           mk_task t = make_task(MK_OP_OPROJ, l);
           t.a[0] = g;
           t.a[1] = cb;
           t.a[2] = x.fin;
+          t.a[3] = per;
           t.b[0] = 1;
           add_wait(t, x.comb + g, B);
           push_at(t, (attn_flat0 + n_oproj % n_attn) % n_w);
