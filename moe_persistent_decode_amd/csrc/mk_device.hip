@@ -254,6 +254,7 @@ struct Smem {
   int rt_slot[128 * MK_MAX_BATCH];  // per active expert: its routed slots b * k + j, ascending b
   int tb[MK_FUSED_B + 1];  // fused MoE residual: each token's range of (claimer, token) rows
 };
+static_assert(2 * MK_FUSED_B * 1024 <= MK_MAX_BATCH * MK_MAX_F, "merged attention operand fits");
 static_assert(2 * MK_FUSED_B * MK_MAX_H + 2 * MK_FUSED_B * 16 <= MK_MAX_BATCH * MK_MAX_F,
               "fused MoE operands fit the expert hidden-row buffer");
 static_assert(offsetof(Smem, out) % 16 == 0 && offsetof(Smem, act) % 16 == 0 && offsetof(Smem, ssq) % 16 == 0,
@@ -591,8 +592,12 @@ __device__ __forceinline__ void set_rows_batch(const mk_params& P, Smem& sm, int
 // first page streams before the dependency wait (the older KV is immutable
 // this step). The split that completes a (sequence, group) merges all splits
 // (ATTN_COMBINE) without a task of its own.
-template <int D>
-__device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm);
+// SB: splits in flight per thread and round; MLR: rounds of 512 (split, head)
+// maxima and sums held in registers (the rest load straight into LDS).
+template <int D, int SB = MK_COMB_SB, int MLR = MK_MAX_SPLITS * 16 / MK_WG_THREADS>
+__device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm,
+                                             uint16_t* lds_h = nullptr, uint16_t* lds_l = nullptr,
+                                             bool to_global = true);
 
 // One wave's operands of one KV page of one kv group: K rows (keys) for the
 // score MFMA, V^T tiles for the output MFMA.
@@ -607,7 +612,8 @@ struct KVPage {
 // splits combines them and signals sig_ctr.
 template <int D>
 __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int g, int s, int ns, int pps,
-                                           int qkv_ctr, int qkv_tgt, int attn_ctr, int sig_ctr, Smem& sm) {
+                                           int qkv_ctr, int qkv_tgt, int attn_ctr, int sig_ctr, bool merged_later,
+                                           Smem& sm) {
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
   const int wv = wave_id(), ln = lane_id();
@@ -786,6 +792,10 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
     }
   }
   mark(sm, 0);
+  if (merged_later) {  // the O projection tasks merge the splits
+    arrive_nr(P, attn_ctr);
+    return;
+  }
   const int old = arrive(P, attn_ctr, sm);
   mark(sm, 1);
   if (old == ns - 1) {
@@ -809,7 +819,10 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
   int id = claim_n(P, t.a[0], 1, sm);
   while (id < n_items) {
     const int bg = id / ns, s = id % ns, b = bg / P.KVH, g = bg % P.KVH;
-    attn_split<D>(P, t.layer, b, g, s, ns, t.a[4], t.a[1] + g, t.a[2], t.a[5] + bg, t.sig_ctr[0] + g, sm);
+    // b[0] = 1: the splits count per group (all sequences); the O projection merges them
+    const bool ml = t.b[0] == 1;
+    attn_split<D>(P, t.layer, b, g, s, ns, t.a[4], t.a[1] + g, t.a[2], t.a[5] + (ml ? g : bg), t.sig_ctr[0] + g, ml,
+                  sm);
     if (ld_relaxed(&P.err[0]) != 0) return;
     id = claim_n(P, t.a[0], 1, sm);
   }
@@ -818,56 +831,86 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
 // Log-sum-exp merge of one (sequence, kv group)'s split partials into the
 // attention output (megakernel post, section "Tasks": ATTN_COMBINE):
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, splits in fixed order.
-template <int D>
-__device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm) {
+template <int D, int SB, int MLR>
+__device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, int ns, Smem& sm, uint16_t* lds_h,
+                                             uint16_t* lds_l, bool to_global) {
   const int G = P.G;
   const int stride = G * D + 2 * G;
   const Pub src(P.part + (size_t)(b * P.KVH + g) * P.max_splits * stride);
   SmemComb& C = sm.u.cb;
-  // split maxima and sums, all loads in flight together
-  for (int i = tid(); i < ns * G; i += MK_WG_THREADS) {
-    const int s = i / G, hh = i % G;
-    C.f[s][hh] = src.ldf(s * stride + G * D + hh);
-    C.l[s][hh] = src.ldf(s * stride + G * D + G + hh);
+  // 16-byte loads of the outputs: a split's G * D outputs are GD4 groups of
+  // four; the workgroup forms NP partitions of GD4 threads, partition p
+  // taking splits p, p + NP, ..., up to SB of them in flight at a time
+  const int GD4 = G * D / 4, NP = MK_WG_THREADS / GD4;
+  const int part = tid() / GD4, j = tid() % GD4, hh = 4 * j / D;
+  // every split's maxima and sums and the first round of outputs: one round trip
+  float mv[MLR], lv[MLR];
+#pragma unroll
+  for (int k = 0; k < MLR; ++k) {
+    const int i = tid() + k * MK_WG_THREADS, s = i / G, h2 = i % G;
+    mv[k] = i < ns * G ? src.ldf(s * stride + G * D + h2) : kNegInf;
+    lv[k] = i < ns * G ? src.ldf(s * stride + G * D + G + h2) : 0.f;
+  }
+  float4 v[SB];
+#pragma unroll
+  for (int k = 0; k < SB; ++k) {
+    const int s = part + k * NP;
+    v[k] = (part < NP && s < ns) ? src.ldf4(s * stride + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < MLR; ++k) {
+    const int i = tid() + k * MK_WG_THREADS, s = i / G, h2 = i % G;
+    if (i < ns * G) {
+      C.f[s][h2] = mv[k];
+      C.l[s][h2] = lv[k];
+    }
+  }
+  for (int i = tid() + MLR * MK_WG_THREADS; i < ns * G; i += MK_WG_THREADS) {
+    const int s = i / G, h2 = i % G;
+    C.f[s][h2] = src.ldf(s * stride + G * D + h2);
+    C.l[s][h2] = src.ldf(s * stride + G * D + G + h2);
   }
   __syncthreads();
-  if (tid() < G) {
-    const int hh = tid();
+  // per head (32 lanes each): the maximum over the splits
+  {
+    const int h2 = tid() >> 5, jj = tid() & 31;
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, C.f[s][hh]);
-    C.M[hh] = M;
+    if (h2 < G)
+      for (int s = jj; s < ns; s += 32) M = fmaxf(M, C.f[s][h2]);
+    M = fmaxf(M, xor_lane<1>(M));
+    M = fmaxf(M, xor_lane<2>(M));
+    M = fmaxf(M, xor_lane<4>(M));
+    M = fmaxf(M, xor_lane<8>(M));
+    M = fmaxf(M, xor_lane<16>(M));
+    if (h2 < G && jj == 0) C.M[h2] = M;
   }
   __syncthreads();
   for (int i = tid(); i < ns * G; i += MK_WG_THREADS) {
-    const int s = i / G, hh = i % G;
-    const float ms = C.f[s][hh];
-    C.f[s][hh] = ms == kNegInf ? 0.f : __expf(ms - C.M[hh]);
+    const int s = i / G, h2 = i % G;
+    const float ms = C.f[s][h2];
+    C.f[s][h2] = ms == kNegInf ? 0.f : __expf(ms - C.M[h2]);
   }
   __syncthreads();
-  if (tid() < G) {
-    const int hh = tid();
+  {
+    const int h2 = tid() >> 5, jj = tid() & 31;
     float L = 0.f;
-    for (int s = 0; s < ns; ++s) L = fmaf(C.f[s][hh], C.l[s][hh], L);
-    C.L[hh] = L;
+    if (h2 < G)
+      for (int s = jj; s < ns; s += 32) L = fmaf(C.f[s][h2], C.l[s][h2], L);
+    L = group_sum(L, 32);
+    if (h2 < G && jj == 0) C.L[h2] = L;
   }
-  __syncthreads();
   mark(sm, 2);
   const size_t dst_off = (size_t)b * P.QH * D + (size_t)g * G * D;
   const Pub dst_h(o_of(P, 0) + dst_off), dst_l(o_of(P, 1) + dst_off);
-  // 16-byte loads: a split's G * D outputs are GD4 groups of four; the
-  // workgroup forms NP partitions of GD4 threads, partition p taking splits
-  // p, p + NP, ..., up to SB of them in flight at a time
-  const int GD4 = G * D / 4, NP = MK_WG_THREADS / GD4;
-  const int part = tid() / GD4, j = tid() % GD4, hh = 4 * j / D;
-  constexpr int SB = MK_COMB_SB;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
   if (part < NP) {
     for (int s0 = part; s0 < ns; s0 += NP * SB) {
-      float4 v[SB];
+      if (s0 != part) {
 #pragma unroll
-      for (int k = 0; k < SB; ++k) {
-        const int s = s0 + k * NP;
-        v[k] = s < ns ? src.ldf4(s * stride + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k = 0; k < SB; ++k) {
+          const int s = s0 + k * NP;
+          v[k] = s < ns ? src.ldf4(s * stride + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
@@ -899,8 +942,16 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
     uint16_t h[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_bf16(r[i], h[i], lo[i]);
-    dst_h.st16x4(4 * j, u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)});
-    dst_l.st16x4(4 * j, u32x2_t{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)});
+    const u32x2_t vh = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    const u32x2_t vl = {(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+    if (lds_h) {  // the consumer's own operand (group-relative)
+      *(u32x2_t*)(lds_h + 4 * j) = vh;
+      *(u32x2_t*)(lds_l + 4 * j) = vl;
+    }
+    if (to_global) {
+      dst_h.st16x4(4 * j, vh);
+      dst_l.st16x4(4 * j, vl);
+    }
   }
 }
 
@@ -1096,7 +1147,11 @@ __device__ __forceinline__ void block_arrive(const mk_params& P, const mk_task& 
 // post, section "Drop false dependencies"); one task per (group, column block),
 // or (NPO = 8, a[3] = 2) per (group, two adjacent column blocks), whose 256 KB
 // of weights all stream before the wait.
-template <int MT, int NCH, int NPO>
+// MERGE (at most MK_FUSED_B tokens): the task waits for the group's attention
+// splits (a[4] of them per sequence) and merges them itself into its operand
+// in LDS (ATTN_COMBINE inside the projection), so no compute unit combines
+// first; the first block's task also stores the merged attention output.
+template <int D, int MT, int NCH, int NPO, bool MERGE>
 __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, g = t.a[0], cb = t.a[1], nblk = NPO == 8 ? t.a[3] : 1;
   const int DP = P.CB / 16, p0 = cb * DP, np = DP * nblk;
@@ -1107,11 +1162,29 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
   wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, np, c0, c1);
   if (!wait_task(P, t, sm)) return;
   mark(sm, 0);
-  set_rows_batch(P, sm, 0, P.QH * P.D, 0);
-  __syncthreads();
   ATile<MT, NCH> Ah, Al;
-  atile_load_bf16(Ah, Pub(o_of(P, 0)), sm.row_off[0], c0, c1);
-  atile_load_bf16(Al, Pub(o_of(P, 1)), sm.row_off[0], c0, c1);
+  if constexpr (MERGE) {
+    const int GD = P.G * D;  // <= 1024
+    uint16_t* oh = sm.act;
+    uint16_t* ol = sm.act + MK_FUSED_B * 1024;
+    for (int b = 0; b < P.B; ++b) {
+      attn_combine<D, 8, 1>(P, b, g, t.a[4], sm, oh + b * GD, ol + b * GD, cb == 0);
+      __syncthreads();
+    }
+    const int wv = wave_id(), ln = lane_id(), row = ln & 15;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cr = wv + MK_WAVES * i;  // chunk relative to the group's first
+      const bool ok = cr < c1 - c0 && row < P.B;
+      Ah.a[0][i] = ok ? *(const u32x4_t*)(oh + row * GD + 32 * cr + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+      Al.a[0][i] = ok ? *(const u32x4_t*)(ol + row * GD + 32 * cr + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  } else {
+    set_rows_batch(P, sm, 0, P.QH * P.D, 0);
+    __syncthreads();
+    atile_load_bf16(Ah, Pub(o_of(P, 0)), sm.row_off[0], c0, c1);
+    atile_load_bf16(Al, Pub(o_of(P, 1)), sm.row_off[0], c0, c1);
+  }
   Acc<NPO, MT> acc;
   mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
@@ -2229,10 +2302,10 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_QKV: op_qkv<MT, 64 / MK_WAVES>(P, t, sm); break;
     case MK_OP_ATTN: op_attn<D>(P, t, sm); break;
     case MK_OP_OPROJ:
-      if (MT == 1 && t.a[3] == 2)
-        op_oproj<1, 32 / MK_WAVES, 8>(P, t, sm);
+      if (MT == 1 && t.b[1] == 1)  // batches up to MK_FUSED_B: merges the splits itself
+        op_oproj<D, 1, 32 / MK_WAVES, 8, true>(P, t, sm);
       else
-        op_oproj<MT, 32 / MK_WAVES, 4>(P, t, sm);
+        op_oproj<D, MT, 32 / MK_WAVES, 4, false>(P, t, sm);
       break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_MOE_UP:

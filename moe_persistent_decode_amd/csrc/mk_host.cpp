@@ -270,7 +270,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     if (lw < c.n_layers) {
       const int ns_win = splits_for(h, lw, S->bucket, S->pps);
       const int pages = ceil_div(S->bucket, c.page_size) + 1;
-      S->pps_full = std::max(S->pps, ceil_div(pages, std::max(ns_win, 1)));
+      S->pps_full = std::max(S->pps, ceil_div(pages, std::max(3 * ns_win / 2, 1)));
     }
   }
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
@@ -335,6 +335,9 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     push(t);
   }
 
+  // Fused MoE (at most MK_FUSED_B tokens): the attention splits only count
+  // per group and the O projection tasks merge them.
+  const bool fused_all = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
   for (int l = 0; l < L; ++l) {
     const CtrIdx x = ci(l);
     auto wait_input = [&](mk_task& t) { add_wait(t, resid(l), NB); };
@@ -397,6 +400,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       t.a[3] = ns;
       t.a[4] = pps_l;
       t.a[5] = x.attn;
+      t.b[0] = fused_all ? 1 : 0;
       t.sig_ctr[0] = x.comb;
       push(t);
     }
@@ -466,8 +470,10 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           t.a[1] = cb;
           t.a[2] = x.fin;
           t.a[3] = per;
+          t.a[4] = ns;
           t.b[0] = 1;
-          add_wait(t, x.comb + g, B);
+          t.b[1] = 1;  // merges the group's splits itself
+          add_wait(t, x.attn + g, B * ns);
           push_at(t, (attn_flat0 + n_oproj % n_attn) % n_w);
           ++n_oproj;
         }
@@ -715,7 +721,10 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
         } else {
           const int bg = u.pending_item / ns, g = bg % KVH;
           if (ctr[t.a[1] + g] >= t.a[2]) {
-            if (++ctr[t.a[5] + bg] == ns) ctr[t.sig_ctr[0] + g]++;
+            if (t.b[0] == 1)
+              ctr[t.a[5] + g]++;
+            else if (++ctr[t.a[5] + bg] == ns)
+              ctr[t.sig_ctr[0] + g]++;
             u.pending_item = -1;
             progress = true;
           }
@@ -761,9 +770,10 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   for (int l = 0; l < L; ++l) {
     const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
     int k = S.c_layer0 + l * S.c_per_layer;
+    const bool merged = S.moe_fused[l] > 0;  // the O projection tasks merge the splits
     for (int g = 0; g < KVH; ++g) want[k++] = S.n_qkv[g];
-    for (int i = 0; i < B * KVH; ++i) want[k++] = ns;
-    for (int g = 0; g < KVH; ++g) want[k++] = B;
+    for (int i = 0; i < B * KVH; ++i) want[k++] = merged ? (i < KVH ? (int64_t)B * ns : 0) : ns;
+    for (int g = 0; g < KVH; ++g) want[k++] = merged ? 0 : B;
     want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
     want[k++] = 1;                                                   // route finalized
     want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
