@@ -270,7 +270,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     if (lw < c.n_layers) {
       const int ns_win = splits_for(h, lw, S->bucket, S->pps);
       const int pages = ceil_div(S->bucket, c.page_size) + 1;
-      S->pps_full = std::max(S->pps, ceil_div(pages, std::max(3 * ns_win / 2, 1)));
+      S->pps_full = std::max(S->pps, ceil_div(pages, std::max(ns_win, 1)));
     }
   }
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
