@@ -76,21 +76,63 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // The thread's index in the workgroup, from the two above.
 __device__ __forceinline__ int tid() { return (wave_id() << 6) | lane_id(); }
 
-// The value of lane (this lane ^ M). Masks below 32 go through ds_swizzle,
-// whose pattern is an immediate: no per-lane address register, which the
-// compiler would otherwise hoist out of the task loop and keep live through
-// every op (as it does for ds_bpermute addresses). Mask 32 uses ds_bpermute.
+// The value of lane (this lane ^ M), M < 16, through ds_swizzle, whose
+// pattern is an immediate: no per-lane address register (the compiler hoists
+// lane-derived addresses out of the task loop and keeps them live through
+// every op, as it does for ds_bpermute's).
 template <int M>
 __device__ __forceinline__ int xor_lane(int v) {
-  static_assert(M > 0 && M <= 32 && (M & (M - 1)) == 0, "power-of-two lane mask");
-  if constexpr (M < 32)
-    return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1f);
-  else
-    return __builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, v);
+  static_assert(M > 0 && M < 16 && (M & (M - 1)) == 0, "power-of-two lane mask below 16");
+  return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1f);
 }
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
   return __int_as_float(xor_lane<M>(__float_as_int(v)));
+}
+// The values of lanes (l, l ^ 16) and of lanes (l, l ^ 32), in lane order,
+// from gfx950's VALU lane swaps (no LDS round trip): permlane16_swap of x
+// with itself gives x[l & ~16] and x[l | 16]; permlane32_swap gives
+// x[l & 31] and x[(l & 31) + 32]. Both lanes of a pair get the same two
+// values in the same order, so any combination of them is identical in both.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair16(int v, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+__device__ __forceinline__ void pair32(int v, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+__device__ __forceinline__ float sum16(float v) {
+  float a, b;
+  pair16(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum32(float v) {
+  float a, b;
+  pair32(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max16(float v) {
+  float a, b;
+  pair16(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max32(float v) {
+  float a, b;
+  pair32(v, a, b);
+  return fmaxf(a, b);
 }
 // Sum over aligned groups of n lanes (n a power of two, at most 64; every
 // lane of a group ends with its sum), butterfly order.
@@ -99,8 +141,8 @@ __device__ __forceinline__ float group_sum(float v, int n) {
   if (n > 2) v += xor_lane<2>(v);
   if (n > 4) v += xor_lane<4>(v);
   if (n > 8) v += xor_lane<8>(v);
-  if (n > 16) v += xor_lane<16>(v);
-  if (n > 32) v += xor_lane<32>(v);
+  if (n > 16) v = sum16(v);
+  if (n > 32) v = sum32(v);
   return v;
 }
 // Sum over the lanes of a wave that share the lane bits below m (m a power
@@ -110,8 +152,8 @@ __device__ __forceinline__ float group_sum_above(float v, int m) {
   if (m <= 2) v += xor_lane<2>(v);
   if (m <= 4) v += xor_lane<4>(v);
   if (m <= 8) v += xor_lane<8>(v);
-  if (m <= 16) v += xor_lane<16>(v);
-  if (m <= 32) v += xor_lane<32>(v);
+  if (m <= 16) v = sum16(v);
+  if (m <= 32) v = sum32(v);
   return v;
 }
 
@@ -400,12 +442,15 @@ __device__ __forceinline__ void inv_rms_lds(const mk_params& P, Smem& sm) {
   const int NB = P.NB;
 #pragma unroll
   for (int k = 0; k < MK_MAX_BATCH * 32 / MK_WG_THREADS; ++k) {
-    const int i = tid() + k * MK_WG_THREADS, b = i >> 5, j = i & 31;
-    float v = 0.f;
-    if (b < P.B)
-      for (int q = j; q < NB; q += 32) v += sm.ssq[b * NB + q];
-    v = group_sum(v, 32);
-    if (b < P.B && j == 0) sm.inv_rms[b] = 1.0f / sqrtf(v / (float)P.H + P.eps);
+    // (waves whose tokens are all past the batch skip the exchange)
+    if ((wave_id() * 64 + k * MK_WG_THREADS) / 32 < P.B) {
+      const int i = tid() + k * MK_WG_THREADS, b = i >> 5, j = i & 31;
+      float v = 0.f;
+      if (b < P.B)
+        for (int q = j; q < NB; q += 32) v += sm.ssq[b * NB + q];
+      v = group_sum(v, 32);
+      if (b < P.B && j == 0) sm.inv_rms[b] = 1.0f / sqrtf(v / (float)P.H + P.eps);
+    }
   }
 }
 
@@ -720,8 +765,7 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
       sv[i] = (pos >= lo && pos <= p) ? sacc[i] * scale : kNegInf;
       mloc = fmaxf(mloc, sv[i]);
     }
-    mloc = fmaxf(mloc, xor_lane<16>(mloc));
-    mloc = fmaxf(mloc, xor_lane<32>(mloc));
+    mloc = max32(max16(mloc));
     const float mnew = fmaxf(m, mloc);
     if (mnew != kNegInf) {
       const float alpha = (m == kNegInf) ? 0.f : __expf(m - mnew);
@@ -733,8 +777,7 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
         pb[i] = f2bf(pv);
         ps += bf2f((uint16_t)pb[i]);
       }
-      ps += xor_lane<16>(ps);
-      ps += xor_lane<32>(ps);
+      ps = sum32(sum16(ps));
       lsum = lsum * alpha + ps;
       m = mnew;
       const s16x4_t pB = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
@@ -881,7 +924,7 @@ __device__ __forceinline__ void attn_combine(const mk_params& P, int b, int g, i
     M = fmaxf(M, xor_lane<2>(M));
     M = fmaxf(M, xor_lane<4>(M));
     M = fmaxf(M, xor_lane<8>(M));
-    M = fmaxf(M, xor_lane<16>(M));
+    M = max16(M);
     if (h2 < G && jj == 0) C.M[h2] = M;
   }
   __syncthreads();
@@ -1006,10 +1049,13 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
       Ul.st16(b * H + c, lo);
     }
     // the row's sum of squares across its CB lanes (a row never straddles
-    // a wave: CB divides 64), butterfly order
-    float sq = idx < n ? hv[k] * hv[k] : 0.f;
-    sq = group_sum(sq, CB);
-    if (idx < n && idx % CB == 0) Pub(ssq_of(P, l_next)).stf((idx / CB) * P.NB + cb, sq);
+    // a wave: CB divides 64), butterfly order; waves past the block's
+    // elements skip it (each step is a dependent LDS exchange)
+    if (wave_id() * 64 + k * MK_WG_THREADS < n) {
+      float sq = idx < n ? hv[k] * hv[k] : 0.f;
+      sq = group_sum(sq, CB);
+      if (idx < n && idx % CB == 0) Pub(ssq_of(P, l_next)).stf((idx / CB) * P.NB + cb, sq);
+    }
   }
 }
 
@@ -1991,7 +2037,10 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
       reduce_tiles(ac, sm);
       // weighted SiLU(gate) * up of the slice for every token routed to the expert
       {
-        const int o = tid();
+        // (the thread index tied to the item: its LDS addresses are then
+        // formed here, not hoisted out of every loop and kept live)
+        int o = tid();
+        asm("" : "+v"(o) : "s"(id));
         if (o < MK_FUSED_B * 16) {
           const int b = o >> 4, r = o & 15;
           float v = 0.f;
@@ -2042,7 +2091,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     const int p = (t0 >> 5) + 16 * j;
 #pragma unroll
     for (int b = 0; b < MK_FUSED_B; ++b) {
-      const float v = acc[j][b] + xor_lane<16>(acc[j][b]);
+      const float v = sum16(acc[j][b]);
       if (wr && p < H / 16 && b < B && ((seen >> b) & 1u)) MP.stf((sk * MK_FUSED_B + b) * H + p * 16 + col, v);
     }
   }
@@ -2175,10 +2224,10 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
     gv[0] = g0;
   }
   __syncthreads();
-  write_block_input(P, l + 1, cb, hv, gv, n, sm);
   mark(sm, 2);
-  arrive_nr(P, t.sig_ctr[0]);
+  write_block_input(P, l + 1, cb, hv, gv, n, sm);
   mark(sm, 3);
+  arrive_nr(P, t.sig_ctr[0]);
 }
 
 // ----------------------------------------------------------------- LM head
@@ -2275,8 +2324,22 @@ __device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm) {
     auto step = [&](float ov, int oi) {
       if (ov > v || (ov == v && oi < ix)) { v = ov; ix = oi; }
     };
-    step(xor_lane<32>(v), xor_lane<32>(ix));
-    step(xor_lane<16>(v), xor_lane<16>(ix));
+    // (the pair steps: both lanes pick the better of the same two entries)
+    auto pair_step = [&](float av, int ai, float bv, int bi) {
+      const bool a_first = av > bv || (av == bv && ai < bi);
+      v = a_first ? av : bv;
+      ix = a_first ? ai : bi;
+    };
+    {
+      float av, bv;
+      int ai, bi;
+      pair32(v, av, bv);
+      pair32(ix, ai, bi);
+      pair_step(av, ai, bv, bi);
+      pair16(v, av, bv);
+      pair16(ix, ai, bi);
+      pair_step(av, ai, bv, bi);
+    }
     step(xor_lane<8>(v), xor_lane<8>(ix));
     step(xor_lane<4>(v), xor_lane<4>(ix));
     step(xor_lane<2>(v), xor_lane<2>(ix));
