@@ -294,6 +294,7 @@ struct Smem {
   int rt_e[128];          // active experts, ascending
   int rt_cnt[128];        // tokens routed to each active expert
   int rt_slot[128 * MK_MAX_BATCH];  // per active expert: its routed slots b * k + j, ascending b
+  int done_cnt[128];      // claiming MoE: up/gate items done per active expert, not yet counted
   int tb[MK_FUSED_B + 1];  // fused MoE residual: each token's range of (claimer, token) rows
 };
 static_assert(2 * MK_FUSED_B * 1024 <= MK_MAX_BATCH * MK_MAX_F, "merged attention operand fits");
@@ -1593,6 +1594,153 @@ __device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Sme
   }
 }
 
+// The claiming MoE above 16 tokens: each up/gate item's matrix-core rows are
+// the tokens routed to its expert (a second 16-row tile when an expert has
+// more), loaded together with the item's weights, so an item's operand takes
+// one row tile of registers instead of the whole batch's two and two items'
+// weights stream at once. Down items as in the claiming variant.
+template <int NCH, int NBMAX, int NCHD>
+__device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task& t, Smem& sm) {
+  if (!wait_task(P, t, sm)) return;
+  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
+  const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, H = P.H;
+  const int kc = H / 32, kh_chunks = kc / 2;
+  const size_t pstride = (size_t)kc * 512;
+  const Pub GU(P.gu), U0(u_of(P, l, 0)), U1(u_of(P, l, 1));
+  claimer_start(P, claim_ctr, 1, l, sm, t.a[3]);
+  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
+  const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
+  int idd = sm.claim2;
+  if ((int)tid() < 128) sm.done_cnt[tid()] = 0;
+  mark(sm, 0);
+  // row offsets of row tile rt of active expert a into sm.row_off[k]
+  auto set_rows = [&](int k, int a, int rt) {
+    if ((int)tid() < 16) {
+      const int r = rt * 16 + (int)tid();
+      sm.row_off[k][tid()] = (a >= 0 && r < sm.rt_cnt[a]) ? (sm.rt_slot[a * B + r] / K) * H : -1;
+    }
+  };
+  // one item's weights and routed rows (a zero tile and no rows past the queue)
+  auto load = [&](WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int k, int id) {
+    const bool valid = id < n_items;
+    const int a = valid ? id / upe : 0, r = id % upe;
+    const int tt = r >> 1, kh = r & 1;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
+               valid ? 2 : 0, kh * kh_chunks, (kh + 1) * kh_chunks);
+    set_rows(k, valid ? a : -1, 0);
+    __syncthreads();
+    atile_load_bf16(Ah, U0, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
+    atile_load_bf16(Al, U1, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
+  };
+  // one item's products and gu stores; the arrival is counted in LDS
+  auto compute = [&](const WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int k, int id) {
+    const int a = id / upe, r = id % upe;
+    const int tt = r >> 1, kh = r & 1;
+    const int cnt = sm.rt_cnt[a];
+    for (int rt = 0; rt * 16 < cnt; ++rt) {
+      if (rt > 0) {  // an expert with more than 16 routed tokens: the next rows
+        __syncthreads();
+        set_rows(k, a, rt);
+        __syncthreads();
+        atile_load_bf16(Ah, U0, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
+        atile_load_bf16(Al, U1, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
+      }
+      Acc<2, 1> acc;
+      mfma_tiles(acc, w, Ah, Al);
+      reduce_tiles(acc, sm);
+      // gu[slot][kh][gate|up][F] of the tile's routed rows
+      const int nr = min(16, cnt - rt * 16);
+      for (int o = tid(); o < 2 * nr * 16; o += MK_WG_THREADS) {
+        const int which = o / (nr * 16), rr = (o / 16) % nr, nn = o % 16;
+        const int slot = sm.rt_slot[a * B + rt * 16 + rr], b = slot / K;
+        GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, sm.out[which * 256 + rr * 16 + nn] * sm.inv_rms[b]);
+      }
+    }
+    if (tid() == 0) sm.done_cnt[a] += 1;
+  };
+  {
+    // two items in flight: the next is claimed and its weights stream while
+    // the current computes; the arrivals wait for the end of the phase (one
+    // drain), since down items start only after this claimer's up/gate items
+    WTile<2, NCH> w0, w1;
+    ATile<1, NCH> h0, l0, h1, l1;
+    int i0 = sm.claim;
+    load(w0, h0, l0, 0, i0);
+    int i1 = claim_n(P, claim_ctr, 1, sm);
+    while (i0 < n_items) {
+      load(w1, h1, l1, 1, i1);
+      compute(w0, h0, l0, 0, i0);
+      i0 = i1 < n_items ? claim_n(P, claim_ctr, 1, sm) : n_items;
+      if (i1 >= n_items) break;
+      load(w0, h0, l0, 0, i0);
+      compute(w1, h1, l1, 1, i1);
+      i1 = i0 < n_items ? claim_n(P, claim_ctr, 1, sm) : n_items;
+    }
+  }
+  mark(sm, 1);
+  sync_published();
+  if ((int)tid() < 128 && sm.done_cnt[tid()] > 0)
+    __hip_atomic_fetch_add(&P.ctr[done_base + tid()], (uint32_t)sm.done_cnt[tid()], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  mark(sm, 2);
+  // down items (two row tiles of routed rows): the next claim travels while
+  // the current item computes
+  const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
+  const size_t pstride_d = (size_t)kcd * 512;
+  WTile<4, NCHD> wd;
+  if (idd < n_down) {
+    const int a = idd / dpe, cb = idd % dpe;
+    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+    wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0, kcd);
+  }
+  while (idd < n_down) {
+    const int next = claim_n(P, t.a[3], 1, sm);
+    down_item<2, NCHD>(P, t, idd / dpe, idd % dpe, wd, sm);
+    if (ld_relaxed(&P.err[0]) != 0) return;
+    idd = next;
+    if (idd < n_down) {
+      const int a = idd / dpe, cb = idd % dpe;
+      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+      wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0,
+                 kcd);
+    }
+  }
+  mark(sm, 3);
+}
+
+// The down projection's operand for routed rows [r0, r0 + nr) of active
+// expert a: SiLU(gate) * up from the two K halves' partial sums, as the split
+// pair in LDS (hi of row r - r0 at act[(r - r0) F + f], lo 16 F further on).
+// Only the routed rows are loaded, eight elements per thread in flight per
+// round; rows past nr are left as they are (the product's output rows past
+// the routed ones are not stored).
+__device__ __forceinline__ void stage_act(const mk_params& P, int a, int r0, int nr, Smem& sm) {
+  const int F = P.F, B = P.B, n = nr * F, lo = 16 * F;
+  const Pub GU(P.gu);
+  constexpr int R = 8;
+  for (int i0 = tid(); i0 < n; i0 += R * MK_WG_THREADS) {
+    float g[R][4];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = i0 + k * MK_WG_THREADS, row = i / F, f = i % F;
+      const bool live = i < n;
+      const int slot = live ? sm.rt_slot[a * B + r0 + row] : 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = i0 + k * MK_WG_THREADS;
+      if (i < n) {
+        const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
+        split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[lo + i]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // One or two (nblk) adjacent column blocks (cb0, cb0 + 1) of one expert's down
 // projection for at most 16 routed tokens, each block's weights already in
 // registers (the second a zero tile when nblk is 1).
@@ -1609,27 +1757,7 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
   const Pub DN(P.dn), GU(P.gu);
   if (stage) {
     if (!wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
-    const int n = 16 * F;
-    for (int i0 = tid(); i0 < n; i0 += 4 * MK_WG_THREADS) {
-      float g[4][4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * MK_WG_THREADS, row = i / F, f = i % F;
-        const bool live = i < n && row < cnt;
-        const int slot = live ? sm.rt_slot[a * B + row] : 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * MK_WG_THREADS;
-        if (i < n) {
-          const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
-          split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[n + i]);
-        }
-      }
-    }
-    __syncthreads();
+    stage_act(P, a, 0, min(cnt, 16), sm);
   }
   Acc<8, 1> acc;
 #pragma unroll
@@ -1833,26 +1961,8 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int n = 16 * F;
-    for (int i0 = tid(); i0 < n; i0 += 4 * MK_WG_THREADS) {
-      float g[4][4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * MK_WG_THREADS, row = mt * 16 + i / F, f = i % F;
-        const bool live = i < n && row < cnt;
-        const int slot = live ? sm.rt_slot[a * B + row] : 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) g[k][q] = live ? GU.ldf(((slot * 2 + (q & 1)) * 2 + (q >> 1)) * F + f) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * MK_WG_THREADS;
-        if (i < n) {
-          const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
-          split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[n + i]);
-        }
-      }
-    }
-    __syncthreads();
+    if (mt * 16 >= cnt) break;  // (uniform) no routed rows in this tile
+    stage_act(P, a, mt * 16, min(16, cnt - mt * 16), sm);
     const int wv = wave_id(), ln = lane_id();
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -2374,8 +2484,10 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_MOE_UP:
       if (MT == 1 && t.b[2] > 0)  // fixed shares (b[2]: the claimer count)
         op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
+      else if (MT == 2)  // above 16 tokens: each item's routed rows
+        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
       else
-        op_moe<MT, 32 / MK_WAVES, MT == 1 ? 2 : 1, 24 / MK_WAVES>(P, t, sm);
+        op_moe<MT, 32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
       break;
     case MK_OP_MOE_FUSED:
       if (MT == 1) op_moe_fused<2048 / 256, 32 / MK_WAVES>(P, t, sm);
