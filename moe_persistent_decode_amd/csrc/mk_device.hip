@@ -1430,7 +1430,7 @@ __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& s
 // the result in sm.claim; none with claim_ctr < 0), the route entries of the layer's active experts
 // and, with l >= 0, the sums of squares of layer l's input (then sm.inv_rms).
 __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_ctr, int n, int l, Smem& sm,
-                                              int32_t claim2_ctr = -1) {
+                                              int32_t claim2_ctr = -1, int n2 = 1) {
   const Pub R(route_of(P, l));
   const int E = P.E, B = P.B;
   const int i = tid();
@@ -1438,7 +1438,7 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
   if (i == 0 && claim_ctr >= 0)
     c = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i == 64 && claim2_ctr >= 0)
-    sm.claim2 = (int)__hip_atomic_fetch_add(&P.ctr[claim2_ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.claim2 = (int)__hip_atomic_fetch_add(&P.ctr[claim2_ctr], (uint32_t)n2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (i < 4) sm.rt_hdr[i] = R.ldi(i);
   if (i < E) {
     sm.rt_e[i] = R.ldi(4 + i);
@@ -1467,7 +1467,7 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
 // batch size spreads the queue over the claimers expected to be free.
 template <int MT, int NCH>
 __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb, const WTile<4, NCH>& w,
-                                          Smem& sm);
+                                          Smem& sm, bool stage = true);
 
 // The MoE claimer: expert up/gate items first, then down items. The first
 // down item is claimed at the start and its weights stream alongside the
@@ -1602,17 +1602,43 @@ __device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Sme
 template <int NCH, int NBMAX, int NCHD>
 __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
-  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
+  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], dclaim_ctr = t.a[3];
   const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, H = P.H;
   const int kc = H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
   const Pub GU(P.gu), U0(u_of(P, l, 0)), U1(u_of(P, l, 1));
-  claimer_start(P, claim_ctr, 1, l, sm, t.a[3]);
+  // Items are claimed CH at a time; the next chunk's claim is issued when a
+  // chunk starts and read when it runs out, so claims (one address shared
+  // by every unit) never sit on the path.
+  constexpr int CH = 4;
+  claimer_start(P, claim_ctr, CH, l, sm, dclaim_ctr, CH);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
   const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
-  int idd = sm.claim2;
+  int dbase = sm.claim2;
   if ((int)tid() < 128) sm.done_cnt[tid()] = 0;
   mark(sm, 0);
+  // the stream of one queue: the item after the current one (uniform)
+  struct Stream {
+    int base, j, pend;
+  };
+  auto stream_start = [&](Stream& q, int base, int32_t ctr, int n) {
+    q.base = base;
+    q.j = 0;
+    q.pend = 0;
+    if (tid() == 0 && base < n)
+      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)CH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto stream_next = [&](Stream& q, int32_t ctr, int n) -> int {
+    if (++q.j < CH) return q.base + q.j;
+    if (tid() == 0) sm.claim = q.pend;
+    __syncthreads();
+    q.base = sm.claim;
+    __syncthreads();
+    q.j = 0;
+    if (tid() == 0 && q.base < n)
+      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)CH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return q.base;
+  };
   // row offsets of row tile rt of active expert a into sm.row_off[k]
   auto set_rows = [&](int k, int a, int rt) {
     if ((int)tid() < 16) {
@@ -1660,22 +1686,24 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     if (tid() == 0) sm.done_cnt[a] += 1;
   };
   {
-    // two items in flight: the next is claimed and its weights stream while
-    // the current computes; the arrivals wait for the end of the phase (one
-    // drain), since down items start only after this claimer's up/gate items
+    // two items in flight: the next one's weights stream while the current
+    // computes; the arrivals wait for the end of the phase (one drain), since
+    // down items start only after this claimer's up/gate items
     WTile<2, NCH> w0, w1;
     ATile<1, NCH> h0, l0, h1, l1;
-    int i0 = sm.claim;
+    Stream q;
+    stream_start(q, sm.claim, claim_ctr, n_items);
+    int i0 = q.base;
     load(w0, h0, l0, 0, i0);
-    int i1 = claim_n(P, claim_ctr, 1, sm);
+    int i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
     while (i0 < n_items) {
       load(w1, h1, l1, 1, i1);
       compute(w0, h0, l0, 0, i0);
-      i0 = i1 < n_items ? claim_n(P, claim_ctr, 1, sm) : n_items;
+      i0 = i1 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
       if (i1 >= n_items) break;
       load(w0, h0, l0, 0, i0);
       compute(w1, h1, l1, 1, i1);
-      i1 = i0 < n_items ? claim_n(P, claim_ctr, 1, sm) : n_items;
+      i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
     }
   }
   mark(sm, 1);
@@ -1684,26 +1712,38 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     __hip_atomic_fetch_add(&P.ctr[done_base + tid()], (uint32_t)sm.done_cnt[tid()], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   mark(sm, 2);
-  // down items (two row tiles of routed rows): the next claim travels while
-  // the current item computes
+  // down items (two row tiles of routed rows), the next item's weights
+  // streaming while the current computes; consecutive items of one expert
+  // reuse its staged operand
   const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
   const size_t pstride_d = (size_t)kcd * 512;
-  WTile<4, NCHD> wd;
-  if (idd < n_down) {
-    const int a = idd / dpe, cb = idd % dpe;
+  auto dload = [&](WTile<4, NCHD>& w, int id) {
+    const bool valid = id < n_down;
+    const int a = valid ? id / dpe : 0, cb = id % dpe;
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0, kcd);
-  }
-  while (idd < n_down) {
-    const int next = claim_n(P, t.a[3], 1, sm);
-    down_item<2, NCHD>(P, t, idd / dpe, idd % dpe, wd, sm);
-    if (ld_relaxed(&P.err[0]) != 0) return;
-    idd = next;
-    if (idd < n_down) {
-      const int a = idd / dpe, cb = idd % dpe;
-      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-      wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0,
-                 kcd);
+    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
+               valid ? DP : 0, 0, kcd);
+  };
+  {
+    WTile<4, NCHD> d0, d1;
+    Stream q;
+    stream_start(q, dbase, dclaim_ctr, n_down);
+    int i0 = q.base;
+    dload(d0, i0);
+    int i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
+    int staged = -1;
+    while (i0 < n_down) {
+      dload(d1, i1);
+      down_item<2, NCHD>(P, t, i0 / dpe, i0 % dpe, d0, sm, i0 / dpe != staged);
+      staged = i0 / dpe;
+      if (ld_relaxed(&P.err[0]) != 0) return;
+      i0 = i1 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
+      if (i1 >= n_down) break;
+      dload(d0, i0);
+      down_item<2, NCHD>(P, t, i1 / dpe, i1 % dpe, d1, sm, i1 / dpe != staged);
+      staged = i1 / dpe;
+      if (ld_relaxed(&P.err[0]) != 0) return;
+      i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
     }
   }
   mark(sm, 3);
@@ -1941,16 +1981,19 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
 // have done differently": MoE down streams weights while up/gate still
 // computes the hidden state it consumes). The contribution counts on the
 // column block; the last one does the residual add.
+// stage = false: the operand in LDS is the previous item's, of the same
+// expert with at most 16 routed rows (already waited for and staged).
 template <int MT, int NCH>
 __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb, const WTile<4, NCH>& w,
-                                          Smem& sm) {
+                                          Smem& sm, bool stage) {
   const int F = P.F, H = P.H, B = P.B;
   const int kc = F / 32;
   const int DP = P.CB / 16;
   const int cnt = sm.rt_cnt[a];
   const Pub DN(P.dn), GU(P.gu);
+  stage = stage || cnt > 16;
   // the up/gate items may run in this same launch (kernel-per-op variant too)
-  if (!wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
+  if (stage && !wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
   // act = silu(g0 + g1) * (u0 + u1) per routed row, staged in LDS as the
   // split pair (16 rows at a time: hi in act[0, 16F), lo in act[16F, 32F))
   Acc<4, MT> acc;
@@ -1962,7 +2005,7 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
   for (int mt = 0; mt < MT; ++mt) {
     const int n = 16 * F;
     if (mt * 16 >= cnt) break;  // (uniform) no routed rows in this tile
-    stage_act(P, a, mt * 16, min(16, cnt - mt * 16), sm);
+    if (stage) stage_act(P, a, mt * 16, min(16, cnt - mt * 16), sm);
     const int wv = wave_id(), ln = lane_id();
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
