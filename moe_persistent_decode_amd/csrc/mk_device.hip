@@ -1689,21 +1689,27 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     // two items in flight: the next one's weights stream while the current
     // computes; the arrivals wait for the end of the phase (one drain), since
     // down items start only after this claimer's up/gate items
-    WTile<2, NCH> w0, w1;
-    ATile<1, NCH> h0, l0, h1, l1;
+    WTile<2, NCH> w0, w1, w2;
+    ATile<1, NCH> h0, l0, h1, l1, h2, l2;
     Stream q;
     stream_start(q, sm.claim, claim_ctr, n_items);
     int i0 = q.base;
     load(w0, h0, l0, 0, i0);
     int i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
+    load(w1, h1, l1, 1, i1);
+    int i2 = i1 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
     while (i0 < n_items) {
-      load(w1, h1, l1, 1, i1);
+      load(w2, h2, l2, 2, i2);
       compute(w0, h0, l0, 0, i0);
-      i0 = i1 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
+      i0 = i2 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
       if (i1 >= n_items) break;
       load(w0, h0, l0, 0, i0);
       compute(w1, h1, l1, 1, i1);
       i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
+      if (i2 >= n_items) break;
+      load(w1, h1, l1, 1, i1);
+      compute(w2, h2, l2, 2, i2);
+      i2 = i1 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
     }
   }
   mark(sm, 1);
