@@ -12,6 +12,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
     # packed fp32 ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics on counters are issued by one lane; the optimizer's rewrite
+    # (elect a lane, broadcast the result) waits for the result at once
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

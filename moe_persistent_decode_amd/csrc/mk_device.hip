@@ -232,6 +232,18 @@ __device__ __forceinline__ void sync_published() {
   __syncthreads();
 }
 
+// Workgroup barrier ordering LDS only. __syncthreads() also releases global
+// memory: it waits for this wave's earlier global stores, and since the
+// memory counter retires in order, for every load issued before them, which
+// empties a pipeline of weight loads at each barrier. Used where the barrier
+// separates LDS writes from LDS reads; hand-offs through global memory keep
+// the draining forms (sync_published, the counter waits).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr float kNegInf = -__builtin_inff();
 
 // ------------------------------------------------------------------ LDS
@@ -400,9 +412,9 @@ __device__ __forceinline__ int arrive(const mk_params& P, int32_t c, Smem& sm) {
 __device__ __forceinline__ int claim_n(const mk_params& P, int32_t c, int n, Smem& sm) {
   if (tid() == 0)
     sm.claim = (int)__hip_atomic_fetch_add(&P.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  lds_sync();
   const int id = sm.claim;
-  __syncthreads();
+  lds_sync();
   return id;
 }
 
@@ -460,9 +472,9 @@ __device__ __forceinline__ void load_inv_rms(const mk_params& P, int l, Smem& sm
   const Pub S(ssq_of(P, l));
   const int n = P.B * P.NB;
   for (int i = tid(); i < n; i += MK_WG_THREADS) sm.ssq[i] = S.ldf(i);
-  __syncthreads();
+  lds_sync();
   inv_rms_lds(P, sm);
-  __syncthreads();
+  lds_sync();
 }
 
 // --------------------------------------------------------- matrix tiles
@@ -518,6 +530,18 @@ __device__ __forceinline__ void atile_load_bf16(ATile<MT, NCH>& A, const Pub& sr
       const int c = c0 + wv + MK_WAVES * i;
       A.a[mt][i] = (c < c1 && o >= 0) ? src.ld16x8(o + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
     }
+  }
+}
+
+// One row tile whose rows each lane names itself: o is the element offset of
+// row l%16 (negative: a zero row). Otherwise as atile_load_bf16.
+template <int NCH>
+__device__ __forceinline__ void atile_load_row(ATile<1, NCH>& A, const Pub& src, int o, int c0, int c1) {
+  const int wv = wave_id(), ln = lane_id();
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = c0 + wv + MK_WAVES * i;
+    A.a[0][i] = (c < c1 && o >= 0) ? src.ld16x8(o + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
@@ -612,7 +636,7 @@ __device__ __forceinline__ void reduce_tiles(const Acc<NP, MT>& acc, Smem& sm) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[(pp * MT + mt) * 256 + (4 * (ln >> 4) + i) * 16 + (ln & 15)] = acc.c[pp][mt][i];
-  __syncthreads();
+  lds_sync();
 #pragma unroll
   for (int o = tid(); o < N; o += MK_WG_THREADS) {
     float s = 0.f;
@@ -620,7 +644,7 @@ __device__ __forceinline__ void reduce_tiles(const Acc<NP, MT>& acc, Smem& sm) {
     for (int k = 0; k < MK_WAVES; ++k) s += sm.u.red[k * N + o];
     sm.out[o] = s;
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // Row offsets of the batch's tokens (row b at b * stride + base), -1 beyond.
@@ -1339,31 +1363,53 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
       if (i < B * P.NB) sm.ssq[i] = sq[k];
     }
   }
-  __syncthreads();
+  lds_sync();
   if (!publish) inv_rms_lds(P, sm);
-  // rank of (b, e): the keys above its own; four threads per pair, each over
-  // a quarter of the experts, summed across the four adjacent lanes
-  for (int i = tid(); i < B * E * 4; i += MK_WG_THREADS) {
-    const int q = i & 3, pe = i >> 2, b = pe / E, e = pe % E;
-    const uint64_t me = T.key[b][e];
-    const int j0 = q * 32;
-    int rank = 0;
-#pragma unroll 4
-    for (int j = 0; j < 32; j += 2) {
-      const uint64_t k0 = T.key[b][j0 + j], k1 = T.key[b][j0 + j + 1];
-      rank += (k0 > me) + (k1 > me);
-    }
-    rank += xor_lane<1>(rank);
-    rank += xor_lane<2>(rank);
-    if (q == 0 && rank < K) {
+  // rank of (b, e): the keys above its own
+  auto keep = [&](int b, int e, int rank) {
+    if (rank < K) {
       T.sel_idx[b][rank] = e;
       T.sel_val[b][rank] = T.logit[b][e];
       // route: each expert's set of tokens as a bit mask (a token keeps an
       // expert at most once)
       atomicOr(&T.tokmask[e], 1u << b);
     }
+  };
+  if (B >= MK_WAVES) {
+    // a wave per token: each lane ranks experts lane and lane + 64 against
+    // every key of the row, read as broadcasts (one address for the wave)
+    const int e0 = lane_id(), e1 = lane_id() + 64;
+    for (int b = wave_id(); b < B; b += MK_WAVES) {
+      const uint64_t me0 = T.key[b][e0], me1 = T.key[b][e1];
+      int r0 = 0, r1 = 0;
+#pragma unroll 8
+      for (int j = 0; j < 128; j += 2) {
+        const uint64_t k0 = T.key[b][j], k1 = T.key[b][j + 1];
+        r0 += (k0 > me0) + (k1 > me0);
+        r1 += (k0 > me1) + (k1 > me1);
+      }
+      if (e0 < E) keep(b, e0, r0);
+      if (e1 < E) keep(b, e1, r1);
+    }
+  } else {
+    // four threads per pair, thread q over the experts j with j % 4 == q (the
+    // four lanes of a pair read adjacent keys: no bank conflicts), summed
+    // across the four adjacent lanes
+    for (int i = tid(); i < B * E * 4; i += MK_WG_THREADS) {
+      const int q = i & 3, pe = i >> 2, b = pe / E, e = pe % E;
+      const uint64_t me = T.key[b][e];
+      int rank = 0;
+#pragma unroll 4
+      for (int j = 0; j < 128; j += 8) {
+        const uint64_t k0 = T.key[b][j + q], k1 = T.key[b][j + 4 + q];
+        rank += (k0 > me) + (k1 > me);
+      }
+      rank += xor_lane<1>(rank);
+      rank += xor_lane<2>(rank);
+      if (q == 0) keep(b, e, rank);
+    }
   }
-  __syncthreads();
+  lds_sync();
   for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
     // softmax over the kept logits (max-subtracted; rank 0 is the max),
     // summed in rank order
@@ -1387,7 +1433,7 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     const uint64_t bal = __ballot(act);
     if (lane_id() == 0) T.ballot[e >> 6] = bal;
   }
-  __syncthreads();
+  lds_sync();
   const uint64_t b0 = T.ballot[0], b1 = E > 64 ? T.ballot[1] : 0ull;
   const int n_active = __popcll(b0) + __popcll(b1);
   if ((int)tid() < E) {
@@ -1404,7 +1450,7 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
       }
     }
   }
-  __syncthreads();
+  lds_sync();
   for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
     const int b = i / K, e = T.sel_idx[b][i % K];
     const int r = __popc(T.tokmask[e] & ((1u << b) - 1u));
@@ -1421,7 +1467,7 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
       RT.sti(2, n_active * P.down_items_per_expert);
     }
   }
-  __syncthreads();
+  lds_sync();
 }
 
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm) { route_build(P, l, sm, true); }
@@ -1621,30 +1667,33 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   struct Stream {
     int base, j, pend;
   };
+  // (the pending claim is issued unconditionally by thread 0 and read only
+  // there, so its result stays in one register: a copy of it, at a join of
+  // paths that did and did not claim, would wait for the atomic at once and,
+  // the memory counter retiring in order, for every weight load before it.
+  // Claims past the queue's end are harmless: their items do not exist.)
   auto stream_start = [&](Stream& q, int base, int32_t ctr, int n) {
     q.base = base;
     q.j = 0;
-    q.pend = 0;
-    if (tid() == 0 && base < n)
+    if (tid() == 0)
       q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)CH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto stream_next = [&](Stream& q, int32_t ctr, int n) -> int {
     if (++q.j < CH) return q.base + q.j;
     if (tid() == 0) sm.claim = q.pend;
-    __syncthreads();
+    lds_sync();
     q.base = sm.claim;
-    __syncthreads();
+    lds_sync();
     q.j = 0;
-    if (tid() == 0 && q.base < n)
+    if (tid() == 0)
       q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)CH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return q.base;
   };
-  // row offsets of row tile rt of active expert a into sm.row_off[k]
-  auto set_rows = [&](int k, int a, int rt) {
-    if ((int)tid() < 16) {
-      const int r = rt * 16 + (int)tid();
-      sm.row_off[k][tid()] = (a >= 0 && r < sm.rt_cnt[a]) ? (sm.rt_slot[a * B + r] / K) * H : -1;
-    }
+  // this lane's row of row tile rt of active expert a: the element offset
+  // of its token's layer input (-1: past the expert's routed tokens)
+  auto row_of = [&](int a, int rt) -> int {
+    const int r = rt * 16 + (int)(lane_id() & 15);
+    return (a >= 0 && r < sm.rt_cnt[a]) ? (sm.rt_slot[a * B + r] / K) * H : -1;
   };
   // one item's weights and routed rows (a zero tile and no rows past the queue)
   auto load = [&](WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int k, int id) {
@@ -1654,23 +1703,24 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
     wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
                valid ? 2 : 0, kh * kh_chunks, (kh + 1) * kh_chunks);
-    set_rows(k, valid ? a : -1, 0);
-    __syncthreads();
-    atile_load_bf16(Ah, U0, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
-    atile_load_bf16(Al, U1, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
+    const int o = row_of(valid ? a : -1, 0);
+    atile_load_row(Ah, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+    atile_load_row(Al, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
   };
   // one item's products and gu stores; the arrival is counted in LDS
   auto compute = [&](const WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int k, int id) {
     const int a = id / upe, r = id % upe;
     const int tt = r >> 1, kh = r & 1;
     const int cnt = sm.rt_cnt[a];
-    for (int rt = 0; rt * 16 < cnt; ++rt) {
+    // (at least one row tile: an active expert has a routed token, and the
+    // compiler then knows the item's loads are consumed before its registers
+    // are loaded again)
+    int rt = 0;
+    do {
       if (rt > 0) {  // an expert with more than 16 routed tokens: the next rows
-        __syncthreads();
-        set_rows(k, a, rt);
-        __syncthreads();
-        atile_load_bf16(Ah, U0, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
-        atile_load_bf16(Al, U1, sm.row_off[k], kh * kh_chunks, (kh + 1) * kh_chunks);
+        const int o = row_of(a, rt);
+        atile_load_row(Ah, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+        atile_load_row(Al, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
       }
       Acc<2, 1> acc;
       mfma_tiles(acc, w, Ah, Al);
@@ -1682,12 +1732,12 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
         const int slot = sm.rt_slot[a * B + rt * 16 + rr], b = slot / K;
         GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, sm.out[which * 256 + rr * 16 + nn] * sm.inv_rms[b]);
       }
-    }
+    } while (++rt * 16 < cnt);
     if (tid() == 0) sm.done_cnt[a] += 1;
   };
   {
-    // two items in flight: the next one's weights stream while the current
-    // computes; the arrivals wait for the end of the phase (one drain), since
+    // three items in flight: the next two items' weights stream while the
+    // current computes; the arrivals wait for the end of the phase (one drain), since
     // down items start only after this claimer's up/gate items
     WTile<2, NCH> w0, w1, w2;
     ATile<1, NCH> h0, l0, h1, l1, h2, l2;
@@ -1784,7 +1834,7 @@ __device__ __forceinline__ void stage_act(const mk_params& P, int a, int r0, int
       }
     }
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // One or two (nblk) adjacent column blocks (cb0, cb0 + 1) of one expert's down
@@ -1835,10 +1885,10 @@ __device__ __forceinline__ void down_pair(const mk_params& P, const mk_task& t, 
   if ((int)tid() < nblk)
     sm.t_old[tid()] = (int)__hip_atomic_fetch_add(&P.ctr[t.a[4] + cb0 + tid()], 1u, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  lds_sync();
   const int last = P.KVH + __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) - 1;
   const int o0 = sm.t_old[0], o1 = sm.t_old[1];
-  __syncthreads();
+  lds_sync();
   if (o0 == last) {
     residual_block(P, t.layer, cb0, sm);
     arrive_nr(P, t.sig_ctr[0]);
@@ -2029,7 +2079,7 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
                                                                 acc.c[pp][mt], 0, 0, 0);
       }
     }
-    __syncthreads();
+    lds_sync();
   }
   reduce_tiles(acc, sm);
   for (int o = tid(); o < 4 * MT * 256; o += MK_WG_THREADS) {
