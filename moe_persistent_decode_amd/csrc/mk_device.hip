@@ -1347,8 +1347,9 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     const int b = i / E, e = i % E;
     T.logit[b][e] = v;
     // a 64-bit key ordered like (logit, -index): the float's bits made
-    // monotone as an unsigned integer, then the complemented index
-    const uint32_t u = __float_as_uint(v);
+    // monotone as an unsigned integer (-0 taken as +0, so equal logits tie
+    // and go by index), then the complemented index
+    const uint32_t u = v == 0.f ? 0u : __float_as_uint(v);
     const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     T.key[b][e] = ((uint64_t)ord << 32) | (uint32_t)(0xffffu - e);
   }

@@ -139,3 +139,46 @@ def test_batch32_ragged_two_row_tiles(mode):
 
 def test_batch17_edge_of_second_tile():
     _run(17, 1, 64, seed=13, mode=0)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_router_ties_go_to_the_lower_index(B):
+    """All router weights zero: every logit is exactly 0, so each token keeps
+    experts 0..k-1 with equal weights 1/k (ties go to the lower index); the
+    ranking runs with four lanes per (token, expert) pair at batch 1 and a
+    wave per token at batch 8. Logits follow the oracle's on the same
+    weights."""
+    cfg = configs.TINY
+    wl = configs.Workload(f"tiny_ties_b{B}", cfg, batch=B, seq_len=(20, 90), ragged=True, seed_batch=57)
+    bs = gen.make_batch(wl, extra_steps=2)
+    weights = gen.make_weights(cfg, seed=tiny_seed()["seed"])
+    for l in range(cfg.n_layers):
+        weights[f"wr.{l}"] = torch.zeros_like(weights[f"wr.{l}"])
+    pool0 = gen.bf16_bits(gen.make_kv_pool(cfg, bs.n_pages, seed=157))
+    lens0 = bs.seq_lens.numpy().astype(np.int64)
+    ref = tj.greedy_decode(cfg, gen.NumpyWeights(weights), pool0.copy(), bs.block_tables.numpy(),
+                           bs.tokens.numpy(), lens0, 2)
+    for s in range(2):
+        for l in range(cfg.n_layers):
+            assert all(sorted(ref.traces[s].topk_idx[l][b].tolist()) == list(range(cfg.top_k)) for b in range(B))
+    pool_gpu = bits_to_torch(pool0)
+    dec = make_decoder(cfg, bs, pool_gpu, int(lens0.max()) + 2, 0, max_batch=B)
+    dec.load_weights({k: v.cuda() for k, v in weights.items()})
+    trace = torch.full((cfg.n_layers, B, cfg.top_k), -1, dtype=torch.int32, device="cuda")
+    dec.set_routing_trace(trace)
+    logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    bt_gpu = bs.block_tables.cuda()
+    for s in range(2):
+        tokens = torch.tensor(ref.tokens_in[s], dtype=torch.int32, device="cuda")
+        seq_lens = torch.tensor(ref.seq_lens[s], dtype=torch.int32, device="cuda")
+        dec.step(tokens, bt_gpu, seq_lens, int(ref.seq_lens[s].max()), logits, nxt)
+        dec.sync()
+        tr = trace.cpu().numpy()
+        assert np.array_equal(tr, np.broadcast_to(np.arange(cfg.top_k, dtype=np.int32), tr.shape)), s
+        lg = logits.cpu().numpy()
+        for b in range(B):
+            ok, mx, rl2 = logits_close(lg[b], ref.logits[s][b])
+            assert ok, (s, b, mx, rl2)
+        say(f"[ties B={B}] step {s}: routes are experts 0..{cfg.top_k - 1} in order")
+    dec.close()
