@@ -1789,17 +1789,22 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     dload(d0, i0);
     int i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
     int staged = -1;
+    // (the error flag is loaded before the next item's weights and tested
+    // after the current item: loaded after them, its test would wait for the
+    // whole prefetch, the memory counter retiring in order)
     while (i0 < n_down) {
+      uint32_t err = ld_relaxed(&P.err[0]);
       dload(d1, i1);
       down_item<2, NCHD>(P, t, i0 / dpe, i0 % dpe, d0, sm, i0 / dpe != staged);
       staged = i0 / dpe;
-      if (ld_relaxed(&P.err[0]) != 0) return;
+      if (err != 0) return;
       i0 = i1 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
       if (i1 >= n_down) break;
+      err = ld_relaxed(&P.err[0]);
       dload(d0, i0);
       down_item<2, NCHD>(P, t, i1 / dpe, i1 % dpe, d1, sm, i1 / dpe != staged);
       staged = i1 / dpe;
-      if (ld_relaxed(&P.err[0]) != 0) return;
+      if (err != 0) return;
       i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
     }
   }
