@@ -209,14 +209,16 @@ WeightFn = Callable[..., np.ndarray]
 
 def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.ndarray,
                 seq_lens: np.ndarray, dtype=np.float32, record: bool = False,
-                router_hook=None):
+                router_hook=None, lm_hook=None):
     """One decode step for a batch; returns (logits [B, V] in dtype, StepTrace).
 
     cfg: mkinputs.configs.ModelConfig. W(name[, layer[, expert]]) returns a
     canonical weight's bf16 bits. pool[l] is layer l's KV pool
     [n_pages, 2, KVH, page_size*D] of bf16 bits; this step's K/V are written
     into it (R1). router_hook(layer, x_norm, wr_bits) -> wr_bits, if given,
-    may replace a layer's router weight before it is used (test inputs only).
+    may replace a layer's router weight before it is used, and
+    lm_hook(x_final, wlm_bits) -> wlm_bits the LM head's (test inputs only:
+    a hook chooses the matrices, the step's arithmetic is unchanged).
     """
     B = len(tokens)
     H, D, P = cfg.hidden, cfg.head_dim, cfg.page_size
@@ -285,5 +287,8 @@ def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.nda
             tr.moe_out.append(y)
     xf = rmsnorm(h, f(W("gamma_f")), cfg.eps)
     tr.x_final = xf
-    logits = xf @ f(W("wlm"))
+    wlm = W("wlm")
+    if lm_hook is not None:
+        wlm = lm_hook(xf, wlm)
+    logits = xf @ f(wlm)
     return logits, tr

@@ -51,26 +51,28 @@ class Run:
         return float(min(greedy_gap(lg).min() for lg in self.logits))
 
 
-def teacher_forced(cfg, W, pool, block_tables, tokens_per_step, seq_len0, dtype=np.float32) -> Run:
-    """Feed given tokens step by step (tokens_per_step [T, B]) from lengths seq_len0."""
+def teacher_forced(cfg, W, pool, block_tables, tokens_per_step, seq_len0, dtype=np.float32, **hooks) -> Run:
+    """Feed given tokens step by step (tokens_per_step [T, B]) from lengths seq_len0.
+    hooks: router_hook / lm_hook, passed to every decode_step."""
     run = Run()
     lens = np.asarray(seq_len0).copy()
     for toks in tokens_per_step:
         toks = np.asarray(toks)
-        lg, tr = decode_step(cfg, W, pool, block_tables, toks, lens, dtype=dtype)
+        lg, tr = decode_step(cfg, W, pool, block_tables, toks, lens, dtype=dtype, **hooks)
         run.tokens_in.append(toks); run.seq_lens.append(lens.copy())
         run.logits.append(lg); run.greedy.append(greedy(lg)); run.traces.append(tr)
         lens = lens + 1
     return run
 
 
-def greedy_decode(cfg, W, pool, block_tables, first_tokens, seq_len0, steps, dtype=np.float32) -> Run:
-    """Decode `steps` greedy steps: each step's argmax is the next step's token."""
+def greedy_decode(cfg, W, pool, block_tables, first_tokens, seq_len0, steps, dtype=np.float32, **hooks) -> Run:
+    """Decode `steps` greedy steps: each step's argmax is the next step's token.
+    hooks: router_hook / lm_hook, passed to every decode_step."""
     run = Run()
     toks = np.asarray(first_tokens).copy()
     lens = np.asarray(seq_len0).copy()
     for _ in range(steps):
-        lg, tr = decode_step(cfg, W, pool, block_tables, toks, lens, dtype=dtype)
+        lg, tr = decode_step(cfg, W, pool, block_tables, toks, lens, dtype=dtype, **hooks)
         run.tokens_in.append(toks.copy()); run.seq_lens.append(lens.copy())
         nxt = greedy(lg)
         run.logits.append(lg); run.greedy.append(nxt); run.traces.append(tr)

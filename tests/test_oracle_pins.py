@@ -350,3 +350,75 @@ def test_moe_reduces_to_single_ffn_when_experts_identical():
     v = od.bf16_to_float(od.float_to_bf16_rne(qkv[0, (QH + KVH) * D:].astype(np.float32)), np.float64).reshape(KVH, D)
     o = np.concatenate([v[hh * KVH // QH] for hh in range(QH)])
     assert np.allclose(attn_part, o @ f(W("wo", 0)), atol=1e-10)
+
+
+# ------------------------------------------------------ trajectory pins ----
+# Multi-step decoding (oracle/trajectory.py) against the independent float64
+# full-sequence forward above: decoding token after token with lengths + 1
+# must give, at every step, the row of the whole sequence's prefill-style
+# logits at that position; greedy decoding must feed each row's argmax as the
+# next token.
+
+from oracle import trajectory as tj
+
+
+def test_greedy_decode_matches_full_sequence_forward():
+    cfg = _tiny(window=8, full_every=2)
+    W = _weights(cfg, seed=21)
+    bt = np.array([[5, 2, 7]])
+    pool = _empty_pool(cfg, 8)
+    run = tj.greedy_decode(cfg, W, pool, bt, np.array([11]), np.array([1]), 19, dtype=np.float64)
+    seq = [11] + [int(g[0]) for g in run.greedy[:-1]]
+    # the tokens fed are the start token then each step's greedy choice
+    assert [int(t[0]) for t in run.tokens_in] == seq
+    # lengths grow by one per step from the start length
+    assert [int(s[0]) for s in run.seq_lens] == list(range(1, 20))
+    full = _full_sequence_forward(cfg, W, seq)
+    got = np.array([lg[0] for lg in run.logits])
+    assert np.max(np.abs(got - full)) < 1e-9
+    # each greedy token is the full forward's argmax (lowest index on ties)
+    assert [int(g[0]) for g in run.greedy] == [int(np.argmax(r)) for r in full]
+    # and every step appended its K/V: 19 positions over pages 5, 2 (16 + 3)
+    assert np.count_nonzero(pool[:, 5]) > 0 and np.count_nonzero(pool[:, 2]) > 0
+    assert np.count_nonzero(pool[:, 7]) == 0
+
+
+def test_teacher_forced_matches_full_sequence_forward_batched():
+    cfg = _tiny()
+    W = _weights(cfg, seed=22)
+    rng = np.random.default_rng(23)
+    T, B = 12, 2
+    toks = rng.integers(0, cfg.vocab, (T, B))
+    bt = np.array([[0, 3], [1, 2]])
+    pool = _empty_pool(cfg, 4)
+    run = tj.teacher_forced(cfg, W, pool, bt, toks, np.array([1, 1]), dtype=np.float64)
+    assert [s.tolist() for s in run.seq_lens] == [[t + 1, t + 1] for t in range(T)]
+    for b in range(B):
+        full = _full_sequence_forward(cfg, W, toks[:, b])
+        got = np.array([lg[b] for lg in run.logits])
+        assert np.max(np.abs(got - full)) < 1e-9
+        assert [int(g[b]) for g in run.greedy] == [int(np.argmax(r)) for r in full]
+
+
+def test_gap_helpers_on_hand_built_rows():
+    # greedy gap: largest minus second largest; a tie gives 0
+    lg = np.array([[1.0, 3.0, 2.5, 3.0], [5.0, 1.0, 4.25, -2.0], [0.0, 0.0, 0.0, 7.5]])
+    assert tj.greedy_gap(lg).tolist() == [0.0, 0.75, 7.5]
+    # router gap at k: k-th minus (k+1)-th largest
+    r = np.array([[0.1, 0.9, 0.5, 0.7], [2.0, 2.0, 1.0, -1.0]])
+    assert np.allclose(tj.router_gap(r, 1), [0.2, 0.0])
+    assert np.allclose(tj.router_gap(r, 2), [0.2, 1.0])
+    assert np.allclose(tj.router_gap(r, 3), [0.4, 2.0])
+    # k = E: nothing is left out, so no decision can flip
+    assert np.all(np.isinf(tj.router_gap(r, 4)))
+
+
+def test_run_minimum_gaps():
+    run = tj.Run()
+    tr = od.StepTrace()
+    tr.router_logits = [np.array([[0.3, 0.1, 0.2]]), np.array([[1.0, 0.95, 0.0]])]
+    run.traces.append(tr)
+    run.logits = [np.array([[1.0, 0.5]]), np.array([[2.0, 1.9, 0.0]])]
+    assert math.isclose(run.min_router_gap(1), 0.05)
+    assert math.isclose(run.min_router_gap(2), 0.1)
+    assert math.isclose(run.min_greedy_gap(), 0.1)
