@@ -78,32 +78,53 @@ typedef struct {
 
 typedef struct mk_handle mk_handle;
 
-/* Create a decoder for `cfg` on HIP device `device`.
- * kv_pool: device, caller-owned, stays valid until mk_destroy. Layout, bf16:
+/* Create a decoder for `cfg` on HIP device `device` (the handle the engine
+ * around the kernel drives step by step: megakernel post, Chinese version,
+ * section "内核周围的推理引擎", the C++ decode service).
+ * kv_pool: the paged KV cache, bf16, in the layout
  *   [n_layers][n_pages][2][n_kv_heads][page_size * head_dim]
  *   plane 0 = K, element (slot s, dim d) at s*head_dim + d;
  *   plane 1 = V, stored transposed: element (slot s, dim d) at d*page_size + s.
  * Page p of a sequence holds its positions [p*page_size, (p+1)*page_size)
  * (tiny-vllm decode walkthrough, section on scattering K/V into blocks).
- * kv_pool_bytes must equal the size of that layout.
- * Allocates the library's weight copy (uninitialised), scratch, counters. */
+ * Either the caller owns it (kv_pool = device pointer, 16-byte aligned,
+ * valid until mk_destroy, kv_pool_bytes = the size of that layout), or
+ * kv_pool = NULL and kv_pool_bytes = 0: the library allocates it, zeroed,
+ * frees it in mk_destroy, and mk_kv_cache gives its address.
+ * Allocates the library's weight copy (uninitialised), scratch and counters.
+ * Errors: MK_ERR_INVALID_ARG / MK_ERR_UNSUPPORTED for the config or the
+ * pool, MK_ERR_OOM, MK_ERR_HIP; nothing is left allocated on failure. */
 mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes,
                     int device, mk_handle** out);
 
+/* Layer `layer`'s part of the KV pool: *kv_base (device) and *bytes, in the
+ * layout above. Valid until mk_destroy; the caller may write context K/V
+ * there (synthetic context, or a prefill's output: the post's engine section
+ * has ordinary prefill kernels fill the pages while the decode service is
+ * parked) when no step is in flight. */
+mk_status mk_kv_cache(mk_handle* h, int layer, void** kv_base, size_t* bytes);
+
 /* Load one layer's weights from caller-owned device bf16 tensors in the
  * canonical row-major [in x out] layout; the library repacks them into its own
- * copy (so the caller may free them once `stream` has passed this call).
+ * copy (so the caller may free them once `stream` has passed this call). The
+ * tensors are the parallel layer's (megakernel post, section "减少波量化":
+ * attention and the MoE read one normalised input; section "任务": QKV and O
+ * projections, router, expert gate/up and down). Errors: MK_ERR_INVALID_ARG
+ * (layer, null or misaligned pointer), MK_ERR_HIP.
  *   gamma [H]; wqkv [H][QH*D + 2*KVH*D] (q heads, then k heads, then v heads);
  *   wo [QH*D][H]; wr [H][E]; wg, wu [E][H][F]; wd [E][F][H]. */
 mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* wqkv,
                         const void* wo, const void* wr, const void* wg, const void* wu,
                         const void* wd, void* stream);
 
-/* Load the embedding [V][H], final norm gain [H] and LM head [H][V] (bf16). */
+/* Load the embedding [V][H], final norm gain [H] and LM head [H][V] (bf16),
+ * caller-owned device tensors, copied or repacked like mk_load_layer's
+ * (section "任务": LM_HEAD). */
 mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f,
                           const void* wlm, void* stream);
 
-/* All weights at once: arrays of n_layers device pointers per tensor kind. */
+/* All weights at once: arrays of n_layers device pointers per tensor kind
+ * (host arrays of device pointers); the same checks as the two calls above. */
 typedef struct {
   const void* emb;
   const void* gamma_f;
@@ -121,7 +142,11 @@ mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream);
 /* Flags of mk_decode_step. */
 #define MK_STEP_ADVANCE 1u /* after the step: tokens[b] = next token, seq_lens[b] += 1 */
 
-/* One decode step for `batch` sequences, enqueued on `stream` (no host sync).
+/* One decode step for `batch` sequences, enqueued on `stream` (no host sync):
+ * one launch of the persistent kernel over the schedule prebuilt for
+ * (batch, context bucket) (megakernel post, section "什么是 Megakernel？";
+ * engine section: select_schedule(max_live_context()), launch; barriers are
+ * cleared by the previous step's kernel, section "屏障").
  *   tokens       device int32 [batch]: token being decoded per sequence
  *   block_tables device int32 [batch][max_pages_per_seq]: physical page ids;
  *                entries for pages holding positions < seq_len must be valid
@@ -143,7 +168,8 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
 
 /* Switch between the persistent megakernel and the kernel-per-op variant
  * (the same op bodies launched once per wave of same-type tasks, with the
- * stream order in place of the counter waits). Takes effect at the next step;
+ * stream order in place of the counter waits: the separate-kernels baseline
+ * of the post's section "加速从何而来"). Takes effect at the next step;
  * steps must not be in flight on another stream. */
 mk_status mk_set_mode(mk_handle* h, int mode);
 
@@ -161,8 +187,16 @@ mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records);
  * to the lower id); NULL stops recording. For checking routing decisions. */
 mk_status mk_set_routing_trace(mk_handle* h, int32_t* trace);
 
+/* Time limit of one dependency wait on the device, in microseconds (0: the
+ * default, 2 s). A wait that exceeds it sets the device error word
+ * (MK_ERR_DEVICE_TIMEOUT) and every workgroup drains to the end of its task
+ * list (the post warns that a wrong arrival count deadlocks: section "屏障").
+ * Takes effect at the next step. */
+mk_status mk_set_wait_limit(mk_handle* h, uint32_t microseconds);
+
 /* Synchronise `stream` and report any device-side error of earlier steps
- * (MK_ERR_DEVICE_TIMEOUT / MK_ERR_DEVICE_FAULT); clears the error word. */
+ * (MK_ERR_DEVICE_TIMEOUT / MK_ERR_DEVICE_FAULT); clears the error word and the
+ * step counters, so the next step starts clean. */
 mk_status mk_sync_status(mk_handle* h, void* stream);
 
 /* Last error message of this handle (or of the last failed mk_create when h is NULL). */
@@ -185,13 +219,14 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
 
 /* ---- schedule introspection (host only, no device work) ---------------- */
 
-/* Task counts of the schedule for (batch, max_seq_len_hint): total tasks and
+/* Task counts of the schedule for (batch, max_seq_len_hint) (section
+ * "任务调度器：将任务映射到 SM": per-SM task lists built on the host): total tasks and
  * the longest per-CU list, and the number of dependency counters. */
 typedef struct {
   int32_t n_tasks;
   int32_t max_tasks_per_cu;   /* longest task list of one resident workgroup */
   int32_t n_counters;
-  int32_t n_cus;              /* resident workgroups (task lists): 2 per compute unit */
+  int32_t n_cus;              /* resident workgroups (task lists): one per compute unit */
   int64_t weight_bytes_per_step; /* weights streamed at batch 1 routing (k experts) */
 } mk_schedule_info;
 mk_status mk_schedule_info_get(mk_handle* h, int batch, int max_seq_len_hint, mk_schedule_info* out);
@@ -202,7 +237,9 @@ mk_status mk_schedule_info_get(mk_handle* h, int batch, int max_seq_len_hint, mk
 mk_status mk_schedule_export(mk_handle* h, int batch, int max_seq_len_hint, int32_t* tasks,
                              int32_t* cu_offsets);
 
-/* Run the schedule on a host model of the device: each CU executes its list
+/* Run the schedule on a host model of the device (the post's advice to check
+ * a schedule's barrier counts before running it: section "你如何编写一个
+ * megakernel？"): each CU executes its list
  * in order, a task runs once its counter waits are met, claimers drain their
  * queues; n_active_experts[l] gives the routing outcome per layer (number of
  * distinct experts). Reports deadlock (a state where no CU can progress) and

@@ -23,7 +23,8 @@ STEP_ADVANCE = 1
 
 # every function include/mk.h declares
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
-           "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_sync_status", "mk_last_error", "mk_destroy",
+           "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
+           "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
 
@@ -60,6 +61,8 @@ def _load():
     lib.mk_load_weights.argtypes = [H, P, P]
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
+    lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
+    lib.mk_kv_cache.argtypes = [H, I, ctypes.POINTER(P), ctypes.POINTER(S)]
     lib.mk_set_mode.argtypes = [H, I]
     lib.mk_set_task_trace.argtypes = [H, P, S]
     lib.mk_debug_read.argtypes = [H, ctypes.c_char_p, P, S]
@@ -111,7 +114,8 @@ def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages
 
 class Decoder:
     """One mk_handle. `kv_pool` is a caller-owned device bf16 tensor in the
-    pool layout of include/mk.h; it must outlive the decoder."""
+    pool layout of include/mk.h (it must outlive the decoder), or None: the
+    library allocates the pool (kv_cache gives each layer's address)."""
 
     def __init__(self, cfg: MkConfig, kv_pool=None, device: int = 0, host_only_cus: int = 0):
         self._h = ctypes.c_void_p()
@@ -120,7 +124,7 @@ class Decoder:
         if host_only_cus:
             st = lib.mk_create_host_only(ctypes.byref(cfg), host_only_cus, ctypes.byref(self._h))
         else:
-            nbytes = kv_pool.numel() * kv_pool.element_size()
+            nbytes = 0 if kv_pool is None else kv_pool.numel() * kv_pool.element_size()
             st = lib.mk_create(ctypes.byref(cfg), _ptr(kv_pool), nbytes, device, ctypes.byref(self._h))
         if st != MK_OK:
             raise MkError(st, lib.mk_last_error(None).decode())
@@ -170,6 +174,15 @@ class Decoder:
 
     def set_routing_trace(self, trace):
         self._check(lib.mk_set_routing_trace(self._h, _ptr(trace)))
+
+    def set_wait_limit(self, microseconds: int):
+        self._check(lib.mk_set_wait_limit(self._h, int(microseconds)))
+
+    def kv_cache(self, layer: int):
+        """(device address, bytes) of layer `layer`'s part of the KV pool."""
+        base, n = ctypes.c_void_p(), ctypes.c_size_t()
+        self._check(lib.mk_kv_cache(self._h, layer, ctypes.byref(base), ctypes.byref(n)))
+        return base.value, n.value
 
     def debug_read(self, name: str, shape, dtype="float32"):
         import numpy as np

@@ -296,6 +296,7 @@ struct Smem {
   float vred[MK_WAVES];
   int ired[MK_WAVES];
   int flag;
+  int errflag;            // thread 0's reading of the device error word, for every wave
   int claim;
   int claim2;
   int old;                // value an arrival counter held before this workgroup's increment
@@ -376,6 +377,24 @@ __device__ __forceinline__ bool wait_task(const mk_params& P, const mk_task& t, 
 
 __device__ __forceinline__ bool wait_one(const mk_params& P, int32_t c, int32_t tgt, Smem& sm, bool force = false) {
   return wait_counters(P, &c, &tgt, 1, sm, force);
+}
+
+// The device error word as thread 0 reads it (other threads: 0). Issued
+// before a streaming loop's next weight loads, so waiting for it later does
+// not wait for them (the memory counter retires in order).
+__device__ __forceinline__ uint32_t error_peek(const mk_params& P) {
+  return tid() == 0 ? ld_relaxed(&P.err[0]) : 0u;
+}
+
+// Whether thread 0's reading e shows a device error, the same answer in every
+// wave (through LDS): a loop that stops on it stops in every wave together, so
+// the workgroup's barriers keep matching.
+__device__ __forceinline__ bool error_seen(uint32_t e, Smem& sm) {
+  if (tid() == 0) sm.errflag = (int)e;
+  lds_sync();
+  const bool r = sm.errflag != 0;
+  lds_sync();
+  return r;
 }
 
 __device__ __forceinline__ int layer_window(const mk_params& P, int l) {
@@ -891,7 +910,7 @@ __device__ __forceinline__ void op_attn(const mk_params& P, const mk_task& t, Sm
     const bool ml = t.b[0] == 1;
     attn_split<D>(P, t.layer, b, g, s, ns, t.a[4], t.a[1] + g, t.a[2], t.a[5] + (ml ? g : bg), t.sig_ctr[0] + g, ml,
                   sm);
-    if (ld_relaxed(&P.err[0]) != 0) return;
+    if (error_seen(error_peek(P), sm)) return;
     id = claim_n(P, t.a[0], 1, sm);
   }
 }
@@ -1516,131 +1535,6 @@ template <int MT, int NCH>
 __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb, const WTile<4, NCH>& w,
                                           Smem& sm, bool stage = true);
 
-// The MoE claimer: expert up/gate items first, then down items. The first
-// down item is claimed at the start and its weights stream alongside the
-// up/gate weights, so they are resident when its expert's up/gate completes.
-//   a[0] up/gate claim counter, a[1] per-expert up/gate done counters,
-//   a[2] items per up/gate claim, a[3] down claim counter, a[4] column-block
-//   counters; sig_ctr[0]: the next layer's input counter.
-template <int MT, int NCH, int NBMAX, int NCHD>
-__device__ __forceinline__ void op_moe(const mk_params& P, const mk_task& t, Smem& sm) {
-  if (!wait_task(P, t, sm)) return;
-  const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1];
-  const int F = P.F, upe = P.up_items_per_expert, B = P.B, K = P.K, E = P.E;
-  const int kc = P.H / 32, kh_chunks = kc / 2;
-  const size_t pstride = (size_t)kc * 512;
-  const Pub GU(P.gu);
-  // items per claim: the host's estimate of the queue over the claimers
-  // expected to be free (any value is correct: claims continue until the
-  // queue is empty)
-  const int nb = min(NBMAX, max(1, t.a[2]));
-  claimer_start(P, claim_ctr, nb, l, sm, t.a[3]);
-  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
-  const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
-  int id0 = sm.claim;
-  int idd = sm.claim2;
-  // the first down item's weights (with one row tile; two row tiles of
-  // operands leave no registers for them, and they load after the up/gate
-  // items)
-  const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
-  const size_t pstride_d = (size_t)kcd * 512;
-  WTile<4, NCHD> wd;
-  if (MT == 1) {
-    const bool v = idd < n_down;
-    const int a = v ? idd / dpe : 0, cb = idd % dpe;
-    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
-               v ? DP : 0, 0, kcd);
-  }
-  // the layer input of every token over the whole K, once per claimer: each
-  // item multiplies its expert's weights with all token rows (one tile of 16
-  // rows costs the same for any count) and keeps the rows routed to it
-  set_rows_batch(P, sm, 0, P.H, 0);
-  __syncthreads();
-  // (per K half, in the chunk-to-wave order the half's weights use)
-  ATile<MT, NCH> Ah0, Al0, Ah1, Al1;
-  atile_load_bf16(Ah0, Pub(u_of(P, l, 0)), sm.row_off[0], 0, kh_chunks);
-  atile_load_bf16(Al0, Pub(u_of(P, l, 1)), sm.row_off[0], 0, kh_chunks);
-  atile_load_bf16(Ah1, Pub(u_of(P, l, 0)), sm.row_off[0], kh_chunks, kc);
-  atile_load_bf16(Al1, Pub(u_of(P, l, 1)), sm.row_off[0], kh_chunks, kc);
-  mark(sm, 0);
-  bool first = true;
-  while (id0 < n_items) {
-    WTile<2, NCH> w[NBMAX];
-#pragma unroll
-    for (int k = 0; k < NBMAX; ++k) {
-      const int id = id0 + k;
-      const bool valid = k < nb && id < n_items;
-      const int a = valid ? id / upe : 0, r = id % upe;
-      const int tt = r >> 1, kh = r & 1;
-      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[min(a, E - 1)]);
-      const int c0 = kh * kh_chunks;
-      // an item past the queue's end loads nothing (np = 0: a zero tile)
-      wtile_load(w[k], P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
-                 valid ? 2 : 0, c0, c0 + kh_chunks);
-    }
-    mark(sm, 1);
-    // the next claim travels while the weights stream
-    const int next = claim_n(P, claim_ctr, nb, sm);
-#pragma unroll
-    for (int k = 0; k < NBMAX; ++k) {
-      const int id = id0 + k;
-      if (k >= nb || id >= n_items) break;
-      const int a = id / upe, r = id % upe;
-      const int tt = r >> 1, kh = r & 1;
-      const int cnt = sm.rt_cnt[a];
-      // this K half's operand (a bitwise blend: a select between the two
-      // tiles would be turned into a dynamically indexed array in scratch)
-      ATile<MT, NCH> Hh, Hl;
-      const uint32_t hi_half = 0u - (uint32_t)kh;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          Hh.a[mt][i] = (Ah1.a[mt][i] & hi_half) | (Ah0.a[mt][i] & ~hi_half);
-          Hl.a[mt][i] = (Al1.a[mt][i] & hi_half) | (Al0.a[mt][i] & ~hi_half);
-        }
-      Acc<2, MT> acc;
-      mfma_tiles(acc, w[k], Hh, Hl);
-      reduce_tiles(acc, sm);
-      if (k == 0 && first) mark(sm, 2);
-      // gu[slot][kh][gate|up][F] for the tokens routed to the expert
-      for (int o = tid(); o < 2 * cnt * 16; o += MK_WG_THREADS) {
-        const int which = o / (cnt * 16), rr = (o / 16) % cnt, nn = o % 16;
-        const int slot = sm.rt_slot[a * B + rr], b = slot / K;
-        const float v = sm.out[(which * MT + b / 16) * 256 + (b % 16) * 16 + nn];
-        GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, v * sm.inv_rms[b]);
-      }
-    }
-    // one drain for the batch, then each item's arrival on its expert's counter
-    sync_published();
-    if ((int)tid() < nb && id0 + (int)tid() < n_items)
-      __hip_atomic_fetch_add(&P.ctr[done_base + (id0 + (int)tid()) / upe], 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    if (first) mark(sm, 3);
-    first = false;
-    id0 = next;
-  }
-  if (MT != 1 && idd < n_down) {
-    const int a = idd / dpe, cb = idd % dpe;
-    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0, kcd);
-  }
-  // down items: the next claim travels while the current item computes
-  while (idd < n_down) {
-    const int next = claim_n(P, t.a[3], 1, sm);
-    down_item<MT, NCHD>(P, t, idd / dpe, idd % dpe, wd, sm);
-    if (ld_relaxed(&P.err[0]) != 0) return;
-    idd = next;
-    if (idd < n_down) {
-      const int a = idd / dpe, cb = idd % dpe;
-      const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-      wtile_load(wd, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d, DP, 0,
-                 kcd);
-    }
-  }
-}
-
 // The claiming MoE above 16 tokens: each up/gate item's matrix-core rows are
 // the tokens routed to its expert (a second 16-row tile when an expert has
 // more), loaded together with the item's weights, so an item's operand takes
@@ -1793,18 +1687,18 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     // after the current item: loaded after them, its test would wait for the
     // whole prefetch, the memory counter retiring in order)
     while (i0 < n_down) {
-      uint32_t err = ld_relaxed(&P.err[0]);
+      uint32_t err = error_peek(P);
       dload(d1, i1);
       down_item<2, NCHD>(P, t, i0 / dpe, i0 % dpe, d0, sm, i0 / dpe != staged);
       staged = i0 / dpe;
-      if (err != 0) return;
+      if (error_seen(err, sm)) return;
       i0 = i1 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
       if (i1 >= n_down) break;
-      err = ld_relaxed(&P.err[0]);
+      err = error_peek(P);
       dload(d0, i0);
       down_item<2, NCHD>(P, t, i1 / dpe, i1 % dpe, d1, sm, i1 / dpe != staged);
       staged = i1 / dpe;
-      if (err != 0) return;
+      if (error_seen(err, sm)) return;
       i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
     }
   }
@@ -2032,7 +1926,7 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
     down_pair<NCHD>(P, t, a, cb0, ng, wd0, wd1, a != staged, sm);
     staged = a;
     i += ng;
-    if (ld_relaxed(&P.err[0]) != 0) return;
+    if (error_seen(error_peek(P), sm)) return;
   }
   mark(sm, 3);
 }
@@ -2560,10 +2454,16 @@ __device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm) {
     step(xor_lane<2>(v), xor_lane<2>(ix));
     step(xor_lane<1>(v), xor_lane<1>(ix));
     if (ln == 0) {
-      if (P.next_tokens) P.next_tokens[b] = ix;
-      if (P.flags & 1u) {
-        P.tokens[b] = ix;
-        P.seq_lens[b] = P.seq_lens[b] + 1;
+      if (ix == 0x7fffffff) {
+        // no logit of the row compares greater than -inf (all NaN or -inf):
+        // there is no greedy token, and the step reports it
+        raise_error(P, MK_DEVERR_FAULT, 6000 + b, 0u);
+      } else {
+        if (P.next_tokens) P.next_tokens[b] = ix;
+        if (P.flags & 1u) {
+          P.tokens[b] = ix;
+          P.seq_lens[b] = P.seq_lens[b] + 1;
+        }
       }
     }
   }
@@ -2587,12 +2487,12 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
       break;
     case MK_OP_ROUTER: op_router<MT, 32 / MK_WAVES>(P, t, sm); break;
     case MK_OP_MOE_UP:
-      if (MT == 1 && t.b[2] > 0)  // fixed shares (b[2]: the claimer count)
+      // at most 16 tokens: fixed shares (b[2], the claimer count, is set);
+      // above: claiming, each item's routed rows
+      if constexpr (MT == 1)
         op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
-      else if (MT == 2)  // above 16 tokens: each item's routed rows
-        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
       else
-        op_moe<MT, 32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
+        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
       break;
     case MK_OP_MOE_FUSED:
       if (MT == 1) op_moe_fused<2048 / 256, 32 / MK_WAVES>(P, t, sm);

@@ -114,6 +114,8 @@ struct mk_handle {
            *wd = nullptr, *wlm = nullptr;
   float* rope = nullptr;
   uint16_t* kv = nullptr;
+  bool kv_owned = false;  // the pool was allocated by mk_create (kv_pool NULL)
+  size_t kv_bytes = 0;
   void* scratch = nullptr;
   uint16_t* u = nullptr;
   uint16_t* o = nullptr;
@@ -872,13 +874,15 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   if (st != MK_OK) return st;
   const mk_config& c = *cfg;
   const size_t kv_want = (size_t)c.n_layers * c.n_pages * 2 * c.n_kv_heads * c.page_size * c.head_dim * 2;
-  if (!kv_pool || kv_pool_bytes != kv_want)
+  if (kv_pool && kv_pool_bytes != kv_want)
     return fail(nullptr, MK_ERR_INVALID_ARG, "kv_pool must be %zu bytes (got %zu)", kv_want, kv_pool_bytes);
+  if (!kv_pool && kv_pool_bytes != 0)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "kv_pool_bytes must be 0 when the library allocates the pool");
   if ((uintptr_t)kv_pool % 16) return fail(nullptr, MK_ERR_INVALID_ARG, "kv_pool must be 16-byte aligned");
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
     return fail(nullptr, MK_ERR_INVALID_ARG, "no HIP device %d", device);
-  auto h = std::make_unique<mk_handle>();
+  auto h = std::unique_ptr<mk_handle, void (*)(mk_handle*)>(new mk_handle(), mk_destroy);
   h->cfg = c;
   h->device = device;
   if (hipSetDevice(device) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "hipSetDevice failed");
@@ -922,7 +926,15 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->wr = h->w_all + o_wr;
   h->wgu = h->w_all + o_wgu;
   h->wd = h->w_all + o_wd;
-  h->kv = (uint16_t*)kv_pool;
+  h->kv_bytes = kv_want;
+  if (kv_pool) {
+    h->kv = (uint16_t*)kv_pool;
+  } else {
+    if (hipMalloc(&h->kv, kv_want) != hipSuccess)
+      return fail(nullptr, MK_ERR_OOM, "cannot allocate the %.2f GB KV pool", kv_want / 1e9);
+    h->kv_owned = true;
+    if (hipMemset(h->kv, 0, kv_want) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "KV pool clear");
+  }
   h->layer_loaded.assign(L, false);
 
   // RoPE table: angle = pos * theta^(-2i/D) in double, cos/sin rounded to float
@@ -1002,6 +1014,7 @@ void mk_destroy(mk_handle* h) {
     if (h->w_all) hipFree(h->w_all);
     if (h->rope) hipFree(h->rope);
     if (h->scratch) hipFree(h->scratch);
+    if (h->kv_owned && h->kv) hipFree(h->kv);
     for (auto* c : h->ctr)
       if (c) hipFree(c);
   }
@@ -1219,6 +1232,22 @@ mk_status mk_set_mode(mk_handle* h, int mode) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (mode != MK_MODE_MEGAKERNEL && mode != MK_MODE_KERNEL_PER_OP) return fail(h, MK_ERR_INVALID_ARG, "unknown mode");
   h->cfg.mode = mode;
+  return MK_OK;
+}
+
+mk_status mk_set_wait_limit(mk_handle* h, uint32_t microseconds) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  h->timeout_ticks = microseconds == 0 ? 200000000 : (int64_t)microseconds * 100;  // 100 MHz ticks
+  return MK_OK;
+}
+
+mk_status mk_kv_cache(mk_handle* h, int layer, void** kv_base, size_t* bytes) {
+  if (!h || !kv_base || !bytes) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  if (layer < 0 || layer >= h->cfg.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
+  const size_t per = h->kv_bytes / h->cfg.n_layers;
+  *kv_base = (char*)h->kv + per * layer;
+  *bytes = per;
   return MK_OK;
 }
 
