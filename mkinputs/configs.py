@@ -79,6 +79,12 @@ class ModelConfig:
 TINY = ModelConfig(name="tiny", hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                    n_experts=8, top_k=2, expert_ffn=128, vocab=1024, n_layers=2)
 
+# the tiny shapes with a sliding window: layer 0 attends to the 48 most recent
+# positions (three pages, not page-aligned in general), layer 1 to all
+TINY_WIN = ModelConfig(name="tiny_win", hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                       n_experts=8, top_k=2, expert_ffn=128, vocab=1024, n_layers=2,
+                       window=48, full_every=2)
+
 LAYER1 = ModelConfig(name="layer1", hidden=2048, n_q_heads=32, n_kv_heads=4, head_dim=128,
                      n_experts=128, top_k=8, expert_ffn=768, vocab=131072, n_layers=1)
 

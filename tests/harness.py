@@ -73,6 +73,15 @@ def make_decoder(cfg, bs: gen.BatchState, pool_gpu: torch.Tensor, max_seq_len: i
     return mk.Decoder(mc, pool_gpu)
 
 
+def _bf16_step(bits, up):
+    """Move bf16 values one unit in the last place up (where `up`) or down."""
+    from oracle import decode as od
+    v = od.bf16_to_float(bits, np.float64)
+    mag = np.abs(v)
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 2.0 ** -133)
+    return od.float_to_bf16_rne((v + np.where(up, ulp, -ulp)).astype(np.float32))
+
+
 def router_repair_hook(cfg, gap: float = 2e-2, coords: int = 16, max_rounds: int = 400):
     """An oracle router_hook that widens every token's gap between its k-th and
     (k+1)-th router logit to at least `gap`, so the top-k set is decided by a
@@ -89,15 +98,11 @@ def router_repair_hook(cfg, gap: float = 2e-2, coords: int = 16, max_rounds: int
     from oracle import decode as od
     repaired = {}
 
-    def bf16_step(bits, up):
-        v = od.bf16_to_float(bits, np.float64)
-        mag = np.abs(v)
-        ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 2.0 ** -133)
-        return od.float_to_bf16_rne((v + np.where(up, ulp, -ulp)).astype(np.float32))
-
     def hook(l, x, wr):
         wr = repaired.get(l, wr).copy()
         k = cfg.top_k
+        if k >= wr.shape[1]:
+            return wr
         changed = False
         for _ in range(max_rounds):
             r = x @ od.bf16_to_float(wr, x.dtype)
@@ -110,8 +115,8 @@ def router_repair_hook(cfg, gap: float = 2e-2, coords: int = 16, max_rounds: int
                 done = False
                 top = np.argsort(-np.abs(x[b]))[:coords]
                 pos = x[b, top] > 0
-                wr[top, e_in] = bf16_step(wr[top, e_in], pos)
-                wr[top, e_out] = bf16_step(wr[top, e_out], ~pos)
+                wr[top, e_in] = _bf16_step(wr[top, e_in], pos)
+                wr[top, e_out] = _bf16_step(wr[top, e_out], ~pos)
                 changed = True
             if done:
                 break
@@ -122,3 +127,81 @@ def router_repair_hook(cfg, gap: float = 2e-2, coords: int = 16, max_rounds: int
         return wr
 
     return hook, repaired
+
+
+def lm_repair_hook(gap: float = 2e-2, coords: int = 16, max_rounds: int = 400):
+    """An oracle lm_hook that widens every row's gap between its largest and
+    second-largest logit to at least `gap`, so the greedy token is decided by a
+    margin far above the GPU's operand rounding.
+
+    Like the router repair: the two columns of the LM head move apart by whole
+    bf16 steps on the `coords` coordinates of the final normalised input with
+    the largest magnitude, round after round, until every row clears the gap.
+    Only the moved columns' logits are recomputed between rounds. The repaired
+    matrix persists (state["wlm"], None until a repair happens), so later steps
+    start from it and the GPU can be given the same weights.
+    """
+    from oracle import decode as od
+    state = {"wlm": None, "repairs": 0}
+
+    def hook(xf, wlm):
+        w = state["wlm"] if state["wlm"] is not None else wlm
+        r = xf @ od.bf16_to_float(w, xf.dtype)
+        copied = False
+        for _ in range(max_rounds):
+            done = True
+            for b in range(r.shape[0]):
+                order = np.argsort(-r[b], kind="stable")[:2]
+                e1, e2 = int(order[0]), int(order[1])
+                if r[b, e1] - r[b, e2] >= gap:
+                    continue
+                done = False
+                if not copied:
+                    w = w.copy()
+                    copied = True
+                top = np.argsort(-np.abs(xf[b]))[:coords]
+                pos = xf[b, top] > 0
+                w[top, e1] = _bf16_step(w[top, e1], pos)
+                w[top, e2] = _bf16_step(w[top, e2], ~pos)
+                cols = [e1, e2]
+                r[:, cols] = xf @ od.bf16_to_float(w[:, cols], xf.dtype)
+                state["repairs"] += 1
+            if done:
+                break
+        else:
+            raise AssertionError("LM-head repair did not converge")
+        if copied:
+            state["wlm"] = w
+        return w
+
+    return hook, state
+
+
+class RepairUploads:
+    """Keeps the decoder's router and LM-head matrices equal to the repaired
+    ones the oracle's hooks chose. layer_weights(l) and global_weights() give
+    the canonical device tensors as drawn (dicts keyed like gen's names)."""
+
+    def __init__(self, dec, repaired_router: dict, lm_state: dict, layer_weights, global_weights):
+        self.dec, self.rrep, self.lst = dec, repaired_router, lm_state
+        self.layer_weights, self.global_weights = layer_weights, global_weights
+        self.up_r, self.up_lm = {}, None
+
+    def sync(self):
+        import torch
+        for l, wr in self.rrep.items():
+            if l in self.up_r and np.array_equal(self.up_r[l], wr):
+                continue
+            w = self.layer_weights(l)
+            w[f"wr.{l}"] = bits_to_torch(wr)
+            self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.LAYER_KINDS))
+            self.up_r[l] = wr.copy()
+        wlm = self.lm_state_wlm()
+        if wlm is not None and (self.up_lm is None or not np.array_equal(self.up_lm, wlm)):
+            g = self.global_weights()
+            self.dec.load_globals(g["emb"], g["gamma_f"], bits_to_torch(wlm))
+            self.up_lm = wlm.copy()
+        torch.cuda.synchronize()
+
+    def lm_state_wlm(self):
+        return self.lst["wlm"]

@@ -204,3 +204,14 @@ def test_fused_moe_residual_tasks(batch):
             assert wait_t[r, j] == len(moe) + len(op)
         assert len(set(sig[res].tolist())) == 1
     d.close()
+
+
+def test_host_only_handle_has_no_kv_pool_and_takes_a_wait_limit():
+    import moe_persistent_decode_amd as mk
+    d = _host(configs.TINY)
+    with pytest.raises(mk.MkError) as e:
+        d.kv_cache(0)
+    assert e.value.status == 7  # MK_ERR_STATE
+    d.set_wait_limit(50)        # stored for later steps
+    d.set_wait_limit(0)         # back to the default
+    d.close()
