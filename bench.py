@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-ab", action="store_true", help="skip the kernel-per-op comparison")
     ap.add_argument("--op-trace", default=None, metavar="PATH",
                     help="after timing, trace one more megakernel step per task and write a per-opcode summary (markdown)")
+    ap.add_argument("--ablation", default=None, metavar="PATH",
+                    help="instead of the benchmark line: time every wave order and placement of the scheduler "
+                         "at batch 1, 2 and 4 (48 layers, 8K) and write the table (markdown) to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference for HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "megakernel_traffic.json"),
@@ -215,6 +218,65 @@ def measure(wl, steps, warmup, ab, trace_path=None):
     return res, bs
 
 
+ORDERS = {0: "shipped", 1: "qkv-first", 2: "attention-first"}
+PLACEMENTS = {0: "tuned", 1: "round-robin", 2: "affinity"}
+
+
+def ablation(path, steps, warmup):
+    """The scheduler ablation (megakernel post, Chinese version, section on the
+    task scheduler: wave orders and a dependency-affinity placement timed at
+    batch 1, 2 and 4 with 8K contexts): tok/s of every combination, the same
+    inputs and greedy decoding, and each one's logits against the shipped
+    schedule's on the same step."""
+    import numpy as np
+    import torch
+
+    import moe_persistent_decode_amd as mk
+    from mkinputs import configs
+    rows = []
+    for name in ("full48_b1_8k", "full48_b2_8k", "full48_b4_8k"):
+        wl = configs.WORKLOADS[name]
+        runs = 1 + len(ORDERS) * len(PLACEMENTS)
+        r = Run(wl, steps, warmup, runs)
+        base = None
+        for placement in PLACEMENTS:
+            for order in ORDERS:
+                r.dec.set_schedule_options(order, placement)
+                ms, first = r.timed(mk.MODE_MEGAKERNEL)
+                # one more step from a fixed state: logits against the shipped schedule's
+                tok0, len0 = r.tokens.clone(), r.seq_lens.clone()
+                r.tokens.copy_(torch.tensor(r.bs.tokens.numpy(), device="cuda"))
+                r.seq_lens.copy_(torch.tensor(r.bs.seq_lens.numpy() + r.done, device="cuda"))
+                r.dec.step(r.tokens, r.bt, r.seq_lens, r.hint + r.done, r.logits, stream=r.stream)
+                r.dec.sync(r.stream)
+                lg = r.logits.cpu().numpy()
+                r.tokens.copy_(tok0)
+                r.seq_lens.copy_(len0)
+                if base is None:
+                    base = lg
+                d = float(np.abs(lg - base).max())
+                rows.append((wl.batch, ORDERS[order], PLACEMENTS[placement], r.B * r.K / (ms / 1e3), ms / r.K, d,
+                              bool(np.array_equal(np.argmax(lg, -1), np.argmax(base, -1)))))
+                log(f"[ablation] B={wl.batch} {ORDERS[order]:15s} {PLACEMENTS[placement]:11s} "
+                    f"{rows[-1][3]:8.1f} tok/s  {ms / r.K:.3f} ms/step  max|logits - shipped| {d:.2e}")
+        r.close()
+    lines = ["# Scheduler ablation: wave order and placement (48 layers, 8K context)", "",
+             "Command (from the repository root on the MI355X box):", "", "```",
+             f"python3 bench.py --ablation {os.path.basename(path)} --steps {steps} --warmup {warmup}", "```", "",
+             "Megakernel decode rate per combination, greedy decoding from the same inputs "
+             f"({steps} timed steps after {warmup} warm-up steps each). The last columns compare one "
+             "step's logits with the shipped order and tuned placement on the same state (the fused "
+             "MoE of at most 4 tokens groups the claimers' partial sums by their shares, so placements "
+             "may differ in the last bits).", "",
+             "| batch | wave order | placement | tok/s | ms/step | vs shipped + tuned | max abs logit diff | greedy equal |",
+             "|---:|---|---|---:|---:|---:|---:|---|"]
+    ref = {b: t for b, o, p, t, _, _, _ in rows if o == "shipped" and p == "tuned"}
+    for b, o, p, t, ms, d, eq in rows:
+        lines.append(f"| {b} | {o} | {p} | {t:.1f} | {ms:.3f} | {t / ref[b] - 1:+.1%} | {d:.1e} | {eq} |")
+    open(path, "w").write("\n".join(lines) + "\n")
+    log(f"[ablation] table written to {path}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -225,6 +287,9 @@ def main():
 
     from mkinputs import configs, gen
     torch.cuda.set_device(0)
+    if args.ablation:
+        ablation(args.ablation, args.steps, args.warmup)
+        return
     wl = configs.WORKLOADS[args.workload]
     res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace)
 

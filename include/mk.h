@@ -187,6 +187,30 @@ mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records);
  * to the lower id); NULL stops recording. For checking routing decisions. */
 mk_status mk_set_routing_trace(mk_handle* h, int32_t* trace);
 
+/* Schedule knobs (megakernel post, Chinese version, section "任务调度器：将任务映射到
+ * SM": the host builds named waves per layer, picks their order, flattens them
+ * and places task k on unit k mod n; an ablation there compares wave orders
+ * and a dependency-affinity placement).
+ *   wave order: MK_ORDER_SHIPPED   router, qkv, attention, MoE, O-proj, residual
+ *               MK_ORDER_QKV_FIRST qkv before router, otherwise shipped
+ *               MK_ORDER_ATTENTION_FIRST  O-proj before the MoE claimers
+ *   placement:  MK_PLACE_TUNED       round-robin, except MoE claimers on units
+ *                                    without attention work, O projections on
+ *                                    the attention units, residual tasks on
+ *                                    units free of the next layer's first tasks
+ *               MK_PLACE_ROUND_ROBIN task k on unit k mod n, nothing else
+ *               MK_PLACE_AFFINITY    tuned, but each attention claimer on the
+ *                                    unit of a QKV task it waits for and each
+ *                                    residual task on the unit of its column
+ *                                    block's first O projection
+ * Every combination decodes the same step (only timing and, in the fused MoE
+ * of at most 4 tokens, the grouping of the claimers' partial sums change).
+ * Drops the cached schedules (synchronises the device); no step may be in
+ * flight on another stream. MK_ERR_INVALID_ARG for an unknown value. */
+enum { MK_ORDER_SHIPPED = 0, MK_ORDER_QKV_FIRST = 1, MK_ORDER_ATTENTION_FIRST = 2 };
+enum { MK_PLACE_TUNED = 0, MK_PLACE_ROUND_ROBIN = 1, MK_PLACE_AFFINITY = 2 };
+mk_status mk_set_schedule_options(mk_handle* h, int wave_order, int placement);
+
 /* Time limit of one dependency wait on the device, in microseconds (0: the
  * default, 2 s). A wait that exceeds it sets the device error word
  * (MK_ERR_DEVICE_TIMEOUT) and every workgroup drains to the end of its task

@@ -119,6 +119,9 @@ WORKLOADS = {
     "layer1_b1_8k": Workload("layer1_b1_8k", LAYER1, batch=1, seq_len=(8192, 8192), steps=16),
     # the 48-layer model at batch 1, 8K context
     "full48_b1_8k": Workload("full48_b1_8k", FULL48, batch=1, seq_len=(8192, 8192), steps=256),
+    # batches 2 and 4 at 8K (the scheduler ablation's batch sizes)
+    "full48_b2_8k": Workload("full48_b2_8k", FULL48, batch=2, seq_len=(8192, 8192), steps=64),
+    "full48_b4_8k": Workload("full48_b4_8k", FULL48, batch=4, seq_len=(8192, 8192), steps=64),
     # batch 32, ragged contexts U{512..16384}
     "full48_b32_ragged": Workload("full48_b32_ragged", FULL48, batch=32, seq_len=(512, 16384),
                                   ragged=True, steps=16),

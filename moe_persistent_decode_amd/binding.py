@@ -19,11 +19,14 @@ STATUS = {0: "MK_OK", 1: "MK_ERR_INVALID_ARG", 2: "MK_ERR_UNSUPPORTED", 3: "MK_E
           5: "MK_ERR_DEVICE_TIMEOUT", 6: "MK_ERR_DEVICE_FAULT", 7: "MK_ERR_STATE"}
 MODE_MEGAKERNEL = 0
 MODE_KERNEL_PER_OP = 1
+ORDER_SHIPPED, ORDER_QKV_FIRST, ORDER_ATTENTION_FIRST = 0, 1, 2
+PLACE_TUNED, PLACE_ROUND_ROBIN, PLACE_AFFINITY = 0, 1, 2
 STEP_ADVANCE = 1
 
 # every function include/mk.h declares
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
+           "mk_set_schedule_options",
            "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
@@ -62,6 +65,7 @@ def _load():
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
     lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
+    lib.mk_set_schedule_options.argtypes = [H, I, I]
     lib.mk_kv_cache.argtypes = [H, I, ctypes.POINTER(P), ctypes.POINTER(S)]
     lib.mk_set_mode.argtypes = [H, I]
     lib.mk_set_task_trace.argtypes = [H, P, S]
@@ -174,6 +178,10 @@ class Decoder:
 
     def set_routing_trace(self, trace):
         self._check(lib.mk_set_routing_trace(self._h, _ptr(trace)))
+
+    def set_schedule_options(self, wave_order: int = 0, placement: int = 0):
+        """Wave order (ORDER_*) and placement (PLACE_*) of later steps' schedules."""
+        self._check(lib.mk_set_schedule_options(self._h, int(wave_order), int(placement)))
 
     def set_wait_limit(self, microseconds: int):
         self._check(lib.mk_set_wait_limit(self._h, int(microseconds)))

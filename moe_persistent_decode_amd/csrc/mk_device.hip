@@ -813,22 +813,28 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
     const float mnew = fmaxf(m, mloc);
     if (mnew != kNegInf) {
       const float alpha = (m == kNegInf) ? 0.f : __expf(m - mnew);
-      uint32_t pb[4];
+      // the probabilities as a split pair too: with context values of mixed
+      // sign the output is a near-cancelling average, and bf16 probabilities
+      // alone would leave it about 2^-9 relative error at any length
+      uint32_t ph[4], pl[4];
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pv = sv[i] == kNegInf ? 0.f : __expf(sv[i] - mnew);
-        pb[i] = f2bf(pv);
-        ps += bf2f((uint16_t)pb[i]);
+        ph[i] = f2bf(pv);
+        pl[i] = f2bf(pv - bf2f((uint16_t)ph[i]));
+        ps += pv;
       }
       ps = sum32(sum16(ps));
       lsum = lsum * alpha + ps;
       m = mnew;
-      const s16x4_t pB = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+      const s16x4_t pH = {(short)ph[0], (short)ph[1], (short)ph[2], (short)ph[3]};
+      const s16x4_t pL = {(short)pl[0], (short)pl[1], (short)pl[2], (short)pl[3]};
 #pragma unroll
       for (int d = 0; d < NT; ++d) {
         oacc[d] *= alpha;
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, pg.v[d]), pB, oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, pg.v[d]), pL, oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, pg.v[d]), pH, oacc[d], 0, 0, 0);
       }
     }
   };

@@ -98,6 +98,8 @@ void add_wait(mk_task& t, int c, int tgt) {
 
 struct mk_handle {
   mk_config cfg{};
+  int wave_order = MK_ORDER_SHIPPED;
+  int placement = MK_PLACE_TUNED;
   int device = 0;
   bool host_only = false;
   int n_cu = 0;       // compute units
@@ -340,110 +342,134 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   // Fused MoE (at most MK_FUSED_B tokens): the attention splits only count
   // per group and the O projection tasks merge them.
   const bool fused_all = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
+  (void)fused_all;
+  const bool tuned = h->placement != MK_PLACE_ROUND_ROBIN;
+  const bool affinity = h->placement == MK_PLACE_AFFINITY;
   for (int l = 0; l < L; ++l) {
     const CtrIdx x = ci(l);
     auto wait_input = [&](mk_task& t) { add_wait(t, resid(l), NB); };
-    // router over K splits; the last one does top-k and route finalize
-    begin_wave();
-    const int rpanels = h->e_pad / 16;
-    for (int ks = 0; ks < h->router_ks; ++ks)
-      for (int p = 0; p < rpanels; p += h->router_np) {
-        mk_task t = make_task(MK_OP_ROUTER, l);
-        t.a[0] = p;
-        t.a[1] = std::min(h->router_np, rpanels - p);
-        t.a[2] = ks * kc / h->router_ks;
-        t.a[3] = (ks + 1) * kc / h->router_ks;
-        t.a[4] = ks;
-        t.a[5] = x.router;
-        wait_input(t);
-        t.sig_ctr[0] = x.route;
-        push(t);
-      }
-    S->n_router = h->n_router_tasks;
-    // qkv, per kv group: its q heads, its k head, its v head
-    begin_wave();
-    for (int g = 0; g < KVH; ++g) {
-      const int ranges[3][2] = {{g * h->G * c.head_dim / 16, (g + 1) * h->G * c.head_dim / 16},
-                                {(h->q_dim + g * c.head_dim) / 16, (h->q_dim + (g + 1) * c.head_dim) / 16},
-                                {(h->q_dim + h->kv_dim + g * c.head_dim) / 16,
-                                 (h->q_dim + h->kv_dim + (g + 1) * c.head_dim) / 16}};
-      int n = 0;
-      for (auto& rg : ranges)
-        for (int p = rg[0]; p < rg[1]; p += qkv_np) {
-          mk_task t = make_task(MK_OP_QKV, l);
-          t.a[0] = p;
-          t.a[1] = std::min(qkv_np, rg[1] - p);
-          t.a[2] = g;
-          wait_input(t);
-          t.sig_ctr[0] = x.qkv + g;
-          push(t);
-          ++n;
-        }
-      S->n_qkv[g] = n;
-    }
-    if (S->n_qkv[KVH - 1] != S->n_qkv[0]) std::abort();
-    // attention splits; the last split of a (sequence, group) combines
-    begin_wave();
-    const int pps_l = window_of(c, l) ? S->pps : S->pps_full;
-    const int ns = splits_for(h, l, S->bucket, pps_l);
-    if (window_of(c, l))
-      S->n_splits_win = ns;
-    else
-      S->n_splits_full = ns;
-    // claimers over the (sequence, group, split) queue
-    const int n_attn_items = B * KVH * ns;
-    const int attn_flat0 = (int)S->flat.size();
-    S->n_attn_claimers.push_back(std::min(n_w, n_attn_items));
-    for (int i = 0; i < S->n_attn_claimers.back(); ++i) {
-      mk_task t = make_task(MK_OP_ATTN, l);
-      t.a[0] = x.attn_claim;
-      t.a[1] = x.qkv;
-      t.a[2] = S->n_qkv[0];
-      t.a[3] = ns;
-      t.a[4] = pps_l;
-      t.a[5] = x.attn;
-      t.b[0] = fused_all ? 1 : 0;
-      t.sig_ctr[0] = x.comb;
-      push(t);
-    }
-    // MoE up/gate claimers
-    begin_wave();
-    const int n_attn = S->n_attn_claimers.back();
-    // Fixed shares (at most 16 tokens): the up/gate items go to the claimers
-    // whose compute unit (round-robin placement: flat index modulo the
-    // workgroups) runs no attention claimer in this layer, when there are
-    // enough of them: the split that completes a (sequence, group) merges
-    // the splits afterwards, and an up/gate share behind that would hold up
-    // the expert's down items. Otherwise every claimer takes a share weighted
-    // so that each compute unit streams about the same bytes in this phase:
-    // the equal share less the key/value bytes of its attention work (weight
-    // wa of 256). Down items are shared equally among the claimers with
-    // up/gate work.
+    // where this layer's tasks went (for the placement of later waves)
+    std::vector<int> qkv_cus, attn_cus;
+    int n_attn = 0, n_attn_items = 0, attn_flat0 = 0, ns = 0, pps_l = 0;
+    int n_free = 0, wa = 256, nt = 0;
     std::vector<char> attn_cu(n_w, 0);
-    for (int i = 0; i < n_attn; ++i) attn_cu[(attn_flat0 + i) % n_w] = 1;
-    const int moe_flat0 = (int)S->flat.size();
-    int n_free = 0;
-    for (int i = 0; i < S->n_up_claimers; ++i) n_free += !attn_cu[(moe_flat0 + i) % n_w];
+    const bool fused = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
     const bool fixed = B <= 16;
-    int wa = 256;
-    {
+    // the unit a task goes to: `cu` when the placement is tuned, else the
+    // round-robin unit of its flat index
+    auto place = [&](const mk_task& t, int cu) {
+      push_at(t, tuned ? cu : -1);
+      return tuned && cu >= 0 ? cu : ((int)S->flat.size() - 1) % n_w;
+    };
+    // router over K splits; the last one does top-k and route finalize
+    auto wave_router = [&]() {
+      begin_wave();
+      const int rpanels = h->e_pad / 16;
+      for (int ks = 0; ks < h->router_ks; ++ks)
+        for (int p = 0; p < rpanels; p += h->router_np) {
+          mk_task t = make_task(MK_OP_ROUTER, l);
+          t.a[0] = p;
+          t.a[1] = std::min(h->router_np, rpanels - p);
+          t.a[2] = ks * kc / h->router_ks;
+          t.a[3] = (ks + 1) * kc / h->router_ks;
+          t.a[4] = ks;
+          t.a[5] = x.router;
+          wait_input(t);
+          t.sig_ctr[0] = x.route;
+          // (it reads the whole layer input: no single producer to follow)
+          place(t, -1);
+        }
+      S->n_router = h->n_router_tasks;
+    };
+    // qkv, per kv group: its q heads, its k head, its v head
+    auto wave_qkv = [&]() {
+      begin_wave();
+      for (int g = 0; g < KVH; ++g) {
+        const int ranges[3][2] = {{g * h->G * c.head_dim / 16, (g + 1) * h->G * c.head_dim / 16},
+                                  {(h->q_dim + g * c.head_dim) / 16, (h->q_dim + (g + 1) * c.head_dim) / 16},
+                                  {(h->q_dim + h->kv_dim + g * c.head_dim) / 16,
+                                   (h->q_dim + h->kv_dim + (g + 1) * c.head_dim) / 16}};
+        int n = 0;
+        for (auto& rg : ranges)
+          for (int p = rg[0]; p < rg[1]; p += qkv_np) {
+            mk_task t = make_task(MK_OP_QKV, l);
+            t.a[0] = p;
+            t.a[1] = std::min(qkv_np, rg[1] - p);
+            t.a[2] = g;
+            wait_input(t);
+            t.sig_ctr[0] = x.qkv + g;
+            qkv_cus.push_back(place(t, -1));
+            ++n;
+          }
+        S->n_qkv[g] = n;
+      }
+      if (S->n_qkv[KVH - 1] != S->n_qkv[0]) std::abort();
+    };
+    // attention splits; the last split of a (sequence, group) combines
+    auto wave_attn = [&]() {
+      begin_wave();
+      pps_l = window_of(c, l) ? S->pps : S->pps_full;
+      ns = splits_for(h, l, S->bucket, pps_l);
+      if (window_of(c, l))
+        S->n_splits_win = ns;
+      else
+        S->n_splits_full = ns;
+      // claimers over the (sequence, group, split) queue
+      n_attn_items = B * KVH * ns;
+      attn_flat0 = (int)S->flat.size();
+      S->n_attn_claimers.push_back(std::min(n_w, n_attn_items));
+      n_attn = S->n_attn_claimers.back();
+      for (int i = 0; i < n_attn; ++i) {
+        mk_task t = make_task(MK_OP_ATTN, l);
+        t.a[0] = x.attn_claim;
+        t.a[1] = x.qkv;
+        t.a[2] = S->n_qkv[0];
+        t.a[3] = ns;
+        t.a[4] = pps_l;
+        t.a[5] = x.attn;
+        t.b[0] = fused ? 1 : 0;
+        t.sig_ctr[0] = x.comb;
+        // affinity: on the unit of a QKV task it depends on (claimers of one
+        // layer never wait for each other, so two may share a unit)
+        const int cu = place(t, affinity && i < (int)qkv_cus.size() ? qkv_cus[i] : -1);
+        attn_cus.push_back(cu);
+        attn_cu[cu] = 1;
+      }
+    };
+    // the MoE claimers' shares (fixed-share and fused paths)
+    auto moe_shares = [&](int moe_flat0) {
+      // Fixed shares (at most 16 tokens): the up/gate items go to the
+      // claimers whose compute unit (round-robin placement: flat index modulo
+      // the workgroups) runs no attention claimer in this layer, when there
+      // are enough of them: the split that completes a (sequence, group)
+      // merges the splits afterwards, and an up/gate share behind that would
+      // hold up the expert's down items. Otherwise every claimer takes a
+      // share weighted so that each compute unit streams about the same bytes
+      // in this phase: the equal share less the key/value bytes of its
+      // attention work (weight wa of 256). Down items are shared equally among
+      // the claimers with up/gate work.
+      n_free = 0;
+      for (int i = 0; i < S->n_up_claimers; ++i) n_free += !attn_cu[(moe_flat0 + i) % n_w];
       const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
       const double up_bytes = e_act * 2.0 * c.expert_ffn * c.hidden * 2.0;
-      const double kv_per = n_attn > 0 ? (double)n_attn_items * pps_l * c.page_size * c.head_dim * 4.0 / n_attn : 0.0;
+      const double kv_per =
+          n_attn > 0 ? (double)n_attn_items * pps_l * c.page_size * c.head_dim * 4.0 / n_attn : 0.0;
       const double f = (up_bytes + (S->n_up_claimers - n_free) * kv_per) / S->n_up_claimers;
       wa = f > 0 ? (int)std::lround(256.0 * std::max(0.0, f - kv_per) / f) : 256;
       if (n_free >= n_w / 4) wa = 0;
       if (n_free == 0 && wa == 0) wa = 256;
-    }
+    };
     // Fused MoE (at most MK_FUSED_B tokens): the same shares over (expert,
     // hidden slice) items; claimers whose share is empty by weight (wa = 0)
     // are left out, and a residual task per column block sums the claimers'
     // rows once all of them and the O projections have arrived.
-    const bool fused = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
-    if (fused) {
-      S->moe_fixed.push_back(0);
-      const int nt = wa == 0 ? n_free : S->n_up_claimers;
+    auto wave_moe_fused = [&]() {
+      begin_wave();
+      const int moe_flat0 = (int)S->flat.size();
+      moe_shares(moe_flat0);
+      nt = wa == 0 ? n_free : S->n_up_claimers;
       S->moe_fused.push_back(nt);
+      S->moe_fixed.push_back(0);
       int k_free = 0, k_attn = n_free;
       for (int i = 0; i < S->n_up_claimers; ++i) {
         const int cu = (moe_flat0 + i) % n_w;
@@ -456,12 +482,15 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         add_wait(t, resid(l), NB);
         add_wait(t, x.router, h->n_router_tasks);
         t.sig_ctr[0] = x.fin;
-        push_at(t, cu);
+        place(t, cu);
       }
       if (k_free + k_attn - n_free != nt) std::abort();
-      // O projection per (group, two column blocks) when that gives at most
-      // one task per attention unit's worth of pairs, so each unit's weights
-      // stream before its wait
+    };
+    // O projection per (group, two column blocks) when that gives at most one
+    // task per attention unit's worth of pairs, so each unit's weights stream
+    // before its wait; on the units that ran the layer's attention
+    std::vector<int> oproj_cus;
+    auto wave_oproj_fused = [&]() {
       begin_wave();
       int n_oproj = 0;
       const int per = (NB % 2 == 0 && KVH * NB / 2 <= n_attn) ? 2 : 1;
@@ -476,13 +505,18 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           t.b[0] = 1;
           t.b[1] = 1;  // merges the group's splits itself
           add_wait(t, x.attn + g, B * ns);
-          push_at(t, (attn_flat0 + n_oproj % n_attn) % n_w);
+          const int cu = place(t, attn_cus[n_oproj % n_attn]);
+          if (g == 0)
+            for (int k = 0; k < per; ++k) oproj_cus.push_back(cu);
           ++n_oproj;
         }
       S->n_oproj = n_oproj;
-      // residual tasks on the units that get no router or QKV task of the
-      // next layer (round-robin from the flat index after these tasks), so
-      // those tasks' weights still stream before the layer input is ready
+    };
+    // residual tasks on the units that get no router or QKV task of the next
+    // layer (round-robin from the flat index after these tasks), so those
+    // tasks' weights still stream before the layer input is ready; with
+    // affinity, on the unit of the block's first O projection
+    auto wave_residual = [&]() {
       begin_wave();
       int n_qkv_tasks = 0;
       for (int g = 0; g < KVH; ++g) n_qkv_tasks += S->n_qkv[g];
@@ -493,60 +527,96 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         t.b[1] = n_free;
         t.b[2] = nt;
         t.b[3] = wa;
-        add_wait(t, x.fin, nt + n_oproj);
+        add_wait(t, x.fin, nt + S->n_oproj);
         add_wait(t, x.route, 1);
         t.sig_ctr[0] = resid(l + 1);
-        push_at(t, (next0 + cb) % n_w);
+        place(t, affinity ? oproj_cus[cb] : (next0 + cb) % n_w);
       }
-      continue;
-    }
-    S->moe_fused.push_back(0);
-    S->moe_fixed.push_back(fixed ? 1 : 0);
-    int k_free = 0, k_attn = n_free;
-    for (int i = 0; i < S->n_up_claimers; ++i) {
-      mk_task t = make_task(MK_OP_MOE_UP, l);
-      t.a[0] = x.up_claim;
-      t.a[1] = x.up_done;
-      // items per claim: the expected queue (distinct experts of B tokens'
-      // top-k under uniform routing) over the claimers likely free when it
-      // opens (those not running attention)
-      const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
-      const int n_early = std::max(1, S->n_up_claimers - n_attn);
-      t.a[2] = std::max(1, (int)std::ceil(e_act * 2 * c.expert_ffn / 16 / n_early));
-      // then the down items (their last block contribution does the residual)
-      t.a[3] = x.down_claim;
-      t.a[4] = x.colblk;
-      t.sig_ctr[0] = resid(l + 1);
-      if (fixed) {
-        t.b[0] = attn_cu[(moe_flat0 + i) % n_w] ? k_attn++ : k_free++;
-        t.b[1] = n_free;
-        t.b[2] = S->n_up_claimers;
-        t.b[3] = wa;
-        add_wait(t, resid(l), NB);
-        add_wait(t, x.router, h->n_router_tasks);
-      } else {
-        add_wait(t, x.route, 1);
+    };
+    // MoE claimers above MK_FUSED_B tokens (fixed shares up to 16, claiming beyond)
+    auto wave_moe = [&]() {
+      begin_wave();
+      const int moe_flat0 = (int)S->flat.size();
+      moe_shares(moe_flat0);
+      S->moe_fused.push_back(0);
+      S->moe_fixed.push_back(fixed ? 1 : 0);
+      int k_free = 0, k_attn = n_free;
+      for (int i = 0; i < S->n_up_claimers; ++i) {
+        mk_task t = make_task(MK_OP_MOE_UP, l);
+        t.a[0] = x.up_claim;
+        t.a[1] = x.up_done;
+        // items per claim: the expected queue (distinct experts of B tokens'
+        // top-k under uniform routing) over the claimers likely free when it
+        // opens (those not running attention)
+        const double e_act = E * (1.0 - std::pow(1.0 - (double)c.top_k / E, B));
+        const int n_early = std::max(1, S->n_up_claimers - n_attn);
+        t.a[2] = std::max(1, (int)std::ceil(e_act * 2 * c.expert_ffn / 16 / n_early));
+        // then the down items (their last block contribution does the residual)
+        t.a[3] = x.down_claim;
+        t.a[4] = x.colblk;
+        t.sig_ctr[0] = resid(l + 1);
+        if (fixed) {
+          t.b[0] = attn_cu[(moe_flat0 + i) % n_w] ? k_attn++ : k_free++;
+          t.b[1] = n_free;
+          t.b[2] = S->n_up_claimers;
+          t.b[3] = wa;
+          add_wait(t, resid(l), NB);
+          add_wait(t, x.router, h->n_router_tasks);
+        } else {
+          add_wait(t, x.route, 1);
+        }
+        // (one claimer per unit: fixed-share claimers wait for each other's
+        // up/gate items)
+        place(t, -1);
       }
-      push(t);
-    }
+    };
     // O projection per (group, column block), on the compute units that ran
     // this layer's attention claimers (their MoE shares are empty or light,
     // so the projection does not queue behind expert work)
-    begin_wave();
-    int n_oproj = 0;
-    for (int g = 0; g < KVH; ++g)
-      for (int cb = 0; cb < NB; ++cb) {
-        mk_task t = make_task(MK_OP_OPROJ, l);
-        t.a[0] = g;
-        t.a[1] = cb;
-        t.a[2] = x.colblk;
-        add_wait(t, x.comb + g, B);
-        add_wait(t, x.route, 1);
-        t.sig_ctr[0] = resid(l + 1);
-        push_at(t, n_attn > 0 ? (attn_flat0 + n_oproj % n_attn) % n_w : -1);
-        ++n_oproj;
+    auto wave_oproj = [&]() {
+      begin_wave();
+      int n_oproj = 0;
+      for (int g = 0; g < KVH; ++g)
+        for (int cb = 0; cb < NB; ++cb) {
+          mk_task t = make_task(MK_OP_OPROJ, l);
+          t.a[0] = g;
+          t.a[1] = cb;
+          t.a[2] = x.colblk;
+          add_wait(t, x.comb + g, B);
+          add_wait(t, x.route, 1);
+          t.sig_ctr[0] = resid(l + 1);
+          place(t, n_attn > 0 ? attn_cus[n_oproj % n_attn] : -1);
+          ++n_oproj;
+        }
+      S->n_oproj = n_oproj;
+    };
+    // the layer's waves in the chosen order (megakernel post, Chinese
+    // version, section on the task scheduler: the host builds named waves per
+    // layer, picks an order and flattens them)
+    if (h->wave_order == MK_ORDER_QKV_FIRST) {
+      wave_qkv();
+      wave_router();
+    } else {
+      wave_router();
+      wave_qkv();
+    }
+    wave_attn();
+    if (fused) {
+      if (h->wave_order == MK_ORDER_ATTENTION_FIRST) {
+        wave_oproj_fused();
+        wave_moe_fused();
+      } else {
+        wave_moe_fused();
+        wave_oproj_fused();
       }
-    S->n_oproj = n_oproj;
+      wave_residual();
+    } else if (h->wave_order == MK_ORDER_ATTENTION_FIRST) {
+      wave_oproj();
+      wave_moe();
+    } else {
+      wave_moe();
+      wave_oproj();
+    }
   }
   // LM head: contiguous panel ranges (whole pairs); the last task picks the
   // greedy tokens
@@ -1232,6 +1302,24 @@ mk_status mk_set_mode(mk_handle* h, int mode) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (mode != MK_MODE_MEGAKERNEL && mode != MK_MODE_KERNEL_PER_OP) return fail(h, MK_ERR_INVALID_ARG, "unknown mode");
   h->cfg.mode = mode;
+  return MK_OK;
+}
+
+mk_status mk_set_schedule_options(mk_handle* h, int wave_order, int placement) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (wave_order < MK_ORDER_SHIPPED || wave_order > MK_ORDER_ATTENTION_FIRST)
+    return fail(h, MK_ERR_INVALID_ARG, "unknown wave order %d", wave_order);
+  if (placement < MK_PLACE_TUNED || placement > MK_PLACE_AFFINITY)
+    return fail(h, MK_ERR_INVALID_ARG, "unknown placement %d", placement);
+  if (wave_order == h->wave_order && placement == h->placement) return MK_OK;
+  if (!h->host_only) {
+    HIPCHECK(h, hipSetDevice(h->device));
+    HIPCHECK(h, hipDeviceSynchronize());  // no step may still read the old lists
+    for (auto& kv : h->scheds) free_schedule(kv.second.get());
+  }
+  h->scheds.clear();
+  h->wave_order = wave_order;
+  h->placement = placement;
   return MK_OK;
 }
 
