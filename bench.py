@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-ab", action="store_true", help="skip the kernel-per-op comparison")
     ap.add_argument("--op-trace", default=None, metavar="PATH",
                     help="after timing, trace one more megakernel step per task and write a per-opcode summary (markdown)")
+    ap.add_argument("--op-trace-raw", default=None, metavar="PATH",
+                    help="with --op-trace: also save the raw per-task records (numpy .npy, int64 [tasks, 8])")
     ap.add_argument("--ablation", default=None, metavar="PATH",
                     help="instead of the benchmark line: time every wave order and placement of the scheduler "
                          "at batch 1, 2 and 4 (48 layers, 8K) and write the table (markdown) to PATH")
@@ -150,7 +152,7 @@ OPNAMES = {1: "EMBED", 2: "QKV", 3: "ATTN (claimer)", 4: "RESIDUAL", 5: "O_PROJ"
            8: "MOE_UP (claimer)", 9: "MOE_FUSED (claimer)", 10: "LM_HEAD"}
 
 
-def op_trace(r, path):
+def op_trace(r, path, raw_path=None):
     """One traced megakernel step: per task its opcode, layer, workgroup and
     device timestamps (start, dependencies satisfied, end); summarised per
     opcode and, for two layers, as a phase timeline."""
@@ -166,6 +168,8 @@ def op_trace(r, path):
     r.dec.sync(r.stream)
     r.dec.set_task_trace(None, 0)
     tr = buf.cpu().numpy().astype(np.int64) & 0xffffffff
+    if raw_path:
+        np.save(raw_path, tr)
     op, layer = tr[:, 0] & 0xff, (tr[:, 0] >> 8) & 0xff
     t0 = tr[:, 1].min()
     us = lambda k: (tr[:, k] - t0) / 100.0  # 100 MHz device clock
@@ -195,7 +199,7 @@ def op_trace(r, path):
     log(f"[bench] per-opcode trace written to {path}")
 
 
-def measure(wl, steps, warmup, ab, trace_path=None):
+def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None):
     import moe_persistent_decode_amd as mk
     r = Run(wl, steps, warmup, 2 if ab else 1)
     ms, first = r.timed(mk.MODE_MEGAKERNEL, record=True)
@@ -212,7 +216,7 @@ def measure(wl, steps, warmup, ab, trace_path=None):
                                 "megakernel_speedup": round(ms_op / ms, 3)}
         log(f"[bench] {wl.name} kernel-per-op: {ms_op / r.K:.3f} ms/step -> megakernel {ms_op / ms:.2f}x")
     if trace_path:
-        op_trace(r, trace_path)
+        op_trace(r, trace_path, raw_path)
     bs = r.bs
     r.close()
     return res, bs
@@ -243,10 +247,13 @@ def ablation(path, steps, warmup):
             for order in ORDERS:
                 r.dec.set_schedule_options(order, placement)
                 ms, first = r.timed(mk.MODE_MEGAKERNEL)
-                # one more step from a fixed state: logits against the shipped schedule's
+                # one more step from the initial state (the first decode position
+                # again: its K/V slot is rewritten with the same values, every
+                # earlier slot is the untouched context): logits against the
+                # shipped schedule's
                 tok0, len0 = r.tokens.clone(), r.seq_lens.clone()
                 r.tokens.copy_(torch.tensor(r.bs.tokens.numpy(), device="cuda"))
-                r.seq_lens.copy_(torch.tensor(r.bs.seq_lens.numpy() + r.done, device="cuda"))
+                r.seq_lens.copy_(torch.tensor(r.bs.seq_lens.numpy(), device="cuda"))
                 r.dec.step(r.tokens, r.bt, r.seq_lens, r.hint + r.done, r.logits, stream=r.stream)
                 r.dec.sync(r.stream)
                 lg = r.logits.cpu().numpy()
@@ -291,7 +298,7 @@ def main():
         ablation(args.ablation, args.steps, args.warmup)
         return
     wl = configs.WORKLOADS[args.workload]
-    res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace)
+    res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace, args.op_trace_raw)
 
     # HBM bytes per launch from the committed counter profile, only while the
     # device code is the one that was profiled

@@ -1119,6 +1119,36 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   const int l = t.layer, p0 = t.a[0], np = t.a[1];
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
+  const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
+  // Each thread's outputs (2 MT of them, element o = tid + k * 512 of the
+  // reduced tiles): the token's length, its page and, for q and k columns,
+  // the RoPE factors depend on no activation, so they load before the
+  // weights and the wait, and the epilogue after the products only computes
+  // and stores.
+  constexpr int NO = 2 * MT * 256 / MK_WG_THREADS;
+  int seq[NO], page[NO];
+  float rc[NO], rs[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int o = tid() + k * MK_WG_THREADS;
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16;
+    const int b = mt * 16 + m;
+    seq[k] = (pp < np && b < P.B) ? P.seq_lens[b] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int o = tid() + k * MK_WG_THREADS;
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int b = mt * 16 + m;
+    const int n = (p0 + pp) * 16 + nn;
+    const bool ok = seq[k] >= 1 && seq[k] <= P.max_seq;
+    const int pos = ok ? seq[k] - 1 : 0;
+    page[k] = ok ? P.bt[b * P.mpps + pos / PS] : -1;
+    const int d = (n < qd ? n : n - qd) % D;
+    const bool rot = ok && n < qd + kvd;
+    rc[k] = rot ? P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0] : 0.f;
+    rs[k] = rot ? P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1] : 0.f;
+  }
   WTile<2, NCH> w;
   wtile_load(w, P.wqkv + l * P.s_wqkv + (size_t)p0 * pstride, pstride, np, 0, kc);
   if (!wait_task(P, t, sm)) return;
@@ -1133,43 +1163,41 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
-  const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
   const Pub KV(P.kv + l * P.s_kv_l), Q(P.q);
-  for (int o = tid(); o < 2 * MT * 256; o += MK_WG_THREADS) {
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int o = tid() + k * MK_WG_THREADS;
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
     if (pp >= np || b >= P.B) continue;
-    const int seq = P.seq_lens[b];
-    if (seq < 1 || seq > P.max_seq) {
-      raise_error(P, MK_DEVERR_FAULT, 2000 + b, (uint32_t)seq);
+    if (seq[k] < 1 || seq[k] > P.max_seq) {
+      raise_error(P, MK_DEVERR_FAULT, 2000 + b, (uint32_t)seq[k]);
       continue;
     }
     const float inv = sm.inv_rms[b];
     const float y = sm.out[o] * inv, yp = sm.out[o ^ 1] * inv;  // o ^ 1: the pair partner column
-    const int pos = seq - 1;
+    const int pos = seq[k] - 1;
     const int n = (p0 + pp) * 16 + nn;
     const bool odd = n & 1;
-    const int page = P.bt[b * P.mpps + pos / PS];
-    const bool page_ok = page >= 0 && page < P.n_pages;
+    const bool page_ok = page[k] >= 0 && page[k] < P.n_pages;
     if (n < qd + kvd) {
       const int d = (n < qd ? n : n - qd) % D;
-      const float c = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 0];
-      const float s = P.rope[((size_t)pos * (D / 2) + d / 2) * 2 + 1];
+      const float c = rc[k], sn = rs[k];
       // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
       const float x0 = odd ? yp : y, x1 = odd ? y : yp;
-      const float r = odd ? (x0 * s + x1 * c) : (x0 * c - x1 * s);
+      const float r = odd ? (x0 * sn + x1 * c) : (x0 * c - x1 * sn);
       if (n < qd) {
         Q.stf(b * qd + n, r);
       } else if (page_ok) {
         const int g = (n - qd) / D;
-        KV.st16(((page * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d, (uint16_t)f2bf(r));
+        KV.st16(((page[k] * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d, (uint16_t)f2bf(r));
       }
     } else if (page_ok) {
       const int nn2 = n - qd - kvd;
       const int g = nn2 / D, d = nn2 % D;
-      KV.st16(((page * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS), (uint16_t)f2bf(y));
+      KV.st16(((page[k] * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS), (uint16_t)f2bf(y));
     }
-    if (!page_ok) raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page);
+    if (!page_ok) raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page[k]);
   }
   arrive_nr(P, t.sig_ctr[0]);
 }
@@ -1828,7 +1856,10 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
   const int kc = P.H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
   const Pub GU(P.gu);
-  if (!wait_one(P, t.wait_ctr[0], t.wait_tgt[0], sm)) return;
+  // the layer input and the router's partial logits complete (one wait): the
+  // input's operand loads, then this claimer's own top-k and route, whose
+  // loads share their round trip
+  if (!wait_task(P, t, sm)) return;
   set_rows_batch(P, sm, 0, P.H, 0);
   __syncthreads();
   ATile<1, NCH> Ah0, Al0, Ah1, Al1;
@@ -1836,8 +1867,6 @@ __device__ __forceinline__ void op_moe_static(const mk_params& P, const mk_task&
   atile_load_bf16(Al0, Pub(u_of(P, l, 1)), sm.row_off[0], 0, kh_chunks);
   atile_load_bf16(Ah1, Pub(u_of(P, l, 0)), sm.row_off[0], kh_chunks, kc);
   atile_load_bf16(Al1, Pub(u_of(P, l, 1)), sm.row_off[0], kh_chunks, kc);
-  // the router's partial logits complete: this claimer's own top-k and route
-  if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
   mark(sm, 0);
   route_build(P, l, sm, false);
   mark(sm, 1);
@@ -2074,7 +2103,11 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   // current slice's weighted hidden values [MK_FUSED_B][16] (float)
   uint16_t* xs = sm.act;
   float* actf = reinterpret_cast<float*>(sm.act + 2 * MK_FUSED_B * MK_MAX_H);
-  if (!wait_one(P, t.wait_ctr[0], t.wait_tgt[0], sm)) return;
+  // the layer input and the router's partial logits complete (one wait):
+  // the input's loads, then this claimer's own top-k and route (whose loads
+  // share the input's round trip), then the input into LDS
+  if (!wait_task(P, t, sm)) return;
+  mark(sm, 0);
   {
     const Pub Uh(u_of(P, l, 0)), Ul(u_of(P, l, 1));
     const int n8 = B * H / 8;  // 8 bf16 per thread and load
@@ -2085,6 +2118,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
       vh[k] = i < n8 ? Uh.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
       vl[k] = i < n8 ? Ul.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
     }
+    route_build(P, l, sm, false);
 #pragma unroll
     for (int k = 0; k < MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS; ++k) {
       const int i = tid() + k * MK_WG_THREADS;
@@ -2093,13 +2127,10 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
         *(u32x4_t*)(xs + MK_FUSED_B * MK_MAX_H + 8 * i) = vl[k];
       }
     }
+    lds_sync();
   }
   const uint16_t* xh = xs;
   const uint16_t* xl = xs + MK_FUSED_B * MK_MAX_H;
-  // the router's partial logits complete: this claimer's own top-k and route
-  if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
-  mark(sm, 0);
-  route_build(P, l, sm, false);
   mark(sm, 1);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) * S;
   int lo, hi;

@@ -96,8 +96,16 @@ void add_wait(mk_task& t, int c, int tgt) {
 
 }  // namespace
 
+// Offsets (bytes) of the per-step scratch buffers inside one block, the same
+// for the handle's allocation and for the static array of the allocation-free
+// step; `ctr` (one counter set) and `total` count only in the static array.
+struct ScratchLayout {
+  size_t h, ssq, u, q, o, part, ao, rp, tki, tkw, route, gu, dn, mp, lmv, lma, err, ctr, total;
+};
+
 struct mk_handle {
   mk_config cfg{};
+  ScratchLayout lay{};
   int wave_order = MK_ORDER_SHIPPED;
   int placement = MK_PLACE_TUNED;
   int device = 0;
@@ -228,7 +236,10 @@ int window_of(const mk_config& c, int l) {
 
 // Pages per attention split for a batch of B sequences up to `len` long:
 // about two tasks per workgroup over a layer's (sequence, group) pairs, at
-// least 16 pages each.
+// least 16 pages each. (Finer splits above MK_FUSED_B tokens, sized per layer
+// kind, and claims of several items at a time were measured slower at batch
+// 32 over ragged contexts: the expert phase that follows on every unit then
+// loses more than the attention gains.)
 int pps_for(const mk_handle* h, int B, int len) {
   const int pages = ceil_div(len, h->cfg.page_size) + 1;
   const int target = std::max(1, 2 * h->n_workers / (B * h->cfg.n_kv_heads));
@@ -261,20 +272,20 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   auto S = std::make_unique<Schedule>();
   S->B = B;
   S->bucket = std::min(bucket_of(hint), c.max_seq_len);
-  S->pps = pps_for(h, B, S->bucket);
+  S->pps_full = pps_for(h, B, S->bucket);
+  S->pps = S->pps_full;
   // Fused MoE with a window pattern: full-attention layers get as many splits
   // as the window layers (longer ones), so the same number of compute units
   // holds attention work and the rest share the experts (fewer attention
   // claimers leave more units, and each fewer expert slices, on the chain
   // that sets the layer's time).
-  S->pps_full = S->pps;
   if (B <= MK_FUSED_B && h->n_workers <= MK_WG_THREADS && c.window > 0) {
     int lw = 0;
     while (lw < c.n_layers && !window_of(c, lw)) ++lw;
     if (lw < c.n_layers) {
       const int ns_win = splits_for(h, lw, S->bucket, S->pps);
       const int pages = ceil_div(S->bucket, c.page_size) + 1;
-      S->pps_full = std::max(S->pps, ceil_div(pages, std::max(ns_win, 1)));
+      S->pps_full = std::max(S->pps_full, ceil_div(pages, std::max(ns_win, 1)));
     }
   }
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;
@@ -665,6 +676,7 @@ void fixed_shares(int k, int nf, int nt, int wa, int n_items, int n_down, int& l
 struct SimCU {
   bool in_claimer = false;
   int pending_item = -1;  // claimed item waiting for its dependency
+  int chunk_end = 0;      // attention: end of the current claim
   int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items, 2 fixed-share down pairs
   int item_end = 0;       // fixed shares: end of this claimer's down items (pending_item: the next)
   int pos = 0;
@@ -789,6 +801,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
             done();
           } else {
             u.pending_item = id;
+            u.chunk_end = id + 1;
           }
         } else {
           const int bg = u.pending_item / ns, g = bg % KVH;
@@ -797,7 +810,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
               ctr[t.a[5] + g]++;
             else if (++ctr[t.a[5] + bg] == ns)
               ctr[t.sig_ctr[0] + g]++;
-            u.pending_item = -1;
+            if (++u.pending_item >= u.chunk_end) u.pending_item = -1;
             progress = true;
           }
         }
@@ -1031,40 +1044,50 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     so += align_up(bytes, 256);
     return o;
   };
-  const size_t s_h = stake((size_t)Bm * H * 4), s_ssq = stake((size_t)2 * Bm * h->NB * 4);
-  const size_t s_u = stake((size_t)4 * Bm * H * 2);
-  const size_t s_q = stake((size_t)Bm * h->q_dim * 4), s_o = stake((size_t)Bm * h->q_dim * 4);
-  const size_t s_part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
+  ScratchLayout& y = h->lay;
+  y.h = stake((size_t)Bm * H * 4);
+  y.ssq = stake((size_t)2 * Bm * h->NB * 4);
+  y.u = stake((size_t)4 * Bm * H * 2);
+  y.q = stake((size_t)Bm * h->q_dim * 4);
+  y.o = stake((size_t)Bm * h->q_dim * 4);
+  y.part = stake((size_t)Bm * KVH * h->max_splits * (G * D + 2 * G) * 4);
   // routing scratch: one region per layer
-  const size_t s_ao = stake((size_t)KVH * Bm * H * 4), s_rp = stake((size_t)L * h->router_ks * Bm * E * 4);
-  const size_t s_tki = stake((size_t)L * Bm * K * 4), s_tkw = stake((size_t)L * Bm * K * 4);
-  const size_t s_route = stake((size_t)L * MK_ROUTE_INTS(E, Bm) * 4);
-  const size_t s_gu = stake((size_t)Bm * K * 4 * F * 4), s_dn = stake((size_t)Bm * K * H * 4);
-  const size_t s_mp = stake((size_t)std::max(h->n_workers, 1) * MK_FUSED_B * H * 4);
-  const size_t s_lmv = stake((size_t)Bm * h->n_lm_tasks * 4), s_lma = stake((size_t)Bm * h->n_lm_tasks * 4);
-  const size_t s_err = stake(16);
-  if (hipMalloc(&h->scratch, so) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "scratch");
-  hipMemset(h->scratch, 0, so);
-  char* sb = (char*)h->scratch;
-  h->h = (float*)(sb + s_h);
-  h->u = (uint16_t*)(sb + s_u);
-  h->ssq = (float*)(sb + s_ssq);
-  h->q = (float*)(sb + s_q);
-  h->o = (uint16_t*)(sb + s_o);
-  h->part = (float*)(sb + s_part);
-  h->ao = (float*)(sb + s_ao);
-  h->rp = (float*)(sb + s_rp);
-  h->tk_idx = (int32_t*)(sb + s_tki);
-  h->tk_w = (float*)(sb + s_tkw);
-  h->route = (int32_t*)(sb + s_route);
-  h->gu = (float*)(sb + s_gu);
-  h->dn = (float*)(sb + s_dn);
-  h->mp = (float*)(sb + s_mp);
-  h->lm_val = (float*)(sb + s_lmv);
-  h->lm_arg = (int32_t*)(sb + s_lma);
-  h->err_word = (uint32_t*)(sb + s_err);
+  y.ao = stake((size_t)KVH * Bm * H * 4);
+  y.rp = stake((size_t)L * h->router_ks * Bm * E * 4);
+  y.tki = stake((size_t)L * Bm * K * 4);
+  y.tkw = stake((size_t)L * Bm * K * 4);
+  y.route = stake((size_t)L * MK_ROUTE_INTS(E, Bm) * 4);
+  y.gu = stake((size_t)Bm * K * 4 * F * 4);
+  y.dn = stake((size_t)Bm * K * H * 4);
+  y.mp = stake((size_t)std::max(h->n_workers, 1) * MK_FUSED_B * H * 4);
+  y.lmv = stake((size_t)Bm * h->n_lm_tasks * 4);
+  y.lma = stake((size_t)Bm * h->n_lm_tasks * 4);
+  y.err = stake(16);
+  const size_t scratch_bytes = so;
   // counters: capacity for the largest batch
   h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 5 + E + h->NB + 1);
+  y.ctr = stake((size_t)h->n_ctr_cap * 4);
+  y.total = so;
+  if (hipMalloc(&h->scratch, scratch_bytes) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "scratch");
+  hipMemset(h->scratch, 0, scratch_bytes);
+  char* sb = (char*)h->scratch;
+  h->h = (float*)(sb + y.h);
+  h->u = (uint16_t*)(sb + y.u);
+  h->ssq = (float*)(sb + y.ssq);
+  h->q = (float*)(sb + y.q);
+  h->o = (uint16_t*)(sb + y.o);
+  h->part = (float*)(sb + y.part);
+  h->ao = (float*)(sb + y.ao);
+  h->rp = (float*)(sb + y.rp);
+  h->tk_idx = (int32_t*)(sb + y.tki);
+  h->tk_w = (float*)(sb + y.tkw);
+  h->route = (int32_t*)(sb + y.route);
+  h->gu = (float*)(sb + y.gu);
+  h->dn = (float*)(sb + y.dn);
+  h->mp = (float*)(sb + y.mp);
+  h->lm_val = (float*)(sb + y.lmv);
+  h->lm_arg = (int32_t*)(sb + y.lma);
+  h->err_word = (uint32_t*)(sb + y.err);
   for (int i = 0; i < 2; ++i) {
     if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
     hipMemset(h->ctr[i], 0, (size_t)h->n_ctr_cap * 4);
@@ -1160,6 +1183,28 @@ mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
   return MK_OK;
 }
 
+// The per-step scratch pointers of P inside a block laid out as h->lay.
+static void scratch_at(const mk_handle* h, char* base, mk_params& P) {
+  const ScratchLayout& y = h->lay;
+  P.h = (float*)(base + y.h);
+  P.u = (uint16_t*)(base + y.u);
+  P.ssq = (float*)(base + y.ssq);
+  P.q = (float*)(base + y.q);
+  P.o = (uint16_t*)(base + y.o);
+  P.part = (float*)(base + y.part);
+  P.ao = (float*)(base + y.ao);
+  P.rp = (float*)(base + y.rp);
+  P.tk_idx = (int32_t*)(base + y.tki);
+  P.tk_w = (float*)(base + y.tkw);
+  P.route = (int32_t*)(base + y.route);
+  P.gu = (float*)(base + y.gu);
+  P.dn = (float*)(base + y.dn);
+  P.mp = (float*)(base + y.mp);
+  P.lm_val = (float*)(base + y.lmv);
+  P.lm_arg = (int32_t*)(base + y.lma);
+  P.err = (uint32_t*)(base + y.err);
+}
+
 static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const int32_t* bt, int32_t* seq_lens,
                         float* logits, int32_t* next_tokens, uint32_t flags, mk_params& P) {
   const mk_config& c = h->cfg;
@@ -1216,31 +1261,17 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.logits = logits;
   P.next_tokens = next_tokens;
   P.flags = flags;
-  P.h = h->h;
-  P.u = h->u;
-  P.ssq = h->ssq;
-  P.q = h->q;
-  P.part = h->part;
-  P.o = h->o;
-  P.ao = h->ao;
-  P.rp = h->rp;
-  P.tk_idx = h->tk_idx;
-  P.tk_w = h->tk_w;
+  scratch_at(h, (char*)h->scratch, P);
   P.tk_trace = h->tk_trace;
   P.trace = h->task_trace;
-  P.route = h->route;
-  P.gu = h->gu;
-  P.dn = h->dn;
-  P.mp = h->mp;
-  P.lm_val = h->lm_val;
-  P.lm_arg = h->lm_arg;
   P.n_ctr = h->n_ctr_cap;  // clear the whole capacity: schedules differ in size
-  P.err = h->err_word;
   P.timeout_ticks = h->timeout_ticks;
 }
 
-mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables, int32_t* seq_lens,
-                         int max_seq_len_hint, float* logits, int32_t* next_tokens, uint32_t flags, void* stream) {
+// One decode step.
+static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
+                             int32_t* seq_lens, int max_seq_len_hint, float* logits, int32_t* next_tokens,
+                             uint32_t flags, void* stream) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
   const mk_config& c = h->cfg;
@@ -1256,8 +1287,10 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
   for (int l = 0; l < c.n_layers; ++l)
     if (!h->layer_loaded[l]) return fail(h, MK_ERR_STATE, "layer %d not loaded", l);
   Schedule* S = nullptr;
-  mk_status st = get_schedule(h, batch, max_seq_len_hint, &S);
-  if (st != MK_OK) return st;
+  {
+    mk_status st = get_schedule(h, batch, max_seq_len_hint, &S);
+    if (st != MK_OK) return st;
+  }
   if (h->task_trace && S->cu_tasks.size() > h->task_trace_cap)
     return fail(h, MK_ERR_INVALID_ARG, "task trace holds %zu records, the schedule has %zu tasks", h->task_trace_cap,
                 S->cu_tasks.size());
@@ -1267,9 +1300,12 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
   fill_params(h, S, batch, tokens, block_tables, seq_lens, logits, next_tokens, flags, P);
   // the lengths limit on the device is the hint (the schedule's splits cover it)
   P.max_seq = max_seq_len_hint;
-  const int cur = (int)(h->steps & 1), nxt = cur ^ 1;
-  P.ctr = h->ctr[cur];
-  P.ctr_clear = h->ctr[nxt];
+  uint32_t* clear_next = nullptr;
+  {
+    const int cur = (int)(h->steps & 1), nxt = cur ^ 1;
+    P.ctr = h->ctr[cur];
+    P.ctr_clear = clear_next = h->ctr[nxt];
+  }
   if (c.mode == MK_MODE_MEGAKERNEL) {
     P.tasks = S->d_cu_tasks;
     P.task_off = S->d_cu_off;
@@ -1283,12 +1319,17 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
       if (n == 0) continue;
       P.tasks = S->d_flat + b0;
       P.trace_base = b0;
-      P.ctr_clear = (w == 0) ? h->ctr[nxt] : nullptr;
+      P.ctr_clear = (w == 0) ? clear_next : nullptr;
       HIPCHECK(h, mk_launch_interp(P, c.head_dim, n, false, s));
     }
   }
   h->steps++;
   return MK_OK;
+}
+
+mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables, int32_t* seq_lens,
+                         int max_seq_len_hint, float* logits, int32_t* next_tokens, uint32_t flags, void* stream) {
+  return decode_step(h, batch, tokens, block_tables, seq_lens, max_seq_len_hint, logits, next_tokens, flags, stream);
 }
 
 mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records) {  // records of 8 words
