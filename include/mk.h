@@ -166,6 +166,27 @@ mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t
                          int32_t* seq_lens, int max_seq_len_hint, float* logits,
                          int32_t* next_tokens, uint32_t flags, void* stream);
 
+/* mk_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, semantics and kernels; the step's scratch (activations,
+ * partial results, routing, counters, error word) lives in a static device
+ * array of MK_STATIC_SCRATCH_BYTES (64 MiB) that each device the library runs
+ * on holds until the process ends, instead of the handle's buffers. It calls
+ * no allocating routine: a fill kernel zeroes the counters, then the step
+ * launches.
+ *   - The schedule for (batch, context bucket of max_seq_len_hint) must
+ *     already be cached on the handle (built by an earlier mk_decode_step or
+ *     mk_schedule_info_get with those sizes): otherwise MK_ERR_STATE.
+ *   - A model and max_batch whose step scratch exceeds the array:
+ *     MK_ERR_UNSUPPORTED (the full-size model fits up to batch 32 at 16K).
+ *   - Every call on one device shares that device's array and keeps the last
+ *     call's contents: calls that overlap on one device (other streams, other
+ *     handles, other threads) race and must be serialised by the caller.
+ *   - mk_sync_status reports device errors of these steps too. */
+mk_status mk_decode_step_noalloc(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
+                                 int32_t* seq_lens, int max_seq_len_hint, float* logits,
+                                 int32_t* next_tokens, uint32_t flags, void* stream);
+
 /* Switch between the persistent megakernel and the kernel-per-op variant
  * (the same op bodies launched once per wave of same-type tasks, with the
  * stream order in place of the counter waits: the separate-kernels baseline

@@ -26,7 +26,7 @@ STEP_ADVANCE = 1
 # every function include/mk.h declares
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
-           "mk_set_schedule_options",
+           "mk_set_schedule_options", "mk_decode_step_noalloc",
            "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
@@ -63,6 +63,7 @@ def _load():
     lib.mk_load_globals.argtypes = [H, P, P, P, P]
     lib.mk_load_weights.argtypes = [H, P, P]
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
+    lib.mk_decode_step_noalloc.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
     lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
     lib.mk_set_schedule_options.argtypes = [H, I, I]
@@ -169,6 +170,14 @@ class Decoder:
         self._check(lib.mk_decode_step(self._h, tokens.shape[0], _ptr(tokens), _ptr(block_tables),
                                        _ptr(seq_lens), int(max_seq_len_hint), _ptr(logits), _ptr(next_tokens),
                                        STEP_ADVANCE if advance else 0, _stream_ptr(stream)))
+
+    def step_noalloc(self, tokens, block_tables, seq_lens, max_seq_len_hint: int, logits, next_tokens=None,
+                     advance: bool = False, stream=None):
+        """The allocation-free step (static scratch; the schedule must be cached)."""
+        self._check(lib.mk_decode_step_noalloc(self._h, tokens.shape[0], _ptr(tokens), _ptr(block_tables),
+                                               _ptr(seq_lens), int(max_seq_len_hint), _ptr(logits),
+                                               _ptr(next_tokens), STEP_ADVANCE if advance else 0,
+                                               _stream_ptr(stream)))
 
     def set_mode(self, mode: int):
         self._check(lib.mk_set_mode(self._h, mode))

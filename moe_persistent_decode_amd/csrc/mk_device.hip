@@ -2638,8 +2638,51 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_panels(const uint16_
   }
 }
 
+// ----------------------------------------------- static scratch (no allocation)
+// The per-step scratch of mk_decode_step_noalloc: activations, partials,
+// routing, counters and the error word of one step, in one file-scope device
+// array (each device the library runs on holds its own copy until the
+// process ends). In host code `scratch` names a host-side stand-in, never the
+// device memory: host code uses only the address hipGetSymbolAddress gives
+// for the current device (mk_static_scratch).
+static __device__ __align__(256) unsigned char scratch[MK_STATIC_SCRATCH_BYTES];
+
+// Zero n words (the counters of a step that must start at zero): a kernel, not
+// a memset, so a caller may capture it in a graph.
+extern "C" __global__ __launch_bounds__(256) void mk_zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
 // ------------------------------------------------------------ host launch
+#include <mutex>
+
 #include "mk_launch.h"
+
+hipError_t mk_static_scratch(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[MK_MAX_DEVICES] = {};
+  if (device < 0 || device >= MK_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != device) hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
+
+hipError_t mk_launch_zero(uint32_t* p, int n, hipStream_t stream) {
+  const int grid = n <= 0 ? 1 : (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+  hipLaunchKernelGGL(mk_zero_words, dim3(grid), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 static const void* interp_fn(int head_dim, int mt) {
   if (head_dim == 64) return mt == 1 ? (const void*)mk_interp<64, 1> : (const void*)mk_interp<64, 2>;

@@ -106,6 +106,8 @@ struct ScratchLayout {
 struct mk_handle {
   mk_config cfg{};
   ScratchLayout lay{};
+  void* static_scratch = nullptr;  // this device's static scratch array (device address)
+  bool static_used = false;        // an allocation-free step ran (its error word is checked too)
   int wave_order = MK_ORDER_SHIPPED;
   int placement = MK_PLACE_TUNED;
   int device = 0;
@@ -1092,6 +1094,10 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
     hipMemset(h->ctr[i], 0, (size_t)h->n_ctr_cap * 4);
   }
+  // this device's static scratch array (the allocation-free step's), looked up
+  // once per device with the device current
+  if (mk_static_scratch(device, &h->static_scratch) != hipSuccess)
+    return fail(nullptr, MK_ERR_HIP, "cannot look up the static scratch array on device %d", device);
   if (hipDeviceSynchronize() != hipSuccess) return fail(nullptr, MK_ERR_HIP, "create sync");
   *out = h.release();
   return MK_OK;
@@ -1268,10 +1274,11 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.timeout_ticks = h->timeout_ticks;
 }
 
-// One decode step.
+// One decode step; `noalloc`: the allocation-free variant (static scratch,
+// counters zeroed by a fill kernel, only cached schedules).
 static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
                              int32_t* seq_lens, int max_seq_len_hint, float* logits, int32_t* next_tokens,
-                             uint32_t flags, void* stream) {
+                             uint32_t flags, void* stream, bool noalloc) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
   const mk_config& c = h->cfg;
@@ -1287,7 +1294,21 @@ static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int
   for (int l = 0; l < c.n_layers; ++l)
     if (!h->layer_loaded[l]) return fail(h, MK_ERR_STATE, "layer %d not loaded", l);
   Schedule* S = nullptr;
-  {
+  if (noalloc) {
+    if (h->lay.total > MK_STATIC_SCRATCH_BYTES)
+      return fail(h, MK_ERR_UNSUPPORTED,
+                  "this model and batch need %zu bytes of step scratch; the static array holds %u",
+                  h->lay.total, (unsigned)MK_STATIC_SCRATCH_BYTES);
+    if (!h->static_scratch) return fail(h, MK_ERR_STATE, "no static scratch on this device");
+    const int bucket = std::min(bucket_of(max_seq_len_hint), c.max_seq_len);
+    auto it = h->scheds.find(std::make_pair(batch, bucket));
+    if (it == h->scheds.end())
+      return fail(h, MK_ERR_STATE,
+                  "no schedule for batch %d, context bucket %d yet (building one allocates): run "
+                  "mk_decode_step or mk_schedule_info_get once with these sizes first",
+                  batch, bucket);
+    S = it->second.get();
+  } else {
     mk_status st = get_schedule(h, batch, max_seq_len_hint, &S);
     if (st != MK_OK) return st;
   }
@@ -1301,7 +1322,16 @@ static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int
   // the lengths limit on the device is the hint (the schedule's splits cover it)
   P.max_seq = max_seq_len_hint;
   uint32_t* clear_next = nullptr;
-  {
+  if (noalloc) {
+    // the static array keeps the last call's contents: only the counters must
+    // start at zero (every other buffer is written before it is read)
+    char* base = (char*)h->static_scratch;
+    scratch_at(h, base, P);
+    P.ctr = (uint32_t*)(base + h->lay.ctr);
+    P.ctr_clear = nullptr;
+    HIPCHECK(h, mk_launch_zero(P.ctr, h->n_ctr_cap, s));
+    h->static_used = true;
+  } else {
     const int cur = (int)(h->steps & 1), nxt = cur ^ 1;
     P.ctr = h->ctr[cur];
     P.ctr_clear = clear_next = h->ctr[nxt];
@@ -1323,13 +1353,21 @@ static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int
       HIPCHECK(h, mk_launch_interp(P, c.head_dim, n, false, s));
     }
   }
-  h->steps++;
+  if (!noalloc) h->steps++;
   return MK_OK;
 }
 
 mk_status mk_decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables, int32_t* seq_lens,
                          int max_seq_len_hint, float* logits, int32_t* next_tokens, uint32_t flags, void* stream) {
-  return decode_step(h, batch, tokens, block_tables, seq_lens, max_seq_len_hint, logits, next_tokens, flags, stream);
+  return decode_step(h, batch, tokens, block_tables, seq_lens, max_seq_len_hint, logits, next_tokens, flags, stream,
+                     false);
+}
+
+mk_status mk_decode_step_noalloc(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
+                                 int32_t* seq_lens, int max_seq_len_hint, float* logits, int32_t* next_tokens,
+                                 uint32_t flags, void* stream) {
+  return decode_step(h, batch, tokens, block_tables, seq_lens, max_seq_len_hint, logits, next_tokens, flags, stream,
+                     true);
 }
 
 mk_status mk_set_task_trace(mk_handle* h, uint32_t* trace, size_t n_records) {  // records of 8 words
@@ -1393,6 +1431,12 @@ mk_status mk_sync_status(mk_handle* h, void* stream) {
   HIPCHECK(h, hipStreamSynchronize((hipStream_t)stream));
   uint32_t e[4];
   HIPCHECK(h, hipMemcpy(e, h->err_word, sizeof(e), hipMemcpyDeviceToHost));
+  if (e[0] == 0 && h->static_used) {
+    // the allocation-free step's error word (in this device's static array)
+    uint32_t* se = (uint32_t*)((char*)h->static_scratch + h->lay.err);
+    HIPCHECK(h, hipMemcpy(e, se, sizeof(e), hipMemcpyDeviceToHost));
+    if (e[0] != 0) HIPCHECK(h, hipMemset(se, 0, sizeof(e)));
+  }
   if (e[0] == 0) return MK_OK;
   HIPCHECK(h, hipMemset(h->err_word, 0, sizeof(e)));
   // a failed step leaves counters mid-way: clear both sets

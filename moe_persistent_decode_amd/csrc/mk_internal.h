@@ -32,6 +32,11 @@
 // and stores one partial output row per token it saw; residual tasks sum them.
 #define MK_FUSED_B 4
 #define MK_TASK_INTS 32
+// Static scratch of the allocation-free step: its size bounds the per-step
+// scratch (and counters) of the models it accepts; the full-size model needs
+// about 55 MB at batch 32 with 16K contexts.
+#define MK_STATIC_SCRATCH_BYTES (64u << 20)
+#define MK_MAX_DEVICES 64
 
 // Opcodes. The post names sixteen opcodes for its model family; this model
 // (no dense FFN) uses the ones below. MOE_GATHER is folded into the expert

@@ -8,3 +8,7 @@ hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool coo
 hipError_t mk_launch_repack(const uint16_t* src, uint16_t* dst, int K, int N, int ld, int dst0, int dstep,
                             int nz, size_t src_zstride, size_t dst_zstride, hipStream_t stream);
 hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu);
+// Device address of the static scratch array on `device` (looked up once per
+// device, then cached), and a fill kernel zeroing n words.
+hipError_t mk_static_scratch(int device, void** ptr);
+hipError_t mk_launch_zero(uint32_t* p, int n, hipStream_t stream);
