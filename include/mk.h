@@ -299,6 +299,76 @@ mk_status mk_schedule_simulate(mk_handle* h, int batch, int max_seq_len_hint,
  * only; mk_load_*, mk_decode_step return MK_ERR_STATE). */
 mk_status mk_create_host_only(const mk_config* cfg, int n_cus, mk_handle** out);
 
+/* ---- decode service (megakernel post, Chinese version, section on the
+ * inference engine around the kernel: a native thread only decodes, step
+ * after step - update the page tables, select the schedule for the longest
+ * live context, launch, sample and stream, retire finished requests - while
+ * a control-plane thread pauses it to prefill, admit or evict and resumes
+ * it; the batch state belongs to the control plane only while the decoder is
+ * parked) ------------------------------------------------------------------ */
+
+/* Called from the service thread for every token: status 0 more follow, 1
+ * the request finished (max_new_tokens reached or the stop token), -1 the
+ * service failed (token is -1; see mk_service_last_error). It runs while the
+ * service holds its lock: it must not call mk_service_* functions. */
+typedef void (*mk_token_fn)(void* user, int64_t request_id, int32_t token, int32_t status);
+
+typedef struct {
+  int32_t max_batch;   /* sequences decoded together, <= the handle's max_batch */
+  int32_t page0;       /* the service owns KV pages [page0, page0 + n_pages) of the pool */
+  int32_t n_pages;
+  mk_token_fn on_token;
+  void* user;
+  void* stream;        /* hipStream_t of the steps; NULL: a stream of the service's own */
+} mk_service_config;
+
+typedef struct {
+  int64_t steps;       /* decode steps run */
+  int64_t tokens;      /* tokens streamed */
+  int32_t active;      /* requests in the batch */
+  int32_t free_pages;  /* pages in the service's free list */
+  int32_t parked;      /* 1 while the decoder is parked */
+  int32_t status;      /* MK_OK, or the error that stopped the service */
+} mk_service_info;
+
+typedef struct mk_service mk_service;
+
+/* Start a service thread over handle h (loaded weights, a KV pool; the
+ * handle must outlive the service and no one else may step it meanwhile).
+ * It starts paused (parked): admit requests, then mk_service_resume. Errors: MK_ERR_INVALID_ARG (config against the
+ * handle), MK_ERR_STATE (host-only handle), MK_ERR_OOM. */
+mk_status mk_service_create(mk_handle* h, const mk_service_config* cfg, mk_service** out);
+
+/* Ask the decoder to park after its current step and wait until it has: the
+ * GPU is idle and the service reads no batch state until mk_service_resume. */
+mk_status mk_service_pause(mk_service* s);
+mk_status mk_service_resume(mk_service* s);
+
+/* While paused: take n pages from the service's free list (for a request's
+ * context, written into the pool through mk_kv_cache, e.g. by a prefill). */
+mk_status mk_service_alloc_pages(mk_service* s, int32_t n, int32_t* pages);
+
+/* While paused: admit a request whose context (positions < context_len) is in
+ * the KV pool on `pages` (page i holds positions [16 i, 16 i + 16), at least
+ * ceil(context_len / 16) of them, from mk_service_alloc_pages). It decodes
+ * first_token at position context_len, then greedily, streaming every token
+ * through on_token until max_new_tokens or stop_token (-1: none). The
+ * service owns the pages from now on and returns them to its free list when
+ * the request finishes or is evicted. MK_ERR_UNSUPPORTED when the batch is
+ * full, MK_ERR_STATE when not paused. */
+mk_status mk_service_admit(mk_service* s, int64_t request_id, int32_t first_token, int32_t context_len,
+                           const int32_t* pages, int32_t n_pages, int32_t max_new_tokens, int32_t stop_token);
+
+/* While paused: drop a request (no more tokens; its pages return). */
+mk_status mk_service_evict(mk_service* s, int64_t request_id);
+
+mk_status mk_service_stats(mk_service* s, mk_service_info* out);
+const char* mk_service_last_error(const mk_service* s);
+
+/* Stop the thread after its current step and free the service (requests
+ * still active get no further tokens). */
+void mk_service_destroy(mk_service* s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,9 @@ STEP_ADVANCE = 1
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
            "mk_set_schedule_options", "mk_decode_step_noalloc",
+           "mk_service_create", "mk_service_pause", "mk_service_resume", "mk_service_alloc_pages",
+           "mk_service_admit", "mk_service_evict", "mk_service_stats", "mk_service_last_error",
+           "mk_service_destroy",
            "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
@@ -43,6 +46,19 @@ class MkConfig(ctypes.Structure):
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("page_size", "window", "full_every", "max_batch", "max_seq_len",
                                       "max_pages_per_seq", "n_pages", "mode")]
+
+
+TOKEN_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32)
+
+
+class MkServiceConfig(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("page0", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+                ("on_token", TOKEN_FN), ("user", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+
+
+class MkServiceInfo(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("tokens", ctypes.c_int64), ("active", ctypes.c_int32),
+                ("free_pages", ctypes.c_int32), ("parked", ctypes.c_int32), ("status", ctypes.c_int32)]
 
 
 class MkScheduleInfo(ctypes.Structure):
@@ -79,8 +95,20 @@ def _load():
     lib.mk_schedule_info_get.argtypes = [H, I, I, ctypes.POINTER(MkScheduleInfo)]
     lib.mk_schedule_export.argtypes = [H, I, I, P, P]
     lib.mk_schedule_simulate.argtypes = [H, I, I, P, U64, ctypes.c_int32, ctypes.c_char_p, S]
+    lib.mk_service_create.argtypes = [H, ctypes.POINTER(MkServiceConfig), ctypes.POINTER(H)]
+    lib.mk_service_pause.argtypes = [H]
+    lib.mk_service_resume.argtypes = [H]
+    lib.mk_service_alloc_pages.argtypes = [H, ctypes.c_int32, P]
+    lib.mk_service_admit.argtypes = [H, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32]
+    lib.mk_service_evict.argtypes = [H, ctypes.c_int64]
+    lib.mk_service_stats.argtypes = [H, ctypes.POINTER(MkServiceInfo)]
+    lib.mk_service_last_error.argtypes = [H]
+    lib.mk_service_last_error.restype = ctypes.c_char_p
+    lib.mk_service_destroy.argtypes = [H]
+    lib.mk_service_destroy.restype = None
     for name in EXPORTS:
-        if name not in ("mk_last_error", "mk_destroy"):
+        if name not in ("mk_last_error", "mk_destroy", "mk_service_last_error", "mk_service_destroy"):
             getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -230,3 +258,83 @@ class Decoder:
         buf = ctypes.create_string_buffer(256)
         st = lib.mk_schedule_simulate(self._h, batch, hint, na.ctypes.data, seed, corrupt_task, buf, 256)
         return st, buf.value.decode()
+
+
+class DecodeService:
+    """The host decode service (mk_service_*): a native thread decoding the
+    admitted requests step after step on `decoder`, streaming greedy tokens.
+    Tokens arrive through a callback into `tokens` (request id -> list) and
+    `status` (request id -> 1 finished / -1 failed). It starts paused: admit
+    requests (with pages from alloc_pages), then resume."""
+
+    def __init__(self, decoder: Decoder, max_batch: int, page0: int, n_pages: int, stream=None):
+        import threading
+        self.decoder = decoder
+        self.tokens: Dict[int, list] = {}
+        self.status: Dict[int, int] = {}
+        self._lock = threading.Lock()
+        self._cb = TOKEN_FN(self._on_token)  # kept alive with the service
+        cfg = MkServiceConfig(max_batch=max_batch, page0=page0, n_pages=n_pages, on_token=self._cb, user=None,
+                              stream=_ptr_or_none(stream))
+        self._s = ctypes.c_void_p()
+        st = lib.mk_service_create(decoder._h, ctypes.byref(cfg), ctypes.byref(self._s))
+        if st != MK_OK:
+            raise MkError(st, "mk_service_create")
+
+    def _on_token(self, user, request_id, token, status):
+        with self._lock:
+            self.tokens.setdefault(int(request_id), []).append(int(token))
+            if status != 0:
+                self.status[int(request_id)] = int(status)
+
+    def _check(self, st: int):
+        if st != MK_OK:
+            raise MkError(st, lib.mk_service_last_error(self._s).decode())
+
+    def pause(self):
+        self._check(lib.mk_service_pause(self._s))
+
+    def resume(self):
+        self._check(lib.mk_service_resume(self._s))
+
+    def alloc_pages(self, n: int):
+        import numpy as np
+        a = np.zeros(max(n, 1), dtype=np.int32)
+        self._check(lib.mk_service_alloc_pages(self._s, n, a.ctypes.data))
+        return a[:n].tolist()
+
+    def admit(self, request_id: int, first_token: int, context_len: int, pages, max_new_tokens: int,
+              stop_token: int = -1):
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(pages, dtype=np.int32))
+        self._check(lib.mk_service_admit(self._s, request_id, first_token, context_len,
+                                         a.ctypes.data if a.size else None, a.size, max_new_tokens, stop_token))
+
+    def evict(self, request_id: int):
+        self._check(lib.mk_service_evict(self._s, request_id))
+
+    def stats(self) -> MkServiceInfo:
+        info = MkServiceInfo()
+        self._check(lib.mk_service_stats(self._s, ctypes.byref(info)))
+        return info
+
+    def snapshot(self):
+        with self._lock:
+            return {k: list(v) for k, v in self.tokens.items()}, dict(self.status)
+
+    def close(self):
+        if self._s:
+            lib.mk_service_destroy(self._s)
+            self._s = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr_or_none(stream):
+    if stream is None:
+        return None
+    return stream if isinstance(stream, int) else stream.cuda_stream

@@ -20,7 +20,7 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, "mk_device.hip"), os.path.join(CSRC, "mk_host.cpp")]
+    srcs = [os.path.join(CSRC, "mk_device.hip"), os.path.join(CSRC, "mk_host.cpp"), os.path.join(CSRC, "mk_service.cpp")]
     tmp = LIB + ".tmp"
     cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

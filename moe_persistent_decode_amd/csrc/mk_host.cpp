@@ -692,11 +692,32 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
   const int up_per_e = 2 * F / 16, down_per_e = NB;
   const int B = S.B;
   std::vector<mk_task> tasks = S.cu_tasks;
-  // make the first wait of the first task at or after `corrupt` that waits
-  // on something unsatisfiable by one arrival
+  // every counter's final value: the arrivals it must receive
+  std::vector<int64_t> want(S.n_ctr, 0);
+  for (int l = 0; l <= L; ++l) want[S.c_resid0 + l] = NB;
+  want[S.c_lm] = S.n_lm;
+  for (int l = 0; l < L; ++l) {
+    const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
+    int k = S.c_layer0 + l * S.c_per_layer;
+    const bool merged = S.moe_fused[l] > 0;  // the O projection tasks merge the splits
+    for (int g = 0; g < KVH; ++g) want[k++] = S.n_qkv[g];
+    for (int i = 0; i < B * KVH; ++i) want[k++] = merged ? (i < KVH ? (int64_t)B * ns : 0) : ns;
+    for (int g = 0; g < KVH; ++g) want[k++] = merged ? 0 : B;
+    want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
+    want[k++] = 1;                                                   // route finalized
+    want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
+    const bool fused = S.moe_fused[l] > 0, claiming = !S.moe_fixed[l] && !fused;
+    want[k++] = claiming ? (int64_t)n_active[l] * up_per_e + S.n_up_claimers : 0;
+    want[k++] = claiming ? (int64_t)n_active[l] * down_per_e + S.n_up_claimers : 0;
+    for (int a = 0; a < E; ++a) want[k++] = (!fused && a < n_active[l]) ? up_per_e : 0;
+    for (int cb = 0; cb < NB; ++cb) want[k++] = fused ? 0 : KVH + n_active[l];
+    want[k++] = fused ? S.moe_fused[l] + S.n_oproj : 0;  // fused MoE: claimers and O projections
+  }
+  // a lost signal: the first wait of the first task at or after `corrupt`
+  // waits for one arrival more than its counter ever receives
   for (int k = std::max(corrupt, 0); corrupt >= 0 && k < (int)tasks.size(); ++k)
     if (tasks[k].wait_ctr[0] >= 0) {
-      tasks[k].wait_tgt[0] += 1;
+      tasks[k].wait_tgt[0] = (int32_t)(want[tasks[k].wait_ctr[0]] + 1);
       break;
     }
   std::vector<int64_t> ctr(S.n_ctr, 0);
@@ -850,27 +871,6 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
       return MK_ERR_DEVICE_TIMEOUT;
     }
   }
-  // every counter against the arrivals it must receive
-  std::vector<int64_t> want(S.n_ctr, 0);
-  for (int l = 0; l <= L; ++l) want[S.c_resid0 + l] = NB;
-  want[S.c_lm] = S.n_lm;
-  for (int l = 0; l < L; ++l) {
-    const int ns = window_of(c, l) ? S.n_splits_win : S.n_splits_full;
-    int k = S.c_layer0 + l * S.c_per_layer;
-    const bool merged = S.moe_fused[l] > 0;  // the O projection tasks merge the splits
-    for (int g = 0; g < KVH; ++g) want[k++] = S.n_qkv[g];
-    for (int i = 0; i < B * KVH; ++i) want[k++] = merged ? (i < KVH ? (int64_t)B * ns : 0) : ns;
-    for (int g = 0; g < KVH; ++g) want[k++] = merged ? 0 : B;
-    want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
-    want[k++] = 1;                                                   // route finalized
-    want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
-    const bool fused = S.moe_fused[l] > 0, claiming = !S.moe_fixed[l] && !fused;
-    want[k++] = claiming ? (int64_t)n_active[l] * up_per_e + S.n_up_claimers : 0;
-    want[k++] = claiming ? (int64_t)n_active[l] * down_per_e + S.n_up_claimers : 0;
-    for (int a = 0; a < E; ++a) want[k++] = (!fused && a < n_active[l]) ? up_per_e : 0;
-    for (int cb = 0; cb < NB; ++cb) want[k++] = fused ? 0 : KVH + n_active[l];
-    want[k++] = fused ? S.moe_fused[l] + S.n_oproj : 0;  // fused MoE: claimers and O projections
-  }
   for (int i = 0; i < S.n_ctr; ++i)
     if (ctr[i] != want[i]) {
       char buf[256];
@@ -925,6 +925,15 @@ void free_schedule(Schedule* S) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
+
+bool mk_handle_dims(const mk_handle* h, int* max_batch, int* mpps, int* n_pages, int* vocab) {
+  if (!h || h->host_only) return false;
+  *max_batch = h->cfg.max_batch;
+  *mpps = h->cfg.max_pages_per_seq;
+  *n_pages = h->cfg.n_pages;
+  *vocab = h->cfg.vocab;
+  return true;
+}
 
 // =================================================================== C ABI
 

@@ -144,3 +144,8 @@ struct mk_params {
   int32_t trace_base;        // index of this launch's first task in the trace
   int64_t timeout_ticks;     // wait time limit in s_memrealtime ticks (100 MHz)
 };
+
+struct mk_handle;
+// The shape a decode service needs from a device handle: largest batch, page
+// table row stride, pages in the pool, vocabulary. False for a host-only handle.
+bool mk_handle_dims(const mk_handle* h, int* max_batch, int* mpps, int* n_pages, int* vocab);

@@ -255,3 +255,12 @@ def test_schedule_options_change_the_lists():
     with pytest.raises(mk.MkError):
         d.set_schedule_options(0, 3)
     d.close()
+
+
+def test_decode_service_needs_a_device_handle():
+    import moe_persistent_decode_amd as mk
+    d = _host(configs.TINY)
+    with pytest.raises(mk.MkError) as e:
+        mk.DecodeService(d, max_batch=1, page0=0, n_pages=8)
+    assert e.value.status == 7  # MK_ERR_STATE
+    d.close()
