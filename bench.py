@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="full48_b1_8k")
     ap.add_argument("--batch-workload", default="full48_b32_ragged",
                     help="second measured workload, reported under second_workload ('none' to skip)")
+    ap.add_argument("--long-workloads", default="full48_b1_256k,full48_b4_64k",
+                    help="comma-separated long-context workloads timed after the others ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ab", action="store_true", help="skip the kernel-per-op comparison")
     ap.add_argument("--op-trace", default=None, metavar="PATH",
@@ -101,10 +103,10 @@ class Run:
         self.done = 0  # steps decoded so far
         self.route = torch.full((steps, self.m.n_layers, self.B, self.m.top_k), -1, dtype=torch.int32, device=dev)
 
-    def run(self, n, record=False):
+    def run(self, n, record=False, slot=0):
         for i in range(n):
             if record:
-                self.dec.set_routing_trace(self.route[i])
+                self.dec.set_routing_trace(self.route[slot + i])
             self.dec.step(self.tokens, self.bt, self.seq_lens, self.hint + self.done, self.logits, advance=True,
                           stream=self.stream)
             self.done += 1
@@ -117,14 +119,17 @@ class Run:
         self.run(self.W)
         self.dec.sync(self.stream)
         first = self.done
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # an event after every step: the region's total and each step's time
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(self.K + 1)]
         torch.cuda.synchronize()
-        start.record(self.stream)
-        self.run(self.K, record)
-        end.record(self.stream)
+        ev[0].record(self.stream)
+        for i in range(self.K):
+            self.run(1, record, slot=i)
+            ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
         self.dec.sync(self.stream)
-        return start.elapsed_time(end), first
+        self.step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(self.K)]
+        return ev[0].elapsed_time(ev[self.K]), first
 
     def algorithmic_bytes(self, first):
         """Mean algorithmic bytes of the timed steps: each step's lengths and,
@@ -199,6 +204,36 @@ def op_trace(r, path, raw_path=None):
     log(f"[bench] per-opcode trace written to {path}")
 
 
+def library_sha16():
+    """Hash of the sources the decode step is built from (device code and the
+    host scheduler): counter figures hold only for the code they measured."""
+    import hashlib
+    hs = hashlib.sha256()
+    for f in ("mk_device.hip", "mk_host.cpp", "mk_internal.h", "mk_launch.h"):
+        hs.update(open(os.path.join(ROOT, "moe_persistent_decode_amd", "csrc", f), "rb").read())
+    return hs.hexdigest()[:16]
+
+
+def counted_traffic(path, workload):
+    """HBM bytes per launch of `workload` from the committed counter profile,
+    or None when there is none for the current sources."""
+    try:
+        e = json.load(open(path)).get(workload)
+        if e and e.get("library_sha256_16") == library_sha16():
+            return e.get("hbm_bytes_per_launch")
+    except (OSError, ValueError, AttributeError):
+        pass
+    return None
+
+
+def percentiles(xs):
+    """Median, 10th and 90th percentile of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
 def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None):
     import moe_persistent_decode_amd as mk
     r = Run(wl, steps, warmup, 2 if ab else 1)
@@ -207,13 +242,14 @@ def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None):
     bytes_avg, n_act = r.algorithmic_bytes(first)
     res = {"ms_per_step": step_ms, "tok_s": r.B * r.K / (ms / 1e3), "bytes": bytes_avg,
            "gbs": bytes_avg / (step_ms / 1e3) / 1e9, "experts_per_layer": n_act, "seq_len": r.hint,
-           "lens": (int(r.lens_host.min()), int(r.lens_host.max()), float(r.lens_host.mean()))}
+           "lens": (int(r.lens_host.min()), int(r.lens_host.max()), float(r.lens_host.mean())),
+           "step_ms": percentiles(r.step_ms)}
     log(f"[bench] {wl.name} megakernel: {step_ms:.3f} ms/step, {res['tok_s']:.1f} tok/s, {res['gbs']:.0f} GB/s "
         f"({res['gbs'] / PEAK_GBS:.1%} of 8 TB/s), {n_act:.1f} experts per layer")
     if ab:
         ms_op, _ = r.timed(mk.MODE_KERNEL_PER_OP)
         res["kernel_per_op"] = {"ms_per_step": round(ms_op / r.K, 4), "tok_s": round(r.B * r.K / (ms_op / 1e3), 2),
-                                "megakernel_speedup": round(ms_op / ms, 3)}
+                                "megakernel_speedup": round(ms_op / ms, 3), "step_ms": percentiles(r.step_ms)}
         log(f"[bench] {wl.name} kernel-per-op: {ms_op / r.K:.3f} ms/step -> megakernel {ms_op / ms:.2f}x")
     if trace_path:
         op_trace(r, trace_path, raw_path)
@@ -300,19 +336,7 @@ def main():
     wl = configs.WORKLOADS[args.workload]
     res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace, args.op_trace_raw)
 
-    # HBM bytes per launch from the committed counter profile, only while the
-    # device code is the one that was profiled
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        import hashlib
-        try:
-            tj = json.load(open(args.traffic_json))
-            src = open(os.path.join(ROOT, "moe_persistent_decode_amd", "csrc", "mk_device.hip"), "rb").read()
-            if tj.get("workload") == wl.name and tj.get("device_source_sha256_16") == hashlib.sha256(src).hexdigest()[:16]:
-                traffic = tj.get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
-
+    traffic = counted_traffic(args.traffic_json, wl.name)
     out = {
         "metric": "decode tok/s at batch 1 and 32, 8K ctx; HBM GB/s as % of MI355X peak",
         "value": round(res["tok_s"], 2),
@@ -328,6 +352,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": res["seq_len"],
                    "decode": "greedy, in-kernel advance"},
+        "step_ms": res["step_ms"],
         "roofline": {"bound": "hbm", "achieved": round(res["gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["gbs"] / PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(res["bytes"]),
@@ -336,15 +361,31 @@ def main():
     if "kernel_per_op" in res:
         out["kernel_per_op"] = res["kernel_per_op"]
 
+    def summary(w, rr, k):
+        d = {"workload": w.name, "batch": w.batch, "lengths": rr["lens"], "steps": k,
+             "tok_s": round(rr["tok_s"], 2), "ms_per_step": round(rr["ms_per_step"], 4), "step_ms": rr["step_ms"],
+             "achieved_gbs": round(rr["gbs"], 1), "frac": round(rr["gbs"] / PEAK_GBS, 4),
+             "algorithmic_bytes_per_launch": int(rr["bytes"]),
+             "experts_per_layer": round(rr["experts_per_layer"], 1)}
+        if "kernel_per_op" in rr:
+            d["kernel_per_op"] = rr["kernel_per_op"]
+        return d
+
+    bs_b = None
     if args.batch_workload != "none":
         wb = configs.WORKLOADS[args.batch_workload]
         kb = max(8, args.steps // 4)
-        rb, _ = measure(wb, kb, min(args.warmup, 4), False)
-        out["second_workload"] = {"workload": wb.name, "batch": wb.batch, "lengths": rb["lens"], "steps": kb,
-                          "tok_s": round(rb["tok_s"], 2), "ms_per_step": round(rb["ms_per_step"], 4),
-                          "achieved_gbs": round(rb["gbs"], 1), "frac": round(rb["gbs"] / PEAK_GBS, 4),
-                          "algorithmic_bytes_per_launch": int(rb["bytes"]),
-                          "experts_per_layer": round(rb["experts_per_layer"], 1)}
+        rb, bs_b = measure(wb, kb, min(args.warmup, 4), not args.no_ab)
+        out["second_workload"] = summary(wb, rb, kb)
+        out["second_workload"]["traffic"] = counted_traffic(args.traffic_json, wb.name)
+    # long contexts: one sequence at 256K and four at 64K (the same model)
+    if args.long_workloads != "none":
+        out["long_context"] = []
+        for name in args.long_workloads.split(","):
+            wq = configs.WORKLOADS[name]
+            kq = max(4, args.steps // 8)
+            rq, _ = measure(wq, kq, min(args.warmup, 2), False)
+            out["long_context"].append(summary(wq, rq, kq))
 
     if args.calibrate_copy:
         # a copy of known size: 256 MiB read and 256 MiB written per launch
@@ -359,6 +400,11 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, bs)
         log(f"[bench] oracle on host: {out['cpu_baseline']}")
+        if bs_b is not None:
+            # one timed step at batch 32 (a step of the oracle there takes
+            # about as long as the budget)
+            out["second_workload"]["cpu_baseline"] = cpu_baseline(wb, bs_b, budget_s=0.0)
+            log(f"[bench] oracle on host, {wb.name}: {out['second_workload']['cpu_baseline']}")
 
     print(json.dumps(out), flush=True)
 
@@ -387,12 +433,15 @@ def cpu_baseline(wl, bs, budget_s=10.0):
         lg, _ = od.decode_step(m, W, pool, bt, toks, lens)
         n += 1
     dt = time.time() - t
+    # the oracle's arithmetic runs in numpy's BLAS: its thread count is the
+    # cores used; the host's CPU count is given beside it
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count()
-    return {"value": round(wl.batch * n / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+    return {"value": round(wl.batch * n / dt, 4), "unit": "tok/s", "cores": cores, "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{n} greedy decode steps of {wl.name} (batch {wl.batch}, from seq_len {int(bs.seq_lens.max())}) "
                       f"after one untimed step; weights resident in host memory; {dt:.1f} s"}
 

@@ -117,7 +117,7 @@ struct mk_handle {
   std::string err;
   // derived
   int G = 0, qkv_dim = 0, q_dim = 0, kv_dim = 0, e_pad = 0;
-  int max_splits = 0, pps = 16, n_lm_tasks = 0, lm_np = 2;
+  int max_splits = 0, n_lm_tasks = 0, lm_np = 2;
   int CB = 64, NB = 32, router_np = 2, router_ks = 4, n_router_tasks = 0;
   // device memory
   uint16_t* w_all = nullptr;
@@ -215,10 +215,10 @@ void derive(mk_handle* h) {
   h->qkv_dim = h->q_dim + 2 * h->kv_dim;
   h->e_pad = ceil_div(c.n_experts, 16) * 16;  // router columns padded to whole panels
   // attention: at least 16 pages per split, more when a context would need
-  // more than MK_MAX_SPLITS splits (the combine keeps one factor per split in LDS)
+  // more than 256 splits (the combine keeps one factor per split in LDS);
+  // a shorter context may take up to 256 splits of 16 pages or more
   const int pages = ceil_div(c.max_seq_len, c.page_size) + 1;
-  h->pps = std::max(16, ceil_div(pages, 256));
-  h->max_splits = ceil_div(pages, h->pps);
+  h->max_splits = std::min(256, ceil_div(pages, 16));
   h->lm_np = 2;
   // LM head: one task per workgroup (fewer for a small vocabulary)
   h->n_lm_tasks = std::min(h->n_workers > 0 ? h->n_workers : 1, ceil_div(c.vocab / 16, 2));
@@ -237,15 +237,18 @@ int window_of(const mk_config& c, int l) {
 }
 
 // Pages per attention split for a batch of B sequences up to `len` long:
-// about two tasks per workgroup over a layer's (sequence, group) pairs, at
-// least 16 pages each. (Finer splits above MK_FUSED_B tokens, sized per layer
+// about two tasks per workgroup over a layer's (sequence, group) pairs. (Finer splits above MK_FUSED_B tokens, sized per layer
 // kind, and claims of several items at a time were measured slower at batch
 // 32 over ragged contexts: the expert phase that follows on every unit then
 // loses more than the attention gains.)
 int pps_for(const mk_handle* h, int B, int len) {
   const int pages = ceil_div(len, h->cfg.page_size) + 1;
   const int target = std::max(1, 2 * h->n_workers / (B * h->cfg.n_kv_heads));
-  int pps = std::max(h->pps, ceil_div(pages, target));
+  // that many splits, each of 16 pages or more, at most 256 (the combine
+  // keeps one factor per split in LDS); the pages spread evenly over them
+  // (a last split of a page or two would take a unit of its own for nothing)
+  const int ns = std::max(1, std::min({target, pages / 16, 256}));
+  int pps = ceil_div(pages, ns);
   // The combine merges up to `cap` splits per round trip to memory; when the
   // split count just passes a multiple of it, splits up to 1/8 longer save
   // that round trip.
@@ -264,7 +267,11 @@ int splits_for(const mk_handle* h, int l, int len, int pps) {
   const int win = window_of(h->cfg, l);
   const int keys = win ? std::min(win, len) : len;
   const int pages = ceil_div(keys, h->cfg.page_size) + 1;  // a window may straddle one extra page
-  return std::min(ceil_div(pages, pps), h->max_splits);
+  const int ns = ceil_div(pages, pps);
+  // (pps_for keeps a split count within the combine's and the scratch's
+  // bound for any length up to the maximum)
+  if (ns > h->max_splits) std::abort();
+  return ns;
 }
 
 int bucket_of(int hint) { return ceil_div(hint, 256) * 256; }
@@ -276,18 +283,24 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   S->bucket = std::min(bucket_of(hint), c.max_seq_len);
   S->pps_full = pps_for(h, B, S->bucket);
   S->pps = S->pps_full;
-  // Fused MoE with a window pattern: full-attention layers get as many splits
-  // as the window layers (longer ones), so the same number of compute units
-  // holds attention work and the rest share the experts (fewer attention
-  // claimers leave more units, and each fewer expert slices, on the chain
-  // that sets the layer's time).
   if (B <= MK_FUSED_B && h->n_workers <= MK_WG_THREADS && c.window > 0) {
+    // Window layers are split for the window's keys, not the whole context.
+    S->pps = pps_for(h, B, std::min(S->bucket, c.window));
+    // Fused MoE with a window pattern: full-attention layers get as many
+    // splits as the window layers (longer ones), so the same number of
+    // compute units holds attention work and the rest share the experts
+    // (fewer attention claimers leave more units, and each fewer expert
+    // slices, on the chain that sets the layer's time) -- while a split stays
+    // within about 512 KiB of keys and values; a longer context is spread
+    // over the units as at any batch.
     int lw = 0;
     while (lw < c.n_layers && !window_of(c, lw)) ++lw;
     if (lw < c.n_layers) {
       const int ns_win = splits_for(h, lw, S->bucket, S->pps);
       const int pages = ceil_div(S->bucket, c.page_size) + 1;
-      S->pps_full = std::max(S->pps_full, ceil_div(pages, std::max(ns_win, 1)));
+      const int page_bytes = c.page_size * c.head_dim * 4;
+      const int match_cap = std::max(16, (512 << 10) / page_bytes);
+      S->pps_full = std::max(S->pps_full, std::min(ceil_div(pages, std::max(ns_win, 1)), match_cap));
     }
   }
   const int L = c.n_layers, KVH = c.n_kv_heads, E = c.n_experts;

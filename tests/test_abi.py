@@ -264,3 +264,29 @@ def test_decode_service_needs_a_device_handle():
         mk.DecodeService(d, max_batch=1, page0=0, n_pages=8)
     assert e.value.status == 7  # MK_ERR_STATE
     d.close()
+
+
+@pytest.mark.parametrize("batch,ctx", [(1, 8192), (1, 262144), (4, 65536), (2, 131072), (32, 16384)])
+def test_attention_splits_cover_the_keys_and_spread_at_long_context(batch, ctx):
+    """The attention splits of every layer cover its keys (a window layer's
+    window, a full layer's whole context, one page of slack for a window that
+    straddles pages), stay within the combine's 256, and at long contexts
+    spread a full layer's keys over one to about two items per compute unit
+    (256 units) -- the schedule then simulates to completion."""
+    m = configs.small_variant(configs.FULL48, n_layers=4)
+    d = _host(m, batch=batch, max_seq=ctx + 64)
+    t, _ = d.schedule_export(batch, ctx)
+    attn = t[t[:, 0] == 3]
+    for layer in range(m.n_layers):
+        a = attn[attn[:, 1] == layer]
+        ns, pps = int(a[0, 5]), int(a[0, 6])
+        assert (a[:, 5] == ns).all() and (a[:, 6] == pps).all()
+        keys = min(ctx, m.layer_window(layer) or ctx)
+        pages = -(-keys // m.page_size) + 1
+        assert ns * pps >= pages and (ns - 1) * pps < pages and ns <= 256, (layer, ns, pps, pages)
+        if not m.layer_window(layer) and ctx >= 65536:
+            assert 256 <= batch * m.n_kv_heads * ns <= 640, (layer, ns, pps)
+    hi = min(m.n_experts, batch * m.top_k)
+    st, msg = d.simulate(batch, ctx, [hi] * m.n_layers, seed=batch)
+    assert st == 0, msg
+    d.close()

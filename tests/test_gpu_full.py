@@ -151,11 +151,13 @@ def _stages_layer1(c, tr):
     m, d = c.m, c.dec
     H, QD, KVH, K = m.hidden, m.q_dim, m.n_kv_heads, m.top_k
 
-    def close(name, got, ref, rtol=2e-2, atol_frac=1e-2):
+    # (split-bf16 operands: stages agree to well under 0.1% of their range;
+    # the attention output is read back as its bf16 hi half)
+    def close(name, got, ref, rtol=4e-3, atol_frac=3e-3):
         got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
         scale = max(np.abs(ref).max(), 1e-30)
         dd = np.abs(got - ref)
-        say(f"    {name:10s} max|d|={dd.max():.3e} (scale {scale:.3e})")
+        say(f"    {name:10s} max|d|={dd.max():.3e} (scale {scale:.3e}, {dd.max() / scale:.1e} of it)")
         assert np.all(dd <= atol_frac * scale + rtol * np.abs(ref)), name
 
     close("q", d.debug_read("q", (1, QD)), tr.q_rot[0].reshape(1, QD))

@@ -17,17 +17,19 @@ from tests.harness import bits_to_torch, logits_close, make_decoder, say
 pytestmark = pytest.mark.gpu
 
 
-# The projections run on the matrix cores with bf16 operands (the layer input,
-# the attention output and the expert hidden state are rounded to bf16, a
-# relative error of 2^-9 each), so a stage may differ from the float32
-# oracle by a few tenths of a percent of its scale.
-def _close(name, got, ref, rtol=2e-2, atol_frac=1e-2):
+# The projections run on the matrix cores with every activation operand split
+# into two bf16 halves (hi = bf16(x), lo = bf16(x - hi)), so an operand carries
+# a relative error near 2^-16 and a stage differs from the float32 oracle by
+# float32 accumulation order plus that; the attention output is read back as
+# its hi half only (one bf16 rounding, up to 2^-9 of each element, which the
+# relative term covers). The other stages agree to within 1e-5 of their range.
+def _close(name, got, ref, rtol=4e-3, atol_frac=3e-3):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     scale = max(np.abs(ref).max(), 1e-30)
     d = np.abs(got - ref)
     ok = np.all(d <= atol_frac * scale + rtol * np.abs(ref))
-    say(f"  {name:10s} max|d|={d.max():.3e} (scale {scale:.3e})")
+    say(f"  {name:10s} max|d|={d.max():.3e} (scale {scale:.3e}, {d.max() / scale:.1e} of it)")
     assert ok, (name, float(d.max()), scale)
 
 
