@@ -47,6 +47,9 @@ def parse():
                     help="second measured workload, reported under second_workload ('none' to skip)")
     ap.add_argument("--long-workloads", default="full48_b1_256k,full48_b4_64k",
                     help="comma-separated long-context workloads timed after the others ('none' to skip)")
+    ap.add_argument("--single-layer", default="layer1_b1_8k",
+                    help="one-layer workload timed with the last-level cache flushed between steps ('none' to skip)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling diagnostic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ab", action="store_true", help="skip the kernel-per-op comparison")
     ap.add_argument("--op-trace", default=None, metavar="PATH",
@@ -258,6 +261,68 @@ def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None):
     return res, bs
 
 
+def stream_ceiling(gib=4, reps=10):
+    """The streaming-read ceiling: GB/s of mk_stream_read over a buffer far
+    larger than the last-level cache (median of `reps` timed reads)."""
+    import numpy as np
+    import torch
+
+    import moe_persistent_decode_amd as mk
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    st = torch.cuda.current_stream()
+    for _ in range(3):
+        mk.stream_read(buf, st)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(st)
+    for i in range(reps):
+        mk.stream_read(buf, st)
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    gbs = (gib << 30) / (float(np.median(ms)) / 1e3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    log(f"[bench] streaming-read ceiling: {gbs:.0f} GB/s ({gbs / PEAK_GBS:.1%} of 8 TB/s) over {gib} GiB")
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4), "bytes": gib << 30, "reads": reps}
+
+
+def measure_flushed(wl, steps, warmup):
+    """One decode step at a time with the last-level cache evicted before each
+    (a 1 GiB streaming read between steps, outside the timed events): for a
+    model whose weights fit in the 256 MB cache, the HBM-bound time."""
+    import numpy as np
+    import torch
+
+    import moe_persistent_decode_amd as mk
+    r = Run(wl, steps, warmup, 2)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    ms_cached, first_c = r.timed(mk.MODE_MEGAKERNEL)
+    r.run(r.W)
+    r.dec.sync(r.stream)
+    first = r.done
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(r.K)]
+    for i, (a, b) in enumerate(pairs):
+        mk.stream_read(flush, r.stream)
+        a.record(r.stream)
+        r.run(1, True, slot=i)
+        b.record(r.stream)
+    torch.cuda.synchronize()
+    r.dec.sync(r.stream)
+    ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    bytes_avg, n_act = r.algorithmic_bytes(first)
+    med = float(np.median(ms))
+    res = {"workload": wl.name, "steps": r.K, "step_ms": percentiles(ms), "tok_s": round(r.B / (med / 1e3), 2),
+           "achieved_gbs": round(bytes_avg / (med / 1e3) / 1e9, 1),
+           "frac": round(bytes_avg / (med / 1e3) / 1e9 / PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(bytes_avg),
+           "unflushed_ms_per_step": round(ms_cached / r.K, 4), "flush": "1 GiB streaming read before each step"}
+    log(f"[bench] {wl.name} flushed: {med:.3f} ms/step median ({res['achieved_gbs']:.0f} GB/s, "
+        f"{res['frac']:.1%} of 8 TB/s); unflushed {ms_cached / r.K:.3f} ms/step")
+    del flush
+    r.close()
+    return res
+
+
 ORDERS = {0: "shipped", 1: "qkv-first", 2: "attention-first"}
 PLACEMENTS = {0: "tuned", 1: "round-robin", 2: "affinity"}
 
@@ -386,6 +451,11 @@ def main():
             kq = max(4, args.steps // 8)
             rq, _ = measure(wq, kq, min(args.warmup, 2), False)
             out["long_context"].append(summary(wq, rq, kq))
+
+    if args.single_layer != "none":
+        out["single_layer"] = measure_flushed(configs.WORKLOADS[args.single_layer], 16, 4)
+    if not args.no_ceiling:
+        out["stream_read_ceiling"] = stream_ceiling()
 
     if args.calibrate_copy:
         # a copy of known size: 256 MiB read and 256 MiB written per launch

@@ -244,6 +244,17 @@ mk_status mk_set_wait_limit(mk_handle* h, uint32_t microseconds);
  * step counters, so the next step starts clean. */
 mk_status mk_sync_status(mk_handle* h, void* stream);
 
+/* Diagnostic: read `bytes` of device memory at `buf` once, in 16-byte
+ * nontemporal loads spread over every compute unit, on `stream` (async). The
+ * time it takes is the practical streaming-read ceiling that the decode
+ * step's achieved bandwidth is set against (the pages' speed-of-light
+ * argument assumes the weights stream at the HBM rate: megakernel post,
+ * introduction); reading a buffer larger than the last-level cache also
+ * evicts it, so a timed step after it reads from HBM. `buf` must be 16-byte
+ * aligned and `bytes` a nonzero multiple of 16 (else MK_ERR_INVALID_ARG,
+ * message through mk_last_error(NULL)); nothing is written. */
+mk_status mk_stream_read(const void* buf, size_t bytes, void* stream);
+
 /* Last error message of this handle (or of the last failed mk_create when h is NULL). */
 const char* mk_last_error(const mk_handle* h);
 

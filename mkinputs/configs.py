@@ -36,6 +36,10 @@ class ModelConfig:
     page_size: int = 16
     window: int = 0          # 0: every layer attends to the whole context
     full_every: int = 1      # with window > 0, layer l is full iff l % full_every == full_every - 1
+    # dense: a sequential layer (attention, then a second RMSNorm and one
+    # SwiGLU FFN of width expert_ffn; n_experts = top_k = 1, no router) and an
+    # LM head tied to the embedding
+    dense: bool = False
 
     @property
     def q_dim(self) -> int:
@@ -61,9 +65,13 @@ class ModelConfig:
         return 0 if self.is_full(layer) else self.window
 
     def param_counts(self) -> Tuple[int, int]:
-        """(total, active per token) parameter counts, untied embedding and LM head."""
+        """(total, active per token) parameter counts, untied embedding and LM
+        head (a dense model's tied matrix counted once)."""
         H, E, F = self.hidden, self.n_experts, self.expert_ffn
         attn = H * self.qkv_dim + self.q_dim * H
+        if self.dense:
+            total = self.n_layers * (attn + 3 * H * F + 2 * H) + self.vocab * H + H
+            return total, total
         router = H * E
         expert = 3 * H * F
         norms = H
@@ -91,6 +99,21 @@ LAYER1 = ModelConfig(name="layer1", hidden=2048, n_q_heads=32, n_kv_heads=4, hea
 FULL48 = ModelConfig(name="full48", hidden=2048, n_q_heads=32, n_kv_heads=4, head_dim=128,
                      n_experts=128, top_k=8, expert_ffn=768, vocab=131072, n_layers=48,
                      window=4096, full_every=4)
+
+# A dense decoder shaped like Llama-3.2-1B (the model of the Hazy Research
+# megakernel the megakernel post starts from, section "Where we started", and
+# of the tiny-vllm walkthrough: hidden 2048, 16 layers, 2048-wide q and
+# 512-wide k/v projections of head_dim 64, vocab 128256, RoPE theta 500000,
+# logits from the embedding matrix). The FFN width 8192 and eps 1e-5 are
+# readings (the model's published configuration; the pages give neither).
+# Random weights: the shapes are what the decode step's cost depends on.
+LLAMA1B = ModelConfig(name="llama1b", hidden=2048, n_q_heads=32, n_kv_heads=8, head_dim=64,
+                      n_experts=1, top_k=1, expert_ffn=8192, vocab=128256, n_layers=16,
+                      rope_theta=500000.0, eps=1e-5, dense=True)
+
+TINY_DENSE = ModelConfig(name="tiny_dense", hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                         n_experts=1, top_k=1, expert_ffn=512, vocab=1024, n_layers=2,
+                         rope_theta=500000.0, eps=1e-5, dense=True)
 
 
 @dataclass(frozen=True)
@@ -133,6 +156,11 @@ WORKLOADS = {
     # long context
     "full48_b1_256k": Workload("full48_b1_256k", FULL48, batch=1, seq_len=(262144, 262144), steps=64),
     "full48_b4_64k": Workload("full48_b4_64k", FULL48, batch=4, seq_len=(65536, 65536), steps=64),
+    # the dense Llama-3.2-1B-shaped decoder at batch 1 and 4, 8K context
+    "llama1b_b1_8k": Workload("llama1b_b1_8k", LLAMA1B, batch=1, seq_len=(8192, 8192), steps=64),
+    "llama1b_b4_ragged": Workload("llama1b_b4_ragged", LLAMA1B, batch=4, seq_len=(512, 16384),
+                                  ragged=True, steps=16),
+    "tiny_dense": Workload("tiny_dense", TINY_DENSE, batch=1, seq_len=(129, 129), steps=16),
 }
 
 

@@ -21,6 +21,8 @@ Canonical layouts (row-major, [in x out]):
   wqkv.{l} [H, QH*D + 2*KVH*D]   columns: q heads, then k heads, then v heads
   wo.{l} [QH*D, H]; wr.{l} [H, E]
   wg.{l}, wu.{l} [E, H, F]; wd.{l} [E, F, H]; wlm [H, V]
+  dense models: gamma2.{l} [H] (the FFN's norm) in place of wr.{l}, E = 1,
+  and wlm = emb transposed (tied)
 KV pool (one page = page_size tokens, shared page ids across layers):
   pool [L, n_pages, 2, KVH, page_size*D] bf16, where plane 0 holds K with
   element (slot, d) at slot*D + d, and plane 1 holds V transposed, element
@@ -53,6 +55,11 @@ def _normal_bf16(shape, seed: int, std: float, mean: float, device) -> torch.Ten
     return x.to(torch.bfloat16)
 
 
+def layer_kinds(m: ModelConfig) -> tuple:
+    """The per-layer weight names of model m."""
+    return DENSE_LAYER_KINDS if m.dense else LAYER_KINDS
+
+
 def weight_shapes(m: ModelConfig) -> Dict[str, tuple]:
     H, E, F = m.hidden, m.n_experts, m.expert_ffn
     s = {"emb": (m.vocab, H), "gamma_f": (H,), "wlm": (H, m.vocab)}
@@ -60,7 +67,10 @@ def weight_shapes(m: ModelConfig) -> Dict[str, tuple]:
         s[f"gamma.{l}"] = (H,)
         s[f"wqkv.{l}"] = (H, m.qkv_dim)
         s[f"wo.{l}"] = (m.q_dim, H)
-        s[f"wr.{l}"] = (H, E)
+        if m.dense:
+            s[f"gamma2.{l}"] = (H,)
+        else:
+            s[f"wr.{l}"] = (H, E)
         s[f"wg.{l}"] = (E, H, F)
         s[f"wu.{l}"] = (E, H, F)
         s[f"wd.{l}"] = (E, F, H)
@@ -73,6 +83,9 @@ def weight_tensor(m: ModelConfig, name: str, seed: int = 1, device="cpu", std: f
     exactly as make_weights draws it, so any piece can be regenerated alone."""
     shape = weight_shapes(m)[name]
     kind = name.split(".")[0]
+    if m.dense and kind == "wlm":
+        # tied: the LM head is the embedding matrix, [H, V]
+        return weight_tensor(m, "emb", seed, device, std).t().contiguous()
     if kind.startswith("gamma"):
         return _normal_bf16(shape, tensor_seed(seed, name), std, 1.0, device)
     if kind in ("wg", "wu", "wd"):
@@ -86,11 +99,13 @@ def weight_tensor(m: ModelConfig, name: str, seed: int = 1, device="cpu", std: f
 
 
 LAYER_KINDS = ("gamma", "wqkv", "wo", "wr", "wg", "wu", "wd")
+# a dense layer: attention norm, QKV, O, FFN norm, gate, up, down
+DENSE_LAYER_KINDS = ("gamma", "wqkv", "wo", "gamma2", "wg", "wu", "wd")
 GLOBAL_NAMES = ("emb", "gamma_f", "wlm")
 
 
 def make_layer_weights(m: ModelConfig, layer: int, seed: int = 1, device="cpu") -> Dict[str, torch.Tensor]:
-    return {f"{k}.{layer}": weight_tensor(m, f"{k}.{layer}", seed, device) for k in LAYER_KINDS}
+    return {f"{k}.{layer}": weight_tensor(m, f"{k}.{layer}", seed, device) for k in layer_kinds(m)}
 
 
 def make_weights(m: ModelConfig, seed: int = 1, device="cpu", std: float = 0.02) -> Dict[str, torch.Tensor]:

@@ -30,7 +30,7 @@ EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals
            "mk_service_create", "mk_service_pause", "mk_service_resume", "mk_service_alloc_pages",
            "mk_service_admit", "mk_service_evict", "mk_service_stats", "mk_service_last_error",
            "mk_service_destroy",
-           "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache",
+           "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache", "mk_stream_read",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
 
 
@@ -84,6 +84,7 @@ def _load():
     lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
     lib.mk_set_schedule_options.argtypes = [H, I, I]
     lib.mk_kv_cache.argtypes = [H, I, ctypes.POINTER(P), ctypes.POINTER(S)]
+    lib.mk_stream_read.argtypes = [P, S, P]
     lib.mk_set_mode.argtypes = [H, I]
     lib.mk_set_task_trace.argtypes = [H, P, S]
     lib.mk_debug_read.argtypes = [H, ctypes.c_char_p, P, S]
@@ -131,6 +132,15 @@ def _stream_ptr(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def stream_read(buf, stream=None) -> None:
+    """mk_stream_read: read a device tensor once (the streaming-read ceiling
+    diagnostic; also evicts the last-level cache when larger than it)."""
+    nbytes = buf.numel() * buf.element_size()
+    st = lib.mk_stream_read(_ptr(buf), nbytes, _stream_ptr(stream))
+    if st != 0:
+        raise MkError(st, lib.mk_last_error(None).decode())
 
 
 def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages_per_seq: int,

@@ -2653,6 +2653,37 @@ extern "C" __global__ __launch_bounds__(256) void mk_zero_words(uint32_t* p, int
   for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
 }
 
+// The streaming-read ceiling, a diagnostic beside the megakernel's figures:
+// each workgroup (two per compute unit, 512 threads) reads one contiguous
+// range of the n16 16-byte words, 8 KB per round (consecutive lanes on
+// consecutive words) with eight rounds' nontemporal loads in flight, as the
+// weight streams of the decode step do. The words are folded into one value
+// per thread that is stored only if it equals a constant the data never
+// makes, so no load can be dropped and nothing is written. (The word has
+// external linkage, so the store, and with it the loads, cannot be proven
+// dead.)
+__device__ uint32_t mk_stream_sink;
+
+extern "C" __global__ __launch_bounds__(512) void mk_stream_read_words(const u32x4_t* p, size_t n16) {
+  constexpr int U = 8;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = per * blockIdx.x, hi = lo + per < n16 ? lo + per : n16;
+  size_t i = lo + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * 512 < hi; i += U * 512) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * 512);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < hi; i += 512) {
+    const u32x4_t a = __builtin_nontemporal_load(p + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9e3779b9u) mk_stream_sink = acc;
+}
+
 // ------------------------------------------------------------ host launch
 #include <mutex>
 
@@ -2676,6 +2707,11 @@ hipError_t mk_static_scratch(int device, void** ptr) {
   }
   *ptr = addr[device];
   return hipSuccess;
+}
+
+hipError_t mk_launch_stream_read(const void* p, size_t n16, hipStream_t stream) {
+  hipLaunchKernelGGL(mk_stream_read_words, dim3(512), dim3(512), 0, stream, (const u32x4_t*)p, n16);
+  return hipGetLastError();
 }
 
 hipError_t mk_launch_zero(uint32_t* p, int n, hipStream_t stream) {

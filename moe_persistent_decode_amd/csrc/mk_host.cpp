@@ -1430,6 +1430,14 @@ mk_status mk_set_wait_limit(mk_handle* h, uint32_t microseconds) {
   return MK_OK;
 }
 
+mk_status mk_stream_read(const void* buf, size_t bytes, void* stream) {
+  if (!buf || bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "stream_read: buffer must be 16-byte aligned, bytes a nonzero multiple of 16");
+  if (mk_launch_stream_read(buf, bytes / 16, (hipStream_t)stream) != hipSuccess)
+    return fail(nullptr, MK_ERR_HIP, "stream_read launch failed");
+  return MK_OK;
+}
+
 mk_status mk_kv_cache(mk_handle* h, int layer, void** kv_base, size_t* bytes) {
   if (!h || !kv_base || !bytes) return MK_ERR_INVALID_ARG;
   if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");

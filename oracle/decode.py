@@ -22,6 +22,18 @@ kept, and each token's k expert outputs are summed weighted by its router
 scores (section "Tasks", MoE routing and MoE GEMMs). After the last layer a
 final RMSNorm and the LM head give the logits; decoding is greedy.
 
+The second model is dense and sequential, shaped like Llama-3.2-1B (the
+model of the Hazy Research megakernel the post starts from, section "Where
+we started", and of the tiny-vllm walkthrough, section "The remaining layers
+and logits"):
+
+    h <- h + Attention(RMSNorm(h; gamma_l))
+    h <- h + FFN(RMSNorm(h; gamma2_l))
+
+with one SwiGLU FFN per layer (section "Tasks": FFN_UPGATE_ACT fuses the
+SiLU-and-multiply, FFN_DOWN) and logits from the embedding matrix (tiny-vllm:
+the logits come from embed_tokens).
+
 Readings where the pages are silent (all fixed here, listed in the design doc):
   R1  seq_lens counts the token being decoded; its position is seq_len - 1,
       and its K/V are written into the cache before attention reads it
@@ -200,12 +212,73 @@ class StepTrace:
     attn_out: List[np.ndarray] = field(default_factory=list)        # [B, QH*D] (record=True)
     attn_proj: List[np.ndarray] = field(default_factory=list)       # [B, H] (record=True)
     expert_out: List[np.ndarray] = field(default_factory=list)      # [B, k, H] (record=True)
-    moe_out: List[np.ndarray] = field(default_factory=list)         # [B, H] (record=True)
+    moe_out: List[np.ndarray] = field(default_factory=list)         # [B, H] (record=True; dense: the FFN's)
+    h_mid: List[np.ndarray] = field(default_factory=list)           # [B, H] dense: h + attention (record=True)
+    x_norm2: List[np.ndarray] = field(default_factory=list)         # [B, H] dense: the FFN's input (record=True)
     x_final: Optional[np.ndarray] = None                             # [B, H]
 
 
 WeightFn = Callable[..., np.ndarray]
 
+
+
+def _attention(cfg, W: WeightFn, pool, block_tables, seq_lens, l, x, f, dtype):
+    """Layer l's attention on the normalised input x [B, H]: QKV projection,
+    RoPE on q and k at each sequence's position, this step's K/V written into
+    the cache (R1, R10), grouped-query attention over the cache, O projection.
+    Returns (a [B, H], rotated q [B, QH, D], per-head outputs [B, QH, D])."""
+    B = x.shape[0]
+    H, D, P = cfg.hidden, cfg.head_dim, cfg.page_size
+    QH, KVH, G = cfg.n_q_heads, cfg.n_kv_heads, cfg.group
+    qkv = x @ f(W("wqkv", l))                                      # [B, QH*D + 2*KVH*D]
+    q = qkv[:, :QH * D].reshape(B, QH, D)
+    k = qkv[:, QH * D:QH * D + KVH * D].reshape(B, KVH, D)
+    v = qkv[:, QH * D + KVH * D:].reshape(B, KVH, D)
+    o = np.zeros((B, QH, D), dtype=dtype)
+    qr = np.zeros((B, QH, D), dtype=dtype)
+    win = cfg.layer_window(l)
+    for b in range(B):
+        p = int(seq_lens[b]) - 1
+        qb = rope(q[b], p, cfg.rope_theta)
+        qr[b] = qb
+        kb = rope(k[b], p, cfg.rope_theta)
+        page, slot = page_slot(block_tables[b], p, P)
+        for g in range(KVH):
+            kv_write(pool[l], int(page), int(slot), g, float_to_bf16_rne(kb[g]),
+                     float_to_bf16_rne(v[b, g]), P)
+        lo = 0 if win == 0 else max(0, p - win + 1)
+        pos = np.arange(lo, p + 1)
+        pages, slots = page_slot(block_tables[b], pos, P)
+        for g in range(KVH):
+            K, V = kv_read(pool[l], pages, slots, g, D, P, dtype)
+            for hh in range(g * G, (g + 1) * G):
+                o[b, hh] = attention_one_head(qb[hh], K, V)
+    a = o.reshape(B, QH * D) @ f(W("wo", l))                       # [B, H]
+    return a, qr, o
+
+
+def _dense_layer(cfg, W: WeightFn, pool, block_tables, seq_lens, l, h, x, f, dtype, tr, record):
+    """A sequential (dense) layer, as in the tiny-vllm walkthrough's
+    Llama-3.2-1B decode path (section "The remaining layers and logits"): the
+    attention output is added to the residual stream, a second RMSNorm
+    (gamma2, the FFN's gain) normalises the sum, and the SwiGLU FFN's output
+    is added in turn (megakernel post, section "Tasks": FFN_UPGATE_ACT with
+    the SiLU-and-multiply, FFN_DOWN). Returns the new residual stream."""
+    a, qr, o = _attention(cfg, W, pool, block_tables, seq_lens, l, x, f, dtype)
+    h1 = h + a
+    x2 = rmsnorm(h1, f(W("gamma2", l)), cfg.eps)
+    y = expert_ffn(x2, f(W("wg", l, 0)), f(W("wu", l, 0)), f(W("wd", l, 0)))
+    h2 = h1 + y
+    if record:
+        tr.x_norm.append(x)
+        tr.q_rot.append(qr)
+        tr.attn_out.append(o.reshape(x.shape[0], -1))
+        tr.attn_proj.append(a)
+        tr.h_mid.append(h1)
+        tr.x_norm2.append(x2)
+        tr.moe_out.append(y)
+        tr.h_out.append(h2.copy())
+    return h2
 
 def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.ndarray,
                 seq_lens: np.ndarray, dtype=np.float32, record: bool = False,
@@ -230,31 +303,11 @@ def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.nda
     h = np.stack([f(emb[int(t)]) for t in tokens])                     # [B, H]
     for l in range(cfg.n_layers):
         x = rmsnorm(h, f(W("gamma", l)), cfg.eps)                      # [B, H]
+        if cfg.dense:
+            h = _dense_layer(cfg, W, pool, block_tables, seq_lens, l, h, x, f, dtype, tr, record)
+            continue
         # attention branch
-        qkv = x @ f(W("wqkv", l))                                      # [B, QH*D + 2*KVH*D]
-        q = qkv[:, :QH * D].reshape(B, QH, D)
-        k = qkv[:, QH * D:QH * D + KVH * D].reshape(B, KVH, D)
-        v = qkv[:, QH * D + KVH * D:].reshape(B, KVH, D)
-        o = np.zeros((B, QH, D), dtype=dtype)
-        qr = np.zeros((B, QH, D), dtype=dtype)
-        win = cfg.layer_window(l)
-        for b in range(B):
-            p = int(seq_lens[b]) - 1
-            qb = rope(q[b], p, cfg.rope_theta)
-            qr[b] = qb
-            kb = rope(k[b], p, cfg.rope_theta)
-            page, slot = page_slot(block_tables[b], p, P)
-            for g in range(KVH):
-                kv_write(pool[l], int(page), int(slot), g, float_to_bf16_rne(kb[g]),
-                         float_to_bf16_rne(v[b, g]), P)
-            lo = 0 if win == 0 else max(0, p - win + 1)
-            pos = np.arange(lo, p + 1)
-            pages, slots = page_slot(block_tables[b], pos, P)
-            for g in range(KVH):
-                K, V = kv_read(pool[l], pages, slots, g, D, P, dtype)
-                for hh in range(g * G, (g + 1) * G):
-                    o[b, hh] = attention_one_head(qb[hh], K, V)
-        a = o.reshape(B, QH * D) @ f(W("wo", l))                       # [B, H]
+        a, qr, o = _attention(cfg, W, pool, block_tables, seq_lens, l, x, f, dtype)
         # MoE branch
         wr = W("wr", l)
         if router_hook is not None:

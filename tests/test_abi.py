@@ -290,3 +290,12 @@ def test_attention_splits_cover_the_keys_and_spread_at_long_context(batch, ctx):
     st, msg = d.simulate(batch, ctx, [hi] * m.n_layers, seed=batch)
     assert st == 0, msg
     d.close()
+
+
+def test_stream_read_rejects_bad_buffers_on_the_host():
+    """mk_stream_read checks alignment and size before any device call."""
+    from moe_persistent_decode_amd.binding import lib
+    assert lib.mk_stream_read(ctypes.c_void_p(4096), 0, None) == 1
+    assert lib.mk_stream_read(ctypes.c_void_p(4099), 64, None) == 1
+    assert lib.mk_stream_read(ctypes.c_void_p(4096), 40, None) == 1
+    assert lib.mk_stream_read(None, 64, None) == 1

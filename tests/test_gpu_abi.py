@@ -128,3 +128,15 @@ def test_all_nan_logits_raise_a_fault():
         _compare(cfg, bs, weights, pool, logits.cpu().numpy(), nxt.cpu().numpy())
     finally:
         dec.close()
+
+
+def test_stream_read_runs_and_writes_nothing():
+    """The streaming-read diagnostic reads a buffer (a ragged length of
+    16-byte words, so both of its loops run) and leaves it unchanged."""
+    import moe_persistent_decode_amd as mk
+    say("[abi] stream_read over 64 MiB + 48 bytes")
+    buf = torch.arange((64 << 20) // 4 + 12, dtype=torch.int32, device="cuda")
+    ref = buf.clone()
+    mk.stream_read(buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)

@@ -261,6 +261,14 @@ def _full_sequence_forward(cfg, W, toks):
             s = np.where(allowed, s, -np.inf)
             o[:, hh] = scipy.special.softmax(s, axis=-1) @ v[:, g]
         a = o.reshape(T, QH * D) @ f(W("wo", l))
+        if cfg.dense:
+            # sequential: the FFN reads the second norm of h + attention
+            h = h + a
+            x2 = rms(h, f(W("gamma2", l)))
+            g_ = x2 @ f(W("wg", l, 0))
+            u_ = x2 @ f(W("wu", l, 0))
+            h = h + (g_ * scipy.special.expit(g_) * u_) @ f(W("wd", l, 0))
+            continue
         r = x @ f(W("wr", l))
         y = np.zeros((T, H))
         for t in range(T):
@@ -285,6 +293,49 @@ def test_incremental_decode_matches_full_recomputation(window, full_every):
     inc, _, _ = _run_incremental(cfg, W, toks, bt, np.float64)
     full = _full_sequence_forward(cfg, W, toks)
     assert np.max(np.abs(inc - full)) < 1e-9
+
+
+def test_dense_incremental_decode_matches_full_recomputation():
+    """The dense sequential layer (attention added, a second norm, the SwiGLU
+    FFN added) step by step equals the whole-sequence float64 forward."""
+    cfg = configs.TINY_DENSE
+    W = _weights(cfg)
+    rng = np.random.default_rng(18)
+    T = 37
+    toks = rng.integers(0, cfg.vocab, T)
+    bt = rng.permutation(8)[:3]
+    inc, _, _ = _run_incremental(cfg, W, toks, bt, np.float64)
+    full = _full_sequence_forward(cfg, W, toks)
+    assert np.max(np.abs(inc - full)) < 1e-9
+
+
+def test_dense_layer_with_silent_outputs_keeps_the_embedding():
+    """With the O projection and the FFN's down projection zero, every dense
+    layer adds nothing: the logits are RMSNorm(emb[token]; gamma_f) times the
+    tied head (the embedding transposed), whatever the attention and the
+    norms inside the layer compute."""
+    cfg = configs.TINY_DENSE
+    t = gen.make_weights(cfg, seed=12, device="cpu")
+    for l in range(cfg.n_layers):
+        t[f"wo.{l}"] = gen.torch.zeros_like(t[f"wo.{l}"])
+        t[f"wd.{l}"] = gen.torch.zeros_like(t[f"wd.{l}"])
+    W = gen.NumpyWeights(t)
+    toks = np.array([5, 900])
+    pool = _empty_pool(cfg, 4)
+    lg, _ = od.decode_step(cfg, W, pool, np.array([[0], [1]]), toks, np.array([1, 1]), dtype=np.float64)
+    emb = t["emb"].double().numpy()
+    gf = t["gamma_f"].double().numpy()
+    for b, tok in enumerate(toks):
+        e = emb[tok]
+        x = e / math.sqrt(float(np.mean(e * e)) + cfg.eps) * gf
+        assert np.max(np.abs(lg[b] - emb @ x)) < 1e-10
+
+
+def test_dense_head_is_the_embedding_transposed():
+    cfg = configs.TINY_DENSE
+    W = _weights(cfg)
+    assert np.array_equal(W("wlm"), W("emb").T)
+    assert "wr.0" not in gen.weight_shapes(cfg) and gen.weight_shapes(cfg)["gamma2.1"] == (cfg.hidden,)
 
 
 def test_paged_equals_contiguous_bit_identical():
