@@ -47,6 +47,8 @@ def parse():
                     help="second measured workload, reported under second_workload ('none' to skip)")
     ap.add_argument("--long-workloads", default="full48_b1_256k,full48_b4_64k",
                     help="comma-separated long-context workloads timed after the others ('none' to skip)")
+    ap.add_argument("--dense-workload", default="llama1b_b1_8k",
+                    help="dense (Llama-3.2-1B-shaped) workload timed after the others ('none' to skip)")
     ap.add_argument("--single-layer", default="layer1_b1_8k",
                     help="one-layer workload timed with the last-level cache flushed between steps ('none' to skip)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling diagnostic")
@@ -91,7 +93,7 @@ class Run:
         del g
         for l in range(self.m.n_layers):
             w = gen.make_layer_weights(self.m, l, wl.seed_weights, dev)
-            self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.LAYER_KINDS))
+            self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.layer_kinds(self.m)))
             self.stream.synchronize()
             del w
         torch.cuda.synchronize()
@@ -140,6 +142,9 @@ class Run:
         import numpy as np
 
         from moe_persistent_decode_amd import sol
+        if self.m.dense:  # one FFN per layer, no routing
+            tot = [sol.step_bytes(self.m, self.lens_host + first + i, [1] * self.m.n_layers) for i in range(self.K)]
+            return float(np.mean(tot)), 1.0
         rt = self.route.cpu().numpy()
         tot = []
         for i in range(self.K):
@@ -443,6 +448,12 @@ def main():
         rb, bs_b = measure(wb, kb, min(args.warmup, 4), not args.no_ab)
         out["second_workload"] = summary(wb, rb, kb)
         out["second_workload"]["traffic"] = counted_traffic(args.traffic_json, wb.name)
+    # the dense Llama-3.2-1B-shaped decoder on the same C ABI
+    if args.dense_workload != "none":
+        wd = configs.WORKLOADS[args.dense_workload]
+        kd = max(8, args.steps // 2)
+        rd, _ = measure(wd, kd, min(args.warmup, 4), not args.no_ab)
+        out["dense_workload"] = summary(wd, rd, kd)
     # long contexts: one sequence at 256K and four at 64K (the same model)
     if args.long_workloads != "none":
         out["long_context"] = []

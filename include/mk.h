@@ -74,6 +74,15 @@ typedef struct {
   int32_t max_pages_per_seq; /* row stride of block_tables */
   int32_t n_pages;         /* pages in the KV pool */
   int32_t mode;            /* mk_mode */
+  int32_t dense;           /* 0: parallel MoE layers (above). 1: dense sequential
+                            * layers, h += Attn(RMSNorm(h; gamma)), then
+                            * h += FFN(RMSNorm(h; gamma2)) with one SwiGLU FFN of
+                            * width expert_ffn (a multiple of 128, <= 8192);
+                            * n_experts = top_k = 1, no router, max_batch <= 4
+                            * (the Llama-3.2-1B decode path of the tiny-vllm
+                            * walkthrough, section "The remaining layers and
+                            * logits"; the post's FFN_UPGATE_ACT and FFN_DOWN,
+                            * section "Tasks") */
 } mk_config;
 
 typedef struct mk_handle mk_handle;
@@ -112,19 +121,36 @@ mk_status mk_kv_cache(mk_handle* h, int layer, void** kv_base, size_t* bytes);
  * projections, router, expert gate/up and down). Errors: MK_ERR_INVALID_ARG
  * (layer, null or misaligned pointer), MK_ERR_HIP.
  *   gamma [H]; wqkv [H][QH*D + 2*KVH*D] (q heads, then k heads, then v heads);
- *   wo [QH*D][H]; wr [H][E]; wg, wu [E][H][F]; wd [E][F][H]. */
+ *   wo [QH*D][H]; wr [H][E]; wg, wu [E][H][F]; wd [E][F][H].
+ * A dense model's layers load through mk_load_layer_dense (MK_ERR_INVALID_ARG
+ * here). */
 mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* wqkv,
                         const void* wo, const void* wr, const void* wg, const void* wu,
                         const void* wd, void* stream);
 
+/* One dense sequential layer's weights (cfg.dense = 1; the tiny-vllm
+ * walkthrough's layer: attention norm, QKV, O projection, post-attention
+ * norm, gate, up, down), caller-owned device bf16 tensors in the canonical
+ * row-major [in x out] layout, repacked like mk_load_layer's:
+ *   gamma [H]; wqkv [H][QH*D + 2*KVH*D]; wo [QH*D][H]; gamma2 [H];
+ *   wg, wu [H][F]; wd [F][H].
+ * Errors: MK_ERR_INVALID_ARG (not a dense model, layer, null or misaligned
+ * pointer), MK_ERR_HIP. */
+mk_status mk_load_layer_dense(mk_handle* h, int layer, const void* gamma, const void* wqkv,
+                              const void* wo, const void* gamma2, const void* wg, const void* wu,
+                              const void* wd, void* stream);
+
 /* Load the embedding [V][H], final norm gain [H] and LM head [H][V] (bf16),
  * caller-owned device tensors, copied or repacked like mk_load_layer's
- * (section "任务": LM_HEAD). */
+ * (section "任务": LM_HEAD). A model whose head is tied to the embedding
+ * passes the embedding's transpose as wlm. */
 mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f,
                           const void* wlm, void* stream);
 
 /* All weights at once: arrays of n_layers device pointers per tensor kind
- * (host arrays of device pointers); the same checks as the two calls above. */
+ * (host arrays of device pointers); the same checks as the calls above. A
+ * dense model gives gamma2 and leaves wr NULL; a MoE model leaves gamma2
+ * NULL. */
 typedef struct {
   const void* emb;
   const void* gamma_f;
@@ -136,6 +162,7 @@ typedef struct {
   const void* const* wg;
   const void* const* wu;
   const void* const* wd;
+  const void* const* gamma2; /* dense models: the FFN's norm gains */
 } mk_weights;
 mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream);
 

@@ -24,7 +24,8 @@ PLACE_TUNED, PLACE_ROUND_ROBIN, PLACE_AFFINITY = 0, 1, 2
 STEP_ADVANCE = 1
 
 # every function include/mk.h declares
-EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_globals", "mk_load_weights",
+EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_dense", "mk_load_globals",
+           "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
            "mk_set_schedule_options", "mk_decode_step_noalloc",
            "mk_service_create", "mk_service_pause", "mk_service_resume", "mk_service_alloc_pages",
@@ -45,7 +46,7 @@ class MkConfig(ctypes.Structure):
                                               "top_k", "expert_ffn", "vocab", "n_layers")] + [
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("page_size", "window", "full_every", "max_batch", "max_seq_len",
-                                      "max_pages_per_seq", "n_pages", "mode")]
+                                      "max_pages_per_seq", "n_pages", "mode", "dense")]
 
 
 TOKEN_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32)
@@ -76,6 +77,7 @@ def _load():
     lib.mk_create.argtypes = [ctypes.POINTER(MkConfig), P, S, I, ctypes.POINTER(H)]
     lib.mk_create_host_only.argtypes = [ctypes.POINTER(MkConfig), I, ctypes.POINTER(H)]
     lib.mk_load_layer.argtypes = [H, I, P, P, P, P, P, P, P, P]
+    lib.mk_load_layer_dense.argtypes = [H, I, P, P, P, P, P, P, P, P]
     lib.mk_load_globals.argtypes = [H, P, P, P, P]
     lib.mk_load_weights.argtypes = [H, P, P]
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
@@ -152,7 +154,7 @@ def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages
                     rope_theta=model.rope_theta, rms_eps=model.eps, page_size=model.page_size,
                     window=model.window, full_every=model.full_every, max_batch=max_batch,
                     max_seq_len=max_seq_len, max_pages_per_seq=max_pages_per_seq, n_pages=n_pages,
-                    mode=mode)
+                    mode=mode, dense=1 if getattr(model, "dense", False) else 0)
 
 
 class Decoder:
@@ -189,8 +191,11 @@ class Decoder:
 
     # ---- weights
     def load_layer(self, layer: int, gamma, wqkv, wo, wr, wg, wu, wd, stream=None):
-        self._check(lib.mk_load_layer(self._h, layer, _ptr(gamma), _ptr(wqkv), _ptr(wo), _ptr(wr),
-                                      _ptr(wg), _ptr(wu), _ptr(wd), _stream_ptr(stream)))
+        """A layer's tensors in the order of mk_load_layer; for a dense model
+        (mk_load_layer_dense) the fourth is gamma2, the FFN's norm gain."""
+        fn = lib.mk_load_layer_dense if self.cfg.dense else lib.mk_load_layer
+        self._check(fn(self._h, layer, _ptr(gamma), _ptr(wqkv), _ptr(wo), _ptr(wr), _ptr(wg), _ptr(wu), _ptr(wd),
+                       _stream_ptr(stream)))
 
     def load_globals(self, emb, gamma_f, wlm, stream=None):
         self._check(lib.mk_load_globals(self._h, _ptr(emb), _ptr(gamma_f), _ptr(wlm), _stream_ptr(stream)))
@@ -199,7 +204,8 @@ class Decoder:
         """Load canonical tensors named emb, gamma_f, wlm, gamma.{l}, wqkv.{l}, ..."""
         self.load_globals(w["emb"], w["gamma_f"], w["wlm"], stream)
         for l in range(self.cfg.n_layers):
-            self.load_layer(l, w[f"gamma.{l}"], w[f"wqkv.{l}"], w[f"wo.{l}"], w[f"wr.{l}"], w[f"wg.{l}"],
+            fourth = w[f"gamma2.{l}"] if self.cfg.dense else w[f"wr.{l}"]
+            self.load_layer(l, w[f"gamma.{l}"], w[f"wqkv.{l}"], w[f"wo.{l}"], fourth, w[f"wg.{l}"],
                             w[f"wu.{l}"], w[f"wd.{l}"], stream)
 
     # ---- decode

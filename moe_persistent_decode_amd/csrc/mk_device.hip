@@ -1331,6 +1331,7 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
 // section "Tasks"): sum the partials in fixed order, top-k (ties to the lower
 // expert index), softmax over the kept logits, the expert work queue.
 __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm, bool publish);
+__device__ __forceinline__ void route_trivial(const mk_params& P, int l, Smem& sm, bool norm);
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm);
 
 template <int MT, int NCH>
@@ -2118,7 +2119,10 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
       vh[k] = i < n8 ? Uh.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
       vl[k] = i < n8 ? Ul.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    route_build(P, l, sm, false);
+    if (P.dense)
+      route_trivial(P, l, sm, true);
+    else
+      route_build(P, l, sm, false);
 #pragma unroll
     for (int k = 0; k < MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS; ++k) {
       const int i = tid() + k * MK_WG_THREADS;
@@ -2258,6 +2262,45 @@ __device__ __forceinline__ void route_load(const mk_params& P, int l, Smem& sm) 
   __syncthreads();
 }
 
+// A dense layer's route into LDS: its one FFN is expert 0, every token is
+// routed to it with weight 1 (slot b of token b); with `norm`, also layer
+// l's sums of squares and 1/rms of every token (the FFN's input, written by
+// the layer's mid residual).
+__device__ __forceinline__ void route_trivial(const mk_params& P, int l, Smem& sm, bool norm) {
+  const int B = P.B, i = tid();
+  float sq[2] = {0.f, 0.f};
+  if (norm) {
+    const Pub S(ssq_of(P, l));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = i + k * MK_WG_THREADS;
+      sq[k] = j < B * P.NB ? S.ldf(j) : 0.f;
+    }
+  }
+  if (i == 0) {
+    sm.rt_hdr[0] = 1;
+    sm.rt_hdr[1] = P.up_items_per_expert;
+    sm.rt_hdr[2] = P.down_items_per_expert;
+    sm.rt_hdr[3] = 0;
+    sm.rt_e[0] = 0;
+    sm.rt_cnt[0] = B;
+  }
+  if (i < B) {
+    sm.rt_slot[i] = i;
+    sm.tkw[i] = 1.0f;
+  }
+  if (norm) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = i + k * MK_WG_THREADS;
+      if (j < B * P.NB) sm.ssq[j] = sq[k];
+    }
+  }
+  lds_sync();
+  if (norm) inv_rms_lds(P, sm);
+  lds_sync();
+}
+
 // Residual add of column block cb once every fused MoE claimer and O
 // projection of the layer has arrived: h += sum_g ao_g + the claimers' rows of
 // each token (summed in claimer order), then the next layer's input and the
@@ -2266,26 +2309,33 @@ __device__ __forceinline__ void route_load(const mk_params& P, int l, Smem& sm) 
 //   a[0] cb; b[1..3] as for the claimers; wait_ctr[0] every contribution,
 //   wait_ctr[1] the route.
 __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t, Smem& sm) {
-  const int l = t.layer, cb = t.a[0];
+  const int l = t.layer, cb = t.a[0], mode = t.a[1];
   const int nf = t.b[1], nt = t.b[2], wa = P.waits_enabled ? t.b[3] : 256;
   const int H = P.H, CB = P.CB, B = P.B, n = B * CB;
   const int S = P.F / 16;
   const int i = tid();
-  // the block's residual stream and gamma, written before this layer began
+  // the block's gain: the next layer's (the dense FFN's after attention); the
+  // residual stream now when it was written before this layer began (parallel
+  // layers), else after the wait (a dense layer's mid residual wrote it)
   float h0 = 0.f, g0 = 0.f;
   if (i < n) {
     const int b = i / CB, c = cb * CB + i % CB;
-    h0 = Pub(P.h).ldf(b * H + c);
-    g0 = bf2f(P.gamma[(size_t)(l + 1) * H + c]);
+    if (mode == MK_RES_PARALLEL) h0 = Pub(P.h).ldf(b * H + c);
+    g0 = bf2f(mode == MK_RES_DENSE_MID ? P.gamma2[(size_t)l * H + c] : P.gamma[(size_t)(l + 1) * H + c]);
   }
-  if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
-  route_load(P, l, sm);
+  if (mode == MK_RES_PARALLEL) {
+    if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
+    route_load(P, l, sm);
+  } else if (mode == MK_RES_DENSE_FFN) {
+    route_trivial(P, l, sm, false);
+  }
   // (claimer, token) rows, token-major, claimers ascending: per wave ballots
+  // (none after a dense layer's attention)
   int* list = sm.rt_slot + 128 * MK_FUSED_B;  // past the slots of at most MK_FUSED_B tokens
   int* wcnt = sm.ired;                         // per wave, one token at a time
-  const int n_items = sm.rt_hdr[0] * S;
+  const int n_items = mode == MK_RES_DENSE_MID ? 0 : sm.rt_hdr[0] * S;
   uint32_t mine = 0u;
-  if (i < nt) {
+  if (i < nt && mode != MK_RES_DENSE_MID) {
     int lo, hi;
     fused_share(i, nf, nt, wa, n_items, lo, hi);
     mine = fused_tokens(P, sm, lo, hi, S);
@@ -2313,9 +2363,11 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
   float av[MK_MAX_KVH];
   {
     const int b = i / CB, c = cb * CB + i % CB;
+    if (mode != MK_RES_PARALLEL && i < n) h0 = Pub(P.h).ldf(b * H + c);
     const Pub ao(P.ao);
+    const int ng = mode == MK_RES_DENSE_FFN ? 0 : P.KVH;  // the O projection's partials
 #pragma unroll
-    for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = (i < n && g < P.KVH) ? ao.ldf((g * B + b) * H + c) : 0.f;
+    for (int g = 0; g < MK_MAX_KVH; ++g) av[g] = (i < n && g < ng) ? ao.ldf((g * B + b) * H + c) : 0.f;
   }
   // the rows: thread = (column quad cq, group gq); groups stride the list
   // (a row's NQ quads in adjacent lanes, so each load instruction reads whole
@@ -2371,7 +2423,9 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
   }
   __syncthreads();
   mark(sm, 2);
-  write_block_input(P, l + 1, cb, hv, gv, n, sm);
+  // (a dense layer's FFN input goes to layer l's input buffers: every reader
+  // of those, the layer's QKV tasks, has finished before its attention did)
+  write_block_input(P, mode == MK_RES_DENSE_MID ? l : l + 1, cb, hv, gv, n, sm);
   mark(sm, 3);
   arrive_nr(P, t.sig_ctr[0]);
 }

@@ -68,7 +68,9 @@ struct CtrIdx {
   int up_claim, down_claim;  // claim counters of the two expert queues
   int up_done;   // [E] up/gate items done per active expert slot
   int colblk;    // [NB] contributions per residual column block
-  int fin;       // fused MoE: claimers and O projections done
+  int fin;       // fused MoE: claimers and O projections done (dense: the FFN claimers)
+  int mid;       // dense: O projections done (the mid residual's wait)
+  int midres;    // dense: mid residual column blocks done (the FFN's input)
 };
 
 mk_task make_task(int op, int layer) {
@@ -122,8 +124,8 @@ struct mk_handle {
   // device memory
   uint16_t* w_all = nullptr;
   size_t s_wqkv = 0, s_wo = 0, s_wr = 0, s_wgu_l = 0, s_wgu_e = 0, s_wd_l = 0, s_wd_e = 0;
-  uint16_t *emb = nullptr, *gamma = nullptr, *wqkv = nullptr, *wo = nullptr, *wr = nullptr, *wgu = nullptr,
-           *wd = nullptr, *wlm = nullptr;
+  uint16_t *emb = nullptr, *gamma = nullptr, *gamma2 = nullptr, *wqkv = nullptr, *wo = nullptr, *wr = nullptr,
+           *wgu = nullptr, *wd = nullptr, *wlm = nullptr;
   float* rope = nullptr;
   uint16_t* kv = nullptr;
   bool kv_owned = false;  // the pool was allocated by mk_create (kv_pool NULL)
@@ -172,6 +174,12 @@ mk_status fail(mk_handle* h, mk_status st, const char* fmt, ...) {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Counters of one layer in the order CtrIdx lists them: QKV per group,
+// attention per (sequence, group), combine per group, router, route,
+// attention claims, up and down claims, up/gate done per expert slot, column
+// blocks, fin, mid, midres.
+int counters_per_layer(int KVH, int B, int E, int NB) { return KVH + B * KVH + KVH + 5 + E + NB + 3; }
+
 mk_status validate_config(const mk_config* c) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null config");
   if (c->hidden <= 0 || c->hidden % 256 || c->hidden > 2048)
@@ -183,12 +191,22 @@ mk_status validate_config(const mk_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G > 16 || G * c->head_dim > 1024)
     return fail(nullptr, MK_ERR_UNSUPPORTED, "group size must be <= 16 and group width <= 1024");
-  if (c->n_experts <= 0 || c->n_experts % 8 || c->n_experts > 128)
-    return fail(nullptr, MK_ERR_UNSUPPORTED, "n_experts must be a multiple of 8, <= 128");
-  if (c->top_k <= 0 || c->top_k > MK_MAX_TOPK || c->top_k > c->n_experts)
-    return fail(nullptr, MK_ERR_UNSUPPORTED, "top_k must be in [1, 8]");
-  if (c->expert_ffn <= 0 || c->expert_ffn % 128 || c->expert_ffn > 768)
-    return fail(nullptr, MK_ERR_UNSUPPORTED, "expert_ffn must be a multiple of 128, <= 768");
+  if (c->dense != 0 && c->dense != 1) return fail(nullptr, MK_ERR_INVALID_ARG, "dense must be 0 or 1");
+  if (c->dense) {
+    if (c->n_experts != 1 || c->top_k != 1)
+      return fail(nullptr, MK_ERR_INVALID_ARG, "a dense model has n_experts = top_k = 1");
+    if (c->expert_ffn <= 0 || c->expert_ffn % 128 || c->expert_ffn > MK_MAX_DENSE_F)
+      return fail(nullptr, MK_ERR_UNSUPPORTED, "a dense FFN width must be a multiple of 128, <= %d", MK_MAX_DENSE_F);
+    if (c->max_batch > MK_FUSED_B)
+      return fail(nullptr, MK_ERR_UNSUPPORTED, "dense models decode at most %d sequences per step", MK_FUSED_B);
+  } else {
+    if (c->n_experts <= 0 || c->n_experts % 8 || c->n_experts > 128)
+      return fail(nullptr, MK_ERR_UNSUPPORTED, "n_experts must be a multiple of 8, <= 128");
+    if (c->top_k <= 0 || c->top_k > MK_MAX_TOPK || c->top_k > c->n_experts)
+      return fail(nullptr, MK_ERR_UNSUPPORTED, "top_k must be in [1, 8]");
+    if (c->expert_ffn <= 0 || c->expert_ffn % 128 || c->expert_ffn > 768)
+      return fail(nullptr, MK_ERR_UNSUPPORTED, "expert_ffn must be a multiple of 128, <= 768");
+  }
   if (c->vocab <= 0 || c->vocab % 16) return fail(nullptr, MK_ERR_UNSUPPORTED, "vocab must be a multiple of 16");
   if (c->n_layers <= 0) return fail(nullptr, MK_ERR_INVALID_ARG, "n_layers must be positive");
   if (c->page_size != 16) return fail(nullptr, MK_ERR_UNSUPPORTED, "page_size must be 16");
@@ -225,10 +243,12 @@ void derive(mk_handle* h) {
   // residual column blocks of 64 columns (4 panels) when the width allows
   h->CB = c.hidden >= 1024 ? 64 : 32;
   h->NB = c.hidden / h->CB;
+  // counters of one step at the largest batch
+  h->n_ctr_cap = (c.n_layers + 2) + c.n_layers * counters_per_layer(c.n_kv_heads, c.max_batch, c.n_experts, h->NB);
   // router: 2-panel tasks over K quarters (K halves for a small hidden size)
   h->router_np = 2;
   h->router_ks = c.hidden >= 1024 ? 4 : 2;
-  h->n_router_tasks = ceil_div(h->e_pad / 16, h->router_np) * h->router_ks;
+  h->n_router_tasks = c.dense ? 0 : ceil_div(h->e_pad / 16, h->router_np) * h->router_ks;
 }
 
 int window_of(const mk_config& c, int l) {
@@ -314,7 +334,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   idx += L + 1;
   S->c_lm = idx++;
   S->c_layer0 = idx;
-  S->c_per_layer = KVH + B * KVH + KVH + 1 + 1 + 1 + 1 + 1 + E + NB + 1;
+  S->c_per_layer = counters_per_layer(KVH, B, E, NB);
   idx += L * S->c_per_layer;
   S->n_ctr = idx;
   auto resid = [&](int l) { return S->c_resid0 + l; };  // input of layer l ready
@@ -336,7 +356,9 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     b0 += E;
     x.colblk = b0;
     b0 += NB;
-    x.fin = b0;
+    x.fin = b0++;
+    x.mid = b0++;
+    x.midres = b0;
     return x;
   };
 
@@ -525,7 +547,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           mk_task t = make_task(MK_OP_OPROJ, l);
           t.a[0] = g;
           t.a[1] = cb;
-          t.a[2] = x.fin;
+          t.a[2] = c.dense ? x.mid : x.fin;
           t.a[3] = per;
           t.a[4] = ns;
           t.b[0] = 1;
@@ -550,13 +572,57 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
       for (int cb = 0; cb < NB; ++cb) {
         mk_task t = make_task(MK_OP_RESIDUAL, l);
         t.a[0] = cb;
+        t.a[1] = c.dense ? MK_RES_DENSE_FFN : MK_RES_PARALLEL;
         t.b[1] = n_free;
         t.b[2] = nt;
         t.b[3] = wa;
-        add_wait(t, x.fin, nt + S->n_oproj);
-        add_wait(t, x.route, 1);
+        if (c.dense) {
+          add_wait(t, x.fin, nt);
+        } else {
+          add_wait(t, x.fin, nt + S->n_oproj);
+          add_wait(t, x.route, 1);
+        }
         t.sig_ctr[0] = resid(l + 1);
         place(t, affinity ? oproj_cus[cb] : (next0 + cb) % n_w);
+      }
+    };
+    // Dense layers: the residual after attention (h + the O projections'
+    // partials, then the FFN's input with the FFN's gain), one task per
+    // column block on the units that ran the O projections
+    auto wave_residual_mid = [&]() {
+      begin_wave();
+      for (int cb = 0; cb < NB; ++cb) {
+        mk_task t = make_task(MK_OP_RESIDUAL, l);
+        t.a[0] = cb;
+        t.a[1] = MK_RES_DENSE_MID;
+        t.b[1] = 0;
+        t.b[2] = 0;
+        t.b[3] = 256;
+        add_wait(t, x.mid, S->n_oproj);
+        t.sig_ctr[0] = x.midres;
+        place(t, oproj_cus[cb % (int)oproj_cus.size()]);
+      }
+    };
+    // Dense layers: the FFN (gate/up, SiLU-and-multiply and down of 16-row
+    // slices of its hidden layer: the post's FFN_UPGATE_ACT and FFN_DOWN
+    // fused per slice, as the fused MoE does for an expert) in equal
+    // contiguous shares over every unit, since attention has finished
+    auto wave_ffn_dense = [&]() {
+      begin_wave();
+      n_free = n_w;
+      nt = n_w;
+      wa = 256;
+      S->moe_fused.push_back(nt);
+      S->moe_fixed.push_back(0);
+      for (int i = 0; i < n_w; ++i) {
+        mk_task t = make_task(MK_OP_MOE_FUSED, l);
+        t.b[0] = i;
+        t.b[1] = n_free;
+        t.b[2] = nt;
+        t.b[3] = wa;
+        add_wait(t, x.midres, NB);
+        t.sig_ctr[0] = x.fin;
+        place(t, i);
       }
     };
     // MoE claimers above MK_FUSED_B tokens (fixed shares up to 16, claiming beyond)
@@ -618,7 +684,17 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     };
     // the layer's waves in the chosen order (megakernel post, Chinese
     // version, section on the task scheduler: the host builds named waves per
-    // layer, picks an order and flattens them)
+    // layer, picks an order and flattens them); a dense layer's in their one
+    // order
+    if (c.dense) {
+      wave_qkv();
+      wave_attn();
+      wave_oproj_fused();
+      wave_residual_mid();
+      wave_ffn_dense();
+      wave_residual();
+      continue;
+    }
     if (h->wave_order == MK_ORDER_QKV_FIRST) {
       wave_qkv();
       wave_router();
@@ -716,15 +792,17 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     for (int g = 0; g < KVH; ++g) want[k++] = S.n_qkv[g];
     for (int i = 0; i < B * KVH; ++i) want[k++] = merged ? (i < KVH ? (int64_t)B * ns : 0) : ns;
     for (int g = 0; g < KVH; ++g) want[k++] = merged ? 0 : B;
-    want[k++] = (int64_t)ceil_div(h->e_pad / 16, 2) * h->router_ks;  // router tasks
-    want[k++] = 1;                                                   // route finalized
+    want[k++] = h->n_router_tasks;                                  // router tasks
+    want[k++] = c.dense ? 0 : 1;                                    // route finalized
     want[k++] = (int64_t)B * KVH * ns + S.n_attn_claimers[l];        // attention claims
     const bool fused = S.moe_fused[l] > 0, claiming = !S.moe_fixed[l] && !fused;
     want[k++] = claiming ? (int64_t)n_active[l] * up_per_e + S.n_up_claimers : 0;
     want[k++] = claiming ? (int64_t)n_active[l] * down_per_e + S.n_up_claimers : 0;
     for (int a = 0; a < E; ++a) want[k++] = (!fused && a < n_active[l]) ? up_per_e : 0;
     for (int cb = 0; cb < NB; ++cb) want[k++] = fused ? 0 : KVH + n_active[l];
-    want[k++] = fused ? S.moe_fused[l] + S.n_oproj : 0;  // fused MoE: claimers and O projections
+    want[k++] = fused ? S.moe_fused[l] + (c.dense ? 0 : S.n_oproj) : 0;  // fused MoE: claimers, O projections
+    want[k++] = c.dense ? S.n_oproj : 0;                                  // dense: O projections
+    want[k++] = c.dense ? NB : 0;                                         // dense: mid residual blocks
   }
   // a lost signal: the first wait of the first task at or after `corrupt`
   // waits for one arrival more than its counter ever receives
@@ -901,7 +979,7 @@ mk_status get_schedule(mk_handle* h, int B, int hint, Schedule** out) {
   auto it = h->scheds.find(key);
   if (it == h->scheds.end()) {
     auto S = build_schedule(h, B, hint);
-    if (S->n_ctr > h->n_ctr_cap && !h->host_only)
+    if (S->n_ctr > h->n_ctr_cap)
       return fail(h, MK_ERR_UNSUPPORTED, "schedule needs %d counters, capacity %d", S->n_ctr, h->n_ctr_cap);
     if (!h->host_only) {
       HIPCHECK(h, hipSetDevice(h->device));
@@ -1009,7 +1087,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   // weights
   h->s_wqkv = (size_t)H * h->qkv_dim;
   h->s_wo = (size_t)h->q_dim * H;
-  h->s_wr = (size_t)H * h->e_pad;
+  h->s_wr = c.dense ? 0 : (size_t)H * h->e_pad;
   h->s_wgu_e = (size_t)H * 2 * F;
   h->s_wgu_l = h->s_wgu_e * E;
   h->s_wd_e = (size_t)F * H;
@@ -1023,6 +1101,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   const size_t o_emb = take((size_t)V * H), o_gamma = take((size_t)(L + 1) * H), o_wlm = take((size_t)H * V);
   const size_t o_wqkv = take(h->s_wqkv * L), o_wo = take(h->s_wo * L), o_wr = take(h->s_wr * L);
   const size_t o_wgu = take(h->s_wgu_l * L), o_wd = take(h->s_wd_l * L);
+  const size_t o_gamma2 = take(c.dense ? (size_t)L * H : 0);
   if (hipMalloc(&h->w_all, off * 2) != hipSuccess)
     return fail(nullptr, MK_ERR_OOM, "cannot allocate %.1f GB of weights", off * 2 / 1e9);
   h->emb = h->w_all + o_emb;
@@ -1033,6 +1112,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->wr = h->w_all + o_wr;
   h->wgu = h->w_all + o_wgu;
   h->wd = h->w_all + o_wd;
+  h->gamma2 = c.dense ? h->w_all + o_gamma2 : nullptr;
   h->kv_bytes = kv_want;
   if (kv_pool) {
     h->kv = (uint16_t*)kv_pool;
@@ -1089,7 +1169,6 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   y.err = stake(16);
   const size_t scratch_bytes = so;
   // counters: capacity for the largest batch
-  h->n_ctr_cap = (L + 2) + L * (KVH + Bm * KVH + KVH + 5 + E + h->NB + 1);
   y.ctr = stake((size_t)h->n_ctr_cap * 4);
   y.total = so;
   if (hipMalloc(&h->scratch, scratch_bytes) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "scratch");
@@ -1142,22 +1221,45 @@ void mk_destroy(mk_handle* h) {
   delete h;
 }
 
+// A layer's attention norm gain, QKV and O projections into the library's copy.
+static mk_status load_attention(mk_handle* h, int layer, const void* gamma, const void* wqkv, const void* wo,
+                                hipStream_t s) {
+  const int H = h->cfg.hidden;
+  HIPCHECK(h, hipMemcpyAsync(h->gamma + (size_t)layer * H, gamma, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wqkv, h->wqkv + layer * h->s_wqkv, H, h->qkv_dim, h->qkv_dim, 0, 1,
+                               1, 0, 0, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wo, h->wo + layer * h->s_wo, h->q_dim, H, H, 0, 1, 1, 0, 0, s));
+  return MK_OK;
+}
+
+// A layer's expert (or dense FFN: one expert) gate, up and down matrices:
+// gate and up panels interleaved (gate panel j -> 2j, up panel j -> 2j+1).
+static mk_status load_ffn(mk_handle* h, int layer, const void* wg, const void* wu, const void* wd, hipStream_t s) {
+  const int H = h->cfg.hidden, E = h->cfg.n_experts, F = h->cfg.expert_ffn;
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wg, h->wgu + layer * h->s_wgu_l, H, F, F, 0, 2, E, (size_t)H * F,
+                               h->s_wgu_e, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wu, h->wgu + layer * h->s_wgu_l, H, F, F, 1, 2, E, (size_t)H * F,
+                               h->s_wgu_e, s));
+  HIPCHECK(h, mk_launch_repack((const uint16_t*)wd, h->wd + layer * h->s_wd_l, F, H, H, 0, 1, E, (size_t)F * H,
+                               h->s_wd_e, s));
+  return MK_OK;
+}
+
 mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* wqkv, const void* wo, const void* wr,
                         const void* wg, const void* wu, const void* wd, void* stream) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
   const mk_config& c = h->cfg;
   if (layer < 0 || layer >= c.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (c.dense) return fail(h, MK_ERR_INVALID_ARG, "a dense model's layers load with mk_load_layer_dense");
   if (!gamma || !wqkv || !wo || !wr || !wg || !wu || !wd) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
   for (const void* p : {gamma, wqkv, wo, wr, wg, wu, wd})
     if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   HIPCHECK(h, hipSetDevice(h->device));
-  const int H = c.hidden, E = c.n_experts, F = c.expert_ffn;
-  HIPCHECK(h, hipMemcpyAsync(h->gamma + (size_t)layer * H, gamma, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
-  HIPCHECK(h, mk_launch_repack((const uint16_t*)wqkv, h->wqkv + layer * h->s_wqkv, H, h->qkv_dim, h->qkv_dim, 0, 1,
-                               1, 0, 0, s));
-  HIPCHECK(h, mk_launch_repack((const uint16_t*)wo, h->wo + layer * h->s_wo, h->q_dim, H, H, 0, 1, 1, 0, 0, s));
+  const int H = c.hidden, E = c.n_experts;
+  mk_status st = load_attention(h, layer, gamma, wqkv, wo, s);
+  if (st != MK_OK) return st;
   if (h->e_pad == E) {
     HIPCHECK(h, mk_launch_repack((const uint16_t*)wr, h->wr + layer * h->s_wr, H, E, E, 0, 1, 1, 0, 0, s));
   } else {
@@ -1170,13 +1272,30 @@ mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* 
     HIPCHECK(h, mk_launch_repack(tmp, h->wr + layer * h->s_wr, H, h->e_pad, h->e_pad, 0, 1, 1, 0, 0, s));
     HIPCHECK(h, hipFreeAsync(tmp, s));
   }
-  // gate and up panels interleaved: gate panel j -> 2j, up panel j -> 2j+1
-  HIPCHECK(h, mk_launch_repack((const uint16_t*)wg, h->wgu + layer * h->s_wgu_l, H, F, F, 0, 2, E, (size_t)H * F,
-                               h->s_wgu_e, s));
-  HIPCHECK(h, mk_launch_repack((const uint16_t*)wu, h->wgu + layer * h->s_wgu_l, H, F, F, 1, 2, E, (size_t)H * F,
-                               h->s_wgu_e, s));
-  HIPCHECK(h, mk_launch_repack((const uint16_t*)wd, h->wd + layer * h->s_wd_l, F, H, H, 0, 1, E, (size_t)F * H,
-                               h->s_wd_e, s));
+  st = load_ffn(h, layer, wg, wu, wd, s);
+  if (st != MK_OK) return st;
+  h->layer_loaded[layer] = true;
+  return MK_OK;
+}
+
+mk_status mk_load_layer_dense(mk_handle* h, int layer, const void* gamma, const void* wqkv, const void* wo,
+                              const void* gamma2, const void* wg, const void* wu, const void* wd, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  const mk_config& c = h->cfg;
+  if (!c.dense) return fail(h, MK_ERR_INVALID_ARG, "not a dense model: load layers with mk_load_layer");
+  if (layer < 0 || layer >= c.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!gamma || !wqkv || !wo || !gamma2 || !wg || !wu || !wd) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  for (const void* p : {gamma, wqkv, wo, gamma2, wg, wu, wd})
+    if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(h, hipSetDevice(h->device));
+  mk_status st = load_attention(h, layer, gamma, wqkv, wo, s);
+  if (st != MK_OK) return st;
+  HIPCHECK(h, hipMemcpyAsync(h->gamma2 + (size_t)layer * c.hidden, gamma2, (size_t)c.hidden * 2,
+                             hipMemcpyDeviceToDevice, s));
+  st = load_ffn(h, layer, wg, wu, wd, s);
+  if (st != MK_OK) return st;
   h->layer_loaded[layer] = true;
   return MK_OK;
 }
@@ -1200,12 +1319,16 @@ mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f, co
 
 mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
   if (!h || !w) return MK_ERR_INVALID_ARG;
-  if (!w->gamma || !w->wqkv || !w->wo || !w->wr || !w->wg || !w->wu || !w->wd)
+  const bool dense = h->cfg.dense != 0;
+  if (!w->gamma || !w->wqkv || !w->wo || !(dense ? w->gamma2 : w->wr) || !w->wg || !w->wu || !w->wd)
     return fail(h, MK_ERR_INVALID_ARG, "null per-layer pointer array");
   mk_status st = mk_load_globals(h, w->emb, w->gamma_f, w->wlm, stream);
   if (st != MK_OK) return st;
   for (int l = 0; l < h->cfg.n_layers; ++l) {
-    st = mk_load_layer(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->wr[l], w->wg[l], w->wu[l], w->wd[l], stream);
+    st = dense ? mk_load_layer_dense(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->gamma2[l], w->wg[l], w->wu[l],
+                                     w->wd[l], stream)
+               : mk_load_layer(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->wr[l], w->wg[l], w->wu[l], w->wd[l],
+                               stream);
     if (st != MK_OK) return st;
   }
   return MK_OK;
@@ -1267,6 +1390,8 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.e_pad = h->e_pad;
   P.emb = h->emb;
   P.gamma = h->gamma;
+  P.gamma2 = h->gamma2;
+  P.dense = h->cfg.dense;
   P.wqkv = h->wqkv;
   P.s_wqkv = h->s_wqkv;
   P.wo = h->wo;

@@ -31,6 +31,7 @@
 // slices of the active experts' hidden layer through up/gate, SiLU and down,
 // and stores one partial output row per token it saw; residual tasks sum them.
 #define MK_FUSED_B 4
+#define MK_MAX_DENSE_F 8192 // widest dense FFN
 #define MK_TASK_INTS 32
 // Static scratch of the allocation-free step: its size bounds the per-step
 // scratch (and counters) of the models it accepts; the full-size model needs
@@ -38,9 +39,11 @@
 #define MK_STATIC_SCRATCH_BYTES (64u << 20)
 #define MK_MAX_DEVICES 64
 
-// Opcodes. The post names sixteen opcodes for its model family; this model
-// (no dense FFN) uses the ones below. MOE_GATHER is folded into the expert
-// up/gate task (it reads the routed token rows directly), MOE_COMBINE into
+// Opcodes. The post names sixteen opcodes for its model family; the ones
+// below cover it. A dense layer's FFN (FFN_UPGATE_ACT, FFN_DOWN) runs as the
+// fused claimer over its one FFN (MOE_FUSED with a fixed route). MOE_GATHER
+// is folded into the expert up/gate task (it reads the routed token rows
+// directly), MOE_COMBINE into
 // the residual + RMSNorm step (it sums each token's k expert outputs in rank
 // order while forming the residual), ROUTER_TOPK and ROUTE_FINALIZE into the
 // last router task, ATTN_COMBINE into the last attention split, and the
@@ -50,7 +53,8 @@ enum mk_opcode : int32_t {
   MK_OP_EMBED = 1,        // embedding rows of one column block: layer 0's input
   MK_OP_QKV = 2,          // QKV panels + RoPE + paged KV append
   MK_OP_ATTN = 3,         // split-KV partial attention (+ combine when last)
-  MK_OP_RESIDUAL = 4,     // residual + MoE combine of one column block, the next layer's input (fused MoE)
+  MK_OP_RESIDUAL = 4,     // residual + MoE combine of one column block, the next layer's input (fused MoE;
+                          // for a dense layer also the mid point: h + attention, the FFN's input)
   MK_OP_OPROJ = 5,        // O projection, split-K by kv group, one column block (+ residual when last)
   MK_OP_ROUTER = 6,       // router logits over a K range (+ top-k / finalize when last)
   MK_OP_MOE_UP = 8,       // MoE claimer: (expert, gate/up panel pair, K half) items, then
@@ -60,6 +64,15 @@ enum mk_opcode : int32_t {
   MK_OP_LMHEAD = 10,      // LM head panels + argmax candidate (+ greedy token when last)
   MK_OP_COUNT = 11
 };
+
+// Residual modes (a[1] of MK_OP_RESIDUAL): a parallel layer's end (O
+// projection partials and the fused MoE claimers' rows; the next layer's
+// input), a dense layer's mid point (O projection partials; the FFN's input
+// with gamma2), a dense layer's end (the FFN claimers' rows; the next
+// layer's input).
+#define MK_RES_PARALLEL 0
+#define MK_RES_DENSE_MID 1
+#define MK_RES_DENSE_FFN 2
 
 struct mk_task {
   int32_t op;
@@ -100,6 +113,8 @@ struct mk_params {
   // packed weights (bf16 bit patterns)
   const uint16_t* emb;           // [V][H] row-major
   const uint16_t* gamma;         // [L+1][H]
+  const uint16_t* gamma2;        // dense models: [L][H] the FFN's norm gains
+  int32_t dense;                 // 1: sequential dense layers (attention, then the FFN)
   const uint16_t* wqkv; size_t s_wqkv;      // per layer: panel-tiled [H x QKV]
   const uint16_t* wo; size_t s_wo;          // per layer: panel-tiled [QH*D x H]
   const uint16_t* wr; size_t s_wr;          // per layer: panel-tiled [H x e_pad]

@@ -7,7 +7,8 @@ bandwidth (its example: 6.6 GB of active weights plus 0.5 GB of KV at 8K on a
 step of the model actually decoded:
 
   per layer: QKV, O and router weights, the RMSNorm gain, the weights of each
-  distinct expert the step routes to (gate, up and down), the KV read by each
+  distinct expert the step routes to (gate, up and down; a dense layer: its
+  second gain and its one FFN instead of router and experts), the KV read by each
   sequence (all positions for full-attention layers, at most the window for
   the others, the current token included), and the current token's K/V append;
   once: the LM head, the final gain, per sequence one embedding row and the
@@ -22,7 +23,12 @@ MI355X_HBM_BYTES_PER_S = 8.0e12
 
 
 def layer_weight_bytes(m) -> int:
+    """Per layer: QKV and O projections and the norm gain; the router (MoE
+    layers) or the second norm gain (dense layers). Expert or FFN weights are
+    counted by step_bytes."""
     H = m.hidden
+    if getattr(m, "dense", False):
+        return 2 * (H * m.qkv_dim + m.q_dim * H + 2 * H)
     return 2 * (H * m.qkv_dim + m.q_dim * H + H * m.n_experts + H)
 
 
@@ -36,7 +42,8 @@ def kv_bytes_per_token(m) -> int:
 
 def step_bytes(m, seq_lens: Sequence[int], n_active: Sequence[int]) -> int:
     """Algorithmic bytes of one step: seq_lens count the decoded token;
-    n_active[l] = distinct experts routed to at layer l."""
+    n_active[l] = distinct experts routed to at layer l (1 for a dense
+    layer's FFN)."""
     B = len(seq_lens)
     kvt = kv_bytes_per_token(m)
     total = 0

@@ -299,3 +299,37 @@ def test_stream_read_rejects_bad_buffers_on_the_host():
     assert lib.mk_stream_read(ctypes.c_void_p(4099), 64, None) == 1
     assert lib.mk_stream_read(ctypes.c_void_p(4096), 40, None) == 1
     assert lib.mk_stream_read(None, 64, None) == 1
+
+
+@pytest.mark.parametrize("model", ["tiny_dense", "llama1b"])
+@pytest.mark.parametrize("batch", [1, 2, 4])
+def test_dense_schedule_simulates(model, batch):
+    """A dense model's per-CU lists (QKV, attention, O projection, the mid
+    residual, the FFN over every unit, the final residual) run to completion
+    on the host model with every counter at its expected count; no router."""
+    m = configs.TINY_DENSE if model == "tiny_dense" else configs.LLAMA1B
+    d = _host(m, batch=batch, max_seq=8192 + 64)
+    t, off = d.schedule_export(batch, 8192)
+    ops = np.bincount(t[:, 0], minlength=11)
+    assert ops[6] == 0 and ops[8] == 0                       # no router, no claiming MoE
+    assert ops[9] == 256 * m.n_layers                         # one FFN claimer per unit and layer
+    assert ops[4] == 2 * (m.hidden // (64 if m.hidden >= 1024 else 32)) * m.n_layers  # two residuals per block
+    res = t[t[:, 0] == 4]
+    assert sorted(set(res[:, 3].tolist())) == [1, 2]          # mid and final residual modes
+    for seed in range(2):
+        st, msg = d.simulate(batch, 8192, [1] * m.n_layers, seed=seed)
+        assert st == 0, msg
+    d.close()
+
+
+def test_dense_config_limits():
+    import moe_persistent_decode_amd as mk
+    from moe_persistent_decode_amd.binding import Decoder, MkError
+    m = configs.TINY_DENSE
+    for kw, bad in ((dict(max_batch=5), "at most"), (dict(n_experts=2), "n_experts"),
+                    (dict(expert_ffn=8320), "FFN width")):
+        cfg = mk.make_config(m, kw.get("max_batch", 1), 1024, 64, 64, 0)
+        for k, v in kw.items():
+            setattr(cfg, k, v)
+        with pytest.raises(MkError, match=bad):
+            Decoder(cfg, host_only_cus=256)

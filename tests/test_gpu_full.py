@@ -80,7 +80,7 @@ class FullCase:
         w = gen.make_layer_weights(self.m, l, self.wl.seed_weights, "cuda")
         if l in self.repaired:
             w[f"wr.{l}"] = bits_to_torch(self.repaired[l])
-        self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.LAYER_KINDS))
+        self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.layer_kinds(self.m)))
         torch.cuda.synchronize()
 
     def oracle_step(self, tokens, lens, record=True):
@@ -112,11 +112,11 @@ class FullCase:
                     f"ref={int(ref_tok[b])} (gap {gaps[b]:.3f})")
             assert ok, (s, b, mx, rl2)
             assert int(tok[b]) == int(ref_tok[b]), (s, b, float(gaps[b]))
-            for l in range(self.m.n_layers):
+            for l in range(0 if self.m.dense else self.m.n_layers):  # (a dense model routes nothing)
                 assert sorted(route[l, b].tolist()) == sorted(tr_ref.topk_idx[l][b].tolist()), (s, b, l)
         say(f"  step {s}: {lg.shape[0]} rows, worst logits max|d|={worst[0]:.2e} relL2={worst[1]:.2e}, every "
-            f"greedy token and {self.m.n_layers} layers' top-k equal; repaired router layers {len(self.repaired)}, "
-            f"LM-head repairs {self.lm_state['repairs']}")
+            f"greedy token{'' if self.m.dense else f' and {self.m.n_layers} layers top-k'} equal; repaired router "
+            f"layers {len(self.repaired)}, LM-head repairs {self.lm_state['repairs']}")
 
     def check_kv(self, lens_per_step):
         gpu = torch_to_bits(self.pool)
