@@ -2092,7 +2092,7 @@ __device__ __forceinline__ void atile_lds(ATile<1, NCH>& A, const uint16_t* xs, 
   }
 }
 
-template <int NJ, int NCH>
+template <int NJ, int NCH, bool DENSE>
 __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& t, Smem& sm) {
   const int sk = t.b[0], nf = t.b[1], nt = t.b[2], wa = P.waits_enabled ? t.b[3] : 256;
   const int l = t.layer;
@@ -2104,6 +2104,35 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   // current slice's weighted hidden values [MK_FUSED_B][16] (float)
   uint16_t* xs = sm.act;
   float* actf = reinterpret_cast<float*>(sm.act + 2 * MK_FUSED_B * MK_MAX_H);
+  // the items' weights: an item past the share reads nothing; a dense
+  // layer's one FFN is expert 0
+  int lo = 0, hi = 0;
+  auto expert_of = [&](int a) { return DENSE ? 0 : __builtin_amdgcn_readfirstlane(sm.rt_e[a]); };
+  auto up_load = [&](WTile<2, NCH>& w, int id, int kh) {
+    const bool valid = id < hi;
+    const int a = valid ? id / S : 0, s = id % S;
+    const int e = expert_of(a);
+    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * s) * pstride, pstride, valid ? 2 : 0,
+               kh * kh_chunks, (kh + 1) * kh_chunks);
+  };
+  auto down_load = [&](DTile<NJ>& d, int id) {
+    const bool valid = id < hi;
+    const int a = valid ? id / S : 0, s = id % S;
+    const int e = expert_of(a);
+    dtile_load(d, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e, pstride_d, H / 16, s, valid);
+  };
+  WTile<2, NCH> wu0, wu1;
+  DTile<NJ> wdn;
+  // A dense layer's FFN and this claimer's share of its slices are known
+  // before the input is: the first slice's three weight units stream before
+  // the wait (weight prefetch, megakernel post section "Where the speedup
+  // comes from"). An expert's weights wait for the route.
+  if constexpr (DENSE) {
+    fused_share(sk, nf, nt, wa, S, lo, hi);
+    up_load(wu0, lo, 0);
+    up_load(wu1, lo, 1);
+    down_load(wdn, lo);
+  }
   // the layer input and the router's partial logits complete (one wait):
   // the input's loads, then this claimer's own top-k and route (whose loads
   // share the input's round trip), then the input into LDS
@@ -2119,7 +2148,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
       vh[k] = i < n8 ? Uh.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
       vl[k] = i < n8 ? Ul.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    if (P.dense)
+    if constexpr (DENSE)
       route_trivial(P, l, sm, true);
     else
       route_build(P, l, sm, false);
@@ -2136,22 +2165,13 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   const uint16_t* xh = xs;
   const uint16_t* xl = xs + MK_FUSED_B * MK_MAX_H;
   mark(sm, 1);
-  const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) * S;
-  int lo, hi;
-  fused_share(sk, nf, nt, wa, n_items, lo, hi);
-  auto up_load = [&](WTile<2, NCH>& w, int id, int kh) {
-    const bool valid = id < hi;
-    const int a = valid ? id / S : 0, s = id % S;
-    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * s) * pstride, pstride, valid ? 2 : 0,
-               kh * kh_chunks, (kh + 1) * kh_chunks);
-  };
-  auto down_load = [&](DTile<NJ>& d, int id) {
-    const bool valid = id < hi;
-    const int a = valid ? id / S : 0, s = id % S;
-    const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    dtile_load(d, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e, pstride_d, H / 16, s, valid);
-  };
+  if constexpr (!DENSE) {
+    const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) * S;
+    fused_share(sk, nf, nt, wa, n_items, lo, hi);
+    up_load(wu0, lo, 0);
+    up_load(wu1, lo, 1);
+    down_load(wdn, lo);
+  }
   float acc[NJ][MK_FUSED_B];
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
@@ -2160,12 +2180,6 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   {
     // one item's three weight units in flight while the previous item's
     // compute: each unit is reissued for the next item as soon as it is used
-    // (an item past the share reads nothing)
-    WTile<2, NCH> wu0, wu1;
-    DTile<NJ> wdn;
-    up_load(wu0, lo, 0);
-    up_load(wu1, lo, 1);
-    down_load(wdn, lo);
     const int rh = (lane_id() >> 4) & 1;
     for (int id = lo; id < hi; ++id) {
       const int a = id / S;
@@ -2586,7 +2600,14 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
         op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
       break;
     case MK_OP_MOE_FUSED:
-      if (MT == 1) op_moe_fused<2048 / 256, 32 / MK_WAVES>(P, t, sm);
+      // (a dense layer's FFN has its own instance: its weight prefetch before
+      // the wait keeps tiles live there, which the experts' instance does not)
+      if (MT == 1) {
+        if (P.dense)
+          op_moe_fused<2048 / 256, 32 / MK_WAVES, true>(P, t, sm);
+        else
+          op_moe_fused<2048 / 256, 32 / MK_WAVES, false>(P, t, sm);
+      }
       break;
     case MK_OP_RESIDUAL:
       if (MT == 1) op_residual(P, t, sm);

@@ -14,9 +14,10 @@ import os
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # instantiation (head dim, row tiles) -> most VGPR spills allowed; SGPR spills
-# (to VGPR lanes, no memory traffic) are bounded loosely
+# (to VGPR lanes, no memory traffic; the dense FFN claimer's own instance
+# roughly doubles them) are bounded loosely
 VGPR_SPILLS = {(64, 1): 4, (64, 2): 3, (128, 1): 4, (128, 2): 3}
-SGPR_SPILLS_MAX = 200
+SGPR_SPILLS_MAX = 350
 
 
 def _build_module():
