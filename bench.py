@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--ablation", default=None, metavar="PATH",
                     help="instead of the benchmark line: time every wave order and placement of the scheduler "
                          "at batch 1, 2 and 4 (48 layers, 8K) and write the table (markdown) to PATH")
+    ap.add_argument("--search", default=None, metavar="PATH",
+                    help="time the cost-model and random placements against tuned and round-robin; write a table")
+    ap.add_argument("--search-workloads", default="llama1b_b1_8k,full48_b1_8k")
+    ap.add_argument("--search-candidates", type=int, default=200)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference for HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "megakernel_traffic.json"),
@@ -390,6 +394,93 @@ def ablation(path, steps, warmup):
     log(f"[ablation] table written to {path}")
 
 
+def search(path, workloads, n_random, steps, warmup):
+    """The other schedulers of the megakernel post (Chinese version, section
+    on the schedulers it tried): a greedy cost-model placement and a
+    brute-force search over seeded random placements, against round-robin
+    and the tuned placement. Every candidate is timed for `steps` steps; the
+    five fastest random candidates, the cost model, round-robin and tuned are
+    then timed again, interleaved, for four times as many steps (the first
+    round's winner is biased upward by the selection). Each candidate's logits
+    on one step from the initial state are compared with the tuned one's."""
+    import numpy as np
+    import torch
+
+    import moe_persistent_decode_amd as mk
+    from mkinputs import configs
+    lines = ["# Schedule search: cost-model and random placements", "",
+             "Command (from the repository root on the MI355X box):", "", "```",
+             f"python3 bench.py --search {os.path.basename(path)} --search-workloads {','.join(workloads)} "
+             f"--search-candidates {n_random} --steps {steps} --warmup {warmup}", "```", "",
+             f"{n_random} random candidates (every wave over a seeded random permutation of the units) and the "
+             "greedy cost-model placement (static tasks on the unit where a bytes-and-hops model says they finish "
+             f"first), timed for {steps} steps each after {warmup} warm-up steps; the five fastest random "
+             f"candidates, the cost model, round-robin and tuned then re-timed, interleaved, for {4 * steps} steps, "
+             "three times (median shown). Logits of one step from the initial state against tuned's.", ""]
+    for name in workloads:
+        wl = configs.WORKLOADS[name]
+        cands = [("tuned", mk.PLACE_TUNED, 0), ("round-robin", mk.PLACE_ROUND_ROBIN, 0),
+                 ("cost model", mk.PLACE_COST_MODEL, 0)] + [(f"random {s}", mk.PLACE_RANDOM, s)
+                                                            for s in range(1, n_random + 1)]
+        runs = len(cands) + 3 * 8 * 4 + 2
+        r = Run(wl, steps, warmup, runs)
+        tok0, len0 = r.tokens.clone(), r.seq_lens.clone()
+
+        def use(pl, seed):
+            r.dec.set_schedule_options(0, pl)
+            r.dec.set_placement_seed(seed if seed else 1)
+
+        def logits_now():
+            t_, l_ = r.tokens.clone(), r.seq_lens.clone()
+            r.tokens.copy_(tok0)
+            r.seq_lens.copy_(len0)
+            r.dec.step(r.tokens, r.bt, r.seq_lens, r.hint + r.done, r.logits, stream=r.stream)
+            r.dec.sync(r.stream)
+            lg = r.logits.cpu().numpy()
+            r.tokens.copy_(t_)
+            r.seq_lens.copy_(l_)
+            return lg
+
+        first = {}
+        base = None
+        for label, pl, seed in cands:
+            use(pl, seed)
+            ms, _ = r.timed(mk.MODE_MEGAKERNEL)
+            lg = logits_now()
+            if base is None:
+                base = lg
+            first[label] = (ms / r.K, float(np.abs(lg - base).max()),
+                            bool(np.array_equal(np.argmax(lg, -1), np.argmax(base, -1))))
+        log(f"[search] {name}: " + ", ".join(f"{k} {v[0]:.3f}" for k, v in list(first.items())[:4]) + " ms ...")
+        rand = sorted((k for k in first if k.startswith("random")), key=lambda k: first[k][0])[:5]
+        final = ["tuned", "round-robin", "cost model"] + rand
+        spec = {lab: (pl, sd) for lab, pl, sd in cands}
+        K0, r.K = r.K, 4 * steps
+        again = {k: [] for k in final}
+        for _ in range(3):
+            for k in final:
+                use(*spec[k])
+                ms, _ = r.timed(mk.MODE_MEGAKERNEL)
+                again[k].append(ms / r.K)
+        r.K = K0
+        r.close()
+        med = {k: float(np.median(v)) for k, v in again.items()}
+        rr = med["round-robin"]
+        allr = sorted(first[k][0] for k in first if k.startswith("random"))
+        lines += [f"## {name} (batch {wl.batch})", "",
+                  f"Random candidates, first round: best {allr[0]:.3f} ms, median {allr[len(allr) // 2]:.3f} ms, "
+                  f"worst {allr[-1]:.3f} ms per step.", "",
+                  "| placement | ms/step (re-timed, median of 3) | tok/s | vs round-robin | vs tuned | first round ms | "
+                  "max abs logit diff vs tuned | greedy equal |", "|---|---:|---:|---:|---:|---:|---:|---|"]
+        for k in final:
+            lines.append(f"| {k} | {med[k]:.3f} | {wl.batch / (med[k] / 1e3):.1f} | {rr / med[k] - 1:+.1%} | "
+                         f"{med['tuned'] / med[k] - 1:+.1%} | {first[k][0]:.3f} | {first[k][1]:.1e} | {first[k][2]} |")
+        lines.append("")
+        log(f"[search] {name}: re-timed " + ", ".join(f"{k} {v:.3f}" for k, v in med.items()))
+    open(path, "w").write("\n".join(lines) + "\n")
+    log(f"[search] table written to {path}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -402,6 +493,9 @@ def main():
     torch.cuda.set_device(0)
     if args.ablation:
         ablation(args.ablation, args.steps, args.warmup)
+        return
+    if args.search:
+        search(args.search, args.search_workloads.split(","), args.search_candidates, args.steps, args.warmup)
         return
     wl = configs.WORKLOADS[args.workload]
     res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace, args.op_trace_raw)

@@ -251,13 +251,28 @@ mk_status mk_set_routing_trace(mk_handle* h, int32_t* trace);
  *                                    unit of a QKV task it waits for and each
  *                                    residual task on the unit of its column
  *                                    block's first O projection
+ *               MK_PLACE_COST_MODEL  the claimers as tuned; every other task,
+ *                                    in list order, on the unit where a cost
+ *                                    model (bytes streamed per unit, a hop per
+ *                                    dependency) says it finishes first (the
+ *                                    greedy scheduler of the post's section on
+ *                                    the other schedulers it tried)
+ *               MK_PLACE_RANDOM      every wave over a random permutation of
+ *                                    the units, seeded by mk_set_placement_seed
+ *                                    (one candidate of that section's
+ *                                    brute-force search)
  * Every combination decodes the same step (only timing and, in the fused MoE
  * of at most 4 tokens, the grouping of the claimers' partial sums change).
  * Drops the cached schedules (synchronises the device); no step may be in
  * flight on another stream. MK_ERR_INVALID_ARG for an unknown value. */
 enum { MK_ORDER_SHIPPED = 0, MK_ORDER_QKV_FIRST = 1, MK_ORDER_ATTENTION_FIRST = 2 };
-enum { MK_PLACE_TUNED = 0, MK_PLACE_ROUND_ROBIN = 1, MK_PLACE_AFFINITY = 2 };
+enum { MK_PLACE_TUNED = 0, MK_PLACE_ROUND_ROBIN = 1, MK_PLACE_AFFINITY = 2, MK_PLACE_COST_MODEL = 3,
+       MK_PLACE_RANDOM = 4 };
 mk_status mk_set_schedule_options(mk_handle* h, int wave_order, int placement);
+
+/* The seed of MK_PLACE_RANDOM's candidate (default 1). Drops the cached
+ * schedules like mk_set_schedule_options. */
+mk_status mk_set_placement_seed(mk_handle* h, uint64_t seed);
 
 /* Time limit of one dependency wait on the device, in microseconds (0: the
  * default, 2 s). A wait that exceeds it sets the device error word

@@ -20,14 +20,14 @@ STATUS = {0: "MK_OK", 1: "MK_ERR_INVALID_ARG", 2: "MK_ERR_UNSUPPORTED", 3: "MK_E
 MODE_MEGAKERNEL = 0
 MODE_KERNEL_PER_OP = 1
 ORDER_SHIPPED, ORDER_QKV_FIRST, ORDER_ATTENTION_FIRST = 0, 1, 2
-PLACE_TUNED, PLACE_ROUND_ROBIN, PLACE_AFFINITY = 0, 1, 2
+PLACE_TUNED, PLACE_ROUND_ROBIN, PLACE_AFFINITY, PLACE_COST_MODEL, PLACE_RANDOM = 0, 1, 2, 3, 4
 STEP_ADVANCE = 1
 
 # every function include/mk.h declares
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_dense", "mk_load_globals",
            "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
-           "mk_set_schedule_options", "mk_decode_step_noalloc",
+           "mk_set_schedule_options", "mk_set_placement_seed", "mk_decode_step_noalloc",
            "mk_service_create", "mk_service_pause", "mk_service_resume", "mk_service_alloc_pages",
            "mk_service_admit", "mk_service_evict", "mk_service_stats", "mk_service_last_error",
            "mk_service_destroy",
@@ -84,6 +84,7 @@ def _load():
     lib.mk_decode_step_noalloc.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
     lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
+    lib.mk_set_placement_seed.argtypes = [H, ctypes.c_uint64]
     lib.mk_set_schedule_options.argtypes = [H, I, I]
     lib.mk_kv_cache.argtypes = [H, I, ctypes.POINTER(P), ctypes.POINTER(S)]
     lib.mk_stream_read.argtypes = [P, S, P]
@@ -235,6 +236,10 @@ class Decoder:
     def set_schedule_options(self, wave_order: int = 0, placement: int = 0):
         """Wave order (ORDER_*) and placement (PLACE_*) of later steps' schedules."""
         self._check(lib.mk_set_schedule_options(self._h, int(wave_order), int(placement)))
+
+    def set_placement_seed(self, seed: int):
+        """The seed of PLACE_RANDOM's candidate placement."""
+        self._check(lib.mk_set_placement_seed(self._h, ctypes.c_uint64(int(seed))))
 
     def set_wait_limit(self, microseconds: int):
         self._check(lib.mk_set_wait_limit(self._h, int(microseconds)))

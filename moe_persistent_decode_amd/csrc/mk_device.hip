@@ -2328,17 +2328,19 @@ __device__ __forceinline__ void op_residual(const mk_params& P, const mk_task& t
   const int H = P.H, CB = P.CB, B = P.B, n = B * CB;
   const int S = P.F / 16;
   const int i = tid();
-  // the block's gain: the next layer's (the dense FFN's after attention); the
-  // residual stream now when it was written before this layer began (parallel
-  // layers), else after the wait (a dense layer's mid residual wrote it)
+  // the block's gain: the next layer's (the dense FFN's after attention)
   float h0 = 0.f, g0 = 0.f;
   if (i < n) {
-    const int b = i / CB, c = cb * CB + i % CB;
-    if (mode == MK_RES_PARALLEL) h0 = Pub(P.h).ldf(b * H + c);
+    const int c = cb * CB + i % CB;
     g0 = bf2f(mode == MK_RES_DENSE_MID ? P.gamma2[(size_t)l * H + c] : P.gamma[(size_t)(l + 1) * H + c]);
   }
   if (mode == MK_RES_PARALLEL) {
     if (!wait_one(P, t.wait_ctr[1], t.wait_tgt[1], sm)) return;
+    // The route is published by a task that waited for this layer's input,
+    // so from here on the residual stream is the one this layer began with.
+    // (Not before: nothing earlier on this unit need have waited for the
+    // previous layer's residual tasks, which write it.)
+    if (i < n) h0 = Pub(P.h).ldf((i / CB) * H + cb * CB + i % CB);
     route_load(P, l, sm);
   } else if (mode == MK_RES_DENSE_FFN) {
     route_trivial(P, l, sm, false);

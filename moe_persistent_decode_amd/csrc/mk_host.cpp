@@ -112,6 +112,7 @@ struct mk_handle {
   bool static_used = false;        // an allocation-free step ran (its error word is checked too)
   int wave_order = MK_ORDER_SHIPPED;
   int placement = MK_PLACE_TUNED;
+  uint64_t place_seed = 1;  // MK_PLACE_RANDOM's seed
   int device = 0;
   bool host_only = false;
   int n_cu = 0;       // compute units
@@ -296,6 +297,121 @@ int splits_for(const mk_handle* h, int l, int len, int pps) {
 
 int bucket_of(int hint) { return ceil_div(hint, 256) * 256; }
 
+// ------------------------------------------------------------ placements
+// Two of the schedulers the megakernel post tried before settling on
+// round-robin with tuned wave orders (Chinese version, section on the other
+// schedulers it tried): a greedy scheduler that estimates each task's cost
+// from the memory it reads, and a brute-force search over random candidates.
+// Both re-place the tasks of a schedule built with the tuned rules (the
+// claimers' shares are computed there); neither changes what a task does, and
+// every list stays in flat order, so any placement decodes the same step and
+// cannot deadlock as long as the claimers of one wave sit on distinct units.
+
+static bool is_claimer(int op) { return op == MK_OP_ATTN || op == MK_OP_MOE_FUSED || op == MK_OP_MOE_UP; }
+
+// A candidate of the brute-force search: every wave's tasks over a seeded
+// random permutation of the units (task j of a wave on unit perm[j mod n], so
+// a wave's claimers stay on distinct units).
+void random_placement(const Schedule& S, std::vector<int>& flat_cu, int n_w, uint64_t seed) {
+  std::vector<int> perm(n_w);
+  for (size_t w = 0; w < S.waves.size(); ++w) {
+    std::mt19937_64 rng(seed * 0x9e3779b97f4a7c15ull + w);
+    for (int i = 0; i < n_w; ++i) perm[i] = i;
+    std::shuffle(perm.begin(), perm.end(), rng);
+    for (int k = S.waves[w].first; k < S.waves[w].second; ++k) flat_cu[k] = perm[(k - S.waves[w].first) % n_w];
+  }
+}
+
+// Bytes a task streams (weights, or keys and values), for the cost model.
+static double task_bytes(const mk_handle* h, const Schedule& S, const mk_task& t, int n_claimers) {
+  const mk_config& c = h->cfg;
+  const double H = c.hidden, panel_row = 16.0 * 2.0;  // a 16-column panel, bytes per row of K
+  switch (t.op) {
+    case MK_OP_QKV: return t.a[1] * panel_row * H;
+    case MK_OP_ROUTER: return t.a[1] * panel_row * (t.a[3] - t.a[2]) * 32.0;
+    case MK_OP_OPROJ: return (t.b[1] == 1 ? t.a[3] : 1) * h->CB * 2.0 * h->G * c.head_dim;
+    case MK_OP_LMHEAD: return (t.a[1] - t.a[0]) * panel_row * H;
+    case MK_OP_ATTN: {
+      const double items = (double)S.B * c.n_kv_heads * t.a[3];
+      return items / std::max(1, n_claimers) * t.a[4] * c.page_size * c.head_dim * 4.0;
+    }
+    case MK_OP_MOE_FUSED:
+    case MK_OP_MOE_UP: {
+      const double e_act = c.dense ? 1.0 : c.n_experts * (1.0 - std::pow(1.0 - (double)c.top_k / c.n_experts, S.B));
+      return e_act * 3.0 * H * c.expert_ffn * 2.0 / std::max(1, n_claimers);
+    }
+    default: return 0.0;
+  }
+}
+
+// The greedy scheduler: tasks in flat order, each static task on the unit
+// where it would finish first under a simple model -- a unit streams 25 GB/s
+// while every unit streams, a static task's weights stream before its
+// dependency wait, a dependency costs a hop of 4 us (a counter poll and a
+// data round trip) after its producers end, and a task's own work 1 us.
+// Claimers keep their units (their work is claimed at run time); their
+// expected share sets when their unit is free again.
+void cost_model_placement(const mk_handle* h, const Schedule& S, std::vector<int>& flat_cu, int n_w) {
+  constexpr double kBytesPerUs = 25.0e3, kHopUs = 4.0, kWorkUs = 1.0;
+  std::vector<double> cu_free(n_w, 0.0);
+  std::vector<std::vector<double>> arr(S.n_ctr);
+  // the time a counter reaches `tgt` arrivals (the tgt-th earliest), or its
+  // latest arrival when the model counted fewer
+  auto reach = [&](int ctr, int tgt) -> double {
+    std::vector<double>& v = arr[ctr];
+    if (v.empty() || tgt <= 0) return 0.0;
+    std::sort(v.begin(), v.end());
+    return v[std::min((size_t)tgt, v.size()) - 1];
+  };
+  // claimers per wave (their shares)
+  std::vector<int> wave_n(S.waves.size());
+  for (size_t w = 0; w < S.waves.size(); ++w) wave_n[w] = S.waves[w].second - S.waves[w].first;
+  const int KVH = h->cfg.n_kv_heads;
+  for (size_t k = 0; k < S.flat.size(); ++k) {
+    const mk_task& t = S.flat[k];
+    double ready = 0.0;
+    for (int i = 0; i < 3; ++i)
+      if (t.wait_ctr[i] >= 0) ready = std::max(ready, reach(t.wait_ctr[i], t.wait_tgt[i]));
+    const double load = task_bytes(h, S, t, wave_n[S.flat_wave[k]]) / kBytesPerUs;
+    const double dep = ready > 0.0 ? ready + kHopUs : 0.0;
+    int cu = flat_cu[k] >= 0 ? flat_cu[k] : (int)(k % n_w);
+    double end;
+    if (is_claimer(t.op)) {
+      end = std::max(cu_free[cu], dep) + load + kWorkUs;
+    } else {
+      double best = 1e300;
+      for (int c2 = 0; c2 < n_w; ++c2) {
+        const double e = std::max(cu_free[c2] + load, dep) + kWorkUs;
+        if (e < best - 1e-9) {
+          best = e;
+          cu = c2;
+        }
+      }
+      end = best;
+    }
+    flat_cu[k] = cu;
+    cu_free[cu] = end;
+    // arrivals: the task's signals and the counters its op counts on
+    for (int i = 0; i < 2; ++i)
+      if (t.sig_ctr[i] >= 0) arr[t.sig_ctr[i]].push_back(end);
+    switch (t.op) {
+      case MK_OP_OPROJ:
+        if (t.b[0] == 1) arr[t.a[2]].push_back(end);
+        break;
+      case MK_OP_ROUTER: arr[t.a[5]].push_back(end); break;
+      case MK_OP_LMHEAD: arr[t.a[3]].push_back(end); break;
+      case MK_OP_ATTN: {
+        // its share of the (sequence, group, split) items, spread over the groups
+        const int items = S.B * KVH * t.a[3], per = (items + wave_n[S.flat_wave[k]] - 1) / wave_n[S.flat_wave[k]];
+        for (int g = 0; g < KVH; ++g)
+          for (int j = 0; j < (per + KVH - 1) / KVH; ++j) arr[(t.b[0] == 1 ? t.a[5] : t.sig_ctr[0]) + g].push_back(end);
+        break;
+      }
+      default: break;
+    }
+  }
+}
+
 std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   const mk_config& c = h->cfg;
   auto S = std::make_unique<Schedule>();
@@ -391,7 +507,9 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   // per group and the O projection tasks merge them.
   const bool fused_all = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
   (void)fused_all;
-  const bool tuned = h->placement != MK_PLACE_ROUND_ROBIN;
+  // (a dense model's tuned placement is round-robin: the schedule search
+  // measured its other rules 6% slower on the dense workload)
+  const bool tuned = h->placement != MK_PLACE_ROUND_ROBIN && !(c.dense && h->placement == MK_PLACE_TUNED);
   const bool affinity = h->placement == MK_PLACE_AFFINITY;
   for (int l = 0; l < L; ++l) {
     const CtrIdx x = ci(l);
@@ -736,6 +854,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     push(t);
   }
 
+  if (h->placement == MK_PLACE_RANDOM) random_placement(*S, flat_cu, n_w, h->place_seed);
+  if (h->placement == MK_PLACE_COST_MODEL) cost_model_placement(h, *S, flat_cu, n_w);
   // per-workgroup lists in flat order (every wait is on an earlier task of
   // the flat list, so the lists cannot deadlock), placed as chosen above
   std::vector<std::vector<mk_task>> per(n_w);
@@ -1531,21 +1651,36 @@ mk_status mk_set_mode(mk_handle* h, int mode) {
   return MK_OK;
 }
 
-mk_status mk_set_schedule_options(mk_handle* h, int wave_order, int placement) {
-  if (!h) return MK_ERR_INVALID_ARG;
-  if (wave_order < MK_ORDER_SHIPPED || wave_order > MK_ORDER_ATTENTION_FIRST)
-    return fail(h, MK_ERR_INVALID_ARG, "unknown wave order %d", wave_order);
-  if (placement < MK_PLACE_TUNED || placement > MK_PLACE_AFFINITY)
-    return fail(h, MK_ERR_INVALID_ARG, "unknown placement %d", placement);
-  if (wave_order == h->wave_order && placement == h->placement) return MK_OK;
+static mk_status drop_schedules(mk_handle* h) {
   if (!h->host_only) {
     HIPCHECK(h, hipSetDevice(h->device));
     HIPCHECK(h, hipDeviceSynchronize());  // no step may still read the old lists
     for (auto& kv : h->scheds) free_schedule(kv.second.get());
   }
   h->scheds.clear();
+  return MK_OK;
+}
+
+mk_status mk_set_schedule_options(mk_handle* h, int wave_order, int placement) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (wave_order < MK_ORDER_SHIPPED || wave_order > MK_ORDER_ATTENTION_FIRST)
+    return fail(h, MK_ERR_INVALID_ARG, "unknown wave order %d", wave_order);
+  if (placement < MK_PLACE_TUNED || placement > MK_PLACE_RANDOM)
+    return fail(h, MK_ERR_INVALID_ARG, "unknown placement %d", placement);
+  if (wave_order == h->wave_order && placement == h->placement) return MK_OK;
+  mk_status st = drop_schedules(h);
+  if (st != MK_OK) return st;
   h->wave_order = wave_order;
   h->placement = placement;
+  return MK_OK;
+}
+
+mk_status mk_set_placement_seed(mk_handle* h, uint64_t seed) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (seed == h->place_seed) return MK_OK;
+  mk_status st = drop_schedules(h);
+  if (st != MK_OK) return st;
+  h->place_seed = seed;
   return MK_OK;
 }
 

@@ -253,7 +253,7 @@ def test_schedule_options_change_the_lists():
     with pytest.raises(mk.MkError):
         d.set_schedule_options(3, 0)
     with pytest.raises(mk.MkError):
-        d.set_schedule_options(0, 3)
+        d.set_schedule_options(0, 5)
     d.close()
 
 
@@ -333,3 +333,38 @@ def test_dense_config_limits():
             setattr(cfg, k, v)
         with pytest.raises(MkError, match=bad):
             Decoder(cfg, host_only_cus=256)
+
+
+@pytest.mark.parametrize("model,batch", [("full48", 1), ("full48", 4), ("full48", 8), ("full48", 32),
+                                         ("llama1b", 1), ("llama1b", 4)])
+def test_cost_model_and_random_placements_simulate(model, batch):
+    """The greedy cost-model placement and seeded random candidates (the
+    post's two other schedulers) keep every list in flat order with a wave's
+    claimers on distinct units: they run to completion on the host model, and
+    candidates differ by seed."""
+    import moe_persistent_decode_amd as mk
+    m = configs.small_variant(configs.FULL48, n_layers=4) if model == "full48" else \
+        configs.small_variant(configs.LLAMA1B, n_layers=4)
+    d = _host(m, batch=batch, max_seq=16384 + 64)
+    seq = 16384 if batch > 4 else 8192
+    hi = 1 if m.dense else min(m.n_experts, batch * m.top_k)
+    seen = set()
+    for placement, seeds in ((mk.PLACE_COST_MODEL, [1]), (mk.PLACE_RANDOM, [1, 2, 3])):
+        d.set_schedule_options(0, placement)
+        for sd in seeds:
+            d.set_placement_seed(sd)
+            t, off = d.schedule_export(batch, seq)
+            seen.add(hash(t.tobytes() + off.tobytes()))
+            # a wave's claimers on distinct units: at most one claimer task
+            # per (unit, layer, opcode)
+            for cu in range(len(off) - 1):
+                lst = t[off[cu]:off[cu + 1]]
+                cl = lst[np.isin(lst[:, 0], [3, 8, 9])]
+                keys = set()
+                for row in cl:
+                    assert (int(row[0]), int(row[1])) not in keys, (placement, sd, cu)
+                    keys.add((int(row[0]), int(row[1])))
+            st, msg = d.simulate(batch, seq, [hi] * m.n_layers, seed=sd)
+            assert st == 0, (placement, sd, msg)
+    assert len(seen) == 4
+    d.close()

@@ -68,7 +68,8 @@ def check_appended_kv(cfg, gpu_bits, ref_bits, pool0, bt, lens_per_step):
 
 def _run(B, lo, hi, seed, mode, cfg=configs.TINY, options=None):
     """Decode STEPS teacher-forced steps on GPU and oracle, compare every row;
-    returns the GPU logits of every step. options: (wave order, placement)."""
+    returns the GPU logits of every step. options: (wave order, placement[,
+    random placement seed])."""
     bs, weights, pool0 = _case(cfg, B, lo, hi, seed)
     W = gen.NumpyWeights(weights)
     bt = bs.block_tables.numpy()
@@ -81,7 +82,9 @@ def _run(B, lo, hi, seed, mode, cfg=configs.TINY, options=None):
     pool_gpu = bits_to_torch(pool0)
     dec = make_decoder(cfg, bs, pool_gpu, int(lens.max()) + STEPS, mode, max_batch=B)
     if options is not None:
-        dec.set_schedule_options(*options)
+        dec.set_schedule_options(*options[:2])
+        if len(options) > 2:
+            dec.set_placement_seed(options[2])
     wgpu = {k: v.cuda() for k, v in weights.items()}
     dec.load_weights(wgpu)
     up = RepairUploads(dec, rrep, lst, lambda l: {f"{k}.{l}": wgpu[f"{k}.{l}"] for k in gen.LAYER_KINDS},
@@ -168,6 +171,21 @@ def test_every_schedule_decodes_the_same_step(B, mode):
                                             options=(order, placement))
     if B > 4:
         base = outs[(0, 0)]
+        for k, o in outs.items():
+            assert all(np.array_equal(a, b) for a, b in zip(o, base)), k
+
+
+@pytest.mark.parametrize("B", [1, 4, 8, 32])
+def test_cost_model_and_random_placements_decode_the_same_step(B):
+    """The greedy cost-model placement and two random candidates of the
+    brute-force search (the post's other schedulers) each match the oracle;
+    above 4 tokens their logits are bit-identical to the tuned placement's."""
+    import moe_persistent_decode_amd as mk
+    outs = {}
+    for opt in ((0, mk.PLACE_TUNED), (0, mk.PLACE_COST_MODEL), (0, mk.PLACE_RANDOM, 7), (0, mk.PLACE_RANDOM, 11)):
+        outs[opt] = _run(B, 8, 160, seed=120 + B, mode=0, cfg=configs.TINY_WIN, options=opt)
+    if B > 4:
+        base = outs[(0, mk.PLACE_TUNED)]
         for k, o in outs.items():
             assert all(np.array_equal(a, b) for a, b in zip(o, base)), k
 
