@@ -348,6 +348,27 @@ mk_status mk_schedule_simulate(mk_handle* h, int batch, int max_seq_len_hint,
                                const int32_t* n_active_experts, uint64_t interleave_seed,
                                int32_t corrupt_task, char* report, size_t report_len);
 
+/* Check the schedule for read-before-arrive and overwrite-before-read
+ * hazards (the post's barrier section: a wrong arrival count lets a task read
+ * before its producer finished): every buffer a task reads or writes is tagged
+ * with the writers of its current version and the readers since, in list
+ * order; a read must be preceded, through the counters the task waited for
+ * (or its unit's earlier tasks), by every writer of the version it reads, and
+ * a write by every reader and writer of the version it replaces. Reads are
+ * placed where the device code issues them (before, between or after the
+ * waits). Accesses among the claimers of one wave, which synchronise through
+ * their own item counters, are not modelled. `flags`: 0, or
+ * MK_CHECK_EARLY_STREAM_READ to model an earlier device version whose residual
+ * task read the residual stream before its waits. MK_OK when no hazard is
+ * found, MK_ERR_STATE with the first few in `report` otherwise.
+ * MK_CHECK_PLANT_MISSING_WAIT checks a schedule whose residual tasks skip
+ * their wait for their contributions (a planted mistake the check must
+ * report). */
+#define MK_CHECK_EARLY_STREAM_READ 1u
+#define MK_CHECK_PLANT_MISSING_WAIT 2u
+mk_status mk_schedule_check(mk_handle* h, int batch, int max_seq_len_hint, uint32_t flags, char* report,
+                            size_t report_len);
+
 /* Create a handle without any device (schedule introspection and simulation
  * only; mk_load_*, mk_decode_step return MK_ERR_STATE). */
 mk_status mk_create_host_only(const mk_config* cfg, int n_cus, mk_handle** out);

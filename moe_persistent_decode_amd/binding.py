@@ -32,7 +32,8 @@ EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_d
            "mk_service_admit", "mk_service_evict", "mk_service_stats", "mk_service_last_error",
            "mk_service_destroy",
            "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache", "mk_stream_read",
-           "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_debug_read")
+           "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_schedule_check",
+           "mk_debug_read")
 
 
 class MkError(RuntimeError):
@@ -85,6 +86,7 @@ def _load():
     lib.mk_set_routing_trace.argtypes = [H, P]
     lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
     lib.mk_set_placement_seed.argtypes = [H, ctypes.c_uint64]
+    lib.mk_schedule_check.argtypes = [H, I, I, ctypes.c_uint32, P, S]
     lib.mk_set_schedule_options.argtypes = [H, I, I]
     lib.mk_kv_cache.argtypes = [H, I, ctypes.POINTER(P), ctypes.POINTER(S)]
     lib.mk_stream_read.argtypes = [P, S, P]
@@ -272,6 +274,12 @@ class Decoder:
         off = np.zeros(info.n_cus + 1, dtype=np.int32)
         self._check(lib.mk_schedule_export(self._h, batch, hint, tasks.ctypes.data, off.ctypes.data))
         return tasks, off
+
+    def check_hazards(self, batch: int, hint: int, flags: int = 0):
+        """mk_schedule_check: (status, report) of the read-before-arrive check."""
+        buf = ctypes.create_string_buffer(2048)
+        st = lib.mk_schedule_check(self._h, batch, hint, ctypes.c_uint32(flags), buf, 2048)
+        return st, buf.value.decode()
 
     def simulate(self, batch: int, hint: int, n_active, seed: int = 0, corrupt_task: int = -1):
         import numpy as np

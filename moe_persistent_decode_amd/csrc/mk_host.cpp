@@ -51,6 +51,7 @@ struct Schedule {
   std::vector<mk_task> cu_tasks;
   std::vector<int32_t> cu_off;
   std::vector<std::pair<int, int>> waves;  // [begin, end) into flat
+  std::vector<int> flat_unit;              // the unit each flat task runs on
   // device copies
   mk_task* d_cu_tasks = nullptr;
   int32_t* d_cu_off = nullptr;
@@ -859,7 +860,11 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
   // per-workgroup lists in flat order (every wait is on an earlier task of
   // the flat list, so the lists cannot deadlock), placed as chosen above
   std::vector<std::vector<mk_task>> per(n_w);
-  for (size_t k = 0; k < S->flat.size(); ++k) per[flat_cu[k] >= 0 ? flat_cu[k] : k % n_w].push_back(S->flat[k]);
+  S->flat_unit.resize(S->flat.size());
+  for (size_t k = 0; k < S->flat.size(); ++k) {
+    S->flat_unit[k] = flat_cu[k] >= 0 ? flat_cu[k] : (int)(k % n_w);
+    per[S->flat_unit[k]].push_back(S->flat[k]);
+  }
   S->cu_off.assign(n_w + 1, 0);
   for (int i = 0; i < n_w; ++i) {
     S->cu_off[i + 1] = S->cu_off[i] + (int)per[i].size();
@@ -892,6 +897,282 @@ struct SimCU {
   int item_end = 0;       // fixed shares: end of this claimer's down items (pending_item: the next)
   int pos = 0;
 };
+
+// ------------------------------------------------------- hazard checker
+// Read-before-arrive and overwrite-before-read checking with per-buffer tags
+// (the megakernel post's warning, Chinese version, barrier section: a wrong
+// arrival count lets a reader run ahead of its producer). Every buffer a task
+// reads or writes is a tagged region; in flat-list order (the program order
+// of the step) each region keeps the writers of its current version and the
+// readers since. A task knows a producer has finished when a counter it
+// waited for is incremented by that producer (every dependency wait in these
+// schedules targets the counter's full count), or transitively through what
+// such a producer, or an earlier task on its own unit, knew. A read must know
+// every writer of the version it reads; a write must know every reader and
+// writer of the version it replaces. Reads are modelled at the point the
+// device code issues them: before the task's waits, after its first wait, or
+// after all of them. Claimers of one wave exchange data among themselves
+// through their own item counters (the up/gate and down phases of the
+// claiming MoE, the attention splits a combine merges); those accesses are
+// not modelled here (the simulator checks those counts).
+namespace {
+struct Bits {
+  std::vector<uint64_t> w;
+  explicit Bits(size_t n = 0) : w((n + 63) / 64, 0ull) {}
+  void set(size_t i) { w[i >> 6] |= 1ull << (i & 63); }
+  bool has(size_t i) const { return (w[i >> 6] >> (i & 63)) & 1ull; }
+  void merge(const Bits& o) {
+    for (size_t i = 0; i < w.size(); ++i) w[i] |= o.w[i];
+  }
+};
+// regions: buffer kind x index
+enum RegionKind { R_H, R_U, R_SSQ, R_Q, R_KV, R_RP, R_ROUTE, R_PART, R_O, R_AO, R_MP, R_LM, R_KINDS };
+const char* kRegionName[R_KINDS] = {"h", "u", "ssq", "q", "kv", "router partials", "route", "attention partials",
+                                    "attention output", "o-proj partials", "claimer rows", "lm candidates"};
+struct Access {
+  int kind, index;
+  bool write;
+  int point;     // 0 before the waits, 1 after the first wait, 2 after all
+  int ver = -1;  // writes with one version key form one version (default: the task's wave)
+};
+}  // namespace
+
+mk_status check_hazards(const mk_handle* h, const Schedule& S, uint32_t flags, std::string& rep) {
+  const mk_config& c = h->cfg;
+  const int n = (int)S.flat.size(), n_w = h->n_workers, NB = h->NB, KVH = c.n_kv_heads, B = S.B;
+  const int qpanels = h->q_dim / 16;
+  // the tasks that may increment each counter
+  std::vector<std::vector<int>> prod(S.n_ctr);
+  auto add_prod = [&](int ctr, int k) {
+    if (ctr >= 0 && ctr < S.n_ctr) prod[ctr].push_back(k);
+  };
+  for (int k = 0; k < n; ++k) {
+    const mk_task& t = S.flat[k];
+    for (int i = 0; i < 2; ++i) add_prod(t.sig_ctr[i], k);
+    switch (t.op) {
+      case MK_OP_OPROJ:
+        if (t.b[1] == 1) add_prod(t.a[2], k);
+        break;
+      case MK_OP_ROUTER: add_prod(t.a[5], k); break;
+      case MK_OP_LMHEAD: add_prod(t.a[3], k); break;
+      case MK_OP_ATTN:
+        for (int g = 0; g < KVH; ++g) {
+          add_prod(t.sig_ctr[0] + g, k);
+          if (t.b[0] == 1) add_prod(t.a[5] + g, k);
+        }
+        if (t.b[0] != 1)
+          for (int i = 0; i < B * KVH; ++i) add_prod(t.a[5] + i, k);
+        break;
+      default: break;
+    }
+  }
+  // the previous task on each task's unit
+  std::vector<int> prev(n, -1), last(n_w, -1);
+  for (int k = 0; k < n; ++k) {
+    prev[k] = last[S.flat_unit[k]];
+    last[S.flat_unit[k]] = k;
+  }
+  // what each task knows: after its first wait and after all (K1, K2); a
+  // counter's union is formed once its producers all precede the waiter
+  std::vector<Bits> K(n, Bits(n)), K1(n, Bits(n));
+  std::vector<Bits> cunion(S.n_ctr);
+  std::vector<char> cdone(S.n_ctr, 0);
+  int skipped = 0;
+  auto counter_union = [&](int ctr, int waiter) -> const Bits* {
+    for (int p : prod[ctr])
+      if (p >= waiter || S.flat_wave[p] == S.flat_wave[waiter]) return nullptr;  // within a wave
+    if (!cdone[ctr]) {
+      cunion[ctr] = Bits(n);
+      for (int p : prod[ctr]) {
+        cunion[ctr].set(p);
+        cunion[ctr].merge(K[p]);
+      }
+      cdone[ctr] = 1;
+    }
+    return &cunion[ctr];
+  };
+  std::vector<Bits> K0(n, Bits(n));  // before the waits: the unit's earlier tasks and what they knew
+  for (int k = 0; k < n; ++k) {
+    const mk_task& t = S.flat[k];
+    if (prev[k] >= 0) {
+      K0[k] = K[prev[k]];
+      K0[k].set(prev[k]);
+    }
+    K1[k] = K0[k];
+    K[k] = K0[k];
+    bool first = true;
+    // the device waits on wait_ctr[1] first where an op does (the residual's
+    // route), else in index order; K1 holds what the first wait gives
+    const int order_res[3] = {1, 0, 2}, order_std[3] = {0, 1, 2};
+    const int* ord = t.op == MK_OP_RESIDUAL ? order_res : order_std;
+    for (int j = 0; j < 3; ++j) {
+      const int i = ord[j];
+      if (t.wait_ctr[i] < 0) continue;
+      // (a planted schedule mistake, to test the checker: the residual tasks'
+      // wait for their contributions left out)
+      if ((flags & MK_CHECK_PLANT_MISSING_WAIT) && t.op == MK_OP_RESIDUAL && i == 0) continue;
+      const Bits* u = counter_union(t.wait_ctr[i], k);
+      if (!u) {
+        ++skipped;
+        continue;
+      }
+      K[k].merge(*u);
+      if (first) K1[k].merge(*u);
+      first = false;
+    }
+    // an attention claimer waits, per item, for the QKV tasks of the item's
+    // group (a[1] + g, count a[2]); it may take an item of any group
+    if (t.op == MK_OP_ATTN)
+      for (int g = 0; g < KVH; ++g) {
+        const Bits* u = counter_union(t.a[1] + g, k);
+        if (u) K[k].merge(*u);
+      }
+  }
+  // the regions each task touches
+  auto accesses = [&](int k) {
+    const mk_task& t = S.flat[k];
+    std::vector<Access> a;
+    const int l = t.layer, par = l & 1, npar = (l + 1) & 1;
+    auto all_input = [&](int p, int point) {
+      for (int cb = 0; cb < NB; ++cb) {
+        a.push_back({R_U, p * NB + cb, false, point});
+        a.push_back({R_SSQ, p * NB + cb, false, point});
+      }
+    };
+    auto write_input = [&](int p, int cb) {
+      a.push_back({R_H, cb, true, 2});
+      a.push_back({R_U, p * NB + cb, true, 2});
+      a.push_back({R_SSQ, p * NB + cb, true, 2});
+    };
+    // above 4 tokens the last contributor to a column block (an O projection
+    // or an expert down item, counted on the block's counter) adds the block's
+    // residual: one version per layer, whichever task writes it
+    auto block_residual = [&](int cb) {
+      const int ver = -(l + 2);
+      a.push_back({R_H, cb, false, 2, ver});
+      a.push_back({R_H, cb, true, 2, ver});
+      a.push_back({R_U, npar * NB + cb, true, 2, ver});
+      a.push_back({R_SSQ, npar * NB + cb, true, 2, ver});
+    };
+    switch (t.op) {
+      case MK_OP_EMBED: write_input(0, t.a[0]); break;
+      case MK_OP_QKV:
+        all_input(par, 2);
+        a.push_back({t.a[0] < qpanels ? R_Q : R_KV, t.a[0] < qpanels ? t.a[2] : l * KVH + t.a[2], true, 2});
+        break;
+      case MK_OP_ROUTER:
+        all_input(par, 2);
+        a.push_back({R_RP, l, true, 2});
+        a.push_back({R_ROUTE, l, true, 2});  // the last one's top-k and route
+        break;
+      case MK_OP_ATTN:
+        for (int g = 0; g < KVH; ++g) {
+          a.push_back({R_Q, g, false, 2});
+          a.push_back({R_KV, l * KVH + g, false, 2});
+          a.push_back({R_PART, g, true, 2});
+          if (t.b[0] != 1) a.push_back({R_O, g, true, 2});  // the split that completes a group combines
+        }
+        break;
+      case MK_OP_OPROJ: {
+        const int g = t.a[0], per = t.b[1] == 1 ? t.a[3] : 1;
+        a.push_back({t.b[1] == 1 ? R_PART : R_O, g, false, 2});
+        for (int j = 0; j < per; ++j) a.push_back({R_AO, g * NB + t.a[1] + j, true, 2});
+        if (t.b[1] != 1) block_residual(t.a[1]);
+        break;
+      }
+      case MK_OP_MOE_FUSED:
+        all_input(par, 2);
+        if (!c.dense) {
+          a.push_back({R_RP, l, false, 2});
+        }
+        a.push_back({R_MP, t.b[0], true, 2});
+        break;
+      case MK_OP_MOE_UP:
+        all_input(par, 2);
+        a.push_back({R_RP, l, false, 2});
+        for (int cb = 0; cb < NB; ++cb) block_residual(cb);
+        break;
+      case MK_OP_RESIDUAL: {
+        const int cb = t.a[0], mode = t.a[1];
+        const int hpoint = mode == MK_RES_PARALLEL ? ((flags & MK_CHECK_EARLY_STREAM_READ) ? 0 : 1) : 2;
+        a.push_back({R_H, cb, false, hpoint});
+        if (mode == MK_RES_PARALLEL) a.push_back({R_ROUTE, l, false, 1});
+        if (mode != MK_RES_DENSE_FFN)
+          for (int g = 0; g < KVH; ++g) a.push_back({R_AO, g * NB + cb, false, 2});
+        if (mode != MK_RES_DENSE_MID)
+          for (int i = 0; i < t.b[2]; ++i) a.push_back({R_MP, i, false, 2});
+        write_input(mode == MK_RES_DENSE_MID ? par : npar, cb);
+        break;
+      }
+      case MK_OP_LMHEAD:
+        all_input(c.n_layers & 1, 2);
+        a.push_back({R_LM, 0, true, 2});
+        break;
+      default: break;
+    }
+    return a;
+  };
+  // tags in flat order
+  struct Tag {
+    std::vector<int> writers, readers;
+    int ver = -1 << 30;
+  };
+  std::vector<std::vector<Tag>> tags(R_KINDS);
+  const int sizes[R_KINDS] = {NB, 2 * NB, 2 * NB, KVH, c.n_layers * KVH, c.n_layers, c.n_layers, KVH, KVH,
+                              KVH * NB, n_w, 1};
+  for (int r = 0; r < R_KINDS; ++r) tags[r].resize(sizes[r]);
+  int n_bad = 0;
+  auto note = [&](const char* what, int k, int other, int kind, int index) {
+    if (n_bad++ < 4) {
+      const mk_task& t = S.flat[k];
+      const mk_task& o = S.flat[other];
+      char buf[320];
+      std::snprintf(buf, sizeof buf,
+                    "%s: task %d (op %d, layer %d, unit %d) and task %d (op %d, layer %d, unit %d) on %s[%d]; ", what,
+                    k, t.op, t.layer, S.flat_unit[k], other, o.op, o.layer, S.flat_unit[other], kRegionName[kind],
+                    index);
+      rep += buf;
+    }
+  };
+  auto knows = [&](int k, int point, int other) {
+    if (other == k) return true;
+    const Bits& kb = point == 0 ? K0[k] : point == 1 ? K1[k] : K[k];
+    return kb.has(other);
+  };
+  for (int k = 0; k < n; ++k) {
+    const int wave = S.flat_wave[k];
+    const bool claimer = is_claimer(S.flat[k].op);
+    for (const Access& x : accesses(k)) {
+      Tag& tg = tags[x.kind][x.index];
+      const int ver = x.ver != -1 ? x.ver : wave;
+      const bool same_ver = tg.ver == ver;
+      if (!x.write) {
+        // (within a version: the claimers of a wave, or the contributors to a
+        // block, synchronise on their own counters)
+        if (!(same_ver && (claimer || x.ver != -1)))
+          for (int w : tg.writers)
+            if (!knows(k, x.point, w)) note("read before its writer is known to have finished", k, w, x.kind, x.index);
+        tg.readers.push_back(k);
+      } else {
+        if (!same_ver) {
+          for (int r : tg.readers)
+            if (!knows(k, x.point, r)) note("overwrite before a reader is known to have finished", k, r, x.kind, x.index);
+          for (int w : tg.writers)
+            if (!knows(k, x.point, w)) note("overwrite before the previous writer is known to have finished", k, w,
+                                            x.kind, x.index);
+          tg.writers.clear();
+          tg.readers.clear();
+          tg.ver = ver;
+        }
+        tg.writers.push_back(k);
+      }
+    }
+  }
+  char buf[160];
+  std::snprintf(buf, sizeof buf, "%d hazards over %d tasks (%d waits within a wave not modelled)", n_bad, n, skipped);
+  rep = n_bad ? rep + buf : std::string("ok: ") + buf;
+  return n_bad ? MK_ERR_STATE : MK_OK;
+}
 
 mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uint64_t seed, int corrupt,
                    std::string& rep) {
@@ -1799,6 +2080,22 @@ mk_status mk_schedule_export(mk_handle* h, int batch, int hint, int32_t* tasks, 
   std::memcpy(tasks, S->cu_tasks.data(), S->cu_tasks.size() * sizeof(mk_task));
   std::memcpy(cu_offsets, S->cu_off.data(), S->cu_off.size() * sizeof(int32_t));
   return MK_OK;
+}
+
+mk_status mk_schedule_check(mk_handle* h, int batch, int hint, uint32_t flags, char* report, size_t report_len) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > h->cfg.max_batch || hint < 1 || hint > h->cfg.max_seq_len)
+    return fail(h, MK_ERR_INVALID_ARG, "bad batch/hint");
+  Schedule* S = nullptr;
+  mk_status st = get_schedule(h, batch, hint, &S);
+  if (st != MK_OK) return st;
+  std::string rep;
+  st = check_hazards(h, *S, flags, rep);
+  if (report && report_len) {
+    std::strncpy(report, rep.c_str(), report_len - 1);
+    report[report_len - 1] = 0;
+  }
+  return st;
 }
 
 mk_status mk_schedule_simulate(mk_handle* h, int batch, int hint, const int32_t* n_active, uint64_t seed,
