@@ -297,6 +297,21 @@ mk_status mk_sync_status(mk_handle* h, void* stream);
  * message through mk_last_error(NULL)); nothing is written. */
 mk_status mk_stream_read(const void* buf, size_t bytes, void* stream);
 
+/* Diagnostic: the cross-XCD message-passing litmus of the protocol every
+ * hand-off between compute units uses (device-coherent stores, a drain, then
+ * a relaxed device-scope atomic on a counter; the reader polls the counter and
+ * reads device-coherently; the post's barrier section relies on the same
+ * release/acquire order with fences). `pairs` producer/consumer workgroup
+ * pairs on different XCDs pass `rounds` 16-word messages each on device
+ * `device` (synchronous; allocates and frees its own buffers). *stale: words
+ * a consumer read older than the round it had been signalled for; *timeouts:
+ * waits that gave up (20 ms each; a pair stops at its first timeout or stale
+ * read, so the kernel always ends). coherent = 0 uses plain loads and stores
+ * for the message instead (the contrast). MK_ERR_INVALID_ARG for pairs
+ * outside [1, 512], rounds outside [1, 1e6] or null outputs. */
+mk_status mk_litmus_message_passing(int device, int pairs, int rounds, int coherent, uint32_t* stale,
+                                    uint32_t* timeouts);
+
 /* Last error message of this handle (or of the last failed mk_create when h is NULL). */
 const char* mk_last_error(const mk_handle* h);
 

@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     Decoder, MkConfig, MkError, make_config, MODE_MEGAKERNEL, MODE_KERNEL_PER_OP, EXPORTS, LIB_PATH,
     ORDER_SHIPPED, ORDER_QKV_FIRST, ORDER_ATTENTION_FIRST, PLACE_TUNED, PLACE_ROUND_ROBIN, PLACE_AFFINITY,
     PLACE_COST_MODEL, PLACE_RANDOM,
-    DecodeService, stream_read,
+    DecodeService, stream_read, litmus_message_passing,
 )

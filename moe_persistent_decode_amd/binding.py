@@ -32,6 +32,7 @@ EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_d
            "mk_service_admit", "mk_service_evict", "mk_service_stats", "mk_service_last_error",
            "mk_service_destroy",
            "mk_sync_status", "mk_last_error", "mk_destroy", "mk_kv_cache", "mk_stream_read",
+           "mk_litmus_message_passing",
            "mk_schedule_info_get", "mk_schedule_export", "mk_schedule_simulate", "mk_schedule_check",
            "mk_debug_read")
 
@@ -90,6 +91,8 @@ def _load():
     lib.mk_set_schedule_options.argtypes = [H, I, I]
     lib.mk_kv_cache.argtypes = [H, I, ctypes.POINTER(P), ctypes.POINTER(S)]
     lib.mk_stream_read.argtypes = [P, S, P]
+    lib.mk_litmus_message_passing.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_uint32),
+                                              ctypes.POINTER(ctypes.c_uint32)]
     lib.mk_set_mode.argtypes = [H, I]
     lib.mk_set_task_trace.argtypes = [H, P, S]
     lib.mk_debug_read.argtypes = [H, ctypes.c_char_p, P, S]
@@ -146,6 +149,17 @@ def stream_read(buf, stream=None) -> None:
     st = lib.mk_stream_read(_ptr(buf), nbytes, _stream_ptr(stream))
     if st != 0:
         raise MkError(st, lib.mk_last_error(None).decode())
+
+
+def litmus_message_passing(pairs: int, rounds: int, coherent: bool = True, device: int = 0):
+    """mk_litmus_message_passing: (stale reads, timeouts) over `pairs` workgroup
+    pairs on different XCDs passing `rounds` messages each."""
+    stale, timeouts = ctypes.c_uint32(0), ctypes.c_uint32(0)
+    st = lib.mk_litmus_message_passing(device, pairs, rounds, 1 if coherent else 0, ctypes.byref(stale),
+                                       ctypes.byref(timeouts))
+    if st != 0:
+        raise MkError(st, lib.mk_last_error(None).decode())
+    return stale.value, timeouts.value
 
 
 def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages_per_seq: int,

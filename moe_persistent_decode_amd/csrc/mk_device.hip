@@ -1583,11 +1583,11 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   const int kc = H / 32, kh_chunks = kc / 2;
   const size_t pstride = (size_t)kc * 512;
   const Pub GU(P.gu), U0(u_of(P, l, 0)), U1(u_of(P, l, 1));
-  // Items are claimed CH at a time; the next chunk's claim is issued when a
+  // Items are claimed CHU (CHD) at a time; the next chunk's claim is issued when a
   // chunk starts and read when it runs out, so claims (one address shared
   // by every unit) never sit on the path.
-  constexpr int CH = 4;
-  claimer_start(P, claim_ctr, CH, l, sm, dclaim_ctr, CH);
+  constexpr int CHU = 4, CHD = 4;  // up/gate and down items per claim
+  claimer_start(P, claim_ctr, CHU, l, sm, dclaim_ctr, CHD);
   const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[1]);
   const int n_down = __builtin_amdgcn_readfirstlane(sm.rt_hdr[2]);
   int dbase = sm.claim2;
@@ -1595,28 +1595,29 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   mark(sm, 0);
   // the stream of one queue: the item after the current one (uniform)
   struct Stream {
-    int base, j, pend;
+    int base, j, pend, ch;
   };
   // (the pending claim is issued unconditionally by thread 0 and read only
   // there, so its result stays in one register: a copy of it, at a join of
   // paths that did and did not claim, would wait for the atomic at once and,
   // the memory counter retiring in order, for every weight load before it.
   // Claims past the queue's end are harmless: their items do not exist.)
-  auto stream_start = [&](Stream& q, int base, int32_t ctr, int n) {
+  auto stream_start = [&](Stream& q, int base, int32_t ctr, int n, int ch) {
     q.base = base;
     q.j = 0;
+    q.ch = ch;
     if (tid() == 0)
-      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)CH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto stream_next = [&](Stream& q, int32_t ctr, int n) -> int {
-    if (++q.j < CH) return q.base + q.j;
+    if (++q.j < q.ch) return q.base + q.j;
     if (tid() == 0) sm.claim = q.pend;
     lds_sync();
     q.base = sm.claim;
     lds_sync();
     q.j = 0;
     if (tid() == 0)
-      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)CH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)q.ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return q.base;
   };
   // this lane's row of row tile rt of active expert a: the element offset
@@ -1656,11 +1657,19 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
       mfma_tiles(acc, w, Ah, Al);
       reduce_tiles(acc, sm);
       // gu[slot][kh][gate|up][F] of the tile's routed rows
+      // (at most 2 x 16 x 16 = 512 values: one predicated store per thread,
+      // a count the compiler's memory-counter waits can track; a loop with a
+      // run-time trip count made it wait for every store before the next
+      // item's loads could be used)
       const int nr = min(16, cnt - rt * 16);
-      for (int o = tid(); o < 2 * nr * 16; o += MK_WG_THREADS) {
-        const int which = o / (nr * 16), rr = (o / 16) % nr, nn = o % 16;
-        const int slot = sm.rt_slot[a * B + rt * 16 + rr], b = slot / K;
-        GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn, sm.out[which * 256 + rr * 16 + nn] * sm.inv_rms[b]);
+      {
+        const int o = tid();
+        if (o < 2 * nr * 16) {
+          const int which = o / (nr * 16), rr = (o / 16) % nr, nn = o % 16;
+          const int slot = sm.rt_slot[a * B + rt * 16 + rr], b = slot / K;
+          GU.stf(((slot * 2 + kh) * 2 + which) * F + tt * 16 + nn,
+                 sm.out[which * 256 + rr * 16 + nn] * sm.inv_rms[b]);
+        }
       }
     } while (++rt * 16 < cnt);
     if (tid() == 0) sm.done_cnt[a] += 1;
@@ -1672,7 +1681,7 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     WTile<2, NCH> w0, w1, w2;
     ATile<1, NCH> h0, l0, h1, l1, h2, l2;
     Stream q;
-    stream_start(q, sm.claim, claim_ctr, n_items);
+    stream_start(q, sm.claim, claim_ctr, n_items, CHU);
     int i0 = q.base;
     load(w0, h0, l0, 0, i0);
     int i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
@@ -1713,7 +1722,7 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   {
     WTile<4, NCHD> d0, d1;
     Stream q;
-    stream_start(q, dbase, dclaim_ctr, n_down);
+    stream_start(q, dbase, dclaim_ctr, n_down, CHD);
     int i0 = q.base;
     dload(d0, i0);
     int i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
@@ -2761,6 +2770,82 @@ extern "C" __global__ __launch_bounds__(512) void mk_stream_read_words(const u32
   if (acc == 0x9e3779b9u) mk_stream_sink = acc;
 }
 
+// Cross-XCD message passing with the step's own primitives (a litmus test of
+// the protocol every hand-off between compute units uses). Pair p is
+// workgroups 2p (producer) and 2p + 1 (consumer), which the dispatcher places
+// on different XCDs. For rounds r = 1..R the producer waits until the
+// consumer has acknowledged round r - 1, writes a 16-word message holding r,
+// drains its stores and increments the pair's flag (as a task does before it
+// signals); the consumer polls the flag until it reaches r, reads the message
+// and counts words below r (stale reads), then acknowledges. With coherent =
+// 0 the message is written and read with plain accesses instead (the
+// contrast). Every wait gives up after limit_ticks (100 MHz) and is counted;
+// a pair stops at its first timeout or stale read, so the kernel always ends.
+// result[2p] stale reads, result[2p + 1] timeouts.
+__device__ __forceinline__ bool litmus_wait(const uint32_t* f, uint32_t want, int64_t limit) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (ld_relaxed(f) < want) {
+    __builtin_amdgcn_s_sleep(1);
+    if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > limit) return false;
+  }
+  return true;
+}
+
+extern "C" __global__ __launch_bounds__(64) void mk_litmus_mp(uint32_t* msg, uint32_t* flag, uint32_t* ack,
+                                                              uint32_t* result, int rounds, int coherent,
+                                                              int64_t limit) {
+  const int p = blockIdx.x >> 1, ln = threadIdx.x;
+  const bool producer = (blockIdx.x & 1) == 0;
+  uint32_t* m = msg + p * 64;  // 256 bytes per pair: its own lines
+  const Pub M(m);
+  __shared__ int stop;
+  if (ln == 0) stop = 0;
+  __syncthreads();
+  uint32_t stale = 0, timeouts = 0;
+  for (int r = 1; r <= rounds; ++r) {
+    if (producer) {
+      if (ln == 0 && !litmus_wait(ack + p, (uint32_t)(r - 1), limit)) stop = 1;
+      __syncthreads();
+      if (stop) {
+        timeouts += ln == 0;
+        break;
+      }
+      if (ln < 16) {
+        if (coherent)
+          M.sti(ln, r);
+        else
+          m[ln] = (uint32_t)r;
+      }
+      drain_memory();
+      __syncthreads();
+      if (ln == 0) __hip_atomic_fetch_add(flag + p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (ln == 0 && !litmus_wait(flag + p, (uint32_t)r, limit)) stop = 1;
+      __syncthreads();
+      if (stop) {
+        timeouts += ln == 0;
+        break;
+      }
+      uint32_t v = 0;
+      if (ln < 16) v = coherent ? (uint32_t)M.ldi(ln) : *(volatile uint32_t*)(m + ln);
+      const bool bad = ln < 16 && v < (uint32_t)r;
+      const uint64_t ballot = __ballot(bad);
+      if (ballot) {
+        stale += ln == 0 ? (uint32_t)__popcll(ballot) : 0u;
+        if (ln == 0) stop = 1;
+      }
+      drain_memory();
+      __syncthreads();
+      // (stopping: the acknowledgement runs ahead of every later round, so
+      // the producer finishes its rounds without waiting)
+      if (ln == 0) __hip_atomic_fetch_add(ack + p, stop ? (1u << 30) : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (stop) break;
+    }
+  }
+  if (ln == 0 && !producer) result[2 * p] = stale;
+  if (ln == 0) __hip_atomic_fetch_add(result + 2 * p + 1, timeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------ host launch
 #include <mutex>
 
@@ -2784,6 +2869,13 @@ hipError_t mk_static_scratch(int device, void** ptr) {
   }
   *ptr = addr[device];
   return hipSuccess;
+}
+
+hipError_t mk_launch_litmus(uint32_t* msg, uint32_t* flag, uint32_t* ack, uint32_t* result, int pairs, int rounds,
+                            int coherent, int64_t limit, hipStream_t stream) {
+  hipLaunchKernelGGL(mk_litmus_mp, dim3(2 * pairs), dim3(64), 0, stream, msg, flag, ack, result, rounds, coherent,
+                     limit);
+  return hipGetLastError();
 }
 
 hipError_t mk_launch_stream_read(const void* p, size_t n16, hipStream_t stream) {

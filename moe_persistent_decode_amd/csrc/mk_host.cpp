@@ -1979,6 +1979,42 @@ mk_status mk_stream_read(const void* buf, size_t bytes, void* stream) {
   return MK_OK;
 }
 
+mk_status mk_litmus_message_passing(int device, int pairs, int rounds, int coherent, uint32_t* stale,
+                                    uint32_t* timeouts) {
+  if (pairs < 1 || pairs > 512 || rounds < 1 || rounds > 1000000 || !stale || !timeouts)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "litmus: pairs in [1, 512], rounds in [1, 1e6], non-null outputs");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "litmus: bad device %d", device);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "hipGetDevice failed");
+  if (hipSetDevice(device) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "hipSetDevice failed");
+  const size_t words = (size_t)pairs * 64 + 3 * (size_t)pairs * 2;
+  uint32_t* buf = nullptr;
+  mk_status st = MK_OK;
+  std::vector<uint32_t> res(2 * (size_t)pairs, 0);
+  if (hipMalloc(&buf, words * 4) != hipSuccess) {
+    st = fail(nullptr, MK_ERR_OOM, "litmus buffers");
+  } else {
+    uint32_t *msg = buf, *flag = buf + (size_t)pairs * 64, *ack = flag + 2 * pairs, *result = ack + 2 * pairs;
+    // every wait gives up after 20 ms (2e6 ticks of the 100 MHz clock)
+    if (hipMemset(buf, 0, words * 4) != hipSuccess ||
+        mk_launch_litmus(msg, flag, ack, result, pairs, rounds, coherent, 2000000, nullptr) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(res.data(), result, res.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      st = fail(nullptr, MK_ERR_HIP, "litmus launch failed");
+    (void)hipFree(buf);
+  }
+  (void)hipSetDevice(cur);
+  if (st != MK_OK) return st;
+  *stale = *timeouts = 0;
+  for (int p = 0; p < pairs; ++p) {
+    *stale += res[2 * p];
+    *timeouts += res[2 * p + 1];
+  }
+  return MK_OK;
+}
+
 mk_status mk_kv_cache(mk_handle* h, int layer, void** kv_base, size_t* bytes) {
   if (!h || !kv_base || !bytes) return MK_ERR_INVALID_ARG;
   if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
