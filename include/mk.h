@@ -278,7 +278,11 @@ mk_status mk_set_placement_seed(mk_handle* h, uint64_t seed);
  * default, 2 s). A wait that exceeds it sets the device error word
  * (MK_ERR_DEVICE_TIMEOUT) and every workgroup drains to the end of its task
  * list (the post warns that a wrong arrival count deadlocks: section "屏障").
- * Takes effect at the next step. */
+ * Takes effect at the next step. At batches up to 4 the queries and the new
+ * key and value reach attention as tagged words (each 8-byte word holds the
+ * value and a tag naming the step and layer, polled by the reader instead of
+ * a counter); a poll that exceeds the limit reports the same error, with
+ * 0xffff0000 | word index in place of the counter index. */
 mk_status mk_set_wait_limit(mk_handle* h, uint32_t microseconds);
 
 /* Synchronise `stream` and report any device-side error of earlier steps

@@ -217,6 +217,13 @@ struct Pub {
   __device__ __forceinline__ u32x2_t ld16x4(int i) const {  // 4 bf16 at 16-bit index i
     return __builtin_amdgcn_raw_buffer_load_b64(r, i * 2, 0, kSC1);
   }
+  // Tagged words (8 bytes: the value's 32 bits, then the tag), index i in words.
+  __device__ __forceinline__ void st_tagged(int i, uint32_t v, uint32_t tag) const {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v, tag}, r, i * 8, 0, kSC1);
+  }
+  __device__ __forceinline__ u32x4_t ld_tagged2(int i) const {  // words i, i + 1 (i even)
+    return __builtin_amdgcn_raw_buffer_load_b128(r, i * 8, 0, kSC1);
+  }
 };
 
 // Wait until this wave's memory operations have completed.
@@ -365,9 +372,13 @@ __device__ __forceinline__ bool wait_counters(const mk_params& P, const int32_t*
     sm.flag = ok;
     sm.t_waited = (uint32_t)__builtin_amdgcn_s_memrealtime();
   }
-  __syncthreads();
+  // (LDS-only barriers: a wave does not wait here for its own outstanding
+  // loads and stores, such as this task's weight prefetch or the previous
+  // task's tagged stores; the data a task reads after its waits is read with
+  // device-coherent loads issued after them)
+  lds_sync();
   const bool ok = sm.flag != 0;
-  __syncthreads();
+  lds_sync();
   return ok;
 }
 
@@ -400,6 +411,35 @@ __device__ __forceinline__ bool error_seen(uint32_t e, Smem& sm) {
 __device__ __forceinline__ int layer_window(const mk_params& P, int l) {
   if (P.window == 0) return 0;
   return (l % P.full_every) == P.full_every - 1 ? 0 : P.window;
+}
+
+// ------------------------------------------------------ tagged hand-offs
+// A producer stores each value with its step's and layer's tag in one 8-byte
+// device-coherent word (a single store: a reader sees the old word or the new
+// one, never half of each) and moves on without waiting for the store to be
+// acknowledged; a consumer loads the words until every tag is the expected
+// one. This replaces, for small hand-offs, the store drain, the counter
+// increment, the counter poll and the data load that follows it by one
+// device-coherent round trip.
+__device__ __forceinline__ uint32_t step_tag(const mk_params& P, int l) { return P.tag_base | (uint32_t)(l + 1); }
+
+// Poll words w, w + 1 (w even) of a tagged buffer until both carry `tag`;
+// false on the time limit or another workgroup's error (each thread polls on
+// its own; the caller combines the results).
+__device__ __forceinline__ bool poll_tagged2(const Pub& src, int w, uint32_t tag, const mk_params& P, u32x4_t& v) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t spins = 0;
+  for (v = src.ld_tagged2(w); v[1] != tag || v[3] != tag; v = src.ld_tagged2(w)) {
+    __builtin_amdgcn_s_sleep(1);
+    if ((++spins & 63u) == 0) {
+      if (ld_relaxed(&P.err[0]) != 0) return false;
+      if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > P.timeout_ticks) {
+        raise_error(P, MK_DEVERR_TIMEOUT, 0xffff0000u | (uint32_t)w, v[1]);
+        return false;
+      }
+    }
+  }
+  return true;
 }
 
 __device__ __forceinline__ void mark(Smem& sm, int k) {
@@ -696,6 +736,40 @@ struct KVPage {
   u32x2_t v[D / 16];
 };
 
+// Tagged hand-off from layer l's QKV tasks: the G query heads of kv group g
+// of sequence b (G * D floats) and the group's new key and value (2 D bf16),
+// polled as tagged words (each thread its own pairs) and placed in LDS: the
+// queries at sm.act as floats, the key and value after the first 1024 floats.
+__device__ __forceinline__ bool poll_qkv(const mk_params& P, int l, int b, int g, Smem& sm) {
+  const uint32_t tag = step_tag(P, l);
+  const int D = P.D, GD = P.G * D, nq = GD / 2, n = nq + D;
+  float* qs = reinterpret_cast<float*>(sm.act);
+  uint16_t* kvs = reinterpret_cast<uint16_t*>(qs + 1024);
+  const Pub QT(P.qt + (size_t)b * P.QH * D + (size_t)g * GD), KT(P.kvt + (size_t)(b * P.KVH + g) * 2 * D);
+  if (tid() == 0) sm.flag = 1;
+  lds_sync();
+  bool ok = true;
+  for (int j = tid(); j < n && ok; j += MK_WG_THREADS) {
+    u32x4_t v;
+    if (j < nq) {
+      ok = poll_tagged2(QT, 2 * j, tag, P, v);
+      qs[2 * j] = __uint_as_float(v[0]);
+      qs[2 * j + 1] = __uint_as_float(v[2]);
+    } else {
+      const int w = 2 * (j - nq);
+      ok = poll_tagged2(KT, w, tag, P, v);
+      kvs[w] = (uint16_t)v[0];
+      kvs[w + 1] = (uint16_t)v[2];
+    }
+  }
+  if (!ok) sm.flag = 0;
+  lds_sync();
+  const bool all = sm.flag != 0;
+  if (tid() == 0) sm.t_waited = (uint32_t)__builtin_amdgcn_s_memrealtime();
+  lds_sync();
+  return all;
+}
+
 // One split (b, g, s): waits until the QKV tasks of group g are done
 // (qkv_ctr >= qkv_tgt), counts itself on attn_ctr, and the last of the ns
 // splits combines them and signals sig_ctr.
@@ -722,6 +796,10 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   bool bad = false;
   // The page holding the current position gets this step's K/V from the QKV
   // tasks of other compute units: read it device-coherently, after the wait.
+  // With tagged hand-offs the new row comes from the tagged words instead
+  // (patched in below), and the page's older rows, written by earlier steps,
+  // stream before the wait like any other page.
+  const bool tg = P.tagged != 0;
   const Pub KV(kvl);
   auto load_page = [&](int lp) {
     KVPage<D> pg;
@@ -731,7 +809,7 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
       return pg;
     }
     const int ko = ((phys * 2 + 0) * P.KVH + g) * (int)plane, vo = ((phys * 2 + 1) * P.KVH + g) * (int)plane;
-    if (lp == lp_last) {
+    if (lp == lp_last && !tg) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) pg.k[c] = KV.ld16x8(ko + (ln & 15) * D + 32 * c + 8 * (ln >> 4));
 #pragma unroll
@@ -752,11 +830,19 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   // each wave's first two pages stream before the wait (two-deep pipeline)
   int lp = my0 + wv;
   const int lpn = lp + MK_WAVES;
-  const bool early0 = lp < my1 && lp != lp_last, early1 = lpn < my1 && lpn != lp_last;
+  const bool early0 = lp < my1 && (tg || lp != lp_last), early1 = lpn < my1 && (tg || lpn != lp_last);
   KVPage<D> cur, nxt;
   if (early0) cur = load_page(lp);
   if (early1) nxt = load_page(lpn);
-  if (!wait_one(P, qkv_ctr, qkv_tgt, sm)) return;
+  // the queries and the new key and value: the tagged words into LDS, or the
+  // QKV tasks' counter
+  float* qs = reinterpret_cast<float*>(sm.act);           // [G * D] queries
+  const uint16_t* kn = reinterpret_cast<uint16_t*>(qs + 1024);  // [D] new key, then [D] new value
+  if (tg) {
+    if (!poll_qkv(P, l, b, g, sm)) return;
+  } else if (!wait_one(P, qkv_ctr, qkv_tgt, sm)) {
+    return;
+  }
   if (!seq_ok) {
     if (tid() == 0) raise_error(P, MK_DEVERR_FAULT, 4000 + b, (uint32_t)seq);
     return;
@@ -772,7 +858,8 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
     const int qo = min(hh, G - 1) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const float4 a0 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4)), a1 = Q.ldf4(qo + 32 * c + 8 * (ln >> 4) + 4);
+      const int e = qo + 32 * c + 8 * (ln >> 4);
+      const float4 a0 = tg ? *(const float4*)(qs + e) : Q.ldf4(e), a1 = tg ? *(const float4*)(qs + e + 4) : Q.ldf4(e + 4);
       const float qv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       u32x4_t pk, pl;
 #pragma unroll
@@ -793,8 +880,8 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   for (int d = 0; d < NT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
 
-  // online softmax over one page (keys as MFMA rows)
-  auto do_page = [&](const KVPage<D>& pg, int lp) {
+  // online softmax over one page (keys as MFMA rows), positions [vlo, vhi]
+  auto do_page = [&](const KVPage<D>& pg, int lp, int vlo, int vhi) {
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -806,7 +893,7 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pos = lp * PS + 4 * (ln >> 4) + i;
-      sv[i] = (pos >= lo && pos <= p) ? sacc[i] * scale : kNegInf;
+      sv[i] = (pos >= vlo && pos <= vhi) ? sacc[i] * scale : kNegInf;
       mloc = fmaxf(mloc, sv[i]);
     }
     mloc = max32(max16(mloc));
@@ -840,16 +927,37 @@ __device__ __forceinline__ void attn_split(const mk_params& P, int l, int b, int
   };
   // two pages in registers: each wave computes one while the page two ahead
   // of it streams into the other's registers
+  // (tagged: position p is left out of its page and taken from the tagged
+  // words below)
+  const int phi = tg ? p - 1 : p;
   while (lp < my1 && !bad) {
-    do_page(cur, lp);
+    do_page(cur, lp, lo, phi);
     if (lp + 2 * MK_WAVES < my1) cur = load_page(lp + 2 * MK_WAVES);
     lp += MK_WAVES;
     if (lp >= my1 || bad) break;
-    do_page(nxt, lp);
+    do_page(nxt, lp, lo, phi);
     if (lp + 2 * MK_WAVES < my1) nxt = load_page(lp + 2 * MK_WAVES);
     lp += MK_WAVES;
   }
   if (bad) raise_error(P, MK_DEVERR_FAULT, 5000 + b, (uint32_t)lp);
+  // tagged: the new token as a page of one key, on the wave that had its
+  // page (key row p % PS of the K operand, element p % 4 of the V^T lanes
+  // holding positions 4 (ln / 16) .. + 3)
+  if (tg && !bad && lp_last >= my0 && lp_last < my1 && wv == (lp_last - my0) % MK_WAVES) {
+    const int r = p % PS, e = r & 3;
+    KVPage<D> vp;
+    const bool krow = (ln & 15) == r, vq = (ln >> 4) == (r >> 2);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      vp.k[c] = krow ? *(const u32x4_t*)(kn + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int d = 0; d < NT; ++d) {
+      const uint32_t v = vq ? (uint32_t)kn[D + 16 * d + (ln & 15)] : 0u;
+      const uint32_t sh = (e & 1) ? (v << 16) : v;
+      vp.v[d] = (e >> 1) ? u32x2_t{0u, sh} : u32x2_t{sh, 0u};
+    }
+    do_page(vp, lp_last, p, p);
+  }
 
   // merge the 8 waves' (m, l, O) per head into this split's partial
   SmemAttn& A = sm.u.at;
@@ -1117,6 +1225,17 @@ __device__ __forceinline__ void write_block_input(const mk_params& P, int l_next
 template <int MT, int NCH>
 __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Smem& sm) {
   const int l = t.layer, p0 = t.a[0], np = t.a[1];
+  // This thread's k-th output, element o of the reduced tiles (panel o / 256,
+  // token o / 16 % 16, column o % 16). One row tile: a bijection that gives
+  // the outputs of tokens 0-3 ([0, 64) and [256, 320)) to waves 6 and 7, so
+  // at batches up to MK_FUSED_B the other waves issue no stores and the next
+  // task's loads on them do not retire behind these (the memory counter
+  // retires in order).
+  auto qkv_out = [&](int k) -> int {
+    const int x = tid();
+    if constexpr (MT == 1) return x < 192 ? x + 64 : x < 384 ? x + 128 : x < 448 ? x - 384 : x - 192;
+    return x + k * MK_WG_THREADS;
+  };
   const int kc = P.H / 32;
   const size_t pstride = (size_t)kc * 512;
   const int qd = P.QH * P.D, kvd = P.KVH * P.D, D = P.D, PS = P.PS;
@@ -1130,14 +1249,14 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   float rc[NO], rs[NO];
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
-    const int o = tid() + k * MK_WG_THREADS;
+    const int o = qkv_out(k);
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16;
     const int b = mt * 16 + m;
     seq[k] = (pp < np && b < P.B) ? P.seq_lens[b] : 0;
   }
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
-    const int o = tid() + k * MK_WG_THREADS;
+    const int o = qkv_out(k);
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
     const int n = (p0 + pp) * 16 + nn;
@@ -1163,10 +1282,12 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
   mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
-  const Pub KV(P.kv + l * P.s_kv_l), Q(P.q);
+  const Pub KV(P.kv + l * P.s_kv_l), Q(P.q), QT(P.qt), KVT(P.kvt);
+  const bool tg = P.tagged != 0;
+  const uint32_t tag = step_tag(P, l);
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
-    const int o = tid() + k * MK_WG_THREADS;
+    const int o = qkv_out(k);
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m;
     if (pp >= np || b >= P.B) continue;
@@ -1187,19 +1308,29 @@ __device__ __forceinline__ void op_qkv(const mk_params& P, const mk_task& t, Sme
       const float x0 = odd ? yp : y, x1 = odd ? y : yp;
       const float r = odd ? (x0 * sn + x1 * c) : (x0 * c - x1 * sn);
       if (n < qd) {
-        Q.stf(b * qd + n, r);
-      } else if (page_ok) {
+        if (tg)
+          QT.st_tagged(b * qd + n, __float_as_uint(r), tag);
+        else
+          Q.stf(b * qd + n, r);
+      } else {
         const int g = (n - qd) / D;
-        KV.st16(((page[k] * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d, (uint16_t)f2bf(r));
+        const uint32_t kb = f2bf(r);
+        if (page_ok) KV.st16(((page[k] * 2 + 0) * P.KVH + g) * PS * D + (pos % PS) * D + d, (uint16_t)kb);
+        if (tg) KVT.st_tagged(((b * P.KVH + g) * 2 + 0) * D + d, kb, tag);
       }
-    } else if (page_ok) {
+    } else {
       const int nn2 = n - qd - kvd;
       const int g = nn2 / D, d = nn2 % D;
-      KV.st16(((page[k] * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS), (uint16_t)f2bf(y));
+      const uint32_t vb = f2bf(y);
+      if (page_ok) KV.st16(((page[k] * 2 + 1) * P.KVH + g) * PS * D + d * PS + (pos % PS), (uint16_t)vb);
+      if (tg) KVT.st_tagged(((b * P.KVH + g) * 2 + 1) * D + d, vb, tag);
     }
     if (!page_ok) raise_error(P, MK_DEVERR_FAULT, 3000 + b, (uint32_t)page[k]);
   }
-  arrive_nr(P, t.sig_ctr[0]);
+  // (tagged: attention polls the words; the stores retire on their own, and
+  // the next task on this unit does not wait for them: only waves 6 and 7
+  // stored at batches up to MK_FUSED_B)
+  if (!tg) arrive_nr(P, t.sig_ctr[0]);
 }
 
 // ------------------------------------------------------------- residual
@@ -2670,7 +2801,10 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
 #else
     run_task_mt<D, MT>(P, t, sm);
 #endif
-    __syncthreads();
+    // (LDS only: a task's stores need no draining here; every hand-off
+    // through a counter drains before its arrival, and tagged words carry
+    // their own readiness)
+    lds_sync();
     if (P.trace && tid() == 0) {
       // per-task timestamps (100 MHz device clock): start, waits satisfied,
       // op-defined marks, end

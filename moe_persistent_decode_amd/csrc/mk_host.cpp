@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -103,7 +104,7 @@ void add_wait(mk_task& t, int c, int tgt) {
 // for the handle's allocation and for the static array of the allocation-free
 // step; `ctr` (one counter set) and `total` count only in the static array.
 struct ScratchLayout {
-  size_t h, ssq, u, q, o, part, ao, rp, tki, tkw, route, gu, dn, mp, lmv, lma, err, ctr, total;
+  size_t h, ssq, u, q, o, part, ao, rp, tki, tkw, route, gu, dn, mp, lmv, lma, qt, kvt, err, ctr, total;
 };
 
 struct mk_handle {
@@ -135,6 +136,7 @@ struct mk_handle {
   void* scratch = nullptr;
   uint16_t* u = nullptr;
   uint16_t* o = nullptr;
+  uint64_t* qt = nullptr;  // tagged queries (batches up to MK_FUSED_B)
   float *h = nullptr, *q = nullptr, *part = nullptr, *ao = nullptr, *ssq = nullptr, *rp = nullptr,
         *tk_w = nullptr, *gu = nullptr, *dn = nullptr, *mp = nullptr, *lm_val = nullptr;
   int32_t *tk_idx = nullptr, *route = nullptr, *lm_arg = nullptr;
@@ -146,6 +148,8 @@ struct mk_handle {
   std::vector<bool> layer_loaded;
   bool globals_loaded = false;
   uint64_t steps = 0;
+  uint32_t epoch = 0;  // the last step's epoch in the handle's scratch (tags of tagged hand-offs)
+  bool last_tagged = false;  // the last step handed its queries to attention as tagged words
   int64_t timeout_ticks = 200000000;  // 2 s at 100 MHz
   int32_t* tk_trace = nullptr;
   uint32_t* task_trace = nullptr;
@@ -211,6 +215,8 @@ mk_status validate_config(const mk_config* c) {
   }
   if (c->vocab <= 0 || c->vocab % 16) return fail(nullptr, MK_ERR_UNSUPPORTED, "vocab must be a multiple of 16");
   if (c->n_layers <= 0) return fail(nullptr, MK_ERR_INVALID_ARG, "n_layers must be positive");
+  // (a tagged hand-off names its layer in the low 8 bits of the tag, 0 reserved)
+  if (c->n_layers > 254) return fail(nullptr, MK_ERR_UNSUPPORTED, "n_layers must be at most 254");
   if (c->page_size != 16) return fail(nullptr, MK_ERR_UNSUPPORTED, "page_size must be 16");
   if (c->window < 0 || c->full_every < 1) return fail(nullptr, MK_ERR_INVALID_ARG, "bad window pattern");
   if (c->max_batch < 1 || c->max_batch > 32) return fail(nullptr, MK_ERR_UNSUPPORTED, "max_batch must be in [1, 32]");
@@ -1567,6 +1573,9 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   y.mp = stake((size_t)std::max(h->n_workers, 1) * MK_FUSED_B * H * 4);
   y.lmv = stake((size_t)Bm * h->n_lm_tasks * 4);
   y.lma = stake((size_t)Bm * h->n_lm_tasks * 4);
+  // tagged hand-offs (batches up to MK_FUSED_B); zero, which no tag equals
+  y.qt = stake((size_t)std::min(Bm, MK_FUSED_B) * h->q_dim * 8);
+  y.kvt = stake((size_t)std::min(Bm, MK_FUSED_B) * KVH * 2 * D * 8);
   y.err = stake(16);
   const size_t scratch_bytes = so;
   // counters: capacity for the largest batch
@@ -1591,6 +1600,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->mp = (float*)(sb + y.mp);
   h->lm_val = (float*)(sb + y.lmv);
   h->lm_arg = (int32_t*)(sb + y.lma);
+  h->qt = (uint64_t*)(sb + y.qt);
   h->err_word = (uint32_t*)(sb + y.err);
   for (int i = 0; i < 2; ++i) {
     if (hipMalloc(&h->ctr[i], (size_t)h->n_ctr_cap * 4) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "counters");
@@ -1754,6 +1764,8 @@ static void scratch_at(const mk_handle* h, char* base, mk_params& P) {
   P.mp = (float*)(base + y.mp);
   P.lm_val = (float*)(base + y.lmv);
   P.lm_arg = (int32_t*)(base + y.lma);
+  P.qt = (uint64_t*)(base + y.qt);
+  P.kvt = (uint64_t*)(base + y.kvt);
   P.err = (uint32_t*)(base + y.err);
 }
 
@@ -1822,6 +1834,20 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.timeout_ticks = h->timeout_ticks;
 }
 
+// Epochs 1 .. 2^24 - 1, in turn (0 is never a tag's epoch: scratch starts zeroed).
+static std::atomic<uint32_t> g_static_epoch[MK_MAX_DEVICES];
+static uint32_t next_epoch(uint32_t* e) {
+  *e = *e >= 0xFFFFFFu ? 1u : *e + 1u;
+  return *e;
+}
+static uint32_t next_epoch(std::atomic<uint32_t>* e) {
+  uint32_t cur = e->load(), nxt;
+  do {
+    nxt = cur >= 0xFFFFFFu ? 1u : cur + 1u;
+  } while (!e->compare_exchange_weak(cur, nxt));
+  return nxt;
+}
+
 // One decode step; `noalloc`: the allocation-free variant (static scratch,
 // counters zeroed by a fill kernel, only cached schedules).
 static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
@@ -1870,6 +1896,12 @@ static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int
   // the lengths limit on the device is the hint (the schedule's splits cover it)
   P.max_seq = max_seq_len_hint;
   uint32_t* clear_next = nullptr;
+  // Tagged hand-offs name the step by an epoch that differs from the last
+  // one written into the same scratch: per handle, and for the static array
+  // (shared by every handle on the device) per device.
+  P.tagged = batch <= MK_FUSED_B ? 1 : 0;
+  h->last_tagged = P.tagged != 0;
+  P.tag_base = (noalloc ? next_epoch(&g_static_epoch[h->device]) : next_epoch(&h->epoch)) << 8;
   if (noalloc) {
     // the static array keeps the last call's contents: only the counters must
     // start at zero (every other buffer is written before it is read)
@@ -2081,6 +2113,16 @@ mk_status mk_debug_read(mk_handle* h, const char* name, void* host, size_t bytes
       if (bytes > it.sz) return fail(h, MK_ERR_INVALID_ARG, "%s holds %zu bytes", name, it.sz);
       HIPCHECK(h, hipSetDevice(h->device));
       HIPCHECK(h, hipDeviceSynchronize());
+      if (std::strcmp(name, "q") == 0 && h->last_tagged) {
+        // the last step handed the queries over as tagged words: their values
+        const size_t rows = std::min<size_t>(Bm, MK_FUSED_B), n = rows * h->q_dim;
+        std::vector<uint64_t> w(n);
+        HIPCHECK(h, hipMemcpy(w.data(), h->qt, n * 8, hipMemcpyDeviceToHost));
+        std::memset(host, 0, bytes);
+        uint32_t* dst = (uint32_t*)host;
+        for (size_t i = 0; i < n && i < bytes / 4; ++i) dst[i] = (uint32_t)w[i];
+        return MK_OK;
+      }
       HIPCHECK(h, hipMemcpy(host, it.p, bytes, hipMemcpyDeviceToHost));
       return MK_OK;
     }

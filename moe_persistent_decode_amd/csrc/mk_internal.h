@@ -158,6 +158,14 @@ struct mk_params {
                              // start, waits satisfied, mark 0, mark 1, end, mark 2, mark 3
   int32_t trace_base;        // index of this launch's first task in the trace
   int64_t timeout_ticks;     // wait time limit in s_memrealtime ticks (100 MHz)
+  // Tagged hand-offs (batches up to MK_FUSED_B): a producer stores each value
+  // with the tag of its step and layer in one 8-byte word, and a consumer
+  // polls the words themselves, so no store has to be acknowledged and no
+  // counter has to travel before the data is used.
+  int32_t tagged;            // 1: the QKV outputs reach attention as tagged words
+  uint32_t tag_base;         // this step's epoch << 8; layer l's tag is tag_base | (l + 1)
+  uint64_t* qt;              // [B][QH*D] rotated queries (float bits | tag << 32)
+  uint64_t* kvt;             // [B][KVH][2][D] the new token's key and value (bf16 bits | tag << 32)
 };
 
 struct mk_handle;
