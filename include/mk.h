@@ -311,8 +311,13 @@ mk_status mk_stream_read(const void* buf, size_t bytes, void* stream);
  * a consumer read older than the round it had been signalled for; *timeouts:
  * waits that gave up (20 ms each; a pair stops at its first timeout or stale
  * read, so the kernel always ends). coherent = 0 uses plain loads and stores
- * for the message instead (the contrast). MK_ERR_INVALID_ARG for pairs
- * outside [1, 512], rounds outside [1, 1e6] or null outputs. */
+ * for the message instead (the contrast). coherent = 2 checks the tagged
+ * hand-off instead: the producer stores 16 words of (value, round) with one
+ * 8-byte device-coherent store each and neither drains nor signals; the
+ * consumer polls the words (16-byte loads) until every tag is the round's,
+ * and *stale counts words whose value is not the one stored with that tag.
+ * MK_ERR_INVALID_ARG for pairs outside [1, 512], rounds outside [1, 1e6],
+ * coherent outside [0, 2] or null outputs. */
 mk_status mk_litmus_message_passing(int device, int pairs, int rounds, int coherent, uint32_t* stale,
                                     uint32_t* timeouts);
 

@@ -151,12 +151,13 @@ def stream_read(buf, stream=None) -> None:
         raise MkError(st, lib.mk_last_error(None).decode())
 
 
-def litmus_message_passing(pairs: int, rounds: int, coherent: bool = True, device: int = 0):
+def litmus_message_passing(pairs: int, rounds: int, coherent=True, device: int = 0):
     """mk_litmus_message_passing: (stale reads, timeouts) over `pairs` workgroup
-    pairs on different XCDs passing `rounds` messages each."""
+    pairs on different XCDs passing `rounds` messages each; coherent: True,
+    False (plain accesses) or "tagged" (the tagged-word hand-off)."""
+    mode = 2 if coherent == "tagged" else (1 if coherent else 0)
     stale, timeouts = ctypes.c_uint32(0), ctypes.c_uint32(0)
-    st = lib.mk_litmus_message_passing(device, pairs, rounds, 1 if coherent else 0, ctypes.byref(stale),
-                                       ctypes.byref(timeouts))
+    st = lib.mk_litmus_message_passing(device, pairs, rounds, mode, ctypes.byref(stale), ctypes.byref(timeouts))
     if st != 0:
         raise MkError(st, lib.mk_last_error(None).decode())
     return stale.value, timeouts.value

@@ -1461,7 +1461,7 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
 // completes the router does ROUTER_TOPK + ROUTE_FINALIZE (megakernel post,
 // section "Tasks"): sum the partials in fixed order, top-k (ties to the lower
 // expert index), softmax over the kept logits, the expert work queue.
-__device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm, bool publish);
+__device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm, bool publish);
 __device__ __forceinline__ void route_trivial(const mk_params& P, int l, Smem& sm, bool norm);
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm);
 
@@ -1484,11 +1484,19 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
   mfma_tiles(acc, w, Ah, Al);
   reduce_tiles(acc, sm);
   mark(sm, 1);
-  const Pub RP(rp_of(P, l));
+  const Pub RP(rp_of(P, l)), RPT(P.rpt);
+  const bool tg = P.tagged != 0;
+  const uint32_t tag = step_tag(P, l);
   for (int o = tid(); o < 2 * MT * 256; o += MK_WG_THREADS) {
     const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
     const int b = mt * 16 + m, e = (p0 + pp) * 16 + nn;
-    if (pp < np && b < P.B && e < P.E) RP.stf((ks * P.B + b) * P.E + e, sm.out[o] * sm.inv_rms[b]);
+    if (pp < np && b < P.B && e < P.E) {
+      const float v = sm.out[o] * sm.inv_rms[b];
+      RP.stf((ks * P.B + b) * P.E + e, v);
+      // (tagged: the fused MoE claimers poll these; the arrival below is for
+      // the task that publishes the route)
+      if (tg) RPT.st_tagged((b * P.E + e) * 4 + ks, __float_as_uint(v), tag);
+    }
   }
   const int old = arrive(P, t.a[5], sm);
   if (old == P.n_router_tasks - 1) {
@@ -1508,10 +1516,14 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
 // in LDS (sm.rt_*, the routing weights in sm.tkw) and, with publish, stored for
 // the other compute units. Without publish, layer l's sums of squares load
 // alongside the router logits (then sm.inv_rms).
-__device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm, bool publish) {
+__device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm, bool publish) {
   const int E = P.E, K = P.K, B = P.B;
-  const Pub R(rp_of(P, l)), TI(tki_of(P, l)), TW(tkw_of(P, l)), RT(route_of(P, l));
+  const Pub R(rp_of(P, l)), TI(tki_of(P, l)), TW(tkw_of(P, l)), RT(route_of(P, l)), RPT(P.rpt);
   SmemTopk& T = sm.u.tk;
+  // a fused claimer with tagged hand-offs polls the partials' tagged words
+  // (sm.flag is 1 from its wait and drops to 0 on a failed poll)
+  const bool poll = !publish && P.tagged != 0;
+  const uint32_t tag = step_tag(P, l);
   float sq[2];  // B * NB <= 1024
   if (!publish) {
     const Pub S(ssq_of(P, l));
@@ -1523,8 +1535,36 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
   }
   for (int i = tid(); i < B * E; i += MK_WG_THREADS) {
     float p[MK_MAX_RKS];
+    if (poll) {
+      const int ks = P.router_ks;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      uint32_t spins = 0;
+      u32x4_t a = RPT.ld_tagged2(4 * i), c = RPT.ld_tagged2(4 * i + 2);
+      while (!((a[1] == tag || ks < 1) && (a[3] == tag || ks < 2) && (c[1] == tag || ks < 3) &&
+               (c[3] == tag || ks < 4))) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++spins & 63u) == 0) {
+          if (ld_relaxed(&P.err[0]) != 0) {
+            sm.flag = 0;
+            break;
+          }
+          if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > P.timeout_ticks) {
+            raise_error(P, MK_DEVERR_TIMEOUT, 0xffff0000u | (uint32_t)(4 * i), a[1]);
+            sm.flag = 0;
+            break;
+          }
+        }
+        a = RPT.ld_tagged2(4 * i);
+        c = RPT.ld_tagged2(4 * i + 2);
+      }
+      p[0] = __uint_as_float(a[0]);
+      p[1] = __uint_as_float(a[2]);
+      p[2] = __uint_as_float(c[0]);
+      p[3] = __uint_as_float(c[2]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < MK_MAX_RKS; ++k) p[k] = k < P.router_ks ? R.ldf(k * B * E + i) : 0.f;
+      for (int k = 0; k < MK_MAX_RKS; ++k) p[k] = k < P.router_ks ? R.ldf(k * B * E + i) : 0.f;
+    }
     float v = 0.f;
 #pragma unroll
     for (int k = 0; k < MK_MAX_RKS; ++k)
@@ -1654,6 +1694,7 @@ __device__ __forceinline__ void route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   lds_sync();
+  return !poll || sm.flag != 0;
 }
 
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm) { route_build(P, l, sm, true); }
@@ -2276,8 +2317,15 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   // the layer input and the router's partial logits complete (one wait):
   // the input's loads, then this claimer's own top-k and route (whose loads
   // share the input's round trip), then the input into LDS
-  if (!wait_task(P, t, sm)) return;
+  // (tagged: only the input's counter; the router's partials are polled as
+  // tagged words in the same round trip as the input's loads)
+  if (!DENSE && P.tagged) {
+    if (!wait_one(P, t.wait_ctr[0], t.wait_tgt[0], sm)) return;
+  } else if (!wait_task(P, t, sm)) {
+    return;
+  }
   mark(sm, 0);
+  bool routed = true;
   {
     const Pub Uh(u_of(P, l, 0)), Ul(u_of(P, l, 1));
     const int n8 = B * H / 8;  // 8 bf16 per thread and load
@@ -2291,7 +2339,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     if constexpr (DENSE)
       route_trivial(P, l, sm, true);
     else
-      route_build(P, l, sm, false);
+      routed = route_build(P, l, sm, false);
 #pragma unroll
     for (int k = 0; k < MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS; ++k) {
       const int i = tid() + k * MK_WG_THREADS;
@@ -2302,6 +2350,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     }
     lds_sync();
   }
+  if (!routed) return;
   const uint16_t* xh = xs;
   const uint16_t* xl = xs + MK_FUSED_B * MK_MAX_H;
   mark(sm, 1);
@@ -2915,7 +2964,8 @@ extern "C" __global__ __launch_bounds__(512) void mk_stream_read_words(const u32
 // 0 the message is written and read with plain accesses instead (the
 // contrast). Every wait gives up after limit_ticks (100 MHz) and is counted;
 // a pair stops at its first timeout or stale read, so the kernel always ends.
-// result[2p] stale reads, result[2p + 1] timeouts.
+// result[2p] stale reads, result[2p + 1] timeouts. With coherent = 2 the
+// message is the tagged words of the step's small hand-offs instead.
 __device__ __forceinline__ bool litmus_wait(const uint32_t* f, uint32_t want, int64_t limit) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (ld_relaxed(f) < want) {
@@ -2936,7 +2986,49 @@ extern "C" __global__ __launch_bounds__(64) void mk_litmus_mp(uint32_t* msg, uin
   if (ln == 0) stop = 0;
   __syncthreads();
   uint32_t stale = 0, timeouts = 0;
-  for (int r = 1; r <= rounds; ++r) {
+  // tagged (coherent = 2): the message is 16 tagged words (value, round) that
+  // the consumer polls itself, with no drain or flag on the producer's side;
+  // a word whose value is not the one written with its tag counts as stale
+  auto value_of = [](int r, int i) { return (uint32_t)r * 0x9E3779B1u + (uint32_t)i * 0x85EBCA77u; };
+  for (int r = 1; r <= rounds && coherent == 2; ++r) {
+    if (producer) {
+      if (ln == 0 && !litmus_wait(ack + p, (uint32_t)(r - 1), limit)) stop = 1;
+      __syncthreads();
+      if (stop) {
+        timeouts += ln == 0;
+        break;
+      }
+      if (ln < 16) M.st_tagged(ln, value_of(r, ln), (uint32_t)r);
+    } else {
+      bool bad = false;
+      if (ln < 8) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        u32x4_t v = M.ld_tagged2(2 * ln);
+        while (v[1] != (uint32_t)r || v[3] != (uint32_t)r) {
+          if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > limit) {
+            stop = 1;
+            break;
+          }
+          v = M.ld_tagged2(2 * ln);
+        }
+        bad = !stop && (v[0] != value_of(r, 2 * ln) || v[2] != value_of(r, 2 * ln + 1));
+      }
+      __syncthreads();
+      if (stop) {
+        timeouts += ln == 0;
+        break;
+      }
+      const uint64_t ballot = __ballot(bad);
+      if (ballot) {
+        stale += ln == 0 ? (uint32_t)__popcll(ballot) : 0u;
+        if (ln == 0) stop = 1;
+      }
+      __syncthreads();
+      if (ln == 0) __hip_atomic_fetch_add(ack + p, stop ? (1u << 30) : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (stop) break;
+    }
+  }
+  for (int r = 1; r <= rounds && coherent != 2; ++r) {
     if (producer) {
       if (ln == 0 && !litmus_wait(ack + p, (uint32_t)(r - 1), limit)) stop = 1;
       __syncthreads();

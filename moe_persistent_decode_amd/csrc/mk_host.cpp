@@ -104,7 +104,7 @@ void add_wait(mk_task& t, int c, int tgt) {
 // for the handle's allocation and for the static array of the allocation-free
 // step; `ctr` (one counter set) and `total` count only in the static array.
 struct ScratchLayout {
-  size_t h, ssq, u, q, o, part, ao, rp, tki, tkw, route, gu, dn, mp, lmv, lma, qt, kvt, err, ctr, total;
+  size_t h, ssq, u, q, o, part, ao, rp, tki, tkw, route, gu, dn, mp, lmv, lma, qt, kvt, rpt, err, ctr, total;
 };
 
 struct mk_handle {
@@ -1576,6 +1576,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   // tagged hand-offs (batches up to MK_FUSED_B); zero, which no tag equals
   y.qt = stake((size_t)std::min(Bm, MK_FUSED_B) * h->q_dim * 8);
   y.kvt = stake((size_t)std::min(Bm, MK_FUSED_B) * KVH * 2 * D * 8);
+  y.rpt = stake((size_t)std::min(Bm, MK_FUSED_B) * E * 4 * 8);
   y.err = stake(16);
   const size_t scratch_bytes = so;
   // counters: capacity for the largest batch
@@ -1766,6 +1767,7 @@ static void scratch_at(const mk_handle* h, char* base, mk_params& P) {
   P.lm_arg = (int32_t*)(base + y.lma);
   P.qt = (uint64_t*)(base + y.qt);
   P.kvt = (uint64_t*)(base + y.kvt);
+  P.rpt = (uint64_t*)(base + y.rpt);
   P.err = (uint32_t*)(base + y.err);
 }
 
@@ -2013,8 +2015,10 @@ mk_status mk_stream_read(const void* buf, size_t bytes, void* stream) {
 
 mk_status mk_litmus_message_passing(int device, int pairs, int rounds, int coherent, uint32_t* stale,
                                     uint32_t* timeouts) {
-  if (pairs < 1 || pairs > 512 || rounds < 1 || rounds > 1000000 || !stale || !timeouts)
-    return fail(nullptr, MK_ERR_INVALID_ARG, "litmus: pairs in [1, 512], rounds in [1, 1e6], non-null outputs");
+  if (pairs < 1 || pairs > 512 || rounds < 1 || rounds > 1000000 || coherent < 0 || coherent > 2 || !stale ||
+      !timeouts)
+    return fail(nullptr, MK_ERR_INVALID_ARG,
+                "litmus: pairs in [1, 512], rounds in [1, 1e6], coherent in [0, 2], non-null outputs");
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
     return fail(nullptr, MK_ERR_INVALID_ARG, "litmus: bad device %d", device);

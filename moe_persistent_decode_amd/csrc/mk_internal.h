@@ -162,10 +162,12 @@ struct mk_params {
   // with the tag of its step and layer in one 8-byte word, and a consumer
   // polls the words themselves, so no store has to be acknowledged and no
   // counter has to travel before the data is used.
-  int32_t tagged;            // 1: the QKV outputs reach attention as tagged words
+  int32_t tagged;            // 1: the QKV outputs reach attention, and the router's partial
+                             // logits the fused MoE claimers, as tagged words
   uint32_t tag_base;         // this step's epoch << 8; layer l's tag is tag_base | (l + 1)
   uint64_t* qt;              // [B][QH*D] rotated queries (float bits | tag << 32)
   uint64_t* kvt;             // [B][KVH][2][D] the new token's key and value (bf16 bits | tag << 32)
+  uint64_t* rpt;             // [B*E][4] router logit partials, K split k in word k (float bits | tag << 32)
 };
 
 struct mk_handle;

@@ -436,3 +436,12 @@ def test_no_read_before_arrive_at_full_size(name, batch, ctx):
     st, rep = d.check_hazards(batch, ctx)
     assert st == 0, rep
     d.close()
+
+
+def test_litmus_rejects_bad_arguments_on_the_host():
+    """mk_litmus_message_passing checks its sizes and mode before any device
+    call: pairs in [1, 512], rounds in [1, 1e6], coherent in [0, 2]."""
+    from moe_persistent_decode_amd.binding import lib
+    s, t = ctypes.c_uint32(0), ctypes.c_uint32(0)
+    for pairs, rounds, mode in [(0, 10, 1), (513, 10, 1), (4, 0, 1), (4, 10, 3), (4, 10, -1)]:
+        assert lib.mk_litmus_message_passing(0, pairs, rounds, mode, ctypes.byref(s), ctypes.byref(t)) == 1

@@ -146,7 +146,9 @@ def test_cross_xcd_message_passing_sees_no_stale_read():
     """The hand-off protocol of every task (device-coherent stores, a drain, a
     relaxed device-scope counter increment; polls and device-coherent reads on
     the other side) between 128 workgroup pairs on different XCDs, 2000
-    messages each: no stale word, no wait that gave up. The same run with
+    messages each: no stale word, no wait that gave up. The tagged-word
+    hand-off (value and tag in one 8-byte store, no drain or counter; the
+    reader polls the words): every value read belongs to its tag. The same run with
     plain accesses for the message is reported for contrast (not asserted:
     whether a stale line is seen there depends on timing)."""
     import moe_persistent_decode_amd as mk
@@ -154,5 +156,8 @@ def test_cross_xcd_message_passing_sees_no_stale_read():
     stale, timeouts = mk.litmus_message_passing(128, 2000, coherent=True)
     say(f"  device-coherent: stale {stale}, timeouts {timeouts}")
     assert stale == 0 and timeouts == 0
+    stale_t, timeouts_t = mk.litmus_message_passing(128, 2000, coherent="tagged")
+    say(f"  tagged words: torn {stale_t}, timeouts {timeouts_t}")
+    assert stale_t == 0 and timeouts_t == 0
     stale_p, timeouts_p = mk.litmus_message_passing(128, 2000, coherent=False)
     say(f"  plain accesses: stale {stale_p}, timeouts {timeouts_p}")

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # instantiation (head dim, row tiles) -> most VGPR spills allowed; SGPR spills
 # (to VGPR lanes, no memory traffic; the dense FFN claimer's own instance
 # roughly doubles them) are bounded loosely
-VGPR_SPILLS = {(64, 1): 7, (64, 2): 3, (128, 1): 7, (128, 2): 3}
+VGPR_SPILLS = {(64, 1): 7, (64, 2): 3, (128, 1): 8, (128, 2): 3}
 SGPR_SPILLS_MAX = 350
 
 
