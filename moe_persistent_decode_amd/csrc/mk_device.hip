@@ -1462,6 +1462,8 @@ __device__ __forceinline__ void op_oproj(const mk_params& P, const mk_task& t, S
 // section "Tasks"): sum the partials in fixed order, top-k (ties to the lower
 // expert index), softmax over the kept logits, the expert work queue.
 __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm, bool publish);
+__device__ __forceinline__ bool route_rank(const mk_params& P, int l, Smem& sm, bool publish, int& n_active);
+__device__ __forceinline__ void route_finish(const mk_params& P, int l, Smem& sm, bool publish, int n_active);
 __device__ __forceinline__ void route_trivial(const mk_params& P, int l, Smem& sm, bool norm);
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm);
 
@@ -1516,9 +1518,21 @@ __device__ __forceinline__ void op_router(const mk_params& P, const mk_task& t, 
 // in LDS (sm.rt_*, the routing weights in sm.tkw) and, with publish, stored for
 // the other compute units. Without publish, layer l's sums of squares load
 // alongside the router logits (then sm.inv_rms).
+// In two parts: route_rank (the logits, each token's top k, the active
+// experts in ascending order with their token counts, and their number) and
+// route_finish (the routing weights, each active expert's slots, the header
+// and, without publish, the layer input's 1/rms); a fused claimer issues its
+// first item's weights between them.
 __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm, bool publish) {
+  int n_active = 0;
+  const bool ok = route_rank(P, l, sm, publish, n_active);
+  route_finish(P, l, sm, publish, n_active);
+  return ok;
+}
+
+__device__ __forceinline__ bool route_rank(const mk_params& P, int l, Smem& sm, bool publish, int& n_active) {
   const int E = P.E, K = P.K, B = P.B;
-  const Pub R(rp_of(P, l)), TI(tki_of(P, l)), TW(tkw_of(P, l)), RT(route_of(P, l)), RPT(P.rpt);
+  const Pub R(rp_of(P, l)), RT(route_of(P, l)), RPT(P.rpt);
   SmemTopk& T = sm.u.tk;
   // a fused claimer with tagged hand-offs polls the partials' tagged words
   // (sm.flag is 1 from its wait and drops to 0 on a failed poll)
@@ -1590,7 +1604,6 @@ __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   lds_sync();
-  if (!publish) inv_rms_lds(P, sm);
   // rank of (b, e): the keys above its own
   auto keep = [&](int b, int e, int rank) {
     if (rank < K) {
@@ -1636,21 +1649,6 @@ __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   lds_sync();
-  for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
-    // softmax over the kept logits (max-subtracted; rank 0 is the max),
-    // summed in rank order
-    const int b = i / K, j = i % K;
-    const float top = T.sel_val[b][0];
-    float sum = 0.f;
-    for (int jj = 0; jj < K; ++jj) sum += __expf(T.sel_val[b][jj] - top);
-    const float w = __expf(T.sel_val[b][j] - top) / sum;
-    sm.tkw[i] = w;
-    if (publish) {
-      TI.sti(i, T.sel_idx[b][j]);
-      TW.stf(i, w);
-      if (P.tk_trace) P.tk_trace[((size_t)l * B + b) * K + j] = T.sel_idx[b][j];
-    }
-  }
   // the experts' positions among the active ones from two wave ballots, and
   // each slot's rank within its expert (tokens in ascending order)
   if (tid() < 128) {
@@ -1661,7 +1659,7 @@ __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm,
   }
   lds_sync();
   const uint64_t b0 = T.ballot[0], b1 = E > 64 ? T.ballot[1] : 0ull;
-  const int n_active = __popcll(b0) + __popcll(b1);
+  n_active = __popcll(b0) + __popcll(b1);
   if ((int)tid() < E) {
     const int e = tid();
     const uint32_t mask = T.tokmask[e];
@@ -1677,6 +1675,29 @@ __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   lds_sync();
+  return !poll || sm.flag != 0;
+}
+
+__device__ __forceinline__ void route_finish(const mk_params& P, int l, Smem& sm, bool publish, int n_active) {
+  const int E = P.E, K = P.K, B = P.B;
+  const Pub TI(tki_of(P, l)), TW(tkw_of(P, l)), RT(route_of(P, l));
+  SmemTopk& T = sm.u.tk;
+  if (!publish) inv_rms_lds(P, sm);
+  for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
+    // softmax over the kept logits (max-subtracted; rank 0 is the max),
+    // summed in rank order
+    const int b = i / K, j = i % K;
+    const float top = T.sel_val[b][0];
+    float sum = 0.f;
+    for (int jj = 0; jj < K; ++jj) sum += __expf(T.sel_val[b][jj] - top);
+    const float w = __expf(T.sel_val[b][j] - top) / sum;
+    sm.tkw[i] = w;
+    if (publish) {
+      TI.sti(i, T.sel_idx[b][j]);
+      TW.stf(i, w);
+      if (P.tk_trace) P.tk_trace[((size_t)l * B + b) * K + j] = T.sel_idx[b][j];
+    }
+  }
   for (int i = tid(); i < B * K; i += MK_WG_THREADS) {
     const int b = i / K, e = T.sel_idx[b][i % K];
     const int r = __popc(T.tokmask[e] & ((1u << b) - 1u));
@@ -1694,7 +1715,6 @@ __device__ __forceinline__ bool route_build(const mk_params& P, int l, Smem& sm,
     }
   }
   lds_sync();
-  return !poll || sm.flag != 0;
 }
 
 __device__ __forceinline__ void topk_finalize(const mk_params& P, int l, Smem& sm) { route_build(P, l, sm, true); }
@@ -2325,7 +2345,6 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     return;
   }
   mark(sm, 0);
-  bool routed = true;
   {
     const Pub Uh(u_of(P, l, 0)), Ul(u_of(P, l, 1));
     const int n8 = B * H / 8;  // 8 bf16 per thread and load
@@ -2336,10 +2355,19 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
       vh[k] = i < n8 ? Uh.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
       vl[k] = i < n8 ? Ul.ld16x8(8 * i) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    if constexpr (DENSE)
+    if constexpr (DENSE) {
       route_trivial(P, l, sm, true);
-    else
-      routed = route_build(P, l, sm, false);
+    } else {
+      // the active experts, then this claimer's share and its first item's
+      // three weight units, then the rest of the route while they stream
+      int n_active = 0;
+      if (!route_rank(P, l, sm, false, n_active)) return;
+      fused_share(sk, nf, nt, wa, n_active * S, lo, hi);
+      up_load(wu0, lo, 0);
+      up_load(wu1, lo, 1);
+      down_load(wdn, lo);
+      route_finish(P, l, sm, false, n_active);
+    }
 #pragma unroll
     for (int k = 0; k < MK_FUSED_B * MK_MAX_H / 8 / MK_WG_THREADS; ++k) {
       const int i = tid() + k * MK_WG_THREADS;
@@ -2350,17 +2378,9 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     }
     lds_sync();
   }
-  if (!routed) return;
   const uint16_t* xh = xs;
   const uint16_t* xl = xs + MK_FUSED_B * MK_MAX_H;
   mark(sm, 1);
-  if constexpr (!DENSE) {
-    const int n_items = __builtin_amdgcn_readfirstlane(sm.rt_hdr[0]) * S;
-    fused_share(sk, nf, nt, wa, n_items, lo, hi);
-    up_load(wu0, lo, 0);
-    up_load(wu1, lo, 1);
-    down_load(wdn, lo);
-  }
   float acc[NJ][MK_FUSED_B];
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
