@@ -274,6 +274,17 @@ mk_status mk_set_schedule_options(mk_handle* h, int wave_order, int placement);
  * schedules like mk_set_schedule_options. */
 mk_status mk_set_placement_seed(mk_handle* h, uint64_t seed);
 
+/* Debug: with on != 0, fill every per-step scratch buffer before each step
+ * (activations, partials, routing, LM-head candidates; not the KV pool, the
+ * counters or the error word) with NaN (float 0xffffffff, bf16 0xffff), the
+ * index buffers with 0 and tagged words with NaN and tag 0, so that a task
+ * reading a value before its producer wrote it turns the logits to NaN or
+ * the step into a device fault report instead of passing with stale data
+ * (the post's barrier section warns that a wrong arrival count can let
+ * readers drift and fail much later). A correct schedule decodes the same
+ * step bit for bit either way. Extra fill kernels on the step's stream. */
+mk_status mk_set_debug_poison(mk_handle* h, int on);
+
 /* Time limit of one dependency wait on the device, in microseconds (0: the
  * default, 2 s). A wait that exceeds it sets the device error word
  * (MK_ERR_DEVICE_TIMEOUT) and every workgroup drains to the end of its task

@@ -27,6 +27,7 @@ STEP_ADVANCE = 1
 EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_dense", "mk_load_globals",
            "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
+           "mk_set_debug_poison",
            "mk_set_schedule_options", "mk_set_placement_seed", "mk_decode_step_noalloc",
            "mk_service_create", "mk_service_pause", "mk_service_resume", "mk_service_alloc_pages",
            "mk_service_admit", "mk_service_evict", "mk_service_stats", "mk_service_last_error",
@@ -86,6 +87,7 @@ def _load():
     lib.mk_decode_step_noalloc.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_set_routing_trace.argtypes = [H, P]
     lib.mk_set_wait_limit.argtypes = [H, ctypes.c_uint32]
+    lib.mk_set_debug_poison.argtypes = [H, I]
     lib.mk_set_placement_seed.argtypes = [H, ctypes.c_uint64]
     lib.mk_schedule_check.argtypes = [H, I, I, ctypes.c_uint32, P, S]
     lib.mk_set_schedule_options.argtypes = [H, I, I]
@@ -260,6 +262,10 @@ class Decoder:
 
     def set_wait_limit(self, microseconds: int):
         self._check(lib.mk_set_wait_limit(self._h, int(microseconds)))
+
+    def set_debug_poison(self, on: bool):
+        """Fill the step's scratch with NaN before each step (read-before-write check)."""
+        self._check(lib.mk_set_debug_poison(self._h, 1 if on else 0))
 
     def kv_cache(self, layer: int):
         """(device address, bytes) of layer `layer`'s part of the KV pool."""

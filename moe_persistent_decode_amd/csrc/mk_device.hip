@@ -2942,6 +2942,13 @@ extern "C" __global__ __launch_bounds__(256) void mk_zero_words(uint32_t* p, int
   for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
 }
 
+// Fill n words with a pattern, word i taking lo (even i) or hi (odd i): the
+// debug poison of the step's scratch (NaN for values, an impossible tag for
+// tagged words).
+extern "C" __global__ __launch_bounds__(256) void mk_fill_words(uint32_t* p, int n, uint32_t lo, uint32_t hi) {
+  for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256) p[i] = (i & 1) ? hi : lo;
+}
+
 // The streaming-read ceiling, a diagnostic beside the megakernel's figures:
 // each workgroup (two per compute unit, 512 threads) reads one contiguous
 // range of the n16 16-byte words, 8 KB per round (consecutive lanes on
@@ -3126,6 +3133,12 @@ hipError_t mk_launch_litmus(uint32_t* msg, uint32_t* flag, uint32_t* ack, uint32
 
 hipError_t mk_launch_stream_read(const void* p, size_t n16, hipStream_t stream) {
   hipLaunchKernelGGL(mk_stream_read_words, dim3(512), dim3(512), 0, stream, (const u32x4_t*)p, n16);
+  return hipGetLastError();
+}
+
+hipError_t mk_launch_fill(uint32_t* p, int n, uint32_t lo, uint32_t hi, hipStream_t stream) {
+  const int grid = n <= 0 ? 1 : (n + 255) / 256 < 256 ? (n + 255) / 256 : 256;
+  hipLaunchKernelGGL(mk_fill_words, dim3(grid), dim3(256), 0, stream, p, n, lo, hi);
   return hipGetLastError();
 }
 

@@ -150,6 +150,7 @@ struct mk_handle {
   uint64_t steps = 0;
   uint32_t epoch = 0;  // the last step's epoch in the handle's scratch (tags of tagged hand-offs)
   bool last_tagged = false;  // the last step handed its queries to attention as tagged words
+  bool poison = false;       // debug: fill the step's scratch with NaN before each step
   int64_t timeout_ticks = 200000000;  // 2 s at 100 MHz
   int32_t* tk_trace = nullptr;
   uint32_t* task_trace = nullptr;
@@ -1850,6 +1851,8 @@ static uint32_t next_epoch(std::atomic<uint32_t>* e) {
   return nxt;
 }
 
+static hipError_t poison_scratch(const mk_handle* h, char* base, hipStream_t s);
+
 // One decode step; `noalloc`: the allocation-free variant (static scratch,
 // counters zeroed by a fill kernel, only cached schedules).
 static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int32_t* block_tables,
@@ -1918,6 +1921,7 @@ static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int
     P.ctr = h->ctr[cur];
     P.ctr_clear = clear_next = h->ctr[nxt];
   }
+  if (h->poison) HIPCHECK(h, poison_scratch(h, noalloc ? (char*)h->static_scratch : (char*)h->scratch, s));
   if (c.mode == MK_MODE_MEGAKERNEL) {
     P.tasks = S->d_cu_tasks;
     P.task_off = S->d_cu_off;
@@ -1997,6 +2001,35 @@ mk_status mk_set_placement_seed(mk_handle* h, uint64_t seed) {
   if (st != MK_OK) return st;
   h->place_seed = seed;
   return MK_OK;
+}
+
+mk_status mk_set_debug_poison(mk_handle* h, int on) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  h->poison = on != 0;
+  return MK_OK;
+}
+
+// Debug poison of one step's scratch block (laid out as h->lay): values NaN
+// (float 0xffffffff, bf16 0xffff), index buffers 0, tagged words NaN with tag
+// 0 (which no step uses); the error word and the counters are left alone.
+static hipError_t poison_scratch(const mk_handle* h, char* base, hipStream_t s) {
+  const ScratchLayout& y = h->lay;
+  const uint32_t NaN = 0xffffffffu;
+  struct Region { size_t off, end; uint32_t lo, hi; };
+  const Region rs[] = {
+      {y.h, y.tki, NaN, NaN},      // h, ssq, u, q, o, part, ao, rp
+      {y.tki, y.tkw, 0u, 0u},      // top-k ids
+      {y.tkw, y.route, NaN, NaN},  // top-k weights
+      {y.route, y.gu, 0u, 0u},     // routes
+      {y.gu, y.lma, NaN, NaN},     // gu, dn, mp, LM-head candidates
+      {y.lma, y.qt, 0u, 0u},       // LM-head candidate ids
+      {y.qt, y.err, NaN, 0u},      // tagged words
+  };
+  for (const Region& r : rs) {
+    hipError_t e = mk_launch_fill((uint32_t*)(base + r.off), (int)((r.end - r.off) / 4), r.lo, r.hi, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 mk_status mk_set_wait_limit(mk_handle* h, uint32_t microseconds) {

@@ -12,6 +12,7 @@ hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu);
 // device, then cached), and a fill kernel zeroing n words.
 hipError_t mk_static_scratch(int device, void** ptr);
 hipError_t mk_launch_zero(uint32_t* p, int n, hipStream_t stream);
+hipError_t mk_launch_fill(uint32_t* p, int n, uint32_t lo, uint32_t hi, hipStream_t stream);
 hipError_t mk_launch_stream_read(const void* p, size_t n16, hipStream_t stream);
 hipError_t mk_launch_litmus(uint32_t* msg, uint32_t* flag, uint32_t* ack, uint32_t* result, int pairs, int rounds,
                             int coherent, int64_t limit, hipStream_t stream);
