@@ -1818,22 +1818,36 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     const int r = rt * 16 + (int)(lane_id() & 15);
     return (a >= 0 && r < sm.rt_cnt[a]) ? (sm.rt_slot[a * B + r] / K) * H : -1;
   };
-  // one item's weights and routed rows (a zero tile and no rows past the queue)
-  auto load = [&](WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int k, int id) {
+  // An expert's up/gate items run K half by K half (item r of expert a:
+  // K half r / half, gate/up panel pair r % half), so the CHU items of a
+  // claimed chunk (claims are CHU-aligned, and half = F / 16 is a multiple of
+  // 8 for the supported widths, so a chunk never straddles a K half or an
+  // expert) share the routed rows of one K half, loaded once per chunk.
+  static_assert(CHU == 4, "one weight slot per item of a chunk");
+  const int half = upe / 2;
+  // one item's weights (a zero tile past the queue)
+  auto wload = [&](WTile<2, NCH>& w, int id) {
     const bool valid = id < n_items;
     const int a = valid ? id / upe : 0, r = id % upe;
-    const int tt = r >> 1, kh = r & 1;
+    const int tt = r % half, kh = r / half;
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
     wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
                valid ? 2 : 0, kh * kh_chunks, (kh + 1) * kh_chunks);
-    const int o = row_of(valid ? a : -1, 0);
-    atile_load_row(Ah, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
-    atile_load_row(Al, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
   };
-  // one item's products and gu stores; the arrival is counted in LDS
-  auto compute = [&](const WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int k, int id) {
+  // a chunk's routed rows (no rows past the queue)
+  auto rows = [&](ATile<1, NCH>& Xh, ATile<1, NCH>& Xl, int id) {
+    const bool valid = id < n_items;
+    const int a = valid ? id / upe : 0, kh = (id % upe) / half;
+    const int o = row_of(valid ? a : -1, 0);
+    atile_load_row(Xh, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+    atile_load_row(Xl, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+  };
+  // one item's products and gu stores with its chunk's rows; the arrival is
+  // counted in LDS
+  auto compute = [&](const WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int id) {
+    if (id >= n_items) return;
     const int a = id / upe, r = id % upe;
-    const int tt = r >> 1, kh = r & 1;
+    const int tt = r % half, kh = r / half;
     const int cnt = sm.rt_cnt[a];
     // (at least one row tile: an active expert has a routed token, and the
     // compiler then knows the item's loads are consumed before its registers
@@ -1864,33 +1878,65 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
         }
       }
     } while (++rt * 16 < cnt);
+    // (a later item of the chunk needs the first row tile again)
+    if (rt > 1 && id % CHU != CHU - 1) {
+      const int o = row_of(a, 0);
+      atile_load_row(Ah, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+      atile_load_row(Al, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+    }
     if (tid() == 0) sm.done_cnt[a] += 1;
   };
+  // the next claimed chunk's first item (the claim after it is issued now,
+  // read when that chunk starts)
+  auto next_chunk = [&](int& pend) -> int {
+    if (tid() == 0) sm.claim = pend;
+    lds_sync();
+    const int base = sm.claim;
+    lds_sync();
+    if (tid() == 0)
+      pend = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)CHU, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return base;
+  };
   {
-    // three items in flight: the next two items' weights stream while the
-    // current computes; the arrivals wait for the end of the phase (one drain), since
-    // down items start only after this claimer's up/gate items
-    WTile<2, NCH> w0, w1, w2;
-    ATile<1, NCH> h0, l0, h1, l1, h2, l2;
-    Stream q;
-    stream_start(q, sm.claim, claim_ctr, n_items, CHU);
-    int i0 = q.base;
-    load(w0, h0, l0, 0, i0);
-    int i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
-    load(w1, h1, l1, 1, i1);
-    int i2 = i1 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
-    while (i0 < n_items) {
-      load(w2, h2, l2, 2, i2);
-      compute(w0, h0, l0, 0, i0);
-      i0 = i2 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
-      if (i1 >= n_items) break;
-      load(w0, h0, l0, 0, i0);
-      compute(w1, h1, l1, 1, i1);
-      i1 = i0 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
-      if (i2 >= n_items) break;
-      load(w1, h1, l1, 1, i1);
-      compute(w2, h2, l2, 2, i2);
-      i2 = i1 < n_items ? stream_next(q, claim_ctr, n_items) : n_items;
+    // four items in flight, one weight slot per item of a chunk: while a
+    // chunk's items compute, the next chunk's weights take their slots one by
+    // one, and its rows go to the other row set (two chunks per loop pass, so
+    // every set index is fixed). The arrivals wait for the end of the phase
+    // (one drain), since down items start only after this claimer's up/gate
+    // items.
+    WTile<2, NCH> w0, w1, w2, w3;
+    ATile<1, NCH> X0h, X0l, X1h, X1l;
+    int pend = 0;
+    if (tid() == 0)
+      pend = (int)__hip_atomic_fetch_add(&P.ctr[claim_ctr], (uint32_t)CHU, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int c0 = sm.claim;
+    wload(w0, c0);
+    wload(w1, c0 + 1);
+    wload(w2, c0 + 2);
+    wload(w3, c0 + 3);
+    rows(X0h, X0l, c0);
+    while (c0 < n_items) {
+      const int c1 = next_chunk(pend);
+      compute(w0, X0h, X0l, c0);
+      wload(w0, c1);
+      rows(X1h, X1l, c1);
+      compute(w1, X0h, X0l, c0 + 1);
+      wload(w1, c1 + 1);
+      compute(w2, X0h, X0l, c0 + 2);
+      wload(w2, c1 + 2);
+      compute(w3, X0h, X0l, c0 + 3);
+      wload(w3, c1 + 3);
+      if (c1 >= n_items) break;
+      c0 = next_chunk(pend);
+      compute(w0, X1h, X1l, c1);
+      wload(w0, c0);
+      rows(X0h, X0l, c0);
+      compute(w1, X1h, X1l, c1 + 1);
+      wload(w1, c0 + 1);
+      compute(w2, X1h, X1l, c1 + 2);
+      wload(w2, c0 + 2);
+      compute(w3, X1h, X1l, c1 + 3);
+      wload(w3, c0 + 3);
     }
   }
   mark(sm, 1);
