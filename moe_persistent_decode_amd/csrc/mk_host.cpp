@@ -272,7 +272,11 @@ int window_of(const mk_config& c, int l) {
 // loses more than the attention gains.)
 int pps_for(const mk_handle* h, int B, int len) {
   const int pages = ceil_div(len, h->cfg.page_size) + 1;
-  const int target = std::max(1, 2 * h->n_workers / (B * h->cfg.n_kv_heads));
+  // (a dense model: at most as many splits as units left free by the QKV
+  // tasks, one per unit, so no attention claimer starts behind a QKV task and
+  // streams its pages late)
+  const int units = h->cfg.dense ? h->n_workers - h->qkv_dim / 32 : 2 * h->n_workers;
+  const int target = std::max(1, units / (B * h->cfg.n_kv_heads));
   // that many splits, each of 16 pages or more, at most 256 (the combine
   // keeps one factor per split in LDS); the pages spread evenly over them
   // (a last split of a page or two would take a unit of its own for nothing)
