@@ -117,14 +117,69 @@ def make_weights(m: ModelConfig, seed: int = 1, device="cpu", std: float = 0.02)
     return {name: weight_tensor(m, name, seed, device, std) for name in weight_shapes(m)}
 
 
+# ---------------------------------------------------------- FP8 weights
+# Feed-forward weights handed over in FP8 (OCP E4M3) with one float32 scale
+# per hidden unit and matrix: this prepares the inputs of a model stored that
+# way (what a checkpoint converter would do); the decode step only ever reads
+# the codes and scales.
+
+E4M3_MAX = 448.0
+FP8_KINDS = ("wg8", "wu8", "wd8", "sg", "su", "sd")
+
+
+def quantize_ffn_fp8(wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor):
+    """FP8 codes and scales of FFN weights wg, wu [..., H, F] and wd [..., F, H]
+    (bf16, on any device). Each hidden unit's gate column, up column and down
+    row gets scale = max|w| / 448 (1 for an all-zero vector) and codes
+    w / scale cast by torch to float8_e4m3fn (nearest, ties to even), clamped
+    to +-448 first. Returns (cg, cu, cd) uint8 in the input layouts and
+    (sg, su, sd) float32 [..., F]."""
+    def q(w: torch.Tensor, axis: int):
+        x = w.float()
+        amax = x.abs().amax(dim=axis)
+        scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        y = (x / scale.unsqueeze(axis)).clamp_(-E4M3_MAX, E4M3_MAX)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+    cg, sg = q(wg, -2)
+    cu, su = q(wu, -2)
+    cd, sd = q(wd, -1)
+    return cg, cu, cd, sg, su, sd
+
+
+def add_fp8_ffn(m: ModelConfig, w: Dict[str, torch.Tensor], drop_bf16: bool = False) -> Dict[str, torch.Tensor]:
+    """Add the FP8 form of every layer's FFN weights to w (names wg8.{l},
+    wu8.{l}, wd8.{l}, sg.{l}, su.{l}, sd.{l}); with drop_bf16 the bf16 FFN
+    tensors are removed. Returns w."""
+    for l in range(m.n_layers):
+        t = quantize_ffn_fp8(w[f"wg.{l}"], w[f"wu.{l}"], w[f"wd.{l}"])
+        for k, v in zip(FP8_KINDS, t):
+            w[f"{k}.{l}"] = v
+        if drop_bf16:
+            for k in ("wg", "wu", "wd"):
+                del w[f"{k}.{l}"]
+    return w
+
+
 class LazyWeights:
     """Host bf16 bits of model weights, each drawn on `device` on first use
     (identical to make_weights on that device) and kept in host memory."""
 
-    def __init__(self, m: ModelConfig, seed: int = 1, device="cuda"):
-        self.m, self.seed, self.device = m, seed, device
+    def __init__(self, m: ModelConfig, seed: int = 1, device="cuda", fp8: bool = False):
+        self.m, self.seed, self.device, self.fp8 = m, seed, device, fp8
+        if fp8:
+            self.fp8_ffn = self._fp8_ffn
         self._c: Dict[tuple, np.ndarray] = {}
         self.overrides: Dict[tuple, np.ndarray] = {}
+
+    def _fp8_ffn(self, layer: int, expert: int):
+        """FP8 codes and scales of one FFN (quantize_ffn_fp8 of the drawn bf16
+        weights, on `device`) as numpy arrays (bound as fp8_ffn when fp8)."""
+        key = ("fp8", layer, expert)
+        if key not in self._c:
+            ws = [weight_tensor(self.m, f"{k}.{layer}", self.seed, self.device, expert=expert)
+                  for k in ("wg", "wu", "wd")]
+            self._c[key] = tuple(t.cpu().numpy() for t in quantize_ffn_fp8(*ws))
+        return self._c[key]
 
     def __call__(self, name: str, layer: Optional[int] = None, expert: Optional[int] = None) -> np.ndarray:
         key = (name, layer, expert)
@@ -214,6 +269,16 @@ class NumpyWeights:
         self.t = tensors
         self.cache = cache
         self._c: Dict[tuple, np.ndarray] = {}
+        if "wg8.0" in tensors:
+            self.fp8_ffn = self._fp8_ffn
+
+    def _fp8_ffn(self, layer: int, expert: int):
+        """One FFN's FP8 codes and scales (add_fp8_ffn's tensors) as numpy
+        arrays: (cg, cu, cd, sg, su, sd); bound as fp8_ffn when present."""
+        key = ("fp8", layer, expert)
+        if key not in self._c:
+            self._c[key] = tuple(self.t[f"{k}.{layer}"][expert].cpu().numpy() for k in FP8_KINDS)
+        return self._c[key]
 
     def __call__(self, name: str, layer: Optional[int] = None, expert: Optional[int] = None) -> np.ndarray:
         key = (name, layer, expert)

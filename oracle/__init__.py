@@ -28,4 +28,7 @@ from .decode import (  # noqa: F401
     decode_step,
     greedy,
     StepTrace,
+    e4m3_to_float,
+    fp8_ffn_weights,
+    ffn_weights,
 )

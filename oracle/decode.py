@@ -57,6 +57,8 @@ Readings where the pages are silent (all fixed here, listed in the design doc):
   R11 Greedy token: argmax of the logits, the lowest index on ties
       (tiny-vllm walkthrough, "The remaining layers and logits": the scan
       replaces the running best only on a strictly greater value).
+  R12, R13 (FP8 feed-forward weights: the format and the scales): in the
+      fp8 section below.
 """
 from __future__ import annotations
 
@@ -84,6 +86,55 @@ def float_to_bf16_rne(x: np.ndarray) -> np.ndarray:
     if nan.any():
         r = np.where(nan, np.uint16(0x7FC0), r)
     return r
+
+
+# ---------------------------------------------------------------- fp8 ------
+# FP8 weights are the post's next step (Chinese version, section "下一步":
+# FP8 and FP4 quantization on the roadmap; section on the other schedulers:
+# narrower types such as FP8). The pages fix neither the format nor the
+# scaling; the readings taken here (listed in the design doc):
+#   R12 The format is the OCP 8-bit floating point E4M3 ("FN": one sign bit,
+#       a 4-bit exponent of bias 7, a 3-bit mantissa; exponent field 0 holds
+#       the subnormals m * 2^-9; S.1111.111 is NaN; no infinities; largest
+#       finite magnitude 448).
+#   R13 Only the feed-forward weights are FP8 (each expert's gate, up and
+#       down matrices, or a dense layer's FFN): they are the bytes a decode
+#       step streams most of. Each hidden unit f of an FFN has three float32
+#       scales: its gate column, its up column and its down row are
+#       code value * scale (Wg[k, f] = e4m3(Cg[k, f]) * sg[f],
+#       Wu[k, f] = e4m3(Cu[k, f]) * su[f], Wd[f, n] = e4m3(Cd[f, n]) * sd[f]).
+#       The rest of the step is as for bf16 weights.
+
+def e4m3_to_float(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64 values (R12), from the fields."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def fp8_ffn_weights(cg, cu, cd, sg, su, sd, dtype=np.float64):
+    """One FFN's weights from FP8 codes and per-hidden-unit scales (R13):
+    cg, cu [H, F] and cd [F, H] uint8 codes; sg, su, sd [F] float32 scales.
+    Returns (Wg, Wu, Wd) with each product formed in float64, then cast."""
+    s = lambda v: np.asarray(v, dtype=np.float32).astype(np.float64)
+    wg = e4m3_to_float(cg) * s(sg)[None, :]
+    wu = e4m3_to_float(cu) * s(su)[None, :]
+    wd = e4m3_to_float(cd) * s(sd)[:, None]
+    return wg.astype(dtype), wu.astype(dtype), wd.astype(dtype)
+
+
+def ffn_weights(W, l: int, e: int, f, dtype):
+    """Expert e's (or a dense layer's, e = 0) gate, up and down matrices of
+    layer l: bf16 weights through W, or FP8 codes and scales when W carries
+    them (W.fp8_ffn(l, e) -> (cg, cu, cd, sg, su, sd))."""
+    q = getattr(W, "fp8_ffn", None)
+    if q is None:
+        return f(W("wg", l, e)), f(W("wu", l, e)), f(W("wd", l, e))
+    return fp8_ffn_weights(*q(l, e), dtype=dtype)
 
 
 # ------------------------------------------------------------ pieces ------
@@ -267,7 +318,7 @@ def _dense_layer(cfg, W: WeightFn, pool, block_tables, seq_lens, l, h, x, f, dty
     a, qr, o = _attention(cfg, W, pool, block_tables, seq_lens, l, x, f, dtype)
     h1 = h + a
     x2 = rmsnorm(h1, f(W("gamma2", l)), cfg.eps)
-    y = expert_ffn(x2, f(W("wg", l, 0)), f(W("wu", l, 0)), f(W("wd", l, 0)))
+    y = expert_ffn(x2, *ffn_weights(W, l, 0, f, dtype))
     h2 = h1 + y
     if record:
         tr.x_norm.append(x)
@@ -286,7 +337,8 @@ def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.nda
     """One decode step for a batch; returns (logits [B, V] in dtype, StepTrace).
 
     cfg: mkinputs.configs.ModelConfig. W(name[, layer[, expert]]) returns a
-    canonical weight's bf16 bits. pool[l] is layer l's KV pool
+    canonical weight's bf16 bits (with FP8 feed-forward weights, W.fp8_ffn
+    gives their codes and scales: see ffn_weights). pool[l] is layer l's KV pool
     [n_pages, 2, KVH, page_size*D] of bf16 bits; this step's K/V are written
     into it (R1). router_hook(layer, x_norm, wr_bits) -> wr_bits, if given,
     may replace a layer's router weight before it is used, and
@@ -320,8 +372,7 @@ def decode_step(cfg, W: WeightFn, pool, block_tables: np.ndarray, tokens: np.nda
         outs = np.zeros((B, cfg.top_k, H), dtype=dtype)
         for e in np.unique(idx):
             rows, ranks = np.nonzero(idx == e)
-            ye = expert_ffn(x[rows], f(W("wg", l, int(e))), f(W("wu", l, int(e))),
-                            f(W("wd", l, int(e))))
+            ye = expert_ffn(x[rows], *ffn_weights(W, l, int(e), f, dtype))
             outs[rows, ranks] = ye
         y = np.zeros((B, H), dtype=dtype)
         for j in range(cfg.top_k):

@@ -473,3 +473,118 @@ def test_run_minimum_gaps():
     assert math.isclose(run.min_router_gap(1), 0.05)
     assert math.isclose(run.min_router_gap(2), 0.1)
     assert math.isclose(run.min_greedy_gap(), 0.1)
+
+
+# ------------------------------------------------------------ FP8 weights ----
+# R12 / R13: OCP E4M3 codes with per-hidden-unit scales (the roadmap's FP8
+# weights, megakernel post, Chinese version, section "下一步").
+
+def test_e4m3_every_code_matches_the_library_decode():
+    """All 256 codes against torch's float8_e4m3fn conversion (a library
+    routine of the same OCP format); NaN codes are NaN on both sides."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = od.e4m3_to_float(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(got).sum() == 2                     # 0x7F and 0xFF only
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_closed_form_values():
+    """Values fixed by the format's definition: bias 7, 3 mantissa bits,
+    subnormals m * 2^-9, largest finite 448, sign in the top bit."""
+    cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+             0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for c, v in cases.items():
+        assert od.e4m3_to_float(np.array([c], dtype=np.uint8))[0] == v, hex(c)
+    assert np.signbit(od.e4m3_to_float(np.array([0x80], dtype=np.uint8))[0])
+
+
+def test_fp8_scales_run_along_the_hidden_unit():
+    """Gate and up scales multiply columns (hidden unit f of [H, F]); down
+    scales multiply rows (hidden unit f of [F, H]): with every code 1.0 each
+    weight equals its unit's scale, and distinct scales expose a transposed
+    or swapped scale vector."""
+    H, F = 3, 4
+    one = np.full((H, F), 0x38, dtype=np.uint8)
+    sg = np.array([1.0, 2.0, 4.0, 8.0], dtype=np.float32)
+    su, sd = sg * 3, sg * 5
+    wg, wu, wd = od.fp8_ffn_weights(one, one, one.T.copy(), sg, su, sd)
+    assert np.array_equal(wg, np.tile(sg.astype(np.float64), (H, 1)))
+    assert np.array_equal(wu, np.tile(su.astype(np.float64), (H, 1)))
+    assert np.array_equal(wd, np.tile(sd.astype(np.float64)[:, None], (1, H)))
+
+
+def test_fp8_dequantization_inverts_the_input_quantizer():
+    """The oracle's decode of codes made by the input generator's quantizer
+    (torch's cast) reproduces each weight within half a step of E4M3 at its
+    magnitude: 2^-4 relative in the normal range, 2^-10 * scale below it."""
+    g = torch.Generator().manual_seed(5)
+    wg = (torch.randn(2, 64, 48, generator=g) * 0.02).to(torch.bfloat16)
+    wu = (torch.randn(2, 64, 48, generator=g) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn(2, 48, 64, generator=g) * 0.02).to(torch.bfloat16)
+    cg, cu, cd, sg, su, sd = (t.numpy() for t in gen.quantize_ffn_fp8(wg, wu, wd))
+    for e in range(2):
+        dq = od.fp8_ffn_weights(cg[e], cu[e], cd[e], sg[e], su[e], sd[e])
+        for w, d, s in zip((wg[e], wu[e], wd[e]), dq, (sg[e][None, :], su[e][None, :], sd[e][:, None])):
+            w = w.double().numpy()
+            s = s.astype(np.float64)
+            normal = np.abs(w) / s >= 2.0 ** -6
+            err = np.abs(d - w)
+            assert np.all(err[normal] <= 2.0 ** -4 * np.abs(w[normal]) * (1 + 1e-6))
+            assert np.all(err[~normal] <= (2.0 ** -10 * np.broadcast_to(s, w.shape))[~normal] * (1 + 1e-6))
+            # the largest magnitude of each vector is exactly code 448
+            assert np.allclose(np.abs(d).max(axis=0 if s.shape[0] == 1 else 1), 448.0 * s.ravel(), rtol=1e-12)
+
+
+class _Fp8View:
+    """bf16 weights W with FP8 codes and scales for the FFNs (test input)."""
+
+    def __init__(self, W, q):
+        self.W, self.q = W, q
+
+    def __call__(self, *a):
+        return self.W(*a)
+
+    def fp8_ffn(self, l, e):
+        return self.q[(l, e)]
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_decode_step_with_fp8_weights_equals_the_same_values_in_bf16(dense):
+    """FP8 codes times power-of-two scales are exact bf16 values: a step with
+    those FFN weights given as codes and scales equals, bit for bit, the step
+    with the same values given as bf16 weights (the FP8 path feeds the gate,
+    up and down matrices to the same places)."""
+    cfg = configs.small_variant(configs.TINY_DENSE if dense else configs.TINY, n_layers=2)
+    w = gen.make_weights(cfg, seed=3, device="cpu")
+    rng = np.random.default_rng(4)
+    E = 1 if dense else cfg.n_experts
+    H, F = cfg.hidden, cfg.expert_ffn
+    q = {}
+    for l in range(cfg.n_layers):
+        bf = {}
+        for k, shape in (("wg", (E, H, F)), ("wu", (E, H, F)), ("wd", (E, F, H))):
+            # codes of magnitude 2^-6 .. 448 with random signs, scales 2^-12 .. 2^-9
+            codes = rng.integers(0x08, 0x7F, size=shape).astype(np.uint8) | (rng.integers(0, 2, shape) << 7).astype(np.uint8)
+            scales = np.exp2(rng.integers(-12, -8, size=(E, F))).astype(np.float32)
+            bf[k] = (codes, scales)
+            vals = od.e4m3_to_float(codes) * (scales[:, None, :] if k != "wd" else scales[:, :, None])
+            w[f"{k}.{l}"] = torch.from_numpy(vals).to(torch.bfloat16)
+            assert np.array_equal(w[f"{k}.{l}"].double().numpy(), vals)
+        for e in range(E):
+            q[(l, e)] = (bf["wg"][0][e], bf["wu"][0][e], bf["wd"][0][e], bf["wg"][1][e], bf["wu"][1][e], bf["wd"][1][e])
+    W = gen.NumpyWeights(w)
+    V = _Fp8View(W, q)
+    toks = np.array([5, 77]) if not dense else np.array([9, 31])
+    bt = np.array([[0], [1]])
+    lens = np.array([1, 1])
+    a, _ = od.decode_step(cfg, W, _empty_pool(cfg, 2), bt, toks, lens, dtype=np.float64)
+    b, _ = od.decode_step(cfg, V, _empty_pool(cfg, 2), bt, toks, lens, dtype=np.float64)
+    assert np.array_equal(a, b)
+    # and a swapped gate/up pair would not be equal
+    q2 = {k: (v[1], v[0]) + v[2:] for k, v in q.items()}
+    c, _ = od.decode_step(cfg, _Fp8View(W, q2), _empty_pool(cfg, 2), bt, toks, lens, dtype=np.float64)
+    assert not np.array_equal(a, c)
