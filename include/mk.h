@@ -83,6 +83,13 @@ typedef struct {
                             * walkthrough, section "The remaining layers and
                             * logits"; the post's FFN_UPGATE_ACT and FFN_DOWN,
                             * section "Tasks") */
+  int32_t ffn_fp8;         /* 0: bf16 feed-forward weights. 1: FP8 (OCP E4M3)
+                            * feed-forward weights, one float32 scale per hidden
+                            * unit for each of its gate column, up column and
+                            * down row, loaded with mk_load_ffn_fp8; the other
+                            * weights stay bf16. max_batch <= 4. (The post's
+                            * roadmap: FP8 weights, Chinese version, section
+                            * "下一步".) */
 } mk_config;
 
 typedef struct mk_handle mk_handle;
@@ -139,6 +146,23 @@ mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* 
 mk_status mk_load_layer_dense(mk_handle* h, int layer, const void* gamma, const void* wqkv,
                               const void* wo, const void* gamma2, const void* wg, const void* wu,
                               const void* wd, void* stream);
+
+/* One layer's FP8 feed-forward weights (cfg.ffn_fp8 = 1; the post's roadmap
+ * of narrower weight types, Chinese version, section "下一步"): caller-owned
+ * device tensors, repacked into the library's copy (free them once `stream`
+ * has passed this call):
+ *   wg8, wu8 [E][H][F] and wd8 [E][F][H]: OCP FP8 E4M3 codes (uint8), the
+ *   canonical row-major layouts of mk_load_layer (a dense model: E = 1);
+ *   sg, su, sd [E][F] float32: hidden unit f's gate column is
+ *   e4m3(wg8[e][:, f]) * sg[e][f], its up column likewise with su, its down
+ *   row e4m3(wd8[e][f][:]) * sd[e][f].
+ * Codes 0x7F and 0xFF (NaN) are not valid weights. An FP8 model's
+ * mk_load_layer / mk_load_layer_dense / mk_load_weights calls pass NULL for
+ * wg, wu and wd; a step needs both calls made for every layer.
+ * Errors: MK_ERR_INVALID_ARG (not an FP8 model, layer, null or misaligned
+ * pointer), MK_ERR_STATE (host-only handle), MK_ERR_HIP. */
+mk_status mk_load_ffn_fp8(mk_handle* h, int layer, const void* wg8, const void* wu8, const void* wd8,
+                          const float* sg, const float* su, const float* sd, void* stream);
 
 /* Load the embedding [V][H], final norm gain [H] and LM head [H][V] (bf16),
  * caller-owned device tensors, copied or repacked like mk_load_layer's

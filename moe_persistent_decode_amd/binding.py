@@ -24,7 +24,7 @@ PLACE_TUNED, PLACE_ROUND_ROBIN, PLACE_AFFINITY, PLACE_COST_MODEL, PLACE_RANDOM =
 STEP_ADVANCE = 1
 
 # every function include/mk.h declares
-EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_dense", "mk_load_globals",
+EXPORTS = ("mk_create", "mk_create_host_only", "mk_load_layer", "mk_load_layer_dense", "mk_load_ffn_fp8", "mk_load_globals",
            "mk_load_weights",
            "mk_decode_step", "mk_set_mode", "mk_set_task_trace", "mk_set_routing_trace", "mk_set_wait_limit",
            "mk_set_debug_poison",
@@ -49,7 +49,7 @@ class MkConfig(ctypes.Structure):
                                               "top_k", "expert_ffn", "vocab", "n_layers")] + [
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("page_size", "window", "full_every", "max_batch", "max_seq_len",
-                                      "max_pages_per_seq", "n_pages", "mode", "dense")]
+                                      "max_pages_per_seq", "n_pages", "mode", "dense", "ffn_fp8")]
 
 
 TOKEN_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32)
@@ -82,6 +82,7 @@ def _load():
     lib.mk_load_layer.argtypes = [H, I, P, P, P, P, P, P, P, P]
     lib.mk_load_layer_dense.argtypes = [H, I, P, P, P, P, P, P, P, P]
     lib.mk_load_globals.argtypes = [H, P, P, P, P]
+    lib.mk_load_ffn_fp8.argtypes = [H, I, P, P, P, P, P, P, P]
     lib.mk_load_weights.argtypes = [H, P, P]
     lib.mk_decode_step.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
     lib.mk_decode_step_noalloc.argtypes = [H, I, P, P, P, I, P, P, ctypes.c_uint32, P]
@@ -166,7 +167,7 @@ def litmus_message_passing(pairs: int, rounds: int, coherent=True, device: int =
 
 
 def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages_per_seq: int,
-                mode: int = MODE_MEGAKERNEL) -> MkConfig:
+                mode: int = MODE_MEGAKERNEL, ffn_fp8: bool = False) -> MkConfig:
     """MkConfig from a model-shape object (fields as in mkinputs.configs.ModelConfig)."""
     return MkConfig(hidden=model.hidden, n_q_heads=model.n_q_heads, n_kv_heads=model.n_kv_heads,
                     head_dim=model.head_dim, n_experts=model.n_experts, top_k=model.top_k,
@@ -174,7 +175,7 @@ def make_config(model, max_batch: int, max_seq_len: int, n_pages: int, max_pages
                     rope_theta=model.rope_theta, rms_eps=model.eps, page_size=model.page_size,
                     window=model.window, full_every=model.full_every, max_batch=max_batch,
                     max_seq_len=max_seq_len, max_pages_per_seq=max_pages_per_seq, n_pages=n_pages,
-                    mode=mode, dense=1 if getattr(model, "dense", False) else 0)
+                    mode=mode, dense=1 if getattr(model, "dense", False) else 0, ffn_fp8=1 if ffn_fp8 else 0)
 
 
 class Decoder:
@@ -217,16 +218,25 @@ class Decoder:
         self._check(fn(self._h, layer, _ptr(gamma), _ptr(wqkv), _ptr(wo), _ptr(wr), _ptr(wg), _ptr(wu), _ptr(wd),
                        _stream_ptr(stream)))
 
+    def load_ffn_fp8(self, layer: int, wg8, wu8, wd8, sg, su, sd, stream=None):
+        """A layer's FP8 feed-forward codes (uint8) and scales (float32), in the
+        order of mk_load_ffn_fp8."""
+        self._check(lib.mk_load_ffn_fp8(self._h, layer, _ptr(wg8), _ptr(wu8), _ptr(wd8), _ptr(sg), _ptr(su),
+                                        _ptr(sd), _stream_ptr(stream)))
+
     def load_globals(self, emb, gamma_f, wlm, stream=None):
         self._check(lib.mk_load_globals(self._h, _ptr(emb), _ptr(gamma_f), _ptr(wlm), _stream_ptr(stream)))
 
     def load_weights(self, w: Dict[str, "object"], stream=None):
         """Load canonical tensors named emb, gamma_f, wlm, gamma.{l}, wqkv.{l}, ..."""
         self.load_globals(w["emb"], w["gamma_f"], w["wlm"], stream)
+        fp8 = bool(self.cfg.ffn_fp8)
         for l in range(self.cfg.n_layers):
             fourth = w[f"gamma2.{l}"] if self.cfg.dense else w[f"wr.{l}"]
-            self.load_layer(l, w[f"gamma.{l}"], w[f"wqkv.{l}"], w[f"wo.{l}"], fourth, w[f"wg.{l}"],
-                            w[f"wu.{l}"], w[f"wd.{l}"], stream)
+            ffn = (None, None, None) if fp8 else (w[f"wg.{l}"], w[f"wu.{l}"], w[f"wd.{l}"])
+            self.load_layer(l, w[f"gamma.{l}"], w[f"wqkv.{l}"], w[f"wo.{l}"], fourth, *ffn, stream)
+            if fp8:
+                self.load_ffn_fp8(l, *(w[f"{k}.{l}"] for k in ("wg8", "wu8", "wd8", "sg", "su", "sd")), stream)
 
     # ---- decode
     def step(self, tokens, block_tables, seq_lens, max_seq_len_hint: int, logits, next_tokens=None,

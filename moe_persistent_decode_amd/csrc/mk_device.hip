@@ -52,6 +52,8 @@
 // normalised vector itself.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "mk_internal.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -2339,7 +2341,119 @@ __device__ __forceinline__ void atile_lds(ATile<1, NCH>& A, const uint16_t* xs, 
   }
 }
 
-template <int NJ, int NCH, bool DENSE>
+// ------------------------------------------------ FP8 feed-forward weights
+// The post's roadmap names FP8 as the next, narrower weight type (Chinese
+// version, section "下一步"). Codes are OCP E4M3 with one float32 scale per
+// hidden unit for each of its gate column, up column and down row (code value
+// times scale). Every E4M3 value is exactly a bf16 value, so the gate/up codes
+// become the matrix cores' bf16 B operand in registers and the products run
+// as for bf16 weights; the scales apply to the hidden unit's gate and up sums
+// and, for the down row, to the unit's SiLU-and-multiply output.
+//
+// Gate/up panels: each 16-column panel is a run of K / 64 chunk pairs of
+// 1 KB; in pair p, lane l holds 16 bytes: the codes of rows 64p + 8(l/16) + i
+// (i = 0..7) of column l%16, then those of rows 64p + 32 + 8(l/16) + i. Pair
+// p goes to wave p % 8: each load is one contiguous 1 KB line per wave.
+template <int NP, int NPR>
+struct WTile8 {
+  u32x4_t v[NP][NPR];
+};
+
+// Pairs outside [p0, p1) and panels at or beyond np are zero (one buffer
+// resource, out-of-range reads return zeros).
+template <int NP, int NPR>
+__device__ __forceinline__ void wtile8_load(WTile8<NP, NPR>& w, const uint8_t* base, int pstride, int np, int p0,
+                                            int p1) {
+  const int wv = wave_id(), ln = lane_id();
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, np * pstride, 0x00020000);
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) {
+      const int p = p0 + wv + MK_WAVES * i;
+      const int off = (pp < np && p < p1) ? pp * pstride + p * 1024 + ln * 16 : 0x7ffffff0;
+      w.v[pp][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
+    }
+}
+
+// Four E4M3 codes -> their values as two words of bf16 pairs (codes 0, 1 in
+// lo; 2, 3 in hi). The hardware conversion gives float32 values of at most
+// four significant bits, so keeping their upper halves is exact.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t c, uint32_t& lo, uint32_t& hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+  lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+}
+
+// One lane's 16 codes of a chunk pair -> the bf16 B operands of its two chunks.
+__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4_t& c, u32x4_t& c0, u32x4_t& c1) {
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) e4m3x4_to_bf16(c[k], w[2 * k], w[2 * k + 1]);
+  c0 = u32x4_t{w[0], w[1], w[2], w[3]};
+  c1 = u32x4_t{w[4], w[5], w[6], w[7]};
+}
+
+// The activation operand matching a WTile8: slot 2i + h holds chunk
+// 2 (p0 + wave + 8 i) + h of the layer input staged in LDS (zero past p1).
+template <int NCH>
+__device__ __forceinline__ void atile_lds_pairs(ATile<1, NCH>& A, const uint16_t* xs, int H, int B, int p0, int p1) {
+  const int wv = wave_id(), ln = lane_id(), row = ln & 15;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int p = p0 + wv + MK_WAVES * (i / 2), c = 2 * p + (i % 2);
+    A.a[0][i] = (p < p1 && row < B) ? *(const u32x4_t*)(xs + row * H + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// acc (+)= (A hi + A lo) W over this wave's chunk pairs, W in E4M3 codes.
+template <int NP, int NPR>
+__device__ __forceinline__ void mfma_tiles8(Acc<NP, 1>& acc, const WTile8<NP, NPR>& w, const ATile<1, 2 * NPR>& Ah,
+                                            const ATile<1, 2 * NPR>& Al, bool add) {
+  if (!add) {
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) acc.c[pp][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < NPR; ++i)
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      u32x4_t b[2];
+      e4m3x16_to_bf16(w.v[pp][i], b[0], b[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Al.a[0][2 * i + h]),
+                                                               __builtin_bit_cast(bf16x8_t, b[h]), acc.c[pp][0], 0, 0, 0);
+        acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Ah.a[0][2 * i + h]),
+                                                               __builtin_bit_cast(bf16x8_t, b[h]), acc.c[pp][0], 0, 0, 0);
+      }
+    }
+}
+
+// Down rows in E4M3: slice s (rows 16 s .. 16 s + 15) of an FFN's [F x H]
+// down matrix is H runs of 16 bytes, run h holding the codes of rows
+// 16 s .. 16 s + 15 of column h (one contiguous 16 H bytes per slice).
+// Thread t takes columns t + 512 j. An invalid slice reads nothing (zeros).
+template <int NJ8>
+struct DTile8 {
+  u32x4_t v[NJ8];
+};
+
+template <int NJ8>
+__device__ __forceinline__ void dtile8_load(DTile8<NJ8>& d, const uint8_t* slice, int H, bool valid) {
+  const int t = tid();
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(slice), (short)0, valid ? H * 16 : 0, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NJ8; ++j) {
+    const int h = t + MK_WG_THREADS * j;
+    d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, h < H ? h * 16 : 0x7ffffff0, 0, kNT);
+  }
+}
+
+template <int NJ, int NCH, bool DENSE, bool FP8>
 __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& t, Smem& sm) {
   const int sk = t.b[0], nf = t.b[1], nt = t.b[2], wa = P.waits_enabled ? t.b[3] : 256;
   const int l = t.layer;
@@ -2355,21 +2469,41 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   // layer's one FFN is expert 0
   int lo = 0, hi = 0;
   auto expert_of = [&](int a) { return DENSE ? 0 : __builtin_amdgcn_readfirstlane(sm.rt_e[a]); };
-  auto up_load = [&](WTile<2, NCH>& w, int id, int kh) {
+  // (FP8: gate/up codes in chunk pairs, kh_pairs per K half; the down
+  // slice's codes and the item's scales, a float4 (gate, up, down, 0) per
+  // hidden unit, loaded by the threads that apply them)
+  constexpr int NJ8 = MK_MAX_H / MK_WG_THREADS;
+  const int kh_pairs = H / 128, pstride8 = (H / 64) * 1024;
+  using WU = std::conditional_t<FP8, WTile8<2, NCH / 2>, WTile<2, NCH>>;
+  using WD = std::conditional_t<FP8, DTile8<NJ8>, DTile<NJ>>;
+  // (the scales of the item whose down tile was loaded last)
+  float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto up_load = [&](WU& w, int id, int kh) {
     const bool valid = id < hi;
     const int a = valid ? id / S : 0, s = id % S;
     const int e = expert_of(a);
-    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * s) * pstride, pstride, valid ? 2 : 0,
-               kh * kh_chunks, (kh + 1) * kh_chunks);
+    if constexpr (FP8)
+      wtile8_load(w, P.wgu8 + l * P.s_gu8_l + (size_t)e * P.s_gu8_e + (size_t)(2 * s) * pstride8, pstride8,
+                  valid ? 2 : 0, kh * kh_pairs, (kh + 1) * kh_pairs);
+    else
+      wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * s) * pstride, pstride,
+                 valid ? 2 : 0, kh * kh_chunks, (kh + 1) * kh_chunks);
   };
-  auto down_load = [&](DTile<NJ>& d, int id) {
+  auto down_load = [&](WD& d, int id) {
     const bool valid = id < hi;
     const int a = valid ? id / S : 0, s = id % S;
     const int e = expert_of(a);
-    dtile_load(d, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e, pstride_d, H / 16, s, valid);
+    if constexpr (FP8) {
+      dtile8_load(d, P.wd8 + l * P.s_d8_l + (size_t)e * P.s_d8_e + (size_t)s * H * 16, H, valid);
+      sc = valid && tid() < 16 * MK_FUSED_B
+                    ? *(const float4*)(P.fsc + l * P.s_fsc_l + (size_t)e * P.s_fsc_e + 4 * (16 * s + (tid() & 15)))
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      dtile_load(d, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e, pstride_d, H / 16, s, valid);
+    }
   };
-  WTile<2, NCH> wu0, wu1;
-  DTile<NJ> wdn;
+  WU wu0, wu1;
+  WD wdn;
   // A dense layer's FFN and this claimer's share of its slices are known
   // before the input is: the first slice's three weight units stream before
   // the wait (weight prefetch, megakernel post section "Where the speedup
@@ -2427,9 +2561,10 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   const uint16_t* xh = xs;
   const uint16_t* xl = xs + MK_FUSED_B * MK_MAX_H;
   mark(sm, 1);
-  float acc[NJ][MK_FUSED_B];
+  constexpr int NA = FP8 ? NJ8 : NJ;
+  float acc[NA][MK_FUSED_B];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+  for (int j = 0; j < NA; ++j)
 #pragma unroll
     for (int b = 0; b < MK_FUSED_B; ++b) acc[j][b] = 0.f;
   {
@@ -2439,20 +2574,37 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
     for (int id = lo; id < hi; ++id) {
       const int a = id / S;
       Acc<2, 1> ac;
-      {
-        ATile<1, NCH> Ah, Al;
-        atile_lds(Ah, xh, H, B, 0, kh_chunks);
-        atile_lds(Al, xl, H, B, 0, kh_chunks);
-        mfma_tiles(ac, wu0, Ah, Al);
+      if constexpr (FP8) {
+        {
+          ATile<1, NCH> Ah, Al;
+          atile_lds_pairs(Ah, xh, H, B, 0, kh_pairs);
+          atile_lds_pairs(Al, xl, H, B, 0, kh_pairs);
+          mfma_tiles8(ac, wu0, Ah, Al, false);
+        }
+        up_load(wu0, id + 1, 0);
+        {
+          ATile<1, NCH> Ah, Al;
+          atile_lds_pairs(Ah, xh, H, B, kh_pairs, 2 * kh_pairs);
+          atile_lds_pairs(Al, xl, H, B, kh_pairs, 2 * kh_pairs);
+          mfma_tiles8(ac, wu1, Ah, Al, true);
+        }
+        up_load(wu1, id + 1, 1);
+      } else {
+        {
+          ATile<1, NCH> Ah, Al;
+          atile_lds(Ah, xh, H, B, 0, kh_chunks);
+          atile_lds(Al, xl, H, B, 0, kh_chunks);
+          mfma_tiles(ac, wu0, Ah, Al);
+        }
+        up_load(wu0, id + 1, 0);
+        {
+          ATile<1, NCH> Ah, Al;
+          atile_lds(Ah, xh, H, B, kh_chunks, kc);
+          atile_lds(Al, xl, H, B, kh_chunks, kc);
+          mfma_tiles_add(ac, wu1, Ah, Al);
+        }
+        up_load(wu1, id + 1, 1);
       }
-      up_load(wu0, id + 1, 0);
-      {
-        ATile<1, NCH> Ah, Al;
-        atile_lds(Ah, xh, H, B, kh_chunks, kc);
-        atile_lds(Al, xl, H, B, kh_chunks, kc);
-        mfma_tiles_add(ac, wu1, Ah, Al);
-      }
-      up_load(wu1, id + 1, 1);
       reduce_tiles(ac, sm);
       // weighted SiLU(gate) * up of the slice for every token routed to the expert
       {
@@ -2471,14 +2623,51 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
             }
             if (slot >= 0) {
               const float inv = sm.inv_rms[b];
-              const float g = sm.out[b * 16 + r] * inv, u = sm.out[256 + b * 16 + r] * inv;
+              float g = sm.out[b * 16 + r] * inv, u = sm.out[256 + b * 16 + r] * inv;
+              if constexpr (FP8) {
+                g *= sc.x;
+                u *= sc.y;
+              }
               v = sm.tkw[slot] * (g / (1.0f + __expf(-g)) * u);
+              if constexpr (FP8) v *= sc.z;
             }
           }
           actf[o] = v;
         }
       }
       __syncthreads();
+      if constexpr (FP8) {
+        // the slice's 16 down rows of columns t + 512 j, converted once and
+        // applied to every token
+#pragma unroll
+        for (int j = 0; j < NJ8; ++j) {
+          float wv[16];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(wdn.v[j][k], false);
+            const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(wdn.v[j][k], true);
+            wv[4 * k] = p0[0];
+            wv[4 * k + 1] = p0[1];
+            wv[4 * k + 2] = p1[0];
+            wv[4 * k + 3] = p1[1];
+          }
+#pragma unroll
+          for (int b = 0; b < MK_FUSED_B; ++b) {
+            if (b < B) {
+              float x = acc[j][b];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float4 av = *(const float4*)(actf + b * 16 + 4 * q);
+                x = fmaf(av.x, wv[4 * q], x);
+                x = fmaf(av.y, wv[4 * q + 1], x);
+                x = fmaf(av.z, wv[4 * q + 2], x);
+                x = fmaf(av.w, wv[4 * q + 3], x);
+              }
+              acc[j][b] = x;
+            }
+          }
+        }
+      } else {
       // the slice's down rows: 8 of them per thread, one token at a time
 #pragma unroll
       for (int b = 0; b < MK_FUSED_B; ++b) {
@@ -2496,6 +2685,7 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
             }
         }
       }
+      }
       down_load(wdn, id + 1);
     }
   }
@@ -2505,6 +2695,15 @@ __device__ __forceinline__ void op_moe_fused(const mk_params& P, const mk_task& 
   const Pub MP(P.mp);
   const int t0 = tid(), col = t0 & 15;
   const bool wr = ((t0 >> 4) & 1) == 0;
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < NJ8; ++j) {
+      const int hh = t0 + MK_WG_THREADS * j;
+#pragma unroll
+      for (int b = 0; b < MK_FUSED_B; ++b)
+        if (hh < H && b < B && ((seen >> b) & 1u)) MP.stf((sk * MK_FUSED_B + b) * H + hh, acc[j][b]);
+    }
+  } else
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int p = (t0 >> 5) + 16 * j;
@@ -2833,7 +3032,7 @@ __device__ __forceinline__ void final_argmax(const mk_params& P, Smem& sm) {
 
 // --------------------------------------------------------------- dispatch
 
-template <int D, int MT>
+template <int D, int MT, bool FP8>
 __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t, Smem& sm) {
   switch (t.op) {
     // chunks per wave: K / 32 / MK_WAVES for the largest K of each op
@@ -2861,9 +3060,9 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
       // the wait keeps tiles live there, which the experts' instance does not)
       if (MT == 1) {
         if (P.dense)
-          op_moe_fused<2048 / 256, 32 / MK_WAVES, true>(P, t, sm);
+          op_moe_fused<2048 / 256, 32 / MK_WAVES, true, FP8>(P, t, sm);
         else
-          op_moe_fused<2048 / 256, 32 / MK_WAVES, false>(P, t, sm);
+          op_moe_fused<2048 / 256, 32 / MK_WAVES, false, FP8>(P, t, sm);
       }
       break;
     case MK_OP_RESIDUAL:
@@ -2878,7 +3077,7 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
 
 // The interpreter: workgroup i runs tasks [task_off[i], task_off[i+1]).
 // MT: row tiles of 16 tokens (1 for batch <= 16, 2 for batch <= 32).
-template <int D, int MT>
+template <int D, int MT, bool FP8>
 __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_params Pk) {
   __shared__ Smem sm;
   const mk_params& P = Pk;
@@ -2912,9 +3111,9 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
     typedef const __attribute__((address_space(4))) mk_params* kparams_ptr;
     kparams_ptr Pt = (kparams_ptr)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(Pt));
-    run_task_mt<D, MT>(*(const mk_params*)Pt, t, sm);
+    run_task_mt<D, MT, FP8>(*(const mk_params*)Pt, t, sm);
 #else
-    run_task_mt<D, MT>(P, t, sm);
+    run_task_mt<D, MT, FP8>(P, t, sm);
 #endif
     // (LDS only: a task's stores need no draining here; every hand-off
     // through a counter drains before its arrival, and tagged words carry
@@ -2936,10 +3135,13 @@ __global__ __launch_bounds__(MK_WG_THREADS, MK_WGS_PER_CU) void mk_interp(mk_par
   }
 }
 
-template __global__ void mk_interp<64, 1>(mk_params);
-template __global__ void mk_interp<64, 2>(mk_params);
-template __global__ void mk_interp<128, 1>(mk_params);
-template __global__ void mk_interp<128, 2>(mk_params);
+template __global__ void mk_interp<64, 1, false>(mk_params);
+template __global__ void mk_interp<64, 2, false>(mk_params);
+template __global__ void mk_interp<128, 1, false>(mk_params);
+template __global__ void mk_interp<128, 2, false>(mk_params);
+// FP8 feed-forward weights: batches of at most MK_FUSED_B (one row tile)
+template __global__ void mk_interp<64, 1, true>(mk_params);
+template __global__ void mk_interp<128, 1, true>(mk_params);
 
 // ------------------------------------------------------------- repacking
 // Canonical row-major [K x N] (leading dimension ld) -> panel-tiled layout,
@@ -2971,6 +3173,55 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_panels(const uint16_
     const int pj = dst0 + (n0 / 16 + j) * dstep;
     *(uint4*)(d + ((size_t)pj * kc + c) * 512 + l * 8) = *(uint4*)tmp;
   }
+}
+
+// FP8 gate/up codes: canonical wg, wu [E][H][F] (bytes) -> per expert 2 F / 16
+// panels (gate panel j at 2j, up panel j at 2j + 1) of H / 64 chunk pairs of
+// 1 KB, lane l of pair p holding rows 64p + 8(l/16) + i, then rows
+// 64p + 32 + 8(l/16) + i (i = 0..7), of column 16j + l%16. One thread per
+// 16-byte lane unit.
+extern "C" __global__ __launch_bounds__(256) void mk_repack_fp8_gu(const uint8_t* wg, const uint8_t* wu,
+                                                                   uint8_t* dst, int H, int F, int E) {
+  const int npair = H / 64, npan = 2 * (F / 16);
+  const size_t n = (size_t)E * npan * npair * 64;
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (size_t)gridDim.x * 256) {
+    const int l = (int)(u % 64), p = (int)((u / 64) % npair);
+    const int pj = (int)((u / ((size_t)64 * npair)) % npan);
+    const int e = (int)(u / ((size_t)64 * npair * npan));
+    const uint8_t* src = (pj & 1 ? wu : wg) + (size_t)e * H * F;
+    const int col = 16 * (pj >> 1) + (l & 15);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int row = 64 * p + (b >= 8 ? 32 : 0) + 8 * (l >> 4) + (b & 7);
+      w[b >> 2] |= (uint32_t)src[(size_t)row * F + col] << (8 * (b & 3));
+    }
+    *(u32x4_t*)(dst + (size_t)e * 2 * H * F + ((size_t)pj * npair + p) * 1024 + l * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// FP8 down codes: canonical wd [E][F][H] -> per expert [F / 16][H][16]: the
+// 16 codes of rows 16 s .. 16 s + 15 of column h contiguous. One thread per
+// (expert, slice, column).
+extern "C" __global__ __launch_bounds__(256) void mk_repack_fp8_d(const uint8_t* wd, uint8_t* dst, int F, int H,
+                                                                  int E) {
+  const int S = F / 16;
+  const size_t n = (size_t)E * S * H;
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (size_t)gridDim.x * 256) {
+    const int h = (int)(u % H), sl = (int)((u / H) % S), e = (int)(u / ((size_t)H * S));
+    const uint8_t* src = wd + (size_t)e * F * H + (size_t)(16 * sl) * H + h;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i >> 2] |= (uint32_t)src[(size_t)i * H] << (8 * (i & 3));
+    *(u32x4_t*)(dst + u * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// The three per-hidden-unit scale vectors as one float4 per unit (gate, up, down, 0).
+extern "C" __global__ __launch_bounds__(256) void mk_pack_scales(const float* sg, const float* su, const float* sd,
+                                                                 float* dst, int n) {
+  for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < n; i += gridDim.x * 256)
+    *(float4*)(dst + 4 * (size_t)i) = make_float4(sg[i], su[i], sd[i], 0.f);
 }
 
 // ----------------------------------------------- static scratch (no allocation)
@@ -3194,17 +3445,36 @@ hipError_t mk_launch_zero(uint32_t* p, int n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-static const void* interp_fn(int head_dim, int mt) {
-  if (head_dim == 64) return mt == 1 ? (const void*)mk_interp<64, 1> : (const void*)mk_interp<64, 2>;
-  return mt == 1 ? (const void*)mk_interp<128, 1> : (const void*)mk_interp<128, 2>;
+static const void* interp_fn(int head_dim, int mt, bool fp8 = false) {
+  if (fp8) return head_dim == 64 ? (const void*)mk_interp<64, 1, true> : (const void*)mk_interp<128, 1, true>;
+  if (head_dim == 64) return mt == 1 ? (const void*)mk_interp<64, 1, false> : (const void*)mk_interp<64, 2, false>;
+  return mt == 1 ? (const void*)mk_interp<128, 1, false> : (const void*)mk_interp<128, 2, false>;
 }
 
 hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool cooperative, hipStream_t stream) {
-  const void* fn = interp_fn(head_dim, P.B > 16 ? 2 : 1);
+  // (FP8 feed-forward weights run at most MK_FUSED_B sequences: the host rejects more)
+  const void* fn = interp_fn(head_dim, P.B > 16 ? 2 : 1, P.ffn_fp8 != 0);
   void* args[] = {(void*)&P};
   if (cooperative)
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(MK_WG_THREADS), args, 0, stream);
   return hipLaunchKernel(fn, dim3(grid), dim3(MK_WG_THREADS), args, 0, stream);
+}
+
+hipError_t mk_launch_repack_fp8_gu(const uint8_t* wg, const uint8_t* wu, uint8_t* dst, int H, int F, int E,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(mk_repack_fp8_gu, dim3(4096), dim3(256), 0, stream, wg, wu, dst, H, F, E);
+  return hipGetLastError();
+}
+
+hipError_t mk_launch_repack_fp8_d(const uint8_t* wd, uint8_t* dst, int F, int H, int E, hipStream_t stream) {
+  hipLaunchKernelGGL(mk_repack_fp8_d, dim3(4096), dim3(256), 0, stream, wd, dst, F, H, E);
+  return hipGetLastError();
+}
+
+hipError_t mk_launch_pack_scales(const float* sg, const float* su, const float* sd, float* dst, int n,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(mk_pack_scales, dim3(256), dim3(256), 0, stream, sg, su, sd, dst, n);
+  return hipGetLastError();
 }
 
 hipError_t mk_launch_repack(const uint16_t* src, uint16_t* dst, int K, int N, int ld, int dst0, int dstep,
@@ -3222,6 +3492,9 @@ hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu) {
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, interp_fn(head_dim, 1), MK_WG_THREADS, 0);
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, interp_fn(head_dim, 2), MK_WG_THREADS, 0);
-  *blocks_per_cu = a < b ? a : b;
+  if (e != hipSuccess) return e;
+  int c = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, interp_fn(head_dim, 1, true), MK_WG_THREADS, 0);
+  *blocks_per_cu = a < b ? (a < c ? a : c) : (b < c ? b : c);
   return e;
 }

@@ -129,6 +129,10 @@ struct mk_handle {
   size_t s_wqkv = 0, s_wo = 0, s_wr = 0, s_wgu_l = 0, s_wgu_e = 0, s_wd_l = 0, s_wd_e = 0;
   uint16_t *emb = nullptr, *gamma = nullptr, *gamma2 = nullptr, *wqkv = nullptr, *wo = nullptr, *wr = nullptr,
            *wgu = nullptr, *wd = nullptr, *wlm = nullptr;
+  // FP8 feed-forward weights (cfg.ffn_fp8): codes in bytes, scales in floats
+  uint8_t *wgu8 = nullptr, *wd8 = nullptr;
+  float* fsc = nullptr;
+  size_t s_gu8_l = 0, s_gu8_e = 0, s_d8_l = 0, s_d8_e = 0, s_fsc_l = 0, s_fsc_e = 0;
   float* rope = nullptr;
   uint16_t* kv = nullptr;
   bool kv_owned = false;  // the pool was allocated by mk_create (kv_pool NULL)
@@ -146,6 +150,7 @@ struct mk_handle {
   int32_t* wg_off_identity = nullptr;  // 0..max_tasks for kernel-per-op launches
   int identity_len = 0;
   std::vector<bool> layer_loaded;
+  std::vector<bool> ffn_loaded;  // FP8 feed-forward weights of each layer (cfg.ffn_fp8)
   bool globals_loaded = false;
   uint64_t steps = 0;
   uint32_t epoch = 0;  // the last step's epoch in the handle's scratch (tags of tagged hand-offs)
@@ -199,6 +204,10 @@ mk_status validate_config(const mk_config* c) {
   if (G > 16 || G * c->head_dim > 1024)
     return fail(nullptr, MK_ERR_UNSUPPORTED, "group size must be <= 16 and group width <= 1024");
   if (c->dense != 0 && c->dense != 1) return fail(nullptr, MK_ERR_INVALID_ARG, "dense must be 0 or 1");
+  if (c->ffn_fp8 != 0 && c->ffn_fp8 != 1) return fail(nullptr, MK_ERR_INVALID_ARG, "ffn_fp8 must be 0 or 1");
+  if (c->ffn_fp8 && c->max_batch > MK_FUSED_B)
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "FP8 feed-forward weights decode at most %d sequences per step",
+                MK_FUSED_B);
   if (c->dense) {
     if (c->n_experts != 1 || c->top_k != 1)
       return fail(nullptr, MK_ERR_INVALID_ARG, "a dense model has n_experts = top_k = 1");
@@ -1512,8 +1521,18 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   };
   const size_t o_emb = take((size_t)V * H), o_gamma = take((size_t)(L + 1) * H), o_wlm = take((size_t)H * V);
   const size_t o_wqkv = take(h->s_wqkv * L), o_wo = take(h->s_wo * L), o_wr = take(h->s_wr * L);
-  const size_t o_wgu = take(h->s_wgu_l * L), o_wd = take(h->s_wd_l * L);
+  // (FP8 feed-forward weights replace the bf16 ones: codes, 2 per element,
+  // and four float scales, 8 elements, per hidden unit)
+  const bool fp8 = c.ffn_fp8 != 0;
+  const size_t o_wgu = take(fp8 ? 0 : h->s_wgu_l * L), o_wd = take(fp8 ? 0 : h->s_wd_l * L);
   const size_t o_gamma2 = take(c.dense ? (size_t)L * H : 0);
+  h->s_gu8_e = fp8 ? (size_t)H * 2 * F : 0;
+  h->s_gu8_l = h->s_gu8_e * E;
+  h->s_d8_e = fp8 ? (size_t)F * H : 0;
+  h->s_d8_l = h->s_d8_e * E;
+  h->s_fsc_e = fp8 ? (size_t)F * 4 : 0;
+  h->s_fsc_l = h->s_fsc_e * E;
+  const size_t o_gu8 = take(h->s_gu8_l * L / 2), o_d8 = take(h->s_d8_l * L / 2), o_fsc = take(h->s_fsc_l * L * 2);
   if (hipMalloc(&h->w_all, off * 2) != hipSuccess)
     return fail(nullptr, MK_ERR_OOM, "cannot allocate %.1f GB of weights", off * 2 / 1e9);
   h->emb = h->w_all + o_emb;
@@ -1525,6 +1544,12 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->wgu = h->w_all + o_wgu;
   h->wd = h->w_all + o_wd;
   h->gamma2 = c.dense ? h->w_all + o_gamma2 : nullptr;
+  if (fp8) {
+    h->wgu8 = (uint8_t*)(h->w_all + o_gu8);
+    h->wd8 = (uint8_t*)(h->w_all + o_d8);
+    h->fsc = (float*)(h->w_all + o_fsc);
+    h->wgu = h->wd = nullptr;
+  }
   h->kv_bytes = kv_want;
   if (kv_pool) {
     h->kv = (uint16_t*)kv_pool;
@@ -1535,6 +1560,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     if (hipMemset(h->kv, 0, kv_want) != hipSuccess) return fail(nullptr, MK_ERR_HIP, "KV pool clear");
   }
   h->layer_loaded.assign(L, false);
+  h->ffn_loaded.assign(L, !fp8);
 
   // RoPE table: angle = pos * theta^(-2i/D) in double, cos/sin rounded to float
   {
@@ -1662,6 +1688,39 @@ static mk_status load_ffn(mk_handle* h, int layer, const void* wg, const void* w
   return MK_OK;
 }
 
+// bf16 feed-forward weights are given with the layer; FP8 ones (cfg.ffn_fp8)
+// through mk_load_ffn_fp8, the layer call then passing NULL for them.
+static mk_status check_ffn_args(mk_handle* h, const void* wg, const void* wu, const void* wd) {
+  if (h->cfg.ffn_fp8) {
+    if (wg || wu || wd)
+      return fail(h, MK_ERR_INVALID_ARG, "FP8 feed-forward weights load with mk_load_ffn_fp8 (pass NULL here)");
+  } else if (!wg || !wu || !wd) {
+    return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  }
+  return MK_OK;
+}
+
+mk_status mk_load_ffn_fp8(mk_handle* h, int layer, const void* wg8, const void* wu8, const void* wd8,
+                          const float* sg, const float* su, const float* sd, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (h->host_only) return fail(h, MK_ERR_STATE, "host-only handle");
+  const mk_config& c = h->cfg;
+  if (!c.ffn_fp8) return fail(h, MK_ERR_INVALID_ARG, "not an FP8 model (cfg.ffn_fp8 = 0)");
+  if (layer < 0 || layer >= c.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!wg8 || !wu8 || !wd8 || !sg || !su || !sd) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  for (const void* p : {wg8, wu8, wd8, (const void*)sg, (const void*)su, (const void*)sd})
+    if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(h, hipSetDevice(h->device));
+  const int H = c.hidden, E = c.n_experts, F = c.expert_ffn;
+  HIPCHECK(h, mk_launch_repack_fp8_gu((const uint8_t*)wg8, (const uint8_t*)wu8, h->wgu8 + layer * h->s_gu8_l, H, F,
+                                      E, s));
+  HIPCHECK(h, mk_launch_repack_fp8_d((const uint8_t*)wd8, h->wd8 + layer * h->s_d8_l, F, H, E, s));
+  HIPCHECK(h, mk_launch_pack_scales(sg, su, sd, h->fsc + layer * h->s_fsc_l, E * F, s));
+  h->ffn_loaded[layer] = true;
+  return MK_OK;
+}
+
 mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* wqkv, const void* wo, const void* wr,
                         const void* wg, const void* wu, const void* wd, void* stream) {
   if (!h) return MK_ERR_INVALID_ARG;
@@ -1669,13 +1728,15 @@ mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* 
   const mk_config& c = h->cfg;
   if (layer < 0 || layer >= c.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
   if (c.dense) return fail(h, MK_ERR_INVALID_ARG, "a dense model's layers load with mk_load_layer_dense");
-  if (!gamma || !wqkv || !wo || !wr || !wg || !wu || !wd) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  mk_status st = check_ffn_args(h, wg, wu, wd);
+  if (st != MK_OK) return st;
+  if (!gamma || !wqkv || !wo || !wr) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
   for (const void* p : {gamma, wqkv, wo, wr, wg, wu, wd})
     if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   HIPCHECK(h, hipSetDevice(h->device));
   const int H = c.hidden, E = c.n_experts;
-  mk_status st = load_attention(h, layer, gamma, wqkv, wo, s);
+  st = load_attention(h, layer, gamma, wqkv, wo, s);
   if (st != MK_OK) return st;
   if (h->e_pad == E) {
     HIPCHECK(h, mk_launch_repack((const uint16_t*)wr, h->wr + layer * h->s_wr, H, E, E, 0, 1, 1, 0, 0, s));
@@ -1689,8 +1750,10 @@ mk_status mk_load_layer(mk_handle* h, int layer, const void* gamma, const void* 
     HIPCHECK(h, mk_launch_repack(tmp, h->wr + layer * h->s_wr, H, h->e_pad, h->e_pad, 0, 1, 1, 0, 0, s));
     HIPCHECK(h, hipFreeAsync(tmp, s));
   }
-  st = load_ffn(h, layer, wg, wu, wd, s);
-  if (st != MK_OK) return st;
+  if (!c.ffn_fp8) {
+    st = load_ffn(h, layer, wg, wu, wd, s);
+    if (st != MK_OK) return st;
+  }
   h->layer_loaded[layer] = true;
   return MK_OK;
 }
@@ -1702,17 +1765,21 @@ mk_status mk_load_layer_dense(mk_handle* h, int layer, const void* gamma, const 
   const mk_config& c = h->cfg;
   if (!c.dense) return fail(h, MK_ERR_INVALID_ARG, "not a dense model: load layers with mk_load_layer");
   if (layer < 0 || layer >= c.n_layers) return fail(h, MK_ERR_INVALID_ARG, "layer %d out of range", layer);
-  if (!gamma || !wqkv || !wo || !gamma2 || !wg || !wu || !wd) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
+  mk_status st = check_ffn_args(h, wg, wu, wd);
+  if (st != MK_OK) return st;
+  if (!gamma || !wqkv || !wo || !gamma2) return fail(h, MK_ERR_INVALID_ARG, "null weight pointer");
   for (const void* p : {gamma, wqkv, wo, gamma2, wg, wu, wd})
     if ((uintptr_t)p % 16) return fail(h, MK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   HIPCHECK(h, hipSetDevice(h->device));
-  mk_status st = load_attention(h, layer, gamma, wqkv, wo, s);
+  st = load_attention(h, layer, gamma, wqkv, wo, s);
   if (st != MK_OK) return st;
   HIPCHECK(h, hipMemcpyAsync(h->gamma2 + (size_t)layer * c.hidden, gamma2, (size_t)c.hidden * 2,
                              hipMemcpyDeviceToDevice, s));
-  st = load_ffn(h, layer, wg, wu, wd, s);
-  if (st != MK_OK) return st;
+  if (!c.ffn_fp8) {
+    st = load_ffn(h, layer, wg, wu, wd, s);
+    if (st != MK_OK) return st;
+  }
   h->layer_loaded[layer] = true;
   return MK_OK;
 }
@@ -1737,15 +1804,18 @@ mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f, co
 mk_status mk_load_weights(mk_handle* h, const mk_weights* w, void* stream) {
   if (!h || !w) return MK_ERR_INVALID_ARG;
   const bool dense = h->cfg.dense != 0;
-  if (!w->gamma || !w->wqkv || !w->wo || !(dense ? w->gamma2 : w->wr) || !w->wg || !w->wu || !w->wd)
+  if (!w->gamma || !w->wqkv || !w->wo || !(dense ? w->gamma2 : w->wr) ||
+      (!h->cfg.ffn_fp8 && (!w->wg || !w->wu || !w->wd)))
     return fail(h, MK_ERR_INVALID_ARG, "null per-layer pointer array");
   mk_status st = mk_load_globals(h, w->emb, w->gamma_f, w->wlm, stream);
   if (st != MK_OK) return st;
   for (int l = 0; l < h->cfg.n_layers; ++l) {
-    st = dense ? mk_load_layer_dense(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->gamma2[l], w->wg[l], w->wu[l],
-                                     w->wd[l], stream)
-               : mk_load_layer(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->wr[l], w->wg[l], w->wu[l], w->wd[l],
-                               stream);
+    // (an FP8 model's feed-forward weights load through mk_load_ffn_fp8)
+    const void* wg = w->wg ? w->wg[l] : nullptr;
+    const void* wu = w->wu ? w->wu[l] : nullptr;
+    const void* wd = w->wd ? w->wd[l] : nullptr;
+    st = dense ? mk_load_layer_dense(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->gamma2[l], wg, wu, wd, stream)
+               : mk_load_layer(h, l, w->gamma[l], w->wqkv[l], w->wo[l], w->wr[l], wg, wu, wd, stream);
     if (st != MK_OK) return st;
   }
   return MK_OK;
@@ -1824,6 +1894,16 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.wd = h->wd;
   P.s_wd_l = h->s_wd_l;
   P.s_wd_e = h->s_wd_e;
+  P.ffn_fp8 = h->cfg.ffn_fp8;
+  P.wgu8 = h->wgu8;
+  P.s_gu8_l = h->s_gu8_l;
+  P.s_gu8_e = h->s_gu8_e;
+  P.wd8 = h->wd8;
+  P.s_d8_l = h->s_d8_l;
+  P.s_d8_e = h->s_d8_e;
+  P.fsc = h->fsc;
+  P.s_fsc_l = h->s_fsc_l;
+  P.s_fsc_e = h->s_fsc_e;
   P.wlm = h->wlm;
   P.rope = h->rope;
   P.kv = h->kv;
@@ -1874,8 +1954,10 @@ static mk_status decode_step(mk_handle* h, int batch, int32_t* tokens, const int
   if ((flags & MK_STEP_ADVANCE) && max_seq_len_hint >= c.max_seq_len)
     return fail(h, MK_ERR_INVALID_ARG, "advancing past max_seq_len");
   if (!h->globals_loaded) return fail(h, MK_ERR_STATE, "embedding/LM head not loaded");
-  for (int l = 0; l < c.n_layers; ++l)
+  for (int l = 0; l < c.n_layers; ++l) {
     if (!h->layer_loaded[l]) return fail(h, MK_ERR_STATE, "layer %d not loaded", l);
+    if (!h->ffn_loaded[l]) return fail(h, MK_ERR_STATE, "layer %d: FP8 feed-forward weights not loaded", l);
+  }
   Schedule* S = nullptr;
   if (noalloc) {
     if (h->lay.total > MK_STATIC_SCRATCH_BYTES)

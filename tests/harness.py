@@ -67,9 +67,11 @@ def tiny_case() -> TinyCase:
     return TinyCase(wl, cfg, weights, gen.NumpyWeights(weights), bs, ctx)
 
 
-def make_decoder(cfg, bs: gen.BatchState, pool_gpu: torch.Tensor, max_seq_len: int, mode: int, max_batch=None):
+def make_decoder(cfg, bs: gen.BatchState, pool_gpu: torch.Tensor, max_seq_len: int, mode: int, max_batch=None,
+                 ffn_fp8: bool = False):
     import moe_persistent_decode_amd as mk
-    mc = mk.make_config(cfg, max_batch or bs.tokens.shape[0], max_seq_len, bs.n_pages, bs.max_pages_per_seq, mode)
+    mc = mk.make_config(cfg, max_batch or bs.tokens.shape[0], max_seq_len, bs.n_pages, bs.max_pages_per_seq, mode,
+                        ffn_fp8=ffn_fp8)
     return mk.Decoder(mc, pool_gpu)
 
 
@@ -194,7 +196,10 @@ class RepairUploads:
                 continue
             w = self.layer_weights(l)
             w[f"wr.{l}"] = bits_to_torch(wr)
-            self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.LAYER_KINDS))
+            # (an FP8 model's feed-forward weights stay as loaded)
+            fp8 = bool(self.dec.cfg.ffn_fp8)
+            self.dec.load_layer(l, *(None if fp8 and k in ("wg", "wu", "wd") else w[f"{k}.{l}"]
+                                     for k in gen.LAYER_KINDS))
             self.up_r[l] = wr.copy()
         wlm = self.lm_state_wlm()
         if wlm is not None and (self.up_lm is None or not np.array_equal(self.up_lm, wlm)):

@@ -445,3 +445,30 @@ def test_litmus_rejects_bad_arguments_on_the_host():
     s, t = ctypes.c_uint32(0), ctypes.c_uint32(0)
     for pairs, rounds, mode in [(0, 10, 1), (513, 10, 1), (4, 0, 1), (4, 10, 3), (4, 10, -1)]:
         assert lib.mk_litmus_message_passing(0, pairs, rounds, mode, ctypes.byref(s), ctypes.byref(t)) == 1
+
+
+def test_fp8_ffn_config_limits_and_loader_checks():
+    """FP8 feed-forward weights: batches of at most 4 (the fused path), a 0/1
+    flag; a host-only handle takes no weights, and a bf16 handle refuses the
+    FP8 loader. An FP8 handle's schedules are the bf16 model's."""
+    import moe_persistent_decode_amd as mk
+    from moe_persistent_decode_amd.binding import Decoder, MkError
+    for m in (configs.TINY, configs.TINY_DENSE):
+        cfg = mk.make_config(m, 5, 1024, 64, 64, 0, ffn_fp8=True)
+        with pytest.raises(MkError, match="FP8"):
+            Decoder(cfg, host_only_cus=256)
+        cfg = mk.make_config(m, 4, 1024, 64, 64, 0)
+        cfg.ffn_fp8 = 2
+        with pytest.raises(MkError, match="ffn_fp8"):
+            Decoder(cfg, host_only_cus=256)
+    cfg = mk.make_config(configs.TINY, 4, 1024, 64, 64, 0, ffn_fp8=True)
+    d = Decoder(cfg, host_only_cus=256)
+    with pytest.raises(MkError, match="host-only"):
+        d.load_ffn_fp8(0, 16, 16, 16, 16, 16, 16, stream=0)
+    st, msg = d.simulate(4, 1000, [1] * configs.TINY.n_layers, seed=3)
+    assert st == 0, msg
+    d.close()
+    bf = _host(configs.TINY, batch=4, max_seq=1024)
+    with pytest.raises(MkError, match="host-only|not an FP8"):
+        bf.load_ffn_fp8(0, 16, 16, 16, 16, 16, 16, stream=0)
+    bf.close()

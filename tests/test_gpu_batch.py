@@ -32,10 +32,12 @@ pytestmark = pytest.mark.gpu
 STEPS = 4
 
 
-def _case(cfg, B, lo, hi, seed):
+def _case(cfg, B, lo, hi, seed, fp8=False):
     wl = configs.Workload(f"{cfg.name}_b{B}", cfg, batch=B, seq_len=(lo, hi), ragged=True, seed_batch=seed)
     bs = gen.make_batch(wl, extra_steps=STEPS)
     weights = gen.make_weights(cfg, seed=tiny_seed()["seed"])
+    if fp8:
+        gen.add_fp8_ffn(cfg, weights, drop_bf16=True)
     pool = gen.bf16_bits(gen.make_kv_pool(cfg, bs.n_pages, seed=seed + 100))
     return bs, weights, pool
 
@@ -66,28 +68,30 @@ def check_appended_kv(cfg, gpu_bits, ref_bits, pool0, bt, lens_per_step):
     assert np.array_equal(gpu_bits[~appended], pool0[~appended]), "a slot no step appended to changed"
 
 
-def _run(B, lo, hi, seed, mode, cfg=configs.TINY, options=None):
+def _run(B, lo, hi, seed, mode, cfg=configs.TINY, options=None, fp8=False):
     """Decode STEPS teacher-forced steps on GPU and oracle, compare every row;
     returns the GPU logits of every step. options: (wave order, placement[,
-    random placement seed])."""
-    bs, weights, pool0 = _case(cfg, B, lo, hi, seed)
+    random placement seed]). fp8: FP8 feed-forward weights (codes and scales
+    from the input quantizer, the same tensors on both sides)."""
+    bs, weights, pool0 = _case(cfg, B, lo, hi, seed, fp8)
     W = gen.NumpyWeights(weights)
     bt = bs.block_tables.numpy()
     toks = bs.tokens.numpy().copy()
     lens = bs.seq_lens.numpy().astype(np.int64)
-    say(f"[batch {B} {cfg.name} mode={mode}] lens {int(lens.min())}..{int(lens.max())} seed={seed}")
+    say(f"[batch {B} {cfg.name} mode={mode}{' fp8' if fp8 else ''}] lens {int(lens.min())}..{int(lens.max())} "
+        f"seed={seed}")
     rhook, rrep = router_repair_hook(cfg)
     lhook, lst = lm_repair_hook()
     pool_ref = pool0.copy()
     pool_gpu = bits_to_torch(pool0)
-    dec = make_decoder(cfg, bs, pool_gpu, int(lens.max()) + STEPS, mode, max_batch=B)
+    dec = make_decoder(cfg, bs, pool_gpu, int(lens.max()) + STEPS, mode, max_batch=B, ffn_fp8=fp8)
     if options is not None:
         dec.set_schedule_options(*options[:2])
         if len(options) > 2:
             dec.set_placement_seed(options[2])
     wgpu = {k: v.cuda() for k, v in weights.items()}
     dec.load_weights(wgpu)
-    up = RepairUploads(dec, rrep, lst, lambda l: {f"{k}.{l}": wgpu[f"{k}.{l}"] for k in gen.LAYER_KINDS},
+    up = RepairUploads(dec, rrep, lst, lambda l: {f"{k}.{l}": wgpu.get(f"{k}.{l}") for k in gen.LAYER_KINDS},
                        lambda: wgpu)
     trace = torch.full((cfg.n_layers, B, cfg.top_k), -1, dtype=torch.int32, device="cuda")
     dec.set_routing_trace(trace)

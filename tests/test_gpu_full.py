@@ -40,15 +40,15 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 
 class FullCase:
-    def __init__(self, wl, steps, mode):
+    def __init__(self, wl, steps, mode, fp8=False):
         m = wl.model
-        self.wl, self.m, self.steps = wl, m, steps
+        self.wl, self.m, self.steps, self.fp8 = wl, m, steps, fp8
         dev = torch.device("cuda:0")
         self.bs = gen.make_batch(wl, extra_steps=steps)
         self.pool = gen.make_kv_pool(m, self.bs.n_pages, seed=wl.seed_kv, device=dev)
         self.pool_host = gen.bf16_bits(self.pool)
         self.pool0 = self.pool_host.copy()
-        self.dec = make_decoder(m, self.bs, self.pool, int(self.bs.seq_lens.max()) + steps, mode)
+        self.dec = make_decoder(m, self.bs, self.pool, int(self.bs.seq_lens.max()) + steps, mode, ffn_fp8=fp8)
         hook, self.repaired = router_repair_hook(m)
         n_layers = m.n_layers
 
@@ -65,7 +65,7 @@ class FullCase:
         for l in range(m.n_layers):
             self._load_layer(l)
         torch.cuda.synchronize()
-        self.W = gen.LazyWeights(m, wl.seed_weights, device="cuda")
+        self.W = gen.LazyWeights(m, wl.seed_weights, device="cuda", fp8=fp8)
         self.up = RepairUploads(self.dec, self.repaired, self.lm_state,
                                 lambda l: gen.make_layer_weights(m, l, wl.seed_weights, "cuda"),
                                 lambda: {n: gen.weight_tensor(m, n, wl.seed_weights, dev) for n in gen.GLOBAL_NAMES})
@@ -80,7 +80,10 @@ class FullCase:
         w = gen.make_layer_weights(self.m, l, self.wl.seed_weights, "cuda")
         if l in self.repaired:
             w[f"wr.{l}"] = bits_to_torch(self.repaired[l])
-        self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.layer_kinds(self.m)))
+        if self.fp8:
+            q = gen.quantize_ffn_fp8(w.pop(f"wg.{l}"), w.pop(f"wu.{l}"), w.pop(f"wd.{l}"))
+            self.dec.load_ffn_fp8(l, *q)
+        self.dec.load_layer(l, *(w.get(f"{k}.{l}") for k in gen.layer_kinds(self.m)))
         torch.cuda.synchronize()
 
     def oracle_step(self, tokens, lens, record=True):
@@ -176,10 +179,10 @@ def _stages_layer1(c, tr):
     close("h", h_out, tr.h_out[0])
 
 
-def _run(wl, steps, mode, stages, advance=False):
-    say(f"[full {wl.name} mode={mode}] {steps} steps from seq_len {wl.seq_len[0]}"
+def _run(wl, steps, mode, stages, advance=False, fp8=False):
+    say(f"[full {wl.name} mode={mode}{' fp8' if fp8 else ''}] {steps} steps from seq_len {wl.seq_len[0]}"
         f"{' (in-kernel advance)' if advance else ''}")
-    c = FullCase(wl, steps, mode)
+    c = FullCase(wl, steps, mode, fp8)
     try:
         tokens = c.bs.tokens.numpy().copy()
         lens = c.bs.seq_lens.numpy().astype(np.int64)
