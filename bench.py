@@ -49,6 +49,14 @@ def parse():
                     help="comma-separated long-context workloads timed after the others ('none' to skip)")
     ap.add_argument("--dense-workload", default="llama1b_b1_8k",
                     help="dense (Llama-3.2-1B-shaped) workload timed after the others ('none' to skip)")
+    ap.add_argument("--fp8-workloads", default="full48_b1_8k,llama1b_b1_8k",
+                    help="workloads measured again with FP8 feed-forward weights, reported under fp8_weights "
+                         "('none' to skip)")
+    ap.add_argument("--ffn-fp8", action="store_true",
+                    help="measure the main workload with FP8 feed-forward weights (for profiling that path; the "
+                         "headline line is the bf16 model's)")
+    ap.add_argument("--fp8-op-trace", default=None, metavar="PATH",
+                    help="write the per-opcode trace of the first FP8 workload's step (markdown)")
     ap.add_argument("--single-layer", default="layer1_b1_8k",
                     help="one-layer workload timed with the last-level cache flushed between steps ('none' to skip)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling diagnostic")
@@ -75,12 +83,12 @@ def parse():
 class Run:
     """One workload resident on the GPU: weights, KV pool, batch state."""
 
-    def __init__(self, wl, steps, warmup, runs):
+    def __init__(self, wl, steps, warmup, runs, fp8=False):
         import torch
 
         import moe_persistent_decode_amd as mk
         from mkinputs import gen
-        self.wl, self.m, self.B = wl, wl.model, wl.batch
+        self.wl, self.m, self.B, self.fp8 = wl, wl.model, wl.batch, fp8
         self.K, self.W = steps, warmup
         dev = torch.device("cuda:0")
         self.stream = torch.cuda.current_stream()
@@ -90,18 +98,21 @@ class Run:
         t0 = time.time()
         self.pool = gen.make_kv_pool(self.m, self.bs.n_pages, seed=wl.seed_kv, device=dev)
         cfg = mk.make_config(self.m, self.B, self.max_seq, self.bs.n_pages, self.bs.max_pages_per_seq,
-                             mk.MODE_MEGAKERNEL)
+                             mk.MODE_MEGAKERNEL, ffn_fp8=fp8)
         self.dec = mk.Decoder(cfg, self.pool)
         g = {n: gen.weight_tensor(self.m, n, wl.seed_weights, dev) for n in gen.GLOBAL_NAMES}
         self.dec.load_globals(g["emb"], g["gamma_f"], g["wlm"])
         del g
         for l in range(self.m.n_layers):
             w = gen.make_layer_weights(self.m, l, wl.seed_weights, dev)
-            self.dec.load_layer(l, *(w[f"{k}.{l}"] for k in gen.layer_kinds(self.m)))
+            if fp8:  # the drawn FFN weights as FP8 codes and scales
+                self.dec.load_ffn_fp8(l, *gen.quantize_ffn_fp8(w.pop(f"wg.{l}"), w.pop(f"wu.{l}"), w.pop(f"wd.{l}")),
+                                      stream=self.stream)
+            self.dec.load_layer(l, *(w.get(f"{k}.{l}") for k in gen.layer_kinds(self.m)), stream=self.stream)
             self.stream.synchronize()
             del w
         torch.cuda.synchronize()
-        log(f"[bench] {wl.name}: B={self.B} lengths {int(self.bs.seq_lens.min())}..{int(self.bs.seq_lens.max())} "
+        log(f"[bench] {wl.name}{' (FP8 feed-forward weights)' if fp8 else ''}: B={self.B} lengths {int(self.bs.seq_lens.min())}..{int(self.bs.seq_lens.max())} "
             f"pages={self.bs.n_pages}; inputs drawn and loaded in {time.time() - t0:.1f}s")
         self.tokens = self.bs.tokens.to(dev)
         self.seq_lens = self.bs.seq_lens.to(dev)
@@ -147,14 +158,15 @@ class Run:
 
         from moe_persistent_decode_amd import sol
         if self.m.dense:  # one FFN per layer, no routing
-            tot = [sol.step_bytes(self.m, self.lens_host + first + i, [1] * self.m.n_layers) for i in range(self.K)]
+            tot = [sol.step_bytes(self.m, self.lens_host + first + i, [1] * self.m.n_layers, self.fp8)
+                   for i in range(self.K)]
             return float(np.mean(tot)), 1.0
         rt = self.route.cpu().numpy()
         tot = []
         for i in range(self.K):
             n_active = [len(np.unique(rt[i, l])) for l in range(self.m.n_layers)]
             assert min(n_active) >= 1 and rt[i].min() >= 0, "routing record incomplete"
-            tot.append(sol.step_bytes(self.m, self.lens_host + first + i, n_active))
+            tot.append(sol.step_bytes(self.m, self.lens_host + first + i, n_active, self.fp8))
         return float(np.mean(tot)), float(np.mean([len(np.unique(rt[i, l])) for i in range(self.K)
                                                    for l in range(self.m.n_layers)]))
 
@@ -246,9 +258,9 @@ def percentiles(xs):
             "p90": round(float(np.percentile(a, 90)), 4)}
 
 
-def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None):
+def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None, fp8=False):
     import moe_persistent_decode_amd as mk
-    r = Run(wl, steps, warmup, 2 if ab else 1)
+    r = Run(wl, steps, warmup, 2 if ab else 1, fp8)
     ms, first = r.timed(mk.MODE_MEGAKERNEL, record=True)
     step_ms = ms / r.K
     bytes_avg, n_act = r.algorithmic_bytes(first)
@@ -256,7 +268,7 @@ def measure(wl, steps, warmup, ab, trace_path=None, raw_path=None):
            "gbs": bytes_avg / (step_ms / 1e3) / 1e9, "experts_per_layer": n_act, "seq_len": r.hint,
            "lens": (int(r.lens_host.min()), int(r.lens_host.max()), float(r.lens_host.mean())),
            "step_ms": percentiles(r.step_ms)}
-    log(f"[bench] {wl.name} megakernel: {step_ms:.3f} ms/step, {res['tok_s']:.1f} tok/s, {res['gbs']:.0f} GB/s "
+    log(f"[bench] {wl.name}{' fp8' if fp8 else ''} megakernel: {step_ms:.3f} ms/step, {res['tok_s']:.1f} tok/s, {res['gbs']:.0f} GB/s "
         f"({res['gbs'] / PEAK_GBS:.1%} of 8 TB/s), {n_act:.1f} experts per layer")
     if ab:
         ms_op, _ = r.timed(mk.MODE_KERNEL_PER_OP)
@@ -498,9 +510,10 @@ def main():
         search(args.search, args.search_workloads.split(","), args.search_candidates, args.steps, args.warmup)
         return
     wl = configs.WORKLOADS[args.workload]
-    res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace, args.op_trace_raw)
+    res, bs = measure(wl, args.steps, args.warmup, not args.no_ab, args.op_trace, args.op_trace_raw,
+                      fp8=args.ffn_fp8)
 
-    traffic = counted_traffic(args.traffic_json, wl.name)
+    traffic = counted_traffic(args.traffic_json, wl.name + ("_fp8" if args.ffn_fp8 else ""))
     out = {
         "metric": "decode tok/s at batch 1 and 32, 8K ctx; HBM GB/s as % of MI355X peak",
         "value": round(res["tok_s"], 2),
@@ -512,7 +525,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16, fp8 e4m3 feed-forward weights" if args.ffn_fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": res["seq_len"],
                    "decode": "greedy, in-kernel advance"},
@@ -520,7 +533,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(res["gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["gbs"] / PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(res["bytes"]),
-                     "kernel": f"mk_interp<{wl.model.head_dim}, 1> (one launch per step)"},
+                     "kernel": f"mk_interp<{wl.model.head_dim}, 1{', true' if args.ffn_fp8 else ''}> "
+                               "(one launch per step)"},
     }
     if "kernel_per_op" in res:
         out["kernel_per_op"] = res["kernel_per_op"]
@@ -548,6 +562,17 @@ def main():
         kd = max(8, args.steps // 2)
         rd, _ = measure(wd, kd, min(args.warmup, 4), not args.no_ab)
         out["dense_workload"] = summary(wd, rd, kd)
+    # the same models with FP8 (E4M3) feed-forward weights, the rest bf16;
+    # bytes and roofline fraction count the FP8 codes and scales
+    if args.fp8_workloads != "none":
+        out["fp8_weights"] = []
+        for i, name in enumerate(args.fp8_workloads.split(",")):
+            wf = configs.WORKLOADS[name]
+            kf = max(8, args.steps // 2)
+            rf, _ = measure(wf, kf, min(args.warmup, 4), False, args.fp8_op_trace if i == 0 else None, fp8=True)
+            d = summary(wf, rf, kf)
+            d["weights"] = "feed-forward FP8 E4M3 (per-hidden-unit float32 scales), other weights bf16"
+            out["fp8_weights"].append(d)
     # long contexts: one sequence at 256K and four at 64K (the same model)
     if args.long_workloads != "none":
         out["long_context"] = []

@@ -32,7 +32,11 @@ def layer_weight_bytes(m) -> int:
     return 2 * (H * m.qkv_dim + m.q_dim * H + H * m.n_experts + H)
 
 
-def expert_bytes(m) -> int:
+def expert_bytes(m, fp8: bool = False) -> int:
+    """One expert's (or a dense layer's FFN) gate, up and down weights: bf16,
+    or FP8 codes plus three float32 scales per hidden unit."""
+    if fp8:
+        return 3 * m.hidden * m.expert_ffn + 3 * 4 * m.expert_ffn
     return 2 * 3 * m.hidden * m.expert_ffn
 
 
@@ -40,17 +44,17 @@ def kv_bytes_per_token(m) -> int:
     return 2 * 2 * m.n_kv_heads * m.head_dim
 
 
-def step_bytes(m, seq_lens: Sequence[int], n_active: Sequence[int]) -> int:
+def step_bytes(m, seq_lens: Sequence[int], n_active: Sequence[int], fp8: bool = False) -> int:
     """Algorithmic bytes of one step: seq_lens count the decoded token;
     n_active[l] = distinct experts routed to at layer l (1 for a dense
-    layer's FFN)."""
+    layer's FFN); fp8: FP8 feed-forward weights."""
     B = len(seq_lens)
     kvt = kv_bytes_per_token(m)
     total = 0
     for l in range(m.n_layers):
         win = m.layer_window(l)
         kv_read = sum(min(int(s), win) if win else int(s) for s in seq_lens) * kvt
-        total += layer_weight_bytes(m) + int(n_active[l]) * expert_bytes(m) + kv_read + B * kvt
+        total += layer_weight_bytes(m) + int(n_active[l]) * expert_bytes(m, fp8) + kv_read + B * kvt
     total += 2 * m.hidden * m.vocab + 2 * m.hidden + B * (2 * m.hidden + 4 * m.vocab)
     return total
 

@@ -57,7 +57,7 @@ Readings where the pages are silent (all fixed here, listed in the design doc):
   R11 Greedy token: argmax of the logits, the lowest index on ties
       (tiny-vllm walkthrough, "The remaining layers and logits": the scan
       replaces the running best only on a strictly greater value).
-  R12, R13 (FP8 feed-forward weights: the format and the scales): in the
+  R19, R20 (FP8 feed-forward weights: the format and the scales): in the
       fp8 section below.
 """
 from __future__ import annotations
@@ -93,11 +93,11 @@ def float_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 # FP8 and FP4 quantization on the roadmap; section on the other schedulers:
 # narrower types such as FP8). The pages fix neither the format nor the
 # scaling; the readings taken here (listed in the design doc):
-#   R12 The format is the OCP 8-bit floating point E4M3 ("FN": one sign bit,
+#   R19 The format is the OCP 8-bit floating point E4M3 ("FN": one sign bit,
 #       a 4-bit exponent of bias 7, a 3-bit mantissa; exponent field 0 holds
 #       the subnormals m * 2^-9; S.1111.111 is NaN; no infinities; largest
 #       finite magnitude 448).
-#   R13 Only the feed-forward weights are FP8 (each expert's gate, up and
+#   R20 Only the feed-forward weights are FP8 (each expert's gate, up and
 #       down matrices, or a dense layer's FFN): they are the bytes a decode
 #       step streams most of. Each hidden unit f of an FFN has three float32
 #       scales: its gate column, its up column and its down row are
@@ -106,7 +106,7 @@ def float_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 #       The rest of the step is as for bf16 weights.
 
 def e4m3_to_float(codes: np.ndarray) -> np.ndarray:
-    """OCP FP8 E4M3 codes (uint8) -> float64 values (R12), from the fields."""
+    """OCP FP8 E4M3 codes (uint8) -> float64 values (R19), from the fields."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
@@ -117,7 +117,7 @@ def e4m3_to_float(codes: np.ndarray) -> np.ndarray:
 
 
 def fp8_ffn_weights(cg, cu, cd, sg, su, sd, dtype=np.float64):
-    """One FFN's weights from FP8 codes and per-hidden-unit scales (R13):
+    """One FFN's weights from FP8 codes and per-hidden-unit scales (R20):
     cg, cu [H, F] and cd [F, H] uint8 codes; sg, su, sd [F] float32 scales.
     Returns (Wg, Wu, Wd) with each product formed in float64, then cast."""
     s = lambda v: np.asarray(v, dtype=np.float32).astype(np.float64)

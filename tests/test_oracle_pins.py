@@ -476,7 +476,7 @@ def test_run_minimum_gaps():
 
 
 # ------------------------------------------------------------ FP8 weights ----
-# R12 / R13: OCP E4M3 codes with per-hidden-unit scales (the roadmap's FP8
+# R19 / R20: OCP E4M3 codes with per-hidden-unit scales (the roadmap's FP8
 # weights, megakernel post, Chinese version, section "下一步").
 
 def test_e4m3_every_code_matches_the_library_decode():
