@@ -87,7 +87,8 @@ typedef struct {
                             * feed-forward weights, one float32 scale per hidden
                             * unit for each of its gate column, up column and
                             * down row, loaded with mk_load_ffn_fp8; the other
-                            * weights stay bf16. max_batch <= 4. (The post's
+                            * weights stay bf16; above 4 sequences the MoE is
+                            * the claiming variant at every batch. (The post's
                             * roadmap: FP8 weights, Chinese version, section
                             * "下一步".) */
 } mk_config;

@@ -708,6 +708,130 @@ __device__ __forceinline__ void reduce_tiles(const Acc<NP, MT>& acc, Smem& sm) {
   lds_sync();
 }
 
+// ------------------------------------------------ FP8 feed-forward weights
+// The post's roadmap names FP8 as the next, narrower weight type (Chinese
+// version, section "下一步"). Codes are OCP E4M3 with one float32 scale per
+// hidden unit for each of its gate column, up column and down row (code value
+// times scale). Every E4M3 value is exactly a bf16 value, so the gate/up codes
+// become the matrix cores' bf16 B operand in registers and the products run
+// as for bf16 weights; the scales apply to the hidden unit's gate and up sums
+// and, for the down row, to the unit's SiLU-and-multiply output.
+//
+// Gate/up panels: each 16-column panel is a run of K / 64 chunk pairs of
+// 1 KB; in pair p, lane l holds 16 bytes: the codes of rows 64p + 8(l/16) + i
+// (i = 0..7) of column l%16, then those of rows 64p + 32 + 8(l/16) + i. Pair
+// p goes to wave p % 8: each load is one contiguous 1 KB line per wave.
+template <int NP, int NPR>
+struct WTile8 {
+  u32x4_t v[NP][NPR];
+};
+
+// Pairs outside [p0, p1) and panels at or beyond np are zero (one buffer
+// resource, out-of-range reads return zeros).
+template <int NP, int NPR>
+__device__ __forceinline__ void wtile8_load(WTile8<NP, NPR>& w, const uint8_t* base, int pstride, int np, int p0,
+                                            int p1) {
+  const int wv = wave_id(), ln = lane_id();
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, np * pstride, 0x00020000);
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) {
+      const int p = p0 + wv + MK_WAVES * i;
+      const int off = (pp < np && p < p1) ? pp * pstride + p * 1024 + ln * 16 : 0x7ffffff0;
+      w.v[pp][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
+    }
+}
+
+// Four E4M3 codes -> their values as two words of bf16 pairs (codes 0, 1 in
+// lo; 2, 3 in hi). The hardware conversion gives float32 values of at most
+// four significant bits, so keeping their upper halves is exact.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t c, uint32_t& lo, uint32_t& hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+  lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+}
+
+// One lane's 16 codes of a chunk pair -> the bf16 B operands of its two chunks.
+__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4_t& c, u32x4_t& c0, u32x4_t& c1) {
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) e4m3x4_to_bf16(c[k], w[2 * k], w[2 * k + 1]);
+  c0 = u32x4_t{w[0], w[1], w[2], w[3]};
+  c1 = u32x4_t{w[4], w[5], w[6], w[7]};
+}
+
+// The activation operand matching a WTile8: slot 2i + h holds chunk
+// 2 (p0 + wave + 8 i) + h of the layer input staged in LDS (zero past p1).
+template <int NCH>
+__device__ __forceinline__ void atile_lds_pairs(ATile<1, NCH>& A, const uint16_t* xs, int H, int B, int p0, int p1) {
+  const int wv = wave_id(), ln = lane_id(), row = ln & 15;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int p = p0 + wv + MK_WAVES * (i / 2), c = 2 * p + (i % 2);
+    A.a[0][i] = (p < p1 && row < B) ? *(const u32x4_t*)(xs + row * H + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// acc (+)= (A hi + A lo) W over this wave's chunk pairs, W in E4M3 codes.
+template <int NP, int NPR>
+__device__ __forceinline__ void mfma_tiles8(Acc<NP, 1>& acc, const WTile8<NP, NPR>& w, const ATile<1, 2 * NPR>& Ah,
+                                            const ATile<1, 2 * NPR>& Al, bool add) {
+  if (!add) {
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) acc.c[pp][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < NPR; ++i)
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      u32x4_t b[2];
+      e4m3x16_to_bf16(w.v[pp][i], b[0], b[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Al.a[0][2 * i + h]),
+                                                               __builtin_bit_cast(bf16x8_t, b[h]), acc.c[pp][0], 0, 0, 0);
+        acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Ah.a[0][2 * i + h]),
+                                                               __builtin_bit_cast(bf16x8_t, b[h]), acc.c[pp][0], 0, 0, 0);
+      }
+    }
+}
+
+// Down rows in E4M3: slice s (rows 16 s .. 16 s + 15) of an FFN's [F x H]
+// down matrix is H runs of 16 bytes, run h holding the codes of rows
+// 16 s .. 16 s + 15 of column h (one contiguous 16 H bytes per slice).
+// Thread t takes columns t + 512 j. An invalid slice reads nothing (zeros).
+template <int NJ8>
+struct DTile8 {
+  u32x4_t v[NJ8];
+};
+
+template <int NJ8>
+__device__ __forceinline__ void dtile8_load(DTile8<NJ8>& d, const uint8_t* slice, int H, bool valid) {
+  const int t = tid();
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(slice), (short)0, valid ? H * 16 : 0, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NJ8; ++j) {
+    const int h = t + MK_WG_THREADS * j;
+    d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, h < H ? h * 16 : 0x7ffffff0, 0, kNT);
+  }
+}
+
+// Row tile of one K half in the chunk-pair order of FP8 weights: slot 2i + h
+// holds chunk 2 (p0 + wave + 8 i) + h of row o (negative: a zero row).
+template <int NCH>
+__device__ __forceinline__ void atile_load_row_pairs(ATile<1, NCH>& A, const Pub& src, int o, int p0, int p1) {
+  const int wv = wave_id(), ln = lane_id();
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int p = p0 + wv + MK_WAVES * (i / 2), c = 2 * p + (i % 2);
+    A.a[0][i] = (p < p1 && o >= 0) ? src.ld16x8(o + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
 // Row offsets of the batch's tokens (row b at b * stride + base), -1 beyond.
 __device__ __forceinline__ void set_rows_batch(const mk_params& P, Smem& sm, int slot, int stride, int base) {
   if (tid() < MK_MAX_BATCH) sm.row_off[slot][tid()] = (int)tid() < P.B ? (int)tid() * stride + base : -1;
@@ -1763,13 +1887,16 @@ __device__ __forceinline__ void claimer_start(const mk_params& P, int32_t claim_
 template <int MT, int NCH>
 __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb, const WTile<4, NCH>& w,
                                           Smem& sm, bool stage = true);
+template <int MT, int NPR>
+__device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb,
+                                          const WTile8<4, NPR>& w, Smem& sm, bool stage = true);
 
 // The claiming MoE above 16 tokens: each up/gate item's matrix-core rows are
 // the tokens routed to its expert (a second 16-row tile when an expert has
 // more), loaded together with the item's weights, so an item's operand takes
 // one row tile of registers instead of the whole batch's two and two items'
 // weights stream at once. Down items as in the claiming variant.
-template <int NCH, int NBMAX, int NCHD>
+template <int NCH, int NBMAX, int NCHD, bool FP8 = false>
 __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], dclaim_ctr = t.a[3];
@@ -1827,26 +1954,44 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   // expert) share the routed rows of one K half, loaded once per chunk.
   static_assert(CHU == 4, "one weight slot per item of a chunk");
   const int half = upe / 2;
+  // (FP8 feed-forward weights: gate/up codes in chunk pairs, kh_pairs per K
+  // half, the routed rows' chunks in the same pair order; the gu partial sums
+  // stay unscaled, the down item's staging applies the unit's scales)
+  const int kh_pairs = H / 128, pstride8 = (H / 64) * 1024;
+  using WG = std::conditional_t<FP8, WTile8<2, NCH / 2>, WTile<2, NCH>>;
   // one item's weights (a zero tile past the queue)
-  auto wload = [&](WTile<2, NCH>& w, int id) {
+  auto wload = [&](WG& w, int id) {
     const bool valid = id < n_items;
     const int a = valid ? id / upe : 0, r = id % upe;
     const int tt = r % half, kh = r / half;
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
-               valid ? 2 : 0, kh * kh_chunks, (kh + 1) * kh_chunks);
+    if constexpr (FP8)
+      wtile8_load(w, P.wgu8 + l * P.s_gu8_l + (size_t)e * P.s_gu8_e + (size_t)(2 * tt) * pstride8, pstride8,
+                  valid ? 2 : 0, kh * kh_pairs, (kh + 1) * kh_pairs);
+    else
+      wtile_load(w, P.wgu + l * P.s_wgu_l + (size_t)e * P.s_wgu_e + (size_t)(2 * tt) * pstride, pstride,
+                 valid ? 2 : 0, kh * kh_chunks, (kh + 1) * kh_chunks);
+  };
+  // row tile rt's rows of one K half
+  auto row_tile = [&](ATile<1, NCH>& Xh, ATile<1, NCH>& Xl, int o, int kh) {
+    if constexpr (FP8) {
+      atile_load_row_pairs(Xh, U0, o, kh * kh_pairs, (kh + 1) * kh_pairs);
+      atile_load_row_pairs(Xl, U1, o, kh * kh_pairs, (kh + 1) * kh_pairs);
+    } else {
+      atile_load_row(Xh, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+      atile_load_row(Xl, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+    }
   };
   // a chunk's routed rows (no rows past the queue)
   auto rows = [&](ATile<1, NCH>& Xh, ATile<1, NCH>& Xl, int id) {
     const bool valid = id < n_items;
     const int a = valid ? id / upe : 0, kh = (id % upe) / half;
     const int o = row_of(valid ? a : -1, 0);
-    atile_load_row(Xh, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
-    atile_load_row(Xl, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
+    row_tile(Xh, Xl, o, kh);
   };
   // one item's products and gu stores with its chunk's rows; the arrival is
   // counted in LDS
-  auto compute = [&](const WTile<2, NCH>& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int id) {
+  auto compute = [&](const WG& w, ATile<1, NCH>& Ah, ATile<1, NCH>& Al, int id) {
     if (id >= n_items) return;
     const int a = id / upe, r = id % upe;
     const int tt = r % half, kh = r / half;
@@ -1856,13 +2001,13 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     // are loaded again)
     int rt = 0;
     do {
-      if (rt > 0) {  // an expert with more than 16 routed tokens: the next rows
-        const int o = row_of(a, rt);
-        atile_load_row(Ah, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
-        atile_load_row(Al, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
-      }
+      if (rt > 0)  // an expert with more than 16 routed tokens: the next rows
+        row_tile(Ah, Al, row_of(a, rt), kh);
       Acc<2, 1> acc;
-      mfma_tiles(acc, w, Ah, Al);
+      if constexpr (FP8)
+        mfma_tiles8(acc, w, Ah, Al, false);
+      else
+        mfma_tiles(acc, w, Ah, Al);
       reduce_tiles(acc, sm);
       // gu[slot][kh][gate|up][F] of the tile's routed rows
       // (at most 2 x 16 x 16 = 512 values: one predicated store per thread,
@@ -1881,11 +2026,7 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
       }
     } while (++rt * 16 < cnt);
     // (a later item of the chunk needs the first row tile again)
-    if (rt > 1 && id % CHU != CHU - 1) {
-      const int o = row_of(a, 0);
-      atile_load_row(Ah, U0, o, kh * kh_chunks, (kh + 1) * kh_chunks);
-      atile_load_row(Al, U1, o, kh * kh_chunks, (kh + 1) * kh_chunks);
-    }
+    if (rt > 1 && id % CHU != CHU - 1) row_tile(Ah, Al, row_of(a, 0), kh);
     if (tid() == 0) sm.done_cnt[a] += 1;
   };
   // the next claimed chunk's first item (the claim after it is issued now,
@@ -1906,7 +2047,7 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     // every set index is fixed). The arrivals wait for the end of the phase
     // (one drain), since down items start only after this claimer's up/gate
     // items.
-    WTile<2, NCH> w0, w1, w2, w3;
+    WG w0, w1, w2, w3;
     ATile<1, NCH> X0h, X0l, X1h, X1l;
     int pend = 0;
     if (tid() == 0)
@@ -1952,15 +2093,21 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   // reuse its staged operand
   const int DP = P.CB / 16, kcd = P.F / 32, dpe = P.down_items_per_expert;
   const size_t pstride_d = (size_t)kcd * 512;
-  auto dload = [&](WTile<4, NCHD>& w, int id) {
+  const int pstride8_d = (P.F / 64) * 1024;
+  using WD = std::conditional_t<FP8, WTile8<4, (NCHD + 1) / 2>, WTile<4, NCHD>>;
+  auto dload = [&](WD& w, int id) {
     const bool valid = id < n_down;
     const int a = valid ? id / dpe : 0, cb = id % dpe;
     const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
-    wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
-               valid ? DP : 0, 0, kcd);
+    if constexpr (FP8)
+      wtile8_load(w, P.wd8p + l * P.s_d8_l + (size_t)e * P.s_d8_e + (size_t)(cb * DP) * pstride8_d, pstride8_d,
+                  valid ? DP : 0, 0, kcd / 2);
+    else
+      wtile_load(w, P.wd + l * P.s_wd_l + (size_t)e * P.s_wd_e + (size_t)(cb * DP) * pstride_d, pstride_d,
+                 valid ? DP : 0, 0, kcd);
   };
   {
-    WTile<4, NCHD> d0, d1;
+    WD d0, d1;
     Stream q;
     stream_start(q, dbase, dclaim_ctr, n_down, CHD);
     int i0 = q.base;
@@ -1973,14 +2120,14 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     while (i0 < n_down) {
       uint32_t err = error_peek(P);
       dload(d1, i1);
-      down_item<2, NCHD>(P, t, i0 / dpe, i0 % dpe, d0, sm, i0 / dpe != staged);
+      down_item<2>(P, t, i0 / dpe, i0 % dpe, d0, sm, i0 / dpe != staged);
       staged = i0 / dpe;
       if (error_seen(err, sm)) return;
       i0 = i1 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
       if (i1 >= n_down) break;
       err = error_peek(P);
       dload(d0, i0);
-      down_item<2, NCHD>(P, t, i1 / dpe, i1 % dpe, d1, sm, i1 / dpe != staged);
+      down_item<2>(P, t, i1 / dpe, i1 % dpe, d1, sm, i1 / dpe != staged);
       staged = i1 / dpe;
       if (error_seen(err, sm)) return;
       i1 = i0 < n_down ? stream_next(q, dclaim_ctr, n_down) : n_down;
@@ -1995,7 +2142,11 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
 // Only the routed rows are loaded, eight elements per thread in flight per
 // round; rows past nr are left as they are (the product's output rows past
 // the routed ones are not stored).
-__device__ __forceinline__ void stage_act(const mk_params& P, int a, int r0, int nr, Smem& sm) {
+// sc: FP8 weights' scale rows of the expert ([F][4]: gate, up, down, 0), or
+// null for bf16 weights: then gate and up are scaled before the SiLU and the
+// product by the down scale.
+__device__ __forceinline__ void stage_act(const mk_params& P, int a, int r0, int nr, Smem& sm,
+                                          const float* sc = nullptr) {
   const int F = P.F, B = P.B, n = nr * F, lo = 16 * F;
   const Pub GU(P.gu);
   constexpr int R = 8;
@@ -2013,8 +2164,14 @@ __device__ __forceinline__ void stage_act(const mk_params& P, int a, int r0, int
     for (int k = 0; k < R; ++k) {
       const int i = i0 + k * MK_WG_THREADS;
       if (i < n) {
-        const float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3];
-        split_bf16(gt / (1.0f + __expf(-gt)) * ut, sm.act[i], sm.act[lo + i]);
+        float gt = g[k][0] + g[k][1], ut = g[k][2] + g[k][3], dsc = 1.f;
+        if (sc) {
+          const float4 s4 = *(const float4*)(sc + 4 * (i % F));
+          gt *= s4.x;
+          ut *= s4.y;
+          dsc = s4.z;
+        }
+        split_bf16(gt / (1.0f + __expf(-gt)) * ut * dsc, sm.act[i], sm.act[lo + i]);
       }
     }
   }
@@ -2275,6 +2432,66 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
   block_arrive(P, t, t.a[4], cb, sm);
 }
 
+// The same with FP8 down codes in chunk pairs (pair p = wave + 8 i of the
+// expert's K = F rows), converted to bf16 operands in registers; the staged
+// operand carries the unit scales (stage_act with the expert's scale rows).
+template <int MT, int NPR>
+__device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, int a, int cb,
+                                          const WTile8<4, NPR>& w, Smem& sm, bool stage) {
+  const int F = P.F, H = P.H, B = P.B;
+  const int kp = F / 64;
+  const int DP = P.CB / 16;
+  const int cnt = sm.rt_cnt[a];
+  const Pub DN(P.dn);
+  stage = stage || cnt > 16;
+  if (stage && !wait_one(P, t.a[1] + a, P.up_items_per_expert, sm, true)) return;
+  const int e = __builtin_amdgcn_readfirstlane(sm.rt_e[a]);
+  const float* sc = P.fsc + t.layer * P.s_fsc_l + (size_t)e * P.s_fsc_e;
+  Acc<4, MT> acc;
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc.c[pp][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int n = 16 * F;
+    if (mt * 16 >= cnt) break;  // (uniform) no routed rows in this tile
+    if (stage) stage_act(P, a, mt * 16, min(16, cnt - mt * 16), sm, sc);
+    const int wv = wave_id(), ln = lane_id();
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) {
+      const int p = wv + MK_WAVES * i;
+      u32x4_t b[4][2];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) e4m3x16_to_bf16(w.v[pp][i], b[pp][0], b[pp][1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * p + h;
+        const int off = (ln & 15) * F + 32 * c + 8 * (ln >> 4);
+        const u32x4_t ah = p < kp ? *(const u32x4_t*)(sm.act + off) : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t al = p < kp ? *(const u32x4_t*)(sm.act + n + off) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                                  __builtin_bit_cast(bf16x8_t, b[pp][h]),
+                                                                  acc.c[pp][mt], 0, 0, 0);
+          acc.c[pp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                                  __builtin_bit_cast(bf16x8_t, b[pp][h]),
+                                                                  acc.c[pp][mt], 0, 0, 0);
+        }
+      }
+    }
+    lds_sync();
+  }
+  reduce_tiles(acc, sm);
+  for (int o = tid(); o < 4 * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int row = mt * 16 + m;
+    if (pp < DP && row < cnt) DN.stf(sm.rt_slot[a * B + row] * H + (cb * DP + pp) * 16 + nn, sm.out[o]);
+  }
+  block_arrive(P, t, t.a[4], cb, sm);
+}
+
 
 // ------------------------------------------------------- fused MoE
 // Batches of at most MK_FUSED_B tokens. An item is one 16-row slice s of an
@@ -2338,118 +2555,6 @@ __device__ __forceinline__ void atile_lds(ATile<1, NCH>& A, const uint16_t* xs, 
   for (int i = 0; i < NCH; ++i) {
     const int c = c0 + wv + MK_WAVES * i;
     A.a[0][i] = (c < c1 && row < B) ? *(const u32x4_t*)(xs + row * H + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-}
-
-// ------------------------------------------------ FP8 feed-forward weights
-// The post's roadmap names FP8 as the next, narrower weight type (Chinese
-// version, section "下一步"). Codes are OCP E4M3 with one float32 scale per
-// hidden unit for each of its gate column, up column and down row (code value
-// times scale). Every E4M3 value is exactly a bf16 value, so the gate/up codes
-// become the matrix cores' bf16 B operand in registers and the products run
-// as for bf16 weights; the scales apply to the hidden unit's gate and up sums
-// and, for the down row, to the unit's SiLU-and-multiply output.
-//
-// Gate/up panels: each 16-column panel is a run of K / 64 chunk pairs of
-// 1 KB; in pair p, lane l holds 16 bytes: the codes of rows 64p + 8(l/16) + i
-// (i = 0..7) of column l%16, then those of rows 64p + 32 + 8(l/16) + i. Pair
-// p goes to wave p % 8: each load is one contiguous 1 KB line per wave.
-template <int NP, int NPR>
-struct WTile8 {
-  u32x4_t v[NP][NPR];
-};
-
-// Pairs outside [p0, p1) and panels at or beyond np are zero (one buffer
-// resource, out-of-range reads return zeros).
-template <int NP, int NPR>
-__device__ __forceinline__ void wtile8_load(WTile8<NP, NPR>& w, const uint8_t* base, int pstride, int np, int p0,
-                                            int p1) {
-  const int wv = wave_id(), ln = lane_id();
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, np * pstride, 0x00020000);
-#pragma unroll
-  for (int pp = 0; pp < NP; ++pp)
-#pragma unroll
-    for (int i = 0; i < NPR; ++i) {
-      const int p = p0 + wv + MK_WAVES * i;
-      const int off = (pp < np && p < p1) ? pp * pstride + p * 1024 + ln * 16 : 0x7ffffff0;
-      w.v[pp][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
-    }
-}
-
-// Four E4M3 codes -> their values as two words of bf16 pairs (codes 0, 1 in
-// lo; 2, 3 in hi). The hardware conversion gives float32 values of at most
-// four significant bits, so keeping their upper halves is exact.
-__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t c, uint32_t& lo, uint32_t& hi) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-  lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-}
-
-// One lane's 16 codes of a chunk pair -> the bf16 B operands of its two chunks.
-__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4_t& c, u32x4_t& c0, u32x4_t& c1) {
-  uint32_t w[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) e4m3x4_to_bf16(c[k], w[2 * k], w[2 * k + 1]);
-  c0 = u32x4_t{w[0], w[1], w[2], w[3]};
-  c1 = u32x4_t{w[4], w[5], w[6], w[7]};
-}
-
-// The activation operand matching a WTile8: slot 2i + h holds chunk
-// 2 (p0 + wave + 8 i) + h of the layer input staged in LDS (zero past p1).
-template <int NCH>
-__device__ __forceinline__ void atile_lds_pairs(ATile<1, NCH>& A, const uint16_t* xs, int H, int B, int p0, int p1) {
-  const int wv = wave_id(), ln = lane_id(), row = ln & 15;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int p = p0 + wv + MK_WAVES * (i / 2), c = 2 * p + (i % 2);
-    A.a[0][i] = (p < p1 && row < B) ? *(const u32x4_t*)(xs + row * H + 32 * c + 8 * (ln >> 4)) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-}
-
-// acc (+)= (A hi + A lo) W over this wave's chunk pairs, W in E4M3 codes.
-template <int NP, int NPR>
-__device__ __forceinline__ void mfma_tiles8(Acc<NP, 1>& acc, const WTile8<NP, NPR>& w, const ATile<1, 2 * NPR>& Ah,
-                                            const ATile<1, 2 * NPR>& Al, bool add) {
-  if (!add) {
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) acc.c[pp][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int i = 0; i < NPR; ++i)
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      u32x4_t b[2];
-      e4m3x16_to_bf16(w.v[pp][i], b[0], b[1]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Al.a[0][2 * i + h]),
-                                                               __builtin_bit_cast(bf16x8_t, b[h]), acc.c[pp][0], 0, 0, 0);
-        acc.c[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Ah.a[0][2 * i + h]),
-                                                               __builtin_bit_cast(bf16x8_t, b[h]), acc.c[pp][0], 0, 0, 0);
-      }
-    }
-}
-
-// Down rows in E4M3: slice s (rows 16 s .. 16 s + 15) of an FFN's [F x H]
-// down matrix is H runs of 16 bytes, run h holding the codes of rows
-// 16 s .. 16 s + 15 of column h (one contiguous 16 H bytes per slice).
-// Thread t takes columns t + 512 j. An invalid slice reads nothing (zeros).
-template <int NJ8>
-struct DTile8 {
-  u32x4_t v[NJ8];
-};
-
-template <int NJ8>
-__device__ __forceinline__ void dtile8_load(DTile8<NJ8>& d, const uint8_t* slice, int H, bool valid) {
-  const int t = tid();
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(slice), (short)0, valid ? H * 16 : 0, 0x00020000);
-#pragma unroll
-  for (int j = 0; j < NJ8; ++j) {
-    const int h = t + MK_WG_THREADS * j;
-    d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, h < H ? h * 16 : 0x7ffffff0, 0, kNT);
   }
 }
 
@@ -3050,7 +3155,10 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
     case MK_OP_MOE_UP:
       // at most 16 tokens: fixed shares (b[2], the claimer count, is set);
       // above: claiming, each item's routed rows
-      if constexpr (MT == 1)
+      // (FP8 feed-forward weights: claiming at every batch above MK_FUSED_B)
+      if constexpr (FP8)
+        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES, true>(P, t, sm);
+      else if constexpr (MT == 1)
         op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
       else
         op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
@@ -3139,9 +3247,11 @@ template __global__ void mk_interp<64, 1, false>(mk_params);
 template __global__ void mk_interp<64, 2, false>(mk_params);
 template __global__ void mk_interp<128, 1, false>(mk_params);
 template __global__ void mk_interp<128, 2, false>(mk_params);
-// FP8 feed-forward weights: batches of at most MK_FUSED_B (one row tile)
+// FP8 feed-forward weights
 template __global__ void mk_interp<64, 1, true>(mk_params);
+template __global__ void mk_interp<64, 2, true>(mk_params);
 template __global__ void mk_interp<128, 1, true>(mk_params);
+template __global__ void mk_interp<128, 2, true>(mk_params);
 
 // ------------------------------------------------------------- repacking
 // Canonical row-major [K x N] (leading dimension ld) -> panel-tiled layout,
@@ -3175,28 +3285,29 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_panels(const uint16_
   }
 }
 
-// FP8 gate/up codes: canonical wg, wu [E][H][F] (bytes) -> per expert 2 F / 16
-// panels (gate panel j at 2j, up panel j at 2j + 1) of H / 64 chunk pairs of
-// 1 KB, lane l of pair p holding rows 64p + 8(l/16) + i, then rows
-// 64p + 32 + 8(l/16) + i (i = 0..7), of column 16j + l%16. One thread per
-// 16-byte lane unit.
-extern "C" __global__ __launch_bounds__(256) void mk_repack_fp8_gu(const uint8_t* wg, const uint8_t* wu,
-                                                                   uint8_t* dst, int H, int F, int E) {
-  const int npair = H / 64, npan = 2 * (F / 16);
-  const size_t n = (size_t)E * npan * npair * 64;
+// FP8 codes of a [K x N] matrix (canonical row-major, bytes) -> panels of K / 64
+// chunk pairs of 1 KB (the layout of the gate/up panels below, for any
+// matrix): source panel j to destination panel dst0 + j * dstep; z strides
+// both sides. One thread per 16-byte lane unit.
+extern "C" __global__ __launch_bounds__(256) void mk_repack_fp8_panels(const uint8_t* src, uint8_t* dst, int K, int N,
+                                                                       int dst0, int dstep, int nz,
+                                                                       size_t src_zstride, size_t dst_zstride) {
+  const int npair = K / 64, npan = N / 16;
+  const size_t n = (size_t)nz * npan * npair * 64;
   for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (size_t)gridDim.x * 256) {
     const int l = (int)(u % 64), p = (int)((u / 64) % npair);
-    const int pj = (int)((u / ((size_t)64 * npair)) % npan);
-    const int e = (int)(u / ((size_t)64 * npair * npan));
-    const uint8_t* src = (pj & 1 ? wu : wg) + (size_t)e * H * F;
-    const int col = 16 * (pj >> 1) + (l & 15);
+    const int j = (int)((u / ((size_t)64 * npair)) % npan);
+    const int z = (int)(u / ((size_t)64 * npair * npan));
+    const uint8_t* s = src + z * src_zstride;
+    const int col = 16 * j + (l & 15);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
       const int row = 64 * p + (b >= 8 ? 32 : 0) + 8 * (l >> 4) + (b & 7);
-      w[b >> 2] |= (uint32_t)src[(size_t)row * F + col] << (8 * (b & 3));
+      w[b >> 2] |= (uint32_t)s[(size_t)row * N + col] << (8 * (b & 3));
     }
-    *(u32x4_t*)(dst + (size_t)e * 2 * H * F + ((size_t)pj * npair + p) * 1024 + l * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+    const int pj = dst0 + j * dstep;
+    *(u32x4_t*)(dst + z * dst_zstride + ((size_t)pj * npair + p) * 1024 + l * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -3446,13 +3557,13 @@ hipError_t mk_launch_zero(uint32_t* p, int n, hipStream_t stream) {
 }
 
 static const void* interp_fn(int head_dim, int mt, bool fp8 = false) {
-  if (fp8) return head_dim == 64 ? (const void*)mk_interp<64, 1, true> : (const void*)mk_interp<128, 1, true>;
+  if (fp8 && head_dim == 64) return mt == 1 ? (const void*)mk_interp<64, 1, true> : (const void*)mk_interp<64, 2, true>;
+  if (fp8) return mt == 1 ? (const void*)mk_interp<128, 1, true> : (const void*)mk_interp<128, 2, true>;
   if (head_dim == 64) return mt == 1 ? (const void*)mk_interp<64, 1, false> : (const void*)mk_interp<64, 2, false>;
   return mt == 1 ? (const void*)mk_interp<128, 1, false> : (const void*)mk_interp<128, 2, false>;
 }
 
 hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool cooperative, hipStream_t stream) {
-  // (FP8 feed-forward weights run at most MK_FUSED_B sequences: the host rejects more)
   const void* fn = interp_fn(head_dim, P.B > 16 ? 2 : 1, P.ffn_fp8 != 0);
   void* args[] = {(void*)&P};
   if (cooperative)
@@ -3460,9 +3571,10 @@ hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool coo
   return hipLaunchKernel(fn, dim3(grid), dim3(MK_WG_THREADS), args, 0, stream);
 }
 
-hipError_t mk_launch_repack_fp8_gu(const uint8_t* wg, const uint8_t* wu, uint8_t* dst, int H, int F, int E,
-                                   hipStream_t stream) {
-  hipLaunchKernelGGL(mk_repack_fp8_gu, dim3(4096), dim3(256), 0, stream, wg, wu, dst, H, F, E);
+hipError_t mk_launch_repack_fp8_panels(const uint8_t* src, uint8_t* dst, int K, int N, int dst0, int dstep, int nz,
+                                       size_t src_zstride, size_t dst_zstride, hipStream_t stream) {
+  hipLaunchKernelGGL(mk_repack_fp8_panels, dim3(4096), dim3(256), 0, stream, src, dst, K, N, dst0, dstep, nz,
+                     src_zstride, dst_zstride);
   return hipGetLastError();
 }
 
@@ -3493,8 +3605,12 @@ hipError_t mk_interp_occupancy(int head_dim, int* blocks_per_cu) {
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, interp_fn(head_dim, 2), MK_WG_THREADS, 0);
   if (e != hipSuccess) return e;
-  int c = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, interp_fn(head_dim, 1, true), MK_WG_THREADS, 0);
-  *blocks_per_cu = a < b ? (a < c ? a : c) : (b < c ? b : c);
+  for (int mt = 1; mt <= 2; ++mt) {
+    int c = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, interp_fn(head_dim, mt, true), MK_WG_THREADS, 0);
+    if (e != hipSuccess) return e;
+    if (c < b) b = c;
+  }
+  *blocks_per_cu = a < b ? a : b;
   return e;
 }

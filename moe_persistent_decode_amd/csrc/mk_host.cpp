@@ -130,7 +130,7 @@ struct mk_handle {
   uint16_t *emb = nullptr, *gamma = nullptr, *gamma2 = nullptr, *wqkv = nullptr, *wo = nullptr, *wr = nullptr,
            *wgu = nullptr, *wd = nullptr, *wlm = nullptr;
   // FP8 feed-forward weights (cfg.ffn_fp8): codes in bytes, scales in floats
-  uint8_t *wgu8 = nullptr, *wd8 = nullptr;
+  uint8_t *wgu8 = nullptr, *wd8 = nullptr, *wd8p = nullptr;
   float* fsc = nullptr;
   size_t s_gu8_l = 0, s_gu8_e = 0, s_d8_l = 0, s_d8_e = 0, s_fsc_l = 0, s_fsc_e = 0;
   float* rope = nullptr;
@@ -205,9 +205,6 @@ mk_status validate_config(const mk_config* c) {
     return fail(nullptr, MK_ERR_UNSUPPORTED, "group size must be <= 16 and group width <= 1024");
   if (c->dense != 0 && c->dense != 1) return fail(nullptr, MK_ERR_INVALID_ARG, "dense must be 0 or 1");
   if (c->ffn_fp8 != 0 && c->ffn_fp8 != 1) return fail(nullptr, MK_ERR_INVALID_ARG, "ffn_fp8 must be 0 or 1");
-  if (c->ffn_fp8 && c->max_batch > MK_FUSED_B)
-    return fail(nullptr, MK_ERR_UNSUPPORTED, "FP8 feed-forward weights decode at most %d sequences per step",
-                MK_FUSED_B);
   if (c->dense) {
     if (c->n_experts != 1 || c->top_k != 1)
       return fail(nullptr, MK_ERR_INVALID_ARG, "a dense model has n_experts = top_k = 1");
@@ -541,7 +538,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     int n_free = 0, wa = 256, nt = 0;
     std::vector<char> attn_cu(n_w, 0);
     const bool fused = B <= MK_FUSED_B && n_w <= MK_WG_THREADS;
-    const bool fixed = B <= 16;
+    // (FP8 feed-forward weights: the claiming MoE at every batch above MK_FUSED_B)
+    const bool fixed = B <= 16 && !c.ffn_fp8;
     // the unit a task goes to: `cu` when the placement is tuned, else the
     // round-robin unit of its flat index
     auto place = [&](const mk_task& t, int cu) {
@@ -1533,6 +1531,9 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
   h->s_fsc_e = fp8 ? (size_t)F * 4 : 0;
   h->s_fsc_l = h->s_fsc_e * E;
   const size_t o_gu8 = take(h->s_gu8_l * L / 2), o_d8 = take(h->s_d8_l * L / 2), o_fsc = take(h->s_fsc_l * L * 2);
+  // (above MK_FUSED_B sequences the claiming MoE reads the down codes as panels)
+  const bool panels8 = fp8 && c.max_batch > MK_FUSED_B;
+  const size_t o_d8p = take(panels8 ? h->s_d8_l * L / 2 : 0);
   if (hipMalloc(&h->w_all, off * 2) != hipSuccess)
     return fail(nullptr, MK_ERR_OOM, "cannot allocate %.1f GB of weights", off * 2 / 1e9);
   h->emb = h->w_all + o_emb;
@@ -1548,6 +1549,7 @@ mk_status mk_create(const mk_config* cfg, void* kv_pool, size_t kv_pool_bytes, i
     h->wgu8 = (uint8_t*)(h->w_all + o_gu8);
     h->wd8 = (uint8_t*)(h->w_all + o_d8);
     h->fsc = (float*)(h->w_all + o_fsc);
+    h->wd8p = panels8 ? (uint8_t*)(h->w_all + o_d8p) : nullptr;
     h->wgu = h->wd = nullptr;
   }
   h->kv_bytes = kv_want;
@@ -1713,9 +1715,14 @@ mk_status mk_load_ffn_fp8(mk_handle* h, int layer, const void* wg8, const void* 
   hipStream_t s = (hipStream_t)stream;
   HIPCHECK(h, hipSetDevice(h->device));
   const int H = c.hidden, E = c.n_experts, F = c.expert_ffn;
-  HIPCHECK(h, mk_launch_repack_fp8_gu((const uint8_t*)wg8, (const uint8_t*)wu8, h->wgu8 + layer * h->s_gu8_l, H, F,
-                                      E, s));
+  // gate and up panels interleaved (gate panel j -> 2j, up panel j -> 2j + 1)
+  uint8_t* gu = h->wgu8 + layer * h->s_gu8_l;
+  HIPCHECK(h, mk_launch_repack_fp8_panels((const uint8_t*)wg8, gu, H, F, 0, 2, E, (size_t)H * F, h->s_gu8_e, s));
+  HIPCHECK(h, mk_launch_repack_fp8_panels((const uint8_t*)wu8, gu, H, F, 1, 2, E, (size_t)H * F, h->s_gu8_e, s));
   HIPCHECK(h, mk_launch_repack_fp8_d((const uint8_t*)wd8, h->wd8 + layer * h->s_d8_l, F, H, E, s));
+  if (h->wd8p)
+    HIPCHECK(h, mk_launch_repack_fp8_panels((const uint8_t*)wd8, h->wd8p + layer * h->s_d8_l, F, H, 0, 1, E,
+                                            (size_t)F * H, h->s_d8_e, s));
   HIPCHECK(h, mk_launch_pack_scales(sg, su, sd, h->fsc + layer * h->s_fsc_l, E * F, s));
   h->ffn_loaded[layer] = true;
   return MK_OK;
@@ -1899,6 +1906,7 @@ static void fill_params(mk_handle* h, Schedule* S, int B, int32_t* tokens, const
   P.s_gu8_l = h->s_gu8_l;
   P.s_gu8_e = h->s_gu8_e;
   P.wd8 = h->wd8;
+  P.wd8p = h->wd8p;
   P.s_d8_l = h->s_d8_l;
   P.s_d8_e = h->s_d8_e;
   P.fsc = h->fsc;

@@ -124,7 +124,8 @@ struct mk_params {
   // FP8 (E4M3) feed-forward weights, when ffn_fp8 (then wgu and wd are unused)
   int32_t ffn_fp8;
   const uint8_t* wgu8; size_t s_gu8_l, s_gu8_e; // per layer, expert: gate/up panels interleaved, chunk pairs
-  const uint8_t* wd8; size_t s_d8_l, s_d8_e;    // per layer, expert: [F/16][H][16] codes
+  const uint8_t* wd8; size_t s_d8_l, s_d8_e;    // per layer, expert: [F/16][H][16] codes (batches <= 4)
+  const uint8_t* wd8p;                           // the same codes in chunk-pair panels [F x H] (larger batches)
   const float* fsc; size_t s_fsc_l, s_fsc_e;    // per layer, expert: [F][4] scales (gate, up, down, 0)
   const float* rope;             // [max_seq][D/2][2] (cos, sin)
   uint16_t* kv; size_t s_kv_l;   // KV pool, layer stride in elements

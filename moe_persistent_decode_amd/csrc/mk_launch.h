@@ -7,11 +7,12 @@
 hipError_t mk_launch_interp(const mk_params& P, int head_dim, int grid, bool cooperative, hipStream_t stream);
 hipError_t mk_launch_repack(const uint16_t* src, uint16_t* dst, int K, int N, int ld, int dst0, int dstep,
                             int nz, size_t src_zstride, size_t dst_zstride, hipStream_t stream);
-// FP8 feed-forward weights: canonical [E][K=H][F] gate and up codes into the
-// interleaved chunk-pair panels, [E][F][H] down codes into per-slice column
-// runs, and the three [E][F] scale vectors into (gate, up, down, 0) float4s.
-hipError_t mk_launch_repack_fp8_gu(const uint8_t* wg, const uint8_t* wu, uint8_t* dst, int H, int F, int E,
-                                   hipStream_t stream);
+// FP8 feed-forward weights: canonical [K x N] codes into chunk-pair panels
+// (source panel j to dst0 + j * dstep, nz matrices), [E][F][H] down codes into
+// per-slice column runs, and the three [E][F] scale vectors into
+// (gate, up, down, 0) float4s.
+hipError_t mk_launch_repack_fp8_panels(const uint8_t* src, uint8_t* dst, int K, int N, int dst0, int dstep, int nz,
+                                       size_t src_zstride, size_t dst_zstride, hipStream_t stream);
 hipError_t mk_launch_repack_fp8_d(const uint8_t* wd, uint8_t* dst, int F, int H, int E, hipStream_t stream);
 hipError_t mk_launch_pack_scales(const float* sg, const float* su, const float* sd, float* dst, int n,
                                  hipStream_t stream);

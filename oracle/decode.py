@@ -105,15 +105,25 @@ def float_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 #       Wu[k, f] = e4m3(Cu[k, f]) * su[f], Wd[f, n] = e4m3(Cd[f, n]) * sd[f]).
 #       The rest of the step is as for bf16 weights.
 
-def e4m3_to_float(codes: np.ndarray) -> np.ndarray:
-    """OCP FP8 E4M3 codes (uint8) -> float64 values (R19), from the fields."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_fields(c: np.ndarray) -> np.ndarray:
+    """The value of each E4M3 code from its sign, exponent and mantissa fields (R19)."""
+    c = np.asarray(c, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
     mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
     mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
     return sign * mag
+
+
+# the 256 code values, decoded once from the fields
+_E4M3_VALUES = _e4m3_fields(np.arange(256))
+
+
+def e4m3_to_float(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64 values (R19): each code's value
+    from its fields (looked up among the 256 decoded once)."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def fp8_ffn_weights(cg, cu, cd, sg, su, sd, dtype=np.float64):

@@ -448,15 +448,16 @@ def test_litmus_rejects_bad_arguments_on_the_host():
 
 
 def test_fp8_ffn_config_limits_and_loader_checks():
-    """FP8 feed-forward weights: batches of at most 4 (the fused path), a 0/1
-    flag; a host-only handle takes no weights, and a bf16 handle refuses the
-    FP8 loader. An FP8 handle's schedules are the bf16 model's."""
+    """FP8 feed-forward weights: a 0/1 flag (a dense model keeps its batch
+    limit of 4); a host-only handle takes no weights, and a bf16 handle
+    refuses the FP8 loader. An FP8 handle's schedules simulate at every batch
+    (the claiming MoE above 4 sequences)."""
     import moe_persistent_decode_amd as mk
     from moe_persistent_decode_amd.binding import Decoder, MkError
+    cfg = mk.make_config(configs.TINY_DENSE, 5, 1024, 64, 64, 0, ffn_fp8=True)
+    with pytest.raises(MkError, match="at most"):
+        Decoder(cfg, host_only_cus=256)
     for m in (configs.TINY, configs.TINY_DENSE):
-        cfg = mk.make_config(m, 5, 1024, 64, 64, 0, ffn_fp8=True)
-        with pytest.raises(MkError, match="FP8"):
-            Decoder(cfg, host_only_cus=256)
         cfg = mk.make_config(m, 4, 1024, 64, 64, 0)
         cfg.ffn_fp8 = 2
         with pytest.raises(MkError, match="ffn_fp8"):
@@ -468,6 +469,13 @@ def test_fp8_ffn_config_limits_and_loader_checks():
     st, msg = d.simulate(4, 1000, [1] * configs.TINY.n_layers, seed=3)
     assert st == 0, msg
     d.close()
+    for B in (5, 8, 16, 17, 32):
+        cfg = mk.make_config(configs.FULL48, B, 8192 + 64, 520 * B, 520, 0, ffn_fp8=True)
+        d = Decoder(cfg, host_only_cus=256)
+        for seed in (1, 2):
+            st, msg = d.simulate(B, 8192, [min(128, 8 * B)] * configs.FULL48.n_layers, seed=seed)
+            assert st == 0, (B, msg)
+        d.close()
     bf = _host(configs.TINY, batch=4, max_seq=1024)
     with pytest.raises(MkError, match="host-only|not an FP8"):
         bf.load_ffn_fp8(0, 16, 16, 16, 16, 16, 16, stream=0)

@@ -16,8 +16,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # instantiation (head dim, row tiles, FP8 feed-forward weights) -> most VGPR
 # spills allowed; SGPR spills (to VGPR lanes, no memory traffic; the dense FFN
 # claimer's own instance roughly doubles them) are bounded loosely
-VGPR_SPILLS = {(64, 1, 0): 7, (64, 2, 0): 3, (128, 1, 0): 8, (128, 2, 0): 3, (64, 1, 1): 12, (128, 1, 1): 11}
-SGPR_SPILLS_MAX = 350
+VGPR_SPILLS = {(64, 1, 0): 7, (64, 2, 0): 3, (128, 1, 0): 8, (128, 2, 0): 3,
+               (64, 1, 1): 10, (64, 2, 1): 6, (128, 1, 1): 10, (128, 2, 1): 6}
+# (the FP8 batch <= 16 instance holds the fused and the claiming MoE)
+SGPR_SPILLS_MAX = {0: 350, 1: 400}
 
 
 def _build_module():
@@ -42,7 +44,7 @@ def test_megakernel_resource_budget():
         assert r["Occupancy [waves/SIMD]"] >= 2, (sym, r)
         assert r["VGPRs"] + r["AGPRs"] <= 256, (sym, r)
         assert r["VGPRs Spill"] <= VGPR_SPILLS[key], (sym, r)
-        assert r["SGPRs Spill"] <= SGPR_SPILLS_MAX, (sym, r)
+        assert r["SGPRs Spill"] <= SGPR_SPILLS_MAX[fp8], (sym, r)
         assert r["ScratchSize [bytes/lane]"] <= 8 * VGPR_SPILLS[key] + 8, (sym, r)
         assert r["LDS Size [bytes/block]"] <= 160 * 1024, (sym, r)
         assert r["Dynamic Stack"] == "False", (sym, r)
