@@ -49,7 +49,7 @@ def parse():
                     help="comma-separated long-context workloads timed after the others ('none' to skip)")
     ap.add_argument("--dense-workload", default="llama1b_b1_8k",
                     help="dense (Llama-3.2-1B-shaped) workload timed after the others ('none' to skip)")
-    ap.add_argument("--fp8-workloads", default="full48_b1_8k,llama1b_b1_8k",
+    ap.add_argument("--fp8-workloads", default="full48_b1_8k,full48_b32_ragged,llama1b_b1_8k",
                     help="workloads measured again with FP8 feed-forward weights, reported under fp8_weights "
                          "('none' to skip)")
     ap.add_argument("--ffn-fp8", action="store_true",
@@ -568,7 +568,7 @@ def main():
         out["fp8_weights"] = []
         for i, name in enumerate(args.fp8_workloads.split(",")):
             wf = configs.WORKLOADS[name]
-            kf = max(8, args.steps // 2)
+            kf = max(8, args.steps // (4 if wf.batch > 4 else 2))
             rf, _ = measure(wf, kf, min(args.warmup, 4), False, args.fp8_op_trace if i == 0 else None, fp8=True)
             d = summary(wf, rf, kf)
             d["weights"] = "feed-forward FP8 E4M3 (per-hidden-unit float32 scales), other weights bf16"
