@@ -204,7 +204,9 @@ def op_trace(r, path, raw_path=None):
     us = lambda k: (tr[:, k] - t0) / 100.0  # 100 MHz device clock
     start, waited, end = us(1), us(2), us(5)
     span = end.max()
-    lines = [f"# Per-opcode time of one decode step: {r.wl.name}", "",
+    cmd = "python3 bench.py " + " ".join(sys.argv[1:])
+    lines = [f"# Per-opcode time of one decode step: {r.wl.name}{' (FP8 feed-forward weights)' if r.fp8 else ''}", "",
+             f"Command (on the MI355X box): `{cmd}`", "",
              f"One traced megakernel step (batch {r.B}); step span {span:.1f} us over {info.n_cus} workgroups.", "",
              "| opcode | tasks | mean wait (us) | mean run after wait (us) | workgroup-time share |",
              "|---|---:|---:|---:|---:|"]
