@@ -1915,20 +1915,29 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   if ((int)tid() < 128) sm.done_cnt[tid()] = 0;
   mark(sm, 0);
   // the stream of one queue: the item after the current one (uniform)
+  // (current claim: base and size ch; pending claim: pend and size pch)
   struct Stream {
-    int base, j, pend, ch;
+    int base, j, pend, ch, pch, full;
   };
   // (the pending claim is issued unconditionally by thread 0 and read only
   // there, so its result stays in one register: a copy of it, at a join of
   // paths that did and did not claim, would wait for the atomic at once and,
   // the memory counter retiring in order, for every weight load before it.
   // Claims past the queue's end are harmless: their items do not exist.)
+  // Near the queue's end the claims shrink to single items, once fewer than
+  // two rounds of full claims over every workgroup remain beyond the current
+  // one, so the last claimers do not each hold a whole chunk while the others
+  // are done.
+  auto claim_size = [&](const Stream& q, int n) -> int {
+    return n - q.base > 2 * q.full * (int)gridDim.x ? q.full : 1;
+  };
   auto stream_start = [&](Stream& q, int base, int32_t ctr, int n, int ch) {
     q.base = base;
     q.j = 0;
-    q.ch = ch;
+    q.ch = q.full = ch;
+    q.pch = claim_size(q, n);
     if (tid() == 0)
-      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)q.pch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto stream_next = [&](Stream& q, int32_t ctr, int n) -> int {
     if (++q.j < q.ch) return q.base + q.j;
@@ -1937,8 +1946,10 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
     q.base = sm.claim;
     lds_sync();
     q.j = 0;
+    q.ch = q.pch;
+    q.pch = claim_size(q, n);
     if (tid() == 0)
-      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)q.ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      q.pend = (int)__hip_atomic_fetch_add(&P.ctr[ctr], (uint32_t)q.pch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return q.base;
   };
   // this lane's row of row tile rt of active expert a: the element offset
