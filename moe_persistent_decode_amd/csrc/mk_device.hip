@@ -1896,7 +1896,40 @@ __device__ __forceinline__ void down_item(const mk_params& P, const mk_task& t, 
 // more), loaded together with the item's weights, so an item's operand takes
 // one row tile of registers instead of the whole batch's two and two items'
 // weights stream at once. Down items as in the claiming variant.
-template <int NCH, int NBMAX, int NCHD, bool FP8 = false>
+// One O-projection item of a claiming MoE claimer: group g's K slice of column
+// block cb for every token (the product op_oproj runs above MK_FUSED_B
+// tokens), once the group's combined attention output is complete (counter
+// b[0] + g, target b[1]); its contribution counts on the block's counter,
+// and the last contribution to the block does its residual.
+template <int MT>
+__device__ __forceinline__ void oproj_item(const mk_params& P, const mk_task& t, int g, int cb, Smem& sm) {
+  constexpr int NCH = 32 / MK_WAVES, NPO = 4;
+  const int l = t.layer;
+  const int DP = P.CB / 16, p0 = cb * DP;
+  const int kc = P.QH * P.D / 32;
+  const int c0 = g * P.G * P.D / 32, c1 = c0 + P.G * P.D / 32;
+  const size_t pstride = (size_t)kc * 512;
+  WTile<NPO, NCH> w;
+  wtile_load(w, P.wo + l * P.s_wo + (size_t)p0 * pstride, pstride, DP, c0, c1);
+  if (!wait_one(P, t.b[0] + g, t.b[1], sm)) return;
+  set_rows_batch(P, sm, 0, P.QH * P.D, 0);
+  __syncthreads();
+  ATile<MT, NCH> Ah, Al;
+  atile_load_bf16(Ah, Pub(o_of(P, 0)), sm.row_off[0], c0, c1);
+  atile_load_bf16(Al, Pub(o_of(P, 1)), sm.row_off[0], c0, c1);
+  Acc<NPO, MT> acc;
+  mfma_tiles(acc, w, Ah, Al);
+  reduce_tiles(acc, sm);
+  const Pub AO(P.ao);
+  for (int o = tid(); o < NPO * MT * 256; o += MK_WG_THREADS) {
+    const int pp = o / (MT * 256), mt = (o / 256) % MT, m = (o / 16) % 16, nn = o % 16;
+    const int b = mt * 16 + m;
+    if (pp < DP && b < P.B) AO.stf((g * P.B + b) * P.H + (p0 + pp) * 16 + nn, sm.out[o]);
+  }
+  block_arrive(P, t, t.a[4], cb, sm);
+}
+
+template <int NCH, int NBMAX, int NCHD, bool FP8 = false, int MT = 2>
 __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task& t, Smem& sm) {
   if (!wait_task(P, t, sm)) return;
   const int l = t.layer, claim_ctr = t.a[0], done_base = t.a[1], dclaim_ctr = t.a[3];
@@ -2098,6 +2131,18 @@ __device__ __forceinline__ void op_moe_gather(const mk_params& P, const mk_task&
   if ((int)tid() < 128 && sm.done_cnt[tid()] > 0)
     __hip_atomic_fetch_add(&P.ctr[done_base + tid()], (uint32_t)sm.done_cnt[tid()], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+  // The layer's O projection as a queue of (group, column block) items
+  // (a[5] its claim counter; -1: the projection runs as tasks), drained
+  // between the up/gate and down phases: by then every group's attention has
+  // long completed, and the projection's work joins the balanced claimed
+  // work instead of following the slowest claimer on fixed units.
+  if (t.a[5] >= 0) {
+    const int n_op = P.KVH * P.NB;
+    for (int id = claim_n(P, t.a[5], 1, sm); id < n_op; id = claim_n(P, t.a[5], 1, sm)) {
+      oproj_item<MT>(P, t, id / P.NB, id % P.NB, sm);
+      if (error_seen(error_peek(P), sm)) return;
+    }
+  }
   mark(sm, 2);
   // down items (two row tiles of routed rows), the next item's weights
   // streaming while the current computes; consecutive items of one expert
@@ -3168,11 +3213,11 @@ __device__ __forceinline__ void run_task_mt(const mk_params& P, const mk_task& t
       // above: claiming, each item's routed rows
       // (FP8 feed-forward weights: claiming at every batch above MK_FUSED_B)
       if constexpr (FP8)
-        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES, true>(P, t, sm);
+        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES, true, MT>(P, t, sm);
       else if constexpr (MT == 1)
         op_moe_static<32 / MK_WAVES, 24 / MK_WAVES, 4>(P, t, sm);
       else
-        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES>(P, t, sm);
+        op_moe_gather<32 / MK_WAVES, 2, 24 / MK_WAVES, false, MT>(P, t, sm);
       break;
     case MK_OP_MOE_FUSED:
       // (a dense layer's FFN has its own instance: its weight prefetch before

@@ -73,6 +73,7 @@ struct CtrIdx {
   int fin;       // fused MoE: claimers and O projections done (dense: the FFN claimers)
   int mid;       // dense: O projections done (the mid residual's wait)
   int midres;    // dense: mid residual column blocks done (the FFN's input)
+  int oproj_claim;  // claiming MoE: claim counter of the O-projection items
 };
 
 mk_task make_task(int op, int layer) {
@@ -190,7 +191,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // attention per (sequence, group), combine per group, router, route,
 // attention claims, up and down claims, up/gate done per expert slot, column
 // blocks, fin, mid, midres.
-int counters_per_layer(int KVH, int B, int E, int NB) { return KVH + B * KVH + KVH + 5 + E + NB + 3; }
+int counters_per_layer(int KVH, int B, int E, int NB) { return KVH + B * KVH + KVH + 5 + E + NB + 4; }
 
 mk_status validate_config(const mk_config* c) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null config");
@@ -492,7 +493,8 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
     b0 += NB;
     x.fin = b0++;
     x.mid = b0++;
-    x.midres = b0;
+    x.midres = b0++;
+    x.oproj_claim = b0;
     return x;
   };
 
@@ -784,6 +786,7 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         t.a[3] = x.down_claim;
         t.a[4] = x.colblk;
         t.sig_ctr[0] = resid(l + 1);
+        t.a[5] = -1;
         if (fixed) {
           t.b[0] = attn_cu[(moe_flat0 + i) % n_w] ? k_attn++ : k_free++;
           t.b[1] = n_free;
@@ -793,6 +796,11 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
           add_wait(t, x.router, h->n_router_tasks);
         } else {
           add_wait(t, x.route, 1);
+          // the O projection's (group, column block) items, claimed between
+          // the up/gate and down phases once the group's output is combined
+          t.a[5] = x.oproj_claim;
+          t.b[0] = x.comb;
+          t.b[1] = B;
         }
         // (one claimer per unit: fixed-share claimers wait for each other's
         // up/gate items)
@@ -849,6 +857,9 @@ std::unique_ptr<Schedule> build_schedule(const mk_handle* h, int B, int hint) {
         wave_oproj_fused();
       }
       wave_residual();
+    } else if (!fixed) {
+      // (claiming: the O projection is the MoE claimers' item queue)
+      wave_moe();
     } else if (h->wave_order == MK_ORDER_ATTENTION_FIRST) {
       wave_oproj();
       wave_moe();
@@ -911,7 +922,8 @@ struct SimCU {
   bool in_claimer = false;
   int pending_item = -1;  // claimed item waiting for its dependency
   int chunk_end = 0;      // attention: end of the current claim
-  int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items, 2 fixed-share down pairs
+  int phase = 0;          // MoE claimer: 0 up/gate items, 1 down items, 2 fixed-share down pairs,
+                          // 3 O-projection items
   int item_end = 0;       // fixed shares: end of this claimer's down items (pending_item: the next)
   int pos = 0;
 };
@@ -1045,6 +1057,13 @@ mk_status check_hazards(const mk_handle* h, const Schedule& S, uint32_t flags, s
         const Bits* u = counter_union(t.a[1] + g, k);
         if (u) K[k].merge(*u);
       }
+    // a claiming MoE claimer's O-projection items wait for their group's
+    // combined output (b[0] + g, count b[1])
+    if (t.op == MK_OP_MOE_UP && t.a[5] >= 0)
+      for (int g = 0; g < KVH; ++g) {
+        const Bits* u = counter_union(t.b[0] + g, k);
+        if (u) K[k].merge(*u);
+      }
   }
   // the regions each task touches
   auto accesses = [&](int k) {
@@ -1108,6 +1127,11 @@ mk_status check_hazards(const mk_handle* h, const Schedule& S, uint32_t flags, s
       case MK_OP_MOE_UP:
         all_input(par, 2);
         a.push_back({R_RP, l, false, 2});
+        if (t.a[5] >= 0)  // O-projection items
+          for (int g = 0; g < KVH; ++g) {
+            a.push_back({R_O, g, false, 2});
+            for (int cb = 0; cb < NB; ++cb) a.push_back({R_AO, g * NB + cb, true, 2});
+          }
         for (int cb = 0; cb < NB; ++cb) block_residual(cb);
         break;
       case MK_OP_RESIDUAL: {
@@ -1222,6 +1246,7 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
     want[k++] = fused ? S.moe_fused[l] + (c.dense ? 0 : S.n_oproj) : 0;  // fused MoE: claimers, O projections
     want[k++] = c.dense ? S.n_oproj : 0;                                  // dense: O projections
     want[k++] = c.dense ? NB : 0;                                         // dense: mid residual blocks
+    want[k++] = claiming ? (int64_t)KVH * NB + S.n_up_claimers : 0;         // O-projection item claims
   }
   // a lost signal: the first wait of the first task at or after `corrupt`
   // waits for one arrival more than its counter ever receives
@@ -1351,10 +1376,23 @@ mk_status simulate(mk_handle* h, const Schedule& S, const int32_t* n_active, uin
         const int id = (int)ctr[t.a[0]]++;
         progress = true;
         if (id >= na * up_per_e) {
-          u.phase = 1;
+          u.phase = t.a[5] >= 0 ? 3 : 1;
           u.pending_item = -1;
         } else {
           ctr[t.a[1] + id / up_per_e]++;
+        }
+      } else if (u.phase == 3) {  // MoE claimer, O-projection items
+        if (u.pending_item < 0) {
+          const int id = (int)ctr[t.a[5]]++;
+          progress = true;
+          if (id >= KVH * NB)
+            u.phase = 1;
+          else
+            u.pending_item = id;
+        } else if (ctr[t.b[0] + u.pending_item / NB] >= t.b[1]) {
+          block(t, t.a[4], u.pending_item % NB, l);
+          u.pending_item = -1;
+          progress = true;
         }
       } else if (u.pending_item < 0) {  // MoE claimer, down items
         const int id = (int)ctr[t.a[3]]++;

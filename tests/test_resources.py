@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # instantiation (head dim, row tiles, FP8 feed-forward weights) -> most VGPR
 # spills allowed; SGPR spills (to VGPR lanes, no memory traffic; the dense FFN
 # claimer's own instance roughly doubles them) are bounded loosely
-VGPR_SPILLS = {(64, 1, 0): 7, (64, 2, 0): 3, (128, 1, 0): 8, (128, 2, 0): 3,
+VGPR_SPILLS = {(64, 1, 0): 7, (64, 2, 0): 4, (128, 1, 0): 8, (128, 2, 0): 4,
                (64, 1, 1): 10, (64, 2, 1): 6, (128, 1, 1): 10, (128, 2, 1): 6}
 # (the FP8 batch <= 16 instance holds the fused and the claiming MoE)
 SGPR_SPILLS_MAX = {0: 350, 1: 400}
