@@ -175,7 +175,8 @@ mk_status mk_load_globals(mk_handle* h, const void* emb, const void* gamma_f,
 /* All weights at once: arrays of n_layers device pointers per tensor kind
  * (host arrays of device pointers); the same checks as the calls above. A
  * dense model gives gamma2 and leaves wr NULL; a MoE model leaves gamma2
- * NULL. */
+ * NULL. An FP8 model (cfg.ffn_fp8) leaves wg, wu and wd NULL and loads its
+ * feed-forward weights with mk_load_ffn_fp8. */
 typedef struct {
   const void* emb;
   const void* gamma_f;
