@@ -480,3 +480,21 @@ def test_fp8_ffn_config_limits_and_loader_checks():
     with pytest.raises(MkError, match="host-only|not an FP8"):
         bf.load_ffn_fp8(0, 16, 16, 16, 16, 16, 16, stream=0)
     bf.close()
+
+
+@pytest.mark.parametrize("batch", [1, 4, 8, 16, 32])
+def test_fp8_schedules_pass_the_hazard_check(batch):
+    """An FP8 model's schedules (the claiming MoE from 5 sequences on, with
+    the O projection as the claimers' item queue) pass the per-buffer tag
+    check in every wave order and the tuned and round-robin placements."""
+    import moe_persistent_decode_amd as mk
+    from moe_persistent_decode_amd.binding import Decoder
+    m = configs.FULL48
+    mpps = -(-(16384 + 64) // m.page_size)
+    d = Decoder(mk.make_config(m, batch, 16384 + 64, mpps * batch, mpps, 0, ffn_fp8=True), host_only_cus=256)
+    for order in range(3):
+        for placement in (0, 1):
+            d.set_schedule_options(order, placement)
+            st, rep = d.check_hazards(batch, 16384 if batch > 4 else 8192)
+            assert st == 0, (order, placement, rep)
+    d.close()
